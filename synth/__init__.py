@@ -1,0 +1,327 @@
+"""Seeded synthetic inputs for the routed int4 MoE expert layer.
+
+This module is shared by the tests, the benchmark and the oracle's callers.  It
+draws random tensors and encodes expert weights into the two int4 group
+formats; it holds none of the layer's own arithmetic (no router product, no
+top-k, no grouping, no expert MLP, no combine).
+
+Sources of the recipe (drama-rs / drama-q4 / drama-3-w4a16 model pages):
+  * expert weights are int4 with a per-group f16 scale and f16 min, group 64
+    along the input dimension (drama-q4 card, "What's quantized" table), or
+    int4 symmetric with one f16 scale per 128 input weights
+    (drama-3-w4a16 card, "At a glance" table and "How it was made");
+  * each scale is picked from 20 clipping ratios 1.0 down to 0.81 by least
+    squared error, with no calibration data (drama-3-w4a16, "How it was
+    made"; drama-q4 names the same "MSE clip search");
+  * router, activations: bf16 (drama-q4 "What's quantized": router bf16).
+
+Random streams: every tensor gets its own torch.Generator seeded from
+(config seed, tensor tag) through a fixed 64-bit mix, so tensors do not depend
+on the order they are drawn in.  Generation runs on the device that will hold
+the tensor (torch's CPU and GPU generators differ, so the same seed gives
+different values on the two; each test draws on one device only).
+
+Layout written here (the library's canonical layout):
+  packed nibbles  uint8  [E][N][K/2], byte j of a row holds k = 2j in its low
+                  nibble and k = 2j+1 in its high nibble;
+  asym scale/min  uint16 (f16 bits) [E][N][K/64][2] = {scale, min};
+  sym scale       uint16 (f16 bits) [E][N][K/128];
+  gate, up: N = inter, K = hidden; down: N = hidden, K = inter.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+
+import torch
+
+FMT_ASYM_G64 = 0
+FMT_SYM_G128 = 1
+GROUP = {FMT_ASYM_G64: 64, FMT_SYM_G128: 128}
+
+# 20 clipping ratios, 1.00, 0.99, ..., 0.81 (drama-3-w4a16, "How it was made").
+CLIP_RATIOS = tuple(round(1.0 - 0.01 * i, 2) for i in range(20))
+
+# Rows quantised per chunk, to bound temporaries on the host.
+_CHUNK_ELEMS = 1 << 24
+
+
+def stream_seed(seed: int, tag: str) -> int:
+    """64-bit seed for the tensor named ``tag`` under config seed ``seed``."""
+    h = hashlib.blake2b(f"{seed}:{tag}".encode(), digest_size=8).digest()
+    return int.from_bytes(h, "little") & ((1 << 63) - 1)
+
+
+def generator(seed: int, tag: str, device) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(stream_seed(seed, tag))
+    return g
+
+
+def normal(shape, std: float, seed: int, tag: str, device="cpu") -> torch.Tensor:
+    """float32 N(0, std^2) of ``shape``."""
+    g = generator(seed, tag, device)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t
+
+
+def bf16_bits(t: torch.Tensor) -> torch.Tensor:
+    """Round float32 to bf16 (round-to-nearest-even) and return the raw bits as int16."""
+    return t.to(torch.bfloat16).view(torch.int16)
+
+
+def f16_bits(t: torch.Tensor) -> torch.Tensor:
+    return t.to(torch.float16).view(torch.int16)
+
+
+def pack_nibbles(q: torch.Tensor) -> torch.Tensor:
+    """q: uint8 [..., K] with values 0..15 -> uint8 [..., K/2] (even k in the low nibble)."""
+    q = q.to(torch.uint8)
+    lo = q[..., 0::2]
+    hi = q[..., 1::2]
+    return (lo | (hi << 4)).contiguous()
+
+
+def _quantize_asym_rows(w: torch.Tensor, g: int, ratios):
+    """w: float32 [R, K] -> (q uint8 [R, K], scale f16 [R, K/g], min f16 [R, K/g])."""
+    R, K = w.shape
+    wg = w.reshape(R, K // g, g)
+    wmin = wg.amin(dim=2)
+    wmax = wg.amax(dim=2)
+    best_err = None
+    best_q = best_s = best_m = None
+    for r in ratios:
+        lo = (wmin * r).to(torch.float16)
+        s16 = ((wmax * r - wmin * r) / 15.0).to(torch.float16)
+        m = lo.float().unsqueeze(2)
+        s = s16.float().unsqueeze(2)
+        safe = torch.where(s > 0, s, torch.ones_like(s))
+        q = torch.round((wg - m) / safe).clamp_(0, 15)
+        q = torch.where(s > 0, q, torch.zeros_like(q))
+        err = ((q * s + m) - wg).square_().sum(dim=2)
+        if best_err is None:
+            best_err, best_q, best_s, best_m = err, q, s16, lo
+        else:
+            better = err < best_err  # ties keep the earlier (larger) ratio
+            best_err = torch.where(better, err, best_err)
+            best_q = torch.where(better.unsqueeze(2), q, best_q)
+            best_s = torch.where(better, s16, best_s)
+            best_m = torch.where(better, lo, best_m)
+    return best_q.reshape(R, K).to(torch.uint8), best_s, best_m
+
+
+def _quantize_sym_rows(w: torch.Tensor, g: int, ratios):
+    """w: float32 [R, K] -> (stored code q+8 uint8 [R, K], scale f16 [R, K/g])."""
+    R, K = w.shape
+    wg = w.reshape(R, K // g, g)
+    amax = wg.abs().amax(dim=2)
+    best_err = None
+    best_q = best_s = None
+    for r in ratios:
+        s16 = (amax * r / 7.0).to(torch.float16)
+        s = s16.float().unsqueeze(2)
+        safe = torch.where(s > 0, s, torch.ones_like(s))
+        q = torch.round(wg / safe).clamp_(-8, 7)
+        q = torch.where(s > 0, q, torch.zeros_like(q))
+        err = ((q * s) - wg).square_().sum(dim=2)
+        if best_err is None:
+            best_err, best_q, best_s = err, q, s16
+        else:
+            better = err < best_err
+            best_err = torch.where(better, err, best_err)
+            best_q = torch.where(better.unsqueeze(2), q, best_q)
+            best_s = torch.where(better, s16, best_s)
+    return (best_q + 8).reshape(R, K).to(torch.uint8), best_s
+
+
+def quantize(w: torch.Tensor, fmt: int, clip: bool = True):
+    """Encode float32 weights [..., N, K] (groups along K).
+
+    Returns (packed uint8 [..., N, K/2], scale/min int16 bits):
+      asym g64: [..., N, K/64, 2] = {scale, min};  sym g128: [..., N, K/128].
+    ``clip`` selects the 20-ratio least-squares search; without it only r = 1
+    (plain round-to-nearest) is used.
+    """
+    g = GROUP[fmt]
+    *lead, N, K = w.shape
+    if K % g:
+        raise ValueError(f"K={K} is not a multiple of the group {g}")
+    ratios = CLIP_RATIOS if clip else (1.0,)
+    rows = w.reshape(-1, K)
+    R = rows.shape[0]
+    step = max(1, _CHUNK_ELEMS // K) if rows.device.type == "cpu" else max(1, (1 << 27) // K)
+    packed = torch.empty((R, K // 2), dtype=torch.uint8, device=w.device)
+    if fmt == FMT_ASYM_G64:
+        sm = torch.empty((R, K // g, 2), dtype=torch.int16, device=w.device)
+    else:
+        sm = torch.empty((R, K // g), dtype=torch.int16, device=w.device)
+    for r0 in range(0, R, step):
+        r1 = min(R, r0 + step)
+        chunk = rows[r0:r1].float()
+        if fmt == FMT_ASYM_G64:
+            q, s, m = _quantize_asym_rows(chunk, g, ratios)
+            sm[r0:r1, :, 0] = s.view(torch.int16)
+            sm[r0:r1, :, 1] = m.view(torch.int16)
+        else:
+            q, s = _quantize_sym_rows(chunk, g, ratios)
+            sm[r0:r1] = s.view(torch.int16)
+        packed[r0:r1] = pack_nibbles(q)
+    return packed.reshape(*lead, N, K // 2), sm.reshape(*lead, N, *sm.shape[1:])
+
+
+@dataclasses.dataclass
+class Layer:
+    """One MoE layer's routed experts in the canonical packed layout."""
+    fmt: int
+    num_experts: int
+    hidden: int
+    inter: int
+    gate_q: torch.Tensor
+    up_q: torch.Tensor
+    down_q: torch.Tensor
+    gate_sm: torch.Tensor
+    up_sm: torch.Tensor
+    down_sm: torch.Tensor
+
+    @property
+    def group(self) -> int:
+        return GROUP[self.fmt]
+
+    def to(self, device) -> "Layer":
+        kw = {f.name: getattr(self, f.name) for f in dataclasses.fields(self)}
+        for k, v in kw.items():
+            if isinstance(v, torch.Tensor):
+                kw[k] = v.to(device)
+        return Layer(**kw)
+
+    def tensors(self):
+        return (self.gate_q, self.up_q, self.down_q, self.gate_sm, self.up_sm, self.down_sm)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.tensors())
+
+    def expert_nbytes(self) -> int:
+        return self.nbytes() // self.num_experts
+
+
+def make_layer(E: int, H: int, I: int, fmt: int, seed: int, tag: str = "layer",
+               clip: bool = True, std: float = 0.02, device="cpu") -> Layer:
+    """Draw N(0, std^2) float32 gate/up/down weights for E experts and encode them."""
+    out = {}
+    # experts are drawn from their own streams, then encoded a batch at a time
+    batch = max(1, (1 << 26) // (H * I)) if torch.device(device).type == "cpu" else E
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        qs, sms = [], []
+        for e0 in range(0, E, batch):
+            e1 = min(E, e0 + batch)
+            w = torch.empty((e1 - e0, N, K), dtype=torch.float32, device=device)
+            for e in range(e0, e1):
+                w[e - e0] = normal((N, K), std, seed, f"{tag}/{name}/{e}", device)
+            q, sm = quantize(w, fmt, clip)
+            qs.append(q)
+            sms.append(sm)
+            del w
+        out[name + "_q"] = torch.cat(qs).contiguous()
+        out[name + "_sm"] = torch.cat(sms).contiguous()
+    return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, **out)
+
+
+def zipf_logits(T: int, E: int, s: float, seed: int, device="cpu") -> torch.Tensor:
+    """bf16 bits [T][E]: ln p_{pi(e)} + Gumbel(0,1), p_r proportional to r^-s.
+
+    Taking the top-k of Gumbel-perturbed log-probabilities draws k experts
+    without replacement with probabilities proportional to p, so expert
+    popularity follows the Zipf law over a seeded permutation pi of the experts.
+    """
+    g = generator(seed, "zipf/perm", device)
+    perm = torch.randperm(E, generator=g, device=device)
+    ranks = torch.arange(1, E + 1, device=device, dtype=torch.float64)
+    p = ranks.pow(-s)
+    p = p / p.sum()
+    logp = torch.log(p)[perm].float()  # expert e gets rank perm[e]
+    g2 = generator(seed, "zipf/gumbel", device)
+    u = torch.rand((T, E), generator=g2, device=device, dtype=torch.float64)
+    u = u.clamp_(min=1e-300)
+    gumbel = -torch.log(-torch.log(u))
+    return bf16_bits((logp.unsqueeze(0).double() + gumbel).float())
+
+
+@dataclasses.dataclass
+class Case:
+    """A complete set of inputs for one MoE layer call (or a chain of layers)."""
+    name: str
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    fmt: int
+    x: torch.Tensor            # int16 bf16 bits [T][H]
+    router_w: torch.Tensor | None   # int16 bf16 bits [E][H] (None when logits are given)
+    logits: torch.Tensor | None     # int16 bf16 bits [T][E] when given directly
+    layers: list               # list[Layer] (one per layer)
+    router_ws: list | None = None   # per-layer router weights for chains
+
+
+CONFIGS = {
+    # name: (T, H, E, k, I, fmt, clip, router)
+    1: ("tiny", 4, 256, 16, 2, 128, FMT_ASYM_G64, False, "gemv"),
+    2: ("decode", 1, 2048, 256, 8, 512, FMT_ASYM_G64, True, "gemv"),
+    3: ("prefill_zipf", 512, 2048, 256, 8, 512, FMT_ASYM_G64, True, "zipf"),
+    4: ("frame", 16, 2048, 256, 8, 512, FMT_ASYM_G64, False, "gemv"),
+    5: ("long_prefill_sym", 4096, 2048, 256, 8, 512, FMT_SYM_G128, True, "normal"),
+}
+FRAME_LAYERS = 40
+
+
+def make_case(cfg: int, device="cpu", seed: int = 0, layers: int | None = None,
+              T: int | None = None) -> Case:
+    """Inputs of one of the five workload configurations (seed 0 by default).
+
+    ``layers`` overrides the 40-layer depth of the frame configuration and
+    ``T`` the token count (both for smaller runs of the same recipe).
+    """
+    name, T0, H, E, k, I, fmt, clip, router = CONFIGS[cfg]
+    T = T0 if T is None else T
+    nl = (FRAME_LAYERS if layers is None else layers) if cfg == 4 else 1
+    x = bf16_bits(normal((T, H), 1.0, seed, f"{name}/x", device))
+    lay, rws = [], []
+    for l in range(nl):
+        # configs 2 and 3 share one set of expert weights
+        wtag = "shared_2_3" if cfg in (2, 3) else f"{name}/L{l}"
+        lay.append(make_layer(E, H, I, fmt, seed, wtag, clip=clip, device=device))
+        if router == "gemv":
+            rtag = "shared_2_3/router" if cfg in (2, 3) else f"{name}/L{l}/router"
+            rws.append(bf16_bits(normal((E, H), 0.02, seed, rtag, device)))
+    logits = None
+    if router == "zipf":
+        logits = zipf_logits(T, E, 1.1, seed, device)
+    elif router == "normal":
+        logits = bf16_bits(normal((T, E), 1.0, seed, f"{name}/logits", device))
+    return Case(name=name, T=T, H=H, E=E, k=k, I=I, fmt=fmt, x=x,
+                router_w=rws[0] if rws else None, logits=logits, layers=lay,
+                router_ws=rws if rws else None)
+
+
+def random_layer(E, H, I, fmt, seed, device="cpu", tag="rand") -> Layer:
+    """Layer with uniformly random codes and scales drawn around the N(0, 0.02) statistics.
+
+    Used for shapes where the clip search would be slow and only the byte
+    layout matters (tests of the kernels' indexing at odd shapes).
+    """
+    g = GROUP[fmt]
+    out = {}
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        gen = generator(seed, f"{tag}/{name}", device)
+        q = torch.randint(0, 256, (E, N, K // 2), generator=gen, device=device, dtype=torch.int32)
+        out[name + "_q"] = q.to(torch.uint8)
+        s = (torch.rand((E, N, K // g), generator=gen, device=device) * 0.004 + 0.004)
+        if fmt == FMT_ASYM_G64:
+            m = -(torch.rand((E, N, K // g), generator=gen, device=device) * 0.03 + 0.03)
+            out[name + "_sm"] = torch.stack([f16_bits(s), f16_bits(m)], dim=-1).contiguous()
+        else:
+            out[name + "_sm"] = f16_bits(s).contiguous()
+    return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, **out)

@@ -1,0 +1,374 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle currently bound
+in the ``oracle`` module disagrees with its pin.  ``test_oracle.py`` runs them
+against the real oracle; ``test_oracle_mutants.py`` runs them against copies of
+the oracle with one planted mistake each and requires some pin to fail.
+
+What pins what:
+  * binary16 / bfloat16 decoding and bf16 rounding: numpy's float16 and
+    torch's bfloat16 conversions (library routines), on every bit pattern or
+    on a wide sample plus the halfway cases;
+  * dequantisation: hand-packed rows with hand-worked values
+    (tests/golden/dequant_cases.txt) and an independent numpy unpacking;
+  * router logits: numpy float64 matrix product, rounded by torch;
+  * top-k: brute force, a full stable sort of every token's logits;
+  * gates: scipy's softmax over all experts renormalised over the selected,
+    sum to one, the k = 1 and k = E special cases;
+  * grouping: numpy's stable argsort and the permutation invariants;
+  * expert MLP + combine: dense float64 numpy matmuls with scipy's logistic
+    function, the one-expert top-1 layer as a plain SwiGLU MLP, and gate
+    linearity (two identical experts selected together equal one);
+  * the synthetic quantiser: relative reconstruction error of symmetric
+    group-128 clip-searched int4 on Gaussian weights, 10.3% on the pages
+    (drama-3-w4a16 card, "How it was made").
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+
+def np_codes(q: np.ndarray, N: int, K: int) -> np.ndarray:
+    """uint8 [N][K/2] -> int codes [N][K] (low nibble = even k), by numpy bit ops."""
+    q = np.asarray(q, dtype=np.uint8).reshape(N, K // 2)
+    out = np.empty((N, K), dtype=np.int64)
+    out[:, 0::2] = q & 0x0F
+    out[:, 1::2] = q >> 4
+    return out
+
+
+def np_dequant64(fmt: int, q, sm, N: int, K: int) -> np.ndarray:
+    """Independent float64 dequantisation using numpy's float16 decoder."""
+    codes = np_codes(q, N, K).astype(np.float64)
+    g = 64 if fmt == oracle.FMT_ASYM_G64 else 128
+    sm = np.asarray(sm).view(np.uint16).view(np.float16).astype(np.float64)
+    if fmt == oracle.FMT_ASYM_G64:
+        sm = sm.reshape(N, K // g, 2)
+        s = np.repeat(sm[:, :, 0], g, axis=1)
+        m = np.repeat(sm[:, :, 1], g, axis=1)
+        return codes * s + m
+    s = np.repeat(sm.reshape(N, K // g), g, axis=1)
+    return (codes - 8.0) * s
+
+
+def torch_bf16_bits(a) -> np.ndarray:
+    t = torch.from_numpy(np.asarray(a, dtype=np.float32).copy())
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def rand_bf16(rng, shape, std=1.0) -> np.ndarray:
+    return torch_bf16_bits(rng.standard_normal(shape) * std)
+
+
+def rand_layer(rng, E, H, I, fmt):
+    """Random codes and f16 scales/mins of plausible magnitude (numpy arrays)."""
+    g = 64 if fmt == oracle.FMT_ASYM_G64 else 128
+    mats = {}
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        mats[name + "_q"] = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        s = (rng.random((E, N, K // g)) * 0.004 + 0.002).astype(np.float16)
+        if fmt == oracle.FMT_ASYM_G64:
+            m = (-(rng.random((E, N, K // g)) * 0.03 + 0.015)).astype(np.float16)
+            mats[name + "_sm"] = np.stack([s, m], axis=-1).view(np.uint16)
+        else:
+            mats[name + "_sm"] = s.view(np.uint16)
+    return mats
+
+
+def layer_args(mats):
+    return [mats[n] for n in ("gate_q", "up_q", "down_q", "gate_sm", "up_sm", "down_sm")]
+
+
+def np_expert_out(fmt, mats, e, x64, H, I):
+    """o = Wd silu(Wg x) * (Wu x) in float64 with numpy matmuls and scipy's expit."""
+    wg = np_dequant64(fmt, mats["gate_q"][e], mats["gate_sm"][e], I, H)
+    wu = np_dequant64(fmt, mats["up_q"][e], mats["up_sm"][e], I, H)
+    wd = np_dequant64(fmt, mats["down_q"][e], mats["down_sm"][e], H, I)
+    a = wg @ x64
+    b = wu @ x64
+    h = a * scipy.special.expit(a) * b
+    return wd @ h
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def read_dequant_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "dequant_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, *rest = line.split()
+            if head == "case":
+                kv = dict(r.split("=") for r in rest[1:])
+                cur = {"name": rest[0], "fmt": int(kv["fmt"]), "N": int(kv["N"]), "K": int(kv["K"])}
+                cases.append(cur)
+            elif head == "bytes":
+                cur["bytes"] = [int(v, 16) for v in rest]
+            elif head == "sm":
+                cur["sm"] = [int(v, 16) for v in rest]
+            elif head == "expect":
+                cur["expect"] = [float(v) for v in rest]
+    return cases
+
+
+def cyc(vals, n):
+    return [vals[i % len(vals)] for i in range(n)]
+
+
+# -------------------------------------------------------------------- pins
+
+def pin_f16_decode_all():
+    """Every binary16 bit pattern decodes as numpy's float16 does."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_value(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_bf16_decode_all():
+    """Every bfloat16 bit pattern decodes as torch's bfloat16 does."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_value(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_bf16_round():
+    """Round-to-nearest-even to bf16 matches torch on a wide sample and on halfway cases."""
+    rng = np.random.default_rng(7)
+    mant = rng.random(40000) + 1.0
+    expo = rng.integers(-133, 128, size=40000)
+    vals = (mant * np.exp2(expo.astype(np.float64))).astype(np.float32)
+    vals *= np.where(rng.random(40000) < 0.5, -1, 1).astype(np.float32)
+    # exact halfway points between neighbouring bf16 values, both parities
+    hw = (rng.integers(0, 0x7f7f, size=4000, dtype=np.uint32) << 16) | 0x8000
+    halfway = hw.astype(np.uint32).view(np.float32)
+    special = np.array([0.0, -0.0, 3.3895314e38, 3.4028235e38, 1e-45, -1e-45, 1.1754944e-38,
+                        np.inf, -np.inf, 1.0, 1.00390625, 1.01171875], dtype=np.float32)
+    allv = np.concatenate([vals, halfway, special])
+    got = oracle.bf16_round_array(allv)
+    ref = torch_bf16_bits(allv)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} mismatches"
+
+
+def pin_dequant_golden():
+    """Hand-packed rows decode to their hand-worked values, exactly."""
+    for c in read_dequant_cases():
+        N, K = c["N"], c["K"]
+        q = np.array(cyc(c["bytes"], N * K // 2), dtype=np.uint8)
+        sm = np.array(c["sm"], dtype=np.uint16)
+        got = oracle.dequant(c["fmt"], q, sm, N, K).ravel()
+        exp = np.array(cyc(c["expect"], N * K), dtype=np.float64)
+        assert np.array_equal(got.astype(np.float64), exp), c["name"]
+
+
+def pin_dequant_random():
+    """Random rows: float32 of the exact value, as computed independently by numpy."""
+    rng = np.random.default_rng(11)
+    for fmt in (oracle.FMT_ASYM_G64, oracle.FMT_SYM_G128):
+        N, K = 7, 384
+        g = 64 if fmt == oracle.FMT_ASYM_G64 else 128
+        q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+        ng = N * (K // g) * (2 if fmt == oracle.FMT_ASYM_G64 else 1)
+        sm = rng.integers(0, 0x7c00, size=ng, dtype=np.uint16)
+        sm |= (rng.integers(0, 2, size=ng, dtype=np.uint16) << 15)
+        ref = np_dequant64(fmt, q, sm, N, K).astype(np.float32)
+        got = oracle.dequant(fmt, q, sm, N, K)
+        assert np.array_equal(got, ref)
+
+
+def pin_router():
+    """Logits = bf16 of the float64 product computed by numpy (plus bias), bit for bit."""
+    rng = np.random.default_rng(3)
+    for (T, H, E) in ((5, 256, 16), (3, 2048, 64)):
+        x = rand_bf16(rng, (T, H))
+        wr = rand_bf16(rng, (E, H), 0.02)
+        bias = (rng.standard_normal(E) * 0.5).astype(np.float32)
+        for b in (None, bias):
+            acc = bf16_to_f64(x) @ bf16_to_f64(wr).T
+            if b is not None:
+                acc = acc + b.astype(np.float64)
+            ref = torch_bf16_bits(acc.astype(np.float32))
+            got = oracle.router(x, wr, T, H, E, b)
+            assert np.array_equal(got, ref.reshape(T, E))
+
+
+def _bf16_small_ints(rng, shape, hi):
+    return torch_bf16_bits(rng.integers(-hi, hi + 1, size=shape).astype(np.float32) * 0.25)
+
+
+def pin_topk_bruteforce():
+    """Top-k = first k of a full stable sort by (logit descending, expert ascending)."""
+    rng = np.random.default_rng(5)
+    for (T, E, k) in ((64, 16, 2), (64, 256, 8), (16, 9, 9), (8, 5, 1)):
+        for lg in (rand_bf16(rng, (T, E)), _bf16_small_ints(rng, (T, E), 3)):
+            idx, _ = oracle.topk(lg, T, E, k)
+            v = bf16_to_f64(lg).reshape(T, E)
+            for t in range(T):
+                order = np.lexsort((np.arange(E), -v[t]))
+                assert list(idx[t]) == list(order[:k]), (T, E, k, t)
+
+
+def pin_topk_adversarial():
+    """All-equal logits give 0..k-1; ties straddling rank k go to the lower index; NaN ranks last."""
+    E, k = 256, 8
+    lg = np.full((1, E), torch_bf16_bits(np.float32([0.5]))[0], dtype=np.uint16)
+    idx, gate = oracle.topk(lg, 1, E, k)
+    assert list(idx[0]) == list(range(k))
+    assert np.allclose(gate, 1.0 / k, rtol=1e-7, atol=0)
+    vals = np.zeros(E, dtype=np.float32)
+    vals[[200, 100, 50, 3]] = 2.0          # four leaders
+    vals[[250, 9, 180, 77, 8, 130]] = 1.0  # six tied for the last four places
+    lg = torch_bf16_bits(vals)[None, :]
+    idx, _ = oracle.topk(lg, 1, E, k)
+    assert list(idx[0]) == [3, 50, 100, 200, 8, 9, 77, 130]
+    vals = np.zeros(E, dtype=np.float32)
+    vals[:k] = np.nan
+    lg = torch_bf16_bits(vals)[None, :]
+    idx, _ = oracle.topk(lg, 1, E, k)
+    assert list(idx[0]) == list(range(k, 2 * k))
+
+
+def pin_gates():
+    """Gates: softmax over all experts renormalised over the selected; sums; special cases."""
+    rng = np.random.default_rng(9)
+    for (T, E, k) in ((32, 256, 8), (32, 16, 2), (8, 12, 12), (8, 40, 1)):
+        lg = rand_bf16(rng, (T, E), 1.5)
+        idx, gate = oracle.topk(lg, T, E, k)
+        v = bf16_to_f64(lg).reshape(T, E)
+        full = scipy.special.softmax(v, axis=1)
+        for t in range(T):
+            sel = full[t, idx[t]]
+            ref = sel / sel.sum()
+            assert np.allclose(gate[t], ref, rtol=1e-6, atol=0)
+            assert abs(float(gate[t].astype(np.float64).sum()) - 1.0) <= 1e-6
+            if k == 1:
+                assert gate[t, 0] == 1.0
+            if k == E:
+                assert np.allclose(gate[t], full[t, idx[t]], rtol=1e-6, atol=0)
+
+
+def pin_group():
+    """Grouping = numpy's stable argsort of the flat expert ids; offsets and inverse consistent."""
+    rng = np.random.default_rng(13)
+    for (T, k, E) in ((1, 8, 256), (37, 2, 16), (512, 8, 256), (64, 4, 5)):
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        cnt, off, perm, inv = oracle.group(idx, T, k, E)
+        flat = idx.ravel()
+        assert np.array_equal(cnt, np.bincount(flat, minlength=E))
+        assert off[0] == 0 and off[E] == T * k and np.all(np.diff(off) == cnt)
+        assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+        assert np.array_equal(inv[perm], np.arange(T * k))
+        assert np.array_equal(np.sort(perm), np.arange(T * k))
+
+
+def pin_one_expert_dense():
+    """E = 1, k = 1: the layer is the dense SwiGLU MLP of the dequantised weights."""
+    rng = np.random.default_rng(17)
+    for fmt, (H, I) in ((oracle.FMT_ASYM_G64, (128, 64)), (oracle.FMT_SYM_G128, (256, 128))):
+        T = 3
+        mats = rand_layer(rng, 1, H, I, fmt)
+        x = rand_bf16(rng, (T, H))
+        idx = np.zeros((T, 1), dtype=np.int32)
+        gate = np.ones((T, 1), dtype=np.float32)
+        y = oracle.experts(fmt, 1, H, I, *layer_args(mats), x, idx, gate, T, 1)
+        for t in range(T):
+            ref = np_expert_out(fmt, mats, 0, bf16_to_f64(x[t]), H, I)
+            assert rel_l2(y[t], ref) < 1e-6
+            assert np.allclose(y[t], ref, rtol=1e-6, atol=1e-6)
+
+
+def pin_experts_bruteforce():
+    """Several experts, top-k routing, gate-weighted sum: float64 numpy per token."""
+    rng = np.random.default_rng(19)
+    for fmt, (E, H, I, k, T) in ((oracle.FMT_ASYM_G64, (6, 128, 64, 3, 5)),
+                                 (oracle.FMT_SYM_G128, (5, 256, 128, 2, 4))):
+        mats = rand_layer(rng, E, H, I, fmt)
+        x = rand_bf16(rng, (T, H))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        gate = rng.random((T, k)).astype(np.float32)
+        y = oracle.experts(fmt, E, H, I, *layer_args(mats), x, idx, gate, T, k)
+        for t in range(T):
+            ref = sum(float(gate[t, i]) * np_expert_out(fmt, mats, idx[t, i], bf16_to_f64(x[t]), H, I)
+                      for i in range(k))
+            assert rel_l2(y[t], ref) < 1e-6
+        sub = [4, 1] if T > 4 else [1]
+        ys = oracle.experts(fmt, E, H, I, *layer_args(mats), x, idx, gate, T, k, tokens=sub)
+        assert np.array_equal(ys, y[sub])
+
+
+def pin_gate_linearity():
+    """Two byte-identical experts selected together give the single expert's output."""
+    rng = np.random.default_rng(23)
+    fmt, H, I, T = oracle.FMT_ASYM_G64, 128, 64, 4
+    one = rand_layer(rng, 1, H, I, fmt)
+    two = {n: np.concatenate([a, a]) for n, a in one.items()}
+    x = rand_bf16(rng, (T, H))
+    lg = torch_bf16_bits(np.tile(np.float32([[0.25, -0.75]]), (T, 1)))
+    idx2, gate2 = oracle.topk(lg, T, 2, 2)
+    assert np.all(np.sort(idx2, axis=1) == [0, 1])
+    y2 = oracle.experts(fmt, 2, H, I, *layer_args(two), x, idx2, gate2, T, 2)
+    y1 = oracle.experts(fmt, 1, H, I, *layer_args(one), x, np.zeros((T, 1), np.int32),
+                        np.ones((T, 1), np.float32), T, 1)
+    assert rel_l2(y2, y1) < 1e-6
+
+
+def pin_layer_chain():
+    """Router + top-k + experts composed through moe_layer agree with the pieces."""
+    rng = np.random.default_rng(29)
+    fmt, E, H, I, k, T = oracle.FMT_ASYM_G64, 8, 128, 64, 2, 6
+    mats = rand_layer(rng, E, H, I, fmt)
+    x = rand_bf16(rng, (T, H))
+    wr = rand_bf16(rng, (E, H), 0.05)
+    lg = oracle.router(x, wr, T, H, E)
+    idx, gate = oracle.topk(lg, T, E, k)
+    y = oracle.experts(fmt, E, H, I, *layer_args(mats), x, idx, gate, T, k)
+    v = bf16_to_f64(lg).reshape(T, E)
+    for t in range(T):
+        sel = np.lexsort((np.arange(E), -v[t]))[:k]
+        w = scipy.special.softmax(v[t, sel])
+        ref = sum(w[i] * np_expert_out(fmt, mats, sel[i], bf16_to_f64(x[t]), H, I) for i in range(k))
+        assert rel_l2(y[t], ref) < 1e-6
+
+
+def pin_residual():
+    """x' = bf16(float32(x) + y) matches torch's float32 add and bf16 rounding."""
+    rng = np.random.default_rng(31)
+    x = rand_bf16(rng, (4, 300))
+    y = (rng.standard_normal((4, 300)) * 0.3).astype(np.float32)
+    got = oracle.residual(x, y)
+    xt = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).float()
+    ref = (xt + torch.from_numpy(y)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+ALL_PINS = [pin_f16_decode_all, pin_bf16_decode_all, pin_bf16_round, pin_dequant_golden,
+            pin_dequant_random, pin_router, pin_topk_bruteforce, pin_topk_adversarial,
+            pin_gates, pin_group, pin_one_expert_dense, pin_experts_bruteforce,
+            pin_gate_linearity, pin_layer_chain, pin_residual]

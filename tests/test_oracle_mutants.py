@@ -1,0 +1,62 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies ``oracle/moe_oracle.c`` with one plausible mistake (a dropped
+term, a wrong sign, index or offset, a transposed operand, a broken tie rule),
+builds it into a temporary directory with the same gcc line, binds the
+``oracle`` module to it and requires at least one pin of ``oracle_pins`` to
+fail.  CPU only; the real oracle is restored afterwards.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")
+
+# (name, original text, planted text)
+MUTANTS = [
+    ("nibble_order_swapped", "(row[k / 2] >> (4 * (k & 1)))", "(row[k / 2] >> (4 * (1 - (k & 1))))"),
+    ("sym_offset_7", "(double)(code - 8)", "(double)(code - 7)"),
+    ("asym_min_sign", "+ oracle_f16_value(sm[2 * gi + 1])", "- oracle_f16_value(sm[2 * gi + 1])"),
+    ("asym_scale_min_swapped", "(double)code * oracle_f16_value(sm[2 * gi]) + oracle_f16_value(sm[2 * gi + 1])",
+     "(double)code * oracle_f16_value(sm[2 * gi + 1]) + oracle_f16_value(sm[2 * gi])"),
+    ("f16_subnormal_exponent", "ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    ("f16_bias", "ldexp((double)(f | 0x400), e - 25)", "ldexp((double)(f | 0x400), e - 24)"),
+    ("bf16_ties_away", "(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
+    ("router_transposed", "oracle_bf16_value(wr[(size_t)e * H + h])", "oracle_bf16_value(wr[(size_t)h * E + e])"),
+    ("router_bias_dropped", "acc += (double)bias[e];", "acc += 0.0;"),
+    ("topk_ties_to_higher", "if (best < 0 || v > bv)", "if (best < 0 || v >= bv)"),
+    ("gates_not_normalised", "- l0) / den);", "- l0));"),
+    ("gates_no_shift_to_first", "exp(logit_value(l[idx[t * k + i]]) - l0) / den", "exp(logit_value(l[idx[t * k + i]])) / den"),
+    ("group_unstable", "for (int64_t p = 0; p < P; p++) {\n        int e = idx[p];",
+     "for (int64_t p = P - 1; p >= 0; p--) {\n        int e = idx[p];"),
+    ("silu_sign", "return a / (1.0 + exp(-a));", "return a / (1.0 + exp(a));"),
+    ("gate_up_swapped", "h[n] = silu(a) * b;", "h[n] = silu(b) * a;"),
+    ("down_transposed", "acc += wd[(size_t)d * I + n] * h[n];", "acc += wd[(size_t)n * H + d] * h[n];"),
+    ("combine_ignores_gate", "acc += (double)gate[t * k + i] * o[", "acc += 1.0 * o["),
+    ("combine_one_slot", "for (int i = 0; i < k; i++)\n                acc += (double)gate",
+     "for (int i = 0; i < 1; i++)\n                acc += (double)gate"),
+    ("residual_truncates", "out[i] = oracle_bf16_round(s);", "out[i] = (uint16_t)(oracle_bf16_round(s) & 0xfffe);"),
+]
+
+
+@pytest.mark.parametrize("name,orig,planted", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, orc, name, orig, planted):
+    text = open(SRC).read()
+    assert text.count(orig) == 1, f"mutation site for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(orig, planted))
+    lib = oracle.compile_source(str(src), str(tmp_path / "libmutant.so"))
+    prev = oracle.use_library(lib)
+    caught = []
+    try:
+        for pin in pins.ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(pin.__name__)
+    finally:
+        oracle._lib = prev
+    assert caught, f"no pin catches the planted mistake {name}"
