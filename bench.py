@@ -1,0 +1,276 @@
+"""Benchmark of the routed int4 MoE expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
+256 routed experts, top-8, SwiGLU inter 512, int4 experts):
+  decode        (default) one decode step of one MoE layer for 1 token:
+                router GEMV + top-k, grouping, gate/up GEMV + SwiGLU, down
+                GEMV, combine; asym g64 clip-searched weights.  Steps rotate
+                over 40 address-distinct copies of the layer, as successive
+                layers of a 40-layer model would, so experts are read from HBM
+                and not from the 256 MB last-level cache.
+  frame         40 sequential layers x 16 tokens (own RTN g64 weights and
+                router per layer), residual bf16(x + y) between layers.
+  prefill       512 tokens, Zipf(1.1)-popular experts (logits given), asym g64.
+  long_prefill  4096 tokens, N(0,1) logits given, sym g128.
+  tiny          4 tokens, 16 experts, top-2 (correctness size).
+
+One JSON line on stdout: value = tokens/s of whole steps (inputs resident in
+HBM), roofline of the dominant kernel measured with HIP events recorded on the
+launch stream at its stage boundaries, and the CPU oracle timed on a bounded
+sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/f16 matrix
+METRIC = "MoE layer tokens/s; decode HBM GB/s, prefill MFMA TFLOPs (% of peak)"
+
+WORKLOADS = {
+    "tiny": 1, "decode": 2, "prefill": 3, "frame": 4, "long_prefill": 5,
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    p.add_argument("--copies", type=int, default=40, help="address-distinct weight copies (decode)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def clone_layer(lay):
+    import synth
+    return synth.Layer(fmt=lay.fmt, num_experts=lay.num_experts, hidden=lay.hidden, inter=lay.inter,
+                       gate_q=lay.gate_q.clone(), up_q=lay.up_q.clone(), down_q=lay.down_q.clone(),
+                       gate_sm=lay.gate_sm.clone(), up_sm=lay.up_sm.clone(), down_sm=lay.down_sm.clone())
+
+
+def expert_bytes(lay) -> int:
+    return lay.nbytes() // lay.num_experts
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import quantized_moe_expert_amd as m
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    m.lib()
+    dev = torch.device("cuda")
+    cfg = WORKLOADS[args.workload]
+    defaults = {"tiny": (200, 20), "decode": (400, 40), "prefill": (50, 5), "frame": (10, 2),
+                "long_prefill": (20, 3)}
+    K = args.steps if args.steps is not None else defaults[args.workload][0]
+    W = args.warmup if args.warmup is not None else defaults[args.workload][1]
+
+    t0 = time.time()
+    case = synth.make_case(cfg, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] generated {args.workload} inputs in {time.time() - t0:.1f}s")
+    T, H, E, k, I = case.T, case.H, case.E, case.k, case.I
+    decode_path = args.workload in ("tiny", "decode", "frame")
+    mode = "decode" if decode_path else "prefill"
+
+    # ---- per-step units of work ------------------------------------------------
+    if args.workload == "decode":
+        copies = max(1, args.copies)
+        base = case.layers[0]
+        layers = [base] + [clone_layer(base) for _ in range(copies - 1)]
+        routers = [case.router_w] + [case.router_w.clone() for _ in range(copies - 1)]
+        nl_per_step = 1
+    elif args.workload == "frame":
+        layers = case.layers
+        routers = case.router_ws
+        nl_per_step = len(layers)
+    else:
+        layers = case.layers
+        routers = case.router_ws or [None]
+        nl_per_step = 1
+    torch.cuda.synchronize()
+    structs = [m.layer_struct(l) for l in layers]
+    kind = m.WS_DECODE if decode_path else m.WS_PREFILL
+    ws = torch.empty(max(m.workspace_size(kind, T, E, k, H, I), 256), dtype=torch.uint8, device=dev)
+    lg = torch.empty((T, E), dtype=torch.int16, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    xbuf = [torch.empty_like(case.x), torch.empty_like(case.x)]
+    experts_fn = m.moe_q4_decode if decode_path else m.moe_q4_prefill
+    timed_fn = m.moe_q4_decode_timed if decode_path else m.moe_q4_prefill_timed
+
+    state = {"i": 0}
+
+    def step(events=None):
+        """One step: every layer of the workload once."""
+        xin = case.x
+        for j in range(nl_per_step):
+            li = (state["i"] % len(layers)) if args.workload == "decode" else j
+            rw = routers[li] if routers[0] is not None else None
+            if rw is not None:
+                m.moe_q4_route(xin, rw, None, lg, T, H, E, k, idx, gate)
+            else:  # given logits (prefill workloads): top-k only, logits read in place
+                m.moe_q4_route(None, None, None, case.logits, T, H, E, k, idx, gate)
+            if events is not None and j == nl_per_step - 1:
+                timed_fn(xin, idx, gate, T, k, structs[li], y, ws, [e.cuda_event for e in events])
+            else:
+                experts_fn(xin, idx, gate, T, k, structs[li], y, ws)
+            if args.workload == "frame":
+                xout = xbuf[j & 1]
+                m.moe_q4_residual_bf16(xin, y, T * H, xout)
+                xin = xout
+        state["i"] += 1
+
+    # ---- warmup + timed steps ------------------------------------------------
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(K):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / K
+    tokens_per_step = T
+    value = tokens_per_step * K / (total_ms / 1e3)
+    log(f"[bench] {args.workload}: {ms_per_step * 1e3:.2f} us/step, {value:.1f} tokens/s")
+
+    # ---- stage timing of the dominant kernel (same steps, events on the stream)
+    nev = m.STAGE_EVENTS
+    stage_ms = []
+    prof_steps = min(K, 50)
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(prof_steps)]
+    for evs in ev_sets:  # materialise the event handles
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+    for evs in ev_sets:
+        step(events=evs)
+    torch.cuda.synchronize()
+    for evs in ev_sets:
+        stage_ms.append([evs[i].elapsed_time(evs[i + 1]) for i in range(nev - 1)])
+    stage_ms = np.array(stage_ms)
+    stage_avg = stage_ms.mean(axis=0)
+    log(f"[bench] stage times (us): {', '.join(f'{v * 1e3:.2f}' for v in stage_avg)}")
+
+    # work actually routed in the profiled layer (outside timed regions)
+    act = torch.unique(idx).numel()
+    lay0 = layers[0]
+    proj_bytes = expert_bytes(lay0) // 3        # one projection of one expert (codes + scales)
+    P = T * k
+    if decode_path:
+        # dominant kernel: gate/up GEMV + SwiGLU (stage 1): reads 2 projections of each
+        # active expert, the activations, writes h (fp32)
+        dom = "decode_gateup_kernel"
+        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 4
+        achieved = alg_bytes / (stage_avg[1] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "avg_us": round(float(stage_avg[1]) * 1e3, 3), "algorithmic_bytes": int(alg_bytes),
+                "active_experts": int(act)}
+    else:
+        dom = "grouped_gemm_kernel<FMT,1> (gate/up GEMM + SwiGLU)"
+        flops = 2.0 * P * H * (2 * I)
+        achieved = flops / (stage_avg[2] * 1e-3) / 1e12
+        wbytes = act * 2 * proj_bytes
+        if args.workload == "prefill":
+            # weight-bandwidth-bound case: report against HBM
+            gbs = (wbytes + T * H * 2 + P * I * 2) / (stage_avg[2] * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                    "avg_us": round(float(stage_avg[2]) * 1e3, 3), "tflops": round(achieved, 2),
+                    "active_experts": int(act)}
+        else:
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": dom, "avg_us": round(float(stage_avg[2]) * 1e3, 3),
+                    "algorithmic_flops": flops, "active_experts": int(act)}
+    roof["stages_us"] = [round(float(v) * 1e3, 3) for v in stage_avg]
+
+    # ---- CPU oracle on a bounded sample ------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args, decode_path, args.cpu_seconds)
+
+    names = {"tiny": "tiny layer: 4 tokens, H=256, 16 experts, top-2, I=128, int4 asym g64",
+             "decode": "decode step, 1 MoE layer: 1 token, H=2048, 256 experts, top-8, I=512, int4 asym g64 "
+                       "(clip search); 40 address-distinct layer copies rotated",
+             "prefill": "prefill, 1 MoE layer: 512 tokens, Zipf(1.1) expert popularity, H=2048, 256 experts, "
+                        "top-8, I=512, int4 asym g64",
+             "frame": "full-depth decode frame: 40 MoE layers x 16 tokens, H=2048, 256 experts, top-8, I=512, "
+                      "int4 asym g64 (RTN), residual chain",
+             "long_prefill": "long prefill, 1 MoE layer: 4096 tokens, N(0,1) logits, H=2048, 256 experts, top-8, "
+                             "I=512, int4 sym g128"}
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+           "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": names[args.workload], "tokens": T, "hidden": H, "experts": E, "top_k": k,
+                      "inter": I, "layers_per_step": nl_per_step, "path": mode,
+                      "format": "asym_g64" if case.fmt == synth.FMT_ASYM_G64 else "sym_g128"},
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(case, args, decode_path, budget_s):
+    """The oracle as it stands, on host cores, over a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    T, H, E, k = case.T, case.H, case.E, case.k
+    lay = case.layers[0]
+    host_layer = oracle.layer_np(lay)
+    x_np = case.x.cpu().numpy().view(np.uint16)
+    rw = case.router_ws[0].cpu().numpy().view(np.uint16) if case.router_ws else None
+    lg_all = case.logits.cpu().numpy().view(np.uint16) if case.logits is not None else None
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # sample: tokens of the first layer, a few at a time, until the budget is spent
+    per = 1 if T == 1 else min(T, 16)
+    done_tokens, t_total, reps = 0, 0.0, 0
+    rng_tokens = np.arange(T)
+    while t_total < budget_s and reps < 10000:
+        sel = rng_tokens[(reps * per) % T:(reps * per) % T + per]
+        t1 = time.perf_counter()
+        xs = np.ascontiguousarray(x_np[sel])
+        lg = oracle.router(xs, rw, len(sel), H, E) if rw is not None else np.ascontiguousarray(lg_all[sel])
+        idx, gate = oracle.topk(lg, len(sel), E, k)
+        oracle.experts(lay.fmt, E, H, lay.inter, *host_layer, xs, idx, gate, len(sel), k)
+        t_total += time.perf_counter() - t1
+        done_tokens += len(sel)
+        reps += 1
+    value = done_tokens / t_total
+    return {"value": round(value, 3), "unit": "tokens/s (one layer)", "cores": threads, "kind": "oracle",
+            "sample": f"{done_tokens} tokens of layer 0 in {reps} calls of {per} token(s), "
+                      f"{t_total:.1f} s (route + experts + combine, fp64)"}
+
+
+if __name__ == "__main__":
+    main()

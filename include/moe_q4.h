@@ -1,0 +1,211 @@
+/*
+ * moe_q4.h -- C ABI of libmoe_q4.so: the routed int4 MoE expert layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (web pages on the Fish Audio Drama 3 4-bit builds):
+ *   - 256 routed experts per layer hold most of the model's parameters and set
+ *     its speed (drama-rs page, "Experts: where they run");
+ *   - each expert has gate, up and down projections (NVFP4 routed experts card,
+ *     "Quantization");
+ *   - expert weights are int4, asymmetric, group 64 along the input dimension,
+ *     with an f16 scale and an f16 min per group (drama-q4 card, "What's
+ *     quantized"), an affine map w = scale * q + min (drama-rs page,
+ *     "Apple Silicon (MLX)"), or int4 symmetric with one f16 scale per 128
+ *     input weights (drama-3-w4a16 card, "At a glance", "How it was made");
+ *   - the router is bf16 (drama-q4 card, "What's quantized");
+ *   - rows are grouped by routed expert before the expert products (drama-rs
+ *     page, "Apple Silicon (MLX)" and "Layout": grouped MoE prefill).
+ * The pages leave the routing function, the activation and the combine open;
+ * this library computes: bf16 logits, the k largest (ties to the lower expert
+ * index), gates = softmax over the k selected logits, SwiGLU experts
+ * h = silu(Wg x) * (Wu x), o = Wd h, and y[t] = sum_i gate[t][i] * o(t, i).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library keeps none of them after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Nothing is synchronised, no device memory is allocated and no
+ *     value is read back to the host.  Inputs must stay valid, and the
+ *     workspace untouched, until the stream has passed the call.  Calls that
+ *     share a workspace must be ordered on one stream.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     negative status is returned and nothing is enqueued on failure.  A
+ *     launch failure reported by the HIP runtime returns MOE_Q4_ERR_HIP.
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - T = 0 returns MOE_Q4_OK without launching anything.
+ *   - bf16 and f16 tensors are passed as raw 16-bit patterns.
+ *   - Expert indices read from device memory are clamped into [0, E) by every
+ *     kernel, so malformed indices give undefined numbers but stay in bounds.
+ *
+ * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 32), T * k < 2^31;
+ * hidden H and inter I are powers of two in [64, 2048] and multiples of the
+ * group (64 asym, 128 sym); moe_q4_prefill additionally needs I % 128 == 0
+ * and H % 256 == 0.  Other shapes return MOE_Q4_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_Q4_H
+#define MOE_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_Q4_API __attribute__((visibility("default")))
+#else
+#define MOE_Q4_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+struct ihipStream_t;
+typedef struct ihipStream_t *moe_q4_stream;
+
+typedef enum {
+    MOE_Q4_ASYM_G64 = 0,   /* w = scale * q + min, q in 0..15, group 64 along K  */
+    MOE_Q4_SYM_G128 = 1    /* w = scale * (q - 8), q in 0..15, group 128 along K */
+} moe_q4_format;
+
+typedef enum {
+    MOE_Q4_OK = 0,
+    MOE_Q4_ERR_INVALID_ARG = -1,   /* NULL pointer, negative size, k > E, ...   */
+    MOE_Q4_ERR_UNSUPPORTED = -2,   /* valid but outside the supported shapes  */
+    MOE_Q4_ERR_WORKSPACE = -3,     /* ws NULL or smaller than moe_q4_workspace_size */
+    MOE_Q4_ERR_HIP = -4            /* the HIP runtime refused a launch          */
+} moe_q4_status;
+
+typedef enum {
+    MOE_Q4_WS_ROUTE = 0,
+    MOE_Q4_WS_DECODE = 1,
+    MOE_Q4_WS_PREFILL = 2,
+    MOE_Q4_WS_GROUP = 3
+} moe_q4_ws_kind;
+
+/*
+ * One MoE layer's routed experts, canonical layout (all device pointers):
+ *   gate_q, up_q   uint8 [E][I][H/2]   packed codes, row n = output n, input k
+ *                                      at byte k/2, low nibble for even k
+ *   down_q         uint8 [E][H][I/2]   same packing, row d = output d
+ *   *_sm           f16 bit patterns:
+ *                    asym g64:  [E][N][K/64][2] = {scale, min}
+ *                    sym g128:  [E][N][K/128]   = scale
+ *                  (N, K) = (I, H) for gate and up, (H, I) for down.
+ */
+typedef struct moe_q4_layer {
+    int32_t num_experts;   /* E */
+    int32_t hidden;        /* H */
+    int32_t inter;         /* I */
+    int32_t format;        /* moe_q4_format */
+    const uint8_t *gate_q, *up_q, *down_q;
+    const uint16_t *gate_sm, *up_sm, *down_sm;
+} moe_q4_layer;
+
+/* Bytes of workspace the call of kind `which` needs for these sizes (0 if
+ * none).  The value covers both weight formats. */
+MOE_Q4_API size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t H, int32_t I);
+
+/*
+ * Router and top-k.
+ *   x         bf16 [T][H] or NULL.  When x != NULL the logits
+ *             logits[t][e] = bf16(float(sum_h x[t][h] * Wr[e][h] + bias[e]))
+ *             are computed with a double-precision sum and WRITTEN to
+ *             `logits`; when x == NULL, `logits` is READ as given.
+ *   router_w  bf16 [E][H] (required when x != NULL)
+ *   bias      float [E] or NULL (added before rounding; the pages describe no
+ *             router bias, it exists to shape synthetic expert popularity)
+ *   logits    bf16 [T][E], output or input as above
+ *   topk_idx  int32 [T][k] out: the k largest logits, descending, equal
+ *             logits ordered by lower expert index
+ *   topk_gate float [T][k] out: exp(l_i - l_0) / sum_j exp(l_j - l_0) over
+ *             the selected, computed in double and rounded once
+ *   ws        unused (may be NULL)
+ */
+MOE_Q4_API int moe_q4_route(const void *x, const void *router_w, const float *bias, void *logits,
+                 int64_t T, int32_t H, int32_t E, int32_t k,
+                 int32_t *topk_idx, float *topk_gate,
+                 void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/*
+ * Grouping of the T*k (token, slot) pairs by routed expert (a stable
+ * counting sort; drama-rs page "Apple Silicon (MLX)": prefill groups rows by
+ * routed expert).  Outputs (int32, device):
+ *   cnt[E]       pairs routed to each expert
+ *   off[E+1]     exclusive prefix sum of cnt, off[E] = T*k
+ *   perm[T*k]    pair index t*k+i at sorted position r, pairs of one expert in
+ *                (t, i) order
+ *   inv[T*k]     sorted position of pair t*k+i
+ * ws: at least moe_q4_workspace_size(MOE_Q4_WS_GROUP, ...) bytes.
+ */
+MOE_Q4_API int moe_q4_group(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E,
+                 int32_t *cnt, int32_t *off, int32_t *perm, int32_t *inv,
+                 void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/*
+ * Expert layer for few tokens (tuned for T <= 64): grouping, then for each
+ * active expert a fused-dequant GEMV over its packed nibbles (gate and up
+ * with SwiGLU, then down) in fp32, then the gate-weighted combine in slot
+ * order (deterministic).
+ *   x          bf16 [T][H]
+ *   topk_idx   int32 [T][k], topk_gate float [T][k] (as from moe_q4_route)
+ *   w          the layer (host struct holding device pointers)
+ *   y          float [T][H] out
+ *   ws         >= moe_q4_workspace_size(MOE_Q4_WS_DECODE, T, E, k, H, I) bytes
+ */
+MOE_Q4_API int moe_q4_decode(const void *x, const int32_t *topk_idx, const float *topk_gate,
+                  int64_t T, int32_t k, const moe_q4_layer *w, float *y,
+                  void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/*
+ * Expert layer for many tokens (tuned for T >= 64): grouping, then grouped
+ * GEMMs on the bf16/f16 matrix cores.  The int4 codes enter the products as
+ * exact small integers and the per-group scale (and min) are applied to fp32
+ * accumulators; h between the two products is rounded to f16, so |h| must
+ * stay below 65504.  y (float [T][H]) is accumulated with float atomics: the
+ * result can differ between runs in the last bits.  Same arguments as
+ * moe_q4_decode; ws >= moe_q4_workspace_size(MOE_Q4_WS_PREFILL, ...).
+ */
+MOE_Q4_API int moe_q4_prefill(const void *x, const int32_t *topk_idx, const float *topk_gate,
+                   int64_t T, int32_t k, const moe_q4_layer *w, float *y,
+                   void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/*
+ * Same as moe_q4_decode / moe_q4_prefill, and additionally records the
+ * caller's HIP events (hipEvent_t handles, created by the caller) on `stream`
+ * at the stage boundaries, so that each stage's kernel time can be read with
+ * hipEventElapsedTime:
+ *   decode:  [0] grouping [1] gate/up GEMV + SwiGLU [2] down GEMV [3] combine [4]
+ *   prefill: [0] grouping [1] row sums + output clear [2] gate/up GEMM + SwiGLU
+ *            [3] down GEMM + combine [4]
+ * events must point to MOE_Q4_STAGE_EVENTS valid events.
+ */
+#define MOE_Q4_STAGE_EVENTS 5
+MOE_Q4_API int moe_q4_decode_timed(const void *x, const int32_t *topk_idx, const float *topk_gate,
+                        int64_t T, int32_t k, const moe_q4_layer *w, float *y,
+                        void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
+MOE_Q4_API int moe_q4_prefill_timed(const void *x, const int32_t *topk_idx, const float *topk_gate,
+                         int64_t T, int32_t k, const moe_q4_layer *w, float *y,
+                         void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
+
+/*
+ * Test hook: dequantise projection `proj` (0 gate [I][H], 1 up [I][H],
+ * 2 down [H][I]) of `expert` to float [N][K] through the kernels' own nibble
+ * unpacking and scale indexing: out = float(scale * q + min) (asym) or
+ * float(scale * (q - 8)) (sym), one rounding.
+ */
+MOE_Q4_API int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *out,
+                   moe_q4_stream stream);
+
+/* Residual step of a chain of layers: out[i] = bf16(float(x[i]) + y[i]) with
+ * one float addition and round-to-nearest-even (x, out: bf16 bits). */
+MOE_Q4_API int moe_q4_residual_bf16(const void *x, const float *y, int64_t n, void *out,
+                         moe_q4_stream stream);
+
+/* Static description of a status code. */
+MOE_Q4_API const char *moe_q4_error_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_Q4_H */

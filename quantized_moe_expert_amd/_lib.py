@@ -1,0 +1,179 @@
+"""ctypes binding of libmoe_q4.so with the C ABI's names.
+
+Argument marshalling only: tensors are passed as device pointers
+(``tensor.data_ptr()``) and the stream as torch's current HIP stream.  Every
+step of the layer runs in the library's HIP kernels; there is no fallback, and
+loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
+
+ASYM_G64 = 0
+SYM_G128 = 1
+WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+
+# every entry point declared in include/moe_q4.h
+EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_decode", "moe_q4_prefill",
+           "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_dequant", "moe_q4_residual_bf16",
+           "moe_q4_error_string")
+STAGE_EVENTS = 5
+
+
+class MoeQ4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({error_string(status)})")
+        self.status = status
+
+
+class Layer(ctypes.Structure):
+    """struct moe_q4_layer"""
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("format", ctypes.c_int32),
+                ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
+                ("gate_sm", ctypes.c_void_p), ("up_sm", ctypes.c_void_p), ("down_sm", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_moe_expert_amd.build` "
+                              "(or __graft_entry__.build())")
+        import torch  # noqa: F401  (load torch's HIP runtime first: one runtime per process)
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.moe_q4_workspace_size.restype = sz
+        L.moe_q4_workspace_size.argtypes = [ctypes.c_int, i64, i32, i32, i32, i32]
+        L.moe_q4_route.restype = ctypes.c_int
+        L.moe_q4_route.argtypes = [P, P, P, P, i64, i32, i32, i32, P, P, P, sz, P]
+        L.moe_q4_group.restype = ctypes.c_int
+        L.moe_q4_group.argtypes = [P, i64, i32, i32, P, P, P, P, P, sz, P]
+        for name in ("moe_q4_decode", "moe_q4_prefill"):
+            fn = getattr(L, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, sz, P]
+        for name in ("moe_q4_decode_timed", "moe_q4_prefill_timed"):
+            fn = getattr(L, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, sz, P, ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_q4_dequant.restype = ctypes.c_int
+        L.moe_q4_dequant.argtypes = [ctypes.POINTER(Layer), i32, i32, P, P]
+        L.moe_q4_residual_bf16.restype = ctypes.c_int
+        L.moe_q4_residual_bf16.argtypes = [P, P, i64, P, P]
+        L.moe_q4_error_string.restype = ctypes.c_char_p
+        L.moe_q4_error_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def error_string(status: int) -> str:
+    return lib().moe_q4_error_string(int(status)).decode()
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL).  Plain ints pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("moe_q4 takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("moe_q4 takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise MoeQ4Error(fn, status)
+
+
+def layer_struct(layer) -> Layer:
+    """struct moe_q4_layer from an object with num_experts, hidden, inter, fmt
+    (or format) and the six gate/up/down code and scale tensors."""
+    fmt = getattr(layer, "fmt", None)
+    if fmt is None:
+        fmt = layer.format
+    return Layer(int(layer.num_experts), int(layer.hidden), int(layer.inter), int(fmt),
+                 _ptr(layer.gate_q), _ptr(layer.up_q), _ptr(layer.down_q),
+                 _ptr(layer.gate_sm), _ptr(layer.up_sm), _ptr(layer.down_sm))
+
+
+def workspace_size(kind: int, T: int, E: int, k: int, H: int, I: int) -> int:
+    return int(lib().moe_q4_workspace_size(int(kind), int(T), int(E), int(k), int(H), int(I)))
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def moe_q4_route(x, router_w, bias, logits, T, H, E, k, topk_idx, topk_gate, ws=None, stream=None):
+    w, nb = _ws(ws)
+    _check("moe_q4_route", lib().moe_q4_route(_ptr(x), _ptr(router_w), _ptr(bias), _ptr(logits), T, H, E, k,
+                                               _ptr(topk_idx), _ptr(topk_gate), w, nb, _stream(stream)))
+
+
+def moe_q4_group(topk_idx, T, k, E, cnt, off, perm, inv, ws, stream=None):
+    w, nb = _ws(ws)
+    _check("moe_q4_group", lib().moe_q4_group(_ptr(topk_idx), T, k, E, _ptr(cnt), _ptr(off), _ptr(perm),
+                                               _ptr(inv), w, nb, _stream(stream)))
+
+
+def moe_q4_decode(x, topk_idx, topk_gate, T, k, layer, y, ws, stream=None):
+    w, nb = _ws(ws)
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    _check("moe_q4_decode", lib().moe_q4_decode(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, k,
+                                                 ctypes.byref(st), _ptr(y), w, nb, _stream(stream)))
+
+
+def moe_q4_prefill(x, topk_idx, topk_gate, T, k, layer, y, ws, stream=None):
+    w, nb = _ws(ws)
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    _check("moe_q4_prefill", lib().moe_q4_prefill(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, k,
+                                                   ctypes.byref(st), _ptr(y), w, nb, _stream(stream)))
+
+
+def _timed(name, x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream):
+    w, nb = _ws(ws)
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    ev = (ctypes.c_void_p * STAGE_EVENTS)(*[int(e) for e in events])
+    _check(name, getattr(lib(), name)(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, k, ctypes.byref(st), _ptr(y),
+                                      w, nb, _stream(stream), ev))
+
+
+def moe_q4_decode_timed(x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream=None):
+    """moe_q4_decode that records the 5 given hipEvent_t handles at its stage boundaries."""
+    _timed("moe_q4_decode_timed", x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream)
+
+
+def moe_q4_prefill_timed(x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream=None):
+    _timed("moe_q4_prefill_timed", x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream)
+
+
+def moe_q4_dequant(layer, expert, proj, out, stream=None):
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    _check("moe_q4_dequant", lib().moe_q4_dequant(ctypes.byref(st), expert, proj, _ptr(out), _stream(stream)))
+
+
+def moe_q4_residual_bf16(x, y, n, out, stream=None):
+    _check("moe_q4_residual_bf16", lib().moe_q4_residual_bf16(_ptr(x), _ptr(y), n, _ptr(out), _stream(stream)))

@@ -1,0 +1,247 @@
+// C ABI of libmoe_q4: argument checks, workspace layout and launch order.
+#include "../../include/moe_q4.h"
+#include "moe_internal.h"
+
+using namespace moeq4;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+inline size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Workspace carving: regions are appended in a fixed order, each 256-byte
+// aligned.  With base == nullptr only the size is computed.
+struct Carver {
+    char *base;
+    size_t used = 0;
+    template <typename T>
+    T *take(size_t count) {
+        T *p = base ? reinterpret_cast<T *>(base + used) : nullptr;
+        used += align_up(count * sizeof(T));
+        return p;
+    }
+};
+
+bool pow2_between(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+int check_route_shape(int64_t T, int H, int E, int k) {
+    if (T < 0 || E < 1 || k < 1 || k > E) return MOE_Q4_ERR_INVALID_ARG;
+    if (E > 1024 || k > 32 || T * (int64_t)k >= (int64_t)1 << 31) return MOE_Q4_ERR_UNSUPPORTED;
+    if (H < 0) return MOE_Q4_ERR_INVALID_ARG;
+    return MOE_Q4_OK;
+}
+
+int check_layer(const moe_q4_layer *w, bool prefill) {
+    if (!w || !w->gate_q || !w->up_q || !w->down_q || !w->gate_sm || !w->up_sm || !w->down_sm)
+        return MOE_Q4_ERR_INVALID_ARG;
+    if (w->num_experts < 1 || w->hidden < 1 || w->inter < 1) return MOE_Q4_ERR_INVALID_ARG;
+    if (w->format != MOE_Q4_ASYM_G64 && w->format != MOE_Q4_SYM_G128) return MOE_Q4_ERR_UNSUPPORTED;
+    const int G = w->format == MOE_Q4_ASYM_G64 ? 64 : 128;
+    if (w->num_experts > 1024) return MOE_Q4_ERR_UNSUPPORTED;
+    if (!pow2_between(w->hidden, 64, 2048) || !pow2_between(w->inter, 64, 2048)) return MOE_Q4_ERR_UNSUPPORTED;
+    if (w->hidden % G || w->inter % G) return MOE_Q4_ERR_UNSUPPORTED;
+    if (prefill && (w->inter % 128 || w->hidden % 256)) return MOE_Q4_ERR_UNSUPPORTED;
+    return MOE_Q4_OK;
+}
+
+LayerPtrs layer_ptrs(const moe_q4_layer *w) {
+    LayerPtrs L;
+    L.E = w->num_experts;
+    L.H = w->hidden;
+    L.I = w->inter;
+    L.fmt = w->format;
+    L.gq = w->gate_q;
+    L.uq = w->up_q;
+    L.dq = w->down_q;
+    L.gsm = w->gate_sm;
+    L.usm = w->up_sm;
+    L.dsm = w->down_sm;
+    return L;
+}
+
+// Grouping regions (shared by group, decode and prefill).
+GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile) {
+    const int64_t P = T * k;
+    const int64_t nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
+    GroupOut g;
+    g.cnt = c.take<int32_t>(E);
+    g.off = c.take<int32_t>(E + 1);
+    g.perm = c.take<int32_t>(P);
+    g.inv = c.take<int32_t>(P);
+    g.tiles = c.take<Tile>(max_tiles(P, E, rows_per_tile));
+    g.ntiles = c.take<int32_t>(1);
+    g.rows_per_tile = rows_per_tile;
+    const bool multi = P > GROUP_SINGLE_MAX;
+    g.chunk_cnt = c.take<int32_t>(multi ? nch * E : 0);
+    g.chunk_base = c.take<int32_t>(multi ? nch * E : 0);
+    return g;
+}
+
+struct DecodeWs {
+    GroupOut g;
+    float *h, *o;
+};
+DecodeWs carve_decode(Carver &c, int64_t T, int E, int k, int H, int I) {
+    DecodeWs d;
+    d.g = carve_group(c, T, E, k, DECODE_TT);
+    d.h = c.take<float>(T * k * (int64_t)I);
+    d.o = c.take<float>(T * k * (int64_t)H);
+    return d;
+}
+
+struct PrefillWs {
+    GroupOut g;
+    float *xsum;
+    uint16_t *h;
+    float *hsum;
+};
+PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
+    PrefillWs p;
+    p.g = carve_group(c, T, E, k, PREFILL_BM);
+    p.xsum = c.take<float>(T * (int64_t)(H / 64));      // sized for the smaller group (64)
+    p.h = c.take<uint16_t>(T * k * (int64_t)I);
+    p.hsum = c.take<float>(T * k * (int64_t)(I / 64));
+    return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
+    if (T <= 0 || E < 1 || k < 1 || H < 1 || I < 1) return 0;
+    Carver c{nullptr};
+    switch (which) {
+        case MOE_Q4_WS_ROUTE: return 0;
+        case MOE_Q4_WS_GROUP: carve_group(c, T, E, k, DECODE_TT); break;
+        case MOE_Q4_WS_DECODE: carve_decode(c, T, E, k, H, I); break;
+        case MOE_Q4_WS_PREFILL: carve_prefill(c, T, E, k, H, I); break;
+        default: return 0;
+    }
+    return c.used;
+}
+
+int moe_q4_route(const void *x, const void *router_w, const float *bias, void *logits, int64_t T, int32_t H,
+                 int32_t E, int32_t k, int32_t *topk_idx, float *topk_gate, void *ws, size_t ws_bytes,
+                 moe_q4_stream stream) {
+    (void)ws;
+    (void)ws_bytes;
+    int st = check_route_shape(T, x ? H : 0, E, k);
+    if (st) return st;
+    if (!logits || !topk_idx || !topk_gate) return MOE_Q4_ERR_INVALID_ARG;
+    if (x && !router_w) return MOE_Q4_ERR_INVALID_ARG;
+    if (x && (H < 8 || H % 8 || H > 2048)) return H < 1 ? MOE_Q4_ERR_INVALID_ARG : MOE_Q4_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_Q4_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (x) {
+        st = hip_status(launch_router_logits(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(router_w),
+                                             bias, T, H, E, static_cast<uint16_t *>(logits), s));
+        if (st) return st;
+    }
+    return hip_status(launch_topk(static_cast<const uint16_t *>(logits), T, E, k, topk_idx, topk_gate, s));
+}
+
+int moe_q4_group(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E, int32_t *cnt, int32_t *off,
+                 int32_t *perm, int32_t *inv, void *ws, size_t ws_bytes, moe_q4_stream stream) {
+    int st = check_route_shape(T, 0, E, k);
+    if (st) return st;
+    if (!topk_idx || !cnt || !off || !perm || !inv) return MOE_Q4_ERR_INVALID_ARG;
+    if (T == 0) return MOE_Q4_OK;
+    const size_t need = moe_q4_workspace_size(MOE_Q4_WS_GROUP, T, E, k, 64, 64);
+    if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
+    Carver c{static_cast<char *>(ws)};
+    GroupOut g = carve_group(c, T, E, k, DECODE_TT);
+    g.cnt = cnt;
+    g.off = off;
+    g.perm = perm;
+    g.inv = inv;
+    return hip_status(launch_group(topk_idx, T, k, E, g, reinterpret_cast<hipStream_t>(stream)));
+}
+
+static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T,
+                       int32_t k, const moe_q4_layer *w, float *y, void *ws, size_t ws_bytes,
+                       moe_q4_stream stream, void *const *events) {
+    int st = check_layer(w, prefill);
+    if (st) return st;
+    st = check_route_shape(T, w->hidden, w->num_experts, k);
+    if (st) return st;
+    if (!x || !topk_idx || !topk_gate || !y) return MOE_Q4_ERR_INVALID_ARG;
+    if (events)
+        for (int i = 0; i < MOE_Q4_STAGE_EVENTS; ++i)
+            if (!events[i]) return MOE_Q4_ERR_INVALID_ARG;
+    if (T == 0) return MOE_Q4_OK;
+    const int E = w->num_experts, H = w->hidden, I = w->inter;
+    const size_t need = moe_q4_workspace_size(prefill ? MOE_Q4_WS_PREFILL : MOE_Q4_WS_DECODE, T, E, k, H, I);
+    if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const LayerPtrs L = layer_ptrs(w);
+    Carver c{static_cast<char *>(ws)};
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MOE_Q4_ERR_HIP;
+    if (!prefill) {
+        DecodeWs d = carve_decode(c, T, E, k, H, I);
+        st = hip_status(launch_group(topk_idx, T, k, E, d.g, s));
+        if (st) return st;
+        return hip_status(launch_decode_experts(xb, topk_gate, T, k, L, d.g, d.h, d.o, y, s, ev ? ev + 1 : nullptr));
+    }
+    PrefillWs p = carve_prefill(c, T, E, k, H, I);
+    st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
+    if (st) return st;
+    return hip_status(
+        launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.xsum, p.h, p.hsum, y, s, ev ? ev + 1 : nullptr));
+}
+
+int moe_q4_decode(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
+                  const moe_q4_layer *w, float *y, void *ws, size_t ws_bytes, moe_q4_stream stream) {
+    return run_experts(false, x, topk_idx, topk_gate, T, k, w, y, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_q4_decode_timed(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
+                        const moe_q4_layer *w, float *y, void *ws, size_t ws_bytes, moe_q4_stream stream,
+                        void *const *events) {
+    if (!events) return MOE_Q4_ERR_INVALID_ARG;
+    return run_experts(false, x, topk_idx, topk_gate, T, k, w, y, ws, ws_bytes, stream, events);
+}
+
+int moe_q4_prefill(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
+                   const moe_q4_layer *w, float *y, void *ws, size_t ws_bytes, moe_q4_stream stream) {
+    return run_experts(true, x, topk_idx, topk_gate, T, k, w, y, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_q4_prefill_timed(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
+                         const moe_q4_layer *w, float *y, void *ws, size_t ws_bytes, moe_q4_stream stream,
+                         void *const *events) {
+    if (!events) return MOE_Q4_ERR_INVALID_ARG;
+    return run_experts(true, x, topk_idx, topk_gate, T, k, w, y, ws, ws_bytes, stream, events);
+}
+
+int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *out, moe_q4_stream stream) {
+    int st = check_layer(w, false);
+    if (st) return st;
+    if (!out || expert < 0 || expert >= w->num_experts || proj < 0 || proj > 2) return MOE_Q4_ERR_INVALID_ARG;
+    return hip_status(launch_dequant(layer_ptrs(w), expert, proj, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_q4_residual_bf16(const void *x, const float *y, int64_t n, void *out, moe_q4_stream stream) {
+    if (n < 0 || (n > 0 && (!x || !y || !out))) return MOE_Q4_ERR_INVALID_ARG;
+    if (n == 0) return MOE_Q4_OK;
+    return hip_status(launch_residual(static_cast<const uint16_t *>(x), y, n, static_cast<uint16_t *>(out),
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char *moe_q4_error_string(int status) {
+    switch (status) {
+        case MOE_Q4_OK: return "ok";
+        case MOE_Q4_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_Q4_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case MOE_Q4_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_Q4_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

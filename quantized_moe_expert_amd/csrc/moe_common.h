@@ -1,0 +1,99 @@
+// Device helpers shared by the HIP kernels of libmoe_q4 (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moeq4 {
+
+constexpr int WAVE = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;    // MFMA bf16 operand
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t; // MFMA f16 operand
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;    // 32x32 accumulator
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// --------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// binary32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Orderable key of a bf16 logit: larger value -> larger key, NaN below -inf.
+__device__ __forceinline__ uint32_t bf16_order(uint32_t b) {
+    b &= 0xffffu;
+    if ((b & 0x7fffu) > 0x7f80u) return 0u;
+    return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
+}
+
+// ---------------------------------------------------------------- nibbles
+//
+// A packed dword holds 8 consecutive codes, code j in bits [4j, 4j+4).
+// unpack_pair(w, j) puts codes j and j+4 into the low 4 mantissa bits of two
+// 16-bit floats whose exponent field comes from `magic`:
+//   bf16 0x4300 = 128 (unit step from 128 to 256)  -> value 128 + q
+//   f16  0x6400 = 1024 (unit step from 1024 to 2048) -> value 1024 + q
+// so each half is exactly OFFSET + q.  Over j = 0..3 the 16-bit lanes carry
+// the codes in the order 0,4,1,5,2,6,3,7 (PERM8); activations are put in the
+// same order so that a dot product pairs each code with its own input.
+
+template <uint32_t MAGIC>
+__device__ __forceinline__ uint32_t unpack_pair(uint32_t w, int j) {
+    return ((w >> (4 * j)) & 0x000f000fu) | MAGIC;
+}
+constexpr uint32_t MAGIC_BF16 = 0x43004300u;   // 128 + q
+constexpr uint32_t MAGIC_F16 = 0x64006400u;    // 1024 + q
+constexpr float OFFSET_BF16 = 128.0f;
+constexpr float OFFSET_F16 = 1024.0f;
+
+// 8 consecutive 16-bit values in 4 dwords (v0 = elements 0,1; v1 = 2,3; ...)
+// reordered to 0,4 | 1,5 | 2,6 | 3,7.
+__device__ __forceinline__ void perm8(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                      uint32_t &o0, uint32_t &o1, uint32_t &o2, uint32_t &o3) {
+    o0 = (v0 & 0xffffu) | (v2 << 16);
+    o1 = (v0 >> 16) | (v2 & 0xffff0000u);
+    o2 = (v1 & 0xffffu) | (v3 << 16);
+    o3 = (v1 >> 16) | (v3 & 0xffff0000u);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Sum of the two bf16 halves of a dword, in float.
+__device__ __forceinline__ float bf16_pair_sum(uint32_t v) {
+    return __uint_as_float(v << 16) + __uint_as_float(v & 0xffff0000u);
+}
+
+// --------------------------------------------------------------- reductions
+
+template <int WIDTH>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+}  // namespace moeq4

@@ -1,0 +1,66 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moeq4 {
+
+// Work item of the expert kernels: `rows` consecutive sorted rows of one
+// expert starting at sorted position `row0`.
+struct Tile {
+    int expert;
+    int row0;
+    int rows;
+    int pad;
+};
+
+// Layer pointers as the kernels take them.
+struct LayerPtrs {
+    int E, H, I, fmt;
+    const uint8_t *gq, *uq, *dq;
+    const uint16_t *gsm, *usm, *dsm;
+};
+
+constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chunk
+constexpr int GROUP_SINGLE_MAX = 1024;   // pairs handled by the one-block grouping
+constexpr int DECODE_TT = 4;             // tokens per decode work item
+constexpr int PREFILL_BM = 128;          // rows per prefill tile
+
+inline int64_t max_tiles(int64_t pairs, int E, int rows_per_tile) {
+    return pairs / rows_per_tile + (pairs < E ? pairs : E) + 1;
+}
+
+// Grouping outputs plus the derived tile list (tiles of at most rows_per_tile
+// rows per expert, in expert order) and its length.
+struct GroupOut {
+    int32_t *cnt, *off, *perm, *inv;
+    Tile *tiles;
+    int32_t *ntiles;
+    int rows_per_tile;
+    int32_t *chunk_cnt;   // [nchunks][E] scratch (multi-block path)
+    int32_t *chunk_base;  // [nchunks][E] scratch (multi-block path)
+};
+
+hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const float *bias, int64_t T, int H,
+                                int E, uint16_t *logits, hipStream_t s);
+hipError_t launch_topk(const uint16_t *logits, int64_t T, int E, int k, int32_t *idx, float *gate, hipStream_t s);
+
+hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s);
+
+hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
+                                 const GroupOut &g, float *h, float *o, float *y, hipStream_t s,
+                                 hipEvent_t const *ev);
+
+hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
+                                  const GroupOut &g, float *xsum, uint16_t *h, float *hsum, float *y,
+                                  hipStream_t s, hipEvent_t const *ev);
+
+// Records ev[i] on s when ev is not null (stage boundaries for timing).
+inline void stage_mark(hipEvent_t const *ev, int i, hipStream_t s) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+}
+
+hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, hipStream_t s);
+hipError_t launch_residual(const uint16_t *x, const float *y, int64_t n, uint16_t *out, hipStream_t s);
+
+}  // namespace moeq4

@@ -1,0 +1,59 @@
+"""Convenience wrapper: buffers for one routed int4 MoE layer call.
+
+Allocates the outputs and the workspace once (torch device memory) and calls
+the C ABI; the computation itself is the library's.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+class MoeQ4Layer:
+    """Route + expert layer for batches of up to ``max_tokens`` tokens.
+
+    ``weights``: object with num_experts, hidden, inter, fmt and the six
+    device tensors gate_q, up_q, down_q, gate_sm, up_sm, down_sm (canonical
+    layout of include/moe_q4.h).  ``mode``: "decode" (GEMV path) or
+    "prefill" (grouped-GEMM path).
+    """
+
+    def __init__(self, weights, k: int, max_tokens: int, mode: str = "decode", device="cuda"):
+        if mode not in ("decode", "prefill"):
+            raise ValueError("mode must be 'decode' or 'prefill'")
+        self.w = weights
+        self.k = k
+        self.E, self.H, self.I = weights.num_experts, weights.hidden, weights.inter
+        self.mode = mode
+        self.max_tokens = max_tokens
+        self.struct = _lib.layer_struct(weights)
+        T = max_tokens
+        kind = _lib.WS_DECODE if mode == "decode" else _lib.WS_PREFILL
+        nbytes = max(_lib.workspace_size(kind, T, self.E, k, self.H, self.I), 256)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.logits = torch.empty((T, self.E), dtype=torch.int16, device=device)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.gate = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.y = torch.empty((T, self.H), dtype=torch.float32, device=device)
+
+    def route(self, x=None, router_w=None, logits=None, bias=None, T=None):
+        """bf16 logits (computed from x and router_w, or copied from ``logits``)
+        -> top-k indices and gates; returns (logits, idx, gate) views."""
+        T = x.shape[0] if x is not None else (logits.shape[0] if T is None else T)
+        lg = self.logits[:T]
+        if x is None:
+            lg.copy_(logits)
+        _lib.moe_q4_route(x, router_w, bias, lg, T, self.H, self.E, self.k, self.idx[:T], self.gate[:T])
+        return lg, self.idx[:T], self.gate[:T]
+
+    def experts(self, x, idx, gate, y=None):
+        T = x.shape[0]
+        y = self.y[:T] if y is None else y
+        fn = _lib.moe_q4_decode if self.mode == "decode" else _lib.moe_q4_prefill
+        fn(x, idx, gate, T, self.k, self.struct, y, self.ws)
+        return y
+
+    def forward(self, x, router_w=None, logits=None, bias=None):
+        _, idx, gate = self.route(x if router_w is not None else None, router_w, logits, bias, T=x.shape[0])
+        return self.experts(x, idx, gate)

@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: exports, error strings, host-side argument checks.
+
+Every call here fails validation (or has T = 0) and returns before anything
+is launched, so no HIP device is needed.  Fake non-NULL pointers are never
+dereferenced on those paths.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_expert_amd as m
+from quantized_moe_expert_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_q4.h")
+FAKE = 0x10000  # never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_Q4_API\s+[\w\s\*]+?\b(moe_q4_\w+)\s*\(", text)
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) == 10
+    assert set(names) == set(m.EXPORTS)
+    lib = m.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_error_strings():
+    assert m.error_string(0) == "ok"
+    for st in (-1, -2, -3, -4):
+        assert m.error_string(st) not in ("ok", "unknown status")
+    assert m.error_string(7) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert m.workspace_size(m.WS_ROUTE, 16, 256, 8, 2048, 512) == 0
+    assert m.workspace_size(m.WS_DECODE, 0, 256, 8, 2048, 512) == 0
+    d1 = m.workspace_size(m.WS_DECODE, 1, 256, 8, 2048, 512)
+    d16 = m.workspace_size(m.WS_DECODE, 16, 256, 8, 2048, 512)
+    assert 0 < d1 < d16
+    # decode keeps fp32 h and o per (token, slot)
+    assert d16 >= 16 * 8 * (512 + 2048) * 4
+    p = m.workspace_size(m.WS_PREFILL, 4096, 256, 8, 2048, 512)
+    assert p >= 4096 * 8 * 512 * 2          # f16 h
+    assert m.workspace_size(m.WS_GROUP, 4096, 256, 8, 64, 64) >= 4096 * 8 * 4 * 2
+
+
+def _layer(fmt=0, E=256, H=2048, I=512, null=None):
+    ptrs = {n: FAKE for n in ("gate_q", "up_q", "down_q", "gate_sm", "up_sm", "down_sm")}
+    if null:
+        ptrs[null] = None
+    return _lib.Layer(E, H, I, fmt, *[ptrs[n] for n in ("gate_q", "up_q", "down_q", "gate_sm", "up_sm", "down_sm")])
+
+
+def _decode(layer, T=4, k=8, ws_bytes=1 << 30, x=FAKE, prefill=False):
+    fn = m.lib().moe_q4_prefill if prefill else m.lib().moe_q4_decode
+    return fn(x, FAKE, FAKE, T, k, ctypes.byref(layer), FAKE, FAKE, ws_bytes, None)
+
+
+def test_route_validation():
+    L = m.lib()
+    r = lambda **kw: L.moe_q4_route(kw.get("x", FAKE), kw.get("w", FAKE), None, kw.get("lg", FAKE),
+                                    kw.get("T", 4), kw.get("H", 2048), kw.get("E", 256), kw.get("k", 8),
+                                    kw.get("idx", FAKE), kw.get("gate", FAKE), None, 0, None)
+    assert r(lg=None) == _lib.ERR_INVALID_ARG
+    assert r(idx=None) == _lib.ERR_INVALID_ARG
+    assert r(w=None) == _lib.ERR_INVALID_ARG            # x given without router weights
+    assert r(k=0) == _lib.ERR_INVALID_ARG
+    assert r(k=9, E=8) == _lib.ERR_INVALID_ARG
+    assert r(T=-1) == _lib.ERR_INVALID_ARG
+    assert r(E=2048, k=8) == _lib.ERR_UNSUPPORTED
+    assert r(k=33, E=256) == _lib.ERR_UNSUPPORTED
+    assert r(H=4096) == _lib.ERR_UNSUPPORTED
+    assert r(H=100) == _lib.ERR_UNSUPPORTED
+    assert r(T=0) == _lib.OK
+
+
+def test_group_validation():
+    L = m.lib()
+    g = lambda T=16, k=8, E=256, ws=FAKE, nb=1 << 30, cnt=FAKE: L.moe_q4_group(FAKE, T, k, E, cnt, FAKE, FAKE,
+                                                                                  FAKE, ws, nb, None)
+    assert g(cnt=None) == _lib.ERR_INVALID_ARG
+    assert g(ws=None) == _lib.ERR_WORKSPACE
+    assert g(nb=16) == _lib.ERR_WORKSPACE
+    assert g(T=0) == _lib.OK
+    assert g(k=300, E=256) == _lib.ERR_INVALID_ARG
+
+
+def test_layer_validation():
+    assert _decode(_layer(null="down_sm")) == _lib.ERR_INVALID_ARG
+    assert _decode(_layer(fmt=2)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(H=3072)) == _lib.ERR_UNSUPPORTED       # not a power of two
+    assert _decode(_layer(H=4096)) == _lib.ERR_UNSUPPORTED       # above 2048
+    assert _decode(_layer(fmt=1, I=64)) == _lib.ERR_UNSUPPORTED  # not a multiple of 128
+    assert _decode(_layer(E=0)) == _lib.ERR_INVALID_ARG
+    assert _decode(_layer(), x=None) == _lib.ERR_INVALID_ARG
+    assert _decode(_layer(), ws_bytes=100) == _lib.ERR_WORKSPACE
+    assert _decode(_layer(), k=0) == _lib.ERR_INVALID_ARG
+    assert _decode(_layer(), T=0) == _lib.OK
+    assert _decode(_layer(I=64), prefill=True) == _lib.ERR_UNSUPPORTED    # prefill needs I % 128 == 0
+    assert _decode(_layer(H=128, I=128), prefill=True) == _lib.ERR_UNSUPPORTED  # and H % 256 == 0
+    assert _decode(_layer(), prefill=True, ws_bytes=100) == _lib.ERR_WORKSPACE
+    assert _decode(_layer(), prefill=True, T=0) == _lib.OK
+    # timed variants: events are required and must be non-NULL
+    L = m.lib()
+    ev_null = (ctypes.c_void_p * 5)(FAKE, FAKE, None, FAKE, FAKE)
+    ev_ok = (ctypes.c_void_p * 5)(*([FAKE] * 5))
+    lay = _layer()
+    for fn in (L.moe_q4_decode_timed, L.moe_q4_prefill_timed):
+        assert fn(FAKE, FAKE, FAKE, 4, 8, ctypes.byref(lay), FAKE, FAKE, 1 << 30, None, None) == _lib.ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, FAKE, 4, 8, ctypes.byref(lay), FAKE, FAKE, 1 << 30, None, ev_null) == _lib.ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, FAKE, 4, 8, ctypes.byref(lay), FAKE, FAKE, 100, None, ev_ok) == _lib.ERR_WORKSPACE
+        assert fn(FAKE, FAKE, FAKE, 0, 8, ctypes.byref(lay), FAKE, FAKE, 1 << 30, None, ev_ok) == _lib.OK
+
+
+def test_dequant_and_residual_validation():
+    L = m.lib()
+    lay = _layer()
+    assert L.moe_q4_dequant(ctypes.byref(lay), 256, 0, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_dequant(ctypes.byref(lay), 0, 3, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_dequant(ctypes.byref(lay), 0, 0, None, None) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_residual_bf16(FAKE, FAKE, -1, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_residual_bf16(FAKE, None, 5, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_residual_bf16(None, None, 0, None, None) == _lib.OK
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, dtype=torch.int16)
+    with pytest.raises(ValueError):
+        _lib._ptr(x)

@@ -1,0 +1,287 @@
+"""HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Bars: dequantised weights, router logits, expert indices, histogram, offsets
+and permutation bit-exact; gates within 1e-6 relative; layer outputs within
+relative L2 2e-3 and max abs 1e-2 of the fp64 oracle.  Inputs are the seeded
+synthetic workloads (synth.make_case) at full size, plus small and ragged
+shapes; where a full-size output is too large for the oracle, sampled tokens
+are compared (the layer is token-wise independent).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_cases import (GATE_RTOL, assert_close, hip_experts, hip_route, np_u16, oracle_route, oracle_y)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_moe_expert_amd as m
+    m.lib()  # fails loudly if the library was not built
+    return torch.device("cuda")
+
+
+_cases = {}
+
+
+def get_case(cfg, **kw):
+    key = (cfg, tuple(sorted(kw.items())))
+    if key not in _cases:
+        say(f"[gen] config {cfg} {kw}")
+        _cases[key] = synth.make_case(cfg, device="cuda", **kw)
+        torch.cuda.synchronize()
+    return _cases[key]
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("fmt", [synth.FMT_ASYM_G64, synth.FMT_SYM_G128])
+@pytest.mark.parametrize("shape", [(3, 256, 128), (2, 2048, 512)])
+def test_dequant_bit_exact(fmt, shape):
+    import quantized_moe_expert_amd as m
+    E, H, I = shape
+    say(f"[dequant] fmt={fmt} E={E} H={H} I={I}")
+    lay = synth.random_layer(E, H, I, fmt, seed=5, device="cuda")
+    host = oracle.layer_np(lay)
+    g = synth.GROUP[fmt]
+    for e in range(E):
+        for proj in range(3):
+            N, K = (H, I) if proj == 2 else (I, H)
+            out = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            m.moe_q4_dequant(lay, e, proj, out)
+            ref = oracle.dequant(fmt, host[proj][e], host[3 + proj][e], N, K)
+            got = out.cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (e, proj)
+    del g
+
+
+def test_dequant_generated_layer_bit_exact():
+    import quantized_moe_expert_amd as m
+    case = get_case(1)
+    lay = case.layers[0]
+    host = oracle.layer_np(lay)
+    for e in (0, 7, 15):
+        out = torch.empty((lay.inter, lay.hidden), dtype=torch.float32, device="cuda")
+        m.moe_q4_dequant(lay, e, 1, out)
+        ref = oracle.dequant(lay.fmt, host[1][e], host[4][e], lay.inter, lay.hidden)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# -------------------------------------------------------------------- route
+
+def _check_route(lg_gpu, idx_gpu, gate_gpu, lg_ref, idx_ref, gate_ref, compare_logits=True):
+    if compare_logits:
+        got = np_u16(lg_gpu)
+        assert np.array_equal(got, lg_ref), f"{int((got != lg_ref).sum())} logits differ"
+    assert np.array_equal(idx_gpu.cpu().numpy(), idx_ref), "expert indices differ"
+    g = gate_gpu.cpu().numpy().astype(np.float64)
+    assert np.allclose(g, gate_ref, rtol=GATE_RTOL, atol=0), float(np.max(np.abs(g / gate_ref - 1)))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_route_configs(cfg):
+    case = get_case(cfg)
+    say(f"[route] config {cfg}")
+    lg, idx, gate = hip_route(case.x, case.router_w, None, case.T, case.H, case.E, case.k)
+    lr, ir, gr = oracle_route(case, np_u16(case.x))
+    _check_route(lg, idx, gate, lr, ir, gr)
+
+
+@pytest.mark.parametrize("T,H,E,k", [(64, 2048, 256, 8), (300, 256, 16, 2), (5, 512, 1000, 32), (3, 64, 8, 8)])
+def test_route_gemv_shapes(T, H, E, k):
+    say(f"[route] T={T} H={H} E={E} k={k}")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 1, "rt/x", "cuda"))
+    wr = synth.bf16_bits(synth.normal((E, H), 0.05, 1, "rt/w", "cuda"))
+    bias = synth.normal((E,), 0.3, 1, "rt/b", "cuda")
+    for b in (None, bias):
+        lg, idx, gate = hip_route(x, wr, None, T, H, E, k, bias=b)
+        lr = oracle.router(np_u16(x), np_u16(wr), T, H, E, None if b is None else b.cpu().numpy())
+        ir, gr = oracle.topk(lr, T, E, k)
+        _check_route(lg, idx, gate, lr, ir, gr)
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 256, 8), (50, 16, 2), (7, 9, 9), (4096, 256, 8)])
+def test_route_given_logits_with_ties(T, E, k):
+    """Logits from a handful of values: ties at the k-th place are everywhere."""
+    say(f"[route ties] T={T} E={E} k={k}")
+    g = synth.generator(3, "ties", "cuda")
+    vals = torch.randint(-3, 4, (T, E), generator=g, device="cuda").float() * 0.25
+    lg_in = synth.bf16_bits(vals)
+    lg, idx, gate = hip_route(None, None, lg_in, T, 0, E, k)
+    lr = np_u16(lg_in)
+    ir, gr = oracle.topk(lr, T, E, k)
+    _check_route(lg, idx, gate, lr, ir, gr)
+
+
+def test_route_all_equal_and_zipf():
+    T, E, k = 8, 256, 8
+    lg_in = synth.bf16_bits(torch.full((T, E), 0.5, device="cuda"))
+    _, idx, gate = hip_route(None, None, lg_in, T, 0, E, k)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(k), (T, 1)))
+    assert np.all(gate.cpu().numpy() == np.float32(1.0 / k))
+    case = get_case(3)
+    lg, idx, gate = hip_route(None, None, case.logits, case.T, case.H, case.E, case.k)
+    lr, ir, gr = oracle_route(case, np_u16(case.x))
+    _check_route(lg, idx, gate, lr, ir, gr, compare_logits=False)
+
+
+# -------------------------------------------------------------------- group
+
+def _hip_group(idx, T, k, E):
+    import quantized_moe_expert_amd as m
+    ws = torch.empty(max(m.workspace_size(m.WS_GROUP, T, E, k, 64, 64), 256), dtype=torch.uint8, device="cuda")
+    cnt = torch.empty(E, dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    m.moe_q4_group(idx, T, k, E, cnt, off, perm, inv, ws)
+    return [t.cpu().numpy() for t in (cnt, off, perm, inv)]
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (4, 2, 16), (16, 8, 256), (64, 8, 256), (128, 8, 256),
+                                   (129, 8, 256), (512, 8, 256), (4096, 8, 256), (333, 3, 1000)])
+def test_group_exact(T, k, E):
+    say(f"[group] T={T} k={k} E={E}")
+    g = synth.generator(4, f"grp/{T}/{k}/{E}", "cuda")
+    idx = torch.argsort(torch.rand((T, E), generator=g, device="cuda"), dim=1)[:, :k].to(torch.int32).contiguous()
+    got = _hip_group(idx, T, k, E)
+    ref = oracle.group(idx.cpu().numpy(), T, k, E)
+    for name, a, b in zip(("cnt", "off", "perm", "inv"), got, ref):
+        assert np.array_equal(a, b), name
+
+
+def test_group_zipf_skew():
+    case = get_case(3)
+    _, idx, _ = hip_route(None, None, case.logits, case.T, case.H, case.E, case.k)
+    got = _hip_group(idx, case.T, case.k, case.E)
+    ref = oracle.group(idx.cpu().numpy(), case.T, case.k, case.E)
+    for name, a, b in zip(("cnt", "off", "perm", "inv"), got, ref):
+        assert np.array_equal(a, b), name
+    say(f"[zipf] active experts {int((ref[0] > 0).sum())}, max load {int(ref[0].max())}, "
+        f"median {int(np.median(ref[0]))}")
+
+
+# -------------------------------------------------------------------- layer
+
+def _layer_parity(case, mode, tokens=None, layer=0):
+    lay = case.layers[layer]
+    x_np = np_u16(case.x)
+    rw = case.router_ws[layer] if case.router_ws else None
+    lg, idx, gate = hip_route(case.x if rw is not None else None, rw, case.logits, case.T, case.H, case.E, case.k)
+    sub = np.arange(case.T) if tokens is None else np.asarray(tokens)
+    if rw is not None:
+        lr = oracle.router(np.ascontiguousarray(x_np[sub]), np_u16(rw), len(sub), case.H, case.E)
+    else:
+        lr = np.ascontiguousarray(np_u16(case.logits)[sub])
+    ir, gr = oracle.topk(lr, len(sub), case.E, case.k)
+    assert np.array_equal(idx.cpu().numpy()[sub], ir), "expert indices differ"
+    y = hip_experts(mode, lay, case.x, idx, gate, case.k)
+    torch.cuda.synchronize()
+    yr = oracle_y(lay, x_np, ir, gr, case.k, tokens=sub)
+    r, a = assert_close(y.cpu().numpy()[sub], yr, f"{case.name} {mode}")
+    say(f"[{mode}] {case.name} T={case.T}: rel L2 {r:.2e}, max abs {a:.2e}")
+    return y
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_decode_configs(cfg):
+    _layer_parity(get_case(cfg), "decode")
+
+
+def test_decode_frame_layer():
+    """One layer of the 16-token frame recipe (RTN weights, GEMV router)."""
+    _layer_parity(get_case(4, layers=1), "decode")
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_prefill_configs(cfg):
+    _layer_parity(get_case(cfg), "prefill")
+
+
+def test_prefill_long_sym_sampled():
+    case = get_case(5)
+    tokens = np.unique(np.concatenate([np.arange(0, 4096, 97), [1, 2, 4094, 4095]]))
+    _layer_parity(case, "prefill", tokens=tokens)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("fmt", [synth.FMT_ASYM_G64, synth.FMT_SYM_G128])
+@pytest.mark.parametrize("T", [1, 37, 200])
+def test_layer_ragged(mode, fmt, T):
+    """Ragged token counts on a 64-expert layer with random codes and scales."""
+    H, I, E, k = 512, 256, 64, 6
+    say(f"[ragged] {mode} fmt={fmt} T={T}")
+    lay = synth.random_layer(E, H, I, fmt, seed=9, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 9, f"rg/x/{T}", "cuda"))
+    wr = synth.bf16_bits(synth.normal((E, H), 0.05, 9, "rg/w", "cuda"))
+    lg, idx, gate = hip_route(x, wr, None, T, H, E, k)
+    lr = oracle.router(np_u16(x), np_u16(wr), T, H, E)
+    ir, gr = oracle.topk(lr, T, E, k)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    y = hip_experts(mode, lay, x, idx, gate, k)
+    yr = oracle.experts(fmt, E, H, I, *oracle.layer_np(lay), np_u16(x), ir, gr, T, k)
+    assert_close(y.cpu().numpy(), yr, f"ragged {mode}")
+
+
+def test_decode_and_prefill_agree():
+    case = get_case(4, layers=1, T=64)
+    lay = case.layers[0]
+    _, idx, gate = hip_route(case.x, case.router_ws[0], None, case.T, case.H, case.E, case.k)
+    yd = hip_experts("decode", lay, case.x, idx, gate, case.k).cpu().numpy()
+    yp = hip_experts("prefill", lay, case.x, idx, gate, case.k).cpu().numpy()
+    assert_close(yp, yd, "prefill vs decode")
+
+
+def test_decode_deterministic():
+    case = get_case(4, layers=1)
+    lay = case.layers[0]
+    _, idx, gate = hip_route(case.x, case.router_ws[0], None, case.T, case.H, case.E, case.k)
+    y1 = hip_experts("decode", lay, case.x, idx, gate, case.k).cpu().numpy()
+    y2 = hip_experts("decode", lay, case.x, idx, gate, case.k).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_residual_bit_exact():
+    import quantized_moe_expert_amd as m
+    n = 16 * 2048 + 5
+    x = synth.bf16_bits(synth.normal((n,), 1.0, 2, "res/x", "cuda"))
+    y = synth.normal((n,), 0.7, 2, "res/y", "cuda")
+    out = torch.empty_like(x)
+    m.moe_q4_residual_bf16(x, y, n, out)
+    ref = oracle.residual(np_u16(x), y.cpu().numpy())
+    assert np.array_equal(np_u16(out), ref)
+
+
+def test_frame_chain_layers():
+    """Frame recipe (16 tokens, RTN g64, own router per layer), 3 layers: each
+    layer runs on the oracle's own chain input x_l (teacher-forced), so a
+    near-tie flip upstream cannot hide a downstream error."""
+    case = get_case(4, layers=3)
+    x_np = np_u16(case.x)
+    for l in range(3):
+        lay, rw = case.layers[l], case.router_ws[l]
+        xl = torch.from_numpy(x_np.view(np.int16).copy()).cuda()
+        lg, idx, gate = hip_route(xl, rw, None, case.T, case.H, case.E, case.k)
+        lr = oracle.router(x_np, np_u16(rw), case.T, case.H, case.E)
+        ir, gr = oracle.topk(lr, case.T, case.E, case.k)
+        assert np.array_equal(np_u16(lg), lr)
+        assert np.array_equal(idx.cpu().numpy(), ir)
+        y = hip_experts("decode", lay, xl, idx, gate, case.k)
+        yr = oracle_y(lay, x_np, ir, gr, case.k)
+        r, a = assert_close(y.cpu().numpy(), yr, f"frame layer {l}")
+        say(f"[frame] layer {l}: rel L2 {r:.2e} max abs {a:.2e}")
+        x_np = oracle.residual(x_np, yr)
