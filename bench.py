@@ -116,35 +116,55 @@ def main():
     structs = [m.layer_struct(l) for l in layers]
     kind = m.WS_DECODE if decode_path else m.WS_PREFILL
     ws = torch.empty(max(m.workspace_size(kind, T, E, k, H, I), 256), dtype=torch.uint8, device=dev)
+    wsf = torch.zeros(max(m.workspace_size(m.WS_FORWARD, T, E, k, H, I), 256), dtype=torch.uint8, device=dev)
+    m.moe_q4_workspace_init(wsf)
     lg = torch.empty((T, E), dtype=torch.int16, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
-    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ybuf = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(2)]
     xbuf = [torch.empty_like(case.x), torch.empty_like(case.x)]
-    experts_fn = m.moe_q4_decode if decode_path else m.moe_q4_prefill
     timed_fn = m.moe_q4_decode_timed if decode_path else m.moe_q4_prefill_timed
-
     state = {"i": 0}
 
-    def step(events=None):
-        """One step: every layer of the workload once."""
-        xin = case.x
-        for j in range(nl_per_step):
-            li = (state["i"] % len(layers)) if args.workload == "decode" else j
+    def layer_ids():
+        if args.workload == "decode":
+            return [state["i"] % len(layers)]
+        return list(range(nl_per_step))
+
+    def step():
+        """One step: every layer of the workload once, each one moe_q4_forward
+        call (routing, grouping, experts; the residual of a chain fused in)."""
+        for j, li in enumerate(layer_ids()):
             rw = routers[li] if routers[0] is not None else None
+            logits_in = lg if rw is not None else case.logits
+            if args.workload == "frame" and j > 0:
+                x_prev = case.x if j == 1 else xbuf[(j - 1) & 1]
+                m.moe_q4_forward(x_prev, ybuf[(j - 1) & 1], xbuf[j & 1], rw, None, logits_in, T, k, structs[li],
+                                 idx, gate, ybuf[j & 1], wsf)
+            else:
+                m.moe_q4_forward(case.x, None, None, rw, None, logits_in, T, k, structs[li], idx, gate,
+                                 ybuf[j & 1], wsf)
+        state["i"] += 1
+
+    def step_profiled(evsets):
+        """Same work as step() through the separate entry points, with the
+        expert stage bracketed by HIP events on the launch stream."""
+        for j, li in enumerate(layer_ids()):
+            rw = routers[li] if routers[0] is not None else None
+            xin = case.x
+            if args.workload == "frame" and j > 0:
+                x_prev = case.x if j == 1 else xbuf[(j - 1) & 1]
+                m.moe_q4_residual_bf16(x_prev, ybuf[(j - 1) & 1], T * H, xbuf[j & 1])
+                xin = xbuf[j & 1]
             if rw is not None:
                 m.moe_q4_route(xin, rw, None, lg, T, H, E, k, idx, gate)
-            else:  # given logits (prefill workloads): top-k only, logits read in place
-                m.moe_q4_route(None, None, None, case.logits, T, H, E, k, idx, gate)
-            if events is not None and j == nl_per_step - 1:
-                timed_fn(xin, idx, gate, T, k, structs[li], y, ws, [e.cuda_event for e in events])
             else:
-                experts_fn(xin, idx, gate, T, k, structs[li], y, ws)
-            if args.workload == "frame":
-                xout = xbuf[j & 1]
-                m.moe_q4_residual_bf16(xin, y, T * H, xout)
-                xin = xout
+                m.moe_q4_route(None, None, None, case.logits, T, H, E, k, idx, gate)
+            timed_fn(xin, idx, gate, T, k, structs[li], ybuf[j & 1], ws, [e.cuda_event for e in evsets[j]])
+            routed.append(idx.clone())
         state["i"] += 1
+
+    routed = []
 
     # ---- warmup + timed steps ------------------------------------------------
     for _ in range(W):
@@ -163,34 +183,36 @@ def main():
     value = tokens_per_step * K / (total_ms / 1e3)
     log(f"[bench] {args.workload}: {ms_per_step * 1e3:.2f} us/step, {value:.1f} tokens/s")
 
-    # ---- stage timing of the dominant kernel (same steps, events on the stream)
+    # ---- stage timing of the dominant kernel (same work, events on the stream)
     nev = m.STAGE_EVENTS
-    stage_ms = []
-    prof_steps = min(K, 50)
-    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(prof_steps)]
-    for evs in ev_sets:  # materialise the event handles
-        for e in evs:
-            e.record()
+    prof_steps = max(1, min(K, 50 if nl_per_step == 1 else 2))
+    ev_sets = [[[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(nl_per_step)]
+               for _ in range(prof_steps)]
+    for per_step in ev_sets:  # materialise the event handles
+        for evs in per_step:
+            for e in evs:
+                e.record()
     torch.cuda.synchronize()
-    for evs in ev_sets:
-        step(events=evs)
+    for per_step in ev_sets:
+        step_profiled(per_step)
     torch.cuda.synchronize()
-    for evs in ev_sets:
-        stage_ms.append([evs[i].elapsed_time(evs[i + 1]) for i in range(nev - 1)])
-    stage_ms = np.array(stage_ms)
+    stage_ms = np.array([[evs[i].elapsed_time(evs[i + 1]) for i in range(nev - 1)]
+                         for per_step in ev_sets for evs in per_step])
     stage_avg = stage_ms.mean(axis=0)
     log(f"[bench] stage times (us): {', '.join(f'{v * 1e3:.2f}' for v in stage_avg)}")
 
     # work actually routed in the profiled layer (outside timed regions)
-    act = torch.unique(idx).numel()
+    # active experts per profiled layer call, averaged (the frame's layers differ)
+    act = float(np.mean([torch.unique(r).numel() for r in routed]))
     lay0 = layers[0]
     proj_bytes = expert_bytes(lay0) // 3        # one projection of one expert (codes + scales)
     P = T * k
     if decode_path:
-        # dominant kernel: gate/up GEMV + SwiGLU (stage 1): reads 2 projections of each
-        # active expert, the activations, writes h (fp32)
-        dom = "decode_gateup_kernel"
-        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 4
+        # dominant kernel: the fused expert kernel (stage 1): reads the gate, up and
+        # down codes and scales of every active expert once, the activations, and
+        # adds into y (fp32)
+        dom = "decode_experts_kernel"
+        alg_bytes = act * 3 * proj_bytes + T * H * 2 + T * H * 4
         achieved = alg_bytes / (stage_avg[1] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,

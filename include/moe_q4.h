@@ -79,7 +79,8 @@ typedef enum {
     MOE_Q4_WS_ROUTE = 0,
     MOE_Q4_WS_DECODE = 1,
     MOE_Q4_WS_PREFILL = 2,
-    MOE_Q4_WS_GROUP = 3
+    MOE_Q4_WS_GROUP = 3,
+    MOE_Q4_WS_FORWARD = 4
 } moe_q4_ws_kind;
 
 /*
@@ -142,10 +143,11 @@ MOE_Q4_API int moe_q4_group(const int32_t *topk_idx, int64_t T, int32_t k, int32
                  void *ws, size_t ws_bytes, moe_q4_stream stream);
 
 /*
- * Expert layer for few tokens (tuned for T <= 64): grouping, then for each
- * active expert a fused-dequant GEMV over its packed nibbles (gate and up
- * with SwiGLU, then down) in fp32, then the gate-weighted combine in slot
- * order (deterministic).
+ * Expert layer for few tokens (tuned for T <= 64): grouping, then one kernel
+ * of fused-dequant GEMVs over the active experts' packed nibbles: gate and
+ * up with SwiGLU in fp32 for a 64-row chunk of h, then that chunk's slice of
+ * the down GEMV, multiplied by the gate and added into y with float atomics
+ * (y may differ between runs in the last bits).
  *   x          bf16 [T][H]
  *   topk_idx   int32 [T][k], topk_gate float [T][k] (as from moe_q4_route)
  *   w          the layer (host struct holding device pointers)
@@ -170,11 +172,41 @@ MOE_Q4_API int moe_q4_prefill(const void *x, const int32_t *topk_idx, const floa
                    void *ws, size_t ws_bytes, moe_q4_stream stream);
 
 /*
+ * Whole layer in one call: routing (router GEMV when router_w != NULL, else
+ * the given logits), top-k gates, grouping and the experts, y float [T][H].
+ * For T <= 64 (and T*k <= 1024) this is two kernel launches: routing with
+ * top-k and grouping fused (the last workgroup to finish its router rows does
+ * the top-k and grouping), then the decode expert kernel; larger T takes the
+ * prefill path.
+ *   residual_y  float [T][H] or NULL.  When given, the layer input is the
+ *               residual step bf16(float(x) + residual_y) of a chain of layers
+ *               (as moe_q4_residual_bf16), written to x_out (bf16 [T][H],
+ *               required then); y must not alias residual_y.
+ *   logits      bf16 [T][E]: written when router_w != NULL, read otherwise.
+ *   topk_idx, topk_gate: as moe_q4_route (outputs).
+ *   ws          >= moe_q4_workspace_size(MOE_Q4_WS_FORWARD, ...) bytes; its
+ *               control block must be cleared once by moe_q4_workspace_init
+ *               before the first call (it is left cleared by every call).
+ * Results equal moe_q4_route followed by moe_q4_decode (T <= 64) or
+ * moe_q4_prefill.
+ */
+MOE_Q4_API int moe_q4_forward(const void *x, const float *residual_y, void *x_out,
+                              const void *router_w, const float *bias, void *logits,
+                              int64_t T, int32_t k, const moe_q4_layer *w,
+                              int32_t *topk_idx, float *topk_gate, float *y,
+                              void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/* Clears the control block of a workspace used with moe_q4_forward (once,
+ * after allocation).  Enqueued on stream. */
+MOE_Q4_API int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/*
  * Same as moe_q4_decode / moe_q4_prefill, and additionally records the
  * caller's HIP events (hipEvent_t handles, created by the caller) on `stream`
  * at the stage boundaries, so that each stage's kernel time can be read with
  * hipEventElapsedTime:
- *   decode:  [0] grouping [1] gate/up GEMV + SwiGLU [2] down GEMV [3] combine [4]
+ *   decode:  [0] grouping + clear y [1] expert kernel (gate/up GEMV, SwiGLU,
+ *            down GEMV slice, gate-weighted add into y) [2] [3] [4] (empty)
  *   prefill: [0] grouping [1] row sums + output clear [2] gate/up GEMM + SwiGLU
  *            [3] down GEMM + combine [4]
  * events must point to MOE_Q4_STAGE_EVENTS valid events.

@@ -9,10 +9,12 @@ binding: ``_lib`` mirrors the C entry points, ``layer`` holds buffers.
 from ._lib import (ASYM_G64, SYM_G128, WS_DECODE, WS_GROUP, WS_PREFILL, WS_ROUTE, EXPORTS, MoeQ4Error,
                    error_string, layer_struct, lib, moe_q4_decode, moe_q4_dequant, moe_q4_group,
                    moe_q4_prefill, moe_q4_residual_bf16, moe_q4_route, workspace_size,
-                   moe_q4_decode_timed, moe_q4_prefill_timed, STAGE_EVENTS)
+                   moe_q4_decode_timed, moe_q4_prefill_timed, STAGE_EVENTS, WS_FORWARD, moe_q4_forward,
+                   moe_q4_workspace_init)
 from .layer import MoeQ4Layer
 
 __all__ = ["ASYM_G64", "SYM_G128", "WS_DECODE", "WS_GROUP", "WS_PREFILL", "WS_ROUTE", "EXPORTS", "MoeQ4Error",
            "error_string", "layer_struct", "lib", "moe_q4_decode", "moe_q4_dequant", "moe_q4_group",
            "moe_q4_prefill", "moe_q4_residual_bf16", "moe_q4_route", "workspace_size", "MoeQ4Layer",
-           "moe_q4_decode_timed", "moe_q4_prefill_timed", "STAGE_EVENTS"]
+           "moe_q4_decode_timed", "moe_q4_prefill_timed", "STAGE_EVENTS", "WS_FORWARD", "moe_q4_forward",
+           "moe_q4_workspace_init"]

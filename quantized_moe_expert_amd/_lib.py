@@ -15,13 +15,13 @@ LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
 
 ASYM_G64 = 0
 SYM_G128 = 1
-WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP = 0, 1, 2, 3
+WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP, WS_FORWARD = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 # every entry point declared in include/moe_q4.h
 EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_decode", "moe_q4_prefill",
-           "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_dequant", "moe_q4_residual_bf16",
-           "moe_q4_error_string")
+           "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_workspace_init",
+           "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string")
 STAGE_EVENTS = 5
 
 
@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, sz, P, ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_q4_forward.restype = ctypes.c_int
+        L.moe_q4_forward.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, P, P, sz, P]
+        L.moe_q4_workspace_init.restype = ctypes.c_int
+        L.moe_q4_workspace_init.argtypes = [P, sz, P]
         L.moe_q4_dequant.restype = ctypes.c_int
         L.moe_q4_dequant.argtypes = [ctypes.POINTER(Layer), i32, i32, P, P]
         L.moe_q4_residual_bf16.restype = ctypes.c_int
@@ -168,6 +172,20 @@ def moe_q4_decode_timed(x, topk_idx, topk_gate, T, k, layer, y, ws, events, stre
 
 def moe_q4_prefill_timed(x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream=None):
     _timed("moe_q4_prefill_timed", x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream)
+
+
+def moe_q4_forward(x, residual_y, x_out, router_w, bias, logits, T, k, layer, topk_idx, topk_gate, y, ws,
+                   stream=None):
+    w, nb = _ws(ws)
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    _check("moe_q4_forward", lib().moe_q4_forward(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias),
+                                                   _ptr(logits), T, k, ctypes.byref(st), _ptr(topk_idx),
+                                                   _ptr(topk_gate), _ptr(y), w, nb, _stream(stream)))
+
+
+def moe_q4_workspace_init(ws, stream=None):
+    w, nb = _ws(ws)
+    _check("moe_q4_workspace_init", lib().moe_q4_workspace_init(w, nb, _stream(stream)))
 
 
 def moe_q4_dequant(layer, expert, proj, out, stream=None):

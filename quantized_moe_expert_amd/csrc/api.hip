@@ -80,15 +80,19 @@ GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile) {
 
 struct DecodeWs {
     GroupOut g;
-    float *h, *o;
 };
 DecodeWs carve_decode(Carver &c, int64_t T, int E, int k, int H, int I) {
+    (void)H;
+    (void)I;
     DecodeWs d;
     d.g = carve_group(c, T, E, k, DECODE_TT);
-    d.h = c.take<float>(T * k * (int64_t)I);
-    d.o = c.take<float>(T * k * (int64_t)H);
     return d;
 }
+
+// moe_q4_forward: a control block (zeroed by moe_q4_workspace_init) followed by
+// the decode or prefill regions.
+constexpr size_t CONTROL_BYTES = 256;
+bool forward_uses_decode(int64_t T, int k) { return T <= 64 && T * k <= GROUP_SINGLE_MAX; }
 
 struct PrefillWs {
     GroupOut g;
@@ -119,6 +123,11 @@ size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t
         case MOE_Q4_WS_GROUP: carve_group(c, T, E, k, DECODE_TT); break;
         case MOE_Q4_WS_DECODE: carve_decode(c, T, E, k, H, I); break;
         case MOE_Q4_WS_PREFILL: carve_prefill(c, T, E, k, H, I); break;
+        case MOE_Q4_WS_FORWARD:
+            c.take<char>(CONTROL_BYTES);
+            if (forward_uses_decode(T, k)) carve_decode(c, T, E, k, H, I);
+            else carve_prefill(c, T, E, k, H, I);
+            break;
         default: return 0;
     }
     return c.used;
@@ -181,12 +190,22 @@ static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, con
     Carver c{static_cast<char *>(ws)};
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
-    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MOE_Q4_ERR_HIP;
+    stage_mark(ev, 0, s);
     if (!prefill) {
         DecodeWs d = carve_decode(c, T, E, k, H, I);
-        st = hip_status(launch_group(topk_idx, T, k, E, d.g, s));
+        if (T * k <= GROUP_SINGLE_MAX) {
+            st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H));
+        } else {
+            st = hip_status(launch_group(topk_idx, T, k, E, d.g, s));
+            if (!st) st = hip_status(launch_fill_zero(y, T * (int64_t)H, s));
+        }
         if (st) return st;
-        return hip_status(launch_decode_experts(xb, topk_gate, T, k, L, d.g, d.h, d.o, y, s, ev ? ev + 1 : nullptr));
+        stage_mark(ev, 1, s);
+        st = hip_status(launch_decode_experts(xb, topk_gate, T, k, L, d.g, y, s));
+        stage_mark(ev, 2, s);
+        stage_mark(ev, 3, s);
+        stage_mark(ev, 4, s);
+        return st;
     }
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
@@ -217,6 +236,59 @@ int moe_q4_prefill_timed(const void *x, const int32_t *topk_idx, const float *to
                          void *const *events) {
     if (!events) return MOE_Q4_ERR_INVALID_ARG;
     return run_experts(true, x, topk_idx, topk_gate, T, k, w, y, ws, ws_bytes, stream, events);
+}
+
+int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream) {
+    if (!ws || ws_bytes < CONTROL_BYTES) return MOE_Q4_ERR_WORKSPACE;
+    return hip_status(launch_fill_zero_u32(static_cast<uint32_t *>(ws), CONTROL_BYTES / 4,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
+                   void *logits, int64_t T, int32_t k, const moe_q4_layer *w, int32_t *topk_idx, float *topk_gate,
+                   float *y, void *ws, size_t ws_bytes, moe_q4_stream stream) {
+    int st = check_layer(w, false);
+    if (st) return st;
+    st = check_route_shape(T, w->hidden, w->num_experts, k);
+    if (st) return st;
+    if (!x || !logits || !topk_idx || !topk_gate || !y) return MOE_Q4_ERR_INVALID_ARG;
+    if (residual_y && !x_out) return MOE_Q4_ERR_INVALID_ARG;
+    if (T == 0) return MOE_Q4_OK;
+    const int E = w->num_experts, H = w->hidden, I = w->inter;
+    const bool dec = forward_uses_decode(T, k);
+    if (!dec && check_layer(w, true)) return MOE_Q4_ERR_UNSUPPORTED;
+    const size_t need = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
+    if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const LayerPtrs L = layer_ptrs(w);
+    Carver c{static_cast<char *>(ws)};
+    unsigned int *counter = c.take<unsigned int>(CONTROL_BYTES / sizeof(unsigned int));
+    const uint16_t *xin = static_cast<const uint16_t *>(residual_y ? x_out : x);
+    const uint16_t *wr = static_cast<const uint16_t *>(router_w);
+    uint16_t *lg = static_cast<uint16_t *>(logits);
+    if (dec) {
+        DecodeWs d = carve_decode(c, T, E, k, H, I);
+        st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
+                                                  static_cast<uint16_t *>(x_out), wr, bias, (int)T, H, E, k, lg,
+                                                  topk_idx, topk_gate, d.g, y, counter, s));
+        if (st) return st;
+        return hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, y, s));
+    }
+    if (residual_y) {
+        st = hip_status(launch_residual(static_cast<const uint16_t *>(x), residual_y, T * (int64_t)H,
+                                        static_cast<uint16_t *>(x_out), s));
+        if (st) return st;
+    }
+    if (wr) {
+        st = hip_status(launch_router_logits(xin, wr, bias, T, H, E, lg, s));
+        if (st) return st;
+    }
+    st = hip_status(launch_topk(lg, T, E, k, topk_idx, topk_gate, s));
+    if (st) return st;
+    PrefillWs p = carve_prefill(c, T, E, k, H, I);
+    st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
+    if (st) return st;
+    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.xsum, p.h, p.hsum, y, s, nullptr));
 }
 
 int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *out, moe_q4_stream stream) {

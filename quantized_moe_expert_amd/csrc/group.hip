@@ -9,100 +9,16 @@
 // expert's pairs in earlier chunks and the expert's offset gives the sorted
 // position.  The same pass emits the tile list used by the expert kernels:
 // each expert's rows cut into tiles of at most rows_per_tile.
-#include "moe_internal.h"
+#include "group_dev.h"
 
 namespace moeq4 {
 
-// Exclusive scan over the block (blockDim.x a multiple of 64, at most 1024).
-// Returns the exclusive prefix of v; *total receives the block sum.
-__device__ int block_exclusive_scan(int v, int *lds16, int *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const int n = __shfl_up(inc, o, WAVE);
-        if (lane >= o) inc += n;
-    }
-    if (lane == 63) lds16[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        int w = lane < nw ? lds16[lane] : 0;
-        int winc = w;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int n = __shfl_up(winc, o, WAVE);
-            if (lane >= o) winc += n;
-        }
-        if (lane < nw) lds16[lane] = winc - w;   // exclusive wave offsets
-        if (lane == nw - 1) lds16[16] = winc;    // block total
-    }
-    __syncthreads();
-    const int r = lds16[wave] + inc - v;
-    *total = lds16[16];
-    __syncthreads();
-    return r;
-}
-
-// Offsets + tile list from per-expert counts held by thread e (< E).
-__device__ void emit_offsets_and_tiles(int v, int E, int P, const GroupOut &g, int *lds16, int *excl_out) {
-    const int e = threadIdx.x;
-    int total;
-    const int excl = block_exclusive_scan(v, lds16, &total);
-    if (e < E) {
-        g.cnt[e] = v;
-        g.off[e] = excl;
-    }
-    if (e == 0) g.off[E] = P;
-    const int S = g.rows_per_tile;
-    const int nt = e < E ? (v + S - 1) / S : 0;
-    int ntot;
-    const int toff = block_exclusive_scan(nt, lds16, &ntot);
-    for (int j = 0; j < nt; ++j) {
-        Tile t;
-        t.expert = e;
-        t.row0 = excl + j * S;
-        t.rows = v - j * S < S ? v - j * S : S;
-        t.pad = 0;
-        g.tiles[toff + j] = t;
-    }
-    if (e == 0) *g.ntiles = ntot;
-    *excl_out = excl;
-}
-
-// Whole grouping in one block of 1024 threads (pairs P <= GROUP_SINGLE_MAX).
+// Whole grouping in one block of 1024 threads (pairs P <= GROUP_SINGLE_MAX);
+// optionally clears y (n floats) for the atomic accumulation that follows.
 __global__ __launch_bounds__(1024) void group_single_kernel(const int32_t *__restrict__ idx, int P, int E,
-                                                            GroupOut g) {
-    __shared__ int s_cnt[1024];
-    __shared__ int s_base[1024];
-    __shared__ unsigned long long s_mask[1024];
-    __shared__ int s_scan[17];
-    const int tid = threadIdx.x;
-    if (tid < E) s_cnt[tid] = 0;
-    __syncthreads();
-    for (int p = tid; p < P; p += blockDim.x) atomicAdd(&s_cnt[clamp_expert(idx[p], E)], 1);
-    __syncthreads();
-    int excl;
-    emit_offsets_and_tiles(tid < E ? s_cnt[tid] : 0, E, P, g, s_scan, &excl);
-    if (tid < E) s_base[tid] = excl;
-    for (int c0 = 0; c0 < P; c0 += GROUP_CHUNK) {
-        if (tid < E) s_mask[tid] = 0ull;
-        __syncthreads();
-        int e = 0;
-        const bool mine = tid < GROUP_CHUNK && c0 + tid < P;
-        if (mine) {
-            e = clamp_expert(idx[c0 + tid], E);
-            atomicOr(&s_mask[e], 1ull << tid);
-        }
-        __syncthreads();
-        if (mine) {
-            const int pos = s_base[e] + __popcll(s_mask[e] & ((1ull << tid) - 1ull));
-            g.perm[pos] = c0 + tid;
-            g.inv[c0 + tid] = pos;
-        }
-        __syncthreads();
-        if (tid < E) s_base[tid] += __popcll(s_mask[tid]);
-        __syncthreads();
-    }
+                                                            GroupOut g, float *__restrict__ yclear, int64_t n) {
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) yclear[i] = 0.f;
+    group_block_single(idx, P, E, g);
 }
 
 // Multi-block path, step 1: per-chunk expert counts.
@@ -118,30 +34,43 @@ __global__ __launch_bounds__(256) void group_count_kernel(const int32_t *__restr
     for (int e = tid; e < E; e += blockDim.x) chunk_cnt[(size_t)c * E + e] = __popcll(s_mask[e]);
 }
 
-// Step 2 (one block of 1024): per-expert running counts over chunks, offsets,
-// tiles, and each chunk's starting position for each expert.
-__global__ __launch_bounds__(1024) void group_scan_kernel(int nchunks, int P, int E, GroupOut g) {
+// Step 2: one block per expert; exclusive scan of the expert's counts over
+// the chunks (chunk order = pair order), written as each chunk's starting rank
+// inside the expert; the total goes to cnt[e].
+__global__ __launch_bounds__(1024) void group_colscan_kernel(int nchunks, int E, GroupOut g) {
     __shared__ int s_scan[17];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E)
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = g.chunk_cnt[(size_t)c * E + e];
-            g.chunk_base[(size_t)c * E + e] = run;
-            run += v;
-        }
-    int excl;
-    emit_offsets_and_tiles(e < E ? run : 0, E, P, g, s_scan, &excl);
-    if (e < E)
-        for (int c = 0; c < nchunks; ++c) g.chunk_base[(size_t)c * E + e] += excl;
+    const int e = blockIdx.x;
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += blockDim.x) {
+        const int c = c0 + threadIdx.x;
+        const int v = c < nchunks ? g.chunk_cnt[(size_t)c * E + e] : 0;
+        int total;
+        const int excl = block_exclusive_scan(v, s_scan, &total);
+        if (c < nchunks) g.chunk_base[(size_t)c * E + e] = carry + excl;
+        carry += total;
+    }
+    if (threadIdx.x == 0) g.cnt[e] = carry;
 }
 
-// Step 3: stable placement inside each chunk.
-__global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t *__restrict__ idx, int P, int E,
-                                                            GroupOut g) {
+// Step 3: stable placement inside each chunk.  Every block rebuilds the
+// expert offsets (exclusive scan of cnt, at most 1024 experts); block 0 also
+// publishes off[] and the tile list.
+__global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__restrict__ idx, int P, int E,
+                                                             GroupOut g) {
     __shared__ unsigned long long s_mask[1024];
+    __shared__ int s_off[1024];
+    __shared__ int s_scan[17];
     const int c = blockIdx.x, tid = threadIdx.x;
-    for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
+    const int v = tid < E ? g.cnt[tid] : 0;
+    if (tid < E) s_mask[tid] = 0ull;
+    int excl;
+    if (c == 0) {
+        emit_offsets_and_tiles(v, E, P, g, s_scan, &excl);
+    } else {
+        int total;
+        excl = block_exclusive_scan(v, s_scan, &total);
+    }
+    if (tid < E) s_off[tid] = excl;
     __syncthreads();
     const int p = c * GROUP_CHUNK + tid;
     const bool mine = tid < GROUP_CHUNK && p < P;
@@ -152,22 +81,25 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t *__res
     }
     __syncthreads();
     if (mine) {
-        const int pos = g.chunk_base[(size_t)c * E + e] + __popcll(s_mask[e] & ((1ull << tid) - 1ull));
+        const int pos = s_off[e] + g.chunk_base[(size_t)c * E + e] + __popcll(s_mask[e] & ((1ull << tid) - 1ull));
         g.perm[pos] = p;
         g.inv[p] = pos;
     }
 }
 
-hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s) {
+hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
+                        float *yclear, int64_t yclear_n) {
     const int P = (int)(T * k);
     if (P <= GROUP_SINGLE_MAX) {
-        hipLaunchKernelGGL(group_single_kernel, dim3(1), dim3(1024), 0, s, idx, P, E, g);
+        hipLaunchKernelGGL(group_single_kernel, dim3(1), dim3(1024), 0, s, idx, P, E, g, yclear, yclear_n);
         return hipGetLastError();
     }
+    if (yclear) return hipErrorInvalidValue;  // clearing is only offered on the one-block path
     const int nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
     hipLaunchKernelGGL(group_count_kernel, dim3(nch), dim3(256), 0, s, idx, P, E, g.chunk_cnt);
-    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, nch, P, E, g);
-    hipLaunchKernelGGL(group_scatter_kernel, dim3(nch), dim3(256), 0, s, idx, P, E, g);
+    hipLaunchKernelGGL(group_colscan_kernel, dim3(E), dim3(nch >= 1024 ? 1024 : ((nch + 63) / 64) * 64), 0, s,
+                       nch, E, g);
+    hipLaunchKernelGGL(group_scatter_kernel, dim3(nch), dim3(E > 64 ? ((E + 63) / 64) * 64 : 64), 0, s, idx, P, E, g);
     return hipGetLastError();
 }
 

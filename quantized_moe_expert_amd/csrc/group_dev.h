@@ -1,0 +1,102 @@
+// Device-side grouping helpers shared by the grouping kernels and the fused
+// decode routing kernel (see group.hip for the method).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moeq4 {
+
+// Exclusive scan over the block (blockDim.x a multiple of 64, at most 1024).
+// Returns the exclusive prefix of v; *total receives the block sum.
+__device__ inline int block_exclusive_scan(int v, int *lds16, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int n = __shfl_up(inc, o, WAVE);
+        if (lane >= o) inc += n;
+    }
+    if (lane == 63) lds16[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < nw ? lds16[lane] : 0;
+        int winc = w;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int n = __shfl_up(winc, o, WAVE);
+            if (lane >= o) winc += n;
+        }
+        if (lane < nw) lds16[lane] = winc - w;   // exclusive wave offsets
+        if (lane == nw - 1) lds16[16] = winc;    // block total
+    }
+    __syncthreads();
+    const int r = lds16[wave] + inc - v;
+    *total = lds16[16];
+    __syncthreads();
+    return r;
+}
+
+// Offsets + tile list from per-expert counts held by thread e (< E).
+__device__ inline void emit_offsets_and_tiles(int v, int E, int P, const GroupOut &g, int *lds16, int *excl_out) {
+    const int e = threadIdx.x;
+    int total;
+    const int excl = block_exclusive_scan(v, lds16, &total);
+    if (e < E) {
+        g.cnt[e] = v;
+        g.off[e] = excl;
+    }
+    if (e == 0) g.off[E] = P;
+    const int S = g.rows_per_tile;
+    const int nt = e < E ? (v + S - 1) / S : 0;
+    int ntot;
+    const int toff = block_exclusive_scan(nt, lds16, &ntot);
+    for (int j = 0; j < nt; ++j) {
+        Tile t;
+        t.expert = e;
+        t.row0 = excl + j * S;
+        t.rows = v - j * S < S ? v - j * S : S;
+        t.pad = 0;
+        g.tiles[toff + j] = t;
+    }
+    if (e == 0) *g.ntiles = ntot;
+    *excl_out = excl;
+}
+
+// Whole grouping by one block of 1024 threads (pairs P <= GROUP_SINGLE_MAX).
+// idx may have been written earlier by this same block (visible after a
+// __syncthreads()).
+__device__ inline void group_block_single(const int32_t *idx, int P, int E, const GroupOut &g) {
+    __shared__ int s_cnt[1024];
+    __shared__ int s_base[1024];
+    __shared__ unsigned long long s_mask[1024];
+    __shared__ int s_scan[17];
+    const int tid = threadIdx.x;
+    if (tid < E) s_cnt[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) atomicAdd(&s_cnt[clamp_expert(idx[p], E)], 1);
+    __syncthreads();
+    int excl;
+    emit_offsets_and_tiles(tid < E ? s_cnt[tid] : 0, E, P, g, s_scan, &excl);
+    if (tid < E) s_base[tid] = excl;
+    for (int c0 = 0; c0 < P; c0 += GROUP_CHUNK) {
+        if (tid < E) s_mask[tid] = 0ull;
+        __syncthreads();
+        int e = 0;
+        const bool mine = tid < GROUP_CHUNK && c0 + tid < P;
+        if (mine) {
+            e = clamp_expert(idx[c0 + tid], E);
+            atomicOr(&s_mask[e], 1ull << tid);
+        }
+        __syncthreads();
+        if (mine) {
+            const int pos = s_base[e] + __popcll(s_mask[e] & ((1ull << tid) - 1ull));
+            g.perm[pos] = c0 + tid;
+            g.inv[c0 + tid] = pos;
+        }
+        __syncthreads();
+        if (tid < E) s_base[tid] += __popcll(s_mask[tid]);
+        __syncthreads();
+    }
+}
+
+}  // namespace moeq4

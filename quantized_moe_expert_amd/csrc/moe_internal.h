@@ -45,11 +45,25 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
                                 int E, uint16_t *logits, hipStream_t s);
 hipError_t launch_topk(const uint16_t *logits, int64_t T, int E, int k, int32_t *idx, float *gate, hipStream_t s);
 
-hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s);
+// Grouping; on the one-block path (T*k <= GROUP_SINGLE_MAX) it can also clear
+// yclear[0..yclear_n).
+hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
+                        float *yclear = nullptr, int64_t yclear_n = 0);
 
+// Fused decode expert kernel (y must be cleared first).
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, float *h, float *o, float *y, hipStream_t s,
-                                 hipEvent_t const *ev);
+                                 const GroupOut &g, float *y, hipStream_t s);
+
+// Router logits (when wr != null), top-k and one-block grouping of T <= 64
+// tokens in one launch; clears y (T*H floats); with yres writes the residual
+// input bf16(x + yres) to xout.  counter: zero on entry, zero on exit.
+hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,
+                                     const float *bias, int T, int H, int E, int k, uint16_t *logits, int32_t *idx,
+                                     float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
+                                     hipStream_t s);
+
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
+hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, float *xsum, uint16_t *h, float *hsum, float *y,

@@ -362,6 +362,15 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
     return hipGetLastError();
 }
 
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n / 4 + 256) / 256)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
+    return launch_fill_zero(reinterpret_cast<float *>(p), n, s);  // all-zero bits either way
+}
+
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, float *xsum, uint16_t *h, float *hsum, float *y,
                                   hipStream_t s, hipEvent_t const *ev) {

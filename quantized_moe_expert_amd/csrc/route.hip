@@ -7,7 +7,7 @@
 // inputs of ordinary magnitude), plus an optional bias, rounded to float and
 // then to bf16.  Top-k and gates: the k largest logits, ties to the lower
 // expert index, gates = softmax over the selected logits.
-#include "moe_internal.h"
+#include "route_dev.h"
 
 namespace moeq4 {
 
@@ -52,48 +52,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     }
 }
 
-// One wave per token.  Each lane holds up to NPL logits (experts lane,
-// lane+64, ...) as 32-bit keys (order(value) << 16 | (0xffff - e)); k rounds of
-// wave-wide max pick the largest value and, among equal values, the lowest e.
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(const uint16_t *__restrict__ logits, int64_t T, int E,
                                                    int k, int32_t *__restrict__ idx, float *__restrict__ gate) {
-    const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const uint16_t *l = logits + t * E;
-    uint32_t key[NPL];
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        const int e = j * WAVE + lane;
-        key[j] = e < E ? (bf16_order(l[e]) << 16) | (0xffffu - (uint32_t)e) : 0u;
-    }
-    int my_e = -1;  // lane i < k keeps the i-th selected expert
-    for (int i = 0; i < k; ++i) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) m = key[j] > m ? key[j] : m;
-#pragma unroll
-        for (int o = WAVE / 2; o > 0; o >>= 1) {
-            const uint32_t other = __shfl_xor(m, o, WAVE);
-            m = other > m ? other : m;
-        }
-        const int e = (int)(0xffffu - (m & 0xffffu));
-        if (lane == i) my_e = e;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j)
-            if (j == (e >> 6) && (e & 63) == lane) key[j] = 0u;  // taken
-    }
-    // gates in double: exp(l_i - l_0) / sum_j exp(l_j - l_0)
-    const int e0 = __shfl(my_e, 0, WAVE);
-    const double l0 = (double)bf16_to_f32(l[e0]);
-    double ex = 0.0;
-    if (lane < k) ex = exp((double)bf16_to_f32(l[my_e]) - l0);
-    const double den = wave_sum_f64(ex);
-    if (lane < k) {
-        idx[t * k + lane] = my_e;
-        gate[t * k + lane] = (float)(ex / den);
-    }
+    topk_token_wave<NPL>(logits + t * E, E, k, idx + t * k, gate + t * k);
 }
 
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const float *bias, int64_t T, int H,

@@ -1,0 +1,82 @@
+// Device-side routing helpers shared by the routing kernels and the fused
+// decode routing kernel (see route.hip for the method).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moeq4 {
+
+// Dot product of bf16 row x and bf16 row w (H elements) by one wave, summed
+// in double; every bf16 x bf16 product is exact in double.  With yres != null
+// the activation is the residual step bf16(float(x) + yres) of a layer chain.
+__device__ inline double router_dot_wave(const uint16_t *__restrict__ x, const float *__restrict__ yres,
+                                         const uint16_t *__restrict__ w, int H) {
+    const int lane = threadIdx.x & 63;
+    double acc = 0.0;
+    for (int h = lane * 8; h < H; h += WAVE * 8) {
+        const uint4 xv = *reinterpret_cast<const uint4 *>(x + h);
+        const uint4 wv = *reinterpret_cast<const uint4 *>(w + h);
+        uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+        if (yres) {
+            const float4 ya = *reinterpret_cast<const float4 *>(yres + h);
+            const float4 yb = *reinterpret_cast<const float4 *>(yres + h + 4);
+            const float yv[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(xs[j] & 0xffffu) + yv[2 * j]);
+                const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(xs[j] >> 16) + yv[2 * j + 1]);
+                xs[j] = lo | (hi << 16);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc = fma((double)bf16_to_f32(xs[j] & 0xffffu), (double)bf16_to_f32(ws[j] & 0xffffu), acc);
+            acc = fma((double)bf16_to_f32(xs[j] >> 16), (double)bf16_to_f32(ws[j] >> 16), acc);
+        }
+    }
+    return wave_sum_f64(acc);
+}
+
+// Top-k of one token by one wave.  Each lane holds up to NPL logits (experts
+// lane, lane+64, ...) as 32-bit keys (order(value) << 16 | (0xffff - e)); k
+// rounds of wave-wide max pick the largest value and, among equal values, the
+// lowest e.  Gates in double: exp(l_i - l_0) / sum_j exp(l_j - l_0).
+template <int NPL>
+__device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, int k, int32_t *__restrict__ idx_out,
+                                float *__restrict__ gate_out) {
+    const int lane = threadIdx.x & 63;
+    uint32_t key[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int e = j * WAVE + lane;
+        key[j] = e < E ? (bf16_order(l[e]) << 16) | (0xffffu - (uint32_t)e) : 0u;
+    }
+    int my_e = -1;  // lane i < k keeps the i-th selected expert
+    for (int i = 0; i < k; ++i) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) m = key[j] > m ? key[j] : m;
+#pragma unroll
+        for (int o = WAVE / 2; o > 0; o >>= 1) {
+            const uint32_t other = __shfl_xor(m, o, WAVE);
+            m = other > m ? other : m;
+        }
+        const int e = (int)(0xffffu - (m & 0xffffu));
+        if (lane == i) my_e = e;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+            if (j == (e >> 6) && (e & 63) == lane) key[j] = 0u;  // taken
+    }
+    const int e0 = __shfl(my_e, 0, WAVE);
+    const double l0 = (double)bf16_to_f32(l[e0]);
+    double ex = 0.0;
+    if (lane < k) ex = exp((double)bf16_to_f32(l[my_e]) - l0);
+    const double den = wave_sum_f64(ex);
+    if (lane < k) {
+        idx_out[lane] = my_e;
+        gate_out[lane] = (float)(ex / den);
+    }
+}
+
+}  // namespace moeq4

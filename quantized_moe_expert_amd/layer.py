@@ -32,6 +32,9 @@ class MoeQ4Layer:
         kind = _lib.WS_DECODE if mode == "decode" else _lib.WS_PREFILL
         nbytes = max(_lib.workspace_size(kind, T, self.E, k, self.H, self.I), 256)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        fbytes = max(_lib.workspace_size(_lib.WS_FORWARD, T, self.E, k, self.H, self.I), 256)
+        self.ws_forward = torch.zeros(fbytes, dtype=torch.uint8, device=device)
+        _lib.moe_q4_workspace_init(self.ws_forward)
         self.logits = torch.empty((T, self.E), dtype=torch.int16, device=device)
         self.idx = torch.empty((T, k), dtype=torch.int32, device=device)
         self.gate = torch.empty((T, k), dtype=torch.float32, device=device)
@@ -54,6 +57,14 @@ class MoeQ4Layer:
         fn(x, idx, gate, T, self.k, self.struct, y, self.ws)
         return y
 
-    def forward(self, x, router_w=None, logits=None, bias=None):
-        _, idx, gate = self.route(x if router_w is not None else None, router_w, logits, bias, T=x.shape[0])
-        return self.experts(x, idx, gate)
+    def forward(self, x, router_w=None, logits=None, bias=None, residual_y=None, x_out=None):
+        """Whole layer through moe_q4_forward (decode path for <= 64 tokens,
+        prefill path above); ``logits`` are used when ``router_w`` is None."""
+        T = x.shape[0]
+        lg = self.logits[:T]
+        if router_w is None:
+            lg.copy_(logits)
+        y = self.y[:T]
+        _lib.moe_q4_forward(x, residual_y, x_out, router_w, bias, lg, T, self.k, self.struct, self.idx[:T],
+                            self.gate[:T], y, self.ws_forward)
+        return y

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -45,8 +45,8 @@ def test_workspace_sizes():
     d1 = m.workspace_size(m.WS_DECODE, 1, 256, 8, 2048, 512)
     d16 = m.workspace_size(m.WS_DECODE, 16, 256, 8, 2048, 512)
     assert 0 < d1 < d16
-    # decode keeps fp32 h and o per (token, slot)
-    assert d16 >= 16 * 8 * (512 + 2048) * 4
+    # decode keeps the grouping (counts, offsets, permutation, tiles) only
+    assert d16 >= 16 * 8 * 4 * 2
     p = m.workspace_size(m.WS_PREFILL, 4096, 256, 8, 2048, 512)
     assert p >= 4096 * 8 * 512 * 2          # f16 h
     assert m.workspace_size(m.WS_GROUP, 4096, 256, 8, 64, 64) >= 4096 * 8 * 4 * 2
@@ -118,6 +118,24 @@ def test_layer_validation():
         assert fn(FAKE, FAKE, FAKE, 4, 8, ctypes.byref(lay), FAKE, FAKE, 1 << 30, None, ev_null) == _lib.ERR_INVALID_ARG
         assert fn(FAKE, FAKE, FAKE, 4, 8, ctypes.byref(lay), FAKE, FAKE, 100, None, ev_ok) == _lib.ERR_WORKSPACE
         assert fn(FAKE, FAKE, FAKE, 0, 8, ctypes.byref(lay), FAKE, FAKE, 1 << 30, None, ev_ok) == _lib.OK
+
+
+def test_forward_validation():
+    L = m.lib()
+    lay = _layer()
+    f = lambda x=FAKE, ry=None, xo=None, lg=FAKE, T=4, k=8, ws=FAKE, nb=1 << 30, layer=lay: L.moe_q4_forward(
+        x, ry, xo, FAKE, None, lg, T, k, ctypes.byref(layer), FAKE, FAKE, FAKE, ws, nb, None)
+    assert f(x=None) == _lib.ERR_INVALID_ARG
+    assert f(lg=None) == _lib.ERR_INVALID_ARG
+    assert f(ry=FAKE, xo=None) == _lib.ERR_INVALID_ARG   # residual needs x_out
+    assert f(ws=None) == _lib.ERR_WORKSPACE
+    assert f(nb=64) == _lib.ERR_WORKSPACE
+    assert f(T=0) == _lib.OK
+    assert f(layer=_layer(fmt=3)) == _lib.ERR_UNSUPPORTED
+    assert f(T=500, layer=_layer(I=64)) == _lib.ERR_UNSUPPORTED  # prefill path shape rules
+    assert m.workspace_size(m.WS_FORWARD, 16, 256, 8, 2048, 512) >= 256
+    assert L.moe_q4_workspace_init(None, 0, None) == _lib.ERR_WORKSPACE
+    assert L.moe_q4_workspace_init(FAKE, 100, None) == _lib.ERR_WORKSPACE
 
 
 def test_dequant_and_residual_validation():
