@@ -201,17 +201,17 @@ MOE_Q4_API int moe_q4_forward(const void *x, const float *residual_y, void *x_ou
 MOE_Q4_API int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream);
 
 /*
- * Same as moe_q4_decode / moe_q4_prefill, and additionally records the
- * caller's HIP events (hipEvent_t handles, created by the caller) on `stream`
- * at the stage boundaries, so that each stage's kernel time can be read with
- * hipEventElapsedTime:
- *   decode:  [0] grouping + clear y [1] expert kernel (gate/up GEMV, SwiGLU,
- *            down GEMV slice, gate-weighted add into y) [2] [3] [4] (empty)
- *   prefill: [0] grouping [1] row sums + output clear [2] gate/up GEMM + SwiGLU
- *            [3] down GEMM + combine [4]
+ * Same as moe_q4_decode / moe_q4_prefill; additionally the caller's HIP
+ * events (hipEvent_t handles created by the caller) are recorded by the
+ * runtime at the start and end of the two main kernels (extended launch), so
+ * that hipEventElapsedTime gives exactly those kernels' durations:
+ *   decode:  events[0..1] the expert kernel (gate/up GEMV, SwiGLU, down GEMV
+ *            slice, gate-weighted add into y), events[2..3] the grouping kernel
+ *   prefill: events[0..1] the gate/up grouped GEMM + SwiGLU,
+ *            events[2..3] the down grouped GEMM + combine
  * events must point to MOE_Q4_STAGE_EVENTS valid events.
  */
-#define MOE_Q4_STAGE_EVENTS 5
+#define MOE_Q4_STAGE_EVENTS 4
 MOE_Q4_API int moe_q4_decode_timed(const void *x, const int32_t *topk_idx, const float *topk_gate,
                         int64_t T, int32_t k, const moe_q4_layer *w, float *y,
                         void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);

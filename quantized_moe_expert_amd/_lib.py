@@ -22,7 +22,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_decode", "moe_q4_prefill",
            "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_workspace_init",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string")
-STAGE_EVENTS = 5
+STAGE_EVENTS = 4
 
 
 class MoeQ4Error(RuntimeError):
@@ -166,7 +166,8 @@ def _timed(name, x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream):
 
 
 def moe_q4_decode_timed(x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream=None):
-    """moe_q4_decode that records the 5 given hipEvent_t handles at its stage boundaries."""
+    """moe_q4_decode that has the runtime record the 4 given hipEvent_t handles at the start and end
+    of its expert kernel ([0], [1]) and grouping kernel ([2], [3])."""
     _timed("moe_q4_decode_timed", x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream)
 
 

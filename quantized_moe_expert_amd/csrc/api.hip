@@ -93,6 +93,8 @@ DecodeWs carve_decode(Carver &c, int64_t T, int E, int k, int H, int I) {
 // the decode or prefill regions.
 constexpr size_t CONTROL_BYTES = 256;
 bool forward_uses_decode(int64_t T, int k) { return T <= 64 && T * k <= GROUP_SINGLE_MAX; }
+// One-launch routing also needs the T x E logits to fit the last workgroup's LDS.
+bool forward_fused_route(int64_t T, int E) { return T * E <= ROUTE_LDS_LOGITS; }
 
 struct PrefillWs {
     GroupOut g;
@@ -125,6 +127,7 @@ size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t
         case MOE_Q4_WS_PREFILL: carve_prefill(c, T, E, k, H, I); break;
         case MOE_Q4_WS_FORWARD:
             c.take<char>(CONTROL_BYTES);
+            c.take<unsigned int>(T * (int64_t)E);  // logit hand-off of the one-launch routing
             if (forward_uses_decode(T, k)) carve_decode(c, T, E, k, H, I);
             else carve_prefill(c, T, E, k, H, I);
             break;
@@ -190,28 +193,24 @@ static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, con
     Carver c{static_cast<char *>(ws)};
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
-    stage_mark(ev, 0, s);
     if (!prefill) {
         DecodeWs d = carve_decode(c, T, E, k, H, I);
         if (T * k <= GROUP_SINGLE_MAX) {
-            st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H));
+            st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H, ev ? ev[2] : nullptr,
+                                         ev ? ev[3] : nullptr));
         } else {
-            st = hip_status(launch_group(topk_idx, T, k, E, d.g, s));
+            st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, nullptr, 0, ev ? ev[2] : nullptr,
+                                         ev ? ev[3] : nullptr));
             if (!st) st = hip_status(launch_fill_zero(y, T * (int64_t)H, s));
         }
         if (st) return st;
-        stage_mark(ev, 1, s);
-        st = hip_status(launch_decode_experts(xb, topk_gate, T, k, L, d.g, y, s));
-        stage_mark(ev, 2, s);
-        stage_mark(ev, 3, s);
-        stage_mark(ev, 4, s);
-        return st;
+        return hip_status(launch_decode_experts(xb, topk_gate, T, k, L, d.g, y, s, ev ? ev[0] : nullptr,
+                                                ev ? ev[1] : nullptr));
     }
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(
-        launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.xsum, p.h, p.hsum, y, s, ev ? ev + 1 : nullptr));
+    return hip_status(launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.xsum, p.h, p.hsum, y, s, ev));
 }
 
 int moe_q4_decode(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
@@ -263,14 +262,24 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
     const LayerPtrs L = layer_ptrs(w);
     Carver c{static_cast<char *>(ws)};
     unsigned int *counter = c.take<unsigned int>(CONTROL_BYTES / sizeof(unsigned int));
+    unsigned int *handoff = c.take<unsigned int>(T * (int64_t)E);
     const uint16_t *xin = static_cast<const uint16_t *>(residual_y ? x_out : x);
     const uint16_t *wr = static_cast<const uint16_t *>(router_w);
     uint16_t *lg = static_cast<uint16_t *>(logits);
     if (dec) {
         DecodeWs d = carve_decode(c, T, E, k, H, I);
-        st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
-                                                  static_cast<uint16_t *>(x_out), wr, bias, (int)T, H, E, k, lg,
-                                                  topk_idx, topk_gate, d.g, y, counter, s));
+        if (forward_fused_route(T, E) || !wr) {
+            st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
+                                                      static_cast<uint16_t *>(x_out), wr, bias, (int)T, H, E, k, lg,
+                                                      topk_idx, topk_gate, d.g, y, counter, handoff, s));
+        } else {  // separate router, top-k and grouping launches
+            if (residual_y)
+                st = hip_status(launch_residual(static_cast<const uint16_t *>(x), residual_y, T * (int64_t)H,
+                                                static_cast<uint16_t *>(x_out), s));
+            if (!st) st = hip_status(launch_router_logits(xin, wr, bias, T, H, E, lg, s));
+            if (!st) st = hip_status(launch_topk(lg, T, E, k, topk_idx, topk_gate, s));
+            if (!st) st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H));
+        }
         if (st) return st;
         return hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, y, s));
     }

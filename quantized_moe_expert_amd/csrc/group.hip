@@ -88,10 +88,10 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
 }
 
 hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
-                        float *yclear, int64_t yclear_n) {
+                        float *yclear, int64_t yclear_n, hipEvent_t e0, hipEvent_t e1) {
     const int P = (int)(T * k);
     if (P <= GROUP_SINGLE_MAX) {
-        hipLaunchKernelGGL(group_single_kernel, dim3(1), dim3(1024), 0, s, idx, P, E, g, yclear, yclear_n);
+        launch_k(group_single_kernel, dim3(1), dim3(1024), s, e0, e1, idx, P, E, g, yclear, yclear_n);
         return hipGetLastError();
     }
     if (yclear) return hipErrorInvalidValue;  // clearing is only offered on the one-block path
@@ -99,7 +99,7 @@ hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const Group
     hipLaunchKernelGGL(group_count_kernel, dim3(nch), dim3(256), 0, s, idx, P, E, g.chunk_cnt);
     hipLaunchKernelGGL(group_colscan_kernel, dim3(E), dim3(nch >= 1024 ? 1024 : ((nch + 63) / 64) * 64), 0, s,
                        nch, E, g);
-    hipLaunchKernelGGL(group_scatter_kernel, dim3(nch), dim3(E > 64 ? ((E + 63) / 64) * 64 : 64), 0, s, idx, P, E, g);
+    launch_k(group_scatter_kernel, dim3(nch), dim3(E > 64 ? ((E + 63) / 64) * 64 : 64), s, e0, e1, idx, P, E, g);
     return hipGetLastError();
 }
 

@@ -86,6 +86,46 @@ __device__ __forceinline__ float seg_sum(float v) {
     return v;
 }
 
+// DPP-moved copy of v (lanes outside row_mask read 0).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                 0xf, false));
+}
+
+// Sum over aligned segments of W lanes with DPP moves only (no LDS).  For
+// W <= 16 every lane of the segment holds the sum; for W = 32 and 64 the last
+// lane of the segment does (lanes 31 / 63).
+template <int W>
+__device__ __forceinline__ float seg_sum_dpp(float v) {
+    if (W >= 2) v += dpp_f32<0xb1>(v);          // quad_perm [1,0,3,2]: lane ^ 1
+    if (W >= 4) v += dpp_f32<0x4e>(v);          // quad_perm [2,3,0,1]: lane ^ 2
+    if (W >= 8) v += dpp_f32<0x141>(v);         // row_half_mirror: 8-lane groups
+    if (W >= 16) v += dpp_f32<0x140>(v);        // row_mirror: 16-lane rows
+    if (W >= 32) v += dpp_f32<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
+    if (W >= 64) v += dpp_f32<0x143, 0xc>(v);   // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Whole-wave double sum with DPP moves; the result is valid in lane 63.
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+    v += dpp_f64<0xb1>(v);
+    v += dpp_f64<0x4e>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    v += dpp_f64<0x142, 0xa>(v);
+    v += dpp_f64<0x143, 0xc>(v);
+    return v;
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);

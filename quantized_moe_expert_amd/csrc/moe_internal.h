@@ -1,6 +1,8 @@
 // Internal launch interface between the C ABI (api.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "moe_common.h"
 
 namespace moeq4 {
@@ -23,8 +25,9 @@ struct LayerPtrs {
 
 constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chunk
 constexpr int GROUP_SINGLE_MAX = 1024;   // pairs handled by the one-block grouping
-constexpr int DECODE_TT = 4;             // tokens per decode work item
+constexpr int DECODE_TT = 2;             // tokens per decode work item
 constexpr int PREFILL_BM = 128;          // rows per prefill tile
+constexpr int ROUTE_LDS_LOGITS = 16384;  // T * E limit of the one-launch decode routing
 
 inline int64_t max_tiles(int64_t pairs, int E, int rows_per_tile) {
     return pairs / rows_per_tile + (pairs < E ? pairs : E) + 1;
@@ -48,11 +51,13 @@ hipError_t launch_topk(const uint16_t *logits, int64_t T, int E, int k, int32_t 
 // Grouping; on the one-block path (T*k <= GROUP_SINGLE_MAX) it can also clear
 // yclear[0..yclear_n).
 hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
-                        float *yclear = nullptr, int64_t yclear_n = 0);
+                        float *yclear = nullptr, int64_t yclear_n = 0, hipEvent_t e0 = nullptr,
+                        hipEvent_t e1 = nullptr);
 
 // Fused decode expert kernel (y must be cleared first).
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, float *y, hipStream_t s);
+                                 const GroupOut &g, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
+                                 hipEvent_t e1 = nullptr);
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64
 // tokens in one launch; clears y (T*H floats); with yres writes the residual
@@ -60,18 +65,23 @@ hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,
                                      const float *bias, int T, int H, int E, int k, uint16_t *logits, int32_t *idx,
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
-                                     hipStream_t s);
+                                     unsigned int *handoff, hipStream_t s);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, float *xsum, uint16_t *h, float *hsum, float *y,
-                                  hipStream_t s, hipEvent_t const *ev);
+                                  hipStream_t s, hipEvent_t const *ev = nullptr);
 
-// Records ev[i] on s when ev is not null (stage boundaries for timing).
-inline void stage_mark(hipEvent_t const *ev, int i, hipStream_t s) {
-    if (ev) (void)hipEventRecord(ev[i], s);
+// Launch on s; when e0 is given the runtime records e0 / e1 at the kernel's
+// own start and end (AMD extended launch), which times exactly that kernel.
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, Args... args) {
+    if (e0)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
 hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, hipStream_t s);

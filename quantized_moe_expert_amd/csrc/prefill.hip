@@ -343,7 +343,6 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
     constexpr int G = FMT == 0 ? 64 : 128;
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
-    stage_mark(ev, 0, s);
     {
         const int64_t n = T * (H / G);
         hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, T, H, G, xsum);
@@ -352,13 +351,12 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
         const int64_t n = T * (int64_t)H;
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n / 4 + 256) / 256)), dim3(256), 0, s, y, n);
     }
-    stage_mark(ev, 1, s);
-    hipLaunchKernelGGL((grouped_gemm_kernel<FMT, 1>), dim3(I / 128, (unsigned)tiles), dim3(PF_BLOCK), 0, s, x,
-                       xsum, H, I, k, L, g.tiles, g.ntiles, g.perm, gate, h, hsum, y);
-    stage_mark(ev, 2, s);
-    hipLaunchKernelGGL((grouped_gemm_kernel<FMT, 2>), dim3(H / 256, (unsigned)tiles), dim3(PF_BLOCK), 0, s, h,
-                       hsum, H, I, k, L, g.tiles, g.ntiles, g.perm, gate, h, hsum, y);
-    stage_mark(ev, 3, s);
+    launch_k(grouped_gemm_kernel<FMT, 1>, dim3(I / 128, (unsigned)tiles), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr,
+             ev ? ev[1] : nullptr, x, (const float *)xsum, H, I, k, L, (const Tile *)g.tiles,
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, hsum, y);
+    launch_k(grouped_gemm_kernel<FMT, 2>, dim3(H / 256, (unsigned)tiles), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr,
+             ev ? ev[3] : nullptr, (const uint16_t *)h, (const float *)hsum, H, I, k, L, (const Tile *)g.tiles,
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, hsum, y);
     return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 namespace moeq4 {
 
 // Dot product of bf16 row x and bf16 row w (H elements) by one wave, summed
-// in double; every bf16 x bf16 product is exact in double.  With yres != null
-// the activation is the residual step bf16(float(x) + yres) of a layer chain.
+// in double (every bf16 x bf16 product is exact in double); the result is
+// valid in lane 63.  With yres != null the activation is the residual step
+// bf16(float(x) + yres) of a layer chain.
 __device__ inline double router_dot_wave(const uint16_t *__restrict__ x, const float *__restrict__ yres,
                                          const uint16_t *__restrict__ w, int H) {
     const int lane = threadIdx.x & 63;
@@ -35,7 +36,7 @@ __device__ inline double router_dot_wave(const uint16_t *__restrict__ x, const f
             acc = fma((double)bf16_to_f32(xs[j] >> 16), (double)bf16_to_f32(ws[j] >> 16), acc);
         }
     }
-    return wave_sum_f64(acc);
+    return wave_sum_f64_dpp(acc);
 }
 
 // Top-k of one token by one wave.  Each lane holds up to NPL logits (experts

@@ -110,8 +110,8 @@ def test_layer_validation():
     assert _decode(_layer(), prefill=True, T=0) == _lib.OK
     # timed variants: events are required and must be non-NULL
     L = m.lib()
-    ev_null = (ctypes.c_void_p * 5)(FAKE, FAKE, None, FAKE, FAKE)
-    ev_ok = (ctypes.c_void_p * 5)(*([FAKE] * 5))
+    ev_null = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    ev_ok = (ctypes.c_void_p * 4)(*([FAKE] * 4))
     lay = _layer()
     for fn in (L.moe_q4_decode_timed, L.moe_q4_prefill_timed):
         assert fn(FAKE, FAKE, FAKE, 4, 8, ctypes.byref(lay), FAKE, FAKE, 1 << 30, None, None) == _lib.ERR_INVALID_ARG

@@ -358,3 +358,20 @@ def test_forward_residual_chain():
         r, a = assert_close(y.cpu().numpy(), yr, f"chain layer {l}")
         say(f"[chain] layer {l}: rel L2 {r:.2e} max abs {a:.2e}")
         x_prev, y_prev = x_l, yr
+
+
+@pytest.mark.parametrize("T,E,k", [(60, 300, 6), (3, 1000, 32)])
+def test_forward_wide_router(T, E, k):
+    """Decode-size forward where T x E exceeds the one-launch routing's LDS
+    (separate router, top-k and grouping launches) or uses many experts."""
+    H, I = 512, 256
+    say(f"[forward wide] T={T} E={E} k={k}")
+    lay = synth.random_layer(E, H, I, synth.FMT_ASYM_G64, seed=11, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 11, f"fw/x/{T}", "cuda"))
+    wr = synth.bf16_bits(synth.normal((E, H), 0.05, 11, f"fw/w/{E}", "cuda"))
+    lg, idx, gate, y, _, _ = _forward(lay, x, wr, None, T, k)
+    lr = oracle.router(np_u16(x), np_u16(wr), T, H, E)
+    ir, gr = oracle.topk(lr, T, E, k)
+    _check_route(lg, idx, gate, lr, ir, gr)
+    yr = oracle.experts(lay.fmt, E, H, I, *oracle.layer_np(lay), np_u16(x), ir, gr, T, k)
+    assert_close(y.cpu().numpy(), yr, f"forward wide T={T} E={E}")
