@@ -211,11 +211,10 @@ def main():
     proj_bytes = expert_bytes(lay0) // 3        # one projection of one expert (codes + scales)
     P = T * k
     if decode_path:
-        # dominant kernel: the fused expert kernel (stage 1): reads the gate, up and
-        # down codes and scales of every active expert once, the activations, and
-        # adds into y (fp32)
-        dom = "decode_experts_kernel"
-        alg_bytes = act * 3 * proj_bytes + T * H * 2 + T * H * 4
+        # dominant kernel: gate/up GEMV + SwiGLU: reads the gate and up codes and
+        # scales of every active expert once and the activations, writes h (fp32)
+        dom = "decode_gateup_kernel"
+        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 4
         achieved = alg_bytes / (stage_avg[0] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,

@@ -80,12 +80,13 @@ GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile) {
 
 struct DecodeWs {
     GroupOut g;
+    float *h;
 };
 DecodeWs carve_decode(Carver &c, int64_t T, int E, int k, int H, int I) {
     (void)H;
-    (void)I;
     DecodeWs d;
     d.g = carve_group(c, T, E, k, DECODE_TT);
+    d.h = c.take<float>(T * k * (int64_t)I);
     return d;
 }
 
@@ -204,7 +205,7 @@ static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, con
             if (!st) st = hip_status(launch_fill_zero(y, T * (int64_t)H, s));
         }
         if (st) return st;
-        return hip_status(launch_decode_experts(xb, topk_gate, T, k, L, d.g, y, s, ev ? ev[0] : nullptr,
+        return hip_status(launch_decode_experts(xb, topk_gate, T, k, L, d.g, d.h, y, s, ev ? ev[0] : nullptr,
                                                 ev ? ev[1] : nullptr));
     }
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
@@ -281,7 +282,7 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
             if (!st) st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H));
         }
         if (st) return st;
-        return hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, y, s));
+        return hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s));
     }
     if (residual_y) {
         st = hip_status(launch_residual(static_cast<const uint16_t *>(x), residual_y, T * (int64_t)H,

@@ -30,7 +30,6 @@
 
 namespace moeq4 {
 
-constexpr int DX_WAVES = 8;  // waves per expert workgroup
 
 // Activation chunk [32c, 32c+32) of a bf16 row in PERM8 order, and its sum.
 __device__ __forceinline__ void load_x_chunk(const uint16_t *__restrict__ xrow, int c, uint32_t xp[16],
@@ -105,72 +104,15 @@ __device__ __forceinline__ void group_params(uint32_t word, float &s, float &m) 
     m = FMT == 0 ? f16_to_f32((uint16_t)(word >> 16)) : -8.0f * s;
 }
 
-// grid.x = ntg * (I / CH) workgroups of DX_WAVES waves (ntg = tile slots, a
-// multiple of 8).  LPR = H / 32 lanes per gate/up row.  Every
-// weight load of both phases is issued before any arithmetic, so a workgroup
-// has all of its ~100 KB in flight at once.
-template <int LPR, int FMT, int CH>
-__global__ __launch_bounds__(DX_WAVES * 64) void decode_experts_kernel(
-    const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
-    int ntg, float *__restrict__ y) {
-    constexpr int RPW = WAVE / LPR;                                          // gate/up rows per wave-load
-    constexpr int GU = CH / DX_WAVES / RPW > 0 ? CH / DX_WAVES / RPW : 1;    // gate/up loads per lane
-    constexpr int G = FMT == 0 ? 64 : 128;
-    constexpr int DL = CH / 32;                                              // lanes per down row (1 or 2)
-    constexpr int DRW = WAVE / DL;                                           // down rows per wave-load
-    constexpr int DN = 2048 / (DX_WAVES * DRW);                              // down loads per lane (H <= 2048)
-    __shared__ float s_h[DECODE_TT][CH];
-    __shared__ int s_tok[DECODE_TT];
-    __shared__ float s_gate[DECODE_TT];
-
-    // Workgroups are dispatched round-robin over the 8 XCDs (bid mod 8).  The
-    // I / CH chunks of tile j get bids (j / 8) * 8 * nch + c * 8 + j % 8: one
-    // XCD, dispatched together, so they share that L2's lines of the down rows
-    // (each chunk reads only a CH/2-byte slice of every row).
-    const int nch = I / CH;
-    const int j = (blockIdx.x % 8) + 8 * (blockIdx.x / (8 * nch)), chunk = (blockIdx.x / 8) % nch;
-    if (j >= *ntiles) return;
-    const Tile tile = sane_tile(tiles[j], L.E, P);
-    const int e = tile.expert, nt = tile.rows;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = chunk * CH;
-
-    // ---- issue every weight load: gate/up rows of this chunk, down slices
-    const int c = lane % LPR, sub = lane / LPR;
-    const int half = DL == 2 ? (lane & 1) : 0, rr = lane / DL;
-    uint4 gv[GU], uv[GU], dv[DN];
-    uint32_t gs[GU], us[GU], ds[DN];
-    {
-        const size_t row_bytes = (size_t)H / 2;
-        const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
-        const int gi = (32 * c) / G;
-#pragma unroll
-        for (int b = 0; b < GU; ++b) {
-            const int nl = (b * DX_WAVES + wave) * RPW + sub;
-            const size_t row = (size_t)e * I + n0 + (nl < CH ? nl : 0);
-            gv[b] = *reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 16 * c);
-            uv[b] = *reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 16 * c);
-            gs[b] = load_group_word<FMT>(L.gsm + row * smr, gi);
-            us[b] = load_group_word<FMT>(L.usm + row * smr, gi);
-        }
-    }
-    {
-        const size_t row_bytes = (size_t)I / 2;
-        const size_t smr = (size_t)(I / G) * (FMT == 0 ? 2 : 1);
-        const int gi = n0 / G;
-#pragma unroll
-        for (int b = 0; b < DN; ++b) {
-            const int d = (b * DX_WAVES + wave) * DRW + rr;
-            const size_t row = (size_t)e * H + (d < H ? d : 0);
-            dv[b] = *reinterpret_cast<const uint4 *>(L.dq + row * row_bytes + n0 / 2 + 16 * half);
-            ds[b] = load_group_word<FMT>(L.dsm + row * smr, gi);
-        }
-    }
+// Tokens of a tile: token index and gate of each of its rows.
+__device__ __forceinline__ void tile_tokens(const Tile &tile, const int32_t *__restrict__ perm,
+                                            const float *__restrict__ topk_gate, int P, int k, int *s_tok,
+                                            float *s_gate) {
+    const int tid = threadIdx.x;
     if (tid < DECODE_TT) {
         int t = 0;
         float gt = 0.f;
-        if (tid < nt) {
+        if (tid < tile.rows) {
             int p = perm[tile.row0 + tid];
             p = p < 0 ? 0 : (p >= P ? P - 1 : p);
             t = p / k;
@@ -179,89 +121,200 @@ __global__ __launch_bounds__(DX_WAVES * 64) void decode_experts_kernel(
         s_tok[tid] = t;
         s_gate[tid] = gt;
     }
+}
+
+constexpr int DEC_WAVES = 4;  // waves per decode workgroup
+constexpr int DEC_NB = 2;     // row loads per lane per pipeline stage
+
+// gate/up GEMV + SwiGLU for rows [n0, n0 + RB) of one tile (one expert, up
+// to DECODE_TT tokens): h[row0 + u][n] in fp32.  Lanes run along the input
+// dimension (LPR = H / 32 lanes per row, 16 bytes = 32 codes each, a full row
+// per wave-load when H = 2048); every row is a contiguous 1 KB read.  Loads
+// of the next DEC_NB rows are in flight while the current ones are reduced.
+// grid.x = ntg * (I / RB), tile j = bid % ntg.
+template <int LPR, int FMT>
+__global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
+    const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
+    int ntg, int rb, float *__restrict__ h) {
+    constexpr int RPW = WAVE / LPR;  // rows per wave-load
+    constexpr int G = FMT == 0 ? 64 : 128;
+    __shared__ int s_tok[DECODE_TT];
+    __shared__ float s_gate[DECODE_TT];
+    const int j = blockIdx.x % ntg;
+    if (j >= *ntiles) return;
+    const Tile tile = sane_tile(tiles[j], L.E, P);
+    const int e = tile.expert, nt = tile.rows;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = (blockIdx.x / ntg) * rb;
+    const int c = lane % LPR, sub = lane / LPR;
+    tile_tokens(tile, perm, topk_gate, P, k, s_tok, s_gate);
     __syncthreads();
 
-    // ---- 1. gate/up rows [n0, n0 + CH) + SwiGLU -> s_h
-    {
-        uint32_t xp[DECODE_TT][16];
-        float xs[DECODE_TT];
+    uint32_t xp[DECODE_TT][16];
+    float xs[DECODE_TT];
 #pragma unroll
-        for (int u = 0; u < DECODE_TT; ++u) {
-            xs[u] = 0.f;
-            if (u < nt) load_x_chunk(x + (size_t)s_tok[u] * H, c, xp[u], xs[u]);
+    for (int u = 0; u < DECODE_TT; ++u) {
+        xs[u] = 0.f;
+        if (u < nt) load_x_chunk(x + (size_t)s_tok[u] * H, c, xp[u], xs[u]);
+    }
+    const size_t row_bytes = (size_t)H / 2;
+    const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
+    const int gi = (32 * c) / G;
+    const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);  // row loads per lane
+    auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
+    struct Stage {
+        uint4 g[DEC_NB], u[DEC_NB];
+        uint32_t gs[DEC_NB], us[DEC_NB];
+    };
+    auto issue = [&](Stage &st, int s0) {
+#pragma unroll
+        for (int b = 0; b < DEC_NB; ++b) {
+            const int nl = row_of(s0 + b);
+            const size_t row = (size_t)e * I + n0 + (nl < rb ? nl : 0);
+            st.g[b] = *reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 16 * c);
+            st.u[b] = *reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 16 * c);
+            st.gs[b] = load_group_word<FMT>(L.gsm + row * smr, gi);
+            st.us[b] = load_group_word<FMT>(L.usm + row * smr, gi);
         }
+    };
+    auto consume = [&](const Stage &st, int s0) {
 #pragma unroll
-        for (int b = 0; b < GU; ++b) {
-            const int nl = (b * DX_WAVES + wave) * RPW + sub;  // >= CH only when H is small
+        for (int b = 0; b < DEC_NB; ++b) {
+            const int nl = row_of(s0 + b);
             float sg, mg, su, mu;
-            group_params<FMT>(gs[b], sg, mg);
-            group_params<FMT>(us[b], su, mu);
+            group_params<FMT>(st.gs[b], sg, mg);
+            group_params<FMT>(st.us[b], su, mu);
             const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
             uint32_t gw[16], uw[16];
-            unpack32(gv[b], gw);
-            unpack32(uv[b], uw);
+            unpack32(st.g[b], gw);
+            unpack32(st.u[b], uw);
 #pragma unroll
             for (int u = 0; u < DECODE_TT; ++u) {
                 if (u < nt) {
                     const float pg = seg_sum_dpp<LPR>(fmaf(sg, dot16(gw, xp[u], 0.f), cg * xs[u]));
                     const float pu = seg_sum_dpp<LPR>(fmaf(su, dot16(uw, xp[u], 0.f), cu * xs[u]));
-                    if (c == LPR - 1 && nl < CH) s_h[u][nl] = silu(pg) * pu;
+                    if (c == LPR - 1 && nl < rb && s0 + b < steps)
+                        h[(size_t)(tile.row0 + u) * I + n0 + nl] = silu(pg) * pu;
                 }
+            }
+        }
+    };
+    // two register stages: the next DEC_NB rows load while the current ones are reduced
+    Stage sa, sb;
+    issue(sa, 0);
+    for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
+        if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
+        consume(sa, s0);
+        if (s0 + DEC_NB >= steps) break;
+        if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
+        consume(sb, s0 + DEC_NB);
+    }
+}
+
+// down GEMV for output rows [d0, d0 + RB) of one tile over the full inner
+// dimension (LPR = I / 32 lanes per row, a contiguous 256-byte row when
+// I = 512), multiplied by each token's gate and added into y (float atomics;
+// each output receives one add per routed (token, slot)).  h enters as bf16
+// hi + lo pairs.  grid.x = ntg * (H / RB), tile j = bid % ntg.
+template <int LPR, int FMT>
+__global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
+    int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
+    const int32_t *__restrict__ perm, const float *__restrict__ topk_gate, const float *__restrict__ h, int ntg,
+    int rb, float *__restrict__ y) {
+    constexpr int RPW = WAVE / LPR;
+    constexpr int G = FMT == 0 ? 64 : 128;
+    __shared__ int s_tok[DECODE_TT];
+    __shared__ float s_gate[DECODE_TT];
+    const int j = blockIdx.x % ntg;
+    if (j >= *ntiles) return;
+    const Tile tile = sane_tile(tiles[j], L.E, P);
+    const int e = tile.expert, nt = tile.rows;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int d0 = (blockIdx.x / ntg) * rb;
+    const int c = lane % LPR, sub = lane / LPR;
+    tile_tokens(tile, perm, topk_gate, P, k, s_tok, s_gate);
+    __syncthreads();
+
+    uint32_t hh[DECODE_TT][16], hl[DECODE_TT][16];
+    float hs[DECODE_TT];
+#pragma unroll
+    for (int u = 0; u < DECODE_TT; ++u) {
+        hs[u] = 0.f;
+        if (u < nt) {
+            const float4 *src = reinterpret_cast<const float4 *>(h + (size_t)(tile.row0 + u) * I + 32 * c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a = src[2 * q], b = src[2 * q + 1];
+                const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
+                    const uint32_t l0 = f32_to_bf16_rne(v[2 * p] - bf16_to_f32(h0));
+                    const uint32_t l1 = f32_to_bf16_rne(v[2 * p + 1] - bf16_to_f32(h1));
+                    hi[p] = h0 | (h1 << 16);
+                    lo[p] = l0 | (l1 << 16);
+                    hs[u] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+                }
+                perm8(hi[0], hi[1], hi[2], hi[3], hh[u][4 * q], hh[u][4 * q + 1], hh[u][4 * q + 2], hh[u][4 * q + 3]);
+                perm8(lo[0], lo[1], lo[2], lo[3], hl[u][4 * q], hl[u][4 * q + 1], hl[u][4 * q + 2], hl[u][4 * q + 3]);
             }
         }
     }
-    __syncthreads();
-
-    // ---- 2. down rows d, inputs [n0, n0 + CH): DL lanes per row
-    {
-        uint32_t hh[DECODE_TT][16], hl[DECODE_TT][16];
-        float hs[DECODE_TT];
+    const size_t row_bytes = (size_t)I / 2;
+    const size_t smr = (size_t)(I / G) * (FMT == 0 ? 2 : 1);
+    const int gi = (32 * c) / G;
+    const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);
+    auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
+    struct Stage {
+        uint4 v[DEC_NB];
+        uint32_t s[DEC_NB];
+    };
+    auto issue = [&](Stage &st, int s0) {
 #pragma unroll
-        for (int u = 0; u < DECODE_TT; ++u) {
-            hs[u] = 0.f;
-            if (u < nt) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t hi[4], lo[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const float v0 = s_h[u][32 * half + 8 * q + 2 * p], v1 = s_h[u][32 * half + 8 * q + 2 * p + 1];
-                        const uint32_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
-                        const uint32_t l0 = f32_to_bf16_rne(v0 - bf16_to_f32(h0));
-                        const uint32_t l1 = f32_to_bf16_rne(v1 - bf16_to_f32(h1));
-                        hi[p] = h0 | (h1 << 16);
-                        lo[p] = l0 | (l1 << 16);
-                        hs[u] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
-                    }
-                    perm8(hi[0], hi[1], hi[2], hi[3], hh[u][4 * q], hh[u][4 * q + 1], hh[u][4 * q + 2], hh[u][4 * q + 3]);
-                    perm8(lo[0], lo[1], lo[2], lo[3], hl[u][4 * q], hl[u][4 * q + 1], hl[u][4 * q + 2], hl[u][4 * q + 3]);
-                }
-            }
+        for (int b = 0; b < DEC_NB; ++b) {
+            const int dl = row_of(s0 + b);
+            const size_t row = (size_t)e * H + d0 + (dl < rb ? dl : 0);
+            st.v[b] = *reinterpret_cast<const uint4 *>(L.dq + row * row_bytes + 16 * c);
+            st.s[b] = load_group_word<FMT>(L.dsm + row * smr, gi);
         }
+    };
+    auto consume = [&](const Stage &st, int s0) {
 #pragma unroll
-        for (int b = 0; b < DN; ++b) {
-            const int d = (b * DX_WAVES + wave) * DRW + rr;
+        for (int b = 0; b < DEC_NB; ++b) {
+            const int dl = row_of(s0 + b);
             float sd, md;
-            group_params<FMT>(ds[b], sd, md);
+            group_params<FMT>(st.s[b], sd, md);
             const float cd = md - OFFSET_BF16 * sd;
             uint32_t dw[16];
-            unpack32(dv[b], dw);
+            unpack32(st.v[b], dw);
 #pragma unroll
             for (int u = 0; u < DECODE_TT; ++u) {
                 if (u < nt) {
                     float a = dot16(dw, hh[u], 0.f);
                     a = dot16(dw, hl[u], a);
-                    float part = fmaf(sd, a, cd * hs[u]);
-                    if (DL == 2) part = seg_sum_dpp<2>(part);
-                    if (half == 0 && d < H) unsafeAtomicAdd(y + (size_t)s_tok[u] * H + d, s_gate[u] * part);
+                    const float o = seg_sum_dpp<LPR>(fmaf(sd, a, cd * hs[u]));
+                    if (c == LPR - 1 && dl < rb && s0 + b < steps)
+                        unsafeAtomicAdd(y + (size_t)s_tok[u] * H + d0 + dl, s_gate[u] * o);
                 }
             }
         }
+    };
+    Stage sa, sb;
+    issue(sa, 0);
+    for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
+        if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
+        consume(sa, s0);
+        if (s0 + DEC_NB >= steps) break;
+        if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
+        consume(sb, s0 + DEC_NB);
     }
 }
 
-// Routing of a few tokens in one launch.  Workgroup e (16 waves) computes
-// the router logits of expert e, wave w taking tokens w, w + 16, ...  The
+// Routing of a few tokens in one launch.  Workgroup b (16 waves) computes
+// the router logits of experts [4 b, 4 b + 4) for every token; the tokens'
+// input rows are staged in LDS 16 at a time (formed once per workgroup).  The
 // logits travel to the workgroup that arrives last through agent-scope
 // relaxed atomic stores and loads (coherent across the XCDs' L2 caches) and a
 // counter in the workspace (zero between calls): each workgroup waits for its
@@ -281,6 +334,7 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     float *__restrict__ yclear, unsigned int *__restrict__ counter, unsigned int *__restrict__ handoff) {
     __shared__ int s_last;
     __shared__ uint16_t s_lg[ROUTE_LDS_LOGITS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[ROUTE_TC * 2048];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = gridDim.x;
     const int64_t n = (int64_t)T * H;
@@ -290,16 +344,71 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     }
     const uint16_t *lsrc = logits;
     if (wr) {
-        const int e = blockIdx.x;
-        const double b = bias ? (double)bias[e] : 0.0;
-        for (int t = wave; t < T; t += 16) {
-            const double acc = router_dot_wave(x + (size_t)t * H, yres ? yres + (size_t)t * H : nullptr,
-                                               wr + (size_t)e * H, H);
-            if (lane == 63) {
-                const uint16_t v = f32_to_bf16_rne((float)(acc + b));
-                logits[(size_t)t * E + e] = v;
-                __hip_atomic_store(handoff + (size_t)t * E + e, (unsigned int)v, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        // workgroup: experts [4 b, 4 b + 4); wave w: expert 4 b + (w & 3), token
+        // slots (w >> 2) + 4 i of each 16-token chunk staged in LDS (the
+        // residual input rows are formed once per workgroup)
+        const int e = blockIdx.x * 4 + (wave & 3);
+        const bool have = e < E;
+        double wd[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int hh = (q * WAVE + lane) * 8;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (have && hh < H) v = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                wd[q][2 * jj] = (double)bf16_to_f32(w4[jj] & 0xffffu);
+                wd[q][2 * jj + 1] = (double)bf16_to_f32(w4[jj] >> 16);
+            }
+        }
+        const double b = (have && bias) ? (double)bias[e] : 0.0;
+        for (int t0 = 0; t0 < T; t0 += ROUTE_TC) {
+            const int tc = T - t0 < ROUTE_TC ? T - t0 : ROUTE_TC;
+            __syncthreads();  // previous chunk consumed
+            for (int i = tid; i < tc * (H / 8); i += blockDim.x) {
+                const int tl = i / (H / 8), hh = (i % (H / 8)) * 8;
+                const size_t gi = (size_t)(t0 + tl) * H + hh;
+                uint4 v = *reinterpret_cast<const uint4 *>(x + gi);
+                if (yres) {
+                    const float4 ya = *reinterpret_cast<const float4 *>(yres + gi);
+                    const float4 yb = *reinterpret_cast<const float4 *>(yres + gi + 4);
+                    const float yv[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+                    uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(w4[jj] & 0xffffu) + yv[2 * jj]);
+                        const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(w4[jj] >> 16) + yv[2 * jj + 1]);
+                        w4[jj] = lo | (hi << 16);
+                    }
+                    v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                }
+                *reinterpret_cast<uint4 *>(&s_x[tl * H + hh]) = v;
+            }
+            __syncthreads();
+            for (int tl = wave >> 2; tl < tc; tl += 4) {
+                double acc = 0.0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int hh = (q * WAVE + lane) * 8;
+                    if (hh < H) {
+                        const uint4 xv = *reinterpret_cast<const uint4 *>(&s_x[tl * H + hh]);
+                        const uint32_t xs4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            acc = fma((double)bf16_to_f32(xs4[jj] & 0xffffu), wd[q][2 * jj], acc);
+                            acc = fma((double)bf16_to_f32(xs4[jj] >> 16), wd[q][2 * jj + 1], acc);
+                        }
+                    }
+                }
+                acc = wave_sum_f64_dpp(acc);
+                if (have && lane == 63) {
+                    const int t = t0 + tl;
+                    const uint16_t v = f32_to_bf16_rne((float)(acc + b));
+                    logits[(size_t)t * E + e] = v;
+                    __hip_atomic_store(handoff + (size_t)t * E + e, (unsigned int)v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
@@ -322,19 +431,28 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
 
 template <int FMT>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                     const GroupOut &g, float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                     const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
+                                     hipEvent_t e1) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
     const int64_t mt = max_tiles(P, L.E, DECODE_TT);
-    const int ntg = (int)((mt + 7) / 8 * 8);
-    // few tiles: 32-row chunks so that more workgroups stream the weights
-    const bool small = mt <= 48;
-    const int ch = small ? 32 : 64;
-    dim3 grid((unsigned)(ntg * (I / ch)));
-    switch ((H / 32) * (small ? 1 : -1)) {
+    const int ntg = (int)mt;
+    // rows per workgroup: enough workgroups to cover the chip (~1024) even for one token
+    int rb_gu = I, rb_dn = H;
+    while (rb_gu > 16 && ntg * (I / rb_gu) < 1024) rb_gu /= 2;
+    while (rb_dn > 64 && ntg * (H / rb_dn) < 1024) rb_dn /= 2;
+    dim3 grid_gu((unsigned)(ntg * (I / rb_gu))), grid_dn((unsigned)(ntg * (H / rb_dn)));
+    const dim3 block(DEC_WAVES * 64);
+    switch (H / 32) {
 #define CASE(LP) \
-    case LP: launch_k(decode_experts_kernel<LP, FMT, 32>, grid, dim3(DX_WAVES * 64), s, e0, e1, x, H, I, k, P, L, g.tiles, g.ntiles, g.perm, gate, ntg, y); break; \
-    case -LP: launch_k(decode_experts_kernel<LP, FMT, 64>, grid, dim3(DX_WAVES * 64), s, e0, e1, x, H, I, k, P, L, g.tiles, g.ntiles, g.perm, gate, ntg, y); break;
+    case LP: launch_k(decode_gateup_kernel<LP, FMT>, grid_gu, block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, ntg, rb_gu, h); break;
+        CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
+#undef CASE
+        default: return hipErrorInvalidValue;
+    }
+    switch (I / 32) {
+#define CASE(LP) \
+    case LP: launch_k(decode_down_kernel<LP, FMT>, grid_dn, block, s, nullptr, nullptr, H, I, k, P, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, (const float *)h, ntg, rb_dn, y); break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
         default: return hipErrorInvalidValue;
@@ -343,9 +461,10 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
 }
 
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    return L.fmt == 0 ? launch_experts_fmt<0>(x, gate, T, k, L, g, y, s, e0, e1)
-                      : launch_experts_fmt<1>(x, gate, T, k, L, g, y, s, e0, e1);
+                                 const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
+                                 hipEvent_t e1) {
+    return L.fmt == 0 ? launch_experts_fmt<0>(x, gate, T, k, L, g, h, y, s, e0, e1)
+                      : launch_experts_fmt<1>(x, gate, T, k, L, g, h, y, s, e0, e1);
 }
 
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,
@@ -353,7 +472,7 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
                                      unsigned int *handoff, hipStream_t s) {
     if (wr && T * E > ROUTE_LDS_LOGITS) return hipErrorInvalidValue;
-    const int nb = wr ? E : 1;
+    const int nb = wr ? (E + 3) / 4 : 1;
     const int npl = (E + 63) / 64;
 #define LAUNCH(N) \
     hipLaunchKernelGGL(decode_route_group_kernel<N>, dim3(nb), dim3(1024), 0, s, x, yres, xout, wr, bias, T, H, E, k, logits, idx, gate, g, yclear, counter, handoff)

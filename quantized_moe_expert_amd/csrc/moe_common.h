@@ -126,6 +126,23 @@ __device__ __forceinline__ double wave_sum_f64_dpp(double v) {
     return v;
 }
 
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Whole-wave unsigned max with DPP moves, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    uint32_t t;
+    t = dpp_u32<0xb1>(v); v = v > t ? v : t;
+    t = dpp_u32<0x4e>(v); v = v > t ? v : t;
+    t = dpp_u32<0x141>(v); v = v > t ? v : t;
+    t = dpp_u32<0x140>(v); v = v > t ? v : t;
+    t = dpp_u32<0x142, 0xa>(v); v = v > t ? v : t;
+    t = dpp_u32<0x143, 0xc>(v); v = v > t ? v : t;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);

@@ -28,6 +28,7 @@ constexpr int GROUP_SINGLE_MAX = 1024;   // pairs handled by the one-block group
 constexpr int DECODE_TT = 2;             // tokens per decode work item
 constexpr int PREFILL_BM = 128;          // rows per prefill tile
 constexpr int ROUTE_LDS_LOGITS = 16384;  // T * E limit of the one-launch decode routing
+constexpr int ROUTE_TC = 16;             // tokens staged per pass of the one-launch routing
 
 inline int64_t max_tiles(int64_t pairs, int E, int rows_per_tile) {
     return pairs / rows_per_tile + (pairs < E ? pairs : E) + 1;
@@ -54,9 +55,11 @@ hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const Group
                         float *yclear = nullptr, int64_t yclear_n = 0, hipEvent_t e0 = nullptr,
                         hipEvent_t e1 = nullptr);
 
-// Fused decode expert kernel (y must be cleared first).
+// Decode expert kernels: gate/up + SwiGLU -> h (fp32 [T*k][I]), then down
+// with the gate-weighted add into y (y must be cleared first).  e0 / e1 time
+// the gate/up kernel.
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
+                                 const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
                                  hipEvent_t e1 = nullptr);
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64

@@ -58,11 +58,7 @@ __device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, in
         uint32_t m = 0;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) m = key[j] > m ? key[j] : m;
-#pragma unroll
-        for (int o = WAVE / 2; o > 0; o >>= 1) {
-            const uint32_t other = __shfl_xor(m, o, WAVE);
-            m = other > m ? other : m;
-        }
+        m = wave_max_u32(m);
         const int e = (int)(0xffffu - (m & 0xffffu));
         if (lane == i) my_e = e;
 #pragma unroll
