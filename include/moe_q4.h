@@ -160,11 +160,14 @@ MOE_Q4_API int moe_q4_decode(const void *x, const int32_t *topk_idx, const float
 
 /*
  * Expert layer for many tokens (tuned for T >= 64): grouping, then grouped
- * GEMMs on the bf16/f16 matrix cores.  The int4 codes enter the products as
- * exact small integers and the per-group scale (and min) are applied to fp32
- * accumulators; h between the two products is rounded to f16, so |h| must
- * stay below 65504.  y (float [T][H]) is accumulated with float atomics: the
- * result can differ between runs in the last bits.  Same arguments as
+ * GEMMs on the f16 matrix cores with fp32 accumulation.  Each x row is scaled
+ * by a power of two and converted to f16 exactly (elements more than 2^31
+ * below the row's largest magnitude may round); weights are dequantised to
+ * f16 in registers with one rounding each (s q + m, or s (q - 8)), so a
+ * dequantised weight must stay below 65504 in magnitude; h between the two
+ * products is rounded to f16, so |h| must stay below 65504 too.  y (float
+ * [T][H]) is accumulated with float atomics: the result can differ between
+ * runs in the last bits.  Same arguments as
  * moe_q4_decode; ws >= moe_q4_workspace_size(MOE_Q4_WS_PREFILL, ...).
  */
 MOE_Q4_API int moe_q4_prefill(const void *x, const int32_t *topk_idx, const float *topk_gate,

@@ -99,16 +99,16 @@ bool forward_fused_route(int64_t T, int E) { return T * E <= ROUTE_LDS_LOGITS; }
 
 struct PrefillWs {
     GroupOut g;
-    float *xsum;
-    uint16_t *h;
-    float *hsum;
+    uint16_t *x16;   // x as f16 after the per-row power-of-two scale [T][H]
+    int32_t *xexp;   // that scale's exponent per token
+    uint16_t *h;     // SwiGLU output per sorted row, f16 [T*k][I]
 };
 PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
     PrefillWs p;
     p.g = carve_group(c, T, E, k, PREFILL_BM);
-    p.xsum = c.take<float>(T * (int64_t)(H / 64));      // sized for the smaller group (64)
+    p.x16 = c.take<uint16_t>(T * (int64_t)H);
+    p.xexp = c.take<int32_t>(T);
     p.h = c.take<uint16_t>(T * k * (int64_t)I);
-    p.hsum = c.take<float>(T * k * (int64_t)(I / 64));
     return p;
 }
 
@@ -211,7 +211,7 @@ static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, con
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.xsum, p.h, p.hsum, y, s, ev));
+    return hip_status(launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, y, s, ev));
 }
 
 int moe_q4_decode(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
@@ -298,7 +298,7 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.xsum, p.h, p.hsum, y, s, nullptr));
+    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, y, s, nullptr));
 }
 
 int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *out, moe_q4_stream stream) {
