@@ -34,13 +34,18 @@
  *     Faults inside kernels surface at the caller's next synchronisation.
  *   - T = 0 returns MOE_Q4_OK without launching anything.
  *   - bf16 and f16 tensors are passed as raw 16-bit patterns.
+ *   - x, y, x_out, residual_y and the packed code arrays must be 16-byte
+ *     aligned, the scale arrays 4-byte aligned; otherwise the call returns
+ *     MOE_Q4_ERR_INVALID_ARG.
  *   - Expert indices read from device memory are clamped into [0, E) by every
  *     kernel, so malformed indices give undefined numbers but stay in bounds.
  *
  * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 32), T * k < 2^31;
  * hidden H and inter I are powers of two in [64, 2048] and multiples of the
  * group (64 asym, 128 sym); moe_q4_prefill additionally needs I % 128 == 0
- * and H % 256 == 0.  Other shapes return MOE_Q4_ERR_UNSUPPORTED.
+ * and H % 256 == 0, T * H < 2^31 and T * k * I < 2^31 (so are the calls of
+ * moe_q4_forward that take the prefill path).  Other shapes return
+ * MOE_Q4_ERR_UNSUPPORTED.
  */
 #ifndef MOE_Q4_H
 #define MOE_Q4_H

@@ -32,8 +32,18 @@ int check_route_shape(int64_t T, int H, int E, int k) {
     return MOE_Q4_OK;
 }
 
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The prefill kernels address activations and weights with 32-bit offsets.
+bool prefill_fits(int64_t T, int k, int H, int I) {
+    return T * (int64_t)H < ((int64_t)1 << 31) && T * (int64_t)k * I < ((int64_t)1 << 31);
+}
+
 int check_layer(const moe_q4_layer *w, bool prefill) {
     if (!w || !w->gate_q || !w->up_q || !w->down_q || !w->gate_sm || !w->up_sm || !w->down_sm)
+        return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(w->gate_q, 16) || !aligned(w->up_q, 16) || !aligned(w->down_q, 16) || !aligned(w->gate_sm, 4) ||
+        !aligned(w->up_sm, 4) || !aligned(w->down_sm, 4))
         return MOE_Q4_ERR_INVALID_ARG;
     if (w->num_experts < 1 || w->hidden < 1 || w->inter < 1) return MOE_Q4_ERR_INVALID_ARG;
     if (w->format != MOE_Q4_ASYM_G64 && w->format != MOE_Q4_SYM_G128) return MOE_Q4_ERR_UNSUPPORTED;
@@ -182,6 +192,8 @@ static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, con
     st = check_route_shape(T, w->hidden, w->num_experts, k);
     if (st) return st;
     if (!x || !topk_idx || !topk_gate || !y) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16)) return MOE_Q4_ERR_INVALID_ARG;
+    if (prefill && !prefill_fits(T, k, w->hidden, w->inter)) return MOE_Q4_ERR_UNSUPPORTED;
     if (events)
         for (int i = 0; i < MOE_Q4_STAGE_EVENTS; ++i)
             if (!events[i]) return MOE_Q4_ERR_INVALID_ARG;
@@ -253,10 +265,12 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
     if (st) return st;
     if (!x || !logits || !topk_idx || !topk_gate || !y) return MOE_Q4_ERR_INVALID_ARG;
     if (residual_y && !x_out) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(x_out, 16) || !aligned(residual_y, 16))
+        return MOE_Q4_ERR_INVALID_ARG;
     if (T == 0) return MOE_Q4_OK;
     const int E = w->num_experts, H = w->hidden, I = w->inter;
     const bool dec = forward_uses_decode(T, k);
-    if (!dec && check_layer(w, true)) return MOE_Q4_ERR_UNSUPPORTED;
+    if (!dec && (check_layer(w, true) || !prefill_fits(T, k, H, I))) return MOE_Q4_ERR_UNSUPPORTED;
     const size_t need = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

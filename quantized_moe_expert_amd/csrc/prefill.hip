@@ -20,16 +20,21 @@
 //    these errors with random signs, about 2^-12 relative on an output).
 //    Per-group scales therefore never touch the fp32 accumulators.
 //
+// Layout of the f16 activations (x16, h): inside every group of 8 elements
+// the order is 0,4,1,5,2,6,3,7 (PERM8), the order in which a packed code
+// dword unpacks most cheaply, so a 16-byte fragment of either operand holds
+// the same 8 contraction indices.
+//
 // Tiles: 128 rows (one tile-list entry, <= 128 rows of one expert) x 256
-// weight rows per workgroup of 4 waves.  Wave w owns 32 columns in each of
+// weight rows per workgroup of 4 waves, two workgroups per CU.  Wave w owns 32 columns in each of
 // two N-subtiles (GEMM1: the gate rows and the up rows of the same 32 h
 // columns, so SwiGLU pairs in registers; GEMM2: two groups of 32 output
 // columns) for every M-subtile of 32 rows the tile uses; the main loop is
 // instantiated per M-subtile count, so ragged tiles issue neither the loads
 // nor the matrix-core work of their empty subtiles.  Both operands travel
 // global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4) through a
-// 4-stage ring of 64-element K-steps; the block's scale words are staged in
-// LDS once.
+// 3-stage ring of 64-element K-steps; each stage also carries the 256 scale
+// words of its group (one 4-byte direct-to-LDS load per thread).
 #include "moe_internal.h"
 
 namespace moeq4 {
@@ -42,7 +47,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // ------------------------------------------------------------ x -> f16
 //
 // One wave per row: e = floor(log2 max|x|) - 14 (0 for a zero row or one
-// holding inf / NaN), x16 = f16(x * 2^-e), xexp[t] = e.
+// holding inf / NaN), x16 = f16(x * 2^-e) in PERM8 order, xexp[t] = e.
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restrict__ x, int64_t T, int H,
                                                        uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -77,7 +82,9 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restric
             const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(w[q] >> 16), -e);
             o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
-        dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+        uint32_t p[4];
+        perm8(o[0], o[1], o[2], o[3], p[0], p[1], p[2], p[3]);
+        dst[i] = make_uint4(p[0], p[1], p[2], p[3]);
     }
     if (lane == 0) xexp[t] = e;
 }
@@ -93,19 +100,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 
 // ------------------------------------------------------------ weights
 //
-// Natural-order unpack: the 8 codes of a dword become four f16 pairs
-// (k0,k1) (k2,k3) (k4,k5) (k6,k7), each half exactly 1024 + q.
-__device__ __forceinline__ void unpack_natural_f16(uint32_t w, uint32_t out[4]) {
-    const uint32_t lo = w & 0x0f0f0f0fu;          // bytes: k0 k2 k4 k6
-    const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;   // bytes: k1 k3 k5 k7
-    const uint32_t c = 0x64646464u;               // high byte of f16 1024
-    // v_perm_b32: selector bytes 0-3 pick the second operand, 4-7 the first
-    const uint32_t t0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // k0 k1 k2 k3
-    const uint32_t t1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // k4 k5 k6 k7
-    out[0] = __builtin_amdgcn_perm(c, t0, 0x04010400u);
-    out[1] = __builtin_amdgcn_perm(c, t0, 0x04030402u);
-    out[2] = __builtin_amdgcn_perm(c, t1, 0x04010400u);
-    out[3] = __builtin_amdgcn_perm(c, t1, 0x04030402u);
+// PERM8 unpack: pair j (j = 0..3) of a code dword holds codes j and j + 4 as
+// the exact f16 values 1024 + q.
+__device__ __forceinline__ uint32_t unpack_pair_f16(uint32_t w, int j) {
+    return ((w >> (4 * j)) & 0x000f000fu) | 0x64006400u;
 }
 
 // Two weights from a pair of 1024 + q halves: s q + m (asym) or s (q - 8)
@@ -126,49 +124,59 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t v, half2_t s2, half2_t
 #define MOEQ4_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | (0x7 << 4))
 
 constexpr int KS = 64;       // contraction elements per pipeline stage
-constexpr int NST = 4;       // LDS ring stages
+constexpr int NST = 3;       // LDS ring stages
 constexpr int BROWS = 256;   // weight rows per workgroup (gate 128 + up 128, or 256 down rows)
 constexpr int A_BYTES = BM * KS * 2;            // 16 KB: 128 rows x 64 f16
 constexpr int B_BYTES = BROWS * KS / 2;         // 8 KB: 256 rows x 64 codes
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 24 KB
+constexpr int S_BYTES = BROWS * 4;              // 1 KB: one scale word per weight row
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
 constexpr int B_LOADS = B_BYTES / 16 / PF_BLOCK;  // 2 sixteen-byte loads per thread and stage
-constexpr int SM_PITCH = BROWS + 1;             // LDS pitch of the per-group scale rows
 
-// Per-block operand sources and LDS addresses used by the main loop.
+// Per-block operand sources used by the main loop.  Sources are a base that
+// is uniform over the wave plus a 32-bit per-thread byte offset.
 struct GemmCtx {
-    const uint8_t *a_src[4];   // this thread's A chunk source, one per 32-row subtile
-    const uint8_t *b_src[B_LOADS];
+    const uint8_t *a_base;
+    uint32_t a_off[4];               // A chunk of each 32-row subtile
+    const uint8_t *b_base[B_LOADS];
+    uint32_t b_off[B_LOADS];
+    const uint8_t *s_base;
+    uint32_t s_off;                  // scale entry of group 0 of weight row `tid`
+    uint32_t s_step;                 // bytes between groups: 4 (scale+min) or 2 (scale)
     uint8_t *ring;
-    const uint32_t *sm;        // [group][SM_PITCH] scale words
-    int brow[2];               // this lane's weight rows (block-local) of the two N-subtiles
-    int nk;                    // K-steps
+    int brow[2];                     // this lane's weight rows (block-local) of the two N-subtiles
+    uint32_t spar[2];                // sym: parity of the scale entry of group 0 of brow[ns]
+    int nk;                          // K-steps
 };
 
 // Barrier between the waves of the block that orders their LDS traffic
-// without waiting for outstanding direct-to-LDS loads (the waits above do
-// that, counted).
+// without waiting for outstanding direct-to-LDS loads (those waits are
+// counted explicitly).
 __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
 }
 
-// One thread's share of K-step `ks` into ring slot `slot`: MS A loads (one per
-// 32-row subtile in use) and B_LOADS B loads, 16 bytes each, lane-ordered.
+// One thread's share of K-step `ks` (group g) into ring slot `slot`: MS A
+// loads (one per 32-row subtile in use) and B_LOADS B loads of 16 bytes, and
+// the dword holding weight row tid's scale entry of group g, all lane-ordered.
 template <int MS>
-__device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int slot, int wave) {
+__device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int slot, int wave) {
     uint8_t *sa = c.ring + slot * STAGE_BYTES;
     uint8_t *sb = sa + A_BYTES;
+    uint8_t *ss = sb + B_BYTES;
 #pragma unroll
     for (int i = 0; i < MS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)(c.a_src[i] + (size_t)ks * (KS * 2)),
+        __builtin_amdgcn_global_load_lds((const void *)(c.a_base + (size_t)ks * (KS * 2) + c.a_off[i]),
                                          (__attribute__((address_space(3))) void *)(sa + (i * 4 + wave) * 1024),
                                          16, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)(c.b_src[i] + (size_t)ks * (KS / 2)),
+        __builtin_amdgcn_global_load_lds((const void *)(c.b_base[i] + (size_t)ks * (KS / 2) + c.b_off[i]),
                                          (__attribute__((address_space(3))) void *)(sb + (i * 4 + wave) * 1024),
                                          16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void *)(c.s_base + ((c.s_off + (uint32_t)g * c.s_step) & ~3u)),
+                                     (__attribute__((address_space(3))) void *)(ss + wave * 256), 4, 0, 0);
 }
 
 // Main loop over K for a tile of MS x 32 rows.
@@ -176,13 +184,13 @@ template <int FMT, int MS>
 __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2], int wave, int lane) {
     constexpr int G = FMT == 0 ? 64 : 128;
     constexpr int KPG = G / KS;
-    constexpr int LPS = MS + B_LOADS;  // loads per thread and stage
+    constexpr int LPS = MS + B_LOADS + 1;  // loads per thread and stage
     const int l32 = lane & 31, hf = lane >> 5;
     const int NK = c.nk;
 
 #pragma unroll
     for (int u = 0; u < NST - 1; ++u)
-        if (u < NK) issue_stage<MS>(c, u, u, wave);
+        if (u < NK) issue_stage<MS>(c, u, u / KPG, u, wave);
 
     half2_t s2[2], m2[2];
     for (int kk = 0; kk < NK; kk += NST) {
@@ -190,22 +198,26 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
         for (int u = 0; u < NST; ++u) {
             const int ks = kk + u;
             if (ks < NK) {
-                // K-step ks has landed once at most `later` younger stages are in flight
-                const int later = NK - 1 - ks < NST - 2 ? NK - 1 - ks : NST - 2;
-                if (later >= 2) MOEQ4_WAIT_VM_LDS(2 * LPS);
-                else if (later == 1) MOEQ4_WAIT_VM_LDS(LPS);
+                // K-step ks has landed once at most the next one is in flight
+                if (ks + 1 < NK) MOEQ4_WAIT_VM_LDS(LPS);
                 else MOEQ4_WAIT_VM_LDS(0);
-                lds_barrier();  // every wave's share of ks is in LDS; slot (u - 1) % NST is free
-                if (ks + NST - 1 < NK) issue_stage<MS>(c, ks + NST - 1, (u + NST - 1) % NST, wave);
+                lds_barrier();  // every wave's share of ks is in LDS; slot (u + NST - 1) % NST is free
+                if (ks + NST - 1 < NK) issue_stage<MS>(c, ks + NST - 1, (ks + NST - 1) / KPG, (u + NST - 1) % NST, wave);
                 const uint8_t *sa = c.ring + u * STAGE_BYTES;
                 const uint8_t *sb = sa + A_BYTES;
+                const uint32_t *ss = reinterpret_cast<const uint32_t *>(sb + B_BYTES);
                 if (ks % KPG == 0) {
-                    const int g = ks / KPG;
 #pragma unroll
                     for (int ns = 0; ns < 2; ++ns) {
-                        const uint32_t pw = c.sm[g * SM_PITCH + c.brow[ns]];
-                        s2[ns] = __builtin_bit_cast(half2_t, (pw & 0xffffu) * 0x10001u);
-                        m2[ns] = __builtin_bit_cast(half2_t, (pw >> 16) * 0x10001u);
+                        const uint32_t pw = ss[c.brow[ns]];
+                        if (FMT == 0) {
+                            s2[ns] = __builtin_bit_cast(half2_t, (pw & 0xffffu) * 0x10001u);
+                            m2[ns] = __builtin_bit_cast(half2_t, (pw >> 16) * 0x10001u);
+                        } else {
+                            const uint32_t h = ((c.spar[ns] + (uint32_t)(ks / KPG)) & 1u) ? pw >> 16 : pw & 0xffffu;
+                            s2[ns] = __builtin_bit_cast(half2_t, h * 0x10001u);
+                            m2[ns] = s2[ns];
+                        }
                     }
                 }
                 // B: 16 bytes (32 codes) of each of this lane's two weight rows
@@ -221,10 +233,10 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
 #pragma unroll
                     for (int ns = 0; ns < 2; ++ns) {
                         const uint32_t word = s == 0 ? bw[ns].x : s == 1 ? bw[ns].y : s == 2 ? bw[ns].z : bw[ns].w;
-                        uint32_t p[4];
-                        unpack_natural_f16(word, p);
-                        bv[ns] = u32x4_t{dequant_pair<FMT>(p[0], s2[ns], m2[ns]), dequant_pair<FMT>(p[1], s2[ns], m2[ns]),
-                                         dequant_pair<FMT>(p[2], s2[ns], m2[ns]), dequant_pair<FMT>(p[3], s2[ns], m2[ns])};
+                        bv[ns] = u32x4_t{dequant_pair<FMT>(unpack_pair_f16(word, 0), s2[ns], m2[ns]),
+                                         dequant_pair<FMT>(unpack_pair_f16(word, 1), s2[ns], m2[ns]),
+                                         dequant_pair<FMT>(unpack_pair_f16(word, 2), s2[ns], m2[ns]),
+                                         dequant_pair<FMT>(unpack_pair_f16(word, 3), s2[ns], m2[ns])};
                     }
                     const int ch = 4 * hf + s;  // logical 16-byte chunk of the A row
 #pragma unroll
@@ -255,14 +267,13 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
 // c ^ ((r >> 1) & 7) and B row rb (32 bytes) at c ^ ((rb >> 3) & 1), so that
 // the fragment reads of 16 lanes hit distinct LDS banks.
 template <int FMT, int STAGE>
-__global__ __launch_bounds__(PF_BLOCK) void grouped_gemm_kernel(
+__global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_gemm_kernel(
     const uint16_t *__restrict__ act,      // STAGE 1: x16 [T][H]; STAGE 2: h [P][I]
     const int32_t *__restrict__ xexp,      // STAGE 1: per-token exponent e
     int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
     uint16_t *__restrict__ h_out, float *__restrict__ y) {
     constexpr int G = FMT == 0 ? 64 : 128;
-    constexpr int NGMAX = 2048 / G;
 
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
     const int nwork = *ntiles * ncb;
@@ -281,7 +292,6 @@ __global__ __launch_bounds__(PF_BLOCK) void grouped_gemm_kernel(
     const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
 
     __shared__ __attribute__((aligned(16))) uint8_t s_ring[NST * STAGE_BYTES];
-    __shared__ uint32_t s_sm[NGMAX * SM_PITCH];
     __shared__ int s_tok[BM];
     __shared__ float s_rs[BM];  // STAGE 1: 2^e of the row's token; STAGE 2: the row's gate
 
@@ -296,29 +306,12 @@ __global__ __launch_bounds__(PF_BLOCK) void grouped_gemm_kernel(
         s_tok[tid] = t;
         s_rs[tid] = v;
     }
-    // scale words [g][weight row] into LDS
-    for (int i = tid; i < BROWS * NG; i += PF_BLOCK) {
-        const int rb = i / NG, g = i % NG;
-        size_t wrow;
-        const uint16_t *smb;
-        if (STAGE == 1) {
-            smb = rb < 128 ? L.gsm : L.usm;
-            wrow = (size_t)e * I + col_base + (rb & 127);
-        } else {
-            smb = L.dsm;
-            wrow = (size_t)e * H + col_base + rb;
-        }
-        uint32_t v;
-        if (FMT == 0) v = reinterpret_cast<const uint32_t *>(smb)[wrow * NG + g];
-        else v = smb[wrow * NG + g];
-        s_sm[g * SM_PITCH + rb] = v;
-    }
     __syncthreads();
 
     GemmCtx c;
     c.ring = s_ring;
-    c.sm = s_sm;
     c.nk = K / KS;
+    c.a_base = reinterpret_cast<const uint8_t *>(act);
     // A slot S = (i * 4 + wave) * 64 + lane (16 bytes): row S / 8 = 32 i + 8 wave + lane / 8,
     // stored chunk S % 8 holding logical chunk (S % 8) ^ ((row >> 1) & 7).
 #pragma unroll
@@ -326,25 +319,47 @@ __global__ __launch_bounds__(PF_BLOCK) void grouped_gemm_kernel(
         const int r = 32 * i + 8 * wave + (lane >> 3);
         const int ch = (lane & 7) ^ ((r >> 1) & 7);
         const int rr = r < rows ? r : 0;  // padding rows read row 0; their outputs are dropped
-        const uint16_t *rowp = STAGE == 1 ? act + (size_t)s_tok[rr] * H : act + (size_t)(row0 + rr) * I;
-        c.a_src[i] = reinterpret_cast<const uint8_t *>(rowp + 8 * ch);
+        const uint32_t arow = STAGE == 1 ? (uint32_t)s_tok[rr] * (uint32_t)H : (uint32_t)(row0 + rr) * (uint32_t)I;
+        c.a_off[i] = (arow + 8u * ch) * 2u;
     }
-    // B slot S: weight row S / 2, stored chunk S % 2 holding logical chunk (S % 2) ^ ((row >> 3) & 1)
-    {
-        const size_t row_bytes = (size_t)K / 2;
+    // B slot S: weight row rb = S / 2 (rows 0-127 gate, 128-255 up in GEMM1),
+    // stored chunk S % 2 holding logical chunk (S % 2) ^ ((rb >> 3) & 1).
+    const uint32_t row_bytes = (uint32_t)K / 2;
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-            const int S = (i * 4 + wave) * 64 + lane;
-            const int rb = S / 2, ch = (S % 2) ^ ((rb >> 3) & 1);
-            const uint8_t *base;
-            if (STAGE == 1) base = rb < 128 ? L.gq + ((size_t)e * I + col_base + rb) * row_bytes
-                                            : L.uq + ((size_t)e * I + col_base + rb - 128) * row_bytes;
-            else base = L.dq + ((size_t)e * H + col_base + rb) * row_bytes;
-            c.b_src[i] = base + 16 * ch;
+    for (int i = 0; i < B_LOADS; ++i) {
+        const int S = (i * 4 + wave) * 64 + lane;
+        const int rb = S / 2, ch = (S % 2) ^ ((rb >> 3) & 1);
+        uint32_t wrow;
+        if (STAGE == 1) {
+            c.b_base[i] = i == 0 ? L.gq : L.uq;  // slots of load 0 are rows 0-127, of load 1 rows 128-255
+            wrow = (uint32_t)e * I + col_base + (rb & 127);
+        } else {
+            c.b_base[i] = L.dq;
+            wrow = (uint32_t)e * H + col_base + rb;
         }
+        c.b_off[i] = wrow * row_bytes + 16u * ch;
+    }
+    // scale entries: thread tid covers weight row tid (waves 0-1 gate, 2-3 up in GEMM1)
+    {
+        const uint32_t esz = FMT == 0 ? 4u : 2u;
+        uint32_t wrow;
+        if (STAGE == 1) {
+            c.s_base = reinterpret_cast<const uint8_t *>(tid < 128 ? L.gsm : L.usm);
+            wrow = (uint32_t)e * I + col_base + (tid & 127);
+        } else {
+            c.s_base = reinterpret_cast<const uint8_t *>(L.dsm);
+            wrow = (uint32_t)e * H + col_base + tid;
+        }
+        c.s_off = wrow * (uint32_t)NG * esz;
+        c.s_step = esz;
     }
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) c.brow[ns] = STAGE == 1 ? ns * 128 + wave * 32 + l32 : wave * 64 + ns * 32 + l32;
+    for (int ns = 0; ns < 2; ++ns) {
+        c.brow[ns] = STAGE == 1 ? ns * 128 + wave * 32 + l32 : wave * 64 + ns * 32 + l32;
+        const uint32_t wrow = STAGE == 1 ? (uint32_t)e * I + col_base + (c.brow[ns] & 127)
+                                         : (uint32_t)e * H + col_base + c.brow[ns];
+        c.spar[ns] = (wrow * (uint32_t)NG) & 1u;
+    }
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -365,7 +380,7 @@ __global__ __launch_bounds__(PF_BLOCK) void grouped_gemm_kernel(
     // ---- epilogue.  Accumulator element r of lane (l32, hf) in M-subtile mi
     // is row 32 mi + 8 (r / 4) + 4 hf + (r % 4), column l32 of the subtile.
     if (STAGE == 1) {
-        // h tile [BM][128] f16 in LDS, then coalesced 16-byte stores.
+        // h tile [BM][128] f16 in LDS, then coalesced 16-byte stores in PERM8 order.
         uint16_t *s_h = reinterpret_cast<uint16_t *>(s_ring);
         constexpr int HP = 128 + 8;
 #pragma unroll
@@ -385,9 +400,12 @@ __global__ __launch_bounds__(PF_BLOCK) void grouped_gemm_kernel(
         __syncthreads();
         for (int i = tid; i < BM * 16; i += PF_BLOCK) {
             const int row = i / 16, cc = i % 16;
-            if (row < rows)
-                *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) =
-                    *reinterpret_cast<const uint4 *>(&s_h[row * HP + cc * 8]);
+            if (row < rows) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(&s_h[row * HP + cc * 8]);
+                uint4 o;
+                perm8(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
+                *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
+            }
         }
     } else {
 #pragma unroll

@@ -108,6 +108,17 @@ def test_layer_validation():
     assert _decode(_layer(H=128, I=128), prefill=True) == _lib.ERR_UNSUPPORTED  # and H % 256 == 0
     assert _decode(_layer(), prefill=True, ws_bytes=100) == _lib.ERR_WORKSPACE
     assert _decode(_layer(), prefill=True, T=0) == _lib.OK
+    # pointer alignment: codes and activations 16 bytes, scale arrays 4 bytes
+    lay = _layer()
+    lay.up_q = FAKE + 8
+    assert _decode(lay) == _lib.ERR_INVALID_ARG
+    lay = _layer()
+    lay.down_sm = FAKE + 2
+    assert _decode(lay, prefill=True) == _lib.ERR_INVALID_ARG
+    assert _decode(_layer(), x=FAKE + 4) == _lib.ERR_INVALID_ARG
+    # prefill offsets are 32-bit: T * H and T * k * I below 2^31
+    assert _decode(_layer(), prefill=True, T=1 << 20) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(H=256, I=2048), prefill=True, T=1 << 17, k=8) == _lib.ERR_UNSUPPORTED
     # timed variants: events are required and must be non-NULL
     L = m.lib()
     ev_null = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
@@ -133,6 +144,9 @@ def test_forward_validation():
     assert f(T=0) == _lib.OK
     assert f(layer=_layer(fmt=3)) == _lib.ERR_UNSUPPORTED
     assert f(T=500, layer=_layer(I=64)) == _lib.ERR_UNSUPPORTED  # prefill path shape rules
+    assert f(T=1 << 20) == _lib.ERR_UNSUPPORTED                  # prefill path 32-bit offsets
+    assert f(x=FAKE + 2) == _lib.ERR_INVALID_ARG                 # misaligned activations
+    assert f(ry=FAKE, xo=FAKE + 8) == _lib.ERR_INVALID_ARG
     assert m.workspace_size(m.WS_FORWARD, 16, 256, 8, 2048, 512) >= 256
     assert L.moe_q4_workspace_init(None, 0, None) == _lib.ERR_WORKSPACE
     assert L.moe_q4_workspace_init(FAKE, 100, None) == _lib.ERR_WORKSPACE
