@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/f16 matrix
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/f16 matrix (the prefill GEMMs run f16)
 METRIC = "MoE layer tokens/s; decode HBM GB/s, prefill MFMA TFLOPs (% of peak)"
 
 WORKLOADS = {
@@ -54,7 +54,67 @@ def parse():
     p.add_argument("--copies", type=int, default=40, help="address-distinct weight copies (decode)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device copy 3 times (HBM counter calibration) and exit")
     return p.parse_args()
+
+
+CSRC = os.path.join(ROOT, "quantized_moe_expert_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest(unit: str) -> str:
+    """sha256 over a kernel source file and the local headers it includes
+    (recursively), so a recorded counter figure can be matched to the code."""
+    import hashlib
+    import re
+    seen, todo = set(), [unit]
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        text = open(os.path.join(CSRC, f), encoding="utf-8").read()
+        todo += [h for h in re.findall(r'#include "([^"]+)"', text) if os.path.exists(os.path.join(CSRC, h))]
+    h = hashlib.sha256()
+    for f in sorted(seen):
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, workload: str, unit: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>.<workload>.traffic.md (FETCH_SIZE and WRITE_SIZE runs,
+    each scaled by the copy calibration), or None when there is none or the
+    kernel's source has changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path, encoding="utf-8"):
+        if ":" in line and line.startswith("- "):
+            key, val = line[2:].split(":", 1)
+            rec[key.strip()] = val.strip().strip("`")
+    if rec.get("source_digest") != source_digest(unit):
+        return None
+    try:
+        return int(float(rec["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device copy of known size: what FETCH_SIZE / WRITE_SIZE report
+    for it gives the scale of those counters on this GPU."""
+    import torch
+    n = 256 * 1024 * 1024
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
 def clone_layer(lay):
@@ -74,6 +134,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
 
@@ -196,7 +259,7 @@ def main():
     for per_step in ev_sets:
         step_profiled(per_step)
     torch.cuda.synchronize()
-    # [0]: the dominant kernel (decode expert kernel / prefill gate-up GEMM),
+    # [0]: the dominant kernel (decode gate/up GEMV / prefill gate-up GEMM),
     # [1]: the second kernel (grouping / prefill down GEMM); each is the span
     # between the events the runtime recorded at that kernel's start and end
     stage_ms = np.array([[evs[0].elapsed_time(evs[1]), evs[2].elapsed_time(evs[3])]
@@ -217,7 +280,8 @@ def main():
         alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 4
         achieved = alg_bytes / (stage_avg[0] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(dom, args.workload, "decode.hip"), "kernel": dom,
                 "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_bytes": int(alg_bytes),
                 "active_experts": int(act)}
     else:
@@ -229,12 +293,14 @@ def main():
             # weight-bandwidth-bound case: report against HBM
             gbs = (wbytes + T * H * 2 + P * I * 2) / (stage_avg[0] * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                    "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic("grouped_gemm_kernel_1", args.workload, "prefill.hip"), "kernel": dom,
                     "avg_us": round(float(stage_avg[0]) * 1e3, 3), "tflops": round(achieved, 2),
                     "active_experts": int(act)}
         else:
             roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": recorded_traffic("grouped_gemm_kernel_1", args.workload, "prefill.hip"),
                     "kernel": dom, "avg_us": round(float(stage_avg[0]) * 1e3, 3),
                     "algorithmic_flops": flops, "active_experts": int(act)}
     roof["second_kernel_us"] = round(float(stage_avg[1]) * 1e3, 3)
@@ -255,7 +321,7 @@ def main():
                              "I=512, int4 sym g128"}
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
            "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16", "data": "synthetic",
+           "dtype": "bf16" if decode_path else "f16", "data": "synthetic",
            "config": {"workload": names[args.workload], "tokens": T, "hidden": H, "experts": E, "top_k": k,
                       "inter": I, "layers_per_step": nl_per_step, "path": mode,
                       "format": "asym_g64" if case.fmt == synth.FMT_ASYM_G64 else "sym_g128"},

@@ -148,11 +148,14 @@ MOE_Q4_API int moe_q4_group(const int32_t *topk_idx, int64_t T, int32_t k, int32
                  void *ws, size_t ws_bytes, moe_q4_stream stream);
 
 /*
- * Expert layer for few tokens (tuned for T <= 64): grouping, then one kernel
- * of fused-dequant GEMVs over the active experts' packed nibbles: gate and
- * up with SwiGLU in fp32 for a 64-row chunk of h, then that chunk's slice of
- * the down GEMV, multiplied by the gate and added into y with float atomics
- * (y may differ between runs in the last bits).
+ * Expert layer for few tokens (tuned for T <= 64): grouping (which also
+ * clears y), then two kernels of fused-dequant GEMVs that stream the active
+ * experts' packed nibbles once: gate and up with SwiGLU in fp32 into h
+ * (workspace), then the down GEMV over full rows, multiplied by the gate and
+ * added into y with float atomics (y may differ between runs in the last
+ * bits).  Dequantisation is exact in fp32 (drama-q4 card, "What's
+ * quantized": scale and min per group of 64; drama-3-w4a16 card: scale per
+ * 128).
  *   x          bf16 [T][H]
  *   topk_idx   int32 [T][k], topk_gate float [T][k] (as from moe_q4_route)
  *   w          the layer (host struct holding device pointers)
@@ -213,8 +216,8 @@ MOE_Q4_API int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream st
  * events (hipEvent_t handles created by the caller) are recorded by the
  * runtime at the start and end of the two main kernels (extended launch), so
  * that hipEventElapsedTime gives exactly those kernels' durations:
- *   decode:  events[0..1] the expert kernel (gate/up GEMV, SwiGLU, down GEMV
- *            slice, gate-weighted add into y), events[2..3] the grouping kernel
+ *   decode:  events[0..1] the gate/up GEMV + SwiGLU kernel,
+ *            events[2..3] the grouping kernel
  *   prefill: events[0..1] the gate/up grouped GEMM + SwiGLU,
  *            events[2..3] the down grouped GEMM + combine
  * events must point to MOE_Q4_STAGE_EVENTS valid events.
