@@ -6,17 +6,18 @@
 // lane takes 16 bytes = 32 codes, consecutive lanes consecutive bytes), and
 // applied to every token routed to its expert.
 //
-// One kernel per layer does all expert work.  Workgroup (tile j, chunk c)
-// takes the <= 4 tokens of tile j (one expert e) and the 64 rows
-// [64c, 64c+64) of h:
-//   1. gate/up GEMV over those 64 rows (lanes along the input dimension, a
-//      segmented wave reduction per row), SwiGLU in registers, h chunk -> LDS;
-//   2. the matching split-K slice of the down GEMV: every output row d, the 64
-//      inputs of the chunk (two lanes per row), multiplied by the token's gate
-//      and added into y with float atomics (y is cleared beforehand).
-// So the down codes of an expert are read once in total, split over its
-// chunk workgroups; chunk workgroups of one tile are numbered to land on the
-// same XCD so that they share the L2 lines of the down rows.
+// Two kernels per layer do the expert work:
+//   1. gate/up GEMV + SwiGLU: every active expert's gate and up rows, applied
+//      to the tokens routed to it, h in fp32 (workspace);
+//   2. down GEMV over full rows of h, multiplied by each token's gate and
+//      added into y with float atomics (y is cleared by the routing kernel).
+// Both launch as many workgroups as the chip holds at once and cut the work
+// on the device, from the actual tile count, into that many items (tile,
+// row chunk), so a layer's expert work runs in one round.  Items are spread
+// XCD-locally (workgroup b runs on XCD b mod 8 and takes a contiguous range
+// of items), so the chunks of one tile and the tiles of one expert share an
+// L2.  Each item issues its first weight loads before it fetches token
+// indices and activations.
 //
 // Group arithmetic.  For a group of codes q_k with scale s and min m,
 //   sum_k a_k (s q_k + m) = s * sum_k a_k (OFF + q_k) + (m - OFF s) * sum_k a_k
@@ -25,6 +26,8 @@
 // dot-product instruction with fp32 accumulation.  h stays fp32 between the
 // two products: for the down slice it is split into bf16 hi + lo parts
 // (|h - hi - lo| <= 2^-17 |h|).
+#include <atomic>
+
 #include "group_dev.h"
 #include "route_dev.h"
 
@@ -42,29 +45,6 @@ __device__ __forceinline__ void load_x_chunk(const uint16_t *__restrict__ xrow, 
         perm8(v.x, v.y, v.z, v.w, xp[4 * j + 0], xp[4 * j + 1], xp[4 * j + 2], xp[4 * j + 3]);
         xs += bf16_pair_sum(v.x) + bf16_pair_sum(v.y) + bf16_pair_sum(v.z) + bf16_pair_sum(v.w);
     }
-}
-
-// Scale and min of group g of a row (sym: min = -8 scale).
-template <int FMT>
-__device__ __forceinline__ void load_group(const uint16_t *__restrict__ sm_row, int g, float &s, float &m) {
-    if (FMT == 0) {
-        const uint32_t p = *reinterpret_cast<const uint32_t *>(sm_row + 2 * g);
-        s = f16_to_f32((uint16_t)(p & 0xffffu));
-        m = f16_to_f32((uint16_t)(p >> 16));
-    } else {
-        s = f16_to_f32(sm_row[g]);
-        m = -8.0f * s;
-    }
-}
-
-// sum over the 32 codes of a dword quad (PERM8 order) against activations a.
-__device__ __forceinline__ float dot32(const uint4 w, const uint32_t a[16], float acc) {
-    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) acc = dot2_bf16(unpack_pair<MAGIC_BF16>(d[q], p), a[4 * q + p], acc);
-    return acc;
 }
 
 // Tile fields made safe to index with (a workspace that was never filled
@@ -104,211 +84,234 @@ __device__ __forceinline__ void group_params(uint32_t word, float &s, float &m) 
     m = FMT == 0 ? f16_to_f32((uint16_t)(word >> 16)) : -8.0f * s;
 }
 
-// Tokens of a tile: token index and gate of each of its rows.
-__device__ __forceinline__ void tile_tokens(const Tile &tile, const int32_t *__restrict__ perm,
-                                            const float *__restrict__ topk_gate, int P, int k, int *s_tok,
-                                            float *s_gate) {
-    const int tid = threadIdx.x;
-    if (tid < DECODE_TT) {
-        int t = 0;
-        float gt = 0.f;
-        if (tid < tile.rows) {
-            int p = perm[tile.row0 + tid];
-            p = p < 0 ? 0 : (p >= P ? P - 1 : p);
-            t = p / k;
-            gt = topk_gate[p];
-        }
-        s_tok[tid] = t;
-        s_gate[tid] = gt;
-    }
+// Work decomposition shared by the two GEMV kernels: nt tiles, each cut into
+// nch chunks of `rows` consecutive rows out of N (nch as large as the grid
+// allows, at most maxch; every chunk starts inside the N rows, the last one
+// may be shorter), items (tile, chunk) numbered tile-major and dealt to the
+// XCDs in contiguous ranges.  The grid is a multiple of 8.
+struct Items {
+    int nch, rows, items, first, stride, end;
+};
+__device__ __forceinline__ Items decode_items(int nt, int N, int maxch) {
+    Items it;
+    const int grid = gridDim.x;
+    maxch = maxch < 1 ? 1 : maxch;
+    int nch = nt > 0 ? grid / nt : 1;
+    nch = nch < 1 ? 1 : (nch > maxch ? maxch : nch);
+    it.rows = (N + nch - 1) / nch;
+    it.nch = (N + it.rows - 1) / it.rows;  // <= nch; chunk c starts at c * rows < N
+    it.items = nt * it.nch;
+    const int per = (it.items + 7) / 8;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    it.first = xcd * per + slot;
+    it.stride = grid / 8;
+    const int e = (xcd + 1) * per;
+    it.end = e < it.items ? e : it.items;
+    return it;
 }
 
 constexpr int DEC_WAVES = 4;  // waves per decode workgroup
 constexpr int DEC_NB = 2;     // row loads per lane per pipeline stage
 
-// gate/up GEMV + SwiGLU for rows [n0, n0 + RB) of one tile (one expert, up
-// to DECODE_TT tokens): h[row0 + u][n] in fp32.  Lanes run along the input
-// dimension (LPR = H / 32 lanes per row, 16 bytes = 32 codes each, a full row
-// per wave-load when H = 2048); every row is a contiguous 1 KB read.  Loads
-// of the next DEC_NB rows are in flight while the current ones are reduced.
-// grid.x = ntg * (I / RB), tile j = bid % ntg.
+// gate/up GEMV + SwiGLU for one item (tile: one expert, up to DECODE_TT
+// tokens; chunk: rows [n0, n0 + rb) of h): h[row0 + u][n] in fp32.  Lanes run
+// along the input dimension (LPR = H / 32 lanes per row, 16 bytes = 32 codes
+// each, a full row per wave-load when H = 2048); every row is a contiguous
+// 1 KB read.  Loads of the next DEC_NB rows are in flight while the current
+// ones are reduced.
 template <int LPR, int FMT>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
-    int ntg, int rb, float *__restrict__ h) {
+    const int32_t *__restrict__ ntiles, int max_nt, const int32_t *__restrict__ perm, float *__restrict__ h) {
     constexpr int RPW = WAVE / LPR;  // rows per wave-load
     constexpr int G = FMT == 0 ? 64 : 128;
-    __shared__ int s_tok[DECODE_TT];
-    __shared__ float s_gate[DECODE_TT];
-    const int j = blockIdx.x % ntg;
-    if (j >= *ntiles) return;
-    const Tile tile = sane_tile(tiles[j], L.E, P);
-    const int e = tile.expert, nt = tile.rows;
+    int nt_all = *ntiles;
+    nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
+    const Items it = decode_items(nt_all, I, I / (DEC_WAVES * RPW));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = (blockIdx.x / ntg) * rb;
     const int c = lane % LPR, sub = lane / LPR;
-    tile_tokens(tile, perm, topk_gate, P, k, s_tok, s_gate);
-    __syncthreads();
-
-    uint32_t xp[DECODE_TT][16];
-    float xs[DECODE_TT];
-#pragma unroll
-    for (int u = 0; u < DECODE_TT; ++u) {
-        xs[u] = 0.f;
-        if (u < nt) load_x_chunk(x + (size_t)s_tok[u] * H, c, xp[u], xs[u]);
-    }
     const size_t row_bytes = (size_t)H / 2;
     const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
     const int gi = (32 * c) / G;
-    const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);  // row loads per lane
-    auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
     struct Stage {
         uint4 g[DEC_NB], u[DEC_NB];
         uint32_t gs[DEC_NB], us[DEC_NB];
     };
-    auto issue = [&](Stage &st, int s0) {
+    for (int w = it.first; w < it.end; w += it.stride) {
+        const int j = w / it.nch, chunk = w % it.nch;
+        const Tile tile = sane_tile(tiles[j], L.E, P);
+        const int e = tile.expert, nt = tile.rows;
+        const int n0 = chunk * it.rows;
+        const int rb = I - n0 < it.rows ? I - n0 : it.rows;
+        if (rb <= 0) continue;
+        const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);  // row loads per lane
+        auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
+        auto issue = [&](Stage &st, int s0) {
 #pragma unroll
-        for (int b = 0; b < DEC_NB; ++b) {
-            const int nl = row_of(s0 + b);
-            const size_t row = (size_t)e * I + n0 + (nl < rb ? nl : 0);
-            st.g[b] = *reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 16 * c);
-            st.u[b] = *reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 16 * c);
-            st.gs[b] = load_group_word<FMT>(L.gsm + row * smr, gi);
-            st.us[b] = load_group_word<FMT>(L.usm + row * smr, gi);
-        }
-    };
-    auto consume = [&](const Stage &st, int s0) {
+            for (int b = 0; b < DEC_NB; ++b) {
+                const int nl = row_of(s0 + b);
+                const size_t row = (size_t)e * I + n0 + (nl < rb ? nl : 0);
+                st.g[b] = *reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 16 * c);
+                st.u[b] = *reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 16 * c);
+                st.gs[b] = load_group_word<FMT>(L.gsm + row * smr, gi);
+                st.us[b] = load_group_word<FMT>(L.usm + row * smr, gi);
+            }
+        };
+        // the first rows depend only on the tile: in flight before the tokens are known
+        Stage sa, sb;
+        issue(sa, 0);
+        uint32_t xp[DECODE_TT][16];
+        float xs[DECODE_TT];
 #pragma unroll
-        for (int b = 0; b < DEC_NB; ++b) {
-            const int nl = row_of(s0 + b);
-            float sg, mg, su, mu;
-            group_params<FMT>(st.gs[b], sg, mg);
-            group_params<FMT>(st.us[b], su, mu);
-            const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
-            uint32_t gw[16], uw[16];
-            unpack32(st.g[b], gw);
-            unpack32(st.u[b], uw);
-#pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) {
-                if (u < nt) {
-                    const float pg = seg_sum_dpp<LPR>(fmaf(sg, dot16(gw, xp[u], 0.f), cg * xs[u]));
-                    const float pu = seg_sum_dpp<LPR>(fmaf(su, dot16(uw, xp[u], 0.f), cu * xs[u]));
-                    if (c == LPR - 1 && nl < rb && s0 + b < steps)
-                        h[(size_t)(tile.row0 + u) * I + n0 + nl] = silu(pg) * pu;
-                }
+        for (int u = 0; u < DECODE_TT; ++u) {
+            xs[u] = 0.f;
+            if (u < nt) {
+                int p = perm[tile.row0 + u];
+                p = p < 0 ? 0 : (p >= P ? P - 1 : p);
+                load_x_chunk(x + (size_t)(p / k) * H, c, xp[u], xs[u]);
             }
         }
-    };
-    // two register stages: the next DEC_NB rows load while the current ones are reduced
-    Stage sa, sb;
-    issue(sa, 0);
-    for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
-        if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
-        consume(sa, s0);
-        if (s0 + DEC_NB >= steps) break;
-        if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
-        consume(sb, s0 + DEC_NB);
+        auto consume = [&](const Stage &st, int s0) {
+#pragma unroll
+            for (int b = 0; b < DEC_NB; ++b) {
+                const int nl = row_of(s0 + b);
+                float sg, mg, su, mu;
+                group_params<FMT>(st.gs[b], sg, mg);
+                group_params<FMT>(st.us[b], su, mu);
+                const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
+                uint32_t gw[16], uw[16];
+                unpack32(st.g[b], gw);
+                unpack32(st.u[b], uw);
+#pragma unroll
+                for (int u = 0; u < DECODE_TT; ++u) {
+                    if (u < nt) {
+                        const float pg = seg_sum_dpp<LPR>(fmaf(sg, dot16(gw, xp[u], 0.f), cg * xs[u]));
+                        const float pu = seg_sum_dpp<LPR>(fmaf(su, dot16(uw, xp[u], 0.f), cu * xs[u]));
+                        if (c == LPR - 1 && nl < rb && s0 + b < steps)
+                            h[(size_t)(tile.row0 + u) * I + n0 + nl] = silu(pg) * pu;
+                    }
+                }
+            }
+        };
+        // two register stages: the next DEC_NB rows load while the current ones are reduced
+        for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
+            if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
+            consume(sa, s0);
+            if (s0 + DEC_NB >= steps) break;
+            if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
+            consume(sb, s0 + DEC_NB);
+        }
     }
 }
 
-// down GEMV for output rows [d0, d0 + RB) of one tile over the full inner
-// dimension (LPR = I / 32 lanes per row, a contiguous 256-byte row when
-// I = 512), multiplied by each token's gate and added into y (float atomics;
-// each output receives one add per routed (token, slot)).  h enters as bf16
-// hi + lo pairs.  grid.x = ntg * (H / RB), tile j = bid % ntg.
+// down GEMV for one item (tile; chunk: output rows [d0, d0 + rb)) over the
+// full inner dimension (LPR = I / 32 lanes per row, a contiguous 256-byte row
+// when I = 512), multiplied by each token's gate and added into y (float
+// atomics; each output receives one add per routed (token, slot)).  h enters
+// as bf16 hi + lo pairs.
 template <int LPR, int FMT>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
-    const int32_t *__restrict__ perm, const float *__restrict__ topk_gate, const float *__restrict__ h, int ntg,
-    int rb, float *__restrict__ y) {
+    int max_nt, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate, const float *__restrict__ h,
+    float *__restrict__ y) {
     constexpr int RPW = WAVE / LPR;
     constexpr int G = FMT == 0 ? 64 : 128;
-    __shared__ int s_tok[DECODE_TT];
-    __shared__ float s_gate[DECODE_TT];
-    const int j = blockIdx.x % ntg;
-    if (j >= *ntiles) return;
-    const Tile tile = sane_tile(tiles[j], L.E, P);
-    const int e = tile.expert, nt = tile.rows;
+    int nt_all = *ntiles;
+    nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
+    const Items it = decode_items(nt_all, H, H / (DEC_WAVES * RPW));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int d0 = (blockIdx.x / ntg) * rb;
     const int c = lane % LPR, sub = lane / LPR;
-    tile_tokens(tile, perm, topk_gate, P, k, s_tok, s_gate);
-    __syncthreads();
-
-    uint32_t hh[DECODE_TT][16], hl[DECODE_TT][16];
-    float hs[DECODE_TT];
-#pragma unroll
-    for (int u = 0; u < DECODE_TT; ++u) {
-        hs[u] = 0.f;
-        if (u < nt) {
-            const float4 *src = reinterpret_cast<const float4 *>(h + (size_t)(tile.row0 + u) * I + 32 * c);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 a = src[2 * q], b = src[2 * q + 1];
-                const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
-                    const uint32_t l0 = f32_to_bf16_rne(v[2 * p] - bf16_to_f32(h0));
-                    const uint32_t l1 = f32_to_bf16_rne(v[2 * p + 1] - bf16_to_f32(h1));
-                    hi[p] = h0 | (h1 << 16);
-                    lo[p] = l0 | (l1 << 16);
-                    hs[u] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
-                }
-                perm8(hi[0], hi[1], hi[2], hi[3], hh[u][4 * q], hh[u][4 * q + 1], hh[u][4 * q + 2], hh[u][4 * q + 3]);
-                perm8(lo[0], lo[1], lo[2], lo[3], hl[u][4 * q], hl[u][4 * q + 1], hl[u][4 * q + 2], hl[u][4 * q + 3]);
-            }
-        }
-    }
     const size_t row_bytes = (size_t)I / 2;
     const size_t smr = (size_t)(I / G) * (FMT == 0 ? 2 : 1);
     const int gi = (32 * c) / G;
-    const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);
-    auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
     struct Stage {
         uint4 v[DEC_NB];
         uint32_t s[DEC_NB];
     };
-    auto issue = [&](Stage &st, int s0) {
+    for (int w = it.first; w < it.end; w += it.stride) {
+        const int j = w / it.nch, chunk = w % it.nch;
+        const Tile tile = sane_tile(tiles[j], L.E, P);
+        const int e = tile.expert, nt = tile.rows;
+        const int d0 = chunk * it.rows;
+        const int rb = H - d0 < it.rows ? H - d0 : it.rows;
+        if (rb <= 0) continue;
+        const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);
+        auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
+        auto issue = [&](Stage &st, int s0) {
 #pragma unroll
-        for (int b = 0; b < DEC_NB; ++b) {
-            const int dl = row_of(s0 + b);
-            const size_t row = (size_t)e * H + d0 + (dl < rb ? dl : 0);
-            st.v[b] = *reinterpret_cast<const uint4 *>(L.dq + row * row_bytes + 16 * c);
-            st.s[b] = load_group_word<FMT>(L.dsm + row * smr, gi);
-        }
-    };
-    auto consume = [&](const Stage &st, int s0) {
+            for (int b = 0; b < DEC_NB; ++b) {
+                const int dl = row_of(s0 + b);
+                const size_t row = (size_t)e * H + d0 + (dl < rb ? dl : 0);
+                st.v[b] = *reinterpret_cast<const uint4 *>(L.dq + row * row_bytes + 16 * c);
+                st.s[b] = load_group_word<FMT>(L.dsm + row * smr, gi);
+            }
+        };
+        Stage sa, sb;
+        issue(sa, 0);
+        int tok[DECODE_TT];
+        float gt[DECODE_TT];
+        uint32_t hh[DECODE_TT][16], hl[DECODE_TT][16];
+        float hs[DECODE_TT];
 #pragma unroll
-        for (int b = 0; b < DEC_NB; ++b) {
-            const int dl = row_of(s0 + b);
-            float sd, md;
-            group_params<FMT>(st.s[b], sd, md);
-            const float cd = md - OFFSET_BF16 * sd;
-            uint32_t dw[16];
-            unpack32(st.v[b], dw);
+        for (int u = 0; u < DECODE_TT; ++u) {
+            hs[u] = 0.f;
+            tok[u] = 0;
+            gt[u] = 0.f;
+            if (u < nt) {
+                int p = perm[tile.row0 + u];
+                p = p < 0 ? 0 : (p >= P ? P - 1 : p);
+                tok[u] = p / k;
+                gt[u] = topk_gate[p];
+                const float4 *src = reinterpret_cast<const float4 *>(h + (size_t)(tile.row0 + u) * I + 32 * c);
 #pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) {
-                if (u < nt) {
-                    float a = dot16(dw, hh[u], 0.f);
-                    a = dot16(dw, hl[u], a);
-                    const float o = seg_sum_dpp<LPR>(fmaf(sd, a, cd * hs[u]));
-                    if (c == LPR - 1 && dl < rb && s0 + b < steps)
-                        unsafeAtomicAdd(y + (size_t)s_tok[u] * H + d0 + dl, s_gate[u] * o);
+                for (int q = 0; q < 4; ++q) {
+                    const float4 a = src[2 * q], b = src[2 * q + 1];
+                    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) {
+                        const uint32_t h0 = f32_to_bf16_rne(v[2 * pp]), h1 = f32_to_bf16_rne(v[2 * pp + 1]);
+                        const uint32_t l0 = f32_to_bf16_rne(v[2 * pp] - bf16_to_f32(h0));
+                        const uint32_t l1 = f32_to_bf16_rne(v[2 * pp + 1] - bf16_to_f32(h1));
+                        hi[pp] = h0 | (h1 << 16);
+                        lo[pp] = l0 | (l1 << 16);
+                        hs[u] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+                    }
+                    perm8(hi[0], hi[1], hi[2], hi[3], hh[u][4 * q], hh[u][4 * q + 1], hh[u][4 * q + 2],
+                          hh[u][4 * q + 3]);
+                    perm8(lo[0], lo[1], lo[2], lo[3], hl[u][4 * q], hl[u][4 * q + 1], hl[u][4 * q + 2],
+                          hl[u][4 * q + 3]);
                 }
             }
         }
-    };
-    Stage sa, sb;
-    issue(sa, 0);
-    for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
-        if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
-        consume(sa, s0);
-        if (s0 + DEC_NB >= steps) break;
-        if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
-        consume(sb, s0 + DEC_NB);
+        auto consume = [&](const Stage &st, int s0) {
+#pragma unroll
+            for (int b = 0; b < DEC_NB; ++b) {
+                const int dl = row_of(s0 + b);
+                float sd, md;
+                group_params<FMT>(st.s[b], sd, md);
+                const float cd = md - OFFSET_BF16 * sd;
+                uint32_t dw[16];
+                unpack32(st.v[b], dw);
+#pragma unroll
+                for (int u = 0; u < DECODE_TT; ++u) {
+                    if (u < nt) {
+                        float a = dot16(dw, hh[u], 0.f);
+                        a = dot16(dw, hl[u], a);
+                        const float o = seg_sum_dpp<LPR>(fmaf(sd, a, cd * hs[u]));
+                        if (c == LPR - 1 && dl < rb && s0 + b < steps)
+                            unsafeAtomicAdd(y + (size_t)tok[u] * H + d0 + dl, gt[u] * o);
+                    }
+                }
+            }
+        };
+        for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
+            if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
+            consume(sa, s0);
+            if (s0 + DEC_NB >= steps) break;
+            if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
+            consume(sb, s0 + DEC_NB);
+        }
     }
 }
 
@@ -429,30 +432,53 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     if (tid == 0 && wr) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Workgroups of `kernel` (256 threads) the device holds at once, a multiple
+// of 8 (queried once per kernel and device).
+template <typename K>
+static int resident_grid(K kernel) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, DEC_WAVES * 64, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    v = per_cu * cus;
+    v = v < 8 ? 8 : v / 8 * 8;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
 template <int FMT>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
-    const int64_t mt = max_tiles(P, L.E, DECODE_TT);
-    const int ntg = (int)mt;
-    // rows per workgroup: enough workgroups to cover the chip (~1024) even for one token
-    int rb_gu = I, rb_dn = H;
-    while (rb_gu > 16 && ntg * (I / rb_gu) < 1024) rb_gu /= 2;
-    while (rb_dn > 64 && ntg * (H / rb_dn) < 1024) rb_dn /= 2;
-    dim3 grid_gu((unsigned)(ntg * (I / rb_gu))), grid_dn((unsigned)(ntg * (H / rb_dn)));
+    const int mt = (int)max_tiles(P, L.E, DECODE_TT);
     const dim3 block(DEC_WAVES * 64);
     switch (H / 32) {
-#define CASE(LP) \
-    case LP: launch_k(decode_gateup_kernel<LP, FMT>, grid_gu, block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, ntg, rb_gu, h); break;
+#define CASE(LP)                                                                                                 \
+    case LP: {                                                                                                   \
+        auto kern = decode_gateup_kernel<LP, FMT>;                                                               \
+        launch_k(kern, dim3(resident_grid(kern)), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,     \
+                 (const int32_t *)g.ntiles, mt, (const int32_t *)g.perm, h);                                     \
+    } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
     switch (I / 32) {
-#define CASE(LP) \
-    case LP: launch_k(decode_down_kernel<LP, FMT>, grid_dn, block, s, nullptr, nullptr, H, I, k, P, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, (const float *)h, ntg, rb_dn, y); break;
+#define CASE(LP)                                                                                                 \
+    case LP: {                                                                                                   \
+        auto kern = decode_down_kernel<LP, FMT>;                                                                 \
+        launch_k(kern, dim3(resident_grid(kern)), block, s, nullptr, nullptr, H, I, k, P, L,                     \
+                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, (const int32_t *)g.perm, gate,            \
+                 (const float *)h, y);                                                                           \
+    } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
         default: return hipErrorInvalidValue;
