@@ -151,9 +151,10 @@ MOE_Q4_API int moe_q4_group(const int32_t *topk_idx, int64_t T, int32_t k, int32
  * Expert layer for few tokens (tuned for T <= 64): grouping (which also
  * clears y), then two kernels of fused-dequant GEMVs that stream the active
  * experts' packed nibbles once: gate and up with SwiGLU in fp32 into h
- * (workspace), then the down GEMV over full rows, multiplied by the gate and
- * added into y with float atomics (y may differ between runs in the last
- * bits).  Dequantisation is exact in fp32 (drama-q4 card, "What's
+ * (workspace), then the down GEMV over full rows with h rounded to f16 (so
+ * |h| must stay below 65504), multiplied by the gate and added into y with
+ * float atomics (y may differ between runs in the last bits).  The group
+ * scale and min are applied exactly in fp32 (drama-q4 card, "What's
  * quantized": scale and min per group of 64; drama-3-w4a16 card: scale per
  * 128).
  *   x          bf16 [T][H]

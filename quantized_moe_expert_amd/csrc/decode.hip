@@ -21,11 +21,11 @@
 //
 // Group arithmetic.  For a group of codes q_k with scale s and min m,
 //   sum_k a_k (s q_k + m) = s * sum_k a_k (OFF + q_k) + (m - OFF s) * sum_k a_k
-// where OFF + q_k is the exact bf16 value a nibble unpacks to (OFF = 128);
-// symmetric groups use m = -8 s.  sum a (OFF + q) runs on the packed bf16
-// dot-product instruction with fp32 accumulation.  h stays fp32 between the
-// two products: for the down slice it is split into bf16 hi + lo parts
-// (|h - hi - lo| <= 2^-17 |h|).
+// where OFF + q_k is the exact 16-bit float value a nibble unpacks to;
+// symmetric groups use m = -8 s.  sum a (OFF + q) runs on the packed
+// dot-product instructions with fp32 accumulation: bf16 (OFF = 128) against
+// x in the gate/up GEMV, f16 (OFF = 1024) against h rounded to f16 in the
+// down GEMV (|h| must stay below 65504).
 #include <atomic>
 
 #include "group_dev.h"
@@ -113,12 +113,18 @@ __device__ __forceinline__ Items decode_items(int nt, int N, int maxch) {
 constexpr int DEC_WAVES = 4;  // waves per decode workgroup
 constexpr int DEC_NB = 2;     // row loads per lane per pipeline stage
 
+// Packed f16 dot product with fp32 accumulation.
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v_t, a), __builtin_bit_cast(half2v_t, b), c, false);
+}
+
 // gate/up GEMV + SwiGLU for one item (tile: one expert, up to DECODE_TT
 // tokens; chunk: rows [n0, n0 + rb) of h): h[row0 + u][n] in fp32.  Lanes run
-// along the input dimension (LPR = H / 32 lanes per row, 16 bytes = 32 codes
-// each, a full row per wave-load when H = 2048); every row is a contiguous
-// 1 KB read.  Loads of the next DEC_NB rows are in flight while the current
-// ones are reduced.
+// along the input dimension: LPR = H / 64 lanes per row, each lane 32 bytes =
+// 64 codes (one 64-group), so a wave-load covers RPW = 64 / LPR rows of gate
+// and of up (2 rows of 1 KB each when H = 2048).  The next wave-load is in
+// flight while the current one is reduced.
 template <int LPR, int FMT>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
@@ -132,10 +138,10 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const int c = lane % LPR, sub = lane / LPR;
     const size_t row_bytes = (size_t)H / 2;
     const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
-    const int gi = (32 * c) / G;
+    const int gi = (64 * c) / G;
     struct Stage {
-        uint4 g[DEC_NB], u[DEC_NB];
-        uint32_t gs[DEC_NB], us[DEC_NB];
+        uint4 g[2], u[2];
+        uint32_t gs, us;
     };
     for (int w = it.first; w < it.end; w += it.stride) {
         const int j = w / it.nch, chunk = w % it.nch;
@@ -144,23 +150,24 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
         const int n0 = chunk * it.rows;
         const int rb = I - n0 < it.rows ? I - n0 : it.rows;
         if (rb <= 0) continue;
-        const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);  // row loads per lane
+        const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);  // wave-loads per wave
         auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
-        auto issue = [&](Stage &st, int s0) {
-#pragma unroll
-            for (int b = 0; b < DEC_NB; ++b) {
-                const int nl = row_of(s0 + b);
-                const size_t row = (size_t)e * I + n0 + (nl < rb ? nl : 0);
-                st.g[b] = *reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 16 * c);
-                st.u[b] = *reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 16 * c);
-                st.gs[b] = load_group_word<FMT>(L.gsm + row * smr, gi);
-                st.us[b] = load_group_word<FMT>(L.usm + row * smr, gi);
-            }
+        auto issue = [&](Stage &st, int s) {
+            const int nl = row_of(s);
+            const size_t row = (size_t)e * I + n0 + (nl < rb ? nl : 0);
+            const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 32 * c);
+            const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 32 * c);
+            st.g[0] = gp[0];
+            st.g[1] = gp[1];
+            st.u[0] = up[0];
+            st.u[1] = up[1];
+            st.gs = load_group_word<FMT>(L.gsm + row * smr, gi);
+            st.us = load_group_word<FMT>(L.usm + row * smr, gi);
         };
         // the first rows depend only on the tile: in flight before the tokens are known
         Stage sa, sb;
         issue(sa, 0);
-        uint32_t xp[DECODE_TT][16];
+        uint32_t xp[DECODE_TT][32];
         float xs[DECODE_TT];
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
@@ -168,38 +175,52 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
             if (u < nt) {
                 int p = perm[tile.row0 + u];
                 p = p < 0 ? 0 : (p >= P ? P - 1 : p);
-                load_x_chunk(x + (size_t)(p / k) * H, c, xp[u], xs[u]);
+                const uint16_t *xrow = x + (size_t)(p / k) * H;
+                float s0, s1;
+                load_x_chunk(xrow, 2 * c, xp[u], s0);
+                load_x_chunk(xrow, 2 * c + 1, xp[u] + 16, s1);
+                xs[u] = s0 + s1;
             }
         }
-        auto consume = [&](const Stage &st, int s0) {
+        auto consume = [&](const Stage &st, int s) {
+            const int nl = row_of(s);
+            float sg, mg, su, mu;
+            group_params<FMT>(st.gs, sg, mg);
+            group_params<FMT>(st.us, su, mu);
+            const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
+            // one code quad unpacked at a time, applied to every token of the tile
+            float dg[DECODE_TT], du[DECODE_TT];
 #pragma unroll
-            for (int b = 0; b < DEC_NB; ++b) {
-                const int nl = row_of(s0 + b);
-                float sg, mg, su, mu;
-                group_params<FMT>(st.gs[b], sg, mg);
-                group_params<FMT>(st.us[b], su, mu);
-                const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
-                uint32_t gw[16], uw[16];
-                unpack32(st.g[b], gw);
-                unpack32(st.u[b], uw);
+            for (int u = 0; u < DECODE_TT; ++u) dg[u] = du[u] = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t wq[16];
+                unpack32(q == 0 ? st.g[0] : q == 1 ? st.g[1] : q == 2 ? st.u[0] : st.u[1], wq);
 #pragma unroll
                 for (int u = 0; u < DECODE_TT; ++u) {
                     if (u < nt) {
-                        const float pg = seg_sum_dpp<LPR>(fmaf(sg, dot16(gw, xp[u], 0.f), cg * xs[u]));
-                        const float pu = seg_sum_dpp<LPR>(fmaf(su, dot16(uw, xp[u], 0.f), cu * xs[u]));
-                        if (c == LPR - 1 && nl < rb && s0 + b < steps)
-                            h[(size_t)(tile.row0 + u) * I + n0 + nl] = silu(pg) * pu;
+                        if (q < 2) dg[u] = dot16(wq, xp[u] + 16 * (q & 1), dg[u]);
+                        else du[u] = dot16(wq, xp[u] + 16 * (q & 1), du[u]);
                     }
                 }
             }
+#pragma unroll
+            for (int u = 0; u < DECODE_TT; ++u) {
+                if (u < nt) {
+                    const float pg = seg_sum_dpp<LPR>(fmaf(sg, dg[u], cg * xs[u]));
+                    const float pu = seg_sum_dpp<LPR>(fmaf(su, du[u], cu * xs[u]));
+                    if (c == LPR - 1 && nl < rb)
+                        h[(size_t)(tile.row0 + u) * I + n0 + nl] = silu(pg) * pu;
+                }
+            }
         };
-        // two register stages: the next DEC_NB rows load while the current ones are reduced
-        for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
-            if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
-            consume(sa, s0);
-            if (s0 + DEC_NB >= steps) break;
-            if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
-            consume(sb, s0 + DEC_NB);
+        // two register stages: the next wave-load is in flight while the current one is reduced
+        for (int s = 0; s < steps; s += 2) {
+            if (s + 1 < steps) issue(sb, s + 1);
+            consume(sa, s);
+            if (s + 1 >= steps) break;
+            if (s + 2 < steps) issue(sa, s + 2);
+            consume(sb, s + 1);
         }
     }
 }
@@ -208,7 +229,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
 // full inner dimension (LPR = I / 32 lanes per row, a contiguous 256-byte row
 // when I = 512), multiplied by each token's gate and added into y (float
 // atomics; each output receives one add per routed (token, slot)).  h enters
-// as bf16 hi + lo pairs.
+// rounded to f16.
 template <int LPR, int FMT>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
@@ -250,7 +271,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         issue(sa, 0);
         int tok[DECODE_TT];
         float gt[DECODE_TT];
-        uint32_t hh[DECODE_TT][16], hl[DECODE_TT][16];
+        uint32_t hp[DECODE_TT][16];
         float hs[DECODE_TT];
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
@@ -267,20 +288,16 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const float4 a = src[2 * q], b = src[2 * q + 1];
                     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                    uint32_t hi[4], lo[4];
+                    uint32_t pr[4];
 #pragma unroll
                     for (int pp = 0; pp < 4; ++pp) {
-                        const uint32_t h0 = f32_to_bf16_rne(v[2 * pp]), h1 = f32_to_bf16_rne(v[2 * pp + 1]);
-                        const uint32_t l0 = f32_to_bf16_rne(v[2 * pp] - bf16_to_f32(h0));
-                        const uint32_t l1 = f32_to_bf16_rne(v[2 * pp + 1] - bf16_to_f32(h1));
-                        hi[pp] = h0 | (h1 << 16);
-                        lo[pp] = l0 | (l1 << 16);
-                        hs[u] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+                        const _Float16 h0 = (_Float16)v[2 * pp], h1 = (_Float16)v[2 * pp + 1];
+                        pr[pp] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                 ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                        hs[u] += (float)h0 + (float)h1;
                     }
-                    perm8(hi[0], hi[1], hi[2], hi[3], hh[u][4 * q], hh[u][4 * q + 1], hh[u][4 * q + 2],
-                          hh[u][4 * q + 3]);
-                    perm8(lo[0], lo[1], lo[2], lo[3], hl[u][4 * q], hl[u][4 * q + 1], hl[u][4 * q + 2],
-                          hl[u][4 * q + 3]);
+                    perm8(pr[0], pr[1], pr[2], pr[3], hp[u][4 * q], hp[u][4 * q + 1], hp[u][4 * q + 2],
+                          hp[u][4 * q + 3]);
                 }
             }
         }
@@ -290,14 +307,19 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
                 const int dl = row_of(s0 + b);
                 float sd, md;
                 group_params<FMT>(st.s[b], sd, md);
-                const float cd = md - OFFSET_BF16 * sd;
+                const float cd = md - OFFSET_F16 * sd;
+                const uint32_t d4[4] = {st.v[b].x, st.v[b].y, st.v[b].z, st.v[b].w};
                 uint32_t dw[16];
-                unpack32(st.v[b], dw);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) dw[4 * q + pp] = unpack_pair<MAGIC_F16>(d4[q], pp);
 #pragma unroll
                 for (int u = 0; u < DECODE_TT; ++u) {
                     if (u < nt) {
-                        float a = dot16(dw, hh[u], 0.f);
-                        a = dot16(dw, hl[u], a);
+                        float a = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) a = dot2_f16(dw[i], hp[u][i], a);
                         const float o = seg_sum_dpp<LPR>(fmaf(sd, a, cd * hs[u]));
                         if (c == LPR - 1 && dl < rb && s0 + b < steps)
                             unsafeAtomicAdd(y + (size_t)tok[u] * H + d0 + dl, gt[u] * o);
@@ -460,14 +482,14 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     const int P = (int)(T * k);
     const int mt = (int)max_tiles(P, L.E, DECODE_TT);
     const dim3 block(DEC_WAVES * 64);
-    switch (H / 32) {
+    switch (H / 64) {
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
         auto kern = decode_gateup_kernel<LP, FMT>;                                                               \
         launch_k(kern, dim3(resident_grid(kern)), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,     \
                  (const int32_t *)g.ntiles, mt, (const int32_t *)g.perm, h);                                     \
     } break;
-        CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
+        CASE(1) CASE(2) CASE(4) CASE(8) CASE(16) CASE(32)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
