@@ -102,7 +102,7 @@ DecodeWs carve_decode(Carver &c, int64_t T, int E, int k, int H, int I) {
 
 // moe_q4_forward: a control block (zeroed by moe_q4_workspace_init) followed by
 // the decode or prefill regions.
-constexpr size_t CONTROL_BYTES = 256;
+constexpr size_t CONTROL_BYTES = ROUTE_CONTROL_BYTES;
 bool forward_uses_decode(int64_t T, int k) { return T <= 64 && T * k <= GROUP_SINGLE_MAX; }
 // One-launch routing also needs the T x E logits to fit the last workgroup's LDS.
 bool forward_fused_route(int64_t T, int E) { return T * E <= ROUTE_LDS_LOGITS; }

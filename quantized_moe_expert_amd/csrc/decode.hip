@@ -338,19 +338,20 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
 }
 
 // Routing of a few tokens in one launch.  Workgroup b (16 waves) computes
-// the router logits of experts [4 b, 4 b + 4) for every token; the tokens'
-// input rows are staged in LDS 16 at a time (formed once per workgroup).  The
-// logits travel to the workgroup that arrives last through agent-scope
-// relaxed atomic stores and loads (coherent across the XCDs' L2 caches) and a
-// counter in the workspace (zero between calls): each workgroup waits for its
-// stores to complete, then counts itself in.  This avoids whole-L2 write-back
-// and invalidate fences, which cost far more than the routing itself when
-// hundreds of workgroups issue them.  The last workgroup stages the logits in
-// LDS, takes the top-k of every token and groups the pairs by expert.
-// Without router weights one workgroup does top-k and grouping on the given
-// logits.  With yres the layer input is the residual step bf16(x + yres),
-// computed on the fly and written to xout.  The workgroups also clear y for
-// the expert kernel's atomics.
+// the router logit of expert b for every token (wave w: tokens w, w + 16,
+// ...); the tokens' input rows are staged in LDS 16 at a time (formed once
+// per workgroup).  The logits travel to the workgroup that arrives last
+// through agent-scope relaxed atomic stores and loads (coherent across the
+// XCDs' L2 caches) and a counter in the workspace (zero between calls): each
+// workgroup waits for its stores to complete, then counts itself in.  This
+// avoids whole-L2 write-back and invalidate fences, which cost far more than
+// the routing itself when hundreds of workgroups issue them.  The last
+// workgroup stages the logits in LDS, takes the top-k of every token and
+// groups the pairs by expert (from LDS copies of the indices).  Without
+// router weights one workgroup does top-k and grouping on the given logits.
+// With yres the layer input is the residual step bf16(x + yres), computed on
+// the fly and written to xout.  The workgroups also clear y for the expert
+// kernels' atomics.
 template <int NPL>
 __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ yres, uint16_t *__restrict__ xout,
@@ -359,6 +360,7 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     float *__restrict__ yclear, unsigned int *__restrict__ counter, unsigned int *__restrict__ handoff) {
     __shared__ int s_last;
     __shared__ uint16_t s_lg[ROUTE_LDS_LOGITS];
+    __shared__ int32_t s_idx[GROUP_SINGLE_MAX];
     __shared__ __attribute__((aligned(16))) uint16_t s_x[ROUTE_TC * 2048];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = gridDim.x;
@@ -369,17 +371,13 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     }
     const uint16_t *lsrc = logits;
     if (wr) {
-        // workgroup: experts [4 b, 4 b + 4); wave w: expert 4 b + (w & 3), token
-        // slots (w >> 2) + 4 i of each 16-token chunk staged in LDS (the
-        // residual input rows are formed once per workgroup)
-        const int e = blockIdx.x * 4 + (wave & 3);
-        const bool have = e < E;
+        const int e = blockIdx.x;  // grid = E
         double wd[4][8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int hh = (q * WAVE + lane) * 8;
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (have && hh < H) v = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
+            if (hh < H) v = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -387,31 +385,50 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
                 wd[q][2 * jj + 1] = (double)bf16_to_f32(w4[jj] >> 16);
             }
         }
-        const double b = (have && bias) ? (double)bias[e] : 0.0;
+        const double b = bias ? (double)bias[e] : 0.0;
         for (int t0 = 0; t0 < T; t0 += ROUTE_TC) {
             const int tc = T - t0 < ROUTE_TC ? T - t0 : ROUTE_TC;
+            const int nvec = tc * (H / 8);
             __syncthreads();  // previous chunk consumed
-            for (int i = tid; i < tc * (H / 8); i += blockDim.x) {
-                const int tl = i / (H / 8), hh = (i % (H / 8)) * 8;
-                const size_t gi = (size_t)(t0 + tl) * H + hh;
-                uint4 v = *reinterpret_cast<const uint4 *>(x + gi);
-                if (yres) {
-                    const float4 ya = *reinterpret_cast<const float4 *>(yres + gi);
-                    const float4 yb = *reinterpret_cast<const float4 *>(yres + gi + 4);
-                    const float yv[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
-                    uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            for (int i0 = tid; i0 < nvec; i0 += 2 * 1024) {
+                // two 8-element pieces per thread, their loads in flight together
+                uint4 v[2];
+                float4 ya[2], yb[2];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(w4[jj] & 0xffffu) + yv[2 * jj]);
-                        const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(w4[jj] >> 16) + yv[2 * jj + 1]);
-                        w4[jj] = lo | (hi << 16);
+                for (int r = 0; r < 2; ++r) {
+                    const int i = i0 + r * 1024;
+                    if (i < nvec) {
+                        const size_t gi = (size_t)(t0 + i / (H / 8)) * H + (i % (H / 8)) * 8;
+                        v[r] = *reinterpret_cast<const uint4 *>(x + gi);
+                        if (yres) {
+                            ya[r] = *reinterpret_cast<const float4 *>(yres + gi);
+                            yb[r] = *reinterpret_cast<const float4 *>(yres + gi + 4);
+                        }
                     }
-                    v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
                 }
-                *reinterpret_cast<uint4 *>(&s_x[tl * H + hh]) = v;
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int i = i0 + r * 1024;
+                    if (i < nvec) {
+                        uint4 o = v[r];
+                        if (yres) {
+                            const float yv[8] = {ya[r].x, ya[r].y, ya[r].z, ya[r].w,
+                                                 yb[r].x, yb[r].y, yb[r].z, yb[r].w};
+                            uint32_t w4[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) {
+                                const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(w4[jj] & 0xffffu) + yv[2 * jj]);
+                                const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(w4[jj] >> 16) + yv[2 * jj + 1]);
+                                w4[jj] = lo | (hi << 16);
+                            }
+                            o = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                        }
+                        *reinterpret_cast<uint4 *>(&s_x[(i / (H / 8)) * H + (i % (H / 8)) * 8]) = o;
+                    }
+                }
             }
             __syncthreads();
-            for (int tl = wave >> 2; tl < tc; tl += 4) {
+            for (int tl = wave; tl < tc; tl += 16) {
                 double acc = 0.0;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -427,7 +444,7 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
                     }
                 }
                 acc = wave_sum_f64_dpp(acc);
-                if (have && lane == 63) {
+                if (lane == 63) {
                     const int t = t0 + tl;
                     const uint16_t v = f32_to_bf16_rne((float)(acc + b));
                     logits[(size_t)t * E + e] = v;
@@ -438,9 +455,19 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
         __syncthreads();
-        if (tid == 0)
-            s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     (unsigned)(nb - 1);
+        if (tid == 0) {
+            // two-level count (one counter per group of workgroups b mod 8, then
+            // one global count of finished groups): same-address atomics
+            // serialise, so no counter sees more than ~E/8 arrivals
+            const int grp = blockIdx.x % 8, ngrp = nb < 8 ? nb : 8;
+            const unsigned in_grp = (unsigned)((nb - grp + 7) / 8);
+            bool last = false;
+            if (__hip_atomic_fetch_add(counter + ROUTE_COUNTER_STRIDE * (grp + 1), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == in_grp - 1)
+                last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (unsigned)(ngrp - 1);
+            s_last = last;
+        }
         __syncthreads();
         if (!s_last) return;
         for (int i = tid; i < T * E; i += blockDim.x)
@@ -448,10 +475,12 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         __syncthreads();
         lsrc = s_lg;
     }
-    for (int t = wave; t < T; t += 16) topk_token_wave<NPL>(lsrc + (size_t)t * E, E, k, idx + t * k, gate + t * k);
+    for (int t = wave; t < T; t += 16)
+        topk_token_wave<NPL>(lsrc + (size_t)t * E, E, k, idx + t * k, gate + t * k, s_idx + t * k);
     __syncthreads();
-    group_block_single(idx, T * k, E, g);
-    if (tid == 0 && wr) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    group_block_single(s_idx, T * k, E, g);
+    if (wr && tid < 9)  // every workgroup has counted in: reset for the next call
+        __hip_atomic_store(counter + ROUTE_COUNTER_STRIDE * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroups of `kernel` (256 threads) the device holds at once, a multiple
@@ -520,7 +549,8 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
                                      unsigned int *handoff, hipStream_t s) {
     if (wr && T * E > ROUTE_LDS_LOGITS) return hipErrorInvalidValue;
-    const int nb = wr ? (E + 3) / 4 : 1;
+    if (T * k > GROUP_SINGLE_MAX) return hipErrorInvalidValue;
+    const int nb = wr ? E : 1;
     const int npl = (E + 63) / 64;
 #define LAUNCH(N) \
     hipLaunchKernelGGL(decode_route_group_kernel<N>, dim3(nb), dim3(1024), 0, s, x, yres, xout, wr, bias, T, H, E, k, logits, idx, gate, g, yclear, counter, handoff)

@@ -29,6 +29,8 @@ constexpr int DECODE_TT = 2;             // tokens per decode work item
 constexpr int PREFILL_BM = 128;          // rows per prefill tile
 constexpr int ROUTE_LDS_LOGITS = 16384;  // T * E limit of the one-launch decode routing
 constexpr int ROUTE_TC = 16;             // tokens staged per pass of the one-launch routing
+constexpr int ROUTE_COUNTER_STRIDE = 32; // uint32 spacing (128 B) of the one-launch routing's 9 counters
+constexpr size_t ROUTE_CONTROL_BYTES = 2048;  // control block holding them (cleared once)
 
 inline int64_t max_tiles(int64_t pairs, int E, int rows_per_tile) {
     return pairs / rows_per_tile + (pairs < E ? pairs : E) + 1;

@@ -45,7 +45,7 @@ __device__ inline double router_dot_wave(const uint16_t *__restrict__ x, const f
 // lowest e.  Gates in double: exp(l_i - l_0) / sum_j exp(l_j - l_0).
 template <int NPL>
 __device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, int k, int32_t *__restrict__ idx_out,
-                                float *__restrict__ gate_out) {
+                                float *__restrict__ gate_out, int32_t *idx_copy = nullptr) {
     const int lane = threadIdx.x & 63;
     uint32_t key[NPL];
 #pragma unroll
@@ -73,6 +73,7 @@ __device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, in
     if (lane < k) {
         idx_out[lane] = my_e;
         gate_out[lane] = (float)(ex / den);
+        if (idx_copy) idx_copy[lane] = my_e;
     }
 }
 
