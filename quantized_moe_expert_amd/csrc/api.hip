@@ -283,6 +283,16 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
     uint16_t *lg = static_cast<uint16_t *>(logits);
     if (dec) {
         DecodeWs d = carve_decode(c, T, E, k, H, I);
+        if ((forward_fused_route(T, E) || !wr) && decode_routes_in_block(T, k, E)) {
+            // router GEMV (+ residual, y clear) in one launch; the expert GEMV
+            // launches route the tokens in every workgroup
+            st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
+                                                      static_cast<uint16_t *>(x_out), wr, bias, (int)T, H, E, k, lg,
+                                                      topk_idx, topk_gate, d.g, y, counter, handoff, s, false));
+            if (st) return st;
+            return hip_status(
+                launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s));
+        }
         if (forward_fused_route(T, E) || !wr) {
             st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
                                                       static_cast<uint16_t *>(x_out), wr, bias, (int)T, H, E, k, lg,

@@ -125,13 +125,74 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
 // 64 codes (one 64-group), so a wave-load covers RPW = 64 / LPR rows of gate
 // and of up (2 rows of 1 KB each when H = 2048).  The next wave-load is in
 // flight while the current one is reduced.
-template <int LPR, int FMT>
+// With ROUTE, every workgroup first routes the tokens itself from the logits
+// lg (written by the previous launch): top-k per token and the one-block
+// grouping, into LDS; workgroup 0 also publishes the indices, gates and
+// grouping arrays (idx_out, gate_out, gout) for the down GEMV and the caller.
+// This replaces a serial last-workgroup step of the routing launch.
+template <int LPR, int FMT, bool ROUTE>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, int max_nt, const int32_t *__restrict__ perm, float *__restrict__ h) {
+    const int32_t *__restrict__ ntiles, int max_nt, const int32_t *__restrict__ perm, float *__restrict__ h,
+    const uint16_t *__restrict__ lg, int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out,
+    GroupOut gout) {
     constexpr int RPW = WAVE / LPR;  // rows per wave-load
     constexpr int G = FMT == 0 ? 64 : 128;
-    int nt_all = *ntiles;
+    int nt_all;
+    if constexpr (ROUTE) {
+        __shared__ int32_t r_idx[DEC_ROUTE_PMAX];
+        __shared__ float r_gate[DEC_ROUTE_PMAX];
+        __shared__ int32_t r_cnt[DEC_ROUTE_EMAX], r_off[DEC_ROUTE_EMAX + 1], r_perm[DEC_ROUTE_PMAX],
+            r_inv[DEC_ROUTE_PMAX];
+        __shared__ Tile r_tiles[DEC_ROUTE_TMAX];
+        __shared__ int32_t r_nt;
+        __shared__ __attribute__((aligned(16))) uint16_t r_lg[DEC_ROUTE_LOGITS];
+        const int E = L.E, tid = threadIdx.x, wave = tid >> 6;
+        const bool b0 = blockIdx.x == 0;
+        // all logits in one coalesced pass (the top-k rounds then read LDS only)
+        {
+            const int n = T * E;
+            for (int i = tid * 8; i < n; i += blockDim.x * 8) {
+                if (i + 8 <= n && ((reinterpret_cast<uintptr_t>(lg) & 15) == 0))
+                    *reinterpret_cast<uint4 *>(&r_lg[i]) = *reinterpret_cast<const uint4 *>(lg + i);
+                else
+                    for (int q = i; q < n && q < i + 8; ++q) r_lg[q] = lg[q];
+            }
+        }
+        __syncthreads();
+        for (int t = wave; t < T; t += DEC_WAVES) {
+            if (b0) topk_token_wave<DEC_ROUTE_NPL>(r_lg + (size_t)t * E, E, k, idx_out + t * k, gate_out + t * k,
+                                                   r_idx + t * k);
+            else topk_token_wave<DEC_ROUTE_NPL>(r_lg + (size_t)t * E, E, k, r_idx + t * k, r_gate + t * k);
+        }
+        __syncthreads();
+        GroupOut gl;
+        gl.cnt = r_cnt;
+        gl.off = r_off;
+        gl.perm = r_perm;
+        gl.inv = r_inv;
+        gl.tiles = r_tiles;
+        gl.ntiles = &r_nt;
+        gl.rows_per_tile = DECODE_TT;
+        gl.chunk_cnt = gl.chunk_base = nullptr;
+        group_block_single(r_idx, P, E, gl);
+        __syncthreads();
+        nt_all = r_nt;
+        if (b0) {
+            for (int i = tid; i < E; i += blockDim.x) gout.cnt[i] = r_cnt[i];
+            for (int i = tid; i <= E; i += blockDim.x) gout.off[i] = r_off[i];
+            for (int i = tid; i < P; i += blockDim.x) {
+                gout.perm[i] = r_perm[i];
+                gout.inv[i] = r_inv[i];
+            }
+            for (int i = tid; i < nt_all; i += blockDim.x) gout.tiles[i] = r_tiles[i];
+            if (tid == 0) *gout.ntiles = nt_all;
+        }
+        tiles = r_tiles;
+        perm = r_perm;
+    } else {
+        nt_all = *ntiles;
+    }
     nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
     const Items it = decode_items(nt_all, I, I / (DEC_WAVES * RPW));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -357,7 +418,8 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ yres, uint16_t *__restrict__ xout,
     const uint16_t *__restrict__ wr, const float *__restrict__ bias, int T, int H, int E, int k,
     uint16_t *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ gate, GroupOut g,
-    float *__restrict__ yclear, unsigned int *__restrict__ counter, unsigned int *__restrict__ handoff) {
+    float *__restrict__ yclear, unsigned int *__restrict__ counter, unsigned int *__restrict__ handoff,
+    bool tail) {
     __shared__ int s_last;
     __shared__ uint16_t s_lg[ROUTE_LDS_LOGITS];
     __shared__ int32_t s_idx[GROUP_SINGLE_MAX];
@@ -448,11 +510,13 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
                     const int t = t0 + tl;
                     const uint16_t v = f32_to_bf16_rne((float)(acc + b));
                     logits[(size_t)t * E + e] = v;
-                    __hip_atomic_store(handoff + (size_t)t * E + e, (unsigned int)v, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                    if (tail)
+                        __hip_atomic_store(handoff + (size_t)t * E + e, (unsigned int)v, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
+        if (!tail) return;  // top-k and grouping run in the next launch
         __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
         __syncthreads();
         if (tid == 0) {
@@ -475,6 +539,7 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         __syncthreads();
         lsrc = s_lg;
     }
+    if (!tail) return;
     for (int t = wave; t < T; t += 16)
         topk_token_wave<NPL>(lsrc + (size_t)t * E, E, k, idx + t * k, gate + t * k, s_idx + t * k);
     __syncthreads();
@@ -503,10 +568,10 @@ static int resident_grid(K kernel) {
     return v;
 }
 
-template <int FMT>
+template <int FMT, bool ROUTE>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
-                                     hipEvent_t e1) {
+                                     hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
     const int mt = (int)max_tiles(P, L.E, DECODE_TT);
@@ -514,9 +579,9 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     switch (H / 64) {
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
-        auto kern = decode_gateup_kernel<LP, FMT>;                                                               \
+        auto kern = decode_gateup_kernel<LP, FMT, ROUTE>;                                                        \
         launch_k(kern, dim3(resident_grid(kern)), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,     \
-                 (const int32_t *)g.ntiles, mt, (const int32_t *)g.perm, h);                                     \
+                 (const int32_t *)g.ntiles, mt, (const int32_t *)g.perm, h, lg, (int)T, idx_out, gate_out, g);   \
     } break;
         CASE(1) CASE(2) CASE(4) CASE(8) CASE(16) CASE(32)
 #undef CASE
@@ -540,20 +605,36 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                  hipEvent_t e1) {
-    return L.fmt == 0 ? launch_experts_fmt<0>(x, gate, T, k, L, g, h, y, s, e0, e1)
-                      : launch_experts_fmt<1>(x, gate, T, k, L, g, h, y, s, e0, e1);
+    return L.fmt == 0 ? launch_experts_fmt<0, false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr)
+                      : launch_experts_fmt<1, false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr);
+}
+
+// Every expert workgroup repeats this routing before its first weight load,
+// so it pays off only while it is short: a few tokens (measured on MI355X:
+// 1 token saves ~3 us per layer, 16 tokens lose ~2 us against the one-launch
+// routing's last-workgroup step).
+bool decode_routes_in_block(int64_t T, int k, int E) {
+    return E <= DEC_ROUTE_EMAX && T * k <= DEC_ROUTE_PMAX_FAST && T * E <= DEC_ROUTE_LOGITS;
+}
+
+hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
+                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
+                                        float *y, hipStream_t s) {
+    if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;
+    return L.fmt == 0 ? launch_experts_fmt<0, true>(x, gate, T, k, L, g, h, y, s, nullptr, nullptr, logits, idx, gate)
+                      : launch_experts_fmt<1, true>(x, gate, T, k, L, g, h, y, s, nullptr, nullptr, logits, idx, gate);
 }
 
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,
                                      const float *bias, int T, int H, int E, int k, uint16_t *logits, int32_t *idx,
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
-                                     unsigned int *handoff, hipStream_t s) {
+                                     unsigned int *handoff, hipStream_t s, bool tail) {
     if (wr && T * E > ROUTE_LDS_LOGITS) return hipErrorInvalidValue;
     if (T * k > GROUP_SINGLE_MAX) return hipErrorInvalidValue;
     const int nb = wr ? E : 1;
     const int npl = (E + 63) / 64;
 #define LAUNCH(N) \
-    hipLaunchKernelGGL(decode_route_group_kernel<N>, dim3(nb), dim3(1024), 0, s, x, yres, xout, wr, bias, T, H, E, k, logits, idx, gate, g, yclear, counter, handoff)
+    hipLaunchKernelGGL(decode_route_group_kernel<N>, dim3(nb), dim3(1024), 0, s, x, yres, xout, wr, bias, T, H, E, k, logits, idx, gate, g, yclear, counter, handoff, tail)
     if (npl <= 4) LAUNCH(4);
     else if (npl <= 8) LAUNCH(8);
     else LAUNCH(16);

@@ -29,6 +29,12 @@ constexpr int DECODE_TT = 2;             // tokens per decode work item
 constexpr int PREFILL_BM = 128;          // rows per prefill tile
 constexpr int ROUTE_LDS_LOGITS = 16384;  // T * E limit of the one-launch decode routing
 constexpr int ROUTE_TC = 16;             // tokens staged per pass of the one-launch routing
+constexpr int DEC_ROUTE_EMAX = 256;      // experts of the per-workgroup decode routing
+constexpr int DEC_ROUTE_PMAX = 256;      // (token, slot) pairs of the per-workgroup decode routing
+constexpr int DEC_ROUTE_PMAX_FAST = 64;  // pairs up to which the forward call uses it
+constexpr int DEC_ROUTE_NPL = 4;         // logits per lane in its top-k (E <= 256)
+constexpr int DEC_ROUTE_LOGITS = 8192;   // T * E logits it stages in LDS
+constexpr int DEC_ROUTE_TMAX = DEC_ROUTE_PMAX / DECODE_TT + DEC_ROUTE_PMAX + 1;  // tiles it can form
 constexpr int ROUTE_COUNTER_STRIDE = 32; // uint32 spacing (128 B) of the one-launch routing's 9 counters
 constexpr size_t ROUTE_CONTROL_BYTES = 2048;  // control block holding them (cleared once)
 
@@ -66,11 +72,23 @@ hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64
 // tokens in one launch; clears y (T*H floats); with yres writes the residual
-// input bf16(x + yres) to xout.  counter: zero on entry, zero on exit.
+// input bf16(x + yres) to xout.  counter: zero on entry, zero on exit.  With
+// tail == false the launch stops after the logits (and y, xout): top-k and
+// grouping are left to launch_decode_experts_routed.
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,
                                      const float *bias, int T, int H, int E, int k, uint16_t *logits, int32_t *idx,
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
-                                     unsigned int *handoff, hipStream_t s);
+                                     unsigned int *handoff, hipStream_t s, bool tail = true);
+
+// Decode experts that route in every workgroup from the logits (written by
+// an earlier launch): top-k into idx / gate and grouping into g are computed
+// per workgroup in LDS and published by workgroup 0.  Used for E <= 256,
+// T * k <= 64, T * E <= 8192 (decode_routes_in_block; the kernel itself
+// holds up to 256 pairs).  y must be cleared first.
+bool decode_routes_in_block(int64_t T, int k, int E);
+hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
+                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
+                                        float *y, hipStream_t s);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
