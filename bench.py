@@ -177,8 +177,6 @@ def main():
         nl_per_step = 1
     torch.cuda.synchronize()
     structs = [m.layer_struct(l) for l in layers]
-    kind = m.WS_DECODE if decode_path else m.WS_PREFILL
-    ws = torch.empty(max(m.workspace_size(kind, T, E, k, H, I), 256), dtype=torch.uint8, device=dev)
     wsf = torch.zeros(max(m.workspace_size(m.WS_FORWARD, T, E, k, H, I), 256), dtype=torch.uint8, device=dev)
     m.moe_q4_workspace_init(wsf)
     lg = torch.empty((T, E), dtype=torch.int16, device=dev)
@@ -186,7 +184,6 @@ def main():
     gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     ybuf = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(2)]
     xbuf = [torch.empty_like(case.x), torch.empty_like(case.x)]
-    timed_fn = m.moe_q4_decode_timed if decode_path else m.moe_q4_prefill_timed
     state = {"i": 0}
 
     def layer_ids():
@@ -210,20 +207,21 @@ def main():
         state["i"] += 1
 
     def step_profiled(evsets):
-        """Same work as step() through the separate entry points, with the
-        expert stage bracketed by HIP events on the launch stream."""
+        """The calls of step(), through moe_q4_forward_timed: the runtime
+        records the events at the start and end of the call's two main
+        kernels (gate/up and routing launches for decode, the two grouped
+        GEMMs for prefill) on the launch stream."""
         for j, li in enumerate(layer_ids()):
             rw = routers[li] if routers[0] is not None else None
-            xin = case.x
+            logits_in = lg if rw is not None else case.logits
+            evs = [e.cuda_event for e in evsets[j]]
             if args.workload == "frame" and j > 0:
                 x_prev = case.x if j == 1 else xbuf[(j - 1) & 1]
-                m.moe_q4_residual_bf16(x_prev, ybuf[(j - 1) & 1], T * H, xbuf[j & 1])
-                xin = xbuf[j & 1]
-            if rw is not None:
-                m.moe_q4_route(xin, rw, None, lg, T, H, E, k, idx, gate)
+                m.moe_q4_forward_timed(x_prev, ybuf[(j - 1) & 1], xbuf[j & 1], rw, None, logits_in, T, k,
+                                       structs[li], idx, gate, ybuf[j & 1], wsf, evs)
             else:
-                m.moe_q4_route(None, None, None, case.logits, T, H, E, k, idx, gate)
-            timed_fn(xin, idx, gate, T, k, structs[li], ybuf[j & 1], ws, [e.cuda_event for e in evsets[j]])
+                m.moe_q4_forward_timed(case.x, None, None, rw, None, logits_in, T, k, structs[li], idx, gate,
+                                       ybuf[j & 1], wsf, evs)
             routed.append(idx.clone())
         state["i"] += 1
 
@@ -260,7 +258,7 @@ def main():
         step_profiled(per_step)
     torch.cuda.synchronize()
     # [0]: the dominant kernel (decode gate/up GEMV / prefill gate-up GEMM),
-    # [1]: the second kernel (grouping / prefill down GEMM); each is the span
+    # [1]: the second kernel (decode routing launch / prefill down GEMM); each is the span
     # between the events the runtime recorded at that kernel's start and end
     stage_ms = np.array([[evs[0].elapsed_time(evs[1]), evs[2].elapsed_time(evs[3])]
                          for per_step in ev_sets for evs in per_step])

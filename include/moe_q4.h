@@ -186,10 +186,11 @@ MOE_Q4_API int moe_q4_prefill(const void *x, const int32_t *topk_idx, const floa
 /*
  * Whole layer in one call: routing (router GEMV when router_w != NULL, else
  * the given logits), top-k gates, grouping and the experts, y float [T][H].
- * For T <= 64 (and T*k <= 1024) this is two kernel launches: routing with
- * top-k and grouping fused (the last workgroup to finish its router rows does
- * the top-k and grouping), then the decode expert kernel; larger T takes the
- * prefill path.
+ * For T <= 64 (and T*k <= 1024) this is three kernel launches: routing, the
+ * gate/up GEMV and the down GEMV.  With at most 64 (token, slot) pairs and
+ * E <= 256 every gate/up workgroup takes the top-k and grouping itself from
+ * the logits; otherwise the routing launch does them in its last workgroup
+ * to finish.  Larger T takes the prefill path.
  *   residual_y  float [T][H] or NULL.  When given, the layer input is the
  *               residual step bf16(float(x) + residual_y) of a chain of layers
  *               (as moe_q4_residual_bf16), written to x_out (bf16 [T][H],
@@ -207,6 +208,19 @@ MOE_Q4_API int moe_q4_forward(const void *x, const float *residual_y, void *x_ou
                               int64_t T, int32_t k, const moe_q4_layer *w,
                               int32_t *topk_idx, float *topk_gate, float *y,
                               void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/*
+ * moe_q4_forward with the caller's MOE_Q4_STAGE_EVENTS HIP events recorded at
+ * the start and end of its two main kernels (extended launch): decode path
+ * events[0..1] the gate/up GEMV, events[2..3] the routing launch (grouping
+ * launch when the router runs separately); prefill path as
+ * moe_q4_prefill_timed.  events must not be NULL.
+ */
+MOE_Q4_API int moe_q4_forward_timed(const void *x, const float *residual_y, void *x_out,
+                                    const void *router_w, const float *bias, void *logits, int64_t T,
+                                    int32_t k, const moe_q4_layer *w, int32_t *topk_idx, float *topk_gate,
+                                    float *y, void *ws, size_t ws_bytes, moe_q4_stream stream,
+                                    void *const *events);
 
 /* Clears the control block of a workspace used with moe_q4_forward (once,
  * after allocation).  Enqueued on stream. */

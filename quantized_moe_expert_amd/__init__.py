@@ -10,6 +10,7 @@ from ._lib import (ASYM_G64, SYM_G128, WS_DECODE, WS_GROUP, WS_PREFILL, WS_ROUTE
                    error_string, layer_struct, lib, moe_q4_decode, moe_q4_dequant, moe_q4_group,
                    moe_q4_prefill, moe_q4_residual_bf16, moe_q4_route, workspace_size,
                    moe_q4_decode_timed, moe_q4_prefill_timed, STAGE_EVENTS, WS_FORWARD, moe_q4_forward,
+                   moe_q4_forward_timed,
                    moe_q4_workspace_init)
 from .layer import MoeQ4Layer
 
@@ -17,4 +18,5 @@ __all__ = ["ASYM_G64", "SYM_G128", "WS_DECODE", "WS_GROUP", "WS_PREFILL", "WS_RO
            "error_string", "layer_struct", "lib", "moe_q4_decode", "moe_q4_dequant", "moe_q4_group",
            "moe_q4_prefill", "moe_q4_residual_bf16", "moe_q4_route", "workspace_size", "MoeQ4Layer",
            "moe_q4_decode_timed", "moe_q4_prefill_timed", "STAGE_EVENTS", "WS_FORWARD", "moe_q4_forward",
+           "moe_q4_forward_timed",
            "moe_q4_workspace_init"]

@@ -20,7 +20,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 # every entry point declared in include/moe_q4.h
 EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_decode", "moe_q4_prefill",
-           "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_workspace_init",
+           "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_forward_timed",
+           "moe_q4_workspace_init",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string")
 STAGE_EVENTS = 4
 
@@ -67,6 +68,9 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, sz, P, ctypes.POINTER(ctypes.c_void_p)]
         L.moe_q4_forward.restype = ctypes.c_int
         L.moe_q4_forward.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, P, P, sz, P]
+        L.moe_q4_forward_timed.restype = ctypes.c_int
+        L.moe_q4_forward_timed.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, P, P, sz, P,
+                                           ctypes.POINTER(ctypes.c_void_p)]
         L.moe_q4_workspace_init.restype = ctypes.c_int
         L.moe_q4_workspace_init.argtypes = [P, sz, P]
         L.moe_q4_dequant.restype = ctypes.c_int
@@ -167,12 +171,26 @@ def _timed(name, x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream):
 
 def moe_q4_decode_timed(x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream=None):
     """moe_q4_decode that has the runtime record the 4 given hipEvent_t handles at the start and end
-    of its expert kernel ([0], [1]) and grouping kernel ([2], [3])."""
+    of its gate/up GEMV kernel ([0], [1]) and grouping kernel ([2], [3])."""
     _timed("moe_q4_decode_timed", x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream)
 
 
 def moe_q4_prefill_timed(x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream=None):
     _timed("moe_q4_prefill_timed", x, topk_idx, topk_gate, T, k, layer, y, ws, events, stream)
+
+
+def moe_q4_forward_timed(x, residual_y, x_out, router_w, bias, logits, T, k, layer, topk_idx, topk_gate, y, ws,
+                         events, stream=None):
+    """moe_q4_forward that has the runtime record the 4 given hipEvent_t handles around its two main
+    kernels: decode [0], [1] gate/up GEMV and [2], [3] routing; prefill [0], [1] gate/up GEMM and [2], [3]
+    down GEMM."""
+    w, nb = _ws(ws)
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    ev = (ctypes.c_void_p * STAGE_EVENTS)(*[int(e) for e in events])
+    _check("moe_q4_forward_timed",
+           lib().moe_q4_forward_timed(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias),
+                                      _ptr(logits), T, k, ctypes.byref(st), _ptr(topk_idx), _ptr(topk_gate),
+                                      _ptr(y), w, nb, _stream(stream), ev))
 
 
 def moe_q4_forward(x, residual_y, x_out, router_w, bias, logits, T, k, layer, topk_idx, topk_gate, y, ws,

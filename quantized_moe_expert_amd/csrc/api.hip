@@ -256,9 +256,10 @@ int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream) {
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
-int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
-                   void *logits, int64_t T, int32_t k, const moe_q4_layer *w, int32_t *topk_idx, float *topk_gate,
-                   float *y, void *ws, size_t ws_bytes, moe_q4_stream stream) {
+static int run_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
+                       void *logits, int64_t T, int32_t k, const moe_q4_layer *w, int32_t *topk_idx,
+                       float *topk_gate, float *y, void *ws, size_t ws_bytes, moe_q4_stream stream,
+                       void *const *events) {
     int st = check_layer(w, false);
     if (st) return st;
     st = check_route_shape(T, w->hidden, w->num_experts, k);
@@ -267,9 +268,15 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
     if (residual_y && !x_out) return MOE_Q4_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(x_out, 16) || !aligned(residual_y, 16))
         return MOE_Q4_ERR_INVALID_ARG;
+    if (events)
+        for (int i = 0; i < MOE_Q4_STAGE_EVENTS; ++i)
+            if (!events[i]) return MOE_Q4_ERR_INVALID_ARG;
     if (T == 0) return MOE_Q4_OK;
     const int E = w->num_experts, H = w->hidden, I = w->inter;
     const bool dec = forward_uses_decode(T, k);
+    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+    hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
     if (!dec && (check_layer(w, true) || !prefill_fits(T, k, H, I))) return MOE_Q4_ERR_UNSUPPORTED;
     const size_t need = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
@@ -288,25 +295,27 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
             // launches route the tokens in every workgroup
             st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
                                                       static_cast<uint16_t *>(x_out), wr, bias, (int)T, H, E, k, lg,
-                                                      topk_idx, topk_gate, d.g, y, counter, handoff, s, false));
+                                                      topk_idx, topk_gate, d.g, y, counter, handoff, s, false, e2,
+                                                      e3));
             if (st) return st;
             return hip_status(
-                launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s));
+                launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s, e0, e1));
         }
         if (forward_fused_route(T, E) || !wr) {
             st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
                                                       static_cast<uint16_t *>(x_out), wr, bias, (int)T, H, E, k, lg,
-                                                      topk_idx, topk_gate, d.g, y, counter, handoff, s));
+                                                      topk_idx, topk_gate, d.g, y, counter, handoff, s, true, e2,
+                                                      e3));
         } else {  // separate router, top-k and grouping launches
             if (residual_y)
                 st = hip_status(launch_residual(static_cast<const uint16_t *>(x), residual_y, T * (int64_t)H,
                                                 static_cast<uint16_t *>(x_out), s));
             if (!st) st = hip_status(launch_router_logits(xin, wr, bias, T, H, E, lg, s));
             if (!st) st = hip_status(launch_topk(lg, T, E, k, topk_idx, topk_gate, s));
-            if (!st) st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H));
+            if (!st) st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H, e2, e3));
         }
         if (st) return st;
-        return hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s));
+        return hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1));
     }
     if (residual_y) {
         st = hip_status(launch_residual(static_cast<const uint16_t *>(x), residual_y, T * (int64_t)H,
@@ -322,7 +331,23 @@ int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const vo
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, y, s, nullptr));
+    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, y, s, ev));
+}
+
+int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
+                   void *logits, int64_t T, int32_t k, const moe_q4_layer *w, int32_t *topk_idx, float *topk_gate,
+                   float *y, void *ws, size_t ws_bytes, moe_q4_stream stream) {
+    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, topk_idx, topk_gate, y, ws, ws_bytes,
+                       stream, nullptr);
+}
+
+int moe_q4_forward_timed(const void *x, const float *residual_y, void *x_out, const void *router_w,
+                         const float *bias, void *logits, int64_t T, int32_t k, const moe_q4_layer *w,
+                         int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes,
+                         moe_q4_stream stream, void *const *events) {
+    if (!events) return MOE_Q4_ERR_INVALID_ARG;
+    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, topk_idx, topk_gate, y, ws, ws_bytes,
+                       stream, events);
 }
 
 int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *out, moe_q4_stream stream) {

@@ -619,22 +619,23 @@ bool decode_routes_in_block(int64_t T, int k, int E) {
 
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
-                                        float *y, hipStream_t s) {
+                                        float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;
-    return L.fmt == 0 ? launch_experts_fmt<0, true>(x, gate, T, k, L, g, h, y, s, nullptr, nullptr, logits, idx, gate)
-                      : launch_experts_fmt<1, true>(x, gate, T, k, L, g, h, y, s, nullptr, nullptr, logits, idx, gate);
+    return L.fmt == 0 ? launch_experts_fmt<0, true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate)
+                      : launch_experts_fmt<1, true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate);
 }
 
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,
                                      const float *bias, int T, int H, int E, int k, uint16_t *logits, int32_t *idx,
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
-                                     unsigned int *handoff, hipStream_t s, bool tail) {
+                                     unsigned int *handoff, hipStream_t s, bool tail, hipEvent_t e0,
+                                     hipEvent_t e1) {
     if (wr && T * E > ROUTE_LDS_LOGITS) return hipErrorInvalidValue;
     if (T * k > GROUP_SINGLE_MAX) return hipErrorInvalidValue;
     const int nb = wr ? E : 1;
     const int npl = (E + 63) / 64;
 #define LAUNCH(N) \
-    hipLaunchKernelGGL(decode_route_group_kernel<N>, dim3(nb), dim3(1024), 0, s, x, yres, xout, wr, bias, T, H, E, k, logits, idx, gate, g, yclear, counter, handoff, tail)
+    launch_k(decode_route_group_kernel<N>, dim3(nb), dim3(1024), s, e0, e1, x, yres, xout, wr, bias, T, H, E, k, logits, idx, gate, g, yclear, counter, handoff, tail)
     if (npl <= 4) LAUNCH(4);
     else if (npl <= 8) LAUNCH(8);
     else LAUNCH(16);

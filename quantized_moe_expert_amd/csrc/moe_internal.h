@@ -78,7 +78,8 @@ hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,
                                      const float *bias, int T, int H, int E, int k, uint16_t *logits, int32_t *idx,
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
-                                     unsigned int *handoff, hipStream_t s, bool tail = true);
+                                     unsigned int *handoff, hipStream_t s, bool tail = true,
+                                     hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // Decode experts that route in every workgroup from the logits (written by
 // an earlier launch): top-k into idx / gate and grouping into g are computed
@@ -88,7 +89,7 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
 bool decode_routes_in_block(int64_t T, int k, int E);
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
-                                        float *y, hipStream_t s);
+                                        float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -147,7 +147,13 @@ def test_forward_validation():
     assert f(T=1 << 20) == _lib.ERR_UNSUPPORTED                  # prefill path 32-bit offsets
     assert f(x=FAKE + 2) == _lib.ERR_INVALID_ARG                 # misaligned activations
     assert f(ry=FAKE, xo=FAKE + 8) == _lib.ERR_INVALID_ARG
-    assert m.workspace_size(m.WS_FORWARD, 16, 256, 8, 2048, 512) >= 256
+    assert m.workspace_size(m.WS_FORWARD, 16, 256, 8, 2048, 512) >= 2048
+    ev_null = (ctypes.c_void_p * 4)(FAKE, None, FAKE, FAKE)
+    ft = lambda ev, T=4: L.moe_q4_forward_timed(FAKE, None, None, FAKE, None, FAKE, T, 8, ctypes.byref(lay), FAKE,
+                                                FAKE, FAKE, FAKE, 1 << 30, None, ev)
+    assert ft(None) == _lib.ERR_INVALID_ARG     # events required
+    assert ft(ev_null) == _lib.ERR_INVALID_ARG  # and non-NULL
+    assert ft((ctypes.c_void_p * 4)(*([FAKE] * 4)), T=0) == _lib.OK
     assert L.moe_q4_workspace_init(None, 0, None) == _lib.ERR_WORKSPACE
     assert L.moe_q4_workspace_init(FAKE, 100, None) == _lib.ERR_WORKSPACE
 

@@ -331,6 +331,31 @@ def _forward(lay, x, rw, logits, T, k, residual_y=None, ws=None):
     return lg, idx, gate, y, xo, ws
 
 
+@pytest.mark.parametrize("cfg,T", [(2, None), (4, None), (3, 128)])
+def test_forward_timed_matches_forward(cfg, T):
+    """The timed entry point runs the same kernels (both decode routing
+    variants and the prefill path) and records positive kernel spans."""
+    import quantized_moe_expert_amd as m
+    case = get_case(cfg, layers=1, T=T) if cfg == 4 else (get_case(cfg, T=T) if T else get_case(cfg))
+    lay = case.layers[0]
+    rw = case.router_ws[0] if case.router_ws else None
+    say(f"[forward timed] cfg={cfg} T={case.T}")
+    lg, idx, gate, y, _, ws = _forward(lay, case.x, rw, case.logits, case.T, case.k)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    lg2 = case.logits.clone() if case.logits is not None else torch.empty_like(lg)
+    idx2, gate2 = torch.empty_like(idx), torch.empty_like(gate)
+    y2 = torch.full_like(y, float("nan"))
+    m.moe_q4_forward_timed(case.x, None, None, rw, None, lg2, case.T, case.k, lay, idx2, gate2, y2, ws,
+                           [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    assert torch.equal(lg, lg2) and torch.equal(idx, idx2) and torch.equal(gate, gate2)
+    assert_close(y2.cpu().numpy(), y.cpu().numpy(), "timed vs plain forward")
+    assert evs[0].elapsed_time(evs[1]) > 0 and evs[2].elapsed_time(evs[3]) > 0
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_forward_decode_configs(cfg):
     case = get_case(cfg, layers=1) if cfg == 4 else get_case(cfg)
