@@ -86,9 +86,11 @@ __device__ __forceinline__ void group_params(uint32_t word, float &s, float &m) 
 
 // Work decomposition shared by the two GEMV kernels: nt tiles, each cut into
 // nch chunks of `rows` consecutive rows out of N (nch as large as the grid
-// allows, at most maxch; every chunk starts inside the N rows, the last one
-// may be shorter), items (tile, chunk) numbered tile-major and dealt to the
-// XCDs in contiguous ranges.  The grid is a multiple of 8.
+// allows, at most maxch, and enough that rows <= DEC_RB_MAX; every chunk
+// starts inside the N rows, the last one may be shorter), items (tile, chunk)
+// numbered tile-major and dealt to the XCDs in contiguous ranges.  The grid
+// is a multiple of 8.
+constexpr int DEC_RB_MAX = 256;  // rows per item (outputs staged in LDS)
 struct Items {
     int nch, rows, items, first, stride, end;
 };
@@ -98,6 +100,8 @@ __device__ __forceinline__ Items decode_items(int nt, int N, int maxch) {
     maxch = maxch < 1 ? 1 : maxch;
     int nch = nt > 0 ? grid / nt : 1;
     nch = nch < 1 ? 1 : (nch > maxch ? maxch : nch);
+    const int minch = (N + DEC_RB_MAX - 1) / DEC_RB_MAX;  // at most DEC_RB_MAX rows per item
+    nch = nch < minch ? minch : nch;
     it.rows = (N + nch - 1) / nch;
     it.nch = (N + it.rows - 1) / it.rows;  // <= nch; chunk c starts at c * rows < N
     it.items = nt * it.nch;
@@ -200,6 +204,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const size_t row_bytes = (size_t)H / 2;
     const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
     const int gi = (64 * c) / G;
+    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     struct Stage {
         uint4 g[2], u[2];
         uint32_t gs, us;
@@ -225,24 +230,24 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
             st.gs = load_group_word<FMT>(L.gsm + row * smr, gi);
             st.us = load_group_word<FMT>(L.usm + row * smr, gi);
         };
-        // the first rows depend only on the tile: in flight before the tokens are known
-        Stage sa, sb;
-        issue(sa, 0);
         uint32_t xp[DECODE_TT][32];
         float xs[DECODE_TT];
+        auto load_x = [&]() {
 #pragma unroll
-        for (int u = 0; u < DECODE_TT; ++u) {
-            xs[u] = 0.f;
-            if (u < nt) {
-                int p = perm[tile.row0 + u];
-                p = p < 0 ? 0 : (p >= P ? P - 1 : p);
-                const uint16_t *xrow = x + (size_t)(p / k) * H;
-                float s0, s1;
-                load_x_chunk(xrow, 2 * c, xp[u], s0);
-                load_x_chunk(xrow, 2 * c + 1, xp[u] + 16, s1);
-                xs[u] = s0 + s1;
+            for (int u = 0; u < DECODE_TT; ++u) {
+                xs[u] = 0.f;
+                if (u < nt) {
+                    int p = perm[tile.row0 + u];
+                    p = p < 0 ? 0 : (p >= P ? P - 1 : p);
+                    const uint16_t *xrow = x + (size_t)(p / k) * H;
+                    float s0, s1;
+                    load_x_chunk(xrow, 2 * c, xp[u], s0);
+                    load_x_chunk(xrow, 2 * c + 1, xp[u] + 16, s1);
+                    xs[u] = s0 + s1;
+                }
             }
-        }
+        };
+        Stage sa, sb;
         auto consume = [&](const Stage &st, int s) {
             const int nl = row_of(s);
             float sg, mg, su, mu;
@@ -270,19 +275,38 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
                 if (u < nt) {
                     const float pg = seg_sum_dpp<LPR>(fmaf(sg, dg[u], cg * xs[u]));
                     const float pu = seg_sum_dpp<LPR>(fmaf(su, du[u], cu * xs[u]));
-                    if (c == LPR - 1 && nl < rb)
-                        h[(size_t)(tile.row0 + u) * I + n0 + nl] = silu(pg) * pu;
+                    if (c == LPR - 1 && nl < rb) s_out[u][nl] = silu(pg) * pu;
                 }
             }
         };
-        // two register stages: the next wave-load is in flight while the current one is reduced
-        for (int s = 0; s < steps; s += 2) {
-            if (s + 1 < steps) issue(sb, s + 1);
-            consume(sa, s);
-            if (s + 1 >= steps) break;
-            if (s + 2 < steps) issue(sa, s + 2);
-            consume(sb, s + 1);
+        // Two register stages, the next one in flight while the current one is
+        // reduced.  The first rows depend only on the tile, so they are issued
+        // before the tokens are known.  The loop issues every stage (rows past
+        // the item re-read its first row) and outputs go to LDS, so it holds
+        // only loads and the compiler's memory-counter waits stay exact.  The
+        // routing variant (a few tokens: items of one wave-load are common)
+        // takes a straight path for them instead of issuing unused stages.
+        if (ROUTE && steps == 1) {
+            issue(sa, 0);
+            load_x();
+            consume(sa, 0);
+        } else {
+            issue(sa, 0);
+            issue(sb, 1);
+            load_x();
+            for (int s = 0; s < steps; s += 2) {
+                consume(sa, s);
+                issue(sa, s + 2);
+                if (s + 1 < steps) consume(sb, s + 1);
+                issue(sb, s + 3);
+            }
         }
+        __syncthreads();
+        for (int i = threadIdx.x; i < nt * rb; i += blockDim.x) {
+            const int u = i / rb, n = i % rb;
+            h[(size_t)(tile.row0 + u) * I + n0 + n] = s_out[u][n];
+        }
+        __syncthreads();
     }
 }
 
@@ -306,6 +330,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     const size_t row_bytes = (size_t)I / 2;
     const size_t smr = (size_t)(I / G) * (FMT == 0 ? 2 : 1);
     const int gi = (32 * c) / G;
+    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     struct Stage {
         uint4 v[DEC_NB];
         uint32_t s[DEC_NB];
@@ -329,11 +354,11 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
             }
         };
         Stage sa, sb;
-        issue(sa, 0);
         int tok[DECODE_TT];
         float gt[DECODE_TT];
         uint32_t hp[DECODE_TT][16];
         float hs[DECODE_TT];
+        auto load_h = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
             hs[u] = 0.f;
@@ -362,6 +387,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
                 }
             }
         }
+        };
         auto consume = [&](const Stage &st, int s0) {
 #pragma unroll
             for (int b = 0; b < DEC_NB; ++b) {
@@ -382,19 +408,35 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
 #pragma unroll
                         for (int i = 0; i < 16; ++i) a = dot2_f16(dw[i], hp[u][i], a);
                         const float o = seg_sum_dpp<LPR>(fmaf(sd, a, cd * hs[u]));
-                        if (c == LPR - 1 && dl < rb && s0 + b < steps)
-                            unsafeAtomicAdd(y + (size_t)tok[u] * H + d0 + dl, gt[u] * o);
+                        if (c == LPR - 1 && dl < rb && s0 + b < steps) s_out[u][dl] = gt[u] * o;
                     }
                 }
             }
         };
-        for (int s0 = 0; s0 < steps; s0 += 2 * DEC_NB) {
-            if (s0 + DEC_NB < steps) issue(sb, s0 + DEC_NB);
-            consume(sa, s0);
-            if (s0 + DEC_NB >= steps) break;
-            if (s0 + 2 * DEC_NB < steps) issue(sa, s0 + 2 * DEC_NB);
-            consume(sb, s0 + DEC_NB);
+        // stages of DEC_NB row loads, pipelined as in the gate/up GEMV
+        const int nst = (steps + DEC_NB - 1) / DEC_NB;
+        if (nst == 1) {
+            issue(sa, 0);
+            load_h();
+            consume(sa, 0);
+        } else {
+            issue(sa, 0);
+            issue(sb, DEC_NB);
+            load_h();
+            for (int q = 0; q < nst; q += 2) {
+                consume(sa, q * DEC_NB);
+                issue(sa, (q + 2) * DEC_NB);
+                if (q + 1 < nst) consume(sb, (q + 1) * DEC_NB);
+                issue(sb, (q + 3) * DEC_NB);
+            }
         }
+        __syncthreads();
+        // one float atomic per output and routed (token, slot), coalesced
+        for (int i = threadIdx.x; i < nt * rb; i += blockDim.x) {
+            const int u = i / rb, d = i % rb;
+            unsafeAtomicAdd(y + (size_t)tok[u] * H + d0 + d, s_out[u][d]);
+        }
+        __syncthreads();
     }
 }
 
