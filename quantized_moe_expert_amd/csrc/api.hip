@@ -90,13 +90,13 @@ GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile) {
 
 struct DecodeWs {
     GroupOut g;
-    float *h;
+    uint16_t *h;  // SwiGLU output per sorted row, f16 [T*k][I] in the down GEMV's order
 };
 DecodeWs carve_decode(Carver &c, int64_t T, int E, int k, int H, int I) {
     (void)H;
     DecodeWs d;
     d.g = carve_group(c, T, E, k, DECODE_TT);
-    d.h = c.take<float>(T * k * (int64_t)I);
+    d.h = c.take<uint16_t>(T * k * (int64_t)I);
     return d;
 }
 

@@ -8,7 +8,8 @@
 //
 // Two kernels per layer do the expert work:
 //   1. gate/up GEMV + SwiGLU: every active expert's gate and up rows, applied
-//      to the tokens routed to it, h in fp32 (workspace);
+//      to the tokens routed to it, h in f16 (workspace), laid out as the
+//      down GEMV reads it;
 //   2. down GEMV over full rows of h, multiplied by each token's gate and
 //      added into y with float atomics (y is cleared by the routing kernel).
 // Both launch as many workgroups as the chip holds at once and cut the work
@@ -34,17 +35,28 @@
 namespace moeq4 {
 
 
-// Activation chunk [32c, 32c+32) of a bf16 row in PERM8 order, and its sum.
-__device__ __forceinline__ void load_x_chunk(const uint16_t *__restrict__ xrow, int c, uint32_t xp[16],
-                                             float &xs) {
+// Activation chunk [32c, 32c+32) of a bf16 row, as loaded (natural order).
+__device__ __forceinline__ void fetch_x_chunk(const uint16_t *__restrict__ xrow, int c, uint32_t xp[16]) {
     const uint4 *src = reinterpret_cast<const uint4 *>(xrow + 32 * c);
-    xs = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint4 v = src[j];
-        perm8(v.x, v.y, v.z, v.w, xp[4 * j + 0], xp[4 * j + 1], xp[4 * j + 2], xp[4 * j + 3]);
-        xs += bf16_pair_sum(v.x) + bf16_pair_sum(v.y) + bf16_pair_sum(v.z) + bf16_pair_sum(v.w);
+        xp[4 * j + 0] = v.x;
+        xp[4 * j + 1] = v.y;
+        xp[4 * j + 2] = v.z;
+        xp[4 * j + 3] = v.w;
     }
+}
+// The fetched chunk put in PERM8 order in place; returns its sum.
+__device__ __forceinline__ float perm_x_chunk(uint32_t xp[16]) {
+    float xs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t v0 = xp[4 * j], v1 = xp[4 * j + 1], v2 = xp[4 * j + 2], v3 = xp[4 * j + 3];
+        xs += bf16_pair_sum(v0) + bf16_pair_sum(v1) + bf16_pair_sum(v2) + bf16_pair_sum(v3);
+        perm8(v0, v1, v2, v3, xp[4 * j + 0], xp[4 * j + 1], xp[4 * j + 2], xp[4 * j + 3]);
+    }
+    return xs;
 }
 
 // Tile fields made safe to index with (a workspace that was never filled
@@ -54,16 +66,21 @@ __device__ __forceinline__ Tile sane_tile(Tile t, int E, int P) {
     t.rows = t.rows < 0 ? 0 : (t.rows > DECODE_TT ? DECODE_TT : t.rows);
     t.rows = t.rows > P ? P : t.rows;
     t.row0 = t.row0 < 0 ? 0 : (t.row0 > P - t.rows ? P - t.rows : t.row0);
+#pragma unroll
+    for (int u = 0; u < DECODE_TT; ++u) t.pair[u] = t.pair[u] < 0 ? 0 : (t.pair[u] >= P ? P - 1 : t.pair[u]);
     return t;
 }
 
+constexpr uint32_t ONES_F16X2 = 0x3c003c00u;  // f16 pair (1, 1)
+
 // 16 bf16 pairs (32 codes in PERM8 order) of a dword quad.
-__device__ __forceinline__ void unpack32(const uint4 w, uint32_t out[16]) {
+// 32 codes as bf16 pairs 128 + q in PERM8 order (kb = opaque MAGIC_BF16).
+__device__ __forceinline__ void unpack32(const uint4 w, uint32_t out[16], uint32_t kb) {
     const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) out[4 * q + p] = unpack_pair<MAGIC_BF16>(d[q], p);
+        for (int p = 0; p < 4; ++p) out[4 * q + p] = insert_codes<0x000f000fu>(d[q] >> (4 * p), kb);
 }
 
 __device__ __forceinline__ float dot16(const uint32_t w[16], const uint32_t a[16], float acc) {
@@ -137,8 +154,7 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
 template <int LPR, int FMT, bool ROUTE>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, int max_nt, const int32_t *__restrict__ perm, float *__restrict__ h,
-    const uint16_t *__restrict__ lg, int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out,
+    const int32_t *__restrict__ ntiles, int max_nt, uint16_t *__restrict__ h, const uint16_t *__restrict__ lg, int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out,
     GroupOut gout) {
     constexpr int RPW = WAVE / LPR;  // rows per wave-load
     constexpr int G = FMT == 0 ? 64 : 128;
@@ -193,7 +209,6 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
             if (tid == 0) *gout.ntiles = nt_all;
         }
         tiles = r_tiles;
-        perm = r_perm;
     } else {
         nt_all = *ntiles;
     }
@@ -204,6 +219,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const size_t row_bytes = (size_t)H / 2;
     const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
     const int gi = (64 * c) / G;
+    const uint32_t kb = opaque_magic(MAGIC_BF16);
     __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     struct Stage {
         uint4 g[2], u[2];
@@ -230,21 +246,26 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
             st.gs = load_group_word<FMT>(L.gsm + row * smr, gi);
             st.us = load_group_word<FMT>(L.usm + row * smr, gi);
         };
+        // Activations: fetched before the first weight stages (they depend
+        // on the tile only), reordered after them, so that waiting for them
+        // leaves the stages in flight.
         uint32_t xp[DECODE_TT][32];
         float xs[DECODE_TT];
-        auto load_x = [&]() {
+        auto fetch_x = [&]() {
+#pragma unroll
+            for (int u = 0; u < DECODE_TT; ++u) {
+                if (u < nt) {
+                    const uint16_t *xrow = x + (size_t)(tile.pair[u] / k) * H;
+                    fetch_x_chunk(xrow, 2 * c, xp[u]);
+                    fetch_x_chunk(xrow, 2 * c + 1, xp[u] + 16);
+                }
+            }
+        };
+        auto prep_x = [&]() {
 #pragma unroll
             for (int u = 0; u < DECODE_TT; ++u) {
                 xs[u] = 0.f;
-                if (u < nt) {
-                    int p = perm[tile.row0 + u];
-                    p = p < 0 ? 0 : (p >= P ? P - 1 : p);
-                    const uint16_t *xrow = x + (size_t)(p / k) * H;
-                    float s0, s1;
-                    load_x_chunk(xrow, 2 * c, xp[u], s0);
-                    load_x_chunk(xrow, 2 * c + 1, xp[u] + 16, s1);
-                    xs[u] = s0 + s1;
-                }
+                if (u < nt) xs[u] = perm_x_chunk(xp[u]) + perm_x_chunk(xp[u] + 16);
             }
         };
         Stage sa, sb;
@@ -261,7 +282,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 uint32_t wq[16];
-                unpack32(q == 0 ? st.g[0] : q == 1 ? st.g[1] : q == 2 ? st.u[0] : st.u[1], wq);
+                unpack32(q == 0 ? st.g[0] : q == 1 ? st.g[1] : q == 2 ? st.u[0] : st.u[1], wq, kb);
 #pragma unroll
                 for (int u = 0; u < DECODE_TT; ++u) {
                     if (u < nt) {
@@ -287,13 +308,15 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
         // routing variant (a few tokens: items of one wave-load are common)
         // takes a straight path for them instead of issuing unused stages.
         if (ROUTE && steps == 1) {
+            fetch_x();
             issue(sa, 0);
-            load_x();
+            prep_x();
             consume(sa, 0);
         } else {
+            fetch_x();
             issue(sa, 0);
             issue(sb, 1);
-            load_x();
+            prep_x();
             for (int s = 0; s < steps; s += 2) {
                 consume(sa, s);
                 issue(sa, s + 2);
@@ -302,9 +325,14 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
             }
         }
         __syncthreads();
+        // h in f16 as the down GEMV consumes it: each 8-block in PERM8 order
+        // (element j at 2j for j < 4, at 2(j - 4) + 1 otherwise), odd
+        // elements divided by 16 (exact scaling by a power of two)
         for (int i = threadIdx.x; i < nt * rb; i += blockDim.x) {
-            const int u = i / rb, n = i % rb;
-            h[(size_t)(tile.row0 + u) * I + n0 + n] = s_out[u][n];
+            const int u = i / rb, n = n0 + i % rb;
+            const float v = (n & 1) ? s_out[u][i % rb] * (1.f / 16.f) : s_out[u][i % rb];
+            const int slot = (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1);
+            h[(size_t)(tile.row0 + u) * I + slot] = __builtin_bit_cast(uint16_t, (_Float16)v);
         }
         __syncthreads();
     }
@@ -318,7 +346,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
 template <int LPR, int FMT>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
-    int max_nt, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate, const float *__restrict__ h,
+    int max_nt, const float *__restrict__ topk_gate, const uint16_t *__restrict__ h,
     float *__restrict__ y) {
     constexpr int RPW = WAVE / LPR;
     constexpr int G = FMT == 0 ? 64 : 128;
@@ -330,6 +358,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     const size_t row_bytes = (size_t)I / 2;
     const size_t smr = (size_t)(I / G) * (FMT == 0 ? 2 : 1);
     const int gi = (32 * c) / G;
+    const uint32_t kf = opaque_magic(MAGIC_F16);
     __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     struct Stage {
         uint4 v[DEC_NB];
@@ -357,36 +386,48 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         int tok[DECODE_TT];
         float gt[DECODE_TT];
         uint32_t hp[DECODE_TT][16];
-        float hs[DECODE_TT];
-        auto load_h = [&]() {
+        // The lane's h elements in f16, odd ones divided by 16 (they meet
+        // codes 1024 + 16 q); ha = sum of the offsets those products carry
+        // (1024 per even element, 64 per odd one, times h), hb = sum of h.
+        float ha[DECODE_TT], hb[DECODE_TT];
+        // h and the gates: fetched before the first weight stages (they
+        // depend on the tile only), summed after them.
+        auto fetch_h = [&]() {
 #pragma unroll
-        for (int u = 0; u < DECODE_TT; ++u) {
-            hs[u] = 0.f;
-            tok[u] = 0;
-            gt[u] = 0.f;
-            if (u < nt) {
-                int p = perm[tile.row0 + u];
-                p = p < 0 ? 0 : (p >= P ? P - 1 : p);
-                tok[u] = p / k;
-                gt[u] = topk_gate[p];
-                const float4 *src = reinterpret_cast<const float4 *>(h + (size_t)(tile.row0 + u) * I + 32 * c);
+            for (int u = 0; u < DECODE_TT; ++u) {
+                tok[u] = 0;
+                gt[u] = 0.f;
+                if (u < nt) {
+                    const int p = tile.pair[u];
+                    tok[u] = p / k;
+                    gt[u] = topk_gate[p];
+                    const uint4 *src = reinterpret_cast<const uint4 *>(h + (size_t)(tile.row0 + u) * I + 32 * c);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 a = src[2 * q], b = src[2 * q + 1];
-                    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                    uint32_t pr[4];
-#pragma unroll
-                    for (int pp = 0; pp < 4; ++pp) {
-                        const _Float16 h0 = (_Float16)v[2 * pp], h1 = (_Float16)v[2 * pp + 1];
-                        pr[pp] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                 ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                        hs[u] += (float)h0 + (float)h1;
+                    for (int q = 0; q < 4; ++q) {
+                        const uint4 v = src[q];
+                        hp[u][4 * q + 0] = v.x;
+                        hp[u][4 * q + 1] = v.y;
+                        hp[u][4 * q + 2] = v.z;
+                        hp[u][4 * q + 3] = v.w;
                     }
-                    perm8(pr[0], pr[1], pr[2], pr[3], hp[u][4 * q], hp[u][4 * q + 1], hp[u][4 * q + 2],
-                          hp[u][4 * q + 3]);
                 }
             }
-        }
+        };
+        auto sum_h = [&]() {
+#pragma unroll
+            for (int u = 0; u < DECODE_TT; ++u) {
+                ha[u] = hb[u] = 0.f;
+                if (u < nt) {
+                    float se = 0.f, so = 0.f;  // sums of the even elements and of the odd ones (/16)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        se = dot2_f16(hp[u][4 * q + 0], ONES_F16X2, dot2_f16(hp[u][4 * q + 2], ONES_F16X2, se));
+                        so = dot2_f16(hp[u][4 * q + 1], ONES_F16X2, dot2_f16(hp[u][4 * q + 3], ONES_F16X2, so));
+                    }
+                    ha[u] = OFFSET_F16 * (se + so);
+                    hb[u] = fmaf(16.f, so, se);
+                }
+            }
         };
         auto consume = [&](const Stage &st, int s0) {
 #pragma unroll
@@ -394,20 +435,25 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
                 const int dl = row_of(s0 + b);
                 float sd, md;
                 group_params<FMT>(st.s[b], sd, md);
-                const float cd = md - OFFSET_F16 * sd;
+                // even codes enter as 1024 + q, odd codes in place as
+                // 1024 + 16 q against h / 16: the dot is sum h q + ha
                 const uint32_t d4[4] = {st.v[b].x, st.v[b].y, st.v[b].z, st.v[b].w};
                 uint32_t dw[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int pp = 0; pp < 4; ++pp) dw[4 * q + pp] = unpack_pair<MAGIC_F16>(d4[q], pp);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w8 = d4[q] >> 8;
+                    dw[4 * q + 0] = insert_codes<0x000f000fu>(d4[q], kf);  // codes 0, 4
+                    dw[4 * q + 1] = insert_codes<0x00f000f0u>(d4[q], kf);  // codes 1, 5 (x16)
+                    dw[4 * q + 2] = insert_codes<0x000f000fu>(w8, kf);     // codes 2, 6
+                    dw[4 * q + 3] = insert_codes<0x00f000f0u>(w8, kf);     // codes 3, 7 (x16)
+                }
 #pragma unroll
                 for (int u = 0; u < DECODE_TT; ++u) {
                     if (u < nt) {
                         float a = 0.f;
 #pragma unroll
                         for (int i = 0; i < 16; ++i) a = dot2_f16(dw[i], hp[u][i], a);
-                        const float o = seg_sum_dpp<LPR>(fmaf(sd, a, cd * hs[u]));
+                        const float o = seg_sum_dpp<LPR>(fmaf(sd, a - ha[u], md * hb[u]));
                         if (c == LPR - 1 && dl < rb && s0 + b < steps) s_out[u][dl] = gt[u] * o;
                     }
                 }
@@ -416,13 +462,15 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         // stages of DEC_NB row loads, pipelined as in the gate/up GEMV
         const int nst = (steps + DEC_NB - 1) / DEC_NB;
         if (nst == 1) {
+            fetch_h();
             issue(sa, 0);
-            load_h();
+            sum_h();
             consume(sa, 0);
         } else {
+            fetch_h();
             issue(sa, 0);
             issue(sb, DEC_NB);
-            load_h();
+            sum_h();
             for (int q = 0; q < nst; q += 2) {
                 consume(sa, q * DEC_NB);
                 issue(sa, (q + 2) * DEC_NB);
@@ -612,7 +660,7 @@ static int resident_grid(K kernel) {
 
 template <int FMT, bool ROUTE>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                     const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
+                                     const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
@@ -623,7 +671,7 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     case LP: {                                                                                                   \
         auto kern = decode_gateup_kernel<LP, FMT, ROUTE>;                                                        \
         launch_k(kern, dim3(resident_grid(kern)), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,     \
-                 (const int32_t *)g.ntiles, mt, (const int32_t *)g.perm, h, lg, (int)T, idx_out, gate_out, g);   \
+                 (const int32_t *)g.ntiles, mt, h, lg, (int)T, idx_out, gate_out, g);                            \
     } break;
         CASE(1) CASE(2) CASE(4) CASE(8) CASE(16) CASE(32)
 #undef CASE
@@ -634,8 +682,8 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     case LP: {                                                                                                   \
         auto kern = decode_down_kernel<LP, FMT>;                                                                 \
         launch_k(kern, dim3(resident_grid(kern)), block, s, nullptr, nullptr, H, I, k, P, L,                     \
-                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, (const int32_t *)g.perm, gate,            \
-                 (const float *)h, y);                                                                           \
+                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate,                                     \
+                 (const uint16_t *)h, y);                                                                           \
     } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
@@ -645,7 +693,7 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
 }
 
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
+                                 const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
                                  hipEvent_t e1) {
     return L.fmt == 0 ? launch_experts_fmt<0, false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr)
                       : launch_experts_fmt<1, false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr);
@@ -660,7 +708,7 @@ bool decode_routes_in_block(int64_t T, int k, int E) {
 }
 
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
-                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
+                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, uint16_t *h,
                                         float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;
     return L.fmt == 0 ? launch_experts_fmt<0, true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate)

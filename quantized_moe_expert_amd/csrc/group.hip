@@ -59,18 +59,25 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
                                                              GroupOut g) {
     __shared__ unsigned long long s_mask[1024];
     __shared__ int s_off[1024];
+    __shared__ int s_tadj[1024];
     __shared__ int s_scan[17];
     const int c = blockIdx.x, tid = threadIdx.x;
     const int v = tid < E ? g.cnt[tid] : 0;
     if (tid < E) s_mask[tid] = 0ull;
-    int excl;
+    int excl, tadj;
     if (c == 0) {
-        emit_offsets_and_tiles(v, E, P, g, s_scan, &excl);
+        emit_offsets_and_tiles(v, E, P, g, s_scan, &excl, &tadj);
     } else {
         int total;
         excl = block_exclusive_scan(v, s_scan, &total);
+        const int S = g.rows_per_tile;
+        const int toff = block_exclusive_scan(tid < E ? (v + S - 1) / S : 0, s_scan, &total);
+        tadj = toff * S - excl;
     }
-    if (tid < E) s_off[tid] = excl;
+    if (tid < E) {
+        s_off[tid] = excl;
+        s_tadj[tid] = tadj;
+    }
     __syncthreads();
     const int p = c * GROUP_CHUNK + tid;
     const bool mine = tid < GROUP_CHUNK && p < P;
@@ -84,6 +91,7 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
         const int pos = s_off[e] + g.chunk_base[(size_t)c * E + e] + __popcll(s_mask[e] & ((1ull << tid) - 1ull));
         g.perm[pos] = p;
         g.inv[p] = pos;
+        record_tile_pair(g, pos, s_tadj[e], p);
     }
 }
 

@@ -52,6 +52,20 @@ template <uint32_t MAGIC>
 __device__ __forceinline__ uint32_t unpack_pair(uint32_t w, int j) {
     return ((w >> (4 * j)) & 0x000f000fu) | MAGIC;
 }
+// The same with one bitfield insert (v_bfi_b32): (w & MASK) | (magic & ~MASK),
+// where magic comes from opaque_magic() once per kernel.  Kept opaque, the
+// constant is not folded into the and + or pair the compiler otherwise
+// emits.  MASK 0x000f000f takes codes 0 and 4 of w (value OFFSET + q); for
+// f16, MASK 0x00f000f0 takes codes 1 and 5 in place, bits 4..7 of the
+// mantissa, value 1024 + 16 q (exact: 1024..1264 are f16 integers).
+template <uint32_t MASK>
+__device__ __forceinline__ uint32_t insert_codes(uint32_t w, uint32_t magic) {
+    return (w & MASK) | (magic & ~MASK);
+}
+__device__ __forceinline__ uint32_t opaque_magic(uint32_t magic) {
+    asm volatile("" : "+v"(magic));
+    return magic;
+}
 constexpr uint32_t MAGIC_BF16 = 0x43004300u;   // 128 + q
 constexpr uint32_t MAGIC_F16 = 0x64006400u;    // 1024 + q
 constexpr float OFFSET_BF16 = 128.0f;

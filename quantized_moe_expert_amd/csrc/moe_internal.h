@@ -7,14 +7,21 @@
 
 namespace moeq4 {
 
+constexpr int DECODE_TT = 2;  // tokens per decode work item
+
 // Work item of the expert kernels: `rows` consecutive sorted rows of one
-// expert starting at sorted position `row0`.
+// expert starting at sorted position `row0`; pair[u] is the flat (token,
+// slot) index t * k + i of row row0 + u for u < min(rows, DECODE_TT) (-1
+// otherwise), so that the decode kernels need no permutation lookup.
 struct Tile {
     int expert;
     int row0;
     int rows;
     int pad;
+    int pair[DECODE_TT];
+    int pad2[4 - DECODE_TT];
 };
+static_assert(sizeof(Tile) == 32, "Tile is two 16-byte words");
 
 // Layer pointers as the kernels take them.
 struct LayerPtrs {
@@ -25,7 +32,6 @@ struct LayerPtrs {
 
 constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chunk
 constexpr int GROUP_SINGLE_MAX = 1024;   // pairs handled by the one-block grouping
-constexpr int DECODE_TT = 2;             // tokens per decode work item
 constexpr int PREFILL_BM = 128;          // rows per prefill tile
 constexpr int ROUTE_LDS_LOGITS = 16384;  // T * E limit of the one-launch decode routing
 constexpr int ROUTE_TC = 16;             // tokens staged per pass of the one-launch routing
@@ -63,11 +69,12 @@ hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const Group
                         float *yclear = nullptr, int64_t yclear_n = 0, hipEvent_t e0 = nullptr,
                         hipEvent_t e1 = nullptr);
 
-// Decode expert kernels: gate/up + SwiGLU -> h (fp32 [T*k][I]), then down
-// with the gate-weighted add into y (y must be cleared first).  e0 / e1 time
-// the gate/up kernel.
+// Decode expert kernels: gate/up + SwiGLU -> h (f16 [T*k][I], each 8-block
+// in PERM8 order, odd elements divided by 16), then down with the
+// gate-weighted add into y (y must be cleared first).  e0 / e1 time the
+// gate/up kernel.
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
+                                 const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
                                  hipEvent_t e1 = nullptr);
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64
@@ -88,7 +95,7 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
 // holds up to 256 pairs).  y must be cleared first.
 bool decode_routes_in_block(int64_t T, int k, int E);
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
-                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
+                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, uint16_t *h,
                                         float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
