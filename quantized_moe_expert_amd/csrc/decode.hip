@@ -131,6 +131,51 @@ __device__ __forceinline__ Items decode_items(int nt, int N, int maxch) {
     return it;
 }
 
+// Rows of one item.  With DEC_INTERLEAVE, chunk `chunk` of nch takes the
+// row blocks chunk, chunk + nch, chunk + 2 nch, ... of BR rows (BR: the rows
+// one step of the workgroup covers), so that at any time the workgroups of a
+// tile read neighbouring blocks of the expert's matrix; otherwise it takes
+// `rows` consecutive rows.  Local row nl (0 <= nl < nloc = steps * BR, or the
+// chunk's row count) is global row grow(nl); valid() excludes rows past N.
+// nloc <= DEC_RB_MAX: decode_items makes nch >= N / DEC_RB_MAX, and BR is a
+// power of two dividing DEC_RB_MAX.
+constexpr bool DEC_INTERLEAVE = true;
+template <int BR>
+struct ItemRows {
+    int chunk, nch, rows, steps, nloc, N;
+    __device__ __forceinline__ int grow(int nl) const {
+        return DEC_INTERLEAVE ? ((nl / BR) * nch + chunk) * BR + nl % BR : chunk * rows + nl;
+    }
+    __device__ __forceinline__ bool valid(int nl) const { return nl < nloc && grow(nl) < N; }
+    // the same for local row s * BR + lrow (step s, 0 <= lrow < BR)
+    __device__ __forceinline__ int grow_step(int s, int lrow) const {
+        return DEC_INTERLEAVE ? (s * nch + chunk) * BR + lrow : chunk * rows + s * BR + lrow;
+    }
+    __device__ __forceinline__ bool valid_step(int s, int lrow) const {
+        return s < steps && grow_step(s, lrow) < N && (DEC_INTERLEAVE || s * BR + lrow < nloc);
+    }
+};
+template <int BR>
+__device__ __forceinline__ ItemRows<BR> item_rows(int chunk, const Items &it, int N) {
+    static_assert(BR > 0 && (BR & (BR - 1)) == 0 && DEC_RB_MAX % BR == 0, "row blocks tile DEC_RB_MAX");
+    ItemRows<BR> r;
+    r.chunk = chunk;
+    r.nch = it.nch;
+    r.rows = it.rows;
+    r.N = N;
+    if (DEC_INTERLEAVE) {
+        const int nblk = (N + BR - 1) / BR;
+        r.steps = chunk < nblk ? (nblk - chunk + it.nch - 1) / it.nch : 0;
+        r.nloc = r.steps * BR;
+    } else {
+        const int n0 = chunk * it.rows;
+        r.nloc = N - n0 < it.rows ? N - n0 : it.rows;
+        r.nloc = r.nloc < 0 ? 0 : r.nloc;
+        r.steps = (r.nloc + BR - 1) / BR;
+    }
+    return r;
+}
+
 constexpr int DEC_WAVES = 4;  // waves per decode workgroup
 constexpr int DEC_NB = 2;     // row loads per lane per pipeline stage
 
@@ -229,14 +274,13 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
         const int j = w / it.nch, chunk = w % it.nch;
         const Tile tile = sane_tile(tiles[j], L.E, P);
         const int e = tile.expert, nt = tile.rows;
-        const int n0 = chunk * it.rows;
-        const int rb = I - n0 < it.rows ? I - n0 : it.rows;
-        if (rb <= 0) continue;
-        const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);  // wave-loads per wave
-        auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
+        const ItemRows<DEC_WAVES * RPW> ir = item_rows<DEC_WAVES * RPW>(chunk, it, I);
+        if (ir.steps <= 0) continue;
+        const int steps = ir.steps;  // wave-loads per wave
+        const int lrow = wave * RPW + sub;  // the lane's row within a step
+        auto row_of = [&](int s) { return s * (DEC_WAVES * RPW) + lrow; };
         auto issue = [&](Stage &st, int s) {
-            const int nl = row_of(s);
-            const size_t row = (size_t)e * I + n0 + (nl < rb ? nl : 0);
+            const size_t row = (size_t)e * I + (ir.valid_step(s, lrow) ? ir.grow_step(s, lrow) : ir.grow(0));
             const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 32 * c);
             const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 32 * c);
             st.g[0] = gp[0];
@@ -296,7 +340,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
                 if (u < nt) {
                     const float pg = seg_sum_dpp<LPR>(fmaf(sg, dg[u], cg * xs[u]));
                     const float pu = seg_sum_dpp<LPR>(fmaf(su, du[u], cu * xs[u]));
-                    if (c == LPR - 1 && nl < rb) s_out[u][nl] = silu(pg) * pu;
+                    if (c == LPR - 1 && ir.valid_step(s, lrow)) s_out[u][nl] = silu(pg) * pu;
                 }
             }
         };
@@ -328,9 +372,11 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
         // h in f16 as the down GEMV consumes it: each 8-block in PERM8 order
         // (element j at 2j for j < 4, at 2(j - 4) + 1 otherwise), odd
         // elements divided by 16 (exact scaling by a power of two)
-        for (int i = threadIdx.x; i < nt * rb; i += blockDim.x) {
-            const int u = i / rb, n = n0 + i % rb;
-            const float v = (n & 1) ? s_out[u][i % rb] * (1.f / 16.f) : s_out[u][i % rb];
+        for (int i = threadIdx.x; i < nt * ir.nloc; i += blockDim.x) {
+            const int u = i / ir.nloc, nl = i % ir.nloc;
+            if (!ir.valid(nl)) continue;
+            const int n = ir.grow(nl);
+            const float v = (n & 1) ? s_out[u][nl] * (1.f / 16.f) : s_out[u][nl];
             const int slot = (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1);
             h[(size_t)(tile.row0 + u) * I + slot] = __builtin_bit_cast(uint16_t, (_Float16)v);
         }
@@ -368,16 +414,16 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         const int j = w / it.nch, chunk = w % it.nch;
         const Tile tile = sane_tile(tiles[j], L.E, P);
         const int e = tile.expert, nt = tile.rows;
-        const int d0 = chunk * it.rows;
-        const int rb = H - d0 < it.rows ? H - d0 : it.rows;
-        if (rb <= 0) continue;
-        const int steps = (rb + DEC_WAVES * RPW - 1) / (DEC_WAVES * RPW);
-        auto row_of = [&](int s) { return (s * DEC_WAVES + wave) * RPW + sub; };
+        const ItemRows<DEC_WAVES * RPW> ir = item_rows<DEC_WAVES * RPW>(chunk, it, H);
+        if (ir.steps <= 0) continue;
+        const int steps = ir.steps;
+        const int lrow = wave * RPW + sub;  // the lane's row within a step
+        auto row_of = [&](int s) { return s * (DEC_WAVES * RPW) + lrow; };
         auto issue = [&](Stage &st, int s0) {
 #pragma unroll
             for (int b = 0; b < DEC_NB; ++b) {
-                const int dl = row_of(s0 + b);
-                const size_t row = (size_t)e * H + d0 + (dl < rb ? dl : 0);
+                const int sb_ = s0 + b;
+                const size_t row = (size_t)e * H + (ir.valid_step(sb_, lrow) ? ir.grow_step(sb_, lrow) : ir.grow(0));
                 st.v[b] = *reinterpret_cast<const uint4 *>(L.dq + row * row_bytes + 16 * c);
                 st.s[b] = load_group_word<FMT>(L.dsm + row * smr, gi);
             }
@@ -454,7 +500,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
 #pragma unroll
                         for (int i = 0; i < 16; ++i) a = dot2_f16(dw[i], hp[u][i], a);
                         const float o = seg_sum_dpp<LPR>(fmaf(sd, a - ha[u], md * hb[u]));
-                        if (c == LPR - 1 && dl < rb && s0 + b < steps) s_out[u][dl] = gt[u] * o;
+                        if (c == LPR - 1 && ir.valid_step(s0 + b, lrow)) s_out[u][dl] = gt[u] * o;
                     }
                 }
             }
@@ -480,9 +526,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         }
         __syncthreads();
         // one float atomic per output and routed (token, slot), coalesced
-        for (int i = threadIdx.x; i < nt * rb; i += blockDim.x) {
-            const int u = i / rb, d = i % rb;
-            unsafeAtomicAdd(y + (size_t)tok[u] * H + d0 + d, s_out[u][d]);
+        for (int i = threadIdx.x; i < nt * ir.nloc; i += blockDim.x) {
+            const int u = i / ir.nloc, d = i % ir.nloc;
+            if (ir.valid(d)) unsafeAtomicAdd(y + (size_t)tok[u] * H + ir.grow(d), s_out[u][d]);
         }
         __syncthreads();
     }
@@ -524,31 +570,26 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     const uint16_t *lsrc = logits;
     if (wr) {
         const int e = blockIdx.x;  // grid = E
-        double wd[4][8];
+        // the expert's router row, 8 bf16 per lane and quarter (H <= 2048)
+        uint4 wv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int hh = (q * WAVE + lane) * 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (hh < H) v = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                wd[q][2 * jj] = (double)bf16_to_f32(w4[jj] & 0xffffu);
-                wd[q][2 * jj + 1] = (double)bf16_to_f32(w4[jj] >> 16);
-            }
+            wv[q] = make_uint4(0, 0, 0, 0);
+            if (hh < H) wv[q] = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
         }
         const double b = bias ? (double)bias[e] : 0.0;
         for (int t0 = 0; t0 < T; t0 += ROUTE_TC) {
             const int tc = T - t0 < ROUTE_TC ? T - t0 : ROUTE_TC;
-            const int nvec = tc * (H / 8);
+            const int nvec = tc * (H / 8);  // <= ROUTE_TC * 256 = 4 pieces per thread
             __syncthreads();  // previous chunk consumed
-            for (int i0 = tid; i0 < nvec; i0 += 2 * 1024) {
-                // two 8-element pieces per thread, their loads in flight together
-                uint4 v[2];
-                float4 ya[2], yb[2];
+            {
+                // all pieces' loads in flight together
+                uint4 v[4];
+                float4 ya[4], yb[4];
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int i = i0 + r * 1024;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = tid + r * 1024;
                     if (i < nvec) {
                         const size_t gi = (size_t)(t0 + i / (H / 8)) * H + (i % (H / 8)) * 8;
                         v[r] = *reinterpret_cast<const uint4 *>(x + gi);
@@ -559,8 +600,8 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
                     }
                 }
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int i = i0 + r * 1024;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = tid + r * 1024;
                     if (i < nvec) {
                         uint4 o = v[r];
                         if (yres) {
@@ -588,10 +629,15 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
                     if (hh < H) {
                         const uint4 xv = *reinterpret_cast<const uint4 *>(&s_x[tl * H + hh]);
                         const uint32_t xs4[4] = {xv.x, xv.y, xv.z, xv.w};
+                        uint32_t ws4[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
+                        // converted per token (a wave takes one token when T <= 16):
+                        // hoisting 32 doubles out of the loop would spill
+                        asm volatile("" : "+v"(ws4[0]), "+v"(ws4[1]), "+v"(ws4[2]), "+v"(ws4[3]));
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
-                            acc = fma((double)bf16_to_f32(xs4[jj] & 0xffffu), wd[q][2 * jj], acc);
-                            acc = fma((double)bf16_to_f32(xs4[jj] >> 16), wd[q][2 * jj + 1], acc);
+                            acc = fma((double)bf16_to_f32(xs4[jj] & 0xffffu), (double)bf16_to_f32(ws4[jj] & 0xffffu),
+                                      acc);
+                            acc = fma((double)bf16_to_f32(xs4[jj] >> 16), (double)bf16_to_f32(ws4[jj] >> 16), acc);
                         }
                     }
                 }

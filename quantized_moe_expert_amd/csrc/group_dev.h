@@ -10,30 +10,18 @@ namespace moeq4 {
 // Returns the exclusive prefix of v; *total receives the block sum.
 __device__ inline int block_exclusive_scan(int v, int *lds16, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const int n = __shfl_up(inc, o, WAVE);
-        if (lane >= o) inc += n;
-    }
+    const int inc = wave_inclusive_scan_i32(v);
     if (lane == 63) lds16[wave] = inc;
     __syncthreads();
-    if (wave == 0) {
-        int w = lane < nw ? lds16[lane] : 0;
-        int winc = w;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int n = __shfl_up(winc, o, WAVE);
-            if (lane >= o) winc += n;
-        }
-        if (lane < nw) lds16[lane] = winc - w;   // exclusive wave offsets
-        if (lane == nw - 1) lds16[16] = winc;    // block total
+    int pre = 0, tot = 0;  // totals of the waves before this one, of all waves
+    for (int w = 0; w < nw; ++w) {
+        const int t = lds16[w];
+        pre += w < wave ? t : 0;
+        tot += t;
     }
-    __syncthreads();
-    const int r = lds16[wave] + inc - v;
-    *total = lds16[16];
-    __syncthreads();
-    return r;
+    __syncthreads();  // lds16 free for the next scan
+    *total = tot;
+    return pre + inc - v;
 }
 
 // Offsets + tile list from per-expert counts held by thread e (< E).  Only
@@ -87,6 +75,37 @@ __device__ inline void group_block_single(const int32_t *idx, int P, int E, cons
     __shared__ int s_tadj[1024];
     __shared__ int s_scan[17];
     const int tid = threadIdx.x;
+    const int nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
+    if (nch * E <= 1024) {
+        // One pass over all chunks: s_mask[c * E + e] marks the pairs of
+        // chunk c routed to expert e; counts and stable ranks are population
+        // counts of these words.
+        for (int i = tid; i < nch * E; i += blockDim.x) s_mask[i] = 0ull;
+        __syncthreads();
+        for (int p = tid; p < P; p += blockDim.x)
+            atomicOr(&s_mask[(p / GROUP_CHUNK) * E + clamp_expert(idx[p], E)], 1ull << (p % GROUP_CHUNK));
+        __syncthreads();
+        int v = 0;
+        if (tid < E)
+            for (int c = 0; c < nch; ++c) v += __popcll(s_mask[c * E + tid]);
+        int excl, tadj;
+        emit_offsets_and_tiles(v, E, P, g, s_scan, &excl, &tadj);
+        if (tid < E) {
+            s_base[tid] = excl;
+            s_tadj[tid] = tadj;
+        }
+        __syncthreads();
+        for (int p = tid; p < P; p += blockDim.x) {
+            const int e = clamp_expert(idx[p], E), c = p / GROUP_CHUNK;
+            int r = __popcll(s_mask[c * E + e] & ((1ull << (p % GROUP_CHUNK)) - 1ull));
+            for (int cc = 0; cc < c; ++cc) r += __popcll(s_mask[cc * E + e]);
+            const int pos = s_base[e] + r;
+            g.perm[pos] = p;
+            g.inv[p] = pos;
+            record_tile_pair(g, pos, s_tadj[e], p);
+        }
+        return;
+    }
     if (tid < E) s_cnt[tid] = 0;
     __syncthreads();
     for (int p = tid; p < P; p += blockDim.x) atomicAdd(&s_cnt[clamp_expert(idx[p], E)], 1);

@@ -145,6 +145,28 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
 }
 
+// The double sum of the whole wave in every lane.
+__device__ __forceinline__ double wave_allsum_f64_dpp(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, wave_sum_f64_dpp(v));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive prefix sum over the wave with DPP moves: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes (lanes shifted in from outside the row add 0),
+// then the last lane of row 0 / 2 added into rows 1 / 3 and lane 31 into
+// rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan_i32(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 // Whole-wave unsigned max with DPP moves, returned to every lane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     uint32_t t;

@@ -69,7 +69,7 @@ __device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, in
     const double l0 = (double)bf16_to_f32(l[e0]);
     double ex = 0.0;
     if (lane < k) ex = exp((double)bf16_to_f32(l[my_e]) - l0);
-    const double den = wave_sum_f64(ex);
+    const double den = wave_allsum_f64_dpp(ex);
     if (lane < k) {
         idx_out[lane] = my_e;
         gate_out[lane] = (float)(ex / den);
