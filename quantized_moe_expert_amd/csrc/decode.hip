@@ -185,194 +185,188 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v_t, a), __builtin_bit_cast(half2v_t, b), c, false);
 }
 
+// Routing inside an expert workgroup (few tokens): top-k per token and the
+// one-block grouping from the logits lg (written by the previous launch),
+// into LDS.  Every workgroup does it; workgroup 0 also publishes the
+// indices, gates and grouping arrays (idx_out, gate_out, gout) for the
+// caller.  Returns the tile count; *tiles_lds and *gates_lds point at the
+// LDS copies.
+__device__ __forceinline__ int route_in_block(const uint16_t *__restrict__ lg, int T, int E, int k, int P,
+                                              int32_t *__restrict__ idx_out, float *__restrict__ gate_out,
+                                              const GroupOut &gout, const Tile **tiles_lds,
+                                              const float **gates_lds) {
+    __shared__ int32_t r_idx[DEC_ROUTE_PMAX];
+    __shared__ float r_gate[DEC_ROUTE_PMAX];
+    __shared__ int32_t r_cnt[DEC_ROUTE_EMAX], r_off[DEC_ROUTE_EMAX + 1], r_perm[DEC_ROUTE_PMAX],
+        r_inv[DEC_ROUTE_PMAX];
+    __shared__ Tile r_tiles[DEC_ROUTE_TMAX];
+    __shared__ int32_t r_nt;
+    __shared__ __attribute__((aligned(16))) uint16_t r_lg[DEC_ROUTE_LOGITS];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const bool b0 = blockIdx.x == 0;
+    // all logits in one coalesced pass (the top-k rounds then read LDS only)
+    {
+        const int n = T * E;
+        for (int i = tid * 8; i < n; i += blockDim.x * 8) {
+            if (i + 8 <= n && ((reinterpret_cast<uintptr_t>(lg) & 15) == 0))
+                *reinterpret_cast<uint4 *>(&r_lg[i]) = *reinterpret_cast<const uint4 *>(lg + i);
+            else
+                for (int q = i; q < n && q < i + 8; ++q) r_lg[q] = lg[q];
+        }
+    }
+    __syncthreads();
+    for (int t = wave; t < T; t += blockDim.x / 64)
+        topk_token_wave<DEC_ROUTE_NPL>(r_lg + (size_t)t * E, E, k, r_idx + t * k, r_gate + t * k);
+    __syncthreads();
+    GroupOut gl;
+    gl.cnt = r_cnt;
+    gl.off = r_off;
+    gl.perm = r_perm;
+    gl.inv = r_inv;
+    gl.tiles = r_tiles;
+    gl.ntiles = &r_nt;
+    gl.rows_per_tile = DECODE_TT;
+    gl.chunk_cnt = gl.chunk_base = nullptr;
+    group_block_single(r_idx, P, E, gl);
+    __syncthreads();
+    const int nt_all = r_nt;
+    if (b0) {
+        for (int i = tid; i < P; i += blockDim.x) {
+            idx_out[i] = r_idx[i];
+            gate_out[i] = r_gate[i];
+            gout.perm[i] = r_perm[i];
+            gout.inv[i] = r_inv[i];
+        }
+        for (int i = tid; i < E; i += blockDim.x) gout.cnt[i] = r_cnt[i];
+        for (int i = tid; i <= E; i += blockDim.x) gout.off[i] = r_off[i];
+        for (int i = tid; i < nt_all; i += blockDim.x) gout.tiles[i] = r_tiles[i];
+        if (tid == 0) *gout.ntiles = nt_all;
+    }
+    *tiles_lds = r_tiles;
+    *gates_lds = r_gate;
+    return nt_all;
+}
+
 // gate/up GEMV + SwiGLU for one item (tile: one expert, up to DECODE_TT
-// tokens; chunk: rows [n0, n0 + rb) of h): h[row0 + u][n] in fp32.  Lanes run
-// along the input dimension: LPR = H / 64 lanes per row, each lane 32 bytes =
-// 64 codes (one 64-group), so a wave-load covers RPW = 64 / LPR rows of gate
-// and of up (2 rows of 1 KB each when H = 2048).  The next wave-load is in
-// flight while the current one is reduced.
-// With ROUTE, every workgroup first routes the tokens itself from the logits
-// lg (written by the previous launch): top-k per token and the one-block
-// grouping, into LDS; workgroup 0 also publishes the indices, gates and
-// grouping arrays (idx_out, gate_out, gout) for the down GEMV and the caller.
-// This replaces a serial last-workgroup step of the routing launch.
-template <int LPR, int FMT, bool ROUTE>
-__global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
-    const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, int max_nt, uint16_t *__restrict__ h, const uint16_t *__restrict__ lg, int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out,
-    GroupOut gout) {
+// tokens; rows ir of I) into h.  Lanes run along the input dimension: LPR =
+// H / 64 lanes per row, each lane 32 bytes = 64 codes (one 64-group), so a
+// wave-load covers RPW = 64 / LPR rows of gate and of up (2 rows of 1 KB
+// each when H = 2048).  The next wave-load is in flight while the current
+// one is reduced.  h is written in f16 as the down GEMV consumes it: each
+// 8-block in PERM8 order (element j at 2j for j < 4, at 2(j - 4) + 1
+// otherwise), odd elements divided by 16 (exact scaling by a power of two).
+// SHORT: items of a single wave-load are common (few tokens), and take a
+// straight path instead of issuing unused stages.
+template <int LPR, int FMT, bool SHORT>
+__device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int H, int I, int k, const LayerPtrs &L,
+                                            const Tile &tile, const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
+                                            uint16_t *__restrict__ h, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;  // rows per wave-load
     constexpr int G = FMT == 0 ? 64 : 128;
-    int nt_all;
-    if constexpr (ROUTE) {
-        __shared__ int32_t r_idx[DEC_ROUTE_PMAX];
-        __shared__ float r_gate[DEC_ROUTE_PMAX];
-        __shared__ int32_t r_cnt[DEC_ROUTE_EMAX], r_off[DEC_ROUTE_EMAX + 1], r_perm[DEC_ROUTE_PMAX],
-            r_inv[DEC_ROUTE_PMAX];
-        __shared__ Tile r_tiles[DEC_ROUTE_TMAX];
-        __shared__ int32_t r_nt;
-        __shared__ __attribute__((aligned(16))) uint16_t r_lg[DEC_ROUTE_LOGITS];
-        const int E = L.E, tid = threadIdx.x, wave = tid >> 6;
-        const bool b0 = blockIdx.x == 0;
-        // all logits in one coalesced pass (the top-k rounds then read LDS only)
-        {
-            const int n = T * E;
-            for (int i = tid * 8; i < n; i += blockDim.x * 8) {
-                if (i + 8 <= n && ((reinterpret_cast<uintptr_t>(lg) & 15) == 0))
-                    *reinterpret_cast<uint4 *>(&r_lg[i]) = *reinterpret_cast<const uint4 *>(lg + i);
-                else
-                    for (int q = i; q < n && q < i + 8; ++q) r_lg[q] = lg[q];
-            }
-        }
-        __syncthreads();
-        for (int t = wave; t < T; t += DEC_WAVES) {
-            if (b0) topk_token_wave<DEC_ROUTE_NPL>(r_lg + (size_t)t * E, E, k, idx_out + t * k, gate_out + t * k,
-                                                   r_idx + t * k);
-            else topk_token_wave<DEC_ROUTE_NPL>(r_lg + (size_t)t * E, E, k, r_idx + t * k, r_gate + t * k);
-        }
-        __syncthreads();
-        GroupOut gl;
-        gl.cnt = r_cnt;
-        gl.off = r_off;
-        gl.perm = r_perm;
-        gl.inv = r_inv;
-        gl.tiles = r_tiles;
-        gl.ntiles = &r_nt;
-        gl.rows_per_tile = DECODE_TT;
-        gl.chunk_cnt = gl.chunk_base = nullptr;
-        group_block_single(r_idx, P, E, gl);
-        __syncthreads();
-        nt_all = r_nt;
-        if (b0) {
-            for (int i = tid; i < E; i += blockDim.x) gout.cnt[i] = r_cnt[i];
-            for (int i = tid; i <= E; i += blockDim.x) gout.off[i] = r_off[i];
-            for (int i = tid; i < P; i += blockDim.x) {
-                gout.perm[i] = r_perm[i];
-                gout.inv[i] = r_inv[i];
-            }
-            for (int i = tid; i < nt_all; i += blockDim.x) gout.tiles[i] = r_tiles[i];
-            if (tid == 0) *gout.ntiles = nt_all;
-        }
-        tiles = r_tiles;
-    } else {
-        nt_all = *ntiles;
-    }
-    nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
-    const Items it = decode_items(nt_all, I, I / (DEC_WAVES * RPW));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR, sub = lane / LPR;
     const size_t row_bytes = (size_t)H / 2;
     const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
     const int gi = (64 * c) / G;
     const uint32_t kb = opaque_magic(MAGIC_BF16);
-    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     struct Stage {
         uint4 g[2], u[2];
         uint32_t gs, us;
     };
-    for (int w = it.first; w < it.end; w += it.stride) {
-        const int j = w / it.nch, chunk = w % it.nch;
-        const Tile tile = sane_tile(tiles[j], L.E, P);
-        const int e = tile.expert, nt = tile.rows;
-        const ItemRows<DEC_WAVES * RPW> ir = item_rows<DEC_WAVES * RPW>(chunk, it, I);
-        if (ir.steps <= 0) continue;
-        const int steps = ir.steps;  // wave-loads per wave
-        const int lrow = wave * RPW + sub;  // the lane's row within a step
-        auto row_of = [&](int s) { return s * (DEC_WAVES * RPW) + lrow; };
-        auto issue = [&](Stage &st, int s) {
-            const size_t row = (size_t)e * I + (ir.valid_step(s, lrow) ? ir.grow_step(s, lrow) : ir.grow(0));
-            const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 32 * c);
-            const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 32 * c);
-            st.g[0] = gp[0];
-            st.g[1] = gp[1];
-            st.u[0] = up[0];
-            st.u[1] = up[1];
-            st.gs = load_group_word<FMT>(L.gsm + row * smr, gi);
-            st.us = load_group_word<FMT>(L.usm + row * smr, gi);
-        };
-        // Activations: fetched before the first weight stages (they depend
-        // on the tile only), reordered after them, so that waiting for them
-        // leaves the stages in flight.
-        uint32_t xp[DECODE_TT][32];
-        float xs[DECODE_TT];
-        auto fetch_x = [&]() {
+    const int e = tile.expert, nt = tile.rows;
+    const int steps = ir.steps;         // wave-loads per wave
+    const int lrow = wave * RPW + sub;  // the lane's row within a step
+    auto row_of = [&](int s) { return s * (DEC_WAVES * RPW) + lrow; };
+    auto issue = [&](Stage &st, int s) {
+        const size_t row = (size_t)e * I + (ir.valid_step(s, lrow) ? ir.grow_step(s, lrow) : ir.grow(0));
+        const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 32 * c);
+        const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 32 * c);
+        st.g[0] = gp[0];
+        st.g[1] = gp[1];
+        st.u[0] = up[0];
+        st.u[1] = up[1];
+        st.gs = load_group_word<FMT>(L.gsm + row * smr, gi);
+        st.us = load_group_word<FMT>(L.usm + row * smr, gi);
+    };
+    // Activations: fetched before the first weight stages (they depend on
+    // the tile only), reordered after them, so that waiting for them leaves
+    // the stages in flight.
+    uint32_t xp[DECODE_TT][32];
+    float xs[DECODE_TT];
+    auto fetch_x = [&]() {
 #pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) {
-                if (u < nt) {
-                    const uint16_t *xrow = x + (size_t)(tile.pair[u] / k) * H;
-                    fetch_x_chunk(xrow, 2 * c, xp[u]);
-                    fetch_x_chunk(xrow, 2 * c + 1, xp[u] + 16);
-                }
-            }
-        };
-        auto prep_x = [&]() {
-#pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) {
-                xs[u] = 0.f;
-                if (u < nt) xs[u] = perm_x_chunk(xp[u]) + perm_x_chunk(xp[u] + 16);
-            }
-        };
-        Stage sa, sb;
-        auto consume = [&](const Stage &st, int s) {
-            const int nl = row_of(s);
-            float sg, mg, su, mu;
-            group_params<FMT>(st.gs, sg, mg);
-            group_params<FMT>(st.us, su, mu);
-            const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
-            // one code quad unpacked at a time, applied to every token of the tile
-            float dg[DECODE_TT], du[DECODE_TT];
-#pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) dg[u] = du[u] = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t wq[16];
-                unpack32(q == 0 ? st.g[0] : q == 1 ? st.g[1] : q == 2 ? st.u[0] : st.u[1], wq, kb);
-#pragma unroll
-                for (int u = 0; u < DECODE_TT; ++u) {
-                    if (u < nt) {
-                        if (q < 2) dg[u] = dot16(wq, xp[u] + 16 * (q & 1), dg[u]);
-                        else du[u] = dot16(wq, xp[u] + 16 * (q & 1), du[u]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) {
-                if (u < nt) {
-                    const float pg = seg_sum_dpp<LPR>(fmaf(sg, dg[u], cg * xs[u]));
-                    const float pu = seg_sum_dpp<LPR>(fmaf(su, du[u], cu * xs[u]));
-                    if (c == LPR - 1 && ir.valid_step(s, lrow)) s_out[u][nl] = silu(pg) * pu;
-                }
-            }
-        };
-        // Two register stages, the next one in flight while the current one is
-        // reduced.  The first rows depend only on the tile, so they are issued
-        // before the tokens are known.  The loop issues every stage (rows past
-        // the item re-read its first row) and outputs go to LDS, so it holds
-        // only loads and the compiler's memory-counter waits stay exact.  The
-        // routing variant (a few tokens: items of one wave-load are common)
-        // takes a straight path for them instead of issuing unused stages.
-        if (ROUTE && steps == 1) {
-            fetch_x();
-            issue(sa, 0);
-            prep_x();
-            consume(sa, 0);
-        } else {
-            fetch_x();
-            issue(sa, 0);
-            issue(sb, 1);
-            prep_x();
-            for (int s = 0; s < steps; s += 2) {
-                consume(sa, s);
-                issue(sa, s + 2);
-                if (s + 1 < steps) consume(sb, s + 1);
-                issue(sb, s + 3);
+        for (int u = 0; u < DECODE_TT; ++u) {
+            if (u < nt) {
+                const uint16_t *xrow = x + (size_t)(tile.pair[u] / k) * H;
+                fetch_x_chunk(xrow, 2 * c, xp[u]);
+                fetch_x_chunk(xrow, 2 * c + 1, xp[u] + 16);
             }
         }
-        __syncthreads();
-        // h in f16 as the down GEMV consumes it: each 8-block in PERM8 order
-        // (element j at 2j for j < 4, at 2(j - 4) + 1 otherwise), odd
-        // elements divided by 16 (exact scaling by a power of two)
-        for (int i = threadIdx.x; i < nt * ir.nloc; i += blockDim.x) {
+    };
+    auto prep_x = [&]() {
+#pragma unroll
+        for (int u = 0; u < DECODE_TT; ++u) {
+            xs[u] = 0.f;
+            if (u < nt) xs[u] = perm_x_chunk(xp[u]) + perm_x_chunk(xp[u] + 16);
+        }
+    };
+    Stage sa, sb;
+    auto consume = [&](const Stage &st, int s) {
+        const int nl = row_of(s);
+        float sg, mg, su, mu;
+        group_params<FMT>(st.gs, sg, mg);
+        group_params<FMT>(st.us, su, mu);
+        const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
+        // one code quad unpacked at a time, applied to every token of the tile
+        float dg[DECODE_TT], du[DECODE_TT];
+#pragma unroll
+        for (int u = 0; u < DECODE_TT; ++u) dg[u] = du[u] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t wq[16];
+            unpack32(q == 0 ? st.g[0] : q == 1 ? st.g[1] : q == 2 ? st.u[0] : st.u[1], wq, kb);
+#pragma unroll
+            for (int u = 0; u < DECODE_TT; ++u) {
+                if (u < nt) {
+                    if (q < 2) dg[u] = dot16(wq, xp[u] + 16 * (q & 1), dg[u]);
+                    else du[u] = dot16(wq, xp[u] + 16 * (q & 1), du[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < DECODE_TT; ++u) {
+            if (u < nt) {
+                const float pg = seg_sum_dpp<LPR>(fmaf(sg, dg[u], cg * xs[u]));
+                const float pu = seg_sum_dpp<LPR>(fmaf(su, du[u], cu * xs[u]));
+                if (c == LPR - 1 && ir.valid_step(s, lrow)) s_out[u][nl] = silu(pg) * pu;
+            }
+        }
+    };
+    // Two register stages, the next one in flight while the current one is
+    // reduced.  The first rows depend only on the tile, so they are issued
+    // before the tokens are known.  The loop issues every stage (rows past
+    // the item re-read its first row) and outputs go to LDS, so it holds only
+    // loads and the compiler's memory-counter waits stay exact.
+    if (SHORT && steps == 1) {
+        fetch_x();
+        issue(sa, 0);
+        prep_x();
+        consume(sa, 0);
+    } else {
+        fetch_x();
+        issue(sa, 0);
+        issue(sb, 1);
+        prep_x();
+        for (int s = 0; s < steps; s += 2) {
+            consume(sa, s);
+            issue(sa, s + 2);
+            if (s + 1 < steps) consume(sb, s + 1);
+            issue(sb, s + 3);
+        }
+    }
+    __syncthreads();
+    {
+        for (int i = tid; i < nt * ir.nloc; i += blockDim.x) {
             const int u = i / ir.nloc, nl = i % ir.nloc;
             if (!ir.valid(nl)) continue;
             const int n = ir.grow(nl);
@@ -380,77 +374,68 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
             const int slot = (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1);
             h[(size_t)(tile.row0 + u) * I + slot] = __builtin_bit_cast(uint16_t, (_Float16)v);
         }
-        __syncthreads();
     }
+    __syncthreads();
 }
 
-// down GEMV for one item (tile; chunk: output rows [d0, d0 + rb)) over the
-// full inner dimension (LPR = I / 32 lanes per row, a contiguous 256-byte row
-// when I = 512), multiplied by each token's gate and added into y (float
-// atomics; each output receives one add per routed (token, slot)).  h enters
-// rounded to f16.
+// down GEMV for one item (tile; output rows ir of H) over the full inner
+// dimension (LPR = I / 32 lanes per row, a contiguous 256-byte row when I =
+// 512), multiplied by each token's gate and added into y (float atomics;
+// each output receives one add per routed (token, slot)).
 template <int LPR, int FMT>
-__global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
-    int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
-    int max_nt, const float *__restrict__ topk_gate, const uint16_t *__restrict__ h,
-    float *__restrict__ y) {
+__device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &L, const Tile &tile,
+                                          const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
+                                          const float *__restrict__ topk_gate, const uint16_t *__restrict__ h,
+                                          float *__restrict__ y, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     constexpr int G = FMT == 0 ? 64 : 128;
-    int nt_all = *ntiles;
-    nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
-    const Items it = decode_items(nt_all, H, H / (DEC_WAVES * RPW));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR, sub = lane / LPR;
     const size_t row_bytes = (size_t)I / 2;
     const size_t smr = (size_t)(I / G) * (FMT == 0 ? 2 : 1);
     const int gi = (32 * c) / G;
     const uint32_t kf = opaque_magic(MAGIC_F16);
-    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     struct Stage {
         uint4 v[DEC_NB];
         uint32_t s[DEC_NB];
     };
-    for (int w = it.first; w < it.end; w += it.stride) {
-        const int j = w / it.nch, chunk = w % it.nch;
-        const Tile tile = sane_tile(tiles[j], L.E, P);
-        const int e = tile.expert, nt = tile.rows;
-        const ItemRows<DEC_WAVES * RPW> ir = item_rows<DEC_WAVES * RPW>(chunk, it, H);
-        if (ir.steps <= 0) continue;
-        const int steps = ir.steps;
-        const int lrow = wave * RPW + sub;  // the lane's row within a step
-        auto row_of = [&](int s) { return s * (DEC_WAVES * RPW) + lrow; };
-        auto issue = [&](Stage &st, int s0) {
+    const int e = tile.expert, nt = tile.rows;
+    const int steps = ir.steps;
+    const int lrow = wave * RPW + sub;  // the lane's row within a step
+    auto row_of = [&](int s) { return s * (DEC_WAVES * RPW) + lrow; };
+    auto issue = [&](Stage &st, int s0) {
 #pragma unroll
-            for (int b = 0; b < DEC_NB; ++b) {
-                const int sb_ = s0 + b;
-                const size_t row = (size_t)e * H + (ir.valid_step(sb_, lrow) ? ir.grow_step(sb_, lrow) : ir.grow(0));
-                st.v[b] = *reinterpret_cast<const uint4 *>(L.dq + row * row_bytes + 16 * c);
-                st.s[b] = load_group_word<FMT>(L.dsm + row * smr, gi);
-            }
-        };
-        Stage sa, sb;
-        int tok[DECODE_TT];
-        float gt[DECODE_TT];
-        uint32_t hp[DECODE_TT][16];
-        // The lane's h elements in f16, odd ones divided by 16 (they meet
-        // codes 1024 + 16 q); ha = sum of the offsets those products carry
-        // (1024 per even element, 64 per odd one, times h), hb = sum of h.
-        float ha[DECODE_TT], hb[DECODE_TT];
-        // h and the gates: fetched before the first weight stages (they
-        // depend on the tile only), summed after them.
-        auto fetch_h = [&]() {
+        for (int b = 0; b < DEC_NB; ++b) {
+            const int sb_ = s0 + b;
+            const size_t row = (size_t)e * H + (ir.valid_step(sb_, lrow) ? ir.grow_step(sb_, lrow) : ir.grow(0));
+            st.v[b] = *reinterpret_cast<const uint4 *>(L.dq + row * row_bytes + 16 * c);
+            st.s[b] = load_group_word<FMT>(L.dsm + row * smr, gi);
+        }
+    };
+    Stage sa, sb;
+    int tok[DECODE_TT];
+    float gt[DECODE_TT];
+    uint32_t hp[DECODE_TT][16];
+    // The lane's h elements in f16, odd ones divided by 16 (they meet codes
+    // 1024 + 16 q); ha = sum of the offsets those products carry (1024 per
+    // even element, 64 per odd one, times h), hb = sum of h.
+    float ha[DECODE_TT], hb[DECODE_TT];
+    // h and the gates: fetched before the first weight stages (they depend on
+    // the tile only), summed after them.
+    auto fetch_h = [&]() {
 #pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) {
-                tok[u] = 0;
-                gt[u] = 0.f;
-                if (u < nt) {
-                    const int p = tile.pair[u];
-                    tok[u] = p / k;
-                    gt[u] = topk_gate[p];
-                    const uint4 *src = reinterpret_cast<const uint4 *>(h + (size_t)(tile.row0 + u) * I + 32 * c);
+        for (int u = 0; u < DECODE_TT; ++u) {
+            tok[u] = 0;
+            gt[u] = 0.f;
+            if (u < nt) {
+                const int p = tile.pair[u];
+                tok[u] = p / k;
+                gt[u] = topk_gate[p];
+                const uint16_t *src = h + (size_t)(tile.row0 + u) * I + 32 * c;
+                {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const uint4 v = src[q];
+                        const uint4 v = reinterpret_cast<const uint4 *>(src)[q];
                         hp[u][4 * q + 0] = v.x;
                         hp[u][4 * q + 1] = v.y;
                         hp[u][4 * q + 2] = v.z;
@@ -458,79 +443,130 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
                     }
                 }
             }
-        };
-        auto sum_h = [&]() {
+        }
+    };
+    auto sum_h = [&]() {
 #pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) {
-                ha[u] = hb[u] = 0.f;
-                if (u < nt) {
-                    float se = 0.f, so = 0.f;  // sums of the even elements and of the odd ones (/16)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        se = dot2_f16(hp[u][4 * q + 0], ONES_F16X2, dot2_f16(hp[u][4 * q + 2], ONES_F16X2, se));
-                        so = dot2_f16(hp[u][4 * q + 1], ONES_F16X2, dot2_f16(hp[u][4 * q + 3], ONES_F16X2, so));
-                    }
-                    ha[u] = OFFSET_F16 * (se + so);
-                    hb[u] = fmaf(16.f, so, se);
-                }
-            }
-        };
-        auto consume = [&](const Stage &st, int s0) {
-#pragma unroll
-            for (int b = 0; b < DEC_NB; ++b) {
-                const int dl = row_of(s0 + b);
-                float sd, md;
-                group_params<FMT>(st.s[b], sd, md);
-                // even codes enter as 1024 + q, odd codes in place as
-                // 1024 + 16 q against h / 16: the dot is sum h q + ha
-                const uint32_t d4[4] = {st.v[b].x, st.v[b].y, st.v[b].z, st.v[b].w};
-                uint32_t dw[16];
+        for (int u = 0; u < DECODE_TT; ++u) {
+            ha[u] = hb[u] = 0.f;
+            if (u < nt) {
+                float se = 0.f, so = 0.f;  // sums of the even elements and of the odd ones (/16)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const uint32_t w8 = d4[q] >> 8;
-                    dw[4 * q + 0] = insert_codes<0x000f000fu>(d4[q], kf);  // codes 0, 4
-                    dw[4 * q + 1] = insert_codes<0x00f000f0u>(d4[q], kf);  // codes 1, 5 (x16)
-                    dw[4 * q + 2] = insert_codes<0x000f000fu>(w8, kf);     // codes 2, 6
-                    dw[4 * q + 3] = insert_codes<0x00f000f0u>(w8, kf);     // codes 3, 7 (x16)
+                    se = dot2_f16(hp[u][4 * q + 0], ONES_F16X2, dot2_f16(hp[u][4 * q + 2], ONES_F16X2, se));
+                    so = dot2_f16(hp[u][4 * q + 1], ONES_F16X2, dot2_f16(hp[u][4 * q + 3], ONES_F16X2, so));
                 }
-#pragma unroll
-                for (int u = 0; u < DECODE_TT; ++u) {
-                    if (u < nt) {
-                        float a = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) a = dot2_f16(dw[i], hp[u][i], a);
-                        const float o = seg_sum_dpp<LPR>(fmaf(sd, a - ha[u], md * hb[u]));
-                        if (c == LPR - 1 && ir.valid_step(s0 + b, lrow)) s_out[u][dl] = gt[u] * o;
-                    }
-                }
-            }
-        };
-        // stages of DEC_NB row loads, pipelined as in the gate/up GEMV
-        const int nst = (steps + DEC_NB - 1) / DEC_NB;
-        if (nst == 1) {
-            fetch_h();
-            issue(sa, 0);
-            sum_h();
-            consume(sa, 0);
-        } else {
-            fetch_h();
-            issue(sa, 0);
-            issue(sb, DEC_NB);
-            sum_h();
-            for (int q = 0; q < nst; q += 2) {
-                consume(sa, q * DEC_NB);
-                issue(sa, (q + 2) * DEC_NB);
-                if (q + 1 < nst) consume(sb, (q + 1) * DEC_NB);
-                issue(sb, (q + 3) * DEC_NB);
+                ha[u] = OFFSET_F16 * (se + so);
+                hb[u] = fmaf(16.f, so, se);
             }
         }
-        __syncthreads();
-        // one float atomic per output and routed (token, slot), coalesced
-        for (int i = threadIdx.x; i < nt * ir.nloc; i += blockDim.x) {
-            const int u = i / ir.nloc, d = i % ir.nloc;
-            if (ir.valid(d)) unsafeAtomicAdd(y + (size_t)tok[u] * H + ir.grow(d), s_out[u][d]);
+    };
+    auto consume = [&](const Stage &st, int s0) {
+#pragma unroll
+        for (int b = 0; b < DEC_NB; ++b) {
+            const int dl = row_of(s0 + b);
+            float sd, md;
+            group_params<FMT>(st.s[b], sd, md);
+            // even codes enter as 1024 + q, odd codes in place as
+            // 1024 + 16 q against h / 16: the dot is sum h q + ha
+            const uint32_t d4[4] = {st.v[b].x, st.v[b].y, st.v[b].z, st.v[b].w};
+            uint32_t dw[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w8 = d4[q] >> 8;
+                dw[4 * q + 0] = insert_codes<0x000f000fu>(d4[q], kf);  // codes 0, 4
+                dw[4 * q + 1] = insert_codes<0x00f000f0u>(d4[q], kf);  // codes 1, 5 (x16)
+                dw[4 * q + 2] = insert_codes<0x000f000fu>(w8, kf);     // codes 2, 6
+                dw[4 * q + 3] = insert_codes<0x00f000f0u>(w8, kf);     // codes 3, 7 (x16)
+            }
+#pragma unroll
+            for (int u = 0; u < DECODE_TT; ++u) {
+                if (u < nt) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) a = dot2_f16(dw[i], hp[u][i], a);
+                    const float o = seg_sum_dpp<LPR>(fmaf(sd, a - ha[u], md * hb[u]));
+                    if (c == LPR - 1 && ir.valid_step(s0 + b, lrow)) s_out[u][dl] = gt[u] * o;
+                }
+            }
         }
-        __syncthreads();
+    };
+    // stages of DEC_NB row loads, pipelined as in the gate/up GEMV
+    const int nst = (steps + DEC_NB - 1) / DEC_NB;
+    if (nst == 1) {
+        fetch_h();
+        issue(sa, 0);
+        sum_h();
+        consume(sa, 0);
+    } else {
+        fetch_h();
+        issue(sa, 0);
+        issue(sb, DEC_NB);
+        sum_h();
+        for (int q = 0; q < nst; q += 2) {
+            consume(sa, q * DEC_NB);
+            issue(sa, (q + 2) * DEC_NB);
+            if (q + 1 < nst) consume(sb, (q + 1) * DEC_NB);
+            issue(sb, (q + 3) * DEC_NB);
+        }
+    }
+    __syncthreads();
+    // one float atomic per output and routed (token, slot), coalesced
+    for (int i = tid; i < nt * ir.nloc; i += blockDim.x) {
+        const int u = i / ir.nloc, d = i % ir.nloc;
+        if (ir.valid(d)) unsafeAtomicAdd(y + (size_t)tok[u] * H + ir.grow(d), s_out[u][d]);
+    }
+    __syncthreads();
+}
+
+// gate/up GEMV + SwiGLU over all items (tiles x row chunks of I), h to the
+// workspace for the down launch.  With ROUTE, every workgroup first routes
+// the tokens itself (route_in_block), which replaces a serial
+// last-workgroup step of the routing launch.
+template <int LPR, int FMT, bool ROUTE>
+__global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
+    const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, int max_nt, uint16_t *__restrict__ h, const uint16_t *__restrict__ lg,
+    int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out, GroupOut gout) {
+    constexpr int BR = DEC_WAVES * (WAVE / LPR);
+    int nt_all;
+    if constexpr (ROUTE) {
+        const Tile *tiles_lds;
+        const float *gates_lds;
+        nt_all = route_in_block(lg, T, L.E, k, P, idx_out, gate_out, gout, &tiles_lds, &gates_lds);
+        tiles = tiles_lds;
+    } else {
+        nt_all = *ntiles;
+    }
+    nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
+    const Items it = decode_items(nt_all, I, I / BR);
+    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
+    for (int w = it.first; w < it.end; w += it.stride) {
+        const int j = w / it.nch, chunk = w % it.nch;
+        const Tile tile = sane_tile(tiles[j], L.E, P);
+        const ItemRows<BR> ir = item_rows<BR>(chunk, it, I);
+        if (ir.steps <= 0) continue;
+        gateup_item<LPR, FMT, ROUTE>(x, H, I, k, L, tile, ir, h, s_out);
+    }
+}
+
+// down GEMV over all items (tiles x row chunks of H), h from the gate/up
+// launch.  h enters rounded to f16.
+template <int LPR, int FMT>
+__global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
+    int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
+    int max_nt, const float *__restrict__ topk_gate, const uint16_t *__restrict__ h, float *__restrict__ y) {
+    constexpr int BR = DEC_WAVES * (WAVE / LPR);
+    int nt_all = *ntiles;
+    nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
+    const Items it = decode_items(nt_all, H, H / BR);
+    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
+    for (int w = it.first; w < it.end; w += it.stride) {
+        const int j = w / it.nch, chunk = w % it.nch;
+        const Tile tile = sane_tile(tiles[j], L.E, P);
+        const ItemRows<BR> ir = item_rows<BR>(chunk, it, H);
+        if (ir.steps <= 0) continue;
+        down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
     }
 }
 
@@ -684,18 +720,17 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         __hip_atomic_store(counter + ROUTE_COUNTER_STRIDE * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroups of `kernel` (256 threads) the device holds at once, a multiple
+// Workgroups of kernel K (256 threads) the device holds at once, a multiple
 // of 8 (queried once per kernel and device).
-template <typename K>
-static int resident_grid(K kernel) {
+template <auto K>
+static int resident_grid() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, DEC_WAVES * 64, 0) != hipSuccess ||
-        per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, DEC_WAVES * 64, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     v = per_cu * cus;
@@ -715,8 +750,8 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     switch (H / 64) {
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
-        auto kern = decode_gateup_kernel<LP, FMT, ROUTE>;                                                        \
-        launch_k(kern, dim3(resident_grid(kern)), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,     \
+        constexpr auto kern = decode_gateup_kernel<LP, FMT, ROUTE>;                                              \
+        launch_k(kern, dim3(resident_grid<kern>()), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,   \
                  (const int32_t *)g.ntiles, mt, h, lg, (int)T, idx_out, gate_out, g);                            \
     } break;
         CASE(1) CASE(2) CASE(4) CASE(8) CASE(16) CASE(32)
@@ -726,10 +761,9 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     switch (I / 32) {
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
-        auto kern = decode_down_kernel<LP, FMT>;                                                                 \
-        launch_k(kern, dim3(resident_grid(kern)), block, s, nullptr, nullptr, H, I, k, P, L,                     \
-                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate,                                     \
-                 (const uint16_t *)h, y);                                                                           \
+        constexpr auto kern = decode_down_kernel<LP, FMT>;                                                       \
+        launch_k(kern, dim3(resident_grid<kern>()), block, s, nullptr, nullptr, H, I, k, P, L,                   \
+                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const uint16_t *)h, y);            \
     } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
@@ -771,7 +805,8 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
     const int nb = wr ? E : 1;
     const int npl = (E + 63) / 64;
 #define LAUNCH(N) \
-    launch_k(decode_route_group_kernel<N>, dim3(nb), dim3(1024), s, e0, e1, x, yres, xout, wr, bias, T, H, E, k, logits, idx, gate, g, yclear, counter, handoff, tail)
+    launch_k(decode_route_group_kernel<N>, dim3(nb), dim3(1024), s, e0, e1, x, yres, xout, wr, bias, T, H, E, k, \
+             logits, idx, gate, g, yclear, counter, handoff, tail)
     if (npl <= 4) LAUNCH(4);
     else if (npl <= 8) LAUNCH(8);
     else LAUNCH(16);

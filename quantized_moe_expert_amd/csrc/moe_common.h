@@ -36,6 +36,12 @@ __device__ __forceinline__ uint32_t bf16_order(uint32_t b) {
     if ((b & 0x7fffu) > 0x7f80u) return 0u;
     return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
 }
+// The bf16 bits of an order key (inverse of bf16_order; key 0, a NaN's,
+// gives a NaN).
+__device__ __forceinline__ uint32_t bf16_from_order(uint32_t o) {
+    o &= 0xffffu;
+    return (o & 0x8000u) ? (o & 0x7fffu) : (~o & 0xffffu);
+}
 
 // ---------------------------------------------------------------- nibbles
 //

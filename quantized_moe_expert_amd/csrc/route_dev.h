@@ -40,12 +40,15 @@ __device__ inline double router_dot_wave(const uint16_t *__restrict__ x, const f
 }
 
 // Top-k of one token by one wave.  Each lane holds up to NPL logits (experts
-// lane, lane+64, ...) as 32-bit keys (order(value) << 16 | (0xffff - e)); k
-// rounds of wave-wide max pick the largest value and, among equal values, the
-// lowest e.  Gates in double: exp(l_i - l_0) / sum_j exp(l_j - l_0).
+// lane, lane+64, ...) as 32-bit keys (order(value) << 16 | (0xffff - e)),
+// sorted in the lane, largest first; k rounds of a wave-wide max over the
+// lanes' first keys pick the largest value and, among equal values, the
+// lowest e (keys are unique), and the winning lane moves to its next key.
+// Lane i keeps the i-th key, from which expert and logit are read back.
+// Gates in double: exp(l_i - l_0) / sum_j exp(l_j - l_0).
 template <int NPL>
 __device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, int k, int32_t *__restrict__ idx_out,
-                                float *__restrict__ gate_out, int32_t *idx_copy = nullptr) {
+                                       float *__restrict__ gate_out, int32_t *idx_copy = nullptr) {
     const int lane = threadIdx.x & 63;
     uint32_t key[NPL];
 #pragma unroll
@@ -53,24 +56,39 @@ __device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, in
         const int e = j * WAVE + lane;
         key[j] = e < E ? (bf16_order(l[e]) << 16) | (0xffffu - (uint32_t)e) : 0u;
     }
-    int my_e = -1;  // lane i < k keeps the i-th selected expert
-    for (int i = 0; i < k; ++i) {
-        uint32_t m = 0;
+    // sorting network, largest first
+    auto cswap = [&](int a, int b) {
+        const uint32_t hi = key[a] > key[b] ? key[a] : key[b], lo = key[a] > key[b] ? key[b] : key[a];
+        key[a] = hi;
+        key[b] = lo;
+    };
+    if constexpr (NPL == 2) {
+        cswap(0, 1);
+    } else if constexpr (NPL == 4) {
+        cswap(0, 1), cswap(2, 3), cswap(0, 2), cswap(1, 3), cswap(1, 2);
+    } else {
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) m = key[j] > m ? key[j] : m;
-        m = wave_max_u32(m);
-        const int e = (int)(0xffffu - (m & 0xffffu));
-        if (lane == i) my_e = e;
+        for (int i = 0; i < NPL; ++i)
 #pragma unroll
-        for (int j = 0; j < NPL; ++j)
-            if (j == (e >> 6) && (e & 63) == lane) key[j] = 0u;  // taken
+            for (int j = 0; j + 1 < NPL - i; ++j) cswap(j, j + 1);
     }
-    const int e0 = __shfl(my_e, 0, WAVE);
-    const double l0 = (double)bf16_to_f32(l[e0]);
+    uint32_t mine = 0;  // lane i < k: the i-th largest key
+    for (int i = 0; i < k; ++i) {
+        const uint32_t m = wave_max_u32(key[0]);
+        if (lane == i) mine = m;
+        if (key[0] == m) {  // the one lane holding it moves on
+#pragma unroll
+            for (int j = 0; j + 1 < NPL; ++j) key[j] = key[j + 1];
+            key[NPL - 1] = 0u;
+        }
+    }
+    const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane((int)mine, 0);
+    const double l0 = (double)bf16_to_f32(bf16_from_order(m0 >> 16));
     double ex = 0.0;
-    if (lane < k) ex = exp((double)bf16_to_f32(l[my_e]) - l0);
+    if (lane < k) ex = exp((double)bf16_to_f32(bf16_from_order(mine >> 16)) - l0);
     const double den = wave_allsum_f64_dpp(ex);
     if (lane < k) {
+        const int my_e = (int)(0xffffu - (mine & 0xffffu));
         idx_out[lane] = my_e;
         gate_out[lane] = (float)(ex / den);
         if (idx_copy) idx_copy[lane] = my_e;
