@@ -43,7 +43,7 @@
  * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 32), T * k < 2^31;
  * hidden H and inter I are powers of two in [64, 2048] and multiples of the
  * group (64 asym, 128 sym); moe_q4_prefill additionally needs I % 128 == 0
- * and H % 256 == 0, T * H < 2^31 and T * k * I < 2^31 (so are the calls of
+ * and H % 256 == 0, T * H, T * k * I and T * k * H below 2^31 (so are the calls of
  * moe_q4_forward that take the prefill path).  Other shapes return
  * MOE_Q4_ERR_UNSUPPORTED.
  */
@@ -174,10 +174,11 @@ MOE_Q4_API int moe_q4_decode(const void *x, const int32_t *topk_idx, const float
  * below the row's largest magnitude may round); weights are dequantised to
  * f16 in registers with one rounding each (s q + m, or s (q - 8)), so a
  * dequantised weight must stay below 65504 in magnitude; h between the two
- * products is rounded to f16, so |h| must stay below 65504 too.  y (float
- * [T][H]) is accumulated with float atomics: the result can differ between
- * runs in the last bits.  Same arguments as
- * moe_q4_decode; ws >= moe_q4_workspace_size(MOE_Q4_WS_PREFILL, ...).
+ * products is rounded to f16, so |h| must stay below 65504 too.  Each
+ * routed row's gate-weighted down output is rounded to f16 as well (so it
+ * must stay below 65504 in magnitude) and a token's k rows are summed in
+ * fp32 into y (float [T][H], written whole; deterministic).  Same arguments
+ * as moe_q4_decode; ws >= moe_q4_workspace_size(MOE_Q4_WS_PREFILL, ...).
  */
 MOE_Q4_API int moe_q4_prefill(const void *x, const int32_t *topk_idx, const float *topk_gate,
                    int64_t T, int32_t k, const moe_q4_layer *w, float *y,
@@ -234,7 +235,8 @@ MOE_Q4_API int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream st
  *   decode:  events[0..1] the gate/up GEMV + SwiGLU kernel,
  *            events[2..3] the grouping kernel
  *   prefill: events[0..1] the gate/up grouped GEMM + SwiGLU,
- *            events[2..3] the down grouped GEMM + combine
+ *            events[2..3] the down grouped GEMM (the combine into y
+ *            follows it)
  * events must point to MOE_Q4_STAGE_EVENTS valid events.
  */
 #define MOE_Q4_STAGE_EVENTS 4

@@ -36,7 +36,8 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // The prefill kernels address activations and weights with 32-bit offsets.
 bool prefill_fits(int64_t T, int k, int H, int I) {
-    return T * (int64_t)H < ((int64_t)1 << 31) && T * (int64_t)k * I < ((int64_t)1 << 31);
+    return T * (int64_t)H < ((int64_t)1 << 31) && T * (int64_t)k * I < ((int64_t)1 << 31) &&
+           T * (int64_t)k * H < ((int64_t)1 << 31);
 }
 
 int check_layer(const moe_q4_layer *w, bool prefill) {
@@ -112,6 +113,7 @@ struct PrefillWs {
     uint16_t *x16;   // x as f16 after the per-row power-of-two scale [T][H]
     int32_t *xexp;   // that scale's exponent per token
     uint16_t *h;     // SwiGLU output per sorted row, f16 [T*k][I]
+    uint16_t *z;     // gate-weighted down output per sorted row, f16 [T*k][H]
 };
 PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
     PrefillWs p;
@@ -119,6 +121,7 @@ PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
     p.x16 = c.take<uint16_t>(T * (int64_t)H);
     p.xexp = c.take<int32_t>(T);
     p.h = c.take<uint16_t>(T * k * (int64_t)I);
+    p.z = c.take<uint16_t>(T * k * (int64_t)H);
     return p;
 }
 
@@ -223,7 +226,7 @@ static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, con
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, y, s, ev));
+    return hip_status(launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev));
 }
 
 int moe_q4_decode(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
@@ -331,7 +334,7 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, y, s, ev));
+    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev));
 }
 
 int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,

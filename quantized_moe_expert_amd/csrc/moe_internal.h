@@ -101,9 +101,11 @@ hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logit
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
+// Grouped GEMMs of the prefill path; z: f16 [T*k][H] workspace of the
+// combine.  y is written whole (no clearing needed).
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                  const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, float *y,
-                                  hipStream_t s, hipEvent_t const *ev = nullptr);
+                                  const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
+                                  float *y, hipStream_t s, hipEvent_t const *ev = nullptr);
 
 // Launch on s; when e0 is given the runtime records e0 / e1 at the kernel's
 // own start and end (AMD extended launch), which times exactly that kernel.

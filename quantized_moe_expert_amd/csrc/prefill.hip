@@ -25,6 +25,13 @@
 // dword unpacks most cheaply, so a 16-byte fragment of either operand holds
 // the same 8 contraction indices.
 //
+// Combine.  GEMM2 writes each routed row's gate-weighted output once, as f16
+// (z, [T*k][H] in sorted row order, |z| must stay below 65504), with
+// coalesced stores; a last kernel sums each token's k rows in fp32 into y.
+// Scattering the rows into y with float atomics (k adds per output, done at
+// the memory side so that the XCDs' L2s agree) took longer than GEMM2's
+// matrix work.
+//
 // Tiles: 128 rows (one tile-list entry, <= 128 rows of one expert) x 256
 // weight rows per workgroup of 4 waves, two workgroups per CU.  Wave w owns 32 columns in each of
 // two N-subtiles (GEMM1: the gate rows and the up rows of the same 32 h
@@ -258,7 +265,7 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
 // STAGE 1: A = x16 rows gathered through perm, B = gate | up codes,
 //          epilogue * 2^e(token), SwiGLU -> h (f16).
 // STAGE 2: A = h rows (contiguous sorted rows), B = down codes,
-//          epilogue gate-weighted float atomic add into y.
+//          epilogue gate-weighted rows of z (f16) for the combine kernel.
 // Work item w = (tile j, column block cb) with cb fastest.  Workgroups are
 // spread over the 8 XCDs round-robin (XCD = block index mod 8); each XCD
 // takes a contiguous range of work items, so the column blocks of one tile
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t *__restrict__ xexp,      // STAGE 1: per-token exponent e
     int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
-    uint16_t *__restrict__ h_out, float *__restrict__ y) {
+    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z) {
     constexpr int G = FMT == 0 ? 64 : 128;
 
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
@@ -408,43 +415,75 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
     } else {
+        // z tile [BM][256] f16 in LDS, then coalesced 16-byte stores
+        uint16_t *s_z = reinterpret_cast<uint16_t *>(s_ring);
+        constexpr int ZP = BROWS + 8;
+        static_assert(BM * ZP * 2 <= NST * STAGE_BYTES, "z tile fits the ring");
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             if (mi < msub) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
-                    if (row < rows) {
-                        const float gt = s_rs[row];
-                        float *dst = y + (size_t)s_tok[row] * H + col_base + wave * 64 + l32;
-                        unsafeAtomicAdd(dst, gt * acc[mi][0][r]);
-                        unsafeAtomicAdd(dst + 32, gt * acc[mi][1][r]);
-                    }
+                    const float gt = s_rs[row];
+                    s_z[row * ZP + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
+                    s_z[row * ZP + wave * 64 + 32 + l32] =
+                        __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
                 }
             }
         }
+        __syncthreads();
+        for (int i = tid; i < BM * (BROWS / 8); i += PF_BLOCK) {
+            const int row = i / (BROWS / 8), cc = i % (BROWS / 8);
+            if (row < rows)
+                *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
+                    *reinterpret_cast<const uint4 *>(&s_z[row * ZP + cc * 8]);
+        }
+    }
+}
+
+// y[t] = sum over the token's k routed rows of z (fp32).  One workgroup of
+// 256 threads per token, 8 columns per thread and pass.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ z, const int32_t *__restrict__ inv,
+                                                      int64_t T, int k, int H, int64_t P, float *__restrict__ y) {
+    const int64_t t = blockIdx.x;
+    if (t >= T) return;
+    for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+        float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < k; ++i) {
+            int64_t row = inv[t * k + i];
+            row = row < 0 ? 0 : (row >= P ? P - 1 : row);
+            const uint4 v = *reinterpret_cast<const uint4 *>(z + row * H + c);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s[2 * q] += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xffffu));
+                s[2 * q + 1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16));
+            }
+        }
+        float4 *dst = reinterpret_cast<float4 *>(y + t * H + c);
+        dst[0] = make_float4(s[0], s[1], s[2], s[3]);
+        dst[1] = make_float4(s[4], s[5], s[6], s[7]);
     }
 }
 
 template <int FMT>
 static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                     const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, float *y,
-                                     hipStream_t s, hipEvent_t const *ev) {
+                                     const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
+                                     float *y, hipStream_t s, hipEvent_t const *ev) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
     hipLaunchKernelGGL(x_to_f16_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, x16, xexp);
-    {
-        const int64_t n = T * (int64_t)H;
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n / 4 + 256) / 256)), dim3(256), 0, s, y, n);
-    }
     const unsigned nb1 = (unsigned)(((I / 128) * tiles + 7) / 8 * 8);
     const unsigned nb2 = (unsigned)(((H / BROWS) * tiles + 7) / 8 * 8);
     launch_k(grouped_gemm_kernel<FMT, 1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
              (const uint16_t *)x16, (const int32_t *)xexp, H, I, k, L, (const Tile *)g.tiles,
-             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, y);
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z);
     launch_k(grouped_gemm_kernel<FMT, 2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, (const int32_t *)nullptr, H, I, k, L, (const Tile *)g.tiles,
-             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, y);
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
+                       (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();
 }
 
@@ -458,10 +497,10 @@ hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                  const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, float *y,
-                                  hipStream_t s, hipEvent_t const *ev) {
-    return L.fmt == 0 ? launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, y, s, ev)
-                      : launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, y, s, ev);
+                                  const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
+                                  float *y, hipStream_t s, hipEvent_t const *ev) {
+    return L.fmt == 0 ? launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev)
+                      : launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
 }
 
 }  // namespace moeq4

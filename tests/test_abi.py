@@ -116,9 +116,10 @@ def test_layer_validation():
     lay.down_sm = FAKE + 2
     assert _decode(lay, prefill=True) == _lib.ERR_INVALID_ARG
     assert _decode(_layer(), x=FAKE + 4) == _lib.ERR_INVALID_ARG
-    # prefill offsets are 32-bit: T * H and T * k * I below 2^31
+    # prefill offsets are 32-bit: T * H, T * k * I and T * k * H below 2^31
     assert _decode(_layer(), prefill=True, T=1 << 20) == _lib.ERR_UNSUPPORTED
     assert _decode(_layer(H=256, I=2048), prefill=True, T=1 << 17, k=8) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(H=2048, I=256), prefill=True, T=1 << 17, k=8) == _lib.ERR_UNSUPPORTED
     # timed variants: events are required and must be non-NULL
     L = m.lib()
     ev_null = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
