@@ -107,17 +107,14 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 
 // ------------------------------------------------------------ weights
 //
-// PERM8 unpack: pair j (j = 0..3) of a code dword holds codes j and j + 4 as
-// the exact f16 values 1024 + q.
-__device__ __forceinline__ uint32_t unpack_pair_f16(uint32_t w, int j) {
-    return ((w >> (4 * j)) & 0x000f000fu) | 0x64006400u;
-}
-
-// Two weights from a pair of 1024 + q halves: s q + m (asym) or s (q - 8)
-// (sym), each rounded once to f16.
+// Two weights from a pair of unpacked halves v = 1024 + q (codes 0 and 4, 2
+// and 6 of a dword) or v = 1024 + 16 q (codes 1 and 5, 3 and 7, taken in
+// place: see insert_codes): (v - off) is exact and equals q, q - 8, 16 q or
+// 16 q - 128; times s2 (the group scale, or scale / 16 for the 16 q pairs,
+// exact while scale / 16 is a normal f16) plus m2 (asym min) it is s q + m or
+// s (q - 8), rounded once to f16.
 template <int FMT>
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t v, half2_t s2, half2_t m2) {
-    const half2_t off = {(_Float16)(FMT == 0 ? 1024.0f : 1032.0f), (_Float16)(FMT == 0 ? 1024.0f : 1032.0f)};
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t v, half2_t off, half2_t s2, half2_t m2) {
     const half2_t q = __builtin_bit_cast(half2_t, v) - off;
     const half2_t r = FMT == 0 ? __builtin_elementwise_fma(s2, q, m2) : s2 * q;
     return __builtin_bit_cast(uint32_t, r);
@@ -172,14 +169,15 @@ __device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int
     uint8_t *sa = c.ring + slot * STAGE_BYTES;
     uint8_t *sb = sa + A_BYTES;
     uint8_t *ss = sb + B_BYTES;
+    const uint8_t *ab = c.a_base + (size_t)ks * (KS * 2);  // uniform part of the addresses
 #pragma unroll
     for (int i = 0; i < MS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)(c.a_base + (size_t)ks * (KS * 2) + c.a_off[i]),
+        __builtin_amdgcn_global_load_lds((const void *)(ab + c.a_off[i]),
                                          (__attribute__((address_space(3))) void *)(sa + (i * 4 + wave) * 1024),
                                          16, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)(c.b_base[i] + (size_t)ks * (KS / 2) + c.b_off[i]),
+        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * (KS / 2)) + c.b_off[i]),
                                          (__attribute__((address_space(3))) void *)(sb + (i * 4 + wave) * 1024),
                                          16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void *)(c.s_base + ((c.s_off + (uint32_t)g * c.s_step) & ~3u)),
@@ -199,7 +197,13 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
     for (int u = 0; u < NST - 1; ++u)
         if (u < NK) issue_stage<MS>(c, u, u / KPG, u, wave);
 
-    half2_t s2[2], m2[2];
+    // per N-subtile: scale and min of the current group, for the 1024 + q
+    // pairs (index 0) and the 1024 + 16 q pairs (index 1)
+    half2_t s2[2][2], m2[2];
+    const uint32_t kf = opaque_magic(MAGIC_F16);
+    const half2_t off0 = {(_Float16)(FMT == 0 ? 1024.0f : 1032.0f), (_Float16)(FMT == 0 ? 1024.0f : 1032.0f)};
+    const half2_t off1 = {(_Float16)(FMT == 0 ? 1024.0f : 1152.0f), (_Float16)(FMT == 0 ? 1024.0f : 1152.0f)};
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     for (int kk = 0; kk < NK; kk += NST) {
 #pragma unroll
         for (int u = 0; u < NST; ++u) {
@@ -218,13 +222,14 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
                     for (int ns = 0; ns < 2; ++ns) {
                         const uint32_t pw = ss[c.brow[ns]];
                         if (FMT == 0) {
-                            s2[ns] = __builtin_bit_cast(half2_t, (pw & 0xffffu) * 0x10001u);
+                            s2[ns][0] = __builtin_bit_cast(half2_t, (pw & 0xffffu) * 0x10001u);
                             m2[ns] = __builtin_bit_cast(half2_t, (pw >> 16) * 0x10001u);
                         } else {
                             const uint32_t h = ((c.spar[ns] + (uint32_t)(ks / KPG)) & 1u) ? pw >> 16 : pw & 0xffffu;
-                            s2[ns] = __builtin_bit_cast(half2_t, h * 0x10001u);
-                            m2[ns] = s2[ns];
+                            s2[ns][0] = __builtin_bit_cast(half2_t, h * 0x10001u);
+                            m2[ns] = s2[ns][0];
                         }
+                        s2[ns][1] = s2[ns][0] * sixteenth;
                     }
                 }
                 // B: 16 bytes (32 codes) of each of this lane's two weight rows
@@ -240,10 +245,12 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
 #pragma unroll
                     for (int ns = 0; ns < 2; ++ns) {
                         const uint32_t word = s == 0 ? bw[ns].x : s == 1 ? bw[ns].y : s == 2 ? bw[ns].z : bw[ns].w;
-                        bv[ns] = u32x4_t{dequant_pair<FMT>(unpack_pair_f16(word, 0), s2[ns], m2[ns]),
-                                         dequant_pair<FMT>(unpack_pair_f16(word, 1), s2[ns], m2[ns]),
-                                         dequant_pair<FMT>(unpack_pair_f16(word, 2), s2[ns], m2[ns]),
-                                         dequant_pair<FMT>(unpack_pair_f16(word, 3), s2[ns], m2[ns])};
+                        const uint32_t w8 = word >> 8;
+                        bv[ns] = u32x4_t{
+                            dequant_pair<FMT>(insert_codes<0x000f000fu>(word, kf), off0, s2[ns][0], m2[ns]),
+                            dequant_pair<FMT>(insert_codes<0x00f000f0u>(word, kf), off1, s2[ns][1], m2[ns]),
+                            dequant_pair<FMT>(insert_codes<0x000f000fu>(w8, kf), off0, s2[ns][0], m2[ns]),
+                            dequant_pair<FMT>(insert_codes<0x00f000f0u>(w8, kf), off1, s2[ns][1], m2[ns])};
                     }
                     const int ch = 4 * hf + s;  // logical 16-byte chunk of the A row
 #pragma unroll
@@ -294,7 +301,8 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int e = tile.expert, rows = tile.rows, row0 = tile.row0;
     const int K = STAGE == 1 ? H : I;
     const int NG = K / G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS slot addresses stay scalar
     const int l32 = lane & 31, hf = lane >> 5;
     const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
 
