@@ -570,6 +570,76 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     }
 }
 
+// Router logits only (the expert launch takes top-k and grouping itself):
+// workgroup e computes expert e's logit for every token, wave w taking
+// tokens w, w + 4, ...; a lane reads its 8-element slices of the router row,
+// of x and of yres straight from memory (no staging), forms the residual
+// input bf16(x + yres) and sums x w in double (exact products).  The grid
+// also clears y and writes the residual input to xout.
+__global__ __launch_bounds__(256) void decode_router_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ yres, uint16_t *__restrict__ xout,
+    const uint16_t *__restrict__ wr, const float *__restrict__ bias, int T, int H, int E,
+    uint16_t *__restrict__ logits, float *__restrict__ yclear) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = gridDim.x;
+    const int64_t n = (int64_t)T * H;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + tid; i < n; i += (int64_t)nb * blockDim.x) {
+        yclear[i] = 0.f;
+        if (yres) xout[i] = f32_to_bf16_rne(bf16_to_f32(x[i]) + yres[i]);
+    }
+    if (!wr) return;
+    const int e = blockIdx.x;  // grid = E
+    uint4 wv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int hh = (q * WAVE + lane) * 8;
+        wv[q] = make_uint4(0, 0, 0, 0);
+        if (hh < H) wv[q] = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
+    }
+    const double b = bias ? (double)bias[e] : 0.0;
+    for (int t = wave; t < T; t += 4) {
+        uint4 xv[4];
+        float4 ya[4], yb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int hh = (q * WAVE + lane) * 8;
+            xv[q] = make_uint4(0, 0, 0, 0);
+            if (hh < H) {
+                const size_t gi = (size_t)t * H + hh;
+                xv[q] = *reinterpret_cast<const uint4 *>(x + gi);
+                if (yres) {
+                    ya[q] = *reinterpret_cast<const float4 *>(yres + gi);
+                    yb[q] = *reinterpret_cast<const float4 *>(yres + gi + 4);
+                }
+            }
+        }
+        double acc = 0.0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if ((q * WAVE + lane) * 8 < H) {
+                uint32_t xs4[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+                if (yres) {
+                    const float yv[8] = {ya[q].x, ya[q].y, ya[q].z, ya[q].w, yb[q].x, yb[q].y, yb[q].z, yb[q].w};
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(xs4[jj] & 0xffffu) + yv[2 * jj]);
+                        const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(xs4[jj] >> 16) + yv[2 * jj + 1]);
+                        xs4[jj] = lo | (hi << 16);
+                    }
+                }
+                const uint32_t ws4[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    acc = fma((double)bf16_to_f32(xs4[jj] & 0xffffu), (double)bf16_to_f32(ws4[jj] & 0xffffu), acc);
+                    acc = fma((double)bf16_to_f32(xs4[jj] >> 16), (double)bf16_to_f32(ws4[jj] >> 16), acc);
+                }
+            }
+        }
+        acc = wave_sum_f64_dpp(acc);
+        if (lane == 63) logits[(size_t)t * E + e] = f32_to_bf16_rne((float)(acc + b));
+    }
+}
+
 // Routing of a few tokens in one launch.  Workgroup b (16 waves) computes
 // the router logit of expert b for every token (wave w: tokens w, w + 16,
 // ...); the tokens' input rows are staged in LDS 16 at a time (formed once
@@ -800,6 +870,12 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
                                      float *gate, const GroupOut &g, float *yclear, unsigned int *counter,
                                      unsigned int *handoff, hipStream_t s, bool tail, hipEvent_t e0,
                                      hipEvent_t e1) {
+    if (!tail) {  // logits only: the lean launch
+        if (H > 2048) return hipErrorInvalidValue;
+        launch_k(decode_router_kernel, dim3(wr ? E : 64), dim3(256), s, e0, e1, x, yres, xout, wr, bias, T, H, E,
+                 logits, yclear);
+        return hipGetLastError();
+    }
     if (wr && T * E > ROUTE_LDS_LOGITS) return hipErrorInvalidValue;
     if (T * k > GROUP_SINGLE_MAX) return hipErrorInvalidValue;
     const int nb = wr ? E : 1;
