@@ -68,6 +68,10 @@ def bind(path: str):
     lib.oracle_group.argtypes = [P, i64, i32, i32, P, P, P, P]
     lib.oracle_experts.restype = i32
     lib.oracle_experts.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, i32, P, i64, P]
+    lib.oracle_dequant_int8.restype = i32
+    lib.oracle_dequant_int8.argtypes = [P, P, i32, i32, P]
+    lib.oracle_shared.restype = i32
+    lib.oracle_shared.argtypes = [i32, i32, P, P, P, P, P, P, P, i64, P, i64, P, P]
     lib.oracle_residual.restype = None
     lib.oracle_residual.argtypes = [P, P, i64, P]
     return lib
@@ -180,6 +184,37 @@ def experts(fmt, E, H, I, gate_q, up_q, down_q, gate_sm, up_sm, down_sm,
                                 _p(tok), int(ntok), _p(y))
     if rc != 0:
         raise ValueError(f"oracle_experts failed ({rc})")
+    return y
+
+
+def dequant_int8(q, s, N: int, K: int) -> np.ndarray:
+    """float32 [N][K] from int8 codes [N][K] and f16-bit scales [N][K/128]."""
+    q = _c(q, np.int8)
+    s = _c(s, np.uint16)
+    out = np.empty((N, K), dtype=np.float32)
+    rc = _load().oracle_dequant_int8(_p(q), _p(s), int(N), int(K), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_dequant_int8: unsupported shape")
+    return out
+
+
+def shared(H, I, gate_q, up_q, down_q, gate_s, up_s, down_s, x, T: int,
+           tokens=None, y_in=None) -> np.ndarray:
+    """float32 [ntok][H]: y_in (or 0) plus the shared expert's output for the
+    listed tokens (all T when ``tokens`` is None)."""
+    qs = [_c(a, np.int8) for a in (gate_q, up_q, down_q)]
+    ss = [_c(a, np.uint16) for a in (gate_s, up_s, down_s)]
+    x = _c(x, np.uint16)
+    tok = _c(np.asarray(tokens, dtype=np.int64), np.int64) if tokens is not None else None
+    ntok = len(tok) if tok is not None else T
+    yi = _c(y_in, np.float32) if y_in is not None else None
+    if yi is not None and yi.size != ntok * H:
+        raise ValueError("shared: y_in must hold ntok * H values")
+    y = np.empty((ntok, H), dtype=np.float32)
+    rc = _load().oracle_shared(int(H), int(I), *[_p(a) for a in qs], *[_p(a) for a in ss],
+                               _p(x), int(T), _p(tok), int(ntok), _p(yi), _p(y))
+    if rc != 0:
+        raise ValueError(f"oracle_shared failed ({rc})")
     return y
 
 

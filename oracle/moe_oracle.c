@@ -24,7 +24,9 @@
  *   - router weights are bf16: drama-q4 "What's quantized", MLX card
  *     "Quantization and provenance";
  *   - rows grouped by routed expert: drama-rs page, "Apple Silicon (MLX)"
- *     and "Layout" (grouped MoE prefill).
+ *     and "Layout" (grouped MoE prefill);
+ *   - the shared expert's linears are int8 symmetric group 128: drama-q4
+ *     card, "What's quantized" (see oracle_shared).
  * The pages do not state the routing function, the activation or the combine.
  * This library takes: bf16 router logits, the 8 (k) largest selected with
  * ties to the lower expert index, gates = softmax over the selected logits
@@ -335,6 +337,107 @@ int oracle_experts(int fmt, int E, int H, int I,
     }
     free(o);
     return 0;
+}
+
+/* --------------------------------------------------------- shared expert */
+
+/*
+ * The shared expert's linears are int8, symmetric, group 128 (drama-q4 card,
+ * "What's quantized": attention / DeltaNet / shared expert / codebook decoder
+ * linears): one f16 scale per 128 input weights and w = scale * q with q a
+ * signed byte.  Layout: q [N][K] int8 with k contiguous, scales [N][K/128]
+ * f16.  scale * q is exact in binary32 (11 + 8 significant bits).
+ */
+static double weight_int8(const int8_t *q, const uint16_t *s, int K, int n, int k)
+{
+    return oracle_f16_value(s[(size_t)n * (K / 128) + k / 128]) * (double)q[(size_t)n * K + k];
+}
+
+int oracle_dequant_int8(const int8_t *q, const uint16_t *s, int N, int K, float *out)
+{
+    if (N < 1 || K < 128 || K % 128)
+        return -1;
+    for (int n = 0; n < N; n++)
+        for (int k = 0; k < K; k++)
+            out[(size_t)n * K + k] = (float)weight_int8(q, s, K, n, k);
+    return 0;
+}
+
+/*
+ * The shared expert of a layer, which every token passes through (the pages
+ * name no gate for it, so its output is added as is):
+ *   a = Wg x_t,  b = Wu x_t,  h = silu(a) * b,  o = Wd h,
+ *   y[j] = float( y_in[j] + o )   (y_in == NULL: 0)
+ * for the tokens tok[0..ntok) (tok == NULL: all T), Wg / Wu [I][H] and
+ * Wd [H][I] in int8 symmetric group 128.
+ */
+int oracle_shared(int H, int I, const int8_t *gate_q, const int8_t *up_q, const int8_t *down_q,
+                  const uint16_t *gate_s, const uint16_t *up_s, const uint16_t *down_s,
+                  const uint16_t *x, int64_t T, const int64_t *tok, int64_t ntok,
+                  const float *y_in, float *y)
+{
+    if (H < 128 || I < 128 || H % 128 || I % 128)
+        return -1;
+    if (!tok)
+        ntok = T;
+    for (int64_t j = 0; j < ntok; j++)
+        if (tok && (tok[j] < 0 || tok[j] >= T))
+            return -1;
+    double *wg = malloc(sizeof(double) * (size_t)I * H);
+    double *wu = malloc(sizeof(double) * (size_t)I * H);
+    double *wd = malloc(sizeof(double) * (size_t)H * I);
+    if (!wg || !wu || !wd) {
+        free(wg);
+        free(wu);
+        free(wd);
+        return -2;
+    }
+    for (int n = 0; n < I; n++)
+        for (int k = 0; k < H; k++) {
+            wg[(size_t)n * H + k] = weight_int8(gate_q, gate_s, H, n, k);
+            wu[(size_t)n * H + k] = weight_int8(up_q, up_s, H, n, k);
+        }
+    for (int d = 0; d < H; d++)
+        for (int n = 0; n < I; n++)
+            wd[(size_t)d * I + n] = weight_int8(down_q, down_s, I, d, n);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *xt = malloc(sizeof(double) * (size_t)H);
+        double *h = malloc(sizeof(double) * (size_t)I);
+        if (!xt || !h) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t j = 0; j < ntok; j++) {
+            if (failed)
+                continue;
+            int64_t t = tok ? tok[j] : j;
+            for (int k = 0; k < H; k++)
+                xt[k] = oracle_bf16_value(x[t * H + k]);
+            for (int n = 0; n < I; n++) {
+                double a = 0.0, b = 0.0;
+                for (int k = 0; k < H; k++) {
+                    a += wg[(size_t)n * H + k] * xt[k];
+                    b += wu[(size_t)n * H + k] * xt[k];
+                }
+                h[n] = b * silu(a);
+            }
+            for (int d = 0; d < H; d++) {
+                double acc = y_in ? (double)y_in[(size_t)j * H + d] : 0.0;
+                for (int n = 0; n < I; n++)
+                    acc += h[n] * wd[(size_t)d * I + n];
+                y[(size_t)j * H + d] = (float)acc;
+            }
+        }
+        free(xt);
+        free(h);
+    }
+    free(wg);
+    free(wu);
+    free(wd);
+    return failed ? -2 : 0;
 }
 
 /* ------------------------------------------------------------- residual */

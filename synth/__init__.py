@@ -249,6 +249,85 @@ def zipf_logits(T: int, E: int, s: float, seed: int, device="cpu") -> torch.Tens
     return bf16_bits((logp.unsqueeze(0).double() + gumbel).float())
 
 
+# ------------------------------------------------------------ shared expert
+
+INT8_GROUP = 128
+
+
+def quantize_int8(w: torch.Tensor):
+    """Encode float32 weights [..., N, K] as int8 symmetric group 128 along K.
+
+    The shared expert's linears use this format (drama-q4 card, "What's
+    quantized": int8, symmetric, group 128).  Each group's f16 scale is
+    f16(max |w| / 127) and q = clamp(round(w / scale), -127, 127); an all-zero
+    group gets scale 0 and codes 0.  Returns (q int8 [..., N, K], scale int16
+    bits [..., N, K/128]).
+    """
+    *lead, N, K = w.shape
+    if K % INT8_GROUP:
+        raise ValueError(f"K={K} is not a multiple of {INT8_GROUP}")
+    wg = w.reshape(-1, K // INT8_GROUP, INT8_GROUP).float()
+    s16 = (wg.abs().amax(dim=2) / 127.0).to(torch.float16)
+    s = s16.float().unsqueeze(2)
+    safe = torch.where(s > 0, s, torch.ones_like(s))
+    q = torch.round(wg / safe).clamp_(-127, 127)
+    q = torch.where(s > 0, q, torch.zeros_like(q))
+    return (q.to(torch.int8).reshape(*lead, N, K).contiguous(),
+            s16.view(torch.int16).reshape(*lead, N, K // INT8_GROUP).contiguous())
+
+
+@dataclasses.dataclass
+class SharedExpert:
+    """A layer's shared expert (SwiGLU MLP every token passes through), int8
+    symmetric group 128: q int8 [N][K], scale f16 bits [N][K/128];
+    gate, up: (N, K) = (inter, hidden); down: (hidden, inter)."""
+    hidden: int
+    inter: int
+    gate_q: torch.Tensor
+    up_q: torch.Tensor
+    down_q: torch.Tensor
+    gate_s: torch.Tensor
+    up_s: torch.Tensor
+    down_s: torch.Tensor
+
+    def to(self, device) -> "SharedExpert":
+        kw = {f.name: getattr(self, f.name) for f in dataclasses.fields(self)}
+        for k, v in kw.items():
+            if isinstance(v, torch.Tensor):
+                kw[k] = v.to(device)
+        return SharedExpert(**kw)
+
+    def tensors(self):
+        return (self.gate_q, self.up_q, self.down_q, self.gate_s, self.up_s, self.down_s)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.tensors())
+
+
+def make_shared(H: int, I: int, seed: int, tag: str = "shared", std: float = 0.02,
+                device="cpu") -> SharedExpert:
+    """Draw N(0, std^2) gate/up/down weights of a shared expert and encode them."""
+    out = {}
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        q, s = quantize_int8(normal((N, K), std, seed, f"{tag}/{name}", device))
+        out[name + "_q"] = q
+        out[name + "_s"] = s
+    return SharedExpert(hidden=H, inter=I, **out)
+
+
+def random_shared(H: int, I: int, seed: int, device="cpu", tag="rand_shared") -> SharedExpert:
+    """Shared expert with uniformly random codes in [-127, 127] and scales
+    around the N(0, 0.02) statistics (1.2e-4 .. 2.4e-4), for shape tests."""
+    out = {}
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        gen = generator(seed, f"{tag}/{name}", device)
+        q = torch.randint(-127, 128, (N, K), generator=gen, device=device, dtype=torch.int32)
+        out[name + "_q"] = q.to(torch.int8)
+        s = torch.rand((N, K // INT8_GROUP), generator=gen, device=device) * 1.2e-4 + 1.2e-4
+        out[name + "_s"] = f16_bits(s).contiguous()
+    return SharedExpert(hidden=H, inter=I, **out)
+
+
 @dataclasses.dataclass
 class Case:
     """A complete set of inputs for one MoE layer call (or a chain of layers)."""

@@ -19,6 +19,13 @@ What pins what:
   * expert MLP + combine: dense float64 numpy matmuls with scipy's logistic
     function, the one-expert top-1 layer as a plain SwiGLU MLP, and gate
     linearity (two identical experts selected together equal one);
+  * int8 dequantisation: hand-written rows with hand-worked values
+    (tests/golden/dequant_int8_cases.txt) and numpy's own int8 and float16
+    decoding;
+  * shared expert: dense float64 numpy matmuls with scipy's logistic
+    function (with and without a given y_in, on a token subset), and a
+    routed one-expert top-1 layer of the same weights when every code fits
+    int4 symmetric;
   * the synthetic quantiser: relative reconstruction error of symmetric
     group-128 clip-searched int4 on Gaussian weights, 10.3% on the pages
     (drama-3-w4a16 card, "How it was made").
@@ -130,6 +137,56 @@ def read_dequant_cases():
             elif head == "expect":
                 cur["expect"] = [float(v) for v in rest]
     return cases
+
+
+def read_dequant_int8_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "dequant_int8_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, *rest = line.split()
+            if head == "case":
+                kv = dict(r.split("=") for r in rest[1:])
+                cur = {"name": rest[0], "N": int(kv["N"]), "K": int(kv["K"]), "expect": []}
+                cases.append(cur)
+            elif head == "bytes":
+                cur["bytes"] = [int(v, 16) for v in rest]
+            elif head == "scale":
+                cur["scale"] = [int(v, 16) for v in rest]
+            elif head == "expect":
+                cur["expect"].append([float(v) for v in rest])
+    return cases
+
+
+def np_dequant_int8_64(q, s, N, K) -> np.ndarray:
+    """Independent float64 int8 dequantisation (numpy's int8 and float16 decoders)."""
+    q = np.asarray(q).view(np.int8).reshape(N, K).astype(np.float64)
+    s = np.asarray(s).view(np.uint16).view(np.float16).astype(np.float64).reshape(N, K // 128)
+    return q * np.repeat(s, 128, axis=1)
+
+
+def rand_shared(rng, H, I, lo=-127, hi=127):
+    """Random int8 codes in [lo, hi] and f16 scales of plausible magnitude."""
+    mats = {}
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        mats[name + "_q"] = rng.integers(lo, hi + 1, size=(N, K)).astype(np.int8)
+        mats[name + "_s"] = (rng.random((N, K // 128)) * 1.2e-3 + 2e-4).astype(np.float16).view(np.uint16)
+    return mats
+
+
+def shared_args(mats):
+    return [mats[n] for n in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")]
+
+
+def np_shared_out(mats, x64, H, I):
+    """Wd silu(Wg x) * (Wu x) in float64 (numpy matmuls, scipy's expit)."""
+    wg = np_dequant_int8_64(mats["gate_q"], mats["gate_s"], I, H)
+    wu = np_dequant_int8_64(mats["up_q"], mats["up_s"], I, H)
+    wd = np_dequant_int8_64(mats["down_q"], mats["down_s"], H, I)
+    a = wg @ x64
+    return wd @ (a * scipy.special.expit(a) * (wu @ x64))
 
 
 def cyc(vals, n):
@@ -368,7 +425,64 @@ def pin_residual():
     assert np.array_equal(got, ref)
 
 
+def pin_dequant_int8_golden():
+    for c in read_dequant_int8_cases():
+        N, K = c["N"], c["K"]
+        q = np.array(cyc(c["bytes"], N * K), dtype=np.uint8).view(np.int8).reshape(N, K)
+        s = np.array(c["scale"], dtype=np.uint16)
+        assert s.size == N * (K // 128) == len(c["expect"]), c["name"]
+        exp = np.concatenate([cyc(e, 128) for e in c["expect"]]).reshape(N, K)
+        got = oracle.dequant_int8(q, s, N, K)
+        assert np.array_equal(got.astype(np.float64), exp), c["name"]
+
+
+def pin_dequant_int8_random():
+    rng = np.random.default_rng(37)
+    for N, K in ((3, 128), (5, 384), (2, 2048)):
+        q = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+        s = rng.integers(0, 0x7c00, size=(N, K // 128)).astype(np.uint16)
+        s[0, 0] |= 0x8000  # a negative scale
+        got = oracle.dequant_int8(q, s, N, K)
+        assert np.array_equal(got, np_dequant_int8_64(q, s, N, K).astype(np.float32))
+
+
+def pin_shared_dense():
+    """The shared expert against float64 numpy, with and without y_in, on all
+    tokens and on a subset."""
+    rng = np.random.default_rng(41)
+    for H, I, T in ((128, 128, 3), (256, 384, 5)):
+        mats = rand_shared(rng, H, I)
+        x = rand_bf16(rng, (T, H))
+        y = oracle.shared(H, I, *shared_args(mats), x, T)
+        ref = np.stack([np_shared_out(mats, bf16_to_f64(x[t]), H, I) for t in range(T)])
+        assert rel_l2(y, ref) < 1e-6
+        assert np.allclose(y, ref, rtol=1e-6, atol=1e-7)
+        sub = [T - 1, 0]
+        y_in = rng.standard_normal((2, H)).astype(np.float32)
+        ys = oracle.shared(H, I, *shared_args(mats), x, T, tokens=sub, y_in=y_in)
+        assert np.allclose(ys, ref[sub] + y_in.astype(np.float64), rtol=1e-6, atol=1e-6)
+
+
+def pin_shared_as_routed_expert():
+    """Codes within [-8, 7] make the shared expert a sym-g128 int4 expert: the
+    routed one-expert top-1 layer of the same weights gives the same output."""
+    rng = np.random.default_rng(43)
+    H, I, T = 256, 128, 4
+    mats = rand_shared(rng, H, I, -8, 7)
+    routed = {}
+    for name in ("gate", "up", "down"):
+        q = mats[name + "_q"].astype(np.int64) + 8
+        routed[name + "_q"] = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)[None]
+        routed[name + "_sm"] = mats[name + "_s"][None]
+    x = rand_bf16(rng, (T, H))
+    y1 = oracle.experts(oracle.FMT_SYM_G128, 1, H, I, *layer_args(routed), x, np.zeros((T, 1), np.int32),
+                        np.ones((T, 1), np.float32), T, 1)
+    ys = oracle.shared(H, I, *shared_args(mats), x, T)
+    assert rel_l2(ys, y1) < 1e-12
+
+
 ALL_PINS = [pin_f16_decode_all, pin_bf16_decode_all, pin_bf16_round, pin_dequant_golden,
             pin_dequant_random, pin_router, pin_topk_bruteforce, pin_topk_adversarial,
             pin_gates, pin_group, pin_one_expert_dense, pin_experts_bruteforce,
-            pin_gate_linearity, pin_layer_chain, pin_residual]
+            pin_gate_linearity, pin_layer_chain, pin_residual, pin_dequant_int8_golden,
+            pin_dequant_int8_random, pin_shared_dense, pin_shared_as_routed_expert]

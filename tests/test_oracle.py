@@ -42,3 +42,20 @@ def test_asym_codes_in_range_and_layout(orc):
     err = np.abs(d - w.numpy())
     # clipped ends may exceed half a step; the bulk must not
     assert np.mean(err <= 0.5 * step + 1e-7) > 0.97
+
+
+def test_int8_encoder_round_trip(orc):
+    """The synthetic int8 symmetric g128 encoder: codes in [-127, 127], every
+    group's largest weight hits +-127 and each weight is within half a step of
+    its dequantised value (through the oracle's int8 dequantisation)."""
+    import synth
+    w = synth.normal((96, 384), 0.02, 0, "pin/int8", "cpu")
+    w[3, 128:256] = 0.0  # an all-zero group
+    q, s = synth.quantize_int8(w)
+    qn = q.numpy()
+    assert qn.dtype == np.int8 and qn.min() >= -127 and qn.max() <= 127
+    amax = np.abs(qn.reshape(96, 3, 128).astype(np.int64)).max(axis=2)
+    assert amax[3, 1] == 0 and (np.delete(amax.ravel(), 3 * 3 + 1) == 127).all()
+    d = orc.dequant_int8(qn, s.numpy(), 96, 384).astype(np.float64)
+    step = np.repeat(np.abs(s.numpy().view(np.float16).astype(np.float64)), 128, axis=1)
+    assert (np.abs(d - w.double().numpy()) <= 0.5 * step * (1 + 1e-3) + 1e-12).all()

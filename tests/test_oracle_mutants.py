@@ -38,6 +38,11 @@ MUTANTS = [
     ("combine_ignores_gate", "acc += (double)gate[t * k + i] * o[", "acc += 1.0 * o["),
     ("combine_one_slot", "for (int i = 0; i < k; i++)\n                acc += (double)gate",
      "for (int i = 0; i < 1; i++)\n                acc += (double)gate"),
+    ("int8_unsigned", "* (double)q[(size_t)n * K + k];", "* (double)(uint8_t)q[(size_t)n * K + k];"),
+    ("int8_first_group_scale", "s[(size_t)n * (K / 128) + k / 128]", "s[(size_t)n * (K / 128)]"),
+    ("shared_silu_on_up", "h[n] = b * silu(a);", "h[n] = a * silu(b);"),
+    ("shared_down_transposed", "acc += h[n] * wd[(size_t)d * I + n];", "acc += h[n] * wd[(size_t)n * H + d];"),
+    ("shared_y_in_dropped", "double acc = y_in ? (double)y_in[(size_t)j * H + d] : 0.0;", "double acc = 0.0;"),
     ("residual_truncates", "out[i] = oracle_bf16_round(s);", "out[i] = (uint16_t)(oracle_bf16_round(s) & 0xfffe);"),
 ]
 
