@@ -85,7 +85,8 @@ typedef enum {
     MOE_Q4_WS_DECODE = 1,
     MOE_Q4_WS_PREFILL = 2,
     MOE_Q4_WS_GROUP = 3,
-    MOE_Q4_WS_FORWARD = 4
+    MOE_Q4_WS_FORWARD = 4,
+    MOE_Q4_WS_SHARED = 5    /* moe_q4_shared: pass the shared expert's H and I */
 } moe_q4_ws_kind;
 
 /*
@@ -106,6 +107,24 @@ typedef struct moe_q4_layer {
     const uint8_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_sm, *up_sm, *down_sm;
 } moe_q4_layer;
+
+/*
+ * A layer's shared expert: a SwiGLU MLP every token passes through, beside
+ * the routed experts.  Its linears are int8, symmetric, with one f16 scale per
+ * 128 input weights (drama-q4 card, "What's quantized"), w = scale * q with q
+ * the signed byte.  All device pointers:
+ *   gate_q, up_q   int8 [I][H]   row n = output n, input k contiguous
+ *   down_q         int8 [H][I]   row d = output d
+ *   gate_s, up_s   f16 bit patterns [I][H/128]; down_s [H][I/128]
+ * hidden H and inter I: powers of two in [128, 2048].  Code arrays 16-byte
+ * aligned, scale arrays 2-byte aligned.
+ */
+typedef struct moe_q4_shared_expert {
+    int32_t hidden;   /* H */
+    int32_t inter;    /* I */
+    const int8_t *gate_q, *up_q, *down_q;
+    const uint16_t *gate_s, *up_s, *down_s;
+} moe_q4_shared_expert;
 
 /* Bytes of workspace the call of kind `which` needs for these sizes (0 if
  * none).  The value covers both weight formats. */
@@ -246,6 +265,30 @@ MOE_Q4_API int moe_q4_decode_timed(const void *x, const int32_t *topk_idx, const
 MOE_Q4_API int moe_q4_prefill_timed(const void *x, const int32_t *topk_idx, const float *topk_gate,
                          int64_t T, int32_t k, const moe_q4_layer *w, float *y,
                          void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
+
+/*
+ * Shared expert for T tokens (tuned for T <= 64; the pages name no gate for
+ * it, so its output is added as is):
+ *   y[t] = (accumulate ? y[t] : 0) + Wd (silu(Wg x_t) * (Wu x_t))
+ * as two GEMV launches that stream the int8 codes: gate and up with SwiGLU
+ * (products of codes and x exact in fp32, fp32 sums, each 128-group's scale
+ * applied to its partial sum) into h rounded to f16 (|h| must stay below
+ * 65504), then the down GEMV (exact products of codes and f16 h, fp32 sums)
+ * written to y by one thread per output (deterministic).
+ *   x   bf16 [T][H];  y  float [T][H], read when accumulate != 0
+ *   ws  >= moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, I) bytes
+ * Same conventions as the other entry points; T * H and T * I below 2^31.
+ */
+MOE_Q4_API int moe_q4_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y,
+                             int32_t accumulate, void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/*
+ * Test hook: dequantise projection `proj` (0 gate [I][H], 1 up [I][H],
+ * 2 down [H][I]) of a shared expert to float [N][K] = float(q) * scale (exact)
+ * through the kernels' own code decoding.
+ */
+MOE_Q4_API int moe_q4_dequant_int8(const moe_q4_shared_expert *sx, int32_t proj, float *out,
+                                   moe_q4_stream stream);
 
 /*
  * Test hook: dequantise projection `proj` (0 gate [I][H], 1 up [I][H],

@@ -15,13 +15,14 @@ LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
 
 ASYM_G64 = 0
 SYM_G128 = 1
-WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP, WS_FORWARD = 0, 1, 2, 3, 4
+WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP, WS_FORWARD, WS_SHARED = 0, 1, 2, 3, 4, 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 # every entry point declared in include/moe_q4.h
 EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_decode", "moe_q4_prefill",
            "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_forward_timed",
            "moe_q4_workspace_init",
+           "moe_q4_shared", "moe_q4_dequant_int8",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string")
 STAGE_EVENTS = 4
 
@@ -38,6 +39,13 @@ class Layer(ctypes.Structure):
                 ("format", ctypes.c_int32),
                 ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
                 ("gate_sm", ctypes.c_void_p), ("up_sm", ctypes.c_void_p), ("down_sm", ctypes.c_void_p)]
+
+
+class SharedExpert(ctypes.Structure):
+    """struct moe_q4_shared_expert"""
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
+                ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
 
 
 _lib = None
@@ -75,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.moe_q4_workspace_init.argtypes = [P, sz, P]
         L.moe_q4_dequant.restype = ctypes.c_int
         L.moe_q4_dequant.argtypes = [ctypes.POINTER(Layer), i32, i32, P, P]
+        L.moe_q4_shared.restype = ctypes.c_int
+        L.moe_q4_shared.argtypes = [P, i64, ctypes.POINTER(SharedExpert), P, i32, P, sz, P]
+        L.moe_q4_dequant_int8.restype = ctypes.c_int
+        L.moe_q4_dequant_int8.argtypes = [ctypes.POINTER(SharedExpert), i32, P, P]
         L.moe_q4_residual_bf16.restype = ctypes.c_int
         L.moe_q4_residual_bf16.argtypes = [P, P, i64, P, P]
         L.moe_q4_error_string.restype = ctypes.c_char_p
@@ -123,6 +135,13 @@ def layer_struct(layer) -> Layer:
     return Layer(int(layer.num_experts), int(layer.hidden), int(layer.inter), int(fmt),
                  _ptr(layer.gate_q), _ptr(layer.up_q), _ptr(layer.down_q),
                  _ptr(layer.gate_sm), _ptr(layer.up_sm), _ptr(layer.down_sm))
+
+
+def shared_struct(sx) -> SharedExpert:
+    """struct moe_q4_shared_expert from an object with hidden, inter and the six
+    gate/up/down code (int8) and scale (f16 bits) tensors."""
+    return SharedExpert(int(sx.hidden), int(sx.inter), _ptr(sx.gate_q), _ptr(sx.up_q), _ptr(sx.down_q),
+                        _ptr(sx.gate_s), _ptr(sx.up_s), _ptr(sx.down_s))
 
 
 def workspace_size(kind: int, T: int, E: int, k: int, H: int, I: int) -> int:
@@ -214,3 +233,15 @@ def moe_q4_dequant(layer, expert, proj, out, stream=None):
 
 def moe_q4_residual_bf16(x, y, n, out, stream=None):
     _check("moe_q4_residual_bf16", lib().moe_q4_residual_bf16(_ptr(x), _ptr(y), n, _ptr(out), _stream(stream)))
+
+
+def moe_q4_shared(x, T, shared, y, accumulate, ws, stream=None):
+    w, nb = _ws(ws)
+    st = shared_struct(shared) if not isinstance(shared, SharedExpert) else shared
+    _check("moe_q4_shared", lib().moe_q4_shared(_ptr(x), T, ctypes.byref(st), _ptr(y), int(bool(accumulate)), w, nb,
+                                                 _stream(stream)))
+
+
+def moe_q4_dequant_int8(shared, proj, out, stream=None):
+    st = shared_struct(shared) if not isinstance(shared, SharedExpert) else shared
+    _check("moe_q4_dequant_int8", lib().moe_q4_dequant_int8(ctypes.byref(st), proj, _ptr(out), _stream(stream)))

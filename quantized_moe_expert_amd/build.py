@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_q4.so")
-SOURCES = ["api.hip", "route.hip", "group.hip", "decode.hip", "prefill.hip", "misc.hip"]
+SOURCES = ["api.hip", "route.hip", "group.hip", "decode.hip", "prefill.hip", "shared.hip", "misc.hip"]
 ARCH = os.environ.get("MOEQ4_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -1,6 +1,7 @@
 // C ABI of libmoe_q4: argument checks, workspace layout and launch order.
 #include "../../include/moe_q4.h"
 #include "moe_internal.h"
+#include "shared_dev.h"
 
 using namespace moeq4;
 
@@ -125,6 +126,30 @@ PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
     return p;
 }
 
+int check_shared(const moe_q4_shared_expert *sx) {
+    if (!sx || !sx->gate_q || !sx->up_q || !sx->down_q || !sx->gate_s || !sx->up_s || !sx->down_s)
+        return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(sx->gate_q, 16) || !aligned(sx->up_q, 16) || !aligned(sx->down_q, 16) || !aligned(sx->gate_s, 2) ||
+        !aligned(sx->up_s, 2) || !aligned(sx->down_s, 2))
+        return MOE_Q4_ERR_INVALID_ARG;
+    if (sx->hidden < 1 || sx->inter < 1) return MOE_Q4_ERR_INVALID_ARG;
+    if (!pow2_between(sx->hidden, 128, 2048) || !pow2_between(sx->inter, 128, 2048)) return MOE_Q4_ERR_UNSUPPORTED;
+    return MOE_Q4_OK;
+}
+
+SharedPtrs shared_ptrs(const moe_q4_shared_expert *sx) {
+    SharedPtrs S;
+    S.H = sx->hidden;
+    S.I = sx->inter;
+    S.gq = sx->gate_q;
+    S.uq = sx->up_q;
+    S.dq = sx->down_q;
+    S.gs = sx->gate_s;
+    S.us = sx->up_s;
+    S.ds = sx->down_s;
+    return S;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_Q4_OK : MOE_Q4_ERR_HIP; }
 
 }  // namespace
@@ -145,6 +170,7 @@ size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t
             if (forward_uses_decode(T, k)) carve_decode(c, T, E, k, H, I);
             else carve_prefill(c, T, E, k, H, I);
             break;
+        case MOE_Q4_WS_SHARED: c.take<uint16_t>(T * (int64_t)I); break;
         default: return 0;
     }
     return c.used;
@@ -358,6 +384,30 @@ int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *o
     if (st) return st;
     if (!out || expert < 0 || expert >= w->num_experts || proj < 0 || proj > 2) return MOE_Q4_ERR_INVALID_ARG;
     return hip_status(launch_dequant(layer_ptrs(w), expert, proj, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_q4_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y, int32_t accumulate, void *ws,
+                  size_t ws_bytes, moe_q4_stream stream) {
+    int st = check_shared(sx);
+    if (st) return st;
+    if (T < 0 || !x || !y) return MOE_Q4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16)) return MOE_Q4_ERR_INVALID_ARG;
+    const int H = sx->hidden, I = sx->inter;
+    if (T * (int64_t)H >= ((int64_t)1 << 31) || T * (int64_t)I >= ((int64_t)1 << 31)) return MOE_Q4_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_Q4_OK;
+    const size_t need = moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, I);
+    if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
+    Carver c{static_cast<char *>(ws)};
+    uint16_t *h = c.take<uint16_t>(T * (int64_t)I);
+    return hip_status(launch_shared(static_cast<const uint16_t *>(x), T, shared_ptrs(sx), h, y, accumulate != 0,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_q4_dequant_int8(const moe_q4_shared_expert *sx, int32_t proj, float *out, moe_q4_stream stream) {
+    int st = check_shared(sx);
+    if (st) return st;
+    if (!out || proj < 0 || proj > 2) return MOE_Q4_ERR_INVALID_ARG;
+    return hip_status(launch_dequant_int8(shared_ptrs(sx), proj, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int moe_q4_residual_bf16(const void *x, const float *y, int64_t n, void *out, moe_q4_stream stream) {

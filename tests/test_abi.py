@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -175,3 +175,40 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(4, dtype=torch.int16)
     with pytest.raises(ValueError):
         _lib._ptr(x)
+
+
+def _shared(H=2048, I=512, null=None, misalign=None):
+    ptrs = {n: FAKE for n in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")}
+    if null:
+        ptrs[null] = None
+    if misalign:
+        ptrs[misalign] += 2 if misalign.endswith("_q") else 1
+    return _lib.SharedExpert(H, I, *[ptrs[n] for n in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")])
+
+
+def test_shared_validation():
+    L = m.lib()
+
+    def call(sx, T=4, x=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return L.moe_q4_shared(x, T, ctypes.byref(sx) if sx is not None else None, y, 0, ws, ws_bytes, None)
+
+    assert call(None) == _lib.ERR_INVALID_ARG
+    for n in ("gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s"):
+        assert call(_shared(null=n)) == _lib.ERR_INVALID_ARG, n
+        assert call(_shared(misalign=n)) == _lib.ERR_INVALID_ARG, n
+    assert call(_shared(), x=None) == _lib.ERR_INVALID_ARG
+    assert call(_shared(), y=None) == _lib.ERR_INVALID_ARG
+    assert call(_shared(), x=FAKE + 8) == _lib.ERR_INVALID_ARG
+    assert call(_shared(), T=-1) == _lib.ERR_INVALID_ARG
+    assert call(_shared(H=0)) == _lib.ERR_INVALID_ARG
+    for H, I in ((64, 512), (4096, 512), (2048, 64), (2048, 4096), (1536, 512), (2048, 384)):
+        assert call(_shared(H=H, I=I)) == _lib.ERR_UNSUPPORTED, (H, I)
+    assert call(_shared(), T=1 << 21) == _lib.ERR_UNSUPPORTED       # T * H >= 2^31
+    assert call(_shared(), T=0) == _lib.OK
+    need = m.workspace_size(m.WS_SHARED, 4, 1, 1, 2048, 512)
+    assert need >= 4 * 512 * 2
+    assert call(_shared(), ws_bytes=need - 1) == _lib.ERR_WORKSPACE
+    assert call(_shared(), ws=None) == _lib.ERR_WORKSPACE
+    assert L.moe_q4_dequant_int8(ctypes.byref(_shared()), 3, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_dequant_int8(ctypes.byref(_shared()), 0, None, None) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_dequant_int8(ctypes.byref(_shared(I=96)), 0, FAKE, None) == _lib.ERR_UNSUPPORTED
