@@ -242,6 +242,24 @@ MOE_Q4_API int moe_q4_forward_timed(const void *x, const float *residual_y, void
                                     float *y, void *ws, size_t ws_bytes, moe_q4_stream stream,
                                     void *const *events);
 
+/*
+ * moe_q4_forward of a layer with a shared expert (drama-q4 card, "What's
+ * quantized": the layer's shared expert, int8 symmetric group 128, beside
+ * the routed experts): y[t] = sum_i gate[t][i] * o(t, i) + shared(x_t), the
+ * shared output added as is.  shared == NULL is moe_q4_forward; events ==
+ * NULL or as moe_q4_forward_timed.  shared->hidden must equal w->hidden.
+ * On the decode path the shared expert's work items run inside the two
+ * expert launches when shared->inter == w->inter (its down outputs added
+ * with float atomics), otherwise in moe_q4_shared's two launches after them;
+ * on the prefill path moe_q4_shared's launches follow the combine.
+ *   ws  >= moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I)
+ *          + moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, shared->inter)
+ */
+MOE_Q4_API int moe_q4_forward_ex(const void *x, const float *residual_y, void *x_out, const void *router_w,
+                                 const float *bias, void *logits, int64_t T, int32_t k, const moe_q4_layer *w,
+                                 const moe_q4_shared_expert *shared, int32_t *topk_idx, float *topk_gate, float *y,
+                                 void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
+
 /* Clears the control block of a workspace used with moe_q4_forward (once,
  * after allocation).  Enqueued on stream. */
 MOE_Q4_API int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream);

@@ -22,7 +22,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_decode", "moe_q4_prefill",
            "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_forward_timed",
            "moe_q4_workspace_init",
-           "moe_q4_shared", "moe_q4_dequant_int8",
+           "moe_q4_shared", "moe_q4_dequant_int8", "moe_q4_forward_ex",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string")
 STAGE_EVENTS = 4
 
@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.moe_q4_forward_timed.restype = ctypes.c_int
         L.moe_q4_forward_timed.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, P, P, sz, P,
                                            ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_q4_forward_ex.restype = ctypes.c_int
+        L.moe_q4_forward_ex.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer),
+                                        ctypes.POINTER(SharedExpert), P, P, P, P, sz, P,
+                                        ctypes.POINTER(ctypes.c_void_p)]
         L.moe_q4_workspace_init.restype = ctypes.c_int
         L.moe_q4_workspace_init.argtypes = [P, sz, P]
         L.moe_q4_dequant.restype = ctypes.c_int
@@ -219,6 +223,22 @@ def moe_q4_forward(x, residual_y, x_out, router_w, bias, logits, T, k, layer, to
     _check("moe_q4_forward", lib().moe_q4_forward(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias),
                                                    _ptr(logits), T, k, ctypes.byref(st), _ptr(topk_idx),
                                                    _ptr(topk_gate), _ptr(y), w, nb, _stream(stream)))
+
+
+def moe_q4_forward_ex(x, residual_y, x_out, router_w, bias, logits, T, k, layer, shared, topk_idx, topk_gate, y,
+                      ws, stream=None, events=None):
+    """moe_q4_forward with the layer's shared expert (None: without); ``events``: None or 4 hipEvent_t
+    handles as moe_q4_forward_timed."""
+    w, nb = _ws(ws)
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    sx = None
+    if shared is not None:
+        sx = ctypes.byref(shared_struct(shared) if not isinstance(shared, SharedExpert) else shared)
+    ev = (ctypes.c_void_p * STAGE_EVENTS)(*[int(e) for e in events]) if events is not None else None
+    _check("moe_q4_forward_ex",
+           lib().moe_q4_forward_ex(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias), _ptr(logits),
+                                   T, k, ctypes.byref(st), sx, _ptr(topk_idx), _ptr(topk_gate), _ptr(y), w, nb,
+                                   _stream(stream), ev))
 
 
 def moe_q4_workspace_init(ws, stream=None):

@@ -286,11 +286,17 @@ int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream) {
 }
 
 static int run_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
-                       void *logits, int64_t T, int32_t k, const moe_q4_layer *w, int32_t *topk_idx,
-                       float *topk_gate, float *y, void *ws, size_t ws_bytes, moe_q4_stream stream,
-                       void *const *events) {
+                       void *logits, int64_t T, int32_t k, const moe_q4_layer *w, const moe_q4_shared_expert *sx,
+                       int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes,
+                       moe_q4_stream stream, void *const *events) {
     int st = check_layer(w, false);
     if (st) return st;
+    if (sx) {
+        st = check_shared(sx);
+        if (st) return st;
+        if (sx->hidden != w->hidden) return MOE_Q4_ERR_INVALID_ARG;
+        if (T * (int64_t)sx->inter >= ((int64_t)1 << 31)) return MOE_Q4_ERR_UNSUPPORTED;
+    }
     st = check_route_shape(T, w->hidden, w->num_experts, k);
     if (st) return st;
     if (!x || !logits || !topk_idx || !topk_gate || !y) return MOE_Q4_ERR_INVALID_ARG;
@@ -307,10 +313,25 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
     if (!dec && (check_layer(w, true) || !prefill_fits(T, k, H, I))) return MOE_Q4_ERR_UNSUPPORTED;
-    const size_t need = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
+    const size_t need_fwd = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
+    const size_t need = need_fwd + (sx ? moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, sx->inter) : 0);
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const LayerPtrs L = layer_ptrs(w);
+    // the shared expert's h follows the forward regions
+    SharedPtrs S{};
+    uint16_t *hs = nullptr;
+    if (sx) {
+        S = shared_ptrs(sx);
+        Carver cs{static_cast<char *>(ws) + need_fwd};
+        hs = cs.take<uint16_t>(T * (int64_t)sx->inter);
+    }
+    const bool fuse = sx && decode_fuses_shared(L, &S);
+    const SharedPtrs *Sf = fuse ? &S : nullptr;
+    // the shared expert on its own, after the routed experts: y += its output
+    auto shared_after = [&](const uint16_t *xin_) {
+        return sx && !fuse ? hip_status(launch_shared(xin_, T, S, hs, y, true, s)) : MOE_Q4_OK;
+    };
     Carver c{static_cast<char *>(ws)};
     unsigned int *counter = c.take<unsigned int>(CONTROL_BYTES / sizeof(unsigned int));
     unsigned int *handoff = c.take<unsigned int>(T * (int64_t)E);
@@ -327,8 +348,9 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
                                                       topk_idx, topk_gate, d.g, y, counter, handoff, s, false, e2,
                                                       e3));
             if (st) return st;
-            return hip_status(
-                launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s, e0, e1));
+            st = hip_status(
+                launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s, e0, e1, Sf, hs));
+            return st ? st : shared_after(xin);
         }
         if (forward_fused_route(T, E) || !wr) {
             st = hip_status(launch_decode_route_group(static_cast<const uint16_t *>(x), residual_y,
@@ -344,7 +366,8 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
             if (!st) st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H, e2, e3));
         }
         if (st) return st;
-        return hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1));
+        st = hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1, Sf, hs));
+        return st ? st : shared_after(xin);
     }
     if (residual_y) {
         st = hip_status(launch_residual(static_cast<const uint16_t *>(x), residual_y, T * (int64_t)H,
@@ -360,14 +383,16 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev));
+    st = hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev));
+    if (st || !sx) return st;
+    return hip_status(launch_shared(xin, T, S, hs, y, true, s));
 }
 
 int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
                    void *logits, int64_t T, int32_t k, const moe_q4_layer *w, int32_t *topk_idx, float *topk_gate,
                    float *y, void *ws, size_t ws_bytes, moe_q4_stream stream) {
-    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, topk_idx, topk_gate, y, ws, ws_bytes,
-                       stream, nullptr);
+    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, nullptr, topk_idx, topk_gate, y, ws,
+                       ws_bytes, stream, nullptr);
 }
 
 int moe_q4_forward_timed(const void *x, const float *residual_y, void *x_out, const void *router_w,
@@ -375,8 +400,16 @@ int moe_q4_forward_timed(const void *x, const float *residual_y, void *x_out, co
                          int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes,
                          moe_q4_stream stream, void *const *events) {
     if (!events) return MOE_Q4_ERR_INVALID_ARG;
-    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, topk_idx, topk_gate, y, ws, ws_bytes,
-                       stream, events);
+    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, nullptr, topk_idx, topk_gate, y, ws,
+                       ws_bytes, stream, events);
+}
+
+int moe_q4_forward_ex(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
+                      void *logits, int64_t T, int32_t k, const moe_q4_layer *w, const moe_q4_shared_expert *shared,
+                      int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes, moe_q4_stream stream,
+                      void *const *events) {
+    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, shared, topk_idx, topk_gate, y, ws,
+                       ws_bytes, stream, events);
 }
 
 int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *out, moe_q4_stream stream) {

@@ -29,6 +29,7 @@
 // down GEMV (|h| must stay below 65504).
 #include "decode_dev.h"
 #include "group_dev.h"
+#include "shared_dev.h"
 #include "route_dev.h"
 
 namespace moeq4 {
@@ -411,13 +412,29 @@ __device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &
 // gate/up GEMV + SwiGLU over all items (tiles x row chunks of I), h to the
 // workspace for the down launch.  With ROUTE, every workgroup first routes
 // the tokens itself (route_in_block), which replaces a serial
-// last-workgroup step of the routing launch.
-template <int LPR, int FMT, bool ROUTE>
+// last-workgroup step of the routing launch.  With SHARED the layer's shared
+// expert runs in the same launch: its (token tile, row chunk) items form a
+// second list, dealt over the grid like the first, its SwiGLU output going
+// to hs.
+template <int LPR, int FMT, bool ROUTE, bool SHARED>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, int max_nt, uint16_t *__restrict__ h, const uint16_t *__restrict__ lg,
-    int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out, GroupOut gout) {
+    int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out, GroupOut gout, SharedPtrs S,
+    uint16_t *__restrict__ hs) {
     constexpr int BR = DEC_WAVES * (WAVE / LPR);
+    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
+    if constexpr (SHARED && LPR >= 2) {  // shared expert: H / 32 lanes per row
+        constexpr int LPS = 2 * LPR, BRS = DEC_WAVES * (WAVE / LPS);
+        const Items is = decode_items((T + DECODE_TT - 1) / DECODE_TT, S.I, S.I / BRS);
+        for (int w = is.first; w < is.end; w += is.stride) {
+            const int j = w / is.nch, chunk = w % is.nch;
+            const int tok0 = j * DECODE_TT, nt = T - tok0 < DECODE_TT ? T - tok0 : DECODE_TT;
+            const ItemRows<BRS> ir = item_rows<BRS>(chunk, is, S.I);
+            if (ir.steps <= 0) continue;
+            shared_gateup_item<LPS>(x, S, tok0, nt, ir, hs, s_out);
+        }
+    }
     int nt_all;
     if constexpr (ROUTE) {
         const Tile *tiles_lds;
@@ -429,7 +446,6 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     }
     nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
     const Items it = decode_items(nt_all, I, I / BR);
-    __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     for (int w = it.first; w < it.end; w += it.stride) {
         const int j = w / it.nch, chunk = w % it.nch;
         const Tile tile = sane_tile(tiles[j], L.E, P);
@@ -440,11 +456,14 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
 }
 
 // down GEMV over all items (tiles x row chunks of H), h from the gate/up
-// launch.  h enters rounded to f16.
-template <int LPR, int FMT>
+// launch.  h enters rounded to f16.  With SHARED the shared expert's down
+// items (its inner size equal to the routed experts') follow, added into y
+// with float atomics as well.
+template <int LPR, int FMT, bool SHARED>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
-    int max_nt, const float *__restrict__ topk_gate, const uint16_t *__restrict__ h, float *__restrict__ y) {
+    int max_nt, const float *__restrict__ topk_gate, const uint16_t *__restrict__ h, float *__restrict__ y, int T,
+    SharedPtrs S, const uint16_t *__restrict__ hs) {
     constexpr int BR = DEC_WAVES * (WAVE / LPR);
     int nt_all = *ntiles;
     nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
@@ -456,6 +475,16 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, H);
         if (ir.steps <= 0) continue;
         down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
+    }
+    if constexpr (SHARED && LPR >= 4) {
+        const Items is = decode_items((T + DECODE_TT - 1) / DECODE_TT, H, H / BR);
+        for (int w = is.first; w < is.end; w += is.stride) {
+            const int j = w / is.nch, chunk = w % is.nch;
+            const int tok0 = j * DECODE_TT, nt = T - tok0 < DECODE_TT ? T - tok0 : DECODE_TT;
+            const ItemRows<BR> ir = item_rows<BR>(chunk, is, H);
+            if (ir.steps <= 0) continue;
+            shared_down_item<LPR, true>(S, tok0, nt, ir, hs, y, true, s_out);
+        }
     }
 }
 
@@ -679,10 +708,11 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         __hip_atomic_store(counter + ROUTE_COUNTER_STRIDE * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int FMT, bool ROUTE>
+template <int FMT, bool ROUTE, bool SHARED>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
-                                     hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out) {
+                                     hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
+                                     const SharedPtrs &S, uint16_t *hs) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
     const int mt = (int)max_tiles(P, L.E, DECODE_TT);
@@ -690,9 +720,9 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     switch (H / 64) {
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
-        constexpr auto kern = decode_gateup_kernel<LP, FMT, ROUTE>;                                              \
+        constexpr auto kern = decode_gateup_kernel<LP, FMT, ROUTE, SHARED>;                                      \
         launch_k(kern, dim3(resident_grid<kern>()), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,   \
-                 (const int32_t *)g.ntiles, mt, h, lg, (int)T, idx_out, gate_out, g);                            \
+                 (const int32_t *)g.ntiles, mt, h, lg, (int)T, idx_out, gate_out, g, S, hs);                     \
     } break;
         CASE(1) CASE(2) CASE(4) CASE(8) CASE(16) CASE(32)
 #undef CASE
@@ -701,9 +731,10 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     switch (I / 32) {
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
-        constexpr auto kern = decode_down_kernel<LP, FMT>;                                                       \
+        constexpr auto kern = decode_down_kernel<LP, FMT, SHARED>;                                               \
         launch_k(kern, dim3(resident_grid<kern>()), block, s, nullptr, nullptr, H, I, k, P, L,                   \
-                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const uint16_t *)h, y);            \
+                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const uint16_t *)h, y, (int)T, S,  \
+                 (const uint16_t *)hs);                                                                          \
     } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
@@ -712,11 +743,35 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     return hipGetLastError();
 }
 
+// The shared expert rides in the routed launches when its sizes fit them
+// (same hidden size, same inner size, H >= 128); otherwise the caller runs it
+// on its own.
+bool decode_fuses_shared(const LayerPtrs &L, const SharedPtrs *S) {
+    return S && S->H == L.H && S->I == L.I && L.H >= 128 && L.I >= 128;
+}
+
+template <bool ROUTE>
+static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
+                                     const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
+                                     hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
+                                     const SharedPtrs *S, uint16_t *hs) {
+    if (S && !decode_fuses_shared(L, S)) return hipErrorInvalidValue;
+    const SharedPtrs none{};
+    if (S)
+        return L.fmt == 0
+                   ? launch_experts_fmt<0, ROUTE, true>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, *S, hs)
+                   : launch_experts_fmt<1, ROUTE, true>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, *S, hs);
+    return L.fmt == 0
+               ? launch_experts_fmt<0, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, none,
+                                                     nullptr)
+               : launch_experts_fmt<1, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, none,
+                                                     nullptr);
+}
+
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1) {
-    return L.fmt == 0 ? launch_experts_fmt<0, false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr)
-                      : launch_experts_fmt<1, false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr);
+                                 hipEvent_t e1, const SharedPtrs *S, uint16_t *hs) {
+    return launch_experts_any<false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr, S, hs);
 }
 
 // Every expert workgroup repeats this routing before its first weight load,
@@ -729,10 +784,10 @@ bool decode_routes_in_block(int64_t T, int k, int E) {
 
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, uint16_t *h,
-                                        float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                        float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const SharedPtrs *S,
+                                        uint16_t *hs) {
     if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;
-    return L.fmt == 0 ? launch_experts_fmt<0, true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate)
-                      : launch_experts_fmt<1, true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate);
+    return launch_experts_any<true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate, S, hs);
 }
 
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,

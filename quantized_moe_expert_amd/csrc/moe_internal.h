@@ -23,6 +23,8 @@ struct Tile {
 };
 static_assert(sizeof(Tile) == 32, "Tile is two 16-byte words");
 
+struct SharedPtrs;
+
 // Layer pointers as the kernels take them.
 struct LayerPtrs {
     int E, H, I, fmt;
@@ -72,10 +74,13 @@ hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const Group
 // Decode expert kernels: gate/up + SwiGLU -> h (f16 [T*k][I], each 8-block
 // in PERM8 order, odd elements divided by 16), then down with the
 // gate-weighted add into y (y must be cleared first).  e0 / e1 time the
-// gate/up kernel.
+// gate/up kernel.  With S the shared expert's items run in the same two
+// launches (hs: its f16 [T][I] SwiGLU output); S needs
+// decode_fuses_shared.
+bool decode_fuses_shared(const LayerPtrs &L, const SharedPtrs *S);
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
-                                 hipEvent_t e1 = nullptr);
+                                 hipEvent_t e1 = nullptr, const SharedPtrs *S = nullptr, uint16_t *hs = nullptr);
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64
 // tokens in one launch; clears y (T*H floats); with yres writes the residual
@@ -96,7 +101,8 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
 bool decode_routes_in_block(int64_t T, int k, int E);
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, uint16_t *h,
-                                        float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+                                        float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
+                                        const SharedPtrs *S = nullptr, uint16_t *hs = nullptr);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
@@ -122,7 +128,6 @@ hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, 
 // Shared expert (int8 symmetric group 128) for few tokens: gate/up + SwiGLU
 // -> h (f16 [T][I] workspace), then down -> y = (accumulate ? y : 0) + o.
 // e0 / e1 time the gate/up kernel.
-struct SharedPtrs;
 hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *h, float *y, bool accumulate,
                          hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_dequant_int8(const SharedPtrs &S, int proj, float *out, hipStream_t s);

@@ -16,10 +16,12 @@ class MoeQ4Layer:
     ``weights``: object with num_experts, hidden, inter, fmt and the six
     device tensors gate_q, up_q, down_q, gate_sm, up_sm, down_sm (canonical
     layout of include/moe_q4.h).  ``mode``: "decode" (GEMV path) or
-    "prefill" (grouped-GEMM path).
+    "prefill" (grouped-GEMM path).  ``shared``: the layer's shared expert
+    (hidden, inter and the six int8 code / f16 scale tensors) or None;
+    forward() then adds its output to every token's.
     """
 
-    def __init__(self, weights, k: int, max_tokens: int, mode: str = "decode", device="cuda"):
+    def __init__(self, weights, k: int, max_tokens: int, mode: str = "decode", device="cuda", shared=None):
         if mode not in ("decode", "prefill"):
             raise ValueError("mode must be 'decode' or 'prefill'")
         self.w = weights
@@ -32,7 +34,12 @@ class MoeQ4Layer:
         kind = _lib.WS_DECODE if mode == "decode" else _lib.WS_PREFILL
         nbytes = max(_lib.workspace_size(kind, T, self.E, k, self.H, self.I), 256)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        fbytes = max(_lib.workspace_size(_lib.WS_FORWARD, T, self.E, k, self.H, self.I), 256)
+        self.shared = _lib.shared_struct(shared) if shared is not None else None
+        self._shared_obj = shared
+        fbytes = _lib.workspace_size(_lib.WS_FORWARD, T, self.E, k, self.H, self.I)
+        if shared is not None:
+            fbytes += _lib.workspace_size(_lib.WS_SHARED, T, 1, 1, self.H, shared.inter)
+        fbytes = max(fbytes, 256)
         self.ws_forward = torch.zeros(fbytes, dtype=torch.uint8, device=device)
         _lib.moe_q4_workspace_init(self.ws_forward)
         self.logits = torch.empty((T, self.E), dtype=torch.int16, device=device)
@@ -65,6 +72,6 @@ class MoeQ4Layer:
         if router_w is None:
             lg.copy_(logits)
         y = self.y[:T]
-        _lib.moe_q4_forward(x, residual_y, x_out, router_w, bias, lg, T, self.k, self.struct, self.idx[:T],
-                            self.gate[:T], y, self.ws_forward)
+        _lib.moe_q4_forward_ex(x, residual_y, x_out, router_w, bias, lg, T, self.k, self.struct, self.shared,
+                               self.idx[:T], self.gate[:T], y, self.ws_forward)
         return y

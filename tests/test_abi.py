@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -212,3 +212,22 @@ def test_shared_validation():
     assert L.moe_q4_dequant_int8(ctypes.byref(_shared()), 3, FAKE, None) == _lib.ERR_INVALID_ARG
     assert L.moe_q4_dequant_int8(ctypes.byref(_shared()), 0, None, None) == _lib.ERR_INVALID_ARG
     assert L.moe_q4_dequant_int8(ctypes.byref(_shared(I=96)), 0, FAKE, None) == _lib.ERR_UNSUPPORTED
+
+
+def test_forward_ex_shared_validation():
+    L = m.lib()
+    lay = _layer()
+
+    def call(sx, T=4, ws_bytes=1 << 30):
+        return L.moe_q4_forward_ex(FAKE, None, None, FAKE, None, FAKE, T, 8, ctypes.byref(lay),
+                                   ctypes.byref(sx) if sx is not None else None, FAKE, FAKE, FAKE, FAKE, ws_bytes,
+                                   None, None)
+
+    assert call(_shared(null="down_s")) == _lib.ERR_INVALID_ARG
+    assert call(_shared(H=1024)) == _lib.ERR_INVALID_ARG          # hidden differs from the layer's
+    assert call(_shared(I=96)) == _lib.ERR_UNSUPPORTED
+    assert call(_shared(), T=0) == _lib.OK
+    fwd = m.workspace_size(m.WS_FORWARD, 4, 256, 8, 2048, 512)
+    sh = m.workspace_size(m.WS_SHARED, 4, 1, 1, 2048, 1024)
+    assert call(_shared(I=1024), ws_bytes=fwd + sh - 1) == _lib.ERR_WORKSPACE
+    assert call(None, ws_bytes=fwd - 1) == _lib.ERR_WORKSPACE

@@ -1,12 +1,15 @@
 """Shared expert (int8 symmetric group 128) on the HIP path against the CPU
 oracle, through the C ABI (needs an MI355X).
 
-Bars: dequantised weights bit-exact; outputs within the layer tolerance
-(relative L2 2e-3, max abs 1e-2 against the fp64 oracle).  Inputs: the
-synthetic shared expert of the layer recipe (H = 2048, I = 512, Gaussian
-weights encoded by synth.quantize_int8) at the decode, frame and long
-prefill token counts (sampled tokens at 4096), plus random codes at the
-smallest and largest supported shapes and ragged token counts.
+Bars: dequantised weights and expert indices bit-exact; outputs within the
+layer tolerance (relative L2 2e-3, max abs 1e-2 against the fp64 oracle).
+Inputs: the synthetic shared expert of the layer recipe (H = 2048, I = 512,
+Gaussian weights encoded by synth.quantize_int8) at the decode, frame and
+long prefill token counts (sampled tokens at 4096), plus random codes at the
+smallest and largest supported shapes and ragged token counts; the layer
+forward with a shared expert on each of its paths (routing inside the
+expert launches, in the routing launch, shared items fused or on their own,
+prefill).
 """
 from __future__ import annotations
 
@@ -144,3 +147,100 @@ def test_shared_zero_tokens_is_a_no_op():
     m.moe_q4_shared(x, 0, sx, y, False, None)
     torch.cuda.synchronize()
     assert bool((y == 3.0).all())
+
+
+# ------------------------------------------------------- layer with shared
+
+def hip_forward_shared(lay, sx, x, k, router_w=None, logits=None, residual_y=None):
+    import quantized_moe_expert_amd as m
+    T, H, E = x.shape[0], lay.hidden, lay.num_experts
+    nb = m.workspace_size(m.WS_FORWARD, T, E, k, H, lay.inter)
+    if sx is not None:
+        nb += m.workspace_size(m.WS_SHARED, T, 1, 1, H, sx.inter)
+    ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+    m.moe_q4_workspace_init(ws)
+    lg = torch.empty((T, E), dtype=torch.int16, device="cuda") if logits is None else logits.clone()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    x_out = torch.empty_like(x) if residual_y is not None else None
+    m.moe_q4_forward_ex(x, residual_y, x_out, router_w, None, lg, T, k, lay, sx, idx, gate, y, ws)
+    torch.cuda.synchronize()
+    return y, idx, x_out
+
+
+def oracle_layer_shared(lay, sx, x_np, k, router_w=None, logits=None):
+    T = x_np.shape[0]
+    _, idx, gate, y = oracle.moe_layer(lay, x_np, T, k, router_w=None if router_w is None else np_u16(router_w),
+                                       logits=None if logits is None else np_u16(logits))
+    if sx is None:
+        return idx, y
+    return idx, oracle.shared(sx.hidden, sx.inter, *host(sx), x_np, T, y_in=y)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_forward_shared_recipe(T):
+    """The frame layer recipe (E = 256, k = 8, GEMV router) with the synthetic
+    shared expert: T = 1 routes inside the expert launches, T = 16 in the
+    routing launch; both run the shared items inside the expert launches."""
+    cfg = 2 if T == 1 else 4
+    case = synth.make_case(cfg, device="cuda", layers=1) if cfg == 4 else synth.make_case(cfg, device="cuda")
+    sx = recipe_shared()
+    say(f"[forward+shared] {case.name} T={T}")
+    y, idx, _ = hip_forward_shared(case.layers[0], sx, case.x, case.k, router_w=case.router_w)
+    ir, yr = oracle_layer_shared(case.layers[0], sx, np_u16(case.x), case.k, router_w=case.router_w)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    r, a = assert_close(y.cpu().numpy(), yr, f"forward+shared T={T}")
+    say(f"[forward+shared] T={T}: rel L2 {r:.2e}, max abs {a:.2e}")
+
+
+@pytest.mark.parametrize("I_s", [256, 512])
+@pytest.mark.parametrize("T", [1, 7, 37, 200])
+def test_forward_shared_ragged(T, I_s):
+    """E = 64 random layer (I = 256): I_s = 256 fuses the shared items into
+    the decode launches, I_s = 512 runs them on their own; T = 200 takes the
+    prefill path."""
+    H, I, E, k = 512, 256, 64, 6
+    say(f"[forward+shared] ragged T={T} I_s={I_s}")
+    lay = synth.random_layer(E, H, I, synth.FMT_ASYM_G64, seed=11, device="cuda")
+    sx = synth.random_shared(H, I_s, seed=11, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 11, f"fs/x/{T}", "cuda"))
+    wr = synth.bf16_bits(synth.normal((E, H), 0.05, 11, "fs/w", "cuda"))
+    y, idx, _ = hip_forward_shared(lay, sx, x, k, router_w=wr)
+    ir, yr = oracle_layer_shared(lay, sx, np_u16(x), k, router_w=wr)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    assert_close(y.cpu().numpy(), yr, f"forward+shared ragged T={T} I_s={I_s}")
+
+
+def test_forward_shared_residual_and_given_logits():
+    """Residual input bf16(x + y_prev) and given logits, with the shared expert."""
+    H, I, E, k, T = 512, 256, 64, 6, 9
+    lay = synth.random_layer(E, H, I, synth.FMT_SYM_G128, seed=13, device="cuda")
+    sx = synth.random_shared(H, I, seed=13, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 13, "fsr/x", "cuda"))
+    yprev = synth.normal((T, H), 0.3, 13, "fsr/y", "cuda")
+    lg = synth.bf16_bits(synth.normal((T, E), 1.0, 13, "fsr/lg", "cuda"))
+    y, idx, x_out = hip_forward_shared(lay, sx, x, k, logits=lg, residual_y=yprev)
+    xin = oracle.residual(np_u16(x), yprev.cpu().numpy())
+    assert np.array_equal(np_u16(x_out), xin)
+    ir, yr = oracle_layer_shared(lay, sx, xin, k, logits=lg)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    assert_close(y.cpu().numpy(), yr, "forward+shared residual")
+
+
+def test_forward_without_shared_unchanged():
+    """forward_ex with no shared expert equals moe_q4_forward bit for bit."""
+    import quantized_moe_expert_amd as m
+    case = synth.make_case(4, device="cuda", layers=1)
+    lay, T, k = case.layers[0], case.T, case.k
+    y1, _, _ = hip_forward_shared(lay, None, case.x, k, router_w=case.router_w)
+    ws = torch.zeros(m.workspace_size(m.WS_FORWARD, T, case.E, k, case.H, case.I), dtype=torch.uint8, device="cuda")
+    m.moe_q4_workspace_init(ws)
+    lg = torch.empty((T, case.E), dtype=torch.int16, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((T, case.H), dtype=torch.float32, device="cuda")
+    m.moe_q4_forward(case.x, None, None, case.router_w, None, lg, T, k, lay, idx, gate, y2, ws)
+    ir, yr = oracle_layer_shared(lay, None, np_u16(case.x), k, router_w=case.router_w)
+    assert_close(y1.cpu().numpy(), yr, "forward_ex without shared")
+    assert_close(y2.cpu().numpy(), yr, "forward")
