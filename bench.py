@@ -15,6 +15,12 @@ Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
   prefill       512 tokens, Zipf(1.1)-popular experts (logits given), asym g64.
   long_prefill  4096 tokens, N(0,1) logits given, sym g128.
   tiny          4 tokens, 16 experts, top-2 (correctness size).
+  decode_shared, frame_shared
+                decode / frame with each layer's shared expert (int8
+                symmetric g128, inter 512) in the same forward call.
+  shared        the shared expert alone (moe_q4_shared) for the frame's 16
+                tokens; steps rotate over 200 address-distinct copies (3 MB
+                each) so its codes are read from HBM.
 
 One JSON line on stdout: value = tokens/s of whole steps (inputs resident in
 HBM), roofline of the dominant kernel measured with HIP events recorded on the
@@ -38,7 +44,10 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s, prefill MFMA TFLOPs (% of peak)"
 
 WORKLOADS = {
     "tiny": 1, "decode": 2, "prefill": 3, "frame": 4, "long_prefill": 5,
+    "decode_shared": 2, "frame_shared": 4, "shared": 4,
 }
+SHARED_INTER = 512   # the shared expert's inner size (that of a routed expert)
+SHARED_COPIES = 200  # address-distinct shared experts of the "shared" workload
 
 
 def log(*a):
@@ -128,6 +137,17 @@ def expert_bytes(lay) -> int:
     return lay.nbytes() // lay.num_experts
 
 
+def clone_shared(sx):
+    import synth
+    return synth.SharedExpert(hidden=sx.hidden, inter=sx.inter, **{n: getattr(sx, n).clone() for n in (
+        "gate_q", "up_q", "down_q", "gate_s", "up_s", "down_s")})
+
+
+def shared_gateup_bytes(sx) -> int:
+    """Codes and scales of the shared expert's gate and up projections."""
+    return sum(t.numel() * t.element_size() for t in (sx.gate_q, sx.up_q, sx.gate_s, sx.up_s))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -148,26 +168,28 @@ def main():
     dev = torch.device("cuda")
     cfg = WORKLOADS[args.workload]
     defaults = {"tiny": (200, 20), "decode": (400, 40), "prefill": (50, 5), "frame": (10, 2),
-                "long_prefill": (20, 3)}
+                "long_prefill": (20, 3), "decode_shared": (400, 40), "frame_shared": (10, 2), "shared": (400, 40)}
     K = args.steps if args.steps is not None else defaults[args.workload][0]
     W = args.warmup if args.warmup is not None else defaults[args.workload][1]
 
     t0 = time.time()
-    case = synth.make_case(cfg, device="cuda")
+    only_shared = args.workload == "shared"
+    with_shared = args.workload in ("decode_shared", "frame_shared", "shared")
+    case = synth.make_case(cfg, device="cuda", layers=1 if only_shared else None)
     torch.cuda.synchronize()
-    log(f"[bench] generated {args.workload} inputs in {time.time() - t0:.1f}s")
     T, H, E, k, I = case.T, case.H, case.E, case.k, case.I
-    decode_path = args.workload in ("tiny", "decode", "frame")
+    base_wl = {"decode_shared": "decode", "frame_shared": "frame"}.get(args.workload, args.workload)
+    decode_path = base_wl in ("tiny", "decode", "frame", "shared")
     mode = "decode" if decode_path else "prefill"
 
     # ---- per-step units of work ------------------------------------------------
-    if args.workload == "decode":
+    if base_wl == "decode":
         copies = max(1, args.copies)
         base = case.layers[0]
         layers = [base] + [clone_layer(base) for _ in range(copies - 1)]
         routers = [case.router_w] + [case.router_w.clone() for _ in range(copies - 1)]
         nl_per_step = 1
-    elif args.workload == "frame":
+    elif base_wl == "frame":
         layers = case.layers
         routers = case.router_ws
         nl_per_step = len(layers)
@@ -175,9 +197,23 @@ def main():
         layers = case.layers
         routers = case.router_ws or [None]
         nl_per_step = 1
+    shareds = None
+    if with_shared:
+        if base_wl == "frame":  # one shared expert per layer
+            shareds = [synth.make_shared(H, SHARED_INTER, 0, f"{case.name}/L{l}/shared", device="cuda")
+                       for l in range(len(layers))]
+        else:
+            s0 = synth.make_shared(H, SHARED_INTER, 0, f"{case.name}/shared", device="cuda")
+            n_sx = SHARED_COPIES if only_shared else len(layers)
+            shareds = [s0] + [clone_shared(s0) for _ in range(n_sx - 1)]
     torch.cuda.synchronize()
+    log(f"[bench] generated {args.workload} inputs in {time.time() - t0:.1f}s")
     structs = [m.layer_struct(l) for l in layers]
-    wsf = torch.zeros(max(m.workspace_size(m.WS_FORWARD, T, E, k, H, I), 256), dtype=torch.uint8, device=dev)
+    sstructs = [m.shared_struct(sx) for sx in shareds] if shareds else None
+    ws_bytes = m.workspace_size(m.WS_FORWARD, T, E, k, H, I)
+    if with_shared:
+        ws_bytes += m.workspace_size(m.WS_SHARED, T, 1, 1, H, SHARED_INTER)
+    wsf = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     m.moe_q4_workspace_init(wsf)
     lg = torch.empty((T, E), dtype=torch.int16, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -187,42 +223,48 @@ def main():
     state = {"i": 0}
 
     def layer_ids():
-        if args.workload == "decode":
+        if base_wl == "decode":
             return [state["i"] % len(layers)]
+        if only_shared:
+            return [state["i"] % len(shareds)]
         return list(range(nl_per_step))
 
-    def step():
-        """One step: every layer of the workload once, each one moe_q4_forward
-        call (routing, grouping, experts; the residual of a chain fused in)."""
-        for j, li in enumerate(layer_ids()):
-            rw = routers[li] if routers[0] is not None else None
-            logits_in = lg if rw is not None else case.logits
-            if args.workload == "frame" and j > 0:
-                x_prev = case.x if j == 1 else xbuf[(j - 1) & 1]
-                m.moe_q4_forward(x_prev, ybuf[(j - 1) & 1], xbuf[j & 1], rw, None, logits_in, T, k, structs[li],
-                                 idx, gate, ybuf[j & 1], wsf)
+    def call(j, li, evs):
+        """One layer: moe_q4_forward_ex (routing, grouping, experts, the
+        shared expert when present; the residual of a chain fused in), or
+        the shared expert alone.  evs: None or the 4 stage events."""
+        if only_shared:
+            if evs is None:
+                m.moe_q4_shared(case.x, T, sstructs[li], ybuf[0], 0, wsf)
             else:
-                m.moe_q4_forward(case.x, None, None, rw, None, logits_in, T, k, structs[li], idx, gate,
-                                 ybuf[j & 1], wsf)
+                m.moe_q4_shared_timed(case.x, T, sstructs[li], ybuf[0], 0, wsf, evs)
+            return
+        rw = routers[li] if routers[0] is not None else None
+        logits_in = lg if rw is not None else case.logits
+        sx = sstructs[li] if sstructs else None
+        if base_wl == "frame" and j > 0:
+            x_prev = case.x if j == 1 else xbuf[(j - 1) & 1]
+            m.moe_q4_forward_ex(x_prev, ybuf[(j - 1) & 1], xbuf[j & 1], rw, None, logits_in, T, k, structs[li], sx,
+                                idx, gate, ybuf[j & 1], wsf, events=evs)
+        else:
+            m.moe_q4_forward_ex(case.x, None, None, rw, None, logits_in, T, k, structs[li], sx, idx, gate,
+                                ybuf[j & 1], wsf, events=evs)
+
+    def step():
+        """One step: every layer of the workload once."""
+        for j, li in enumerate(layer_ids()):
+            call(j, li, None)
         state["i"] += 1
 
     def step_profiled(evsets):
-        """The calls of step(), through moe_q4_forward_timed: the runtime
-        records the events at the start and end of the call's two main
-        kernels (gate/up and routing launches for decode, the two grouped
-        GEMMs for prefill) on the launch stream."""
+        """The calls of step() with stage events: the runtime records them at
+        the start and end of the call's two main kernels (gate/up and routing
+        launches for decode, the two grouped GEMMs for prefill, gate/up and
+        down launches of the shared expert alone) on the launch stream."""
         for j, li in enumerate(layer_ids()):
-            rw = routers[li] if routers[0] is not None else None
-            logits_in = lg if rw is not None else case.logits
-            evs = [e.cuda_event for e in evsets[j]]
-            if args.workload == "frame" and j > 0:
-                x_prev = case.x if j == 1 else xbuf[(j - 1) & 1]
-                m.moe_q4_forward_timed(x_prev, ybuf[(j - 1) & 1], xbuf[j & 1], rw, None, logits_in, T, k,
-                                       structs[li], idx, gate, ybuf[j & 1], wsf, evs)
-            else:
-                m.moe_q4_forward_timed(case.x, None, None, rw, None, logits_in, T, k, structs[li], idx, gate,
-                                       ybuf[j & 1], wsf, evs)
-            routed.append(idx.clone())
+            call(j, li, [e.cuda_event for e in evsets[j]])
+            if not only_shared:
+                routed.append(idx.clone())
         state["i"] += 1
 
     routed = []
@@ -267,19 +309,31 @@ def main():
 
     # work actually routed in the profiled layer (outside timed regions)
     # active experts per profiled layer call, averaged (the frame's layers differ)
-    act = float(np.mean([torch.unique(r).numel() for r in routed]))
+    act = float(np.mean([torch.unique(r).numel() for r in routed])) if routed else 0.0
     lay0 = layers[0]
     proj_bytes = expert_bytes(lay0) // 3        # one projection of one expert (codes + scales)
     P = T * k
-    if decode_path:
-        # dominant kernel: gate/up GEMV + SwiGLU: reads the gate and up codes and
-        # scales of every active expert once and the activations, writes h (fp32)
-        dom = "decode_gateup_kernel"
-        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 4
+    sx_bytes = shared_gateup_bytes(shareds[0]) + T * SHARED_INTER * 2 if with_shared else 0
+    if only_shared:
+        # dominant kernel: the shared gate/up GEMV + SwiGLU: its int8 codes and
+        # scales once, the activations, h (f16) out
+        dom = "shared_gateup_kernel"
+        alg_bytes = sx_bytes + T * H * 2
         achieved = alg_bytes / (stage_avg[0] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(dom, args.workload, "decode.hip"), "kernel": dom,
+                "traffic": recorded_traffic(dom, args.workload, "shared.hip"), "kernel": dom,
+                "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_bytes": int(alg_bytes)}
+    elif decode_path:
+        # dominant kernel: gate/up GEMV + SwiGLU: reads the gate and up codes and
+        # scales of every active expert once and the activations, writes h (f16)
+        dom = "decode_gateup_kernel"
+        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 2 + sx_bytes
+        achieved = alg_bytes / (stage_avg[0] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(dom, args.workload, "decode.hip"), "kernel": dom + (
+                    " (routed and shared items)" if with_shared else ""),
                 "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_bytes": int(alg_bytes),
                 "active_experts": int(act)}
     else:
@@ -306,7 +360,8 @@ def main():
     # ---- CPU oracle on a bounded sample ------------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, args, decode_path, args.cpu_seconds)
+        cpu = cpu_baseline(case, args, decode_path, args.cpu_seconds, shareds[0] if with_shared else None,
+                           only_shared)
 
     names = {"tiny": "tiny layer: 4 tokens, H=256, 16 experts, top-2, I=128, int4 asym g64",
              "decode": "decode step, 1 MoE layer: 1 token, H=2048, 256 experts, top-8, I=512, int4 asym g64 "
@@ -317,17 +372,25 @@ def main():
                       "int4 asym g64 (RTN), residual chain",
              "long_prefill": "long prefill, 1 MoE layer: 4096 tokens, N(0,1) logits, H=2048, 256 experts, top-8, "
                              "I=512, int4 sym g128"}
+    sx_note = f" + shared expert int8 sym g128 I={SHARED_INTER} per layer"
+    names["decode_shared"] = names["decode"] + sx_note
+    names["frame_shared"] = names["frame"] + sx_note
+    names["shared"] = (f"shared expert alone: 16 tokens, H=2048, I={SHARED_INTER}, int8 sym g128; "
+                       f"{SHARED_COPIES} address-distinct copies rotated")
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
            "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16" if decode_path else "f16", "data": "synthetic",
-           "config": {"workload": names[args.workload], "tokens": T, "hidden": H, "experts": E, "top_k": k,
-                      "inter": I, "layers_per_step": nl_per_step, "path": mode,
-                      "format": "asym_g64" if case.fmt == synth.FMT_ASYM_G64 else "sym_g128"},
+           "config": {"workload": names[args.workload], "tokens": T, "hidden": H, "experts": 0 if only_shared else E,
+                      "top_k": 0 if only_shared else k, "inter": SHARED_INTER if only_shared else I,
+                      "layers_per_step": nl_per_step, "path": mode,
+                      "format": "int8_sym_g128" if only_shared else (
+                          "asym_g64" if case.fmt == synth.FMT_ASYM_G64 else "sym_g128"),
+                      "shared_expert": with_shared},
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(case, args, decode_path, budget_s):
+def cpu_baseline(case, args, decode_path, budget_s, shared=None, only_shared=False):
     """The oracle as it stands, on host cores, over a bounded sample of the same workload."""
     import numpy as np
 
@@ -336,6 +399,7 @@ def cpu_baseline(case, args, decode_path, budget_s):
     T, H, E, k = case.T, case.H, case.E, case.k
     lay = case.layers[0]
     host_layer = oracle.layer_np(lay)
+    host_sx = [t.cpu().numpy() for t in shared.tensors()] if shared is not None else None
     x_np = case.x.cpu().numpy().view(np.uint16)
     rw = case.router_ws[0].cpu().numpy().view(np.uint16) if case.router_ws else None
     lg_all = case.logits.cpu().numpy().view(np.uint16) if case.logits is not None else None
@@ -348,16 +412,22 @@ def cpu_baseline(case, args, decode_path, budget_s):
         sel = rng_tokens[(reps * per) % T:(reps * per) % T + per]
         t1 = time.perf_counter()
         xs = np.ascontiguousarray(x_np[sel])
-        lg = oracle.router(xs, rw, len(sel), H, E) if rw is not None else np.ascontiguousarray(lg_all[sel])
-        idx, gate = oracle.topk(lg, len(sel), E, k)
-        oracle.experts(lay.fmt, E, H, lay.inter, *host_layer, xs, idx, gate, len(sel), k)
+        y = None
+        if not only_shared:
+            lg = oracle.router(xs, rw, len(sel), H, E) if rw is not None else np.ascontiguousarray(lg_all[sel])
+            idx, gate = oracle.topk(lg, len(sel), E, k)
+            y = oracle.experts(lay.fmt, E, H, lay.inter, *host_layer, xs, idx, gate, len(sel), k)
+        if host_sx is not None:
+            oracle.shared(H, shared.inter, *host_sx, xs, len(sel), y_in=y)
         t_total += time.perf_counter() - t1
         done_tokens += len(sel)
         reps += 1
     value = done_tokens / t_total
+    what = "shared expert" if only_shared else (
+        "route + experts + combine" + (" + shared expert" if host_sx is not None else ""))
     return {"value": round(value, 3), "unit": "tokens/s (one layer)", "cores": threads, "kind": "oracle",
             "sample": f"{done_tokens} tokens of layer 0 in {reps} calls of {per} token(s), "
-                      f"{t_total:.1f} s (route + experts + combine, fp64)"}
+                      f"{t_total:.1f} s ({what}, fp64)"}
 
 
 if __name__ == "__main__":

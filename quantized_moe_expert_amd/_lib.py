@@ -22,7 +22,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_decode", "moe_q4_prefill",
            "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_forward_timed",
            "moe_q4_workspace_init",
-           "moe_q4_shared", "moe_q4_dequant_int8", "moe_q4_forward_ex",
+           "moe_q4_shared", "moe_q4_shared_timed", "moe_q4_dequant_int8", "moe_q4_forward_ex",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string")
 STAGE_EVENTS = 4
 
@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.moe_q4_dequant.argtypes = [ctypes.POINTER(Layer), i32, i32, P, P]
         L.moe_q4_shared.restype = ctypes.c_int
         L.moe_q4_shared.argtypes = [P, i64, ctypes.POINTER(SharedExpert), P, i32, P, sz, P]
+        L.moe_q4_shared_timed.restype = ctypes.c_int
+        L.moe_q4_shared_timed.argtypes = [P, i64, ctypes.POINTER(SharedExpert), P, i32, P, sz, P,
+                                          ctypes.POINTER(ctypes.c_void_p)]
         L.moe_q4_dequant_int8.restype = ctypes.c_int
         L.moe_q4_dequant_int8.argtypes = [ctypes.POINTER(SharedExpert), i32, P, P]
         L.moe_q4_residual_bf16.restype = ctypes.c_int
@@ -260,6 +263,16 @@ def moe_q4_shared(x, T, shared, y, accumulate, ws, stream=None):
     st = shared_struct(shared) if not isinstance(shared, SharedExpert) else shared
     _check("moe_q4_shared", lib().moe_q4_shared(_ptr(x), T, ctypes.byref(st), _ptr(y), int(bool(accumulate)), w, nb,
                                                  _stream(stream)))
+
+
+def moe_q4_shared_timed(x, T, shared, y, accumulate, ws, events, stream=None):
+    """moe_q4_shared that has the runtime record the 4 given hipEvent_t handles at the start and end of its
+    gate/up launch ([0], [1]) and its down launch ([2], [3])."""
+    w, nb = _ws(ws)
+    st = shared_struct(shared) if not isinstance(shared, SharedExpert) else shared
+    ev = (ctypes.c_void_p * STAGE_EVENTS)(*[int(e) for e in events])
+    _check("moe_q4_shared_timed", lib().moe_q4_shared_timed(_ptr(x), T, ctypes.byref(st), _ptr(y),
+                                                             int(bool(accumulate)), w, nb, _stream(stream), ev))
 
 
 def moe_q4_dequant_int8(shared, proj, out, stream=None):

@@ -419,8 +419,8 @@ int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *o
     return hip_status(launch_dequant(layer_ptrs(w), expert, proj, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int moe_q4_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y, int32_t accumulate, void *ws,
-                  size_t ws_bytes, moe_q4_stream stream) {
+static int run_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y, int32_t accumulate,
+                      void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events) {
     int st = check_shared(sx);
     if (st) return st;
     if (T < 0 || !x || !y) return MOE_Q4_ERR_INVALID_ARG;
@@ -432,8 +432,23 @@ int moe_q4_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, floa
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
     Carver c{static_cast<char *>(ws)};
     uint16_t *h = c.take<uint16_t>(T * (int64_t)I);
+    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
     return hip_status(launch_shared(static_cast<const uint16_t *>(x), T, shared_ptrs(sx), h, y, accumulate != 0,
-                                    reinterpret_cast<hipStream_t>(stream)));
+                                    reinterpret_cast<hipStream_t>(stream), ev ? ev[0] : nullptr,
+                                    ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr));
+}
+
+int moe_q4_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y, int32_t accumulate, void *ws,
+                  size_t ws_bytes, moe_q4_stream stream) {
+    return run_shared(x, T, sx, y, accumulate, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_q4_shared_timed(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y, int32_t accumulate,
+                        void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events) {
+    if (!events) return MOE_Q4_ERR_INVALID_ARG;
+    for (int i = 0; i < MOE_Q4_STAGE_EVENTS; ++i)
+        if (!events[i]) return MOE_Q4_ERR_INVALID_ARG;
+    return run_shared(x, T, sx, y, accumulate, ws, ws_bytes, stream, events);
 }
 
 int moe_q4_dequant_int8(const moe_q4_shared_expert *sx, int32_t proj, float *out, moe_q4_stream stream) {

@@ -426,9 +426,10 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     if constexpr (SHARED && LPR >= 2) {  // shared expert: H / 32 lanes per row
         constexpr int LPS = 2 * LPR, BRS = DEC_WAVES * (WAVE / LPS);
-        const Items is = decode_items((T + DECODE_TT - 1) / DECODE_TT, S.I, S.I / BRS);
+        const int ntt = (T + DECODE_TT - 1) / DECODE_TT;
+        const Items is = decode_items(ntt, S.I, S.I / BRS);
         for (int w = is.first; w < is.end; w += is.stride) {
-            const int j = w / is.nch, chunk = w % is.nch;
+            const int j = w % ntt, chunk = w / ntt;  // chunk-major: a chunk's token tiles share an XCD
             const int tok0 = j * DECODE_TT, nt = T - tok0 < DECODE_TT ? T - tok0 : DECODE_TT;
             const ItemRows<BRS> ir = item_rows<BRS>(chunk, is, S.I);
             if (ir.steps <= 0) continue;
@@ -477,9 +478,10 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
     }
     if constexpr (SHARED && LPR >= 4) {
-        const Items is = decode_items((T + DECODE_TT - 1) / DECODE_TT, H, H / BR);
+        const int ntt = (T + DECODE_TT - 1) / DECODE_TT;
+        const Items is = decode_items(ntt, H, H / BR);
         for (int w = is.first; w < is.end; w += is.stride) {
-            const int j = w / is.nch, chunk = w % is.nch;
+            const int j = w % ntt, chunk = w / ntt;  // chunk-major: a chunk's token tiles share an XCD
             const int tok0 = j * DECODE_TT, nt = T - tok0 < DECODE_TT ? T - tok0 : DECODE_TT;
             const ItemRows<BR> ir = item_rows<BR>(chunk, is, H);
             if (ir.steps <= 0) continue;

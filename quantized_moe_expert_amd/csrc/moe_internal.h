@@ -127,9 +127,10 @@ hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, 
 
 // Shared expert (int8 symmetric group 128) for few tokens: gate/up + SwiGLU
 // -> h (f16 [T][I] workspace), then down -> y = (accumulate ? y : 0) + o.
-// e0 / e1 time the gate/up kernel.
+// e0 / e1 time the gate/up kernel, e2 / e3 the down kernel.
 hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *h, float *y, bool accumulate,
-                         hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+                         hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr, hipEvent_t e2 = nullptr,
+                         hipEvent_t e3 = nullptr);
 hipError_t launch_dequant_int8(const SharedPtrs &S, int proj, float *out, hipStream_t s);
 hipError_t launch_residual(const uint16_t *x, const float *y, int64_t n, uint16_t *out, hipStream_t s);
 

@@ -14,7 +14,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void shared_gateup_kernel(const uin
     const Items it = decode_items(ntt, S.I, S.I / BR);
     __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     for (int w = it.first; w < it.end; w += it.stride) {
-        const int j = w / it.nch, chunk = w % it.nch;
+        const int j = w % ntt, chunk = w / ntt;  // chunk-major: a chunk's token tiles share an XCD
         const int tok0 = j * DECODE_TT, nt = T - tok0 < DECODE_TT ? T - tok0 : DECODE_TT;
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, S.I);
         if (ir.steps <= 0) continue;
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void shared_down_kernel(int T, Shar
     const Items it = decode_items(ntt, S.H, S.H / BR);
     __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     for (int w = it.first; w < it.end; w += it.stride) {
-        const int j = w / it.nch, chunk = w % it.nch;
+        const int j = w % ntt, chunk = w / ntt;  // chunk-major: a chunk's token tiles share an XCD
         const int tok0 = j * DECODE_TT, nt = T - tok0 < DECODE_TT ? T - tok0 : DECODE_TT;
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, S.H);
         if (ir.steps <= 0) continue;
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void shared_down_kernel(int T, Shar
 }
 
 hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *h, float *y, bool accumulate,
-                         hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                         hipStream_t s, hipEvent_t e0, hipEvent_t e1, hipEvent_t e2, hipEvent_t e3) {
     const dim3 block(DEC_WAVES * 64);
     switch (S.H / 32) {
 #define CASE(LP)                                                                                              \
@@ -56,7 +56,7 @@ hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint
 #define CASE(LP)                                                                                              \
     case LP: {                                                                                                \
         constexpr auto kern = shared_down_kernel<LP>;                                                         \
-        launch_k(kern, dim3(resident_grid<kern>()), block, s, nullptr, nullptr, (int)T, S,                    \
+        launch_k(kern, dim3(resident_grid<kern>()), block, s, e2, e3, (int)T, S,                              \
                  (const uint16_t *)h, y, accumulate ? 1 : 0);                                                 \
     } break;
         CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)

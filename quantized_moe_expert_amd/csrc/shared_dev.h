@@ -5,8 +5,10 @@
 // launches and, beside the routed experts' items, by the decode launches of
 // the layer.
 //
-// Work items are (token tile of up to DECODE_TT tokens, row chunk), cut and
-// dealt exactly as the routed decode items (decode_items, item_rows).
+// Work items are (token tile of up to DECODE_TT tokens, row chunk), cut as
+// the routed decode items (decode_items, item_rows) but numbered chunk-major,
+// so that the token tiles of one row chunk fall in one XCD's contiguous range
+// and read the chunk's codes through one L2.
 //
 // Code arithmetic.  A signed byte q becomes u = q + 128 by flipping its top
 // bit (one XOR per four codes):
