@@ -27,6 +27,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 FMT_ASYM_G64 = 0
 FMT_SYM_G128 = 1
+FMT_FP8_B128 = 2
 
 _lib = None
 
@@ -56,6 +57,8 @@ def bind(path: str):
     lib.oracle_f16_value.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_value.restype = ctypes.c_double
     lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_bf16_round.restype = ctypes.c_uint16
     lib.oracle_bf16_round.argtypes = [ctypes.c_float]
     lib.oracle_dequant.restype = i32
@@ -114,6 +117,18 @@ def bf16_value(bits: int) -> float:
     return _load().oracle_bf16_value(int(bits) & 0xFFFF)
 
 
+def e4m3_value(bits: int) -> float:
+    return _load().oracle_e4m3_value(int(bits) & 0xFF)
+
+
+def _scales(fmt, sm):
+    """Scale array as the library takes it: f16 bits, or float32 for fp8."""
+    if fmt == FMT_FP8_B128:
+        a = np.ascontiguousarray(sm)
+        return a if a.dtype == np.float32 else a.astype(np.float32)
+    return _c(sm, np.uint16)
+
+
 def bf16_round(f: float) -> int:
     return int(_load().oracle_bf16_round(float(f)))
 
@@ -126,9 +141,10 @@ def bf16_round_array(a) -> np.ndarray:
 
 
 def dequant(fmt: int, q, sm, N: int, K: int) -> np.ndarray:
-    """float32 [N][K] from packed uint8 [N][K/2] and f16-bit scales (see moe_oracle.c)."""
+    """float32 [N][K] from packed uint8 [N][K/2] and f16-bit scales, or (fp8)
+    uint8 codes [N][K] and float32 block scales [N/128][K/128] (see moe_oracle.c)."""
     q = _c(q, np.uint8)
-    sm = _c(sm, np.uint16)
+    sm = _scales(fmt, sm)
     out = np.empty((N, K), dtype=np.float32)
     rc = _load().oracle_dequant(int(fmt), _p(q), _p(sm), int(N), int(K), _p(out))
     if rc != 0:
@@ -172,7 +188,7 @@ def experts(fmt, E, H, I, gate_q, up_q, down_q, gate_sm, up_sm, down_sm,
             x, idx, gate, T: int, k: int, tokens=None) -> np.ndarray:
     """float32 y [ntok][H] for the listed tokens (all T when ``tokens`` is None)."""
     arrs = [_c(a, np.uint8) for a in (gate_q, up_q, down_q)]
-    sms = [_c(a, np.uint16) for a in (gate_sm, up_sm, down_sm)]
+    sms = [_scales(fmt, a) for a in (gate_sm, up_sm, down_sm)]
     x = _c(x, np.uint16)
     idx = _c(idx, np.int32)
     gate = _c(gate, np.float32)

@@ -26,7 +26,10 @@
  *   - rows grouped by routed expert: drama-rs page, "Apple Silicon (MLX)"
  *     and "Layout" (grouped MoE prefill);
  *   - the shared expert's linears are int8 symmetric group 128: drama-q4
- *     card, "What's quantized" (see oracle_shared).
+ *     card, "What's quantized" (see oracle_shared);
+ *   - block-FP8 experts with one scale per 128 x 128 block, each matrix
+ *     dequantised with its block scales: drama-3-w4a16 card, "At a glance"
+ *     table and "How it was made" (the released experts' format).
  * The pages do not state the routing function, the activation or the combine.
  * This library takes: bf16 router logits, the 8 (k) largest selected with
  * ties to the lower expert index, gates = softmax over the selected logits
@@ -41,6 +44,7 @@
 
 #define ORACLE_FMT_ASYM_G64 0
 #define ORACLE_FMT_SYM_G128 1
+#define ORACLE_FMT_FP8_B128 2
 
 /* ---------------------------------------------------------------- numbers */
 
@@ -86,9 +90,31 @@ uint16_t oracle_bf16_round(float f)
     return (uint16_t)kept;
 }
 
+/*
+ * OCP 8-bit float E4M3 ("fn": no infinities): sign bit 7, exponent bits 6..3
+ * with bias 7, mantissa bits 2..0.  Exponent 0 is subnormal, m/8 * 2^-6; the
+ * pattern S.1111.111 is NaN; the largest finite value is 1.75 * 2^8 = 448.
+ */
+double oracle_e4m3_value(uint8_t b)
+{
+    int sgn = b >> 7, e = (b >> 3) & 0xf, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return sgn ? -v : v;
+}
+
 /* --------------------------------------------------------------- dequant */
 
 static int group_of(int fmt) { return fmt == ORACLE_FMT_ASYM_G64 ? 64 : 128; }
+static int known_fmt(int fmt)
+{
+    return fmt == ORACLE_FMT_ASYM_G64 || fmt == ORACLE_FMT_SYM_G128 || fmt == ORACLE_FMT_FP8_B128;
+}
 
 /* 4-bit code of input index k in a packed row: byte k/2, low nibble for even k. */
 static int nibble(const uint8_t *row, int k)
@@ -99,9 +125,16 @@ static int nibble(const uint8_t *row, int k)
 /* Exact value of weight (n, k) of one [N][K] matrix.
  *   asym g64:  w = scale * q + min,  scale/min f16 at sm[(n*(K/64) + k/64)*2 + {0,1}]
  *   sym g128:  w = scale * (q - 8),  scale f16 at sm[n*(K/128) + k/128]
- * Both are exact in double (at most 15 + 40 significant bits). */
+ *   fp8 b128:  w = e4m3(q[n][k]) * scale, scale float32 at
+ *              ((const float *)sm)[(n/128)*(K/128) + k/128] (one per block of
+ *              128 rows x 128 inputs), codes one byte per weight
+ * All are exact in double (at most 15 + 40, or 4 + 24, significant bits). */
 static double weight(int fmt, const uint8_t *q, const uint16_t *sm, int K, int n, int k)
 {
+    if (fmt == ORACLE_FMT_FP8_B128) {
+        const float *bs = (const float *)sm;
+        return oracle_e4m3_value(q[(size_t)n * K + k]) * (double)bs[(size_t)(n / 128) * (K / 128) + k / 128];
+    }
     int g = group_of(fmt);
     int code = nibble(q + (size_t)n * (K / 2), k);
     size_t gi = (size_t)n * (K / g) + (size_t)(k / g);
@@ -113,7 +146,7 @@ static double weight(int fmt, const uint8_t *q, const uint16_t *sm, int K, int n
 /* Dequantise one [N][K] matrix to float32 (the exact value, rounded once). */
 int oracle_dequant(int fmt, const uint8_t *q, const uint16_t *sm, int N, int K, float *out)
 {
-    if ((fmt != ORACLE_FMT_ASYM_G64 && fmt != ORACLE_FMT_SYM_G128) || K % group_of(fmt))
+    if (!known_fmt(fmt) || K % group_of(fmt) || (fmt == ORACLE_FMT_FP8_B128 && N % 128))
         return -1;
     for (int n = 0; n < N; n++)
         for (int k = 0; k < K; k++)
@@ -229,7 +262,8 @@ static double silu(double a) { return a / (1.0 + exp(-a)); }
  *   y[t] = float( sum_{i = 0..k-1} gate[t][i] * o(t, i) )        (slot order)
  * Each expert that a listed token uses is dequantised (exactly, in double)
  * once, then applied to every listed (token, slot) routed to it.
- * Layout of the packed tensors: [E][N][K/2] bytes; scales as in weight().
+ * Layout of the code tensors: [E][N][K/2] bytes (int4) or [E][N][K] (fp8);
+ * scales as in weight(), one matrix after another.
  */
 int oracle_experts(int fmt, int E, int H, int I,
                    const uint8_t *gate_q, const uint8_t *up_q, const uint8_t *down_q,
@@ -238,7 +272,7 @@ int oracle_experts(int fmt, int E, int H, int I,
                    int64_t T, int k, const int64_t *tok, int64_t ntok, float *y)
 {
     int g = group_of(fmt);
-    if ((fmt != ORACLE_FMT_ASYM_G64 && fmt != ORACLE_FMT_SYM_G128) || H % g || I % g)
+    if (!known_fmt(fmt) || H % g || I % g)
         return -1;
     if (!tok)
         ntok = T;
@@ -253,6 +287,12 @@ int oracle_experts(int fmt, int E, int H, int I,
     size_t gu_bytes = (size_t)I * (H / 2), d_bytes = (size_t)H * (I / 2);
     size_t gu_sm = (size_t)I * (H / g) * (fmt == ORACLE_FMT_ASYM_G64 ? 2 : 1);
     size_t d_sm = (size_t)H * (I / g) * (fmt == ORACLE_FMT_ASYM_G64 ? 2 : 1);
+    if (fmt == ORACLE_FMT_FP8_B128) {  /* bytes per code; float scales counted in 16-bit units */
+        gu_bytes = (size_t)I * H;
+        d_bytes = (size_t)H * I;
+        gu_sm = (size_t)(I / 128) * (H / 128) * 2;
+        d_sm = (size_t)(H / 128) * (I / 128) * 2;
+    }
     /* o[j][i][d] for every listed (token, slot) */
     double *o = calloc((size_t)ntok * k * H, sizeof(double));
     if (!o)

@@ -13,7 +13,11 @@ Sources of the recipe (drama-rs / drama-q4 / drama-3-w4a16 model pages):
   * each scale is picked from 20 clipping ratios 1.0 down to 0.81 by least
     squared error, with no calibration data (drama-3-w4a16, "How it was
     made"; drama-q4 names the same "MSE clip search");
-  * router, activations: bf16 (drama-q4 "What's quantized": router bf16).
+  * router, activations: bf16 (drama-q4 "What's quantized": router bf16);
+  * block-FP8 experts: E4M3 codes with one float32 scale per block of 128
+    rows x 128 inputs, the released experts' format (drama-3-w4a16 card,
+    "At a glance": routed experts block-FP8 with 128 x 128 scales; "How it
+    was made": each matrix dequantised with its block scales).
 
 Random streams: every tensor gets its own torch.Generator seeded from
 (config seed, tensor tag) through a fixed 64-bit mix, so tensors do not depend
@@ -26,6 +30,8 @@ Layout written here (the library's canonical layout):
                   nibble and k = 2j+1 in its high nibble;
   asym scale/min  uint16 (f16 bits) [E][N][K/64][2] = {scale, min};
   sym scale       uint16 (f16 bits) [E][N][K/128];
+  fp8 codes       uint8 (E4M3 bits) [E][N][K], one byte per weight;
+  fp8 scale       float32 [E][N/128][K/128];
   gate, up: N = inter, K = hidden; down: N = hidden, K = inter.
 """
 from __future__ import annotations
@@ -38,7 +44,9 @@ import torch
 
 FMT_ASYM_G64 = 0
 FMT_SYM_G128 = 1
-GROUP = {FMT_ASYM_G64: 64, FMT_SYM_G128: 128}
+FMT_FP8_B128 = 2
+GROUP = {FMT_ASYM_G64: 64, FMT_SYM_G128: 128, FMT_FP8_B128: 128}
+E4M3_MAX = 448.0
 
 # 20 clipping ratios, 1.00, 0.99, ..., 0.81 (drama-3-w4a16, "How it was made").
 CLIP_RATIOS = tuple(round(1.0 - 0.01 * i, 2) for i in range(20))
@@ -137,14 +145,35 @@ def _quantize_sym_rows(w: torch.Tensor, g: int, ratios):
     return (best_q + 8).reshape(R, K).to(torch.uint8), best_s
 
 
+def quantize_fp8(w: torch.Tensor):
+    """Encode float32 weights [..., N, K] as E4M3 with one float32 scale per
+    128 x 128 block: scale = max |w| / 448 over the block, codes =
+    e4m3(w / scale) (torch's round-to-nearest-even cast; an all-zero block
+    gets scale 0 and codes 0).  Returns (codes uint8 [..., N, K], scales
+    float32 [..., N/128, K/128])."""
+    *lead, N, K = w.shape
+    if N % 128 or K % 128:
+        raise ValueError(f"({N}, {K}) is not a multiple of the 128 x 128 block")
+    wb = w.reshape(-1, N // 128, 128, K // 128, 128).float()
+    amax = wb.abs().amax(dim=(2, 4))
+    sc = amax / E4M3_MAX
+    safe = torch.where(sc > 0, sc, torch.ones_like(sc))[:, :, None, :, None]
+    v = (wb / safe).clamp_(-E4M3_MAX, E4M3_MAX)
+    q = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.reshape(*lead, N, K).contiguous(), sc.reshape(*lead, N // 128, K // 128).contiguous()
+
+
 def quantize(w: torch.Tensor, fmt: int, clip: bool = True):
     """Encode float32 weights [..., N, K] (groups along K).
 
     Returns (packed uint8 [..., N, K/2], scale/min int16 bits):
-      asym g64: [..., N, K/64, 2] = {scale, min};  sym g128: [..., N, K/128].
+      asym g64: [..., N, K/64, 2] = {scale, min};  sym g128: [..., N, K/128];
+    fp8 b128: (codes uint8 [..., N, K], float32 scales [..., N/128, K/128]).
     ``clip`` selects the 20-ratio least-squares search; without it only r = 1
     (plain round-to-nearest) is used.
     """
+    if fmt == FMT_FP8_B128:
+        return quantize_fp8(w)
     g = GROUP[fmt]
     *lead, N, K = w.shape
     if K % g:
@@ -393,6 +422,14 @@ def random_layer(E, H, I, fmt, seed, device="cpu", tag="rand") -> Layer:
     """
     g = GROUP[fmt]
     out = {}
+    if fmt == FMT_FP8_B128:
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            gen = generator(seed, f"{tag}/{name}", device)
+            q = torch.randint(0, 256, (E, N, K), generator=gen, device=device, dtype=torch.int32)
+            q = torch.where((q & 0x7f) == 0x7f, q - 1, q)  # no NaN codes
+            out[name + "_q"] = q.to(torch.uint8)
+            out[name + "_sm"] = torch.rand((E, N // 128, K // 128), generator=gen, device=device) * 1e-4 + 5e-5
+        return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, **out)
     for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
         gen = generator(seed, f"{tag}/{name}", device)
         q = torch.randint(0, 256, (E, N, K // 2), generator=gen, device=device, dtype=torch.int32)

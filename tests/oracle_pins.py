@@ -10,7 +10,9 @@ What pins what:
     torch's bfloat16 conversions (library routines), on every bit pattern or
     on a wide sample plus the halfway cases;
   * dequantisation: hand-packed rows with hand-worked values
-    (tests/golden/dequant_cases.txt) and an independent numpy unpacking;
+    (tests/golden/dequant_cases.txt, dequant_fp8_cases.txt) and an
+    independent numpy unpacking (torch's float8_e4m3fn decoding for FP8);
+  * E4M3 decoding: torch's float8_e4m3fn conversion on all 256 patterns;
   * router logits: numpy float64 matrix product, rounded by torch;
   * top-k: brute force, a full stable sort of every token's logits;
   * gates: scipy's softmax over all experts renormalised over the selected,
@@ -55,7 +57,12 @@ def np_codes(q: np.ndarray, N: int, K: int) -> np.ndarray:
 
 
 def np_dequant64(fmt: int, q, sm, N: int, K: int) -> np.ndarray:
-    """Independent float64 dequantisation using numpy's float16 decoder."""
+    """Independent float64 dequantisation using numpy's float16 decoder
+    (torch's float8_e4m3fn decoder for FP8 codes)."""
+    if fmt == oracle.FMT_FP8_B128:
+        v = torch.from_numpy(np.asarray(q, dtype=np.uint8).reshape(N, K).copy()).view(torch.float8_e4m3fn)
+        s = np.asarray(sm, dtype=np.float32).reshape(N // 128, K // 128).astype(np.float64)
+        return v.double().numpy() * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
     codes = np_codes(q, N, K).astype(np.float64)
     g = 64 if fmt == oracle.FMT_ASYM_G64 else 128
     sm = np.asarray(sm).view(np.uint16).view(np.float16).astype(np.float64)
@@ -86,6 +93,13 @@ def rand_layer(rng, E, H, I, fmt):
     """Random codes and f16 scales/mins of plausible magnitude (numpy arrays)."""
     g = 64 if fmt == oracle.FMT_ASYM_G64 else 128
     mats = {}
+    if fmt == oracle.FMT_FP8_B128:
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            q = rng.integers(0, 256, size=(E, N, K), dtype=np.uint8)
+            q[(q & 0x7F) == 0x7F] -= 1  # no NaN codes
+            mats[name + "_q"] = q
+            mats[name + "_sm"] = (rng.random((E, N // 128, K // 128)) * 1e-4 + 5e-5).astype(np.float32)
+        return mats
     for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
         mats[name + "_q"] = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
         s = (rng.random((E, N, K // g)) * 0.004 + 0.002).astype(np.float16)
@@ -136,6 +150,27 @@ def read_dequant_cases():
                 cur["sm"] = [int(v, 16) for v in rest]
             elif head == "expect":
                 cur["expect"] = [float(v) for v in rest]
+    return cases
+
+
+def read_dequant_fp8_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "dequant_fp8_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, *rest = line.split()
+            if head == "case":
+                kv = dict(r.split("=") for r in rest[1:])
+                cur = {"name": rest[0], "N": int(kv["N"]), "K": int(kv["K"]), "expect": []}
+                cases.append(cur)
+            elif head == "bytes":
+                cur["bytes"] = [int(v, 16) for v in rest]
+            elif head == "scale":
+                cur["scale"] = [float(v) for v in rest]
+            elif head == "expect":
+                cur["expect"].append([float(v) for v in rest])
     return cases
 
 
@@ -245,6 +280,29 @@ def pin_dequant_golden():
         assert np.array_equal(got.astype(np.float64), exp), c["name"]
 
 
+def pin_e4m3_decode_all():
+    """Every E4M3 pattern against torch's float8_e4m3fn decoding (NaN where it is NaN)."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_value(b) for b in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def pin_dequant_fp8_golden():
+    for c in read_dequant_fp8_cases():
+        N, K = c["N"], c["K"]
+        nb, kb = N // 128, K // 128
+        q = np.array(cyc(c["bytes"], N * K), dtype=np.uint8).reshape(N, K)
+        s = np.array(c["scale"], dtype=np.float32)
+        assert s.size == nb * kb == len(c["expect"]), c["name"]
+        got = oracle.dequant(oracle.FMT_FP8_B128, q, s, N, K).astype(np.float64)
+        for bi, e in enumerate(c["expect"]):
+            r, cc = divmod(bi, kb)
+            blk = got[128 * r:128 * (r + 1), 128 * cc:128 * (cc + 1)].ravel()
+            assert np.array_equal(blk, np.array(cyc(e, 128 * 128))), (c["name"], bi)
+
+
 def pin_dequant_random():
     """Random rows: float32 of the exact value, as computed independently by numpy."""
     rng = np.random.default_rng(11)
@@ -258,6 +316,14 @@ def pin_dequant_random():
         ref = np_dequant64(fmt, q, sm, N, K).astype(np.float32)
         got = oracle.dequant(fmt, q, sm, N, K)
         assert np.array_equal(got, ref)
+    # fp8: every code with random float32 block scales (four blocks)
+    N = K = 256
+    q = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] -= 1
+    sm = (rng.standard_normal((2, 2)) * 1e-3).astype(np.float32)
+    ref = np_dequant64(oracle.FMT_FP8_B128, q, sm, N, K).astype(np.float32)
+    got = oracle.dequant(oracle.FMT_FP8_B128, q, sm, N, K)
+    assert np.array_equal(got, ref)
 
 
 def pin_router():
@@ -348,7 +414,8 @@ def pin_group():
 def pin_one_expert_dense():
     """E = 1, k = 1: the layer is the dense SwiGLU MLP of the dequantised weights."""
     rng = np.random.default_rng(17)
-    for fmt, (H, I) in ((oracle.FMT_ASYM_G64, (128, 64)), (oracle.FMT_SYM_G128, (256, 128))):
+    for fmt, (H, I) in ((oracle.FMT_ASYM_G64, (128, 64)), (oracle.FMT_SYM_G128, (256, 128)),
+                        (oracle.FMT_FP8_B128, (256, 128))):
         T = 3
         mats = rand_layer(rng, 1, H, I, fmt)
         x = rand_bf16(rng, (T, H))
@@ -365,7 +432,8 @@ def pin_experts_bruteforce():
     """Several experts, top-k routing, gate-weighted sum: float64 numpy per token."""
     rng = np.random.default_rng(19)
     for fmt, (E, H, I, k, T) in ((oracle.FMT_ASYM_G64, (6, 128, 64, 3, 5)),
-                                 (oracle.FMT_SYM_G128, (5, 256, 128, 2, 4))):
+                                 (oracle.FMT_SYM_G128, (5, 256, 128, 2, 4)),
+                                 (oracle.FMT_FP8_B128, (3, 256, 128, 2, 3))):
         mats = rand_layer(rng, E, H, I, fmt)
         x = rand_bf16(rng, (T, H))
         idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
@@ -485,4 +553,5 @@ ALL_PINS = [pin_f16_decode_all, pin_bf16_decode_all, pin_bf16_round, pin_dequant
             pin_dequant_random, pin_router, pin_topk_bruteforce, pin_topk_adversarial,
             pin_gates, pin_group, pin_one_expert_dense, pin_experts_bruteforce,
             pin_gate_linearity, pin_layer_chain, pin_residual, pin_dequant_int8_golden,
-            pin_dequant_int8_random, pin_shared_dense, pin_shared_as_routed_expert]
+            pin_dequant_int8_random, pin_shared_dense, pin_shared_as_routed_expert, pin_e4m3_decode_all,
+            pin_dequant_fp8_golden]

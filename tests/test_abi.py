@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -209,6 +209,11 @@ def test_shared_validation():
     assert need >= 4 * 512 * 2
     assert call(_shared(), ws_bytes=need - 1) == _lib.ERR_WORKSPACE
     assert call(_shared(), ws=None) == _lib.ERR_WORKSPACE
+    ev = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    assert L.moe_q4_shared_timed(FAKE, 4, ctypes.byref(_shared()), FAKE, 0, FAKE, 1 << 30, None,
+                                 ev) == _lib.ERR_INVALID_ARG
+    assert L.moe_q4_shared_timed(FAKE, 4, ctypes.byref(_shared()), FAKE, 0, FAKE, 1 << 30, None,
+                                 None) == _lib.ERR_INVALID_ARG
     assert L.moe_q4_dequant_int8(ctypes.byref(_shared()), 3, FAKE, None) == _lib.ERR_INVALID_ARG
     assert L.moe_q4_dequant_int8(ctypes.byref(_shared()), 0, None, None) == _lib.ERR_INVALID_ARG
     assert L.moe_q4_dequant_int8(ctypes.byref(_shared(I=96)), 0, FAKE, None) == _lib.ERR_UNSUPPORTED

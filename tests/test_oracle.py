@@ -1,5 +1,6 @@
 """The CPU oracle against its pins (no GPU needed).  See oracle_pins.py."""
 import numpy as np
+import torch
 import pytest
 
 import oracle_pins as pins
@@ -59,3 +60,24 @@ def test_int8_encoder_round_trip(orc):
     d = orc.dequant_int8(qn, s.numpy(), 96, 384).astype(np.float64)
     step = np.repeat(np.abs(s.numpy().view(np.float16).astype(np.float64)), 128, axis=1)
     assert (np.abs(d - w.double().numpy()) <= 0.5 * step * (1 + 1e-3) + 1e-12).all()
+
+
+def test_fp8_encoder_round_trip(orc):
+    """The synthetic block-FP8 encoder: each 128 x 128 block's largest weight
+    becomes +-448 (its scale is max|w| / 448), and each weight is within half
+    an E4M3 step of its dequantised value (checked through the oracle)."""
+    import synth
+    w = synth.normal((256, 384), 0.02, 0, "pin/fp8", "cpu")
+    w[128:, 128:256] = 0.0  # an all-zero block
+    q, s = synth.quantize_fp8(w)
+    assert q.dtype == torch.uint8 and s.shape == (2, 3)
+    assert float(s[1, 1]) == 0.0
+    d = orc.dequant(synth.FMT_FP8_B128, q.numpy(), s.numpy(), 256, 384).astype(np.float64)
+    v = np.array([orc.e4m3_value(b) for b in range(256)])[q.numpy()]
+    blocks = np.abs(v).reshape(2, 128, 3, 128).max(axis=(1, 3))
+    assert (blocks[s.numpy() > 0] == 448.0).all()
+    ratio = w.double().numpy() / np.repeat(np.repeat(np.where(s.numpy() > 0, s.numpy(), 1.0), 128, 0), 128, 1)
+    # half a step: 2^(e-4) for normal values (e the binade), 2^-10 below 2^-6
+    step = np.where(np.abs(v) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v), 1e-30))) - 4), 2.0 ** -10)
+    assert (np.abs(ratio - v) <= step * (1 + 1e-6) + 1e-12).all()
+    assert np.allclose(d, v * np.repeat(np.repeat(s.numpy().astype(np.float64), 128, 0), 128, 1))

@@ -43,6 +43,10 @@ MUTANTS = [
     ("shared_silu_on_up", "h[n] = b * silu(a);", "h[n] = a * silu(b);"),
     ("shared_down_transposed", "acc += h[n] * wd[(size_t)d * I + n];", "acc += h[n] * wd[(size_t)n * H + d];"),
     ("shared_y_in_dropped", "double acc = y_in ? (double)y_in[(size_t)j * H + d] : 0.0;", "double acc = 0.0;"),
+    ("e4m3_bias_8", "ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    ("e4m3_subnormal_scale", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("e4m3_sign_dropped", "return sgn ? -v : v;", "return v;"),
+    ("fp8_block_row_ignored", "bs[(size_t)(n / 128) * (K / 128) + k / 128]", "bs[(size_t)(k / 128)]"),
     ("residual_truncates", "out[i] = oracle_bf16_round(s);", "out[i] = (uint16_t)(oracle_bf16_round(s) & 0xfffe);"),
 ]
 
