@@ -69,7 +69,8 @@ typedef struct ihipStream_t *moe_q4_stream;
 
 typedef enum {
     MOE_Q4_ASYM_G64 = 0,   /* w = scale * q + min, q in 0..15, group 64 along K  */
-    MOE_Q4_SYM_G128 = 1    /* w = scale * (q - 8), q in 0..15, group 128 along K */
+    MOE_Q4_SYM_G128 = 1,   /* w = scale * (q - 8), q in 0..15, group 128 along K */
+    MOE_Q4_FP8_B128 = 2    /* w = e4m3(q) * scale, one float scale per 128 x 128 block */
 } moe_q4_format;
 
 typedef enum {
@@ -98,6 +99,15 @@ typedef enum {
  *                    asym g64:  [E][N][K/64][2] = {scale, min}
  *                    sym g128:  [E][N][K/128]   = scale
  *                  (N, K) = (I, H) for gate and up, (H, I) for down.
+ * Block FP8 (MOE_Q4_FP8_B128; the released experts' format: drama-3-w4a16
+ * card, "At a glance", each matrix dequantised with its 128 x 128 block
+ * scales, "How it was made"):
+ *   *_q            uint8 [E][N][K], one OCP E4M3 code per weight
+ *   *_sm           point to float32 [E][N/128][K/128] block scales (cast to
+ *                  the field's type)
+ * Block FP8 needs H and I of at least 128; it runs on the GEMV kernels at
+ * every T (moe_q4_prefill returns MOE_Q4_ERR_UNSUPPORTED for it, and
+ * moe_q4_forward takes the GEMV kernels above 64 tokens as well).
  */
 typedef struct moe_q4_layer {
     int32_t num_experts;   /* E */
@@ -299,6 +309,13 @@ MOE_Q4_API int moe_q4_prefill_timed(const void *x, const int32_t *topk_idx, cons
  */
 MOE_Q4_API int moe_q4_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y,
                              int32_t accumulate, void *ws, size_t ws_bytes, moe_q4_stream stream);
+
+/* moe_q4_shared with the caller's MOE_Q4_STAGE_EVENTS HIP events recorded at
+ * the start and end of its gate/up launch (events[0..1]) and its down launch
+ * (events[2..3]) by the runtime (extended launch).  events must not be NULL. */
+MOE_Q4_API int moe_q4_shared_timed(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y,
+                                   int32_t accumulate, void *ws, size_t ws_bytes, moe_q4_stream stream,
+                                   void *const *events);
 
 /*
  * Test hook: dequantise projection `proj` (0 gate [I][H], 1 up [I][H],

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
 
 ASYM_G64 = 0
 SYM_G128 = 1
+FP8_B128 = 2
 WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP, WS_FORWARD, WS_SHARED = 0, 1, 2, 3, 4, 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 

@@ -28,6 +28,7 @@
 // x in the gate/up GEMV, f16 (OFF = 1024) against h rounded to f16 in the
 // down GEMV (|h| must stay below 65504).
 #include "decode_dev.h"
+#include "fp8_dev.h"
 #include "group_dev.h"
 #include "shared_dev.h"
 #include "route_dev.h"
@@ -137,6 +138,8 @@ __device__ __forceinline__ int route_in_block(const uint16_t *__restrict__ lg, i
     return nt_all;
 }
 
+constexpr int DEC_GU_STAGES = 2;  // register stages of the gate/up GEMV
+
 // gate/up GEMV + SwiGLU for one item (tile: one expert, up to DECODE_TT
 // tokens; rows ir of I) into h.  Lanes run along the input dimension: LPR =
 // H / 64 lanes per row, each lane 32 bytes = 64 codes (one 64-group), so a
@@ -200,7 +203,7 @@ __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int 
             if (u < nt) xs[u] = perm_x_chunk(xp[u]) + perm_x_chunk(xp[u] + 16);
         }
     };
-    Stage sa, sb;
+    Stage st[DEC_GU_STAGES];
     auto consume = [&](const Stage &st, int s) {
         const int nl = row_of(s);
         float sg, mg, su, mu;
@@ -232,26 +235,28 @@ __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int 
             }
         }
     };
-    // Two register stages, the next one in flight while the current one is
-    // reduced.  The first rows depend only on the tile, so they are issued
-    // before the tokens are known.  The loop issues every stage (rows past
-    // the item re-read its first row) and outputs go to LDS, so it holds only
-    // loads and the compiler's memory-counter waits stay exact.
+    // DEC_GU_STAGES register stages, the next ones in flight while the
+    // current one is reduced.  The first rows depend only on the tile, so
+    // they are issued before the tokens are known.  The loop issues every
+    // stage (rows past the item re-read its first row) and outputs go to LDS,
+    // so it holds only loads and the compiler's memory-counter waits stay
+    // exact.
     if (SHORT && steps == 1) {
         fetch_x();
-        issue(sa, 0);
+        issue(st[0], 0);
         prep_x();
-        consume(sa, 0);
+        consume(st[0], 0);
     } else {
         fetch_x();
-        issue(sa, 0);
-        issue(sb, 1);
+#pragma unroll
+        for (int u = 0; u < DEC_GU_STAGES; ++u) issue(st[u], u);
         prep_x();
-        for (int s = 0; s < steps; s += 2) {
-            consume(sa, s);
-            issue(sa, s + 2);
-            if (s + 1 < steps) consume(sb, s + 1);
-            issue(sb, s + 3);
+        for (int s = 0; s < steps; s += DEC_GU_STAGES) {
+#pragma unroll
+            for (int u = 0; u < DEC_GU_STAGES; ++u) {
+                if (u == 0 || s + u < steps) consume(st[u], s + u);
+                issue(st[u], s + u + DEC_GU_STAGES);
+            }
         }
     }
     __syncthreads();
@@ -422,7 +427,10 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const int32_t *__restrict__ ntiles, int max_nt, uint16_t *__restrict__ h, const uint16_t *__restrict__ lg,
     int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out, GroupOut gout, SharedPtrs S,
     uint16_t *__restrict__ hs) {
-    constexpr int BR = DEC_WAVES * (WAVE / LPR);
+    // lanes per gate/up row: H / 64 for int4 (64 codes a lane), H / 32 for
+    // fp8 (32 codes a lane)
+    constexpr int LPG = FMT == 2 ? 2 * LPR : LPR;
+    constexpr int BR = DEC_WAVES * (WAVE / LPG);
     __shared__ float s_out[DECODE_TT][DEC_RB_MAX];
     if constexpr (SHARED && LPR >= 2) {  // shared expert: H / 32 lanes per row
         constexpr int LPS = 2 * LPR, BRS = DEC_WAVES * (WAVE / LPS);
@@ -452,7 +460,8 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
         const Tile tile = sane_tile(tiles[j], L.E, P);
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, I);
         if (ir.steps <= 0) continue;
-        gateup_item<LPR, FMT, ROUTE>(x, H, I, k, L, tile, ir, h, s_out);
+        if constexpr (FMT == 2) fp8_gateup_item<LPG, ROUTE>(x, H, I, k, L, tile, ir, h, s_out);
+        else gateup_item<LPR, FMT, ROUTE>(x, H, I, k, L, tile, ir, h, s_out);
     }
 }
 
@@ -475,7 +484,8 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         const Tile tile = sane_tile(tiles[j], L.E, P);
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, H);
         if (ir.steps <= 0) continue;
-        down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
+        if constexpr (FMT == 2) fp8_down_item<LPR>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
+        else down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
     }
     if constexpr (SHARED && LPR >= 4) {
         const int ntt = (T + DECODE_TT - 1) / DECODE_TT;
@@ -759,15 +769,17 @@ static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64
                                      const SharedPtrs *S, uint16_t *hs) {
     if (S && !decode_fuses_shared(L, S)) return hipErrorInvalidValue;
     const SharedPtrs none{};
-    if (S)
-        return L.fmt == 0
-                   ? launch_experts_fmt<0, ROUTE, true>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, *S, hs)
-                   : launch_experts_fmt<1, ROUTE, true>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, *S, hs);
-    return L.fmt == 0
-               ? launch_experts_fmt<0, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, none,
-                                                     nullptr)
-               : launch_experts_fmt<1, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, none,
-                                                     nullptr);
+#define FMT_CASE(F)                                                                                            \
+    case F:                                                                                                    \
+        return S ? launch_experts_fmt<F, ROUTE, true>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, \
+                                                      *S, hs)                                                  \
+                 : launch_experts_fmt<F, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out,      \
+                                                       gate_out, none, nullptr);
+    switch (L.fmt) {
+        FMT_CASE(0) FMT_CASE(1) FMT_CASE(2)
+        default: return hipErrorInvalidValue;
+    }
+#undef FMT_CASE
 }
 
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,

@@ -1,5 +1,5 @@
-// Small kernels: the dequantisation test hook, the residual step of a chain
-// of layers, and a float fill.
+// Small kernels: the dequantisation test hooks (int4 and fp8), the residual
+// step of a chain of layers, and a float fill.
 #include "moe_internal.h"
 
 namespace moeq4 {
@@ -44,6 +44,26 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     }
 }
 
+// out[n][k] of one fp8 projection: the code converted as the expert kernels
+// convert it (an exact bf16), times the float32 block scale, one rounding.
+__global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint8_t *__restrict__ q, const float *__restrict__ sc,
+                                                          int N, int K, float *__restrict__ out) {
+    const int64_t words = (int64_t)N * K / 4;
+    const int64_t wi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (wi >= words) return;
+    const int64_t n = wi / (K / 4);
+    const int k0 = (int)(wi % (K / 4)) * 4;
+    const uint32_t w = reinterpret_cast<const uint32_t *>(q)[wi];
+    const float s = sc[(size_t)(n / 128) * (K / 128) + k0 / 128];
+    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    float *dst = out + (size_t)n * K + k0;
+    dst[0] = bf16_to_f32(lo & 0xffffu) * s;
+    dst[1] = bf16_to_f32(lo >> 16) * s;
+    dst[2] = bf16_to_f32(hi & 0xffffu) * s;
+    dst[3] = bf16_to_f32(hi >> 16) * s;
+}
+
 __global__ __launch_bounds__(256) void residual_kernel(const uint16_t *__restrict__ x, const float *__restrict__ y,
                                                        int64_t n, uint16_t *__restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -55,6 +75,14 @@ hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, 
     const int N = proj == 2 ? L.H : L.I, K = proj == 2 ? L.I : L.H;
     const uint8_t *q = proj == 0 ? L.gq : (proj == 1 ? L.uq : L.dq);
     const uint16_t *sm = proj == 0 ? L.gsm : (proj == 1 ? L.usm : L.dsm);
+    if (L.fmt == 2) {
+        q += (size_t)expert * N * K;
+        const float *sc = reinterpret_cast<const float *>(sm) + (size_t)expert * (N / 128) * (K / 128);
+        const int64_t words = (int64_t)N * K / 4;
+        hipLaunchKernelGGL(dequant_fp8_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, q, sc, N, K,
+                           out);
+        return hipGetLastError();
+    }
     q += (size_t)expert * N * (K / 2);
     sm += (size_t)expert * N * (K / G) * (L.fmt == 0 ? 2 : 1);
     const int64_t words = (int64_t)N * K / 8;

@@ -95,7 +95,7 @@ def test_group_validation():
 
 def test_layer_validation():
     assert _decode(_layer(null="down_sm")) == _lib.ERR_INVALID_ARG
-    assert _decode(_layer(fmt=2)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(fmt=3)) == _lib.ERR_UNSUPPORTED       # unknown format
     assert _decode(_layer(H=3072)) == _lib.ERR_UNSUPPORTED       # not a power of two
     assert _decode(_layer(H=4096)) == _lib.ERR_UNSUPPORTED       # above 2048
     assert _decode(_layer(fmt=1, I=64)) == _lib.ERR_UNSUPPORTED  # not a multiple of 128
@@ -236,3 +236,14 @@ def test_forward_ex_shared_validation():
     sh = m.workspace_size(m.WS_SHARED, 4, 1, 1, 2048, 1024)
     assert call(_shared(I=1024), ws_bytes=fwd + sh - 1) == _lib.ERR_WORKSPACE
     assert call(None, ws_bytes=fwd - 1) == _lib.ERR_WORKSPACE
+
+
+def test_fp8_layer_validation():
+    """Block-FP8 experts: accepted by the GEMV entry points, refused by the
+    grouped-GEMM one, and needing H, I >= 128."""
+    assert _decode(_layer(fmt=2), prefill=True) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(fmt=2, H=64)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(fmt=2, I=64)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(fmt=2), T=0) == _lib.OK
+    assert _decode(_layer(fmt=3)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(fmt=2), ws_bytes=16) == _lib.ERR_WORKSPACE
