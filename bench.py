@@ -18,6 +18,10 @@ Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
   decode_shared, frame_shared
                 decode / frame with each layer's shared expert (int8
                 symmetric g128, inter 512) in the same forward call.
+  decode_fp8, frame_fp8
+                decode / frame with block-FP8 experts (E4M3, float32 scale per
+                128 x 128 block; the released experts' format) of the same
+                Gaussian weights.
   shared        the shared expert alone (moe_q4_shared) for the frame's 16
                 tokens; steps rotate over 200 address-distinct copies (3 MB
                 each) so its codes are read from HBM.
@@ -44,7 +48,7 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s, prefill MFMA TFLOPs (% of peak)"
 
 WORKLOADS = {
     "tiny": 1, "decode": 2, "prefill": 3, "frame": 4, "long_prefill": 5,
-    "decode_shared": 2, "frame_shared": 4, "shared": 4,
+    "decode_shared": 2, "frame_shared": 4, "shared": 4, "decode_fp8": 2, "frame_fp8": 4,
 }
 SHARED_INTER = 512   # the shared expert's inner size (that of a routed expert)
 SHARED_COPIES = 200  # address-distinct shared experts of the "shared" workload
@@ -168,17 +172,21 @@ def main():
     dev = torch.device("cuda")
     cfg = WORKLOADS[args.workload]
     defaults = {"tiny": (200, 20), "decode": (400, 40), "prefill": (50, 5), "frame": (10, 2),
-                "long_prefill": (20, 3), "decode_shared": (400, 40), "frame_shared": (10, 2), "shared": (400, 40)}
+                "long_prefill": (20, 3), "decode_shared": (400, 40), "frame_shared": (10, 2), "shared": (400, 40),
+                "decode_fp8": (400, 40), "frame_fp8": (10, 2)}
     K = args.steps if args.steps is not None else defaults[args.workload][0]
     W = args.warmup if args.warmup is not None else defaults[args.workload][1]
 
     t0 = time.time()
     only_shared = args.workload == "shared"
     with_shared = args.workload in ("decode_shared", "frame_shared", "shared")
-    case = synth.make_case(cfg, device="cuda", layers=1 if only_shared else None)
+    fp8 = args.workload.endswith("_fp8")
+    case = synth.make_case(cfg, device="cuda", layers=1 if only_shared else None,
+                           fmt=synth.FMT_FP8_B128 if fp8 else None)
     torch.cuda.synchronize()
     T, H, E, k, I = case.T, case.H, case.E, case.k, case.I
-    base_wl = {"decode_shared": "decode", "frame_shared": "frame"}.get(args.workload, args.workload)
+    base_wl = {"decode_shared": "decode", "frame_shared": "frame", "decode_fp8": "decode",
+               "frame_fp8": "frame"}.get(args.workload, args.workload)
     decode_path = base_wl in ("tiny", "decode", "frame", "shared")
     mode = "decode" if decode_path else "prefill"
 
@@ -375,6 +383,8 @@ def main():
     sx_note = f" + shared expert int8 sym g128 I={SHARED_INTER} per layer"
     names["decode_shared"] = names["decode"] + sx_note
     names["frame_shared"] = names["frame"] + sx_note
+    names["decode_fp8"] = names["decode"].replace("int4 asym g64 (clip search)", "block-FP8 E4M3, 128x128 scales")
+    names["frame_fp8"] = names["frame"].replace("int4 asym g64 (RTN)", "block-FP8 E4M3, 128x128 scales")
     names["shared"] = (f"shared expert alone: 16 tokens, H=2048, I={SHARED_INTER}, int8 sym g128; "
                        f"{SHARED_COPIES} address-distinct copies rotated")
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -383,8 +393,9 @@ def main():
            "config": {"workload": names[args.workload], "tokens": T, "hidden": H, "experts": 0 if only_shared else E,
                       "top_k": 0 if only_shared else k, "inter": SHARED_INTER if only_shared else I,
                       "layers_per_step": nl_per_step, "path": mode,
-                      "format": "int8_sym_g128" if only_shared else (
-                          "asym_g64" if case.fmt == synth.FMT_ASYM_G64 else "sym_g128"),
+                      "format": "int8_sym_g128" if only_shared else {
+                          synth.FMT_ASYM_G64: "asym_g64", synth.FMT_SYM_G128: "sym_g128",
+                          synth.FMT_FP8_B128: "fp8_e4m3_b128"}[case.fmt],
                       "shared_expert": with_shared},
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)

@@ -386,13 +386,16 @@ FRAME_LAYERS = 40
 
 
 def make_case(cfg: int, device="cpu", seed: int = 0, layers: int | None = None,
-              T: int | None = None) -> Case:
+              T: int | None = None, fmt: int | None = None) -> Case:
     """Inputs of one of the five workload configurations (seed 0 by default).
 
     ``layers`` overrides the 40-layer depth of the frame configuration and
-    ``T`` the token count (both for smaller runs of the same recipe).
+    ``T`` the token count (both for smaller runs of the same recipe); ``fmt``
+    encodes the same Gaussian weights in another expert format (e.g. block
+    FP8, the released experts' format).
     """
-    name, T0, H, E, k, I, fmt, clip, router = CONFIGS[cfg]
+    name, T0, H, E, k, I, fmt0, clip, router = CONFIGS[cfg]
+    fmt = fmt0 if fmt is None else fmt
     T = T0 if T is None else T
     nl = (FRAME_LAYERS if layers is None else layers) if cfg == 4 else 1
     x = bf16_bits(normal((T, H), 1.0, seed, f"{name}/x", device))
