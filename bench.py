@@ -18,10 +18,10 @@ Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
   decode_shared, frame_shared
                 decode / frame with each layer's shared expert (int8
                 symmetric g128, inter 512) in the same forward call.
-  decode_fp8, frame_fp8
-                decode / frame with block-FP8 experts (E4M3, float32 scale per
-                128 x 128 block; the released experts' format) of the same
-                Gaussian weights.
+  decode_fp8, frame_fp8, prefill_fp8, long_prefill_fp8
+                decode / frame / prefill / long prefill with block-FP8 experts
+                (E4M3, float32 scale per 128 x 128 block; the released
+                experts' format) of the same Gaussian weights.
   shared        the shared expert alone (moe_q4_shared) for the frame's 16
                 tokens; steps rotate over 200 address-distinct copies (3 MB
                 each) so its codes are read from HBM.
@@ -49,6 +49,7 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s, prefill MFMA TFLOPs (% of peak)"
 WORKLOADS = {
     "tiny": 1, "decode": 2, "prefill": 3, "frame": 4, "long_prefill": 5,
     "decode_shared": 2, "frame_shared": 4, "shared": 4, "decode_fp8": 2, "frame_fp8": 4,
+    "prefill_fp8": 3, "long_prefill_fp8": 5,
 }
 SHARED_INTER = 512   # the shared expert's inner size (that of a routed expert)
 SHARED_COPIES = 200  # address-distinct shared experts of the "shared" workload
@@ -173,7 +174,7 @@ def main():
     cfg = WORKLOADS[args.workload]
     defaults = {"tiny": (200, 20), "decode": (400, 40), "prefill": (50, 5), "frame": (10, 2),
                 "long_prefill": (20, 3), "decode_shared": (400, 40), "frame_shared": (10, 2), "shared": (400, 40),
-                "decode_fp8": (400, 40), "frame_fp8": (10, 2)}
+                "decode_fp8": (400, 40), "frame_fp8": (10, 2), "prefill_fp8": (50, 5), "long_prefill_fp8": (20, 3)}
     K = args.steps if args.steps is not None else defaults[args.workload][0]
     W = args.warmup if args.warmup is not None else defaults[args.workload][1]
 
@@ -186,7 +187,8 @@ def main():
     torch.cuda.synchronize()
     T, H, E, k, I = case.T, case.H, case.E, case.k, case.I
     base_wl = {"decode_shared": "decode", "frame_shared": "frame", "decode_fp8": "decode",
-               "frame_fp8": "frame"}.get(args.workload, args.workload)
+               "frame_fp8": "frame", "prefill_fp8": "prefill",
+               "long_prefill_fp8": "long_prefill"}.get(args.workload, args.workload)
     decode_path = base_wl in ("tiny", "decode", "frame", "shared")
     mode = "decode" if decode_path else "prefill"
 
@@ -345,11 +347,12 @@ def main():
                 "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_bytes": int(alg_bytes),
                 "active_experts": int(act)}
     else:
-        dom = "grouped_gemm_kernel<FMT,1> (gate/up GEMM + SwiGLU)"
+        dom = ("grouped_gemm_fp8_kernel<1> (gate/up bf16 GEMM + SwiGLU)" if fp8
+               else "grouped_gemm_kernel<FMT,1> (gate/up GEMM + SwiGLU)")
         flops = 2.0 * P * H * (2 * I)
         achieved = flops / (stage_avg[0] * 1e-3) / 1e12
         wbytes = act * 2 * proj_bytes
-        if args.workload == "prefill":
+        if base_wl == "prefill":
             # weight-bandwidth-bound case: report against HBM
             gbs = (wbytes + T * H * 2 + P * I * 2) / (stage_avg[0] * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -385,11 +388,13 @@ def main():
     names["frame_shared"] = names["frame"] + sx_note
     names["decode_fp8"] = names["decode"].replace("int4 asym g64 (clip search)", "block-FP8 E4M3, 128x128 scales")
     names["frame_fp8"] = names["frame"].replace("int4 asym g64 (RTN)", "block-FP8 E4M3, 128x128 scales")
+    names["prefill_fp8"] = names["prefill"].replace("int4 asym g64", "block-FP8 E4M3, 128x128 scales")
+    names["long_prefill_fp8"] = names["long_prefill"].replace("int4 sym g128", "block-FP8 E4M3, 128x128 scales")
     names["shared"] = (f"shared expert alone: 16 tokens, H=2048, I={SHARED_INTER}, int8 sym g128; "
                        f"{SHARED_COPIES} address-distinct copies rotated")
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
            "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16" if decode_path else "f16", "data": "synthetic",
+           "dtype": "bf16" if decode_path or fp8 else "f16", "data": "synthetic",
            "config": {"workload": names[args.workload], "tokens": T, "hidden": H, "experts": 0 if only_shared else E,
                       "top_k": 0 if only_shared else k, "inter": SHARED_INTER if only_shared else I,
                       "layers_per_step": nl_per_step, "path": mode,

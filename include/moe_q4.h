@@ -105,9 +105,11 @@ typedef enum {
  *   *_q            uint8 [E][N][K], one OCP E4M3 code per weight
  *   *_sm           point to float32 [E][N/128][K/128] block scales (cast to
  *                  the field's type)
- * Block FP8 needs H and I of at least 128; it runs on the GEMV kernels at
- * every T (moe_q4_prefill returns MOE_Q4_ERR_UNSUPPORTED for it, and
- * moe_q4_forward takes the GEMV kernels above 64 tokens as well).
+ * Block FP8 needs H and I of at least 128.  Its codes are converted to
+ * 16-bit floats exactly; the decode GEMVs use exact products with fp32 sums
+ * (block scale on each 32-code partial sum), the prefill GEMMs run bf16 (x
+ * as given) and f16 (h) matrix cores with the block scales applied by
+ * rescaling the fp32 accumulators at each 128-input block.
  */
 typedef struct moe_q4_layer {
     int32_t num_experts;   /* E */

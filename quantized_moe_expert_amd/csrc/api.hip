@@ -55,7 +55,6 @@ int check_layer(const moe_q4_layer *w, bool prefill) {
     if (!pow2_between(w->hidden, 64, 2048) || !pow2_between(w->inter, 64, 2048)) return MOE_Q4_ERR_UNSUPPORTED;
     if (w->hidden % G || w->inter % G) return MOE_Q4_ERR_UNSUPPORTED;
     if (prefill && (w->inter % 128 || w->hidden % 256)) return MOE_Q4_ERR_UNSUPPORTED;
-    if (prefill && w->format == MOE_Q4_FP8_B128) return MOE_Q4_ERR_UNSUPPORTED;  // GEMV path only
     return MOE_Q4_OK;
 }
 
@@ -169,14 +168,8 @@ size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t
         case MOE_Q4_WS_FORWARD:
             c.take<char>(CONTROL_BYTES);
             c.take<unsigned int>(T * (int64_t)E);  // logit hand-off of the one-launch routing
-            if (forward_uses_decode(T, k)) {
-                carve_decode(c, T, E, k, H, I);
-            } else {  // the prefill regions, or the decode regions for fp8 experts
-                Carver a{nullptr}, b{nullptr};
-                carve_prefill(a, T, E, k, H, I);
-                carve_decode(b, T, E, k, H, I);
-                c.used += a.used > b.used ? a.used : b.used;
-            }
+            if (forward_uses_decode(T, k)) carve_decode(c, T, E, k, H, I);
+            else carve_prefill(c, T, E, k, H, I);
             break;
         case MOE_Q4_WS_SHARED: c.take<uint16_t>(T * (int64_t)I); break;
         default: return 0;
@@ -317,12 +310,10 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     if (T == 0) return MOE_Q4_OK;
     const int E = w->num_experts, H = w->hidden, I = w->inter;
     const bool dec = forward_uses_decode(T, k);
-    // block-FP8 experts take the GEMV kernels at every T
-    const bool gemv_many = !dec && w->format == MOE_Q4_FP8_B128;
     hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-    if (!dec && !gemv_many && (check_layer(w, true) || !prefill_fits(T, k, H, I))) return MOE_Q4_ERR_UNSUPPORTED;
+    if (!dec && (check_layer(w, true) || !prefill_fits(T, k, H, I))) return MOE_Q4_ERR_UNSUPPORTED;
     const size_t need_fwd = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
     const size_t need = need_fwd + (sx ? moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, sx->inter) : 0);
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
@@ -390,13 +381,6 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     }
     st = hip_status(launch_topk(lg, T, E, k, topk_idx, topk_gate, s));
     if (st) return st;
-    if (gemv_many) {
-        DecodeWs d = carve_decode(c, T, E, k, H, I);
-        st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, nullptr, 0, e2, e3));
-        if (!st) st = hip_status(launch_fill_zero(y, T * (int64_t)H, s));
-        if (!st) st = hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1, Sf, hs));
-        return st ? st : shared_after(xin);
-    }
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;

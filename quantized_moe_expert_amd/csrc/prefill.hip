@@ -450,6 +450,304 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+// ------------------------------------------------------- block-FP8 GEMMs
+//
+// The same grouped GEMMs for block-FP8 experts (E4M3 codes, one float32
+// scale per 128 weight rows x 128 inputs; the released experts' format,
+// drama-3-w4a16 card "At a glance", each matrix dequantised with its block
+// scales, "How it was made").  Codes are converted to 16-bit floats exactly
+// (two per gfx950 conversion instruction; every E4M3 value is a bf16 and an
+// f16), so both operands of the matrix cores are exact:
+//   GEMM1: A = the token's bf16 x row itself (no f16 pass), B = codes as
+//          bf16, bf16 MFMA;
+//   GEMM2: A = h (f16), B = codes as f16, f16 MFMA.
+// Block scales.  A wave's 32 output columns of an N-subtile lie in one
+// 128-row block, so its scale is uniform over the subtile for each 128-input
+// block of K.  The accumulator carries sum_b s_b P_b / sigma, sigma the last
+// nonzero block scale met: at each K-block with scale s != 0 it is multiplied
+// by sigma / s (rounded once) before the block's products, and by sigma at
+// the end.  An all-zero block (scale 0, codes 0) adds nothing.
+// Tiles, work order and the LDS ring are as above, with 64 bytes of codes
+// per weight row and K-step, two ring stages (two workgroups per CU).
+
+constexpr int NST8 = 2;
+constexpr int B8_BYTES = BROWS * KS;             // 16 KB: 256 rows x 64 codes
+constexpr int STAGE8_BYTES = A_BYTES + B8_BYTES;
+constexpr int B8_LOADS = B8_BYTES / 16 / PF_BLOCK;  // 4 sixteen-byte loads per thread and stage
+constexpr int ZP8 = BROWS + 8;
+constexpr int RING8_BYTES = NST8 * STAGE8_BYTES > BM * ZP8 * 2 ? NST8 * STAGE8_BYTES : BM * ZP8 * 2;
+
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+
+struct Gemm8Ctx {
+    const uint8_t *a_base;
+    uint32_t a_off[4];
+    const uint8_t *b_base[B8_LOADS];
+    uint32_t b_off[B8_LOADS];
+    const float *sc[2];  // block scales of this wave's two N-subtiles, one per 128 inputs
+    uint8_t *ring;
+    int brow[2];
+    int nk;
+};
+
+template <int MS>
+__device__ __forceinline__ void issue_stage8(const Gemm8Ctx &c, int ks, int slot, int wave) {
+    uint8_t *sa = c.ring + slot * STAGE8_BYTES;
+    uint8_t *sb = sa + A_BYTES;
+    const uint8_t *ab = c.a_base + (size_t)ks * (KS * 2);
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+        __builtin_amdgcn_global_load_lds((const void *)(ab + c.a_off[i]),
+                                         (__attribute__((address_space(3))) void *)(sa + (i * 4 + wave) * 1024),
+                                         16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B8_LOADS; ++i)
+        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * KS) + c.b_off[i]),
+                                         (__attribute__((address_space(3))) void *)(sb + (i * 4 + wave) * 1024),
+                                         16, 0, 0);
+}
+
+// Four codes of a dword as four exact 16-bit floats (bf16 for GEMM1, f16 for
+// GEMM2), in order.
+template <int STAGE>
+__device__ __forceinline__ uint2 e4m3x4(uint32_t w) {
+    if (STAGE == 1)
+        return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
+}
+
+template <int STAGE, int MS>
+__device__ __forceinline__ void gemm8_main(const Gemm8Ctx &c, f32x16_t (&acc)[4][2], int wave, int lane) {
+    constexpr int LPS = MS + B8_LOADS;  // loads per thread and stage
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int NK = c.nk;
+#pragma unroll
+    for (int u = 0; u < NST8 - 1; ++u)
+        if (u < NK) issue_stage8<MS>(c, u, u, wave);
+    float sig[2] = {1.f, 1.f};
+    float snext[2] = {c.sc[0][0], c.sc[1][0]};
+    for (int kk = 0; kk < NK; kk += NST8) {
+#pragma unroll
+        for (int u = 0; u < NST8; ++u) {
+            const int ks = kk + u;
+            if (ks < NK) {
+                // stage ks has landed once only the stages issued after it are in flight
+                if (NST8 > 2 && ks + 1 < NK) MOEQ4_WAIT_VM_LDS(LPS);
+                else MOEQ4_WAIT_VM_LDS(0);
+                lds_barrier();
+                if (ks + NST8 - 1 < NK) issue_stage8<MS>(c, ks + NST8 - 1, (u + NST8 - 1) % NST8, wave);
+                if ((ks & 1) == 0) {  // a new 128-input block
+                    const int kb = ks >> 1;
+#pragma unroll
+                    for (int ns = 0; ns < 2; ++ns) {
+                        const float sb = snext[ns];
+                        if (sb != 0.f) {
+                            if (kb > 0) {
+                                const float r = sig[ns] / sb;
+#pragma unroll
+                                for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+                                    for (int q = 0; q < 16; ++q) acc[mi][ns][q] *= r;
+                            }
+                            sig[ns] = sb;
+                        }
+                        if (2 * (kb + 1) < NK) snext[ns] = c.sc[ns][kb + 1];
+                    }
+                }
+                const uint8_t *sa = c.ring + u * STAGE8_BYTES;
+                const uint8_t *sbp = sa + A_BYTES;
+                // B: the lane's 32 codes (k in [32 hf, 32 hf + 32)) of each of its two weight rows
+                uint4 bw[2][2];
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) {
+                    const int rb = c.brow[ns];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        bw[ns][t] = *reinterpret_cast<const uint4 *>(sbp + rb * 64 + 16 * ((2 * hf + t) ^ ((rb >> 2) & 3)));
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {  // matrix-core K-steps of 16: elements [32 hf + 8 s, +8) per lane
+                    u32x4_t bv[2];
+#pragma unroll
+                    for (int ns = 0; ns < 2; ++ns) {
+                        const uint4 v = bw[ns][s >> 1];
+                        const uint32_t d0 = (s & 1) ? v.z : v.x, d1 = (s & 1) ? v.w : v.y;
+                        const uint2 p0 = e4m3x4<STAGE>(d0), p1 = e4m3x4<STAGE>(d1);
+                        bv[ns] = u32x4_t{p0.x, p0.y, p1.x, p1.y};
+                    }
+                    const int ch = 4 * hf + s;
+#pragma unroll
+                    for (int mi = 0; mi < MS; ++mi) {
+                        const int r = 32 * mi + l32;
+                        const uint4 av = *reinterpret_cast<const uint4 *>(sa + r * 128 + 16 * (ch ^ ((r >> 1) & 7)));
+                        const u32x4_t a4 = u32x4_t{av.x, av.y, av.z, av.w};
+#pragma unroll
+                        for (int ns = 0; ns < 2; ++ns) {
+                            if (STAGE == 1)
+                                acc[mi][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    __builtin_bit_cast(bf16x8v_t, a4), __builtin_bit_cast(bf16x8v_t, bv[ns]),
+                                    acc[mi][ns], 0, 0, 0);
+                            else
+                                acc[mi][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    __builtin_bit_cast(f16x8_t, a4), __builtin_bit_cast(f16x8_t, bv[ns]),
+                                    acc[mi][ns], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[mi][ns][q] *= sig[ns];
+}
+
+// STAGE 1: A = x rows (bf16) gathered through perm, B = gate | up codes,
+//          epilogue SwiGLU -> h (f16, natural order).
+// STAGE 2: A = h rows, B = down codes, epilogue gate-weighted rows of z (f16).
+template <int STAGE>
+__global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_gemm_fp8_kernel(
+    const uint16_t *__restrict__ act, int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles,
+    const int32_t *__restrict__ ntiles, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
+    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z) {
+    const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
+    const int nwork = *ntiles * ncb;
+    const int per = (nwork + 7) / 8;
+    const int bx = blockIdx.x;
+    if (bx / 8 >= per) return;
+    const int w = (bx % 8) * per + bx / 8;
+    if (w >= nwork) return;
+    const int j = w / ncb, cb = w % ncb;
+    const Tile tile = tiles[j];
+    const int e = tile.expert, rows = tile.rows, row0 = tile.row0;
+    const int K = STAGE == 1 ? H : I;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
+
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring[RING8_BYTES];
+    __shared__ int s_tok[BM];
+    __shared__ float s_gt[BM];  // STAGE 2: the row's gate
+    if (tid < BM) {
+        int t = 0;
+        float v = 0.f;
+        if (tid < rows) {
+            const int p = perm[row0 + tid];
+            t = p / k;
+            v = STAGE == 2 ? topk_gate[p] : 1.f;
+        }
+        s_tok[tid] = t;
+        s_gt[tid] = v;
+    }
+    __syncthreads();
+
+    Gemm8Ctx c;
+    c.ring = s_ring;
+    c.nk = K / KS;
+    c.a_base = reinterpret_cast<const uint8_t *>(act);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + 8 * wave + (lane >> 3);
+        const int ch = (lane & 7) ^ ((r >> 1) & 7);
+        const int rr = r < rows ? r : 0;  // padding rows read row 0; their outputs are dropped
+        const uint32_t arow = STAGE == 1 ? (uint32_t)s_tok[rr] * (uint32_t)H : (uint32_t)(row0 + rr) * (uint32_t)I;
+        c.a_off[i] = (arow + 8u * ch) * 2u;
+    }
+    // B slot S: weight row rb = S / 4 (rows 0-127 gate, 128-255 up in GEMM1),
+    // stored chunk S % 4 holding logical chunk (S % 4) ^ ((rb >> 2) & 3).
+#pragma unroll
+    for (int i = 0; i < B8_LOADS; ++i) {
+        const int S = (i * 4 + wave) * 64 + lane;
+        const int rb = S / 4, ch = (S % 4) ^ ((rb >> 2) & 3);
+        uint32_t wrow;
+        if (STAGE == 1) {
+            c.b_base[i] = i < 2 ? L.gq : L.uq;  // slots of loads 0-1 are rows 0-127, of loads 2-3 rows 128-255
+            wrow = (uint32_t)e * I + col_base + (rb & 127);
+        } else {
+            c.b_base[i] = L.dq;
+            wrow = (uint32_t)e * H + col_base + rb;
+        }
+        c.b_off[i] = wrow * (uint32_t)K + 16u * ch;
+    }
+    const int nkb = K / 128;
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+        c.brow[ns] = STAGE == 1 ? ns * 128 + wave * 32 + l32 : wave * 64 + ns * 32 + l32;
+        // the subtile's 128-row block (GEMM1: ns 0 the gate rows, ns 1 the up rows)
+        const int nrow = STAGE == 1 ? col_base : col_base + wave * 64 + ns * 32;
+        const float *sbase = reinterpret_cast<const float *>(STAGE == 1 ? (ns == 0 ? L.gsm : L.usm) : L.dsm);
+        const int N = STAGE == 1 ? I : H;
+        c.sc[ns] = sbase + ((size_t)e * (N / 128) + nrow / 128) * nkb;
+    }
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ns][r] = 0.f;
+    const int msub = (rows + 31) / 32;
+    switch (msub) {
+        case 1: gemm8_main<STAGE, 1>(c, acc, wave, lane); break;
+        case 2: gemm8_main<STAGE, 2>(c, acc, wave, lane); break;
+        case 3: gemm8_main<STAGE, 3>(c, acc, wave, lane); break;
+        default: gemm8_main<STAGE, 4>(c, acc, wave, lane); break;
+    }
+    __syncthreads();  // ring no longer read: the epilogue may reuse it
+
+    if (STAGE == 1) {
+        uint16_t *s_h = reinterpret_cast<uint16_t *>(s_ring);
+        constexpr int HP = 128 + 8;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi < msub) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+                    const _Float16 hv = (_Float16)(silu(acc[mi][0][r]) * acc[mi][1][r]);
+                    s_h[row * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
+                }
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < BM * 16; i += PF_BLOCK) {
+            const int row = i / 16, cc = i % 16;
+            if (row < rows)
+                *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) =
+                    *reinterpret_cast<const uint4 *>(&s_h[row * HP + cc * 8]);
+        }
+    } else {
+        uint16_t *s_z = reinterpret_cast<uint16_t *>(s_ring);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi < msub) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+                    const float gt = s_gt[row];
+                    s_z[row * ZP8 + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
+                    s_z[row * ZP8 + wave * 64 + 32 + l32] =
+                        __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
+                }
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < BM * (BROWS / 8); i += PF_BLOCK) {
+            const int row = i / (BROWS / 8), cc = i % (BROWS / 8);
+            if (row < rows)
+                *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
+                    *reinterpret_cast<const uint4 *>(&s_z[row * ZP8 + cc * 8]);
+        }
+    }
+}
+
 // y[t] = sum over the token's k routed rows of z (fp32).  One workgroup of
 // 256 threads per token, 8 columns per thread and pass.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ z, const int32_t *__restrict__ inv,
@@ -504,11 +802,32 @@ hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
     return launch_fill_zero(reinterpret_cast<float *>(p), n, s);  // all-zero bits either way
 }
 
+static hipError_t launch_prefill_fp8(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
+                                     const GroupOut &g, uint16_t *h, uint16_t *z, float *y, hipStream_t s,
+                                     hipEvent_t const *ev) {
+    const int H = L.H, I = L.I;
+    const int64_t tiles = max_tiles(T * k, L.E, BM);
+    const unsigned nb1 = (unsigned)(((I / 128) * tiles + 7) / 8 * 8);
+    const unsigned nb2 = (unsigned)(((H / BROWS) * tiles + 7) / 8 * 8);
+    launch_k(grouped_gemm_fp8_kernel<1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, x,
+             H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z);
+    launch_k(grouped_gemm_fp8_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
+             (const uint16_t *)h, H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles,
+             (const int32_t *)g.perm, gate, h, z);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
+                       (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
                                   float *y, hipStream_t s, hipEvent_t const *ev) {
-    return L.fmt == 0 ? launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev)
-                      : launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
+    switch (L.fmt) {
+        case 0: return launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
+        case 1: return launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
+        case 2: return launch_prefill_fp8(x, gate, T, k, L, g, h, z, y, s, ev);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moeq4

@@ -239,9 +239,9 @@ def test_forward_ex_shared_validation():
 
 
 def test_fp8_layer_validation():
-    """Block-FP8 experts: accepted by the GEMV entry points, refused by the
-    grouped-GEMM one, and needing H, I >= 128."""
-    assert _decode(_layer(fmt=2), prefill=True) == _lib.ERR_UNSUPPORTED
+    """Block-FP8 experts: H, I >= 128 (and the grouped GEMMs' H % 256)."""
+    assert _decode(_layer(fmt=2, H=128, I=128), prefill=True) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(fmt=2), prefill=True, ws_bytes=16) == _lib.ERR_WORKSPACE
     assert _decode(_layer(fmt=2, H=64)) == _lib.ERR_UNSUPPORTED
     assert _decode(_layer(fmt=2, I=64)) == _lib.ERR_UNSUPPORTED
     assert _decode(_layer(fmt=2), T=0) == _lib.OK

@@ -5,9 +5,10 @@ MI355X).
 Bars: dequantised weights and expert indices bit-exact; layer outputs within
 relative L2 2e-3 and max abs 1e-2 of the fp64 oracle.  Inputs: the layer
 recipe (H = 2048, 256 experts, top-8, I = 512) with N(0, 0.02) weights
-encoded per 128 x 128 block (synth.quantize_fp8), at 1 and 16 tokens, and
-random codes (subnormals included) at small and ragged shapes; large token
-counts run the GEMV kernels (sampled tokens).
+encoded per 128 x 128 block (synth.quantize_fp8), at 1 and 16 tokens
+(decode GEMVs) and at 512 (Zipf popularity) and 4096 tokens (grouped GEMMs,
+sampled tokens), and random codes (subnormals included) at small, ragged
+and extreme shapes, with all-zero blocks.
 """
 from __future__ import annotations
 
@@ -177,3 +178,84 @@ def test_fp8_forward_with_shared_and_residual():
     assert np.array_equal(idx.cpu().numpy(), ir)
     yr = oracle.shared(H, 512, *[t.cpu().numpy() for t in sx.tensors()], xin, T, y_in=yr)
     assert_close(y.cpu().numpy(), yr, "fp8 + shared + residual")
+
+
+# ------------------------------------------------------------------ prefill
+
+def hip_experts(mode, lay, x, idx, gate, k):
+    import quantized_moe_expert_amd as m
+    T = x.shape[0]
+    kind = m.WS_DECODE if mode == "decode" else m.WS_PREFILL
+    ws = torch.empty(max(m.workspace_size(kind, T, lay.num_experts, k, lay.hidden, lay.inter), 256),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.full((T, lay.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    (m.moe_q4_decode if mode == "decode" else m.moe_q4_prefill)(x, idx, gate, T, k, lay, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_fp8_prefill_recipe_zipf_sampled():
+    """512 tokens with Zipf(1.1) expert popularity (the prefill recipe) on the FP8 layer."""
+    lay, _ = recipe_layer()
+    T, k, E = 512, 8, 256
+    x = synth.bf16_bits(synth.normal((T, 2048), 1.0, 0, "fp8/px", "cuda"))
+    lg = synth.zipf_logits(T, E, 1.1, 0, "cuda")
+    _, idx, gate = hip_route(None, None, lg, T, 2048, E, k)
+    y = hip_experts("prefill", lay, x, idx, gate, k).cpu().numpy()
+    tokens = np.array([0, 3, 100, 255, 256, 389, 511])
+    _, ir, _, yr = oracle.moe_layer(lay, np_u16(x), T, k, logits=np_u16(lg), tokens=tokens)
+    assert np.array_equal(idx.cpu().numpy()[tokens], ir)
+    r, a = assert_close(y[tokens], yr, "fp8 prefill zipf")
+    say(f"[fp8 prefill] T=512 zipf sampled: rel L2 {r:.2e}, max abs {a:.2e}")
+    yd = hip_experts("decode", lay, x, idx, gate, k).cpu().numpy()
+    assert_close(y, yd, "fp8 prefill vs decode")
+
+
+def test_fp8_prefill_long_sampled():
+    """4096 tokens, N(0,1) logits (the long-prompt recipe) on the FP8 layer."""
+    lay, _ = recipe_layer()
+    T, k, E = 4096, 8, 256
+    x = synth.bf16_bits(synth.normal((T, 2048), 1.0, 0, "fp8/lx", "cuda"))
+    lg = synth.bf16_bits(synth.normal((T, E), 1.0, 0, "fp8/llg", "cuda"))
+    _, idx, gate = hip_route(None, None, lg, T, 2048, E, k)
+    y = hip_experts("prefill", lay, x, idx, gate, k).cpu().numpy()
+    tokens = np.unique(np.concatenate([np.arange(0, T, 257), [1, T - 1]]))
+    _, ir, _, yr = oracle.moe_layer(lay, np_u16(x), T, k, logits=np_u16(lg), tokens=tokens)
+    r, a = assert_close(y[tokens], yr, "fp8 prefill long")
+    say(f"[fp8 prefill] T=4096 sampled: rel L2 {r:.2e}, max abs {a:.2e}")
+
+
+@pytest.mark.parametrize("T", [1, 37, 200])
+def test_fp8_prefill_ragged(T):
+    H, I, E, k = 512, 256, 64, 6
+    lay = synth.random_layer(E, H, I, FP8, seed=21, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 21, f"fp8/prx/{T}", "cuda"))
+    lg = synth.bf16_bits(synth.normal((T, E), 1.0, 21, f"fp8/prl/{T}", "cuda"))
+    _, idx, gate = hip_route(None, None, lg, T, H, E, k)
+    y = hip_experts("prefill", lay, x, idx, gate, k)
+    _, ir, gr, yr = oracle.moe_layer(lay, np_u16(x), T, k, logits=np_u16(lg))
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    assert_close(y.cpu().numpy(), yr, f"fp8 prefill T={T}")
+
+
+def test_fp8_prefill_zero_blocks():
+    """All-zero 128 x 128 blocks (scale 0, codes 0), the first input block
+    among them, in gate, up and down: the accumulator rescale skips them."""
+    H, I, E, k, T = 512, 256, 4, 2, 64
+    lay = synth.random_layer(E, H, I, FP8, seed=23, device="cuda")
+    for e in range(E):
+        lay.gate_q[e, 0:128, 0:128] = 0
+        lay.gate_sm[e, 0, 0] = 0.0
+        lay.up_q[e, 128:256, 256:384] = 0
+        lay.up_sm[e, 1, 2] = 0.0
+        lay.down_q[e, 256:384, 128:256] = 0
+        lay.down_sm[e, 2, 1] = 0.0
+    lay.gate_q[1, 128:256, :] = 0          # every block of a row block zero
+    lay.gate_sm[1, 1, :] = 0.0
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 23, "fp8/zx", "cuda"))
+    lg = synth.bf16_bits(synth.normal((T, E), 1.0, 23, "fp8/zl", "cuda"))
+    _, idx, gate = hip_route(None, None, lg, T, H, E, k)
+    _, ir, gr, yr = oracle.moe_layer(lay, np_u16(x), T, k, logits=np_u16(lg))
+    for mode in ("prefill", "decode"):
+        y = hip_experts(mode, lay, x, idx, gate, k)
+        assert_close(y.cpu().numpy(), yr, f"fp8 zero blocks {mode}")
