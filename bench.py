@@ -349,6 +349,7 @@ def main():
     else:
         dom = ("grouped_gemm_fp8_kernel<1> (gate/up bf16 GEMM + SwiGLU)" if fp8
                else "grouped_gemm_kernel<FMT,1> (gate/up GEMM + SwiGLU)")
+        gemm_key = "grouped_gemm_fp8_kernel_1" if fp8 else "grouped_gemm_kernel_1"
         flops = 2.0 * P * H * (2 * I)
         achieved = flops / (stage_avg[0] * 1e-3) / 1e12
         wbytes = act * 2 * proj_bytes
@@ -357,13 +358,13 @@ def main():
             gbs = (wbytes + T * H * 2 + P * I * 2) / (stage_avg[0] * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic("grouped_gemm_kernel_1", args.workload, "prefill.hip"), "kernel": dom,
+                    "traffic": recorded_traffic(gemm_key, args.workload, "prefill.hip"), "kernel": dom,
                     "avg_us": round(float(stage_avg[0]) * 1e3, 3), "tflops": round(achieved, 2),
                     "active_experts": int(act)}
         else:
             roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": recorded_traffic("grouped_gemm_kernel_1", args.workload, "prefill.hip"),
+                    "traffic": recorded_traffic(gemm_key, args.workload, "prefill.hip"),
                     "kernel": dom, "avg_us": round(float(stage_avg[0]) * 1e3, 3),
                     "algorithmic_flops": flops, "active_experts": int(act)}
     roof["second_kernel_us"] = round(float(stage_avg[1]) * 1e3, 3)
