@@ -28,6 +28,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 FMT_ASYM_G64 = 0
 FMT_SYM_G128 = 1
 FMT_FP8_B128 = 2
+FMT_NVFP4 = 3
 
 _lib = None
 
@@ -57,6 +58,10 @@ def bind(path: str):
     lib.oracle_f16_value.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_value.restype = ctypes.c_double
     lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_e2m1_value.restype = ctypes.c_double
+    lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_dequant_global.restype = i32
+    lib.oracle_dequant_global.argtypes = [i32, P, P, ctypes.c_float, i32, i32, P]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_bf16_round.restype = ctypes.c_uint16
@@ -70,7 +75,7 @@ def bind(path: str):
     lib.oracle_group.restype = i32
     lib.oracle_group.argtypes = [P, i64, i32, i32, P, P, P, P]
     lib.oracle_experts.restype = i32
-    lib.oracle_experts.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, i32, P, i64, P]
+    lib.oracle_experts.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, i64, i32, P, i64, P, P]
     lib.oracle_dequant_int8.restype = i32
     lib.oracle_dequant_int8.argtypes = [P, P, i32, i32, P]
     lib.oracle_shared.restype = i32
@@ -117,6 +122,10 @@ def bf16_value(bits: int) -> float:
     return _load().oracle_bf16_value(int(bits) & 0xFFFF)
 
 
+def e2m1_value(code: int) -> float:
+    return _load().oracle_e2m1_value(int(code) & 0xF)
+
+
 def e4m3_value(bits: int) -> float:
     return _load().oracle_e4m3_value(int(bits) & 0xFF)
 
@@ -126,6 +135,8 @@ def _scales(fmt, sm):
     if fmt == FMT_FP8_B128:
         a = np.ascontiguousarray(sm)
         return a if a.dtype == np.float32 else a.astype(np.float32)
+    if fmt == FMT_NVFP4:
+        return _c(sm, np.uint8)
     return _c(sm, np.uint16)
 
 
@@ -140,13 +151,15 @@ def bf16_round_array(a) -> np.ndarray:
     return np.array([f(float(v)) for v in a], dtype=np.uint16)
 
 
-def dequant(fmt: int, q, sm, N: int, K: int) -> np.ndarray:
+def dequant(fmt: int, q, sm, N: int, K: int, global_scale: float = 1.0) -> np.ndarray:
     """float32 [N][K] from packed uint8 [N][K/2] and f16-bit scales, or (fp8)
-    uint8 codes [N][K] and float32 block scales [N/128][K/128] (see moe_oracle.c)."""
+    uint8 codes [N][K] and float32 block scales [N/128][K/128], or (NVFP4)
+    packed E2M1 [N][K/2], E4M3 block scales [N][K/16] and the matrix's global
+    scale (see moe_oracle.c)."""
     q = _c(q, np.uint8)
     sm = _scales(fmt, sm)
     out = np.empty((N, K), dtype=np.float32)
-    rc = _load().oracle_dequant(int(fmt), _p(q), _p(sm), int(N), int(K), _p(out))
+    rc = _load().oracle_dequant_global(int(fmt), _p(q), _p(sm), float(global_scale), int(N), int(K), _p(out))
     if rc != 0:
         raise ValueError("oracle_dequant: unsupported format or shape")
     return out
@@ -185,8 +198,9 @@ def group(idx, T: int, k: int, E: int):
 
 
 def experts(fmt, E, H, I, gate_q, up_q, down_q, gate_sm, up_sm, down_sm,
-            x, idx, gate, T: int, k: int, tokens=None) -> np.ndarray:
-    """float32 y [ntok][H] for the listed tokens (all T when ``tokens`` is None)."""
+            x, idx, gate, T: int, k: int, tokens=None, global_scale=None) -> np.ndarray:
+    """float32 y [ntok][H] for the listed tokens (all T when ``tokens`` is None);
+    ``global_scale``: NVFP4 float32 [E][2] = {gate and up, down}."""
     arrs = [_c(a, np.uint8) for a in (gate_q, up_q, down_q)]
     sms = [_scales(fmt, a) for a in (gate_sm, up_sm, down_sm)]
     x = _c(x, np.uint16)
@@ -194,10 +208,11 @@ def experts(fmt, E, H, I, gate_q, up_q, down_q, gate_sm, up_sm, down_sm,
     gate = _c(gate, np.float32)
     tok = _c(np.asarray(tokens, dtype=np.int64), np.int64) if tokens is not None else None
     ntok = len(tok) if tok is not None else T
+    gs = np.ascontiguousarray(global_scale, dtype=np.float32) if global_scale is not None else None
     y = np.empty((ntok, H), dtype=np.float32)
     rc = _load().oracle_experts(int(fmt), int(E), int(H), int(I), *[_p(a) for a in arrs],
                                 *[_p(a) for a in sms], _p(x), _p(idx), _p(gate), int(T), int(k),
-                                _p(tok), int(ntok), _p(y))
+                                _p(tok), int(ntok), _p(y), _p(gs))
     if rc != 0:
         raise ValueError(f"oracle_experts failed ({rc})")
     return y
@@ -249,6 +264,12 @@ def layer_np(layer):
                                       layer.gate_sm, layer.up_sm, layer.down_sm)]
 
 
+def layer_global(layer):
+    """NVFP4 global scales of a synth.Layer (host float32 [E][2]) or None."""
+    g = getattr(layer, "global_scale", None)
+    return g.cpu().numpy() if g is not None else None
+
+
 def moe_layer(layer, x, T, k, router_w=None, logits=None, bias=None, tokens=None):
     """Whole layer for the listed tokens: returns (logits, idx, gate, y) of those tokens.
 
@@ -267,5 +288,5 @@ def moe_layer(layer, x, T, k, router_w=None, logits=None, bias=None, tokens=None
     else:
         lg = np.ascontiguousarray(np.asarray(logits).view(np.uint16).reshape(T, E)[tokens])
     idx, gate = topk(lg, n, E, k)
-    y = experts(layer.fmt, E, H, I, *layer_np(layer), xs, idx, gate, n, k)
+    y = experts(layer.fmt, E, H, I, *layer_np(layer), xs, idx, gate, n, k, global_scale=layer_global(layer))
     return lg, idx, gate, y

@@ -29,7 +29,10 @@
  *     card, "What's quantized" (see oracle_shared);
  *   - block-FP8 experts with one scale per 128 x 128 block, each matrix
  *     dequantised with its block scales: drama-3-w4a16 card, "At a glance"
- *     table and "How it was made" (the released experts' format).
+ *     table and "How it was made" (the released experts' format);
+ *   - NVFP4 experts: packed E2M1 values, one E4M3 scale per 16 input
+ *     weights and a float32 global scale per matrix, gate and up sharing
+ *     theirs within an expert: drama-3-nvfp4 card, "Quantization".
  * The pages do not state the routing function, the activation or the combine.
  * This library takes: bf16 router logits, the 8 (k) largest selected with
  * ties to the lower expert index, gates = softmax over the selected logits
@@ -45,6 +48,7 @@
 #define ORACLE_FMT_ASYM_G64 0
 #define ORACLE_FMT_SYM_G128 1
 #define ORACLE_FMT_FP8_B128 2
+#define ORACLE_FMT_NVFP4 3
 
 /* ---------------------------------------------------------------- numbers */
 
@@ -108,12 +112,28 @@ double oracle_e4m3_value(uint8_t b)
     return sgn ? -v : v;
 }
 
+/*
+ * OCP 4-bit float E2M1 (the element type of the MX and NVFP4 formats): sign
+ * bit 3, exponent bits 2..1 with bias 1, mantissa bit 0; exponent 0 is
+ * subnormal, m * 2^-1.  The magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ */
+double oracle_e2m1_value(uint8_t c)
+{
+    int sgn = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (sgn ? -1.0 : 1.0) * v;
+}
+
 /* --------------------------------------------------------------- dequant */
 
-static int group_of(int fmt) { return fmt == ORACLE_FMT_ASYM_G64 ? 64 : 128; }
+static int group_of(int fmt)
+{
+    return fmt == ORACLE_FMT_ASYM_G64 ? 64 : fmt == ORACLE_FMT_NVFP4 ? 16 : 128;
+}
 static int known_fmt(int fmt)
 {
-    return fmt == ORACLE_FMT_ASYM_G64 || fmt == ORACLE_FMT_SYM_G128 || fmt == ORACLE_FMT_FP8_B128;
+    return fmt == ORACLE_FMT_ASYM_G64 || fmt == ORACLE_FMT_SYM_G128 || fmt == ORACLE_FMT_FP8_B128 ||
+           fmt == ORACLE_FMT_NVFP4;
 }
 
 /* 4-bit code of input index k in a packed row: byte k/2, low nibble for even k. */
@@ -128,9 +148,17 @@ static int nibble(const uint8_t *row, int k)
  *   fp8 b128:  w = e4m3(q[n][k]) * scale, scale float32 at
  *              ((const float *)sm)[(n/128)*(K/128) + k/128] (one per block of
  *              128 rows x 128 inputs), codes one byte per weight
+ *   nvfp4:     w = e2m1(q) * e4m3(((const uint8_t *)sm)[n*(K/16) + k/16]),
+ *              nibbles packed as the int4 formats; the matrix's global scale
+ *              is applied by the caller
  * All are exact in double (at most 15 + 40, or 4 + 24, significant bits). */
 static double weight(int fmt, const uint8_t *q, const uint16_t *sm, int K, int n, int k)
 {
+    if (fmt == ORACLE_FMT_NVFP4) {
+        const uint8_t *sb = (const uint8_t *)sm;
+        return oracle_e2m1_value((uint8_t)nibble(q + (size_t)n * (K / 2), k)) *
+               oracle_e4m3_value(sb[(size_t)n * (K / 16) + k / 16]);
+    }
     if (fmt == ORACLE_FMT_FP8_B128) {
         const float *bs = (const float *)sm;
         return oracle_e4m3_value(q[(size_t)n * K + k]) * (double)bs[(size_t)(n / 128) * (K / 128) + k / 128];
@@ -143,15 +171,23 @@ static double weight(int fmt, const uint8_t *q, const uint16_t *sm, int K, int n
     return (double)(code - 8) * oracle_f16_value(sm[gi]);
 }
 
-/* Dequantise one [N][K] matrix to float32 (the exact value, rounded once). */
-int oracle_dequant(int fmt, const uint8_t *q, const uint16_t *sm, int N, int K, float *out)
+/* Dequantise one [N][K] matrix to float32 (the exact value times the
+ * matrix's global scale, rounded once; the global scale is used by NVFP4
+ * only, the other formats have none). */
+int oracle_dequant_global(int fmt, const uint8_t *q, const uint16_t *sm, float global, int N, int K, float *out)
 {
     if (!known_fmt(fmt) || K % group_of(fmt) || (fmt == ORACLE_FMT_FP8_B128 && N % 128))
         return -1;
+    double g = fmt == ORACLE_FMT_NVFP4 ? (double)global : 1.0;
     for (int n = 0; n < N; n++)
         for (int k = 0; k < K; k++)
-            out[(size_t)n * K + k] = (float)weight(fmt, q, sm, K, n, k);
+            out[(size_t)n * K + k] = (float)(weight(fmt, q, sm, K, n, k) * g);
     return 0;
+}
+
+int oracle_dequant(int fmt, const uint8_t *q, const uint16_t *sm, int N, int K, float *out)
+{
+    return oracle_dequant_global(fmt, q, sm, 1.0f, N, K, out);
 }
 
 /* ---------------------------------------------------------------- router */
@@ -262,17 +298,18 @@ static double silu(double a) { return a / (1.0 + exp(-a)); }
  *   y[t] = float( sum_{i = 0..k-1} gate[t][i] * o(t, i) )        (slot order)
  * Each expert that a listed token uses is dequantised (exactly, in double)
  * once, then applied to every listed (token, slot) routed to it.
- * Layout of the code tensors: [E][N][K/2] bytes (int4) or [E][N][K] (fp8);
- * scales as in weight(), one matrix after another.
+ * Layout of the code tensors: [E][N][K/2] bytes (int4, NVFP4) or [E][N][K]
+ * (fp8); scales as in weight(), one matrix after another; NVFP4 global
+ * scales glob[E][2] = {gate and up, down} (NULL for the other formats).
  */
 int oracle_experts(int fmt, int E, int H, int I,
                    const uint8_t *gate_q, const uint8_t *up_q, const uint8_t *down_q,
                    const uint16_t *gate_sm, const uint16_t *up_sm, const uint16_t *down_sm,
                    const uint16_t *x, const int32_t *idx, const float *gate,
-                   int64_t T, int k, const int64_t *tok, int64_t ntok, float *y)
+                   int64_t T, int k, const int64_t *tok, int64_t ntok, float *y, const float *glob)
 {
     int g = group_of(fmt);
-    if (!known_fmt(fmt) || H % g || I % g)
+    if (!known_fmt(fmt) || H % g || I % g || (fmt == ORACLE_FMT_NVFP4 && !glob))
         return -1;
     if (!tok)
         ntok = T;
@@ -292,6 +329,10 @@ int oracle_experts(int fmt, int E, int H, int I,
         d_bytes = (size_t)H * I;
         gu_sm = (size_t)(I / 128) * (H / 128) * 2;
         d_sm = (size_t)(H / 128) * (I / 128) * 2;
+    }
+    if (fmt == ORACLE_FMT_NVFP4) {  /* one byte per 16 weights, counted in 16-bit units */
+        gu_sm = (size_t)I * (H / 16) / 2;
+        d_sm = (size_t)H * (I / 16) / 2;
     }
     /* o[j][i][d] for every listed (token, slot) */
     double *o = calloc((size_t)ntok * k * H, sizeof(double));
@@ -323,14 +364,16 @@ int oracle_experts(int fmt, int E, int H, int I,
                 continue;
             const uint8_t *gq = gate_q + e * gu_bytes, *uq = up_q + e * gu_bytes, *dq = down_q + e * d_bytes;
             const uint16_t *gs = gate_sm + e * gu_sm, *us = up_sm + e * gu_sm, *ds = down_sm + e * d_sm;
+            double ggu = fmt == ORACLE_FMT_NVFP4 ? (double)glob[2 * e] : 1.0;
+            double gd = fmt == ORACLE_FMT_NVFP4 ? (double)glob[2 * e + 1] : 1.0;
             for (int n = 0; n < I; n++)
                 for (int kk = 0; kk < H; kk++) {
-                    wg[(size_t)n * H + kk] = weight(fmt, gq, gs, H, n, kk);
-                    wu[(size_t)n * H + kk] = weight(fmt, uq, us, H, n, kk);
+                    wg[(size_t)n * H + kk] = weight(fmt, gq, gs, H, n, kk) * ggu;
+                    wu[(size_t)n * H + kk] = weight(fmt, uq, us, H, n, kk) * ggu;
                 }
             for (int d = 0; d < H; d++)
                 for (int n = 0; n < I; n++)
-                    wd[(size_t)d * I + n] = weight(fmt, dq, ds, I, d, n);
+                    wd[(size_t)d * I + n] = weight(fmt, dq, ds, I, d, n) * gd;
             for (int64_t j = 0; j < ntok; j++) {
                 int64_t t = tok ? tok[j] : j;
                 for (int i = 0; i < k; i++) {

@@ -17,7 +17,11 @@ Sources of the recipe (drama-rs / drama-q4 / drama-3-w4a16 model pages):
   * block-FP8 experts: E4M3 codes with one float32 scale per block of 128
     rows x 128 inputs, the released experts' format (drama-3-w4a16 card,
     "At a glance": routed experts block-FP8 with 128 x 128 scales; "How it
-    was made": each matrix dequantised with its block scales).
+    was made": each matrix dequantised with its block scales);
+  * NVFP4 experts: packed E2M1 values, one E4M3 scale per 16 input weights
+    and a float32 global scale per matrix, gate and up sharing theirs within
+    an expert, converted by round-to-nearest (drama-3-nvfp4 card,
+    "Quantization").
 
 Random streams: every tensor gets its own torch.Generator seeded from
 (config seed, tensor tag) through a fixed 64-bit mix, so tensors do not depend
@@ -32,6 +36,9 @@ Layout written here (the library's canonical layout):
   sym scale       uint16 (f16 bits) [E][N][K/128];
   fp8 codes       uint8 (E4M3 bits) [E][N][K], one byte per weight;
   fp8 scale       float32 [E][N/128][K/128];
+  nvfp4 codes     uint8 [E][N][K/2], E2M1 nibbles packed as the int4 codes;
+  nvfp4 scale     uint8 (E4M3 bits) [E][N][K/16]; global float32 [E][2] =
+                  {gate and up, down};
   gate, up: N = inter, K = hidden; down: N = hidden, K = inter.
 """
 from __future__ import annotations
@@ -45,8 +52,11 @@ import torch
 FMT_ASYM_G64 = 0
 FMT_SYM_G128 = 1
 FMT_FP8_B128 = 2
-GROUP = {FMT_ASYM_G64: 64, FMT_SYM_G128: 128, FMT_FP8_B128: 128}
+FMT_NVFP4 = 3
+GROUP = {FMT_ASYM_G64: 64, FMT_SYM_G128: 128, FMT_FP8_B128: 128, FMT_NVFP4: 16}
 E4M3_MAX = 448.0
+# magnitudes of the 4-bit float E2M1 for codes 0..7 (bit 3 is the sign)
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 # 20 clipping ratios, 1.00, 0.99, ..., 0.81 (drama-3-w4a16, "How it was made").
 CLIP_RATIOS = tuple(round(1.0 - 0.01 * i, 2) for i in range(20))
@@ -163,6 +173,40 @@ def quantize_fp8(w: torch.Tensor):
     return q.reshape(*lead, N, K).contiguous(), sc.reshape(*lead, N // 128, K // 128).contiguous()
 
 
+def _e2m1_codes(v: torch.Tensor) -> torch.Tensor:
+    """Nearest E2M1 code of each value (magnitudes above 6 saturate; ties go
+    to the code with an even mantissa bit).  Returns uint8 codes 0..15."""
+    grid = torch.tensor(E2M1_GRID, dtype=torch.float32, device=v.device)
+    mids = (grid[1:] + grid[:-1]) / 2
+    a = v.abs().clamp(max=6.0)
+    idx = torch.bucketize(a, mids)  # mids[idx - 1] < a <= mids[idx]
+    tie = (idx < 7) & (a == mids[idx.clamp(max=6)])
+    idx = torch.where(tie & (idx % 2 == 1), idx + 1, idx)
+    neg = (v < 0) & (idx > 0)
+    return (idx + 8 * neg.to(idx.dtype)).to(torch.uint8)
+
+
+def quantize_nvfp4(w: torch.Tensor, global_amax: torch.Tensor):
+    """Encode float32 weights [B, N, K] as NVFP4 with the given per-matrix
+    amax [B] that sets the global scale (the gate and up projections of an
+    expert pass the larger of their two).
+
+    global = amax / (6 * 448); each block of 16 inputs gets the E4M3 scale
+    e4m3(block amax / (6 * global)) and codes e2m1(w / (scale * global)).
+    Returns (packed uint8 [B, N, K/2], E4M3 scales uint8 [B, N, K/16],
+    global float32 [B])."""
+    B, N, K = w.shape
+    g = global_amax.float() / (6.0 * E4M3_MAX)
+    gs = torch.where(g > 0, g, torch.ones_like(g))[:, None, None]
+    wb = w.float().reshape(B, N, K // 16, 16)
+    sb = (wb.abs().amax(dim=3) / (6.0 * gs)).clamp_(max=E4M3_MAX).to(torch.float8_e4m3fn)
+    den = sb.float() * gs
+    v = torch.where(den[..., None] > 0, wb / torch.where(den > 0, den, torch.ones_like(den))[..., None],
+                    torch.zeros_like(wb))
+    codes = _e2m1_codes(v).reshape(B, N, K)
+    return pack_nibbles(codes), sb.view(torch.uint8).contiguous(), g.contiguous()
+
+
 def quantize(w: torch.Tensor, fmt: int, clip: bool = True):
     """Encode float32 weights [..., N, K] (groups along K).
 
@@ -214,6 +258,7 @@ class Layer:
     gate_sm: torch.Tensor
     up_sm: torch.Tensor
     down_sm: torch.Tensor
+    global_scale: torch.Tensor | None = None  # NVFP4: float32 [E][2] = {gate and up, down}
 
     @property
     def group(self) -> int:
@@ -230,7 +275,8 @@ class Layer:
         return (self.gate_q, self.up_q, self.down_q, self.gate_sm, self.up_sm, self.down_sm)
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in self.tensors())
+        extra = self.global_scale.numel() * 4 if self.global_scale is not None else 0
+        return sum(t.numel() * t.element_size() for t in self.tensors()) + extra
 
     def expert_nbytes(self) -> int:
         return self.nbytes() // self.num_experts
@@ -239,6 +285,8 @@ class Layer:
 def make_layer(E: int, H: int, I: int, fmt: int, seed: int, tag: str = "layer",
                clip: bool = True, std: float = 0.02, device="cpu") -> Layer:
     """Draw N(0, std^2) float32 gate/up/down weights for E experts and encode them."""
+    if fmt == FMT_NVFP4:
+        return _make_layer_nvfp4(E, H, I, seed, tag, std, device)
     out = {}
     # experts are drawn from their own streams, then encoded a batch at a time
     batch = max(1, (1 << 26) // (H * I)) if torch.device(device).type == "cpu" else E
@@ -256,6 +304,31 @@ def make_layer(E: int, H: int, I: int, fmt: int, seed: int, tag: str = "layer",
         out[name + "_q"] = torch.cat(qs).contiguous()
         out[name + "_sm"] = torch.cat(sms).contiguous()
     return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, **out)
+
+
+def _make_layer_nvfp4(E, H, I, seed, tag, std, device) -> Layer:
+    """make_layer for NVFP4: the gate and up projections of an expert share
+    one global scale (the larger amax of the two)."""
+    out = {n: [] for n in ("gate_q", "up_q", "down_q", "gate_sm", "up_sm", "down_sm")}
+    glob = []
+    batch = max(1, (1 << 26) // (H * I)) if torch.device(device).type == "cpu" else 64
+    for e0 in range(0, E, batch):
+        e1 = min(E, e0 + batch)
+        mats = {}
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            mats[name] = torch.stack([normal((N, K), std, seed, f"{tag}/{name}/{e}", device) for e in range(e0, e1)])
+        amax = lambda t: t.abs().flatten(1).amax(dim=1)
+        gu = torch.maximum(amax(mats["gate"]), amax(mats["up"]))
+        gl = []
+        for name, ga in (("gate", gu), ("up", gu), ("down", amax(mats["down"]))):
+            q, sb, g = quantize_nvfp4(mats[name], ga)
+            out[name + "_q"].append(q)
+            out[name + "_sm"].append(sb)
+            gl.append(g)
+        glob.append(torch.stack([gl[0], gl[2]], dim=1))
+        del mats
+    kw = {n: torch.cat(v).contiguous() for n, v in out.items()}
+    return Layer(fmt=FMT_NVFP4, num_experts=E, hidden=H, inter=I, global_scale=torch.cat(glob).contiguous(), **kw)
 
 
 def zipf_logits(T: int, E: int, s: float, seed: int, device="cpu") -> torch.Tensor:
@@ -425,6 +498,17 @@ def random_layer(E, H, I, fmt, seed, device="cpu", tag="rand") -> Layer:
     """
     g = GROUP[fmt]
     out = {}
+    if fmt == FMT_NVFP4:
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            gen = generator(seed, f"{tag}/{name}", device)
+            q = torch.randint(0, 256, (E, N, K // 2), generator=gen, device=device, dtype=torch.int32)
+            out[name + "_q"] = q.to(torch.uint8)
+            # E4M3 scales 0.25 .. 2 (codes 0x28 .. 0x40)
+            sb = torch.randint(0x28, 0x41, (E, N, K // 16), generator=gen, device=device, dtype=torch.int32)
+            out[name + "_sm"] = sb.to(torch.uint8)
+        gen = generator(seed, f"{tag}/global", device)
+        glob = torch.rand((E, 2), generator=gen, device=device) * 0.004 + 0.004
+        return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, global_scale=glob, **out)
     if fmt == FMT_FP8_B128:
         for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
             gen = generator(seed, f"{tag}/{name}", device)

@@ -13,6 +13,9 @@ What pins what:
     (tests/golden/dequant_cases.txt, dequant_fp8_cases.txt) and an
     independent numpy unpacking (torch's float8_e4m3fn decoding for FP8);
   * E4M3 decoding: torch's float8_e4m3fn conversion on all 256 patterns;
+  * E2M1 and NVFP4: hand-worked rows (tests/golden/dequant_nvfp4_cases.txt),
+    a hand-listed value table in numpy for random rows, the one-expert dense
+    MLP and brute force with global scales;
   * router logits: numpy float64 matrix product, rounded by torch;
   * top-k: brute force, a full stable sort of every token's logits;
   * gates: scipy's softmax over all experts renormalised over the selected,
@@ -89,10 +92,27 @@ def rand_bf16(rng, shape, std=1.0) -> np.ndarray:
     return torch_bf16_bits(rng.standard_normal(shape) * std)
 
 
+E2M1_TABLE = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def np_nvfp4_64(q, sb, glob, N, K) -> np.ndarray:
+    """Independent float64 NVFP4 dequantisation: a hand-listed E2M1 table and
+    torch's E4M3 decoding."""
+    codes = np_codes(q, N, K)
+    s = torch.from_numpy(np.asarray(sb, dtype=np.uint8).reshape(N, K // 16).copy()).view(torch.float8_e4m3fn)
+    return E2M1_TABLE[codes] * np.repeat(s.double().numpy(), 16, axis=1) * float(glob)
+
+
 def rand_layer(rng, E, H, I, fmt):
     """Random codes and f16 scales/mins of plausible magnitude (numpy arrays)."""
     g = 64 if fmt == oracle.FMT_ASYM_G64 else 128
     mats = {}
+    if fmt == oracle.FMT_NVFP4:
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            mats[name + "_q"] = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+            mats[name + "_sm"] = rng.integers(0x28, 0x41, size=(E, N, K // 16), dtype=np.uint8)
+        mats["global"] = (rng.random((E, 2)) * 0.004 + 0.004).astype(np.float32)
+        return mats
     if fmt == oracle.FMT_FP8_B128:
         for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
             q = rng.integers(0, 256, size=(E, N, K), dtype=np.uint8)
@@ -115,11 +135,21 @@ def layer_args(mats):
     return [mats[n] for n in ("gate_q", "up_q", "down_q", "gate_sm", "up_sm", "down_sm")]
 
 
+def glob_kw(mats):
+    return {"global_scale": mats["global"]} if "global" in mats else {}
+
+
 def np_expert_out(fmt, mats, e, x64, H, I):
     """o = Wd silu(Wg x) * (Wu x) in float64 with numpy matmuls and scipy's expit."""
-    wg = np_dequant64(fmt, mats["gate_q"][e], mats["gate_sm"][e], I, H)
-    wu = np_dequant64(fmt, mats["up_q"][e], mats["up_sm"][e], I, H)
-    wd = np_dequant64(fmt, mats["down_q"][e], mats["down_sm"][e], H, I)
+    if fmt == oracle.FMT_NVFP4:
+        g = mats["global"][e]
+        wg = np_nvfp4_64(mats["gate_q"][e], mats["gate_sm"][e], g[0], I, H)
+        wu = np_nvfp4_64(mats["up_q"][e], mats["up_sm"][e], g[0], I, H)
+        wd = np_nvfp4_64(mats["down_q"][e], mats["down_sm"][e], g[1], H, I)
+    else:
+        wg = np_dequant64(fmt, mats["gate_q"][e], mats["gate_sm"][e], I, H)
+        wu = np_dequant64(fmt, mats["up_q"][e], mats["up_sm"][e], I, H)
+        wd = np_dequant64(fmt, mats["down_q"][e], mats["down_sm"][e], H, I)
     a = wg @ x64
     b = wu @ x64
     h = a * scipy.special.expit(a) * b
@@ -150,6 +180,28 @@ def read_dequant_cases():
                 cur["sm"] = [int(v, 16) for v in rest]
             elif head == "expect":
                 cur["expect"] = [float(v) for v in rest]
+    return cases
+
+
+def read_dequant_nvfp4_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "dequant_nvfp4_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, *rest = line.split()
+            if head == "case":
+                kv = dict(r.split("=") for r in rest[1:])
+                cur = {"name": rest[0], "N": int(kv["N"]), "K": int(kv["K"]), "global": float(kv["global"]),
+                       "expect": []}
+                cases.append(cur)
+            elif head == "bytes":
+                cur["bytes"] = [int(v, 16) for v in rest]
+            elif head == "scale":
+                cur["scale"] = [int(v, 16) for v in rest]
+            elif head == "expect":
+                cur["expect"].append([float(v) for v in rest])
     return cases
 
 
@@ -303,6 +355,24 @@ def pin_dequant_fp8_golden():
             assert np.array_equal(blk, np.array(cyc(e, 128 * 128))), (c["name"], bi)
 
 
+def pin_dequant_nvfp4_golden():
+    for c in read_dequant_nvfp4_cases():
+        N, K = c["N"], c["K"]
+        q = np.array(cyc(c["bytes"], N * K // 2), dtype=np.uint8).reshape(N, K // 2)
+        sb = np.array(c["scale"], dtype=np.uint8)
+        assert sb.size == N * (K // 16) == len(c["expect"]), c["name"]
+        got = oracle.dequant(oracle.FMT_NVFP4, q, sb, N, K, c["global"]).astype(np.float64)
+        exp = np.concatenate([cyc(e, 16) for e in c["expect"]]).reshape(N, K)
+        assert np.array_equal(got, exp), c["name"]
+
+
+def pin_e2m1_table():
+    """The 16 E2M1 codes: the hand-listed magnitudes, sign bit 3."""
+    got = np.array([oracle.e2m1_value(c) for c in range(16)])
+    assert np.array_equal(got, E2M1_TABLE)
+    assert np.array_equal(np.signbit(got), np.arange(16) >= 8)
+
+
 def pin_dequant_random():
     """Random rows: float32 of the exact value, as computed independently by numpy."""
     rng = np.random.default_rng(11)
@@ -323,6 +393,14 @@ def pin_dequant_random():
     sm = (rng.standard_normal((2, 2)) * 1e-3).astype(np.float32)
     ref = np_dequant64(oracle.FMT_FP8_B128, q, sm, N, K).astype(np.float32)
     got = oracle.dequant(oracle.FMT_FP8_B128, q, sm, N, K)
+    assert np.array_equal(got, ref)
+    # nvfp4: every code and block scale byte (no NaN), a global scale
+    N, K = 5, 256
+    q = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sb = rng.integers(0, 256, size=(N, K // 16), dtype=np.uint8)
+    sb[(sb & 0x7F) == 0x7F] -= 1
+    ref = np_nvfp4_64(q, sb, 0.375, N, K).astype(np.float32)
+    got = oracle.dequant(oracle.FMT_NVFP4, q, sb, N, K, 0.375)
     assert np.array_equal(got, ref)
 
 
@@ -415,13 +493,13 @@ def pin_one_expert_dense():
     """E = 1, k = 1: the layer is the dense SwiGLU MLP of the dequantised weights."""
     rng = np.random.default_rng(17)
     for fmt, (H, I) in ((oracle.FMT_ASYM_G64, (128, 64)), (oracle.FMT_SYM_G128, (256, 128)),
-                        (oracle.FMT_FP8_B128, (256, 128))):
+                        (oracle.FMT_FP8_B128, (256, 128)), (oracle.FMT_NVFP4, (128, 64))):
         T = 3
         mats = rand_layer(rng, 1, H, I, fmt)
         x = rand_bf16(rng, (T, H))
         idx = np.zeros((T, 1), dtype=np.int32)
         gate = np.ones((T, 1), dtype=np.float32)
-        y = oracle.experts(fmt, 1, H, I, *layer_args(mats), x, idx, gate, T, 1)
+        y = oracle.experts(fmt, 1, H, I, *layer_args(mats), x, idx, gate, T, 1, **glob_kw(mats))
         for t in range(T):
             ref = np_expert_out(fmt, mats, 0, bf16_to_f64(x[t]), H, I)
             assert rel_l2(y[t], ref) < 1e-6
@@ -433,18 +511,19 @@ def pin_experts_bruteforce():
     rng = np.random.default_rng(19)
     for fmt, (E, H, I, k, T) in ((oracle.FMT_ASYM_G64, (6, 128, 64, 3, 5)),
                                  (oracle.FMT_SYM_G128, (5, 256, 128, 2, 4)),
-                                 (oracle.FMT_FP8_B128, (3, 256, 128, 2, 3))):
+                                 (oracle.FMT_FP8_B128, (3, 256, 128, 2, 3)),
+                                 (oracle.FMT_NVFP4, (4, 128, 64, 2, 4))):
         mats = rand_layer(rng, E, H, I, fmt)
         x = rand_bf16(rng, (T, H))
         idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
         gate = rng.random((T, k)).astype(np.float32)
-        y = oracle.experts(fmt, E, H, I, *layer_args(mats), x, idx, gate, T, k)
+        y = oracle.experts(fmt, E, H, I, *layer_args(mats), x, idx, gate, T, k, **glob_kw(mats))
         for t in range(T):
             ref = sum(float(gate[t, i]) * np_expert_out(fmt, mats, idx[t, i], bf16_to_f64(x[t]), H, I)
                       for i in range(k))
             assert rel_l2(y[t], ref) < 1e-6
         sub = [4, 1] if T > 4 else [1]
-        ys = oracle.experts(fmt, E, H, I, *layer_args(mats), x, idx, gate, T, k, tokens=sub)
+        ys = oracle.experts(fmt, E, H, I, *layer_args(mats), x, idx, gate, T, k, tokens=sub, **glob_kw(mats))
         assert np.array_equal(ys, y[sub])
 
 
@@ -554,4 +633,4 @@ ALL_PINS = [pin_f16_decode_all, pin_bf16_decode_all, pin_bf16_round, pin_dequant
             pin_gates, pin_group, pin_one_expert_dense, pin_experts_bruteforce,
             pin_gate_linearity, pin_layer_chain, pin_residual, pin_dequant_int8_golden,
             pin_dequant_int8_random, pin_shared_dense, pin_shared_as_routed_expert, pin_e4m3_decode_all,
-            pin_dequant_fp8_golden]
+            pin_dequant_fp8_golden, pin_e2m1_table, pin_dequant_nvfp4_golden]

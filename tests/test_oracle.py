@@ -81,3 +81,29 @@ def test_fp8_encoder_round_trip(orc):
     step = np.where(np.abs(v) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v), 1e-30))) - 4), 2.0 ** -10)
     assert (np.abs(ratio - v) <= step * (1 + 1e-6) + 1e-12).all()
     assert np.allclose(d, v * np.repeat(np.repeat(s.numpy().astype(np.float64), 128, 0), 128, 1))
+
+
+def test_nvfp4_encoder_round_trip(orc):
+    """The synthetic NVFP4 encoder: gate and up share a global scale (the
+    larger amax / (6 * 448)), each weight is within half an E2M1 step (of
+    the grid around it) of its dequantised value, and each 16-block's
+    largest weight dequantises to at least 4 times its scale."""
+    import synth
+    lay = synth.make_layer(2, 256, 128, synth.FMT_NVFP4, seed=0, tag="pin/nvfp4")
+    g = lay.global_scale.numpy().astype(np.float64)
+    for e in range(2):
+        w = {n: synth.normal(shape, 0.02, 0, f"pin/nvfp4/{n}/{e}", "cpu").double().numpy()
+             for n, shape in (("gate", (128, 256)), ("up", (128, 256)), ("down", (256, 128)))}
+        assert np.isclose(g[e, 0], max(np.abs(w["gate"]).max(), np.abs(w["up"]).max()) / 2688, rtol=1e-6)
+        assert np.isclose(g[e, 1], np.abs(w["down"]).max() / 2688, rtol=1e-6)
+        for name, q, sb, gi, (N, K) in (("gate", lay.gate_q, lay.gate_sm, 0, (128, 256)),
+                                        ("up", lay.up_q, lay.up_sm, 0, (128, 256)),
+                                        ("down", lay.down_q, lay.down_sm, 1, (256, 128))):
+            d = orc.dequant(synth.FMT_NVFP4, q[e].numpy(), sb[e].numpy(), N, K, float(g[e, gi])).astype(np.float64)
+            s = np.array([orc.e4m3_value(b) for b in sb[e].numpy().ravel()]).reshape(N, K // 16) * g[e, gi]
+            s = np.repeat(s, 16, axis=1)
+            a = np.abs(w[name]) / s
+            half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+            assert (np.abs(w[name] - d) <= (half + 1e-6) * s).all(), name
+            blk = (np.abs(d) / s).reshape(N, K // 16, 16).max(axis=2)
+            assert (blk >= 4).all(), name

@@ -47,6 +47,12 @@ MUTANTS = [
     ("e4m3_subnormal_scale", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     ("e4m3_sign_dropped", "return sgn ? -v : v;", "return v;"),
     ("fp8_block_row_ignored", "bs[(size_t)(n / 128) * (K / 128) + k / 128]", "bs[(size_t)(k / 128)]"),
+    ("e2m1_sign_dropped", "return (sgn ? -1.0 : 1.0) * v;", "return v;"),
+    ("e2m1_bias_2", "ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e - 2)"),
+    ("e2m1_subnormal_quarter", "double v = e == 0 ? 0.5 * m :", "double v = e == 0 ? 0.25 * m :"),
+    ("nvfp4_block_of_32", "sb[(size_t)n * (K / 16) + k / 16]", "sb[(size_t)n * (K / 16) + k / 32]"),
+    ("nvfp4_global_dropped", "double ggu = fmt == ORACLE_FMT_NVFP4 ? (double)glob[2 * e] : 1.0;",
+     "double ggu = 1.0;"),
     ("residual_truncates", "out[i] = oracle_bf16_round(s);", "out[i] = (uint16_t)(oracle_bf16_round(s) & 0xfffe);"),
 ]
 
