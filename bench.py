@@ -22,6 +22,9 @@ Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
                 decode / frame / prefill / long prefill with block-FP8 experts
                 (E4M3, float32 scale per 128 x 128 block; the released
                 experts' format) of the same Gaussian weights.
+  decode_nvfp4, frame_nvfp4, prefill_nvfp4, long_prefill_nvfp4
+                the same with NVFP4 experts (E2M1, E4M3 scale per 16 inputs,
+                float32 global per matrix).
   shared        the shared expert alone (moe_q4_shared) for the frame's 16
                 tokens; steps rotate over 200 address-distinct copies (3 MB
                 each) so its codes are read from HBM.
@@ -50,6 +53,7 @@ WORKLOADS = {
     "tiny": 1, "decode": 2, "prefill": 3, "frame": 4, "long_prefill": 5,
     "decode_shared": 2, "frame_shared": 4, "shared": 4, "decode_fp8": 2, "frame_fp8": 4,
     "prefill_fp8": 3, "long_prefill_fp8": 5,
+    "decode_nvfp4": 2, "frame_nvfp4": 4, "prefill_nvfp4": 3, "long_prefill_nvfp4": 5,
 }
 SHARED_INTER = 512   # the shared expert's inner size (that of a routed expert)
 SHARED_COPIES = 200  # address-distinct shared experts of the "shared" workload
@@ -135,7 +139,8 @@ def clone_layer(lay):
     import synth
     return synth.Layer(fmt=lay.fmt, num_experts=lay.num_experts, hidden=lay.hidden, inter=lay.inter,
                        gate_q=lay.gate_q.clone(), up_q=lay.up_q.clone(), down_q=lay.down_q.clone(),
-                       gate_sm=lay.gate_sm.clone(), up_sm=lay.up_sm.clone(), down_sm=lay.down_sm.clone())
+                       gate_sm=lay.gate_sm.clone(), up_sm=lay.up_sm.clone(), down_sm=lay.down_sm.clone(),
+                       global_scale=lay.global_scale.clone() if lay.global_scale is not None else None)
 
 
 def expert_bytes(lay) -> int:
@@ -174,7 +179,9 @@ def main():
     cfg = WORKLOADS[args.workload]
     defaults = {"tiny": (200, 20), "decode": (400, 40), "prefill": (50, 5), "frame": (10, 2),
                 "long_prefill": (20, 3), "decode_shared": (400, 40), "frame_shared": (10, 2), "shared": (400, 40),
-                "decode_fp8": (400, 40), "frame_fp8": (10, 2), "prefill_fp8": (50, 5), "long_prefill_fp8": (20, 3)}
+                "decode_fp8": (400, 40), "frame_fp8": (10, 2), "prefill_fp8": (50, 5), "long_prefill_fp8": (20, 3),
+                "decode_nvfp4": (400, 40), "frame_nvfp4": (10, 2), "prefill_nvfp4": (50, 5),
+                "long_prefill_nvfp4": (20, 3)}
     K = args.steps if args.steps is not None else defaults[args.workload][0]
     W = args.warmup if args.warmup is not None else defaults[args.workload][1]
 
@@ -182,13 +189,15 @@ def main():
     only_shared = args.workload == "shared"
     with_shared = args.workload in ("decode_shared", "frame_shared", "shared")
     fp8 = args.workload.endswith("_fp8")
+    nvfp4 = args.workload.endswith("_nvfp4")
     case = synth.make_case(cfg, device="cuda", layers=1 if only_shared else None,
-                           fmt=synth.FMT_FP8_B128 if fp8 else None)
+                           fmt=synth.FMT_FP8_B128 if fp8 else synth.FMT_NVFP4 if nvfp4 else None)
     torch.cuda.synchronize()
     T, H, E, k, I = case.T, case.H, case.E, case.k, case.I
     base_wl = {"decode_shared": "decode", "frame_shared": "frame", "decode_fp8": "decode",
                "frame_fp8": "frame", "prefill_fp8": "prefill",
-               "long_prefill_fp8": "long_prefill"}.get(args.workload, args.workload)
+               "long_prefill_fp8": "long_prefill", "decode_nvfp4": "decode", "frame_nvfp4": "frame",
+               "prefill_nvfp4": "prefill", "long_prefill_nvfp4": "long_prefill"}.get(args.workload, args.workload)
     decode_path = base_wl in ("tiny", "decode", "frame", "shared")
     mode = "decode" if decode_path else "prefill"
 
@@ -391,6 +400,11 @@ def main():
     names["frame_fp8"] = names["frame"].replace("int4 asym g64 (RTN)", "block-FP8 E4M3, 128x128 scales")
     names["prefill_fp8"] = names["prefill"].replace("int4 asym g64", "block-FP8 E4M3, 128x128 scales")
     names["long_prefill_fp8"] = names["long_prefill"].replace("int4 sym g128", "block-FP8 E4M3, 128x128 scales")
+    nv = "NVFP4 (E2M1, E4M3 scale per 16, fp32 global)"
+    names["decode_nvfp4"] = names["decode"].replace("int4 asym g64 (clip search)", nv)
+    names["frame_nvfp4"] = names["frame"].replace("int4 asym g64 (RTN)", nv)
+    names["prefill_nvfp4"] = names["prefill"].replace("int4 asym g64", nv)
+    names["long_prefill_nvfp4"] = names["long_prefill"].replace("int4 sym g128", nv)
     names["shared"] = (f"shared expert alone: 16 tokens, H=2048, I={SHARED_INTER}, int8 sym g128; "
                        f"{SHARED_COPIES} address-distinct copies rotated")
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -401,7 +415,7 @@ def main():
                       "layers_per_step": nl_per_step, "path": mode,
                       "format": "int8_sym_g128" if only_shared else {
                           synth.FMT_ASYM_G64: "asym_g64", synth.FMT_SYM_G128: "sym_g128",
-                          synth.FMT_FP8_B128: "fp8_e4m3_b128"}[case.fmt],
+                          synth.FMT_FP8_B128: "fp8_e4m3_b128", synth.FMT_NVFP4: "nvfp4"}[case.fmt],
                       "shared_expert": with_shared},
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
@@ -433,7 +447,8 @@ def cpu_baseline(case, args, decode_path, budget_s, shared=None, only_shared=Fal
         if not only_shared:
             lg = oracle.router(xs, rw, len(sel), H, E) if rw is not None else np.ascontiguousarray(lg_all[sel])
             idx, gate = oracle.topk(lg, len(sel), E, k)
-            y = oracle.experts(lay.fmt, E, H, lay.inter, *host_layer, xs, idx, gate, len(sel), k)
+            y = oracle.experts(lay.fmt, E, H, lay.inter, *host_layer, xs, idx, gate, len(sel), k,
+                               global_scale=oracle.layer_global(lay))
         if host_sx is not None:
             oracle.shared(H, shared.inter, *host_sx, xs, len(sel), y_in=y)
         t_total += time.perf_counter() - t1

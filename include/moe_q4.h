@@ -70,7 +70,8 @@ typedef struct ihipStream_t *moe_q4_stream;
 typedef enum {
     MOE_Q4_ASYM_G64 = 0,   /* w = scale * q + min, q in 0..15, group 64 along K  */
     MOE_Q4_SYM_G128 = 1,   /* w = scale * (q - 8), q in 0..15, group 128 along K */
-    MOE_Q4_FP8_B128 = 2    /* w = e4m3(q) * scale, one float scale per 128 x 128 block */
+    MOE_Q4_FP8_B128 = 2,   /* w = e4m3(q) * scale, one float scale per 128 x 128 block */
+    MOE_Q4_NVFP4 = 3       /* w = e2m1(q) * e4m3(scale) * global, scale per 16 along K */
 } moe_q4_format;
 
 typedef enum {
@@ -110,6 +111,16 @@ typedef enum {
  * (block scale on each 32-code partial sum), the prefill GEMMs run bf16 (x
  * as given) and f16 (h) matrix cores with the block scales applied by
  * rescaling the fp32 accumulators at each 128-input block.
+ * NVFP4 (MOE_Q4_NVFP4; drama-3-nvfp4 card, "Quantization": packed E2M1
+ * values, one E4M3 scale per 16 input weights, a float32 global scale per
+ * matrix, gate and up sharing theirs within an expert):
+ *   *_q            uint8 [E][N][K/2], E2M1 codes packed as the int4 formats
+ *   *_sm           point to uint8 [E][N][K/16] E4M3 block scales
+ *   global_scale   float [E][2] = {gate and up, down} (required; NULL for the
+ *                  other formats); 4-byte aligned
+ * Codes times block scales are exact in bf16 and f16; the decode GEMVs take
+ * exact products with fp32 sums, the prefill GEMMs run f16 matrix cores on
+ * the exact weights; the global scale multiplies each output.
  */
 typedef struct moe_q4_layer {
     int32_t num_experts;   /* E */
@@ -118,6 +129,7 @@ typedef struct moe_q4_layer {
     int32_t format;        /* moe_q4_format */
     const uint8_t *gate_q, *up_q, *down_q;
     const uint16_t *gate_sm, *up_sm, *down_sm;
+    const float *global_scale;   /* NVFP4 only (see below), else NULL */
 } moe_q4_layer;
 
 /*

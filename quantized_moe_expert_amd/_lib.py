@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
 ASYM_G64 = 0
 SYM_G128 = 1
 FP8_B128 = 2
+NVFP4 = 3
 WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP, WS_FORWARD, WS_SHARED = 0, 1, 2, 3, 4, 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
@@ -39,7 +40,8 @@ class Layer(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("format", ctypes.c_int32),
                 ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
-                ("gate_sm", ctypes.c_void_p), ("up_sm", ctypes.c_void_p), ("down_sm", ctypes.c_void_p)]
+                ("gate_sm", ctypes.c_void_p), ("up_sm", ctypes.c_void_p), ("down_sm", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p)]
 
 
 class SharedExpert(ctypes.Structure):
@@ -142,7 +144,8 @@ def layer_struct(layer) -> Layer:
         fmt = layer.format
     return Layer(int(layer.num_experts), int(layer.hidden), int(layer.inter), int(fmt),
                  _ptr(layer.gate_q), _ptr(layer.up_q), _ptr(layer.down_q),
-                 _ptr(layer.gate_sm), _ptr(layer.up_sm), _ptr(layer.down_sm))
+                 _ptr(layer.gate_sm), _ptr(layer.up_sm), _ptr(layer.down_sm),
+                 _ptr(getattr(layer, "global_scale", None)))
 
 
 def shared_struct(sx) -> SharedExpert:

@@ -48,9 +48,12 @@ int check_layer(const moe_q4_layer *w, bool prefill) {
         !aligned(w->up_sm, 4) || !aligned(w->down_sm, 4))
         return MOE_Q4_ERR_INVALID_ARG;
     if (w->num_experts < 1 || w->hidden < 1 || w->inter < 1) return MOE_Q4_ERR_INVALID_ARG;
-    if (w->format != MOE_Q4_ASYM_G64 && w->format != MOE_Q4_SYM_G128 && w->format != MOE_Q4_FP8_B128)
+    if (w->format != MOE_Q4_ASYM_G64 && w->format != MOE_Q4_SYM_G128 && w->format != MOE_Q4_FP8_B128 &&
+        w->format != MOE_Q4_NVFP4)
         return MOE_Q4_ERR_UNSUPPORTED;
-    const int G = w->format == MOE_Q4_ASYM_G64 ? 64 : 128;
+    if (w->format == MOE_Q4_NVFP4 && (!w->global_scale || !aligned(w->global_scale, 4)))
+        return MOE_Q4_ERR_INVALID_ARG;
+    const int G = w->format == MOE_Q4_ASYM_G64 ? 64 : w->format == MOE_Q4_NVFP4 ? 16 : 128;
     if (w->num_experts > 1024) return MOE_Q4_ERR_UNSUPPORTED;
     if (!pow2_between(w->hidden, 64, 2048) || !pow2_between(w->inter, 64, 2048)) return MOE_Q4_ERR_UNSUPPORTED;
     if (w->hidden % G || w->inter % G) return MOE_Q4_ERR_UNSUPPORTED;
@@ -70,6 +73,7 @@ LayerPtrs layer_ptrs(const moe_q4_layer *w) {
     L.gsm = w->gate_sm;
     L.usm = w->up_sm;
     L.dsm = w->down_sm;
+    L.glob = w->format == MOE_Q4_NVFP4 ? w->global_scale : nullptr;
     return L;
 }
 

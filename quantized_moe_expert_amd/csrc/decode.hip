@@ -29,6 +29,7 @@
 // down GEMV (|h| must stay below 65504).
 #include "decode_dev.h"
 #include "fp8_dev.h"
+#include "nvfp4_dev.h"
 #include "group_dev.h"
 #include "shared_dev.h"
 #include "route_dev.h"
@@ -461,6 +462,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, I);
         if (ir.steps <= 0) continue;
         if constexpr (FMT == 2) fp8_gateup_item<LPG, ROUTE>(x, H, I, k, L, tile, ir, h, s_out);
+        else if constexpr (FMT == 3) nvfp4_gateup_item<LPR, ROUTE>(x, H, I, k, L, tile, ir, h, s_out);
         else gateup_item<LPR, FMT, ROUTE>(x, H, I, k, L, tile, ir, h, s_out);
     }
 }
@@ -485,6 +487,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, H);
         if (ir.steps <= 0) continue;
         if constexpr (FMT == 2) fp8_down_item<LPR>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
+        else if constexpr (FMT == 3) nvfp4_down_item<LPR>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
         else down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
     }
     if constexpr (SHARED && LPR >= 4) {
@@ -776,7 +779,7 @@ static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64
                  : launch_experts_fmt<F, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out,      \
                                                        gate_out, none, nullptr);
     switch (L.fmt) {
-        FMT_CASE(0) FMT_CASE(1) FMT_CASE(2)
+        FMT_CASE(0) FMT_CASE(1) FMT_CASE(2) FMT_CASE(3)
         default: return hipErrorInvalidValue;
     }
 #undef FMT_CASE

@@ -1,4 +1,4 @@
-// Small kernels: the dequantisation test hooks (int4 and fp8), the residual
+// Small kernels: the dequantisation test hooks (int4, fp8, NVFP4), the residual
 // step of a chain of layers, and a float fill.
 #include "moe_internal.h"
 
@@ -64,6 +64,34 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint8_t *__restr
     dst[3] = bf16_to_f32(hi >> 16) * s;
 }
 
+// out[n][k] of one NVFP4 projection: codes converted as the expert kernels
+// convert them (exact bf16), times the E4M3 block scale (exact product in
+// fp32), times the global scale, one rounding.
+__global__ __launch_bounds__(256) void dequant_nvfp4_kernel(const uint8_t *__restrict__ q,
+                                                            const uint8_t *__restrict__ sb,
+                                                            const float *__restrict__ gp, int N, int K,
+                                                            float *__restrict__ out) {
+    const int64_t words = (int64_t)N * K / 8;
+    const int64_t wi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (wi >= words) return;
+    const float glob = *gp;
+    const int64_t n = wi / (K / 8);
+    const int k0 = (int)(wi % (K / 8)) * 8;
+    const uint32_t w = reinterpret_cast<const uint32_t *>(q)[wi];
+    const float s = __builtin_amdgcn_cvt_f32_fp8((int)sb[(size_t)n * (K / 16) + k0 / 16], 0);
+    const uint32_t p[4] = {
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3))};
+    float *dst = out + (size_t)n * K + k0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dst[2 * j] = (bf16_to_f32(p[j] & 0xffffu) * s) * glob;
+        dst[2 * j + 1] = (bf16_to_f32(p[j] >> 16) * s) * glob;
+    }
+}
+
 __global__ __launch_bounds__(256) void residual_kernel(const uint16_t *__restrict__ x, const float *__restrict__ y,
                                                        int64_t n, uint16_t *__restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -75,6 +103,14 @@ hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, 
     const int N = proj == 2 ? L.H : L.I, K = proj == 2 ? L.I : L.H;
     const uint8_t *q = proj == 0 ? L.gq : (proj == 1 ? L.uq : L.dq);
     const uint16_t *sm = proj == 0 ? L.gsm : (proj == 1 ? L.usm : L.dsm);
+    if (L.fmt == 3) {
+        q += (size_t)expert * N * (K / 2);
+        const uint8_t *sb = reinterpret_cast<const uint8_t *>(sm) + (size_t)expert * N * (K / 16);
+        const int64_t words = (int64_t)N * K / 8;
+        hipLaunchKernelGGL(dequant_nvfp4_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, q, sb,
+                           L.glob + 2 * expert + (proj == 2 ? 1 : 0), N, K, out);
+        return hipGetLastError();
+    }
     if (L.fmt == 2) {
         q += (size_t)expert * N * K;
         const float *sc = reinterpret_cast<const float *>(sm) + (size_t)expert * (N / 128) * (K / 128);

@@ -30,6 +30,7 @@ struct LayerPtrs {
     int E, H, I, fmt;
     const uint8_t *gq, *uq, *dq;
     const uint16_t *gsm, *usm, *dsm;
+    const float *glob;  // NVFP4 global scales [E][2] = {gate and up, down}
 };
 
 constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chunk

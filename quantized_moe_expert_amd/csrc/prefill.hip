@@ -54,7 +54,9 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // ------------------------------------------------------------ x -> f16
 //
 // One wave per row: e = floor(log2 max|x|) - 14 (0 for a zero row or one
-// holding inf / NaN), x16 = f16(x * 2^-e) in PERM8 order, xexp[t] = e.
+// holding inf / NaN), x16 = f16(x * 2^-e) in PERM8 order (natural order
+// without PERM), xexp[t] = e.
+template <bool PERM>
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restrict__ x, int64_t T, int H,
                                                        uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -89,8 +91,8 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restric
             const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(w[q] >> 16), -e);
             o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
-        uint32_t p[4];
-        perm8(o[0], o[1], o[2], o[3], p[0], p[1], p[2], p[3]);
+        uint32_t p[4] = {o[0], o[1], o[2], o[3]};
+        if (PERM) perm8(o[0], o[1], o[2], o[3], p[0], p[1], p[2], p[3]);
         dst[i] = make_uint4(p[0], p[1], p[2], p[3]);
     }
     if (lane == 0) xexp[t] = e;
@@ -187,7 +189,9 @@ __device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int
 // Main loop over K for a tile of MS x 32 rows.
 template <int FMT, int MS>
 __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2], int wave, int lane) {
-    constexpr int G = FMT == 0 ? 64 : 128;
+    // K elements per scale word of the ring (NVFP4: one word of four E4M3
+    // block scales per weight row and K-step)
+    constexpr int G = FMT == 0 || FMT == 3 ? 64 : 128;
     constexpr int KPG = G / KS;
     constexpr int LPS = MS + B_LOADS + 1;  // loads per thread and stage
     const int l32 = lane & 31, hf = lane >> 5;
@@ -200,6 +204,7 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
     // per N-subtile: scale and min of the current group, for the 1024 + q
     // pairs (index 0) and the 1024 + 16 q pairs (index 1)
     half2_t s2[2][2], m2[2];
+    uint32_t nvs[2][2];  // NVFP4: the lane's two block scales of the K-step, as f16 pairs (s, s)
     const uint32_t kf = opaque_magic(MAGIC_F16);
     const half2_t off0 = {(_Float16)(FMT == 0 ? 1024.0f : 1032.0f), (_Float16)(FMT == 0 ? 1024.0f : 1032.0f)};
     const half2_t off1 = {(_Float16)(FMT == 0 ? 1024.0f : 1152.0f), (_Float16)(FMT == 0 ? 1024.0f : 1152.0f)};
@@ -217,7 +222,17 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
                 const uint8_t *sa = c.ring + u * STAGE_BYTES;
                 const uint8_t *sb = sa + A_BYTES;
                 const uint32_t *ss = reinterpret_cast<const uint32_t *>(sb + B_BYTES);
-                if (ks % KPG == 0) {
+                if (FMT == 3) {
+#pragma unroll
+                    for (int ns = 0; ns < 2; ++ns) {
+                        // blocks 2 hf and 2 hf + 1 of the K-step: k in [32 hf, 32 hf + 32)
+                        const uint32_t pw = ss[c.brow[ns]] >> (16 * hf);
+                        const uint32_t sp =
+                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw, 1.0f, false));
+                        nvs[ns][0] = (sp & 0xffffu) * 0x10001u;
+                        nvs[ns][1] = (sp >> 16) * 0x10001u;
+                    }
+                } else if (ks % KPG == 0) {
 #pragma unroll
                     for (int ns = 0; ns < 2; ++ns) {
                         const uint32_t pw = ss[c.brow[ns]];
@@ -245,12 +260,25 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
 #pragma unroll
                     for (int ns = 0; ns < 2; ++ns) {
                         const uint32_t word = s == 0 ? bw[ns].x : s == 1 ? bw[ns].y : s == 2 ? bw[ns].z : bw[ns].w;
-                        const uint32_t w8 = word >> 8;
-                        bv[ns] = u32x4_t{
-                            dequant_pair<FMT>(insert_codes<0x000f000fu>(word, kf), off0, s2[ns][0], m2[ns]),
-                            dequant_pair<FMT>(insert_codes<0x00f000f0u>(word, kf), off1, s2[ns][1], m2[ns]),
-                            dequant_pair<FMT>(insert_codes<0x000f000fu>(w8, kf), off0, s2[ns][0], m2[ns]),
-                            dequant_pair<FMT>(insert_codes<0x00f000f0u>(w8, kf), off1, s2[ns][1], m2[ns])};
+                        if constexpr (FMT == 3) {
+                            // E2M1 pairs in natural order times the block scale: exact in f16
+                            const half2_t sc = __builtin_bit_cast(half2_t, nvs[ns][s >> 1]);
+                            auto nv = [&](uint32_t p) {
+                                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p) * sc);
+                            };
+                            bv[ns] = u32x4_t{
+                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0))),
+                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1))),
+                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2))),
+                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3)))};
+                        } else {
+                            const uint32_t w8 = word >> 8;
+                            bv[ns] = u32x4_t{
+                                dequant_pair<FMT>(insert_codes<0x000f000fu>(word, kf), off0, s2[ns][0], m2[ns]),
+                                dequant_pair<FMT>(insert_codes<0x00f000f0u>(word, kf), off1, s2[ns][1], m2[ns]),
+                                dequant_pair<FMT>(insert_codes<0x000f000fu>(w8, kf), off0, s2[ns][0], m2[ns]),
+                                dequant_pair<FMT>(insert_codes<0x00f000f0u>(w8, kf), off1, s2[ns][1], m2[ns])};
+                        }
                     }
                     const int ch = 4 * hf + s;  // logical 16-byte chunk of the A row
 #pragma unroll
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
     uint16_t *__restrict__ h_out, uint16_t *__restrict__ z) {
-    constexpr int G = FMT == 0 ? 64 : 128;
+    constexpr int G = FMT == 0 || FMT == 3 ? 64 : 128;  // K elements per scale word (see gemm_main)
 
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
     const int nwork = *ntiles * ncb;
@@ -317,6 +345,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int p = perm[row0 + tid];
             t = p / k;
             v = STAGE == 2 ? topk_gate[p] : ldexpf(1.0f, xexp[t]);
+            if (FMT == 3) v *= L.glob[2 * e + (STAGE == 2 ? 1 : 0)];  // NVFP4 global scale
         }
         s_tok[tid] = t;
         s_rs[tid] = v;
@@ -356,7 +385,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     // scale entries: thread tid covers weight row tid (waves 0-1 gate, 2-3 up in GEMM1)
     {
-        const uint32_t esz = FMT == 0 ? 4u : 2u;
+        const uint32_t esz = FMT == 0 || FMT == 3 ? 4u : 2u;
         uint32_t wrow;
         if (STAGE == 1) {
             c.s_base = reinterpret_cast<const uint8_t *>(tid < 128 ? L.gsm : L.usm);
@@ -417,8 +446,8 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int row = i / 16, cc = i % 16;
             if (row < rows) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(&s_h[row * HP + cc * 8]);
-                uint4 o;
-                perm8(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
+                uint4 o = v;
+                if (FMT != 3) perm8(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
                 *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
             }
         }
@@ -779,7 +808,8 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
                                      float *y, hipStream_t s, hipEvent_t const *ev) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
-    hipLaunchKernelGGL(x_to_f16_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, x16, xexp);
+    hipLaunchKernelGGL(x_to_f16_kernel<FMT != 3>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, x16,
+                       xexp);
     const unsigned nb1 = (unsigned)(((I / 128) * tiles + 7) / 8 * 8);
     const unsigned nb2 = (unsigned)(((H / BROWS) * tiles + 7) / 8 * 8);
     launch_k(grouped_gemm_kernel<FMT, 1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
@@ -826,6 +856,7 @@ hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t 
         case 0: return launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
         case 1: return launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
         case 2: return launch_prefill_fp8(x, gate, T, k, L, g, h, z, y, s, ev);
+        case 3: return launch_prefill_fmt<3>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
         default: return hipErrorInvalidValue;
     }
 }

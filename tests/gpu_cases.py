@@ -73,4 +73,4 @@ def oracle_y(layer, x_np, idx, gate, k, tokens=None):
     n = x_np.shape[0] if tokens is None else len(tokens)
     xs = x_np if tokens is None else np.ascontiguousarray(x_np[tokens])
     return oracle.experts(layer.fmt, layer.num_experts, layer.hidden, layer.inter, *oracle.layer_np(layer),
-                          xs, idx, gate, n, k)
+                          xs, idx, gate, n, k, global_scale=oracle.layer_global(layer))

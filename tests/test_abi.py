@@ -95,7 +95,7 @@ def test_group_validation():
 
 def test_layer_validation():
     assert _decode(_layer(null="down_sm")) == _lib.ERR_INVALID_ARG
-    assert _decode(_layer(fmt=3)) == _lib.ERR_UNSUPPORTED       # unknown format
+    assert _decode(_layer(fmt=4)) == _lib.ERR_UNSUPPORTED       # unknown format
     assert _decode(_layer(H=3072)) == _lib.ERR_UNSUPPORTED       # not a power of two
     assert _decode(_layer(H=4096)) == _lib.ERR_UNSUPPORTED       # above 2048
     assert _decode(_layer(fmt=1, I=64)) == _lib.ERR_UNSUPPORTED  # not a multiple of 128
@@ -143,7 +143,7 @@ def test_forward_validation():
     assert f(ws=None) == _lib.ERR_WORKSPACE
     assert f(nb=64) == _lib.ERR_WORKSPACE
     assert f(T=0) == _lib.OK
-    assert f(layer=_layer(fmt=3)) == _lib.ERR_UNSUPPORTED
+    assert f(layer=_layer(fmt=4)) == _lib.ERR_UNSUPPORTED
     assert f(T=500, layer=_layer(I=64)) == _lib.ERR_UNSUPPORTED  # prefill path shape rules
     assert f(T=1 << 20) == _lib.ERR_UNSUPPORTED                  # prefill path 32-bit offsets
     assert f(x=FAKE + 2) == _lib.ERR_INVALID_ARG                 # misaligned activations
@@ -245,5 +245,20 @@ def test_fp8_layer_validation():
     assert _decode(_layer(fmt=2, H=64)) == _lib.ERR_UNSUPPORTED
     assert _decode(_layer(fmt=2, I=64)) == _lib.ERR_UNSUPPORTED
     assert _decode(_layer(fmt=2), T=0) == _lib.OK
-    assert _decode(_layer(fmt=3)) == _lib.ERR_UNSUPPORTED
+    assert _decode(_layer(fmt=4)) == _lib.ERR_UNSUPPORTED
     assert _decode(_layer(fmt=2), ws_bytes=16) == _lib.ERR_WORKSPACE
+
+
+def test_nvfp4_layer_validation():
+    """NVFP4 experts need their global scales (4-byte aligned)."""
+    lay = _layer(fmt=3)
+    assert _decode(lay) == _lib.ERR_INVALID_ARG          # no global scales
+    lay.global_scale = FAKE + 2
+    assert _decode(lay) == _lib.ERR_INVALID_ARG          # misaligned
+    lay.global_scale = FAKE
+    assert _decode(lay, T=0) == _lib.OK
+    assert _decode(lay, ws_bytes=16) == _lib.ERR_WORKSPACE
+    assert _decode(lay, prefill=True, ws_bytes=16) == _lib.ERR_WORKSPACE
+    lay64 = _layer(fmt=3, H=64, I=64)
+    lay64.global_scale = FAKE
+    assert _decode(lay64, prefill=True) == _lib.ERR_UNSUPPORTED   # grouped GEMMs: H % 256, I % 128
