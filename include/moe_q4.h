@@ -309,14 +309,18 @@ MOE_Q4_API int moe_q4_prefill_timed(const void *x, const int32_t *topk_idx, cons
                          void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
 
 /*
- * Shared expert for T tokens (tuned for T <= 64; the pages name no gate for
- * it, so its output is added as is):
- *   y[t] = (accumulate ? y[t] : 0) + Wd (silu(Wg x_t) * (Wu x_t))
- * as two GEMV launches that stream the int8 codes: gate and up with SwiGLU
- * (products of codes and x exact in fp32, fp32 sums, each 128-group's scale
- * applied to its partial sum) into h rounded to f16 (|h| must stay below
- * 65504), then the down GEMV (exact products of codes and f16 h, fp32 sums)
- * written to y by one thread per output (deterministic).
+ * Shared expert for T tokens (the pages name no gate for it, so its output
+ * is added as is):
+ *   y[t] = (accumulate ? y[t] : 0) + Wd (silu(Wg x_t) * (Wu x_t)).
+ * Up to 64 tokens (or H not a multiple of 256): two GEMV launches that
+ * stream the int8 codes: gate and up with SwiGLU (products of codes and x
+ * exact in fp32, fp32 sums, each 128-group's scale applied to its partial
+ * sum) into h rounded to f16 (|h| must stay below 65504), then the down GEMV
+ * (exact products of codes and f16 h, fp32 sums).  From 65 tokens: x scaled
+ * per token by a power of two into f16 (as moe_q4_prefill), then two dense
+ * f16 matrix-core GEMMs whose weights are s * q rounded once to f16; h is
+ * rounded to f16 between them.  y is written by one thread per output
+ * (deterministic).
  *   x   bf16 [T][H];  y  float [T][H], read when accumulate != 0
  *   ws  >= moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, I) bytes
  * Same conventions as the other entry points; T * H and T * I below 2^31.

@@ -142,6 +142,30 @@ int check_shared(const moe_q4_shared_expert *sx) {
     return MOE_Q4_OK;
 }
 
+// Shared expert workspace: h, plus the GEMM path's f16 activations and
+// exponents when it runs.
+bool shared_uses_gemm(int64_t T, int H) { return T >= SHARED_GEMM_MIN_T && H % 256 == 0; }
+struct SharedWs {
+    uint16_t *h;
+    uint16_t *x16;
+    int32_t *xexp;
+};
+SharedWs carve_shared(Carver &c, int64_t T, int H, int I) {
+    SharedWs w;
+    w.h = c.take<uint16_t>(T * (int64_t)I);
+    const bool gemm = shared_uses_gemm(T, H);
+    w.x16 = c.take<uint16_t>(gemm ? T * (int64_t)H : 0);
+    w.xexp = c.take<int32_t>(gemm ? T : 0);
+    return w;
+}
+hipError_t launch_shared_any(const uint16_t *x, int64_t T, const SharedPtrs &S, const SharedWs &w, float *y,
+                             bool accumulate, hipStream_t s, hipEvent_t const *ev) {
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr, e2 = ev ? ev[2] : nullptr,
+               e3 = ev ? ev[3] : nullptr;
+    if (shared_uses_gemm(T, S.H)) return launch_shared_gemm(x, T, S, w.x16, w.xexp, w.h, y, accumulate, s, e0, e1, e2, e3);
+    return launch_shared(x, T, S, w.h, y, accumulate, s, e0, e1, e2, e3);
+}
+
 SharedPtrs shared_ptrs(const moe_q4_shared_expert *sx) {
     SharedPtrs S;
     S.H = sx->hidden;
@@ -175,7 +199,7 @@ size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t
             if (forward_uses_decode(T, k)) carve_decode(c, T, E, k, H, I);
             else carve_prefill(c, T, E, k, H, I);
             break;
-        case MOE_Q4_WS_SHARED: c.take<uint16_t>(T * (int64_t)I); break;
+        case MOE_Q4_WS_SHARED: carve_shared(c, T, H, I); break;
         default: return 0;
     }
     return c.used;
@@ -325,17 +349,19 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     const LayerPtrs L = layer_ptrs(w);
     // the shared expert's h follows the forward regions
     SharedPtrs S{};
+    SharedWs sws{};
     uint16_t *hs = nullptr;
     if (sx) {
         S = shared_ptrs(sx);
         Carver cs{static_cast<char *>(ws) + need_fwd};
-        hs = cs.take<uint16_t>(T * (int64_t)sx->inter);
+        sws = carve_shared(cs, T, H, sx->inter);
+        hs = sws.h;
     }
-    const bool fuse = sx && decode_fuses_shared(L, &S);
+    const bool fuse = sx && dec && decode_fuses_shared(L, &S);
     const SharedPtrs *Sf = fuse ? &S : nullptr;
     // the shared expert on its own, after the routed experts: y += its output
     auto shared_after = [&](const uint16_t *xin_) {
-        return sx && !fuse ? hip_status(launch_shared(xin_, T, S, hs, y, true, s)) : MOE_Q4_OK;
+        return sx && !fuse ? hip_status(launch_shared_any(xin_, T, S, sws, y, true, s, nullptr)) : MOE_Q4_OK;
     };
     Carver c{static_cast<char *>(ws)};
     unsigned int *counter = c.take<unsigned int>(CONTROL_BYTES / sizeof(unsigned int));
@@ -389,8 +415,7 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
     st = hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev));
-    if (st || !sx) return st;
-    return hip_status(launch_shared(xin, T, S, hs, y, true, s));
+    return st ? st : shared_after(xin);
 }
 
 int moe_q4_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
@@ -436,11 +461,10 @@ static int run_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, 
     const size_t need = moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, I);
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
     Carver c{static_cast<char *>(ws)};
-    uint16_t *h = c.take<uint16_t>(T * (int64_t)I);
-    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
-    return hip_status(launch_shared(static_cast<const uint16_t *>(x), T, shared_ptrs(sx), h, y, accumulate != 0,
-                                    reinterpret_cast<hipStream_t>(stream), ev ? ev[0] : nullptr,
-                                    ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr));
+    const SharedWs w = carve_shared(c, T, H, I);
+    return hip_status(launch_shared_any(static_cast<const uint16_t *>(x), T, shared_ptrs(sx), w, y, accumulate != 0,
+                                        reinterpret_cast<hipStream_t>(stream),
+                                        reinterpret_cast<hipEvent_t const *>(events)));
 }
 
 int moe_q4_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y, int32_t accumulate, void *ws,

@@ -133,6 +133,13 @@ hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint
                          hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr, hipEvent_t e2 = nullptr,
                          hipEvent_t e3 = nullptr);
 hipError_t launch_dequant_int8(const SharedPtrs &S, int proj, float *out, hipStream_t s);
+// Shared expert for many tokens: dense f16 matrix-core GEMMs (x16, xexp: the
+// [T][H] f16 activations and per-token exponents, h: [T][I] f16, both
+// workspace).  Needs H % 256 == 0.
+constexpr int SHARED_GEMM_MIN_T = 65;  // token count from which the GEMMs run
+hipError_t launch_shared_gemm(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *x16, int32_t *xexp,
+                              uint16_t *h, float *y, bool accumulate, hipStream_t s, hipEvent_t e0 = nullptr,
+                              hipEvent_t e1 = nullptr, hipEvent_t e2 = nullptr, hipEvent_t e3 = nullptr);
 hipError_t launch_residual(const uint16_t *x, const float *y, int64_t n, uint16_t *out, hipStream_t s);
 
 }  // namespace moeq4

@@ -43,6 +43,7 @@
 // 3-stage ring of 64-element K-steps; each stage also carries the 256 scale
 // words of its group (one 4-byte direct-to-LDS load per thread).
 #include "moe_internal.h"
+#include "shared_dev.h"
 
 namespace moeq4 {
 
@@ -54,9 +55,10 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // ------------------------------------------------------------ x -> f16
 //
 // One wave per row: e = floor(log2 max|x|) - 14 (0 for a zero row or one
-// holding inf / NaN), x16 = f16(x * 2^-e) in PERM8 order (natural order
-// without PERM), xexp[t] = e.
-template <bool PERM>
+// holding inf / NaN), x16 = f16(x * 2^-e), xexp[t] = e.  ORDER of the
+// elements inside each group of 8: 0 natural, 1 PERM8 (0,4,1,5,2,6,3,7),
+// 2 PERM4 (0,2,1,3,4,6,5,7).
+template <int ORDER>
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restrict__ x, int64_t T, int H,
                                                        uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -92,7 +94,14 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restric
             o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
         uint32_t p[4] = {o[0], o[1], o[2], o[3]};
-        if (PERM) perm8(o[0], o[1], o[2], o[3], p[0], p[1], p[2], p[3]);
+        if (ORDER == 1) perm8(o[0], o[1], o[2], o[3], p[0], p[1], p[2], p[3]);
+        if (ORDER == 2) {
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                p[j] = (o[j] & 0xffffu) | (o[j + 1] << 16);
+                p[j + 1] = (o[j] >> 16) | (o[j + 1] & 0xffff0000u);
+            }
+        }
         dst[i] = make_uint4(p[0], p[1], p[2], p[3]);
     }
     if (lane == 0) xexp[t] = e;
@@ -777,6 +786,262 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+// ------------------------------------------------- shared expert GEMMs
+//
+// The layer's shared expert (int8 symmetric, one f16 scale per 128 input
+// weights; drama-q4 card, "What's quantized") for many tokens: the same two
+// products as the routed experts over every token, as dense GEMMs on the f16
+// matrix cores.  Tiles are 128 consecutive tokens x 256 weight rows (GEMM1:
+// the gate and up rows of 128 h columns; GEMM2: 256 output columns), 4
+// waves, the tile operand and the codes staged through a two-stage LDS ring
+// (64 code bytes per weight row and K-step, as the FP8 GEMMs).
+// Codes: the signed byte's top bit is flipped (u = q + 128) and two bytes
+// are inserted into the f16 pair (1024, 1024); subtracting 1152 leaves q
+// exactly, and one packed multiply by the row's group scale rounds s q once
+// to f16 (as the int4 path rounds its weights).  A code dword gives the pairs
+// (q0, q2) and (q1, q3), so x16 and h are kept in PERM4 order (0,2,1,3 in each
+// group of 4).  x16 is x scaled per token by a power of two (x_to_f16);
+// GEMM1 multiplies back, GEMM2 writes y (or adds into it) from the
+// accumulators, each output owned by one lane.
+
+constexpr int SG_NST = 2;
+constexpr int SG_B_BYTES = BROWS * KS;            // 16 KB: 256 rows x 64 int8 codes
+constexpr int SG_STAGE = A_BYTES + SG_B_BYTES;    // 32 KB
+constexpr int SG_B_LOADS = SG_B_BYTES / 16 / PF_BLOCK;  // 4
+constexpr int SG_HP = 128 + 8;
+constexpr int SG_RING = SG_NST * SG_STAGE > BM * SG_HP * 2 ? SG_NST * SG_STAGE : BM * SG_HP * 2;
+
+struct SGemmCtx {
+    const uint8_t *a_base;
+    uint32_t a_off[4];
+    const uint8_t *b_base[SG_B_LOADS];
+    uint32_t b_off[SG_B_LOADS];
+    const uint16_t *srow[2];  // this lane's two weight rows' group scales
+    uint8_t *ring;
+    int brow[2];
+    int nk;
+};
+
+template <int MS>
+__device__ __forceinline__ void sg_issue(const SGemmCtx &c, int ks, int slot, int wave) {
+    uint8_t *sa = c.ring + slot * SG_STAGE;
+    uint8_t *sb = sa + A_BYTES;
+    const uint8_t *ab = c.a_base + (size_t)ks * (KS * 2);
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+        __builtin_amdgcn_global_load_lds((const void *)(ab + c.a_off[i]),
+                                         (__attribute__((address_space(3))) void *)(sa + (i * 4 + wave) * 1024),
+                                         16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < SG_B_LOADS; ++i)
+        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * KS) + c.b_off[i]),
+                                         (__attribute__((address_space(3))) void *)(sb + (i * 4 + wave) * 1024),
+                                         16, 0, 0);
+}
+
+// four int8 codes of a dword (top bits flipped) as f16 pairs (q0, q2), (q1, q3)
+// times the scale pair
+__device__ __forceinline__ uint2 sg_codes(uint32_t w, uint32_t kf, half2_t sc) {
+    const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t u = w ^ 0x80808080u;
+    const half2_t a = __builtin_bit_cast(half2_t, insert_codes<0x00ff00ffu>(u, kf)) - off;
+    const half2_t b = __builtin_bit_cast(half2_t, insert_codes<0x00ff00ffu>(u >> 8, kf)) - off;
+    return make_uint2(__builtin_bit_cast(uint32_t, a * sc), __builtin_bit_cast(uint32_t, b * sc));
+}
+
+template <int MS>
+__device__ __forceinline__ void sg_main(const SGemmCtx &c, f32x16_t (&acc)[4][2], int wave, int lane) {
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int NK = c.nk;
+    const uint32_t kf = opaque_magic(MAGIC_F16);
+    sg_issue<MS>(c, 0, 0, wave);
+    half2_t sc[2];
+    uint32_t snext[2] = {(uint32_t)c.srow[0][0], (uint32_t)c.srow[1][0]};
+    for (int kk = 0; kk < NK; kk += SG_NST) {
+#pragma unroll
+        for (int u = 0; u < SG_NST; ++u) {
+            const int ks = kk + u;
+            if (ks < NK) {
+                MOEQ4_WAIT_VM_LDS(0);  // stage ks has landed (only it was in flight)
+                lds_barrier();
+                if (ks + 1 < NK) sg_issue<MS>(c, ks + 1, (u + 1) % SG_NST, wave);
+                if ((ks & 1) == 0) {  // a new group of 128 inputs
+                    const int kg = ks >> 1;
+#pragma unroll
+                    for (int ns = 0; ns < 2; ++ns) {
+                        sc[ns] = __builtin_bit_cast(half2_t, snext[ns] * 0x10001u);
+                        if (2 * (kg + 1) < NK) snext[ns] = (uint32_t)c.srow[ns][kg + 1];
+                    }
+                }
+                const uint8_t *sa = c.ring + u * SG_STAGE;
+                const uint8_t *sbp = sa + A_BYTES;
+                uint4 bw[2][2];
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) {
+                    const int rb = c.brow[ns];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        bw[ns][t] = *reinterpret_cast<const uint4 *>(sbp + rb * 64 + 16 * ((2 * hf + t) ^ ((rb >> 2) & 3)));
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    u32x4_t bv[2];
+#pragma unroll
+                    for (int ns = 0; ns < 2; ++ns) {
+                        const uint4 v = bw[ns][s >> 1];
+                        const uint32_t d0 = (s & 1) ? v.z : v.x, d1 = (s & 1) ? v.w : v.y;
+                        const uint2 p0 = sg_codes(d0, kf, sc[ns]), p1 = sg_codes(d1, kf, sc[ns]);
+                        bv[ns] = u32x4_t{p0.x, p0.y, p1.x, p1.y};
+                    }
+                    const int ch = 4 * hf + s;
+#pragma unroll
+                    for (int mi = 0; mi < MS; ++mi) {
+                        const int r = 32 * mi + l32;
+                        const uint4 av = *reinterpret_cast<const uint4 *>(sa + r * 128 + 16 * (ch ^ ((r >> 1) & 7)));
+                        const f16x8_t a8 = __builtin_bit_cast(f16x8_t, u32x4_t{av.x, av.y, av.z, av.w});
+#pragma unroll
+                        for (int ns = 0; ns < 2; ++ns)
+                            acc[mi][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                a8, __builtin_bit_cast(f16x8_t, bv[ns]), acc[mi][ns], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// STAGE 1: A = x16 rows (PERM4), B = gate | up codes, epilogue * 2^e, SwiGLU
+//          -> h (f16, PERM4).
+// STAGE 2: A = h rows, B = down codes, epilogue y = (accumulate ? y : 0) + acc.
+template <int STAGE>
+__global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_gemm_kernel(
+    const uint16_t *__restrict__ act, const int32_t *__restrict__ xexp, int T, int H, int I, SharedPtrs S,
+    uint16_t *__restrict__ h_out, float *__restrict__ y, int accumulate) {
+    const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
+    const int ntiles = (T + BM - 1) / BM;
+    const int nwork = ntiles * ncb;
+    const int per = (nwork + 7) / 8;
+    const int bx = blockIdx.x;
+    if (bx / 8 >= per) return;
+    const int w = (bx % 8) * per + bx / 8;
+    if (w >= nwork) return;
+    const int j = w / ncb, cb = w % ncb;
+    const int row0 = j * BM, rows = T - row0 < BM ? T - row0 : BM;
+    const int K = STAGE == 1 ? H : I;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
+
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring[SG_RING];
+    SGemmCtx c;
+    c.ring = s_ring;
+    c.nk = K / KS;
+    c.a_base = reinterpret_cast<const uint8_t *>(act);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 32 * i + 8 * wave + (lane >> 3);
+        const int ch = (lane & 7) ^ ((r >> 1) & 7);
+        const int rr = r < rows ? r : 0;  // padding rows read row 0; their outputs are dropped
+        c.a_off[i] = ((uint32_t)(row0 + rr) * (uint32_t)K + 8u * ch) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < SG_B_LOADS; ++i) {
+        const int S_ = (i * 4 + wave) * 64 + lane;
+        const int rb = S_ / 4, ch = (S_ % 4) ^ ((rb >> 2) & 3);
+        uint32_t wrow;
+        if (STAGE == 1) {
+            c.b_base[i] = reinterpret_cast<const uint8_t *>(i < 2 ? S.gq : S.uq);
+            wrow = (uint32_t)col_base + (rb & 127);
+        } else {
+            c.b_base[i] = reinterpret_cast<const uint8_t *>(S.dq);
+            wrow = (uint32_t)col_base + rb;
+        }
+        c.b_off[i] = wrow * (uint32_t)K + 16u * ch;
+    }
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+        c.brow[ns] = STAGE == 1 ? ns * 128 + wave * 32 + l32 : wave * 64 + ns * 32 + l32;
+        const int wrow = STAGE == 1 ? col_base + wave * 32 + l32 : col_base + c.brow[ns];
+        const uint16_t *sb = STAGE == 1 ? (ns == 0 ? S.gs : S.us) : S.ds;
+        c.srow[ns] = sb + (size_t)wrow * (K / 128);
+    }
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ns][r] = 0.f;
+    const int msub = (rows + 31) / 32;
+    switch (msub) {
+        case 1: sg_main<1>(c, acc, wave, lane); break;
+        case 2: sg_main<2>(c, acc, wave, lane); break;
+        case 3: sg_main<3>(c, acc, wave, lane); break;
+        default: sg_main<4>(c, acc, wave, lane); break;
+    }
+    __syncthreads();  // ring no longer read
+
+    if (STAGE == 1) {
+        uint16_t *s_h = reinterpret_cast<uint16_t *>(s_ring);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi < msub) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+                    const float sc = row < rows ? ldexpf(1.0f, xexp[row0 + row]) : 0.f;
+                    const _Float16 hv = (_Float16)(silu(acc[mi][0][r] * sc) * (acc[mi][1][r] * sc));
+                    s_h[row * SG_HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
+                }
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < BM * 16; i += PF_BLOCK) {
+            const int row = i / 16, cc = i % 16;
+            if (row < rows) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(&s_h[row * SG_HP + cc * 8]);
+                const uint4 o = make_uint4((v.x & 0xffffu) | (v.y << 16), (v.x >> 16) | (v.y & 0xffff0000u),
+                                           (v.z & 0xffffu) | (v.w << 16), (v.z >> 16) | (v.w & 0xffff0000u));
+                *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi < msub) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+                    if (row < rows) {
+#pragma unroll
+                        for (int ns = 0; ns < 2; ++ns) {
+                            float *dst = y + (size_t)(row0 + row) * H + col_base + wave * 64 + ns * 32 + l32;
+                            *dst = accumulate ? *dst + acc[mi][ns][r] : acc[mi][ns][r];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_shared_gemm(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *x16, int32_t *xexp,
+                              uint16_t *h, float *y, bool accumulate, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                              hipEvent_t e2, hipEvent_t e3) {
+    const int H = S.H, I = S.I;
+    const int64_t ntiles = (T + BM - 1) / BM;
+    hipLaunchKernelGGL(x_to_f16_kernel<2>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, x16, xexp);
+    const unsigned nb1 = (unsigned)(((I / 128) * ntiles + 7) / 8 * 8);
+    const unsigned nb2 = (unsigned)(((H / BROWS) * ntiles + 7) / 8 * 8);
+    launch_k(shared_gemm_kernel<1>, dim3(nb1), dim3(PF_BLOCK), s, e0, e1, (const uint16_t *)x16,
+             (const int32_t *)xexp, (int)T, H, I, S, h, y, accumulate ? 1 : 0);
+    launch_k(shared_gemm_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, e2, e3, (const uint16_t *)h, (const int32_t *)xexp,
+             (int)T, H, I, S, h, y, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
 // y[t] = sum over the token's k routed rows of z (fp32).  One workgroup of
 // 256 threads per token, 8 columns per thread and pass.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ z, const int32_t *__restrict__ inv,
@@ -808,8 +1073,8 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
                                      float *y, hipStream_t s, hipEvent_t const *ev) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
-    hipLaunchKernelGGL(x_to_f16_kernel<FMT != 3>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, x16,
-                       xexp);
+    hipLaunchKernelGGL(x_to_f16_kernel<FMT == 3 ? 0 : 1>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H,
+                       x16, xexp);
     const unsigned nb1 = (unsigned)(((I / 128) * tiles + 7) / 8 * 8);
     const unsigned nb2 = (unsigned)(((H / BROWS) * tiles + 7) / 8 * 8);
     launch_k(grouped_gemm_kernel<FMT, 1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,

@@ -244,3 +244,16 @@ def test_forward_without_shared_unchanged():
     ir, yr = oracle_layer_shared(lay, None, np_u16(case.x), k, router_w=case.router_w)
     assert_close(y1.cpu().numpy(), yr, "forward_ex without shared")
     assert_close(y2.cpu().numpy(), yr, "forward")
+
+
+@pytest.mark.parametrize("T", [64, 65, 300])
+def test_shared_gemv_gemm_threshold(T):
+    """64 tokens take the GEMVs, 65 and more the matrix-core GEMMs (a ragged
+    last tile at 65 and 300); both against the oracle, with accumulate."""
+    sx = recipe_shared()
+    x = synth.bf16_bits(synth.normal((T, 2048), 1.0, 2, f"shared/thr/{T}", "cuda"))
+    y0 = synth.normal((T, 2048), 0.05, 2, f"shared/thr/y/{T}", "cuda")
+    y = hip_shared(sx, x, y=y0.clone(), accumulate=True)
+    ref = oracle.shared(2048, 512, *host(sx), np_u16(x), T, y_in=y0.cpu().numpy())
+    r, a = assert_close(y.cpu().numpy(), ref, f"shared threshold T={T}")
+    say(f"[shared] T={T} accumulate: rel L2 {r:.2e}, max abs {a:.2e}")
