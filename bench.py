@@ -28,6 +28,9 @@ Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
   shared        the shared expert alone (moe_q4_shared) for the frame's 16
                 tokens; steps rotate over 200 address-distinct copies (3 MB
                 each) so its codes are read from HBM.
+  shared_prefill
+                the shared expert alone for the long prompt's 4096 tokens
+                (matrix-core GEMMs).
 
 One JSON line on stdout: value = tokens/s of whole steps (inputs resident in
 HBM), roofline of the dominant kernel measured with HIP events recorded on the
@@ -54,6 +57,7 @@ WORKLOADS = {
     "decode_shared": 2, "frame_shared": 4, "shared": 4, "decode_fp8": 2, "frame_fp8": 4,
     "prefill_fp8": 3, "long_prefill_fp8": 5,
     "decode_nvfp4": 2, "frame_nvfp4": 4, "prefill_nvfp4": 3, "long_prefill_nvfp4": 5,
+    "shared_prefill": 5,
 }
 SHARED_INTER = 512   # the shared expert's inner size (that of a routed expert)
 SHARED_COPIES = 200  # address-distinct shared experts of the "shared" workload
@@ -181,13 +185,13 @@ def main():
                 "long_prefill": (20, 3), "decode_shared": (400, 40), "frame_shared": (10, 2), "shared": (400, 40),
                 "decode_fp8": (400, 40), "frame_fp8": (10, 2), "prefill_fp8": (50, 5), "long_prefill_fp8": (20, 3),
                 "decode_nvfp4": (400, 40), "frame_nvfp4": (10, 2), "prefill_nvfp4": (50, 5),
-                "long_prefill_nvfp4": (20, 3)}
+                "long_prefill_nvfp4": (20, 3), "shared_prefill": (50, 5)}
     K = args.steps if args.steps is not None else defaults[args.workload][0]
     W = args.warmup if args.warmup is not None else defaults[args.workload][1]
 
     t0 = time.time()
-    only_shared = args.workload == "shared"
-    with_shared = args.workload in ("decode_shared", "frame_shared", "shared")
+    only_shared = args.workload in ("shared", "shared_prefill")
+    with_shared = args.workload in ("decode_shared", "frame_shared", "shared", "shared_prefill")
     fp8 = args.workload.endswith("_fp8")
     nvfp4 = args.workload.endswith("_nvfp4")
     case = synth.make_case(cfg, device="cuda", layers=1 if only_shared else None,
@@ -199,6 +203,7 @@ def main():
                "long_prefill_fp8": "long_prefill", "decode_nvfp4": "decode", "frame_nvfp4": "frame",
                "prefill_nvfp4": "prefill", "long_prefill_nvfp4": "long_prefill"}.get(args.workload, args.workload)
     decode_path = base_wl in ("tiny", "decode", "frame", "shared")
+    shared_gemm = args.workload == "shared_prefill"
     mode = "decode" if decode_path else "prefill"
 
     # ---- per-step units of work ------------------------------------------------
@@ -333,7 +338,15 @@ def main():
     proj_bytes = expert_bytes(lay0) // 3        # one projection of one expert (codes + scales)
     P = T * k
     sx_bytes = shared_gateup_bytes(shareds[0]) + T * SHARED_INTER * 2 if with_shared else 0
-    if only_shared:
+    if shared_gemm:
+        # dominant kernel: the shared gate/up GEMM + SwiGLU on the matrix cores
+        dom = "shared_gemm_kernel<1> (gate/up f16 GEMM + SwiGLU)"
+        flops = 2.0 * T * H * (2 * SHARED_INTER)
+        achieved = flops / (stage_avg[0] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_flops": flops}
+    elif only_shared:
         # dominant kernel: the shared gate/up GEMV + SwiGLU: its int8 codes and
         # scales once, the activations, h (f16) out
         dom = "shared_gateup_kernel"
@@ -405,6 +418,8 @@ def main():
     names["frame_nvfp4"] = names["frame"].replace("int4 asym g64 (RTN)", nv)
     names["prefill_nvfp4"] = names["prefill"].replace("int4 asym g64", nv)
     names["long_prefill_nvfp4"] = names["long_prefill"].replace("int4 sym g128", nv)
+    names["shared_prefill"] = (f"shared expert alone: 4096 tokens, H=2048, I={SHARED_INTER}, int8 sym g128, "
+                               "matrix-core GEMMs")
     names["shared"] = (f"shared expert alone: 16 tokens, H=2048, I={SHARED_INTER}, int8 sym g128; "
                        f"{SHARED_COPIES} address-distinct copies rotated")
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,

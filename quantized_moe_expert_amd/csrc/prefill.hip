@@ -916,9 +916,9 @@ __device__ __forceinline__ void sg_main(const SGemmCtx &c, f32x16_t (&acc)[4][2]
 template <int STAGE>
 __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_gemm_kernel(
     const uint16_t *__restrict__ act, const int32_t *__restrict__ xexp, int T, int H, int I, SharedPtrs S,
-    uint16_t *__restrict__ h_out, float *__restrict__ y, int accumulate) {
+    uint16_t *__restrict__ h_out, float *__restrict__ y, int accumulate, int tile_rows) {
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
-    const int ntiles = (T + BM - 1) / BM;
+    const int ntiles = (T + tile_rows - 1) / tile_rows;
     const int nwork = ntiles * ncb;
     const int per = (nwork + 7) / 8;
     const int bx = blockIdx.x;
@@ -926,7 +926,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int w = (bx % 8) * per + bx / 8;
     if (w >= nwork) return;
     const int j = w / ncb, cb = w % ncb;
-    const int row0 = j * BM, rows = T - row0 < BM ? T - row0 : BM;
+    const int row0 = j * tile_rows, rows = T - row0 < tile_rows ? T - row0 : tile_rows;
     const int K = STAGE == 1 ? H : I;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1027,18 +1027,28 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+// Token rows per tile: the largest of 128, 64, 32 that still gives
+// SG_MIN_WORK work items (more, shorter tiles fill the chip when the
+// products are small; the codes they re-read come from L2).
+constexpr int SG_MIN_WORK = 512;
+static int sg_tile_rows(int64_t T, int ncb) {
+    for (int tr = BM; tr > 32; tr /= 2)
+        if ((T + tr - 1) / tr * ncb >= SG_MIN_WORK) return tr;
+    return 32;
+}
+
 hipError_t launch_shared_gemm(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *x16, int32_t *xexp,
                               uint16_t *h, float *y, bool accumulate, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
                               hipEvent_t e2, hipEvent_t e3) {
     const int H = S.H, I = S.I;
-    const int64_t ntiles = (T + BM - 1) / BM;
     hipLaunchKernelGGL(x_to_f16_kernel<2>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, x16, xexp);
-    const unsigned nb1 = (unsigned)(((I / 128) * ntiles + 7) / 8 * 8);
-    const unsigned nb2 = (unsigned)(((H / BROWS) * ntiles + 7) / 8 * 8);
+    const int tr1 = sg_tile_rows(T, I / 128), tr2 = sg_tile_rows(T, H / BROWS);
+    const unsigned nb1 = (unsigned)(((I / 128) * ((T + tr1 - 1) / tr1) + 7) / 8 * 8);
+    const unsigned nb2 = (unsigned)(((H / BROWS) * ((T + tr2 - 1) / tr2) + 7) / 8 * 8);
     launch_k(shared_gemm_kernel<1>, dim3(nb1), dim3(PF_BLOCK), s, e0, e1, (const uint16_t *)x16,
-             (const int32_t *)xexp, (int)T, H, I, S, h, y, accumulate ? 1 : 0);
+             (const int32_t *)xexp, (int)T, H, I, S, h, y, accumulate ? 1 : 0, tr1);
     launch_k(shared_gemm_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, e2, e3, (const uint16_t *)h, (const int32_t *)xexp,
-             (int)T, H, I, S, h, y, accumulate ? 1 : 0);
+             (int)T, H, I, S, h, y, accumulate ? 1 : 0, tr2);
     return hipGetLastError();
 }
 
