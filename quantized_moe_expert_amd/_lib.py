@@ -25,7 +25,8 @@ EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_deco
            "moe_q4_decode_timed", "moe_q4_prefill_timed", "moe_q4_forward", "moe_q4_forward_timed",
            "moe_q4_workspace_init",
            "moe_q4_shared", "moe_q4_shared_timed", "moe_q4_dequant_int8", "moe_q4_forward_ex",
-           "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string")
+           "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string",
+           "moe_q4_prefill_pack_size", "moe_q4_prefill_pack")
 STAGE_EVENTS = 4
 
 
@@ -41,7 +42,7 @@ class Layer(ctypes.Structure):
                 ("format", ctypes.c_int32),
                 ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
                 ("gate_sm", ctypes.c_void_p), ("up_sm", ctypes.c_void_p), ("down_sm", ctypes.c_void_p),
-                ("global_scale", ctypes.c_void_p)]
+                ("global_scale", ctypes.c_void_p), ("prefill_pack", ctypes.c_void_p)]
 
 
 class SharedExpert(ctypes.Structure):
@@ -99,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.moe_q4_dequant_int8.argtypes = [ctypes.POINTER(SharedExpert), i32, P, P]
         L.moe_q4_residual_bf16.restype = ctypes.c_int
         L.moe_q4_residual_bf16.argtypes = [P, P, i64, P, P]
+        L.moe_q4_prefill_pack_size.restype = sz
+        L.moe_q4_prefill_pack_size.argtypes = [ctypes.POINTER(Layer)]
+        L.moe_q4_prefill_pack.restype = ctypes.c_int
+        L.moe_q4_prefill_pack.argtypes = [ctypes.POINTER(Layer), P, sz, P]
         L.moe_q4_error_string.restype = ctypes.c_char_p
         L.moe_q4_error_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -136,16 +141,17 @@ def _check(fn: str, status: int):
         raise MoeQ4Error(fn, status)
 
 
-def layer_struct(layer) -> Layer:
+def layer_struct(layer, pack=None) -> Layer:
     """struct moe_q4_layer from an object with num_experts, hidden, inter, fmt
-    (or format) and the six gate/up/down code and scale tensors."""
+    (or format) and the six gate/up/down code and scale tensors; ``pack``:
+    the layer's prefill copy (uint8 device tensor from prefill_pack) or None."""
     fmt = getattr(layer, "fmt", None)
     if fmt is None:
         fmt = layer.format
     return Layer(int(layer.num_experts), int(layer.hidden), int(layer.inter), int(fmt),
                  _ptr(layer.gate_q), _ptr(layer.up_q), _ptr(layer.down_q),
                  _ptr(layer.gate_sm), _ptr(layer.up_sm), _ptr(layer.down_sm),
-                 _ptr(getattr(layer, "global_scale", None)))
+                 _ptr(getattr(layer, "global_scale", None)), _ptr(pack))
 
 
 def shared_struct(sx) -> SharedExpert:
@@ -256,6 +262,31 @@ def moe_q4_workspace_init(ws, stream=None):
 def moe_q4_dequant(layer, expert, proj, out, stream=None):
     st = layer_struct(layer) if not isinstance(layer, Layer) else layer
     _check("moe_q4_dequant", lib().moe_q4_dequant(ctypes.byref(st), expert, proj, _ptr(out), _stream(stream)))
+
+
+def moe_q4_prefill_pack_size(layer) -> int:
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    return int(lib().moe_q4_prefill_pack_size(ctypes.byref(st)))
+
+
+def moe_q4_prefill_pack(layer, dst, stream=None):
+    """Writes the layer's prefill copy into ``dst`` (uint8 device tensor of at
+    least moe_q4_prefill_pack_size bytes, 256-byte aligned)."""
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    nb = 0 if dst is None else dst.numel() * dst.element_size()
+    _check("moe_q4_prefill_pack", lib().moe_q4_prefill_pack(ctypes.byref(st), _ptr(dst), nb, _stream(stream)))
+
+
+def prefill_pack(layer, device="cuda", stream=None):
+    """Allocates and fills the layer's prefill copy; returns the uint8 tensor
+    (pass it to layer_struct(layer, pack=...))."""
+    import torch
+    n = moe_q4_prefill_pack_size(layer)
+    if n == 0:
+        raise MoeQ4Error("moe_q4_prefill_pack_size", -2)
+    dst = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_q4_prefill_pack(layer, dst, stream)
+    return dst
 
 
 def moe_q4_residual_bf16(x, y, n, out, stream=None):

@@ -58,6 +58,8 @@ int check_layer(const moe_q4_layer *w, bool prefill) {
     if (!pow2_between(w->hidden, 64, 2048) || !pow2_between(w->inter, 64, 2048)) return MOE_Q4_ERR_UNSUPPORTED;
     if (w->hidden % G || w->inter % G) return MOE_Q4_ERR_UNSUPPORTED;
     if (prefill && (w->inter % 128 || w->hidden % 256)) return MOE_Q4_ERR_UNSUPPORTED;
+    if (w->prefill_pack && w->format == MOE_Q4_FP8_B128) return MOE_Q4_ERR_UNSUPPORTED;
+    if (!aligned(w->prefill_pack, 256)) return MOE_Q4_ERR_INVALID_ARG;
     return MOE_Q4_OK;
 }
 
@@ -74,6 +76,7 @@ LayerPtrs layer_ptrs(const moe_q4_layer *w) {
     L.usm = w->up_sm;
     L.dsm = w->down_sm;
     L.glob = w->format == MOE_Q4_NVFP4 ? w->global_scale : nullptr;
+    L.pack = static_cast<const uint8_t *>(w->prefill_pack);
     return L;
 }
 
@@ -447,6 +450,34 @@ int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *o
     if (st) return st;
     if (!out || expert < 0 || expert >= w->num_experts || proj < 0 || proj > 2) return MOE_Q4_ERR_INVALID_ARG;
     return hip_status(launch_dequant(layer_ptrs(w), expert, proj, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// The prefill copy is made from the canonical arrays; the field that would
+// point to a copy is not read here.
+static int check_pack_source(const moe_q4_layer *w, moe_q4_layer *plain) {
+    if (!w) return MOE_Q4_ERR_INVALID_ARG;
+    *plain = *w;
+    plain->prefill_pack = nullptr;
+    int st = check_layer(plain, true);
+    if (st) return st;
+    if (plain->format == MOE_Q4_FP8_B128) return MOE_Q4_ERR_UNSUPPORTED;
+    return MOE_Q4_OK;
+}
+
+size_t moe_q4_prefill_pack_size(const moe_q4_layer *w) {
+    moe_q4_layer plain;
+    if (check_pack_source(w, &plain)) return 0;
+    return pack_layout(plain.num_experts, plain.hidden, plain.inter).total;
+}
+
+int moe_q4_prefill_pack(const moe_q4_layer *w, void *dst, size_t dst_bytes, moe_q4_stream stream) {
+    moe_q4_layer plain;
+    int st = check_pack_source(w, &plain);
+    if (st) return st;
+    if (!dst || !aligned(dst, 256) || dst_bytes < pack_layout(plain.num_experts, plain.hidden, plain.inter).total)
+        return MOE_Q4_ERR_INVALID_ARG;
+    return hip_status(
+        launch_prefill_pack(layer_ptrs(&plain), static_cast<uint8_t *>(dst), reinterpret_cast<hipStream_t>(stream)));
 }
 
 static int run_shared(const void *x, int64_t T, const moe_q4_shared_expert *sx, float *y, int32_t accumulate,

@@ -31,7 +31,18 @@ struct LayerPtrs {
     const uint8_t *gq, *uq, *dq;
     const uint16_t *gsm, *usm, *dsm;
     const float *glob;  // NVFP4 global scales [E][2] = {gate and up, down}
+    const uint8_t *pack;  // prefill copy (tiles of 256 weight rows per K-step) or null
 };
+
+// Byte offsets of the prefill copy's regions: gate|up codes, gate|up scale
+// words, down codes, down scale words, and its size.
+struct PackLayout {
+    size_t gu_q, gu_s, d_q, d_s, total;
+};
+__host__ __device__ inline PackLayout pack_layout(int E, int H, int I) {
+    const size_t eih = (size_t)E * I * H;
+    return PackLayout{0, eih, eih + eih / 8, eih + eih / 8 + eih / 2, eih + eih / 8 + eih / 2 + eih / 16};
+}
 
 constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chunk
 constexpr int GROUP_SINGLE_MAX = 1024;   // pairs handled by the one-block grouping
@@ -125,6 +136,8 @@ inline void launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t 
 }
 
 hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, hipStream_t s);
+// Writes the prefill copy of L's codes and scales (int4 formats, NVFP4) to dst.
+hipError_t launch_prefill_pack(const LayerPtrs &L, uint8_t *dst, hipStream_t s);
 
 // Shared expert (int8 symmetric group 128) for few tokens: gate/up + SwiGLU
 // -> h (f16 [T][I] workspace), then down -> y = (accumulate ? y : 0) + o.

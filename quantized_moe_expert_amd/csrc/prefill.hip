@@ -147,6 +147,27 @@ constexpr int S_BYTES = BROWS * 4;              // 1 KB: one scale word per weig
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
 constexpr int B_LOADS = B_BYTES / 16 / PF_BLOCK;  // 2 sixteen-byte loads per thread and stage
 
+// The ring holds NST full stages; a tile with fewer 32-row subtiles uses
+// shorter stages (A takes 4 KB per subtile) and so fits more of them in the
+// same bytes, which keeps more K-steps in flight for small tiles.
+template <int MS>
+constexpr int stage_bytes() { return MS * (A_BYTES / 4) + B_BYTES + S_BYTES; }
+template <int MS>
+constexpr int ring_depth() { return (NST * STAGE_BYTES) / stage_bytes<MS>() > 6 ? 6 : (NST * STAGE_BYTES) / stage_bytes<MS>(); }
+
+// Wait until at most n stages of LPS loads each are in flight (n <= 4; the
+// count must be an immediate).
+template <int LPS>
+__device__ __forceinline__ void wait_stages(int n) {
+    switch (n) {
+        case 0: MOEQ4_WAIT_VM_LDS(0); break;
+        case 1: MOEQ4_WAIT_VM_LDS(LPS); break;
+        case 2: MOEQ4_WAIT_VM_LDS(2 * LPS); break;
+        case 3: MOEQ4_WAIT_VM_LDS(3 * LPS); break;
+        default: MOEQ4_WAIT_VM_LDS(4 * LPS); break;
+    }
+}
+
 // Per-block operand sources used by the main loop.  Sources are a base that
 // is uniform over the wave plus a 32-bit per-thread byte offset.
 struct GemmCtx {
@@ -154,9 +175,11 @@ struct GemmCtx {
     uint32_t a_off[4];               // A chunk of each 32-row subtile
     const uint8_t *b_base[B_LOADS];
     uint32_t b_off[B_LOADS];
+    uint32_t b_kstep;                // bytes between K-steps of a weight row chunk
     const uint8_t *s_base;
     uint32_t s_off;                  // scale entry of group 0 of weight row `tid`
-    uint32_t s_step;                 // bytes between groups: 4 (scale+min) or 2 (scale)
+    uint32_t s_step;                 // bytes between groups: 4 (scale+min) or 2 (scale); 0 in the copy
+    uint32_t s_kstep;                // bytes between K-steps: 0, or 1 KB in the copy
     uint8_t *ring;
     int brow[2];                     // this lane's weight rows (block-local) of the two N-subtiles
     uint32_t spar[2];                // sym: parity of the scale entry of group 0 of brow[ns]
@@ -177,8 +200,8 @@ __device__ __forceinline__ void lds_barrier() {
 // the dword holding weight row tid's scale entry of group g, all lane-ordered.
 template <int MS>
 __device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int slot, int wave) {
-    uint8_t *sa = c.ring + slot * STAGE_BYTES;
-    uint8_t *sb = sa + A_BYTES;
+    uint8_t *sa = c.ring + slot * stage_bytes<MS>();
+    uint8_t *sb = sa + MS * (A_BYTES / 4);
     uint8_t *ss = sb + B_BYTES;
     const uint8_t *ab = c.a_base + (size_t)ks * (KS * 2);  // uniform part of the addresses
 #pragma unroll
@@ -188,10 +211,11 @@ __device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int
                                          16, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * (KS / 2)) + c.b_off[i]),
+        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * c.b_kstep) + c.b_off[i]),
                                          (__attribute__((address_space(3))) void *)(sb + (i * 4 + wave) * 1024),
                                          16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void *)(c.s_base + ((c.s_off + (uint32_t)g * c.s_step) & ~3u)),
+    __builtin_amdgcn_global_load_lds(
+        (const void *)(c.s_base + ((c.s_off + (uint32_t)ks * c.s_kstep + (uint32_t)g * c.s_step) & ~3u)),
                                      (__attribute__((address_space(3))) void *)(ss + wave * 256), 4, 0, 0);
 }
 
@@ -203,11 +227,13 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
     constexpr int G = FMT == 0 || FMT == 3 ? 64 : 128;
     constexpr int KPG = G / KS;
     constexpr int LPS = MS + B_LOADS + 1;  // loads per thread and stage
+    constexpr int D = ring_depth<MS>();    // stages in the ring for this tile height
+    static_assert(D >= 3 && (D - 2) * LPS <= 63, "wait counts fit vmcnt");
     const int l32 = lane & 31, hf = lane >> 5;
     const int NK = c.nk;
 
 #pragma unroll
-    for (int u = 0; u < NST - 1; ++u)
+    for (int u = 0; u < D - 1; ++u)
         if (u < NK) issue_stage<MS>(c, u, u / KPG, u, wave);
 
     // per N-subtile: scale and min of the current group, for the 1024 + q
@@ -218,18 +244,17 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
     const half2_t off0 = {(_Float16)(FMT == 0 ? 1024.0f : 1032.0f), (_Float16)(FMT == 0 ? 1024.0f : 1032.0f)};
     const half2_t off1 = {(_Float16)(FMT == 0 ? 1024.0f : 1152.0f), (_Float16)(FMT == 0 ? 1024.0f : 1152.0f)};
     const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    for (int kk = 0; kk < NK; kk += NST) {
+    for (int kk = 0; kk < NK; kk += D) {
 #pragma unroll
-        for (int u = 0; u < NST; ++u) {
+        for (int u = 0; u < D; ++u) {
             const int ks = kk + u;
             if (ks < NK) {
-                // K-step ks has landed once at most the next one is in flight
-                if (ks + 1 < NK) MOEQ4_WAIT_VM_LDS(LPS);
-                else MOEQ4_WAIT_VM_LDS(0);
-                lds_barrier();  // every wave's share of ks is in LDS; slot (u + NST - 1) % NST is free
-                if (ks + NST - 1 < NK) issue_stage<MS>(c, ks + NST - 1, (ks + NST - 1) / KPG, (u + NST - 1) % NST, wave);
-                const uint8_t *sa = c.ring + u * STAGE_BYTES;
-                const uint8_t *sb = sa + A_BYTES;
+                // K-step ks has landed once only the stages issued after it are in flight
+                wait_stages<LPS>(NK - 1 - ks < D - 2 ? NK - 1 - ks : D - 2);
+                lds_barrier();  // every wave's share of ks is in LDS; slot (u + D - 1) % D is free
+                if (ks + D - 1 < NK) issue_stage<MS>(c, ks + D - 1, (ks + D - 1) / KPG, (u + D - 1) % D, wave);
+                const uint8_t *sa = c.ring + u * stage_bytes<MS>();
+                const uint8_t *sb = sa + MS * (A_BYTES / 4);
                 const uint32_t *ss = reinterpret_cast<const uint32_t *>(sb + B_BYTES);
                 if (FMT == 3) {
 #pragma unroll
@@ -405,6 +430,25 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         c.s_off = wrow * (uint32_t)NG * esz;
         c.s_step = esz;
+    }
+    c.b_kstep = KS / 2;
+    c.s_kstep = 0;
+    if (L.pack) {
+        // prefill copy: per K-step, tile (e, cb) holds its 256 rows' chunks in
+        // slot order (8 KB) and their scale words in row order (1 KB)
+        const PackLayout pl = pack_layout(L.E, H, I);
+        const size_t tile = (size_t)e * ncb + cb;
+        const uint8_t *q = L.pack + (STAGE == 1 ? pl.gu_q : pl.d_q) + tile * (size_t)c.nk * B_BYTES;
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) {
+            c.b_base[i] = q;
+            c.b_off[i] = 16u * (uint32_t)((i * 4 + wave) * 64 + lane);
+        }
+        c.b_kstep = B_BYTES;
+        c.s_base = L.pack + (STAGE == 1 ? pl.gu_s : pl.d_s) + tile * (size_t)c.nk * S_BYTES;
+        c.s_off = 4u * (uint32_t)tid;
+        c.s_step = 0;
+        c.s_kstep = S_BYTES;
     }
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
@@ -1075,6 +1119,85 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         dst[0] = make_float4(s[0], s[1], s[2], s[3]);
         dst[1] = make_float4(s[4], s[5], s[6], s[7]);
     }
+}
+
+// ------------------------------------------------------- prefill copy
+//
+// Gather of the canonical codes and scale words into the GEMMs' tile order
+// (the layout is stated with moe_q4_prefill_pack in the public header).
+// Codes: one thread per 16-byte chunk of the copy; slot S of a K-step holds
+// chunk (S % 2) ^ ((row >> 3) & 1) of row S / 2, the order in which the
+// GEMM's direct-to-LDS loads place them.
+template <int STAGE>
+__global__ __launch_bounds__(256) void pack_codes_kernel(LayerPtrs L, uint8_t *__restrict__ dst) {
+    const int H = L.H, I = L.I;
+    const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
+    const int K = STAGE == 1 ? H : I, nk = K / KS;
+    constexpr int SLOTS = B_BYTES / 16;
+    const int64_t n = (int64_t)L.E * ncb * nk * SLOTS;
+    const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (o >= n) return;
+    const int S = (int)(o % SLOTS);
+    const int64_t t = o / SLOTS;
+    const int ks = (int)(t % nk);
+    const int64_t tile = t / nk;
+    const int cb = (int)(tile % ncb), e = (int)(tile / ncb);
+    const int rb = S / 2, ch = (S % 2) ^ ((rb >> 3) & 1);
+    const uint8_t *src;
+    size_t row;
+    if (STAGE == 1) {
+        src = rb < 128 ? L.gq : L.uq;
+        row = (size_t)e * I + cb * 128 + (rb & 127);
+    } else {
+        src = L.dq;
+        row = (size_t)e * H + cb * BROWS + rb;
+    }
+    const uint4 v = *reinterpret_cast<const uint4 *>(src + row * (size_t)(K / 2) + ks * (KS / 2) + 16 * ch);
+    const PackLayout pl = pack_layout(L.E, H, I);
+    *reinterpret_cast<uint4 *>(dst + (STAGE == 1 ? pl.gu_q : pl.d_q) + (size_t)o * 16) = v;
+}
+
+// Scale words: one thread per word; K-step j of slot r gets the aligned word
+// of the row's canonical scale array holding its group 64 j / G entry.
+template <int STAGE>
+__global__ __launch_bounds__(256) void pack_scales_kernel(LayerPtrs L, uint8_t *__restrict__ dst) {
+    const int H = L.H, I = L.I;
+    const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
+    const int K = STAGE == 1 ? H : I, nk = K / KS;
+    const int64_t n = (int64_t)L.E * ncb * nk * BROWS;
+    const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (o >= n) return;
+    const int r = (int)(o % BROWS);
+    const int64_t t = o / BROWS;
+    const int ks = (int)(t % nk);
+    const int64_t tile = t / nk;
+    const int cb = (int)(tile % ncb), e = (int)(tile / ncb);
+    const int G = L.fmt == 1 ? 128 : 64;  // NVFP4: four 16-input scales per word, as one 64-input entry
+    const int esz = L.fmt == 1 ? 2 : 4;
+    const uint16_t *src;
+    size_t row;
+    if (STAGE == 1) {
+        src = r < 128 ? L.gsm : L.usm;
+        row = (size_t)e * I + cb * 128 + (r & 127);
+    } else {
+        src = L.dsm;
+        row = (size_t)e * H + cb * BROWS + r;
+    }
+    const size_t byte = ((row * (size_t)(K / G) + (size_t)(ks * KS / G)) * esz) & ~(size_t)3;
+    const uint32_t wv = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(src) + byte);
+    const PackLayout pl = pack_layout(L.E, H, I);
+    reinterpret_cast<uint32_t *>(dst + (STAGE == 1 ? pl.gu_s : pl.d_s))[o] = wv;
+}
+
+hipError_t launch_prefill_pack(const LayerPtrs &L, uint8_t *dst, hipStream_t s) {
+    const int64_t E = L.E, H = L.H, I = L.I;
+    const int64_t n1 = E * (I / 128) * (H / KS) * (B_BYTES / 16), n2 = E * (H / BROWS) * (I / KS) * (B_BYTES / 16);
+    const int64_t s1 = E * (I / 128) * (H / KS) * BROWS, s2 = E * (H / BROWS) * (I / KS) * BROWS;
+    hipLaunchKernelGGL(pack_codes_kernel<1>, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, L, dst);
+    hipLaunchKernelGGL(pack_codes_kernel<2>, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, L, dst);
+    hipLaunchKernelGGL(pack_scales_kernel<1>, dim3((unsigned)((s1 + 255) / 256)), dim3(256), 0, s, L, dst);
+    hipLaunchKernelGGL(pack_scales_kernel<2>, dim3((unsigned)((s2 + 255) / 256)), dim3(256), 0, s, L, dst);
+    return hipGetLastError();
 }
 
 template <int FMT>

@@ -18,10 +18,13 @@ class MoeQ4Layer:
     layout of include/moe_q4.h).  ``mode``: "decode" (GEMV path) or
     "prefill" (grouped-GEMM path).  ``shared``: the layer's shared expert
     (hidden, inter and the six int8 code / f16 scale tensors) or None;
-    forward() then adds its output to every token's.
+    forward() then adds its output to every token's.  ``pack_prefill``: make
+    the prefill copy of the weights (int4 formats and NVFP4), which the
+    prefill GEMMs then read.
     """
 
-    def __init__(self, weights, k: int, max_tokens: int, mode: str = "decode", device="cuda", shared=None):
+    def __init__(self, weights, k: int, max_tokens: int, mode: str = "decode", device="cuda", shared=None,
+                 pack_prefill: bool = False):
         if mode not in ("decode", "prefill"):
             raise ValueError("mode must be 'decode' or 'prefill'")
         self.w = weights
@@ -29,7 +32,8 @@ class MoeQ4Layer:
         self.E, self.H, self.I = weights.num_experts, weights.hidden, weights.inter
         self.mode = mode
         self.max_tokens = max_tokens
-        self.struct = _lib.layer_struct(weights)
+        self.pack = _lib.prefill_pack(weights, device) if pack_prefill else None
+        self.struct = _lib.layer_struct(weights, pack=self.pack)
         T = max_tokens
         kind = _lib.WS_DECODE if mode == "decode" else _lib.WS_PREFILL
         nbytes = max(_lib.workspace_size(kind, T, self.E, k, self.H, self.I), 256)

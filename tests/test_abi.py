@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -262,3 +262,40 @@ def test_nvfp4_layer_validation():
     lay64 = _layer(fmt=3, H=64, I=64)
     lay64.global_scale = FAKE
     assert _decode(lay64, prefill=True) == _lib.ERR_UNSUPPORTED   # grouped GEMMs: H % 256, I % 128
+
+
+def test_prefill_pack_validation():
+    """The prefill copy: its size (27 E I H / 16 bytes, a host computation),
+    the formats and shapes it takes, and the checks of dst and of the
+    layer's prefill_pack field."""
+    lib = m.lib()
+    for fmt in (0, 1):
+        assert m.moe_q4_prefill_pack_size(_layer(fmt=fmt)) == 27 * 256 * 512 * 2048 // 16
+    nv = _layer(fmt=3, E=8, H=256, I=128)
+    nv.global_scale = FAKE
+    assert m.moe_q4_prefill_pack_size(nv) == 27 * 8 * 128 * 256 // 16
+    assert m.moe_q4_prefill_pack_size(_layer(fmt=2)) == 0            # block FP8: no copy
+    assert m.moe_q4_prefill_pack_size(_layer(H=64, I=64)) == 0       # not a prefill shape
+    assert m.moe_q4_prefill_pack_size(_layer(null="gate_q")) == 0
+    lay = _layer()
+    need = m.moe_q4_prefill_pack_size(lay)
+
+    def pack(layer, dst=FAKE, nbytes=None):
+        return lib.moe_q4_prefill_pack(ctypes.byref(layer), dst, need if nbytes is None else nbytes, None)
+
+    assert pack(lay, dst=None) == _lib.ERR_INVALID_ARG
+    assert pack(lay, dst=FAKE + 16) == _lib.ERR_INVALID_ARG       # 256-byte alignment
+    assert pack(lay, nbytes=need - 1) == _lib.ERR_INVALID_ARG
+    assert pack(_layer(fmt=2)) == _lib.ERR_UNSUPPORTED
+    assert pack(_layer(H=64, I=64)) == _lib.ERR_UNSUPPORTED
+    assert pack(_layer(null="down_sm")) == _lib.ERR_INVALID_ARG
+    # the field itself: 256-byte aligned, and not for block FP8
+    lay.prefill_pack = FAKE + 64
+    assert _decode(lay, prefill=True) == _lib.ERR_INVALID_ARG
+    assert _decode(lay) == _lib.ERR_INVALID_ARG
+    lay.prefill_pack = FAKE
+    assert _decode(lay, prefill=True, T=0) == _lib.OK
+    assert _decode(lay, prefill=True, ws_bytes=16) == _lib.ERR_WORKSPACE
+    fp8 = _layer(fmt=2)
+    fp8.prefill_pack = FAKE
+    assert _decode(fp8, prefill=True) == _lib.ERR_UNSUPPORTED

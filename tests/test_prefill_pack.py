@@ -1,0 +1,170 @@
+"""The prefill copy of the routed weights (moe_q4_prefill_pack) on the HIP
+path, through the C ABI (needs an MI355X).
+
+Bars:
+  * the copy is bit-exact against its layout as the public header states it,
+    built here on the host from the canonical arrays by reshapes and
+    transposes (a reordering: no arithmetic);
+  * the prefill path gives bit-identical outputs with and without the copy,
+    and with it stays within relative L2 2e-3 and max abs 1e-2 of the fp64
+    oracle.
+Formats: int4 asymmetric g64, symmetric g128 and NVFP4.  Shapes: two column
+blocks and several K-steps per GEMM at small sizes with ragged token counts;
+the 512-token Zipf layer and the 4096-token symmetric layer at full size
+(all tokens bit-identical, sampled tokens against the oracle).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_cases import assert_close, hip_experts, hip_route, np_u16, oracle_y
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_moe_expert_amd as m
+    m.lib()
+    return torch.device("cuda")
+
+
+def _host_bytes(t):
+    return t.detach().cpu().contiguous().numpy().view(np.uint8).reshape(-1)
+
+
+def _tiles_codes(rows, ncb, block_rows, K):
+    """[E][N][K/2] codes -> [E][ncb][K/64][block_rows][32], halves of the
+    32-byte chunk swapped in rows whose bit 3 is set."""
+    E = rows.shape[0]
+    t = rows.reshape(E, ncb, block_rows, K // 64, 2, 16).transpose(0, 1, 3, 2, 4, 5).copy()
+    sw = ((np.arange(block_rows) >> 3) & 1).astype(bool)
+    t[:, :, :, sw] = t[:, :, :, sw][:, :, :, :, ::-1]
+    return t.reshape(-1)
+
+
+# canonical scale entries: (inputs per entry, bytes per entry)
+ENTRY = {synth.FMT_ASYM_G64: (64, 4), synth.FMT_SYM_G128: (128, 2), synth.FMT_NVFP4: (16, 1)}
+
+
+def _step_words(sm, E, N, K, fmt):
+    """[E][N][K/64]: for each row and K-step j, the 4-byte-aligned word of the
+    canonical scale array that holds the row's entry for input 64 j."""
+    words = _host_bytes(sm).view(np.uint32)
+    G, esz = ENTRY[fmt]
+    row = np.arange(E * N)[:, None]
+    j = np.arange(K // 64)[None, :]
+    byte = (row * (K // G) + (64 * j) // G) * esz
+    return words[byte // 4].reshape(E, N, K // 64)
+
+
+def expected_pack(lay):
+    E, H, I, fmt = lay.num_experts, lay.hidden, lay.inter, lay.fmt
+    gq = _host_bytes(lay.gate_q).reshape(E, I, H // 2)
+    uq = _host_bytes(lay.up_q).reshape(E, I, H // 2)
+    dq = _host_bytes(lay.down_q).reshape(E, H, I // 2)
+    # gate|up: column block c = gate rows 128c.. then the same up rows
+    gu = np.concatenate([gq.reshape(E, I // 128, 128, H // 2), uq.reshape(E, I // 128, 128, H // 2)], axis=2)
+    gu_q = _tiles_codes(gu, I // 128, 256, H)
+    d_q = _tiles_codes(dq, H // 256, 256, I)
+    gw = _step_words(lay.gate_sm, E, I, H, fmt).reshape(E, I // 128, 128, H // 64)
+    uw = _step_words(lay.up_sm, E, I, H, fmt).reshape(E, I // 128, 128, H // 64)
+    gu_s = np.concatenate([gw, uw], axis=2).transpose(0, 1, 3, 2).reshape(-1)
+    d_s = _step_words(lay.down_sm, E, H, I, fmt).reshape(E, H // 256, 256, I // 64).transpose(0, 1, 3, 2).reshape(-1)
+    out = np.concatenate([gu_q, np.ascontiguousarray(gu_s).view(np.uint8), d_q,
+                          np.ascontiguousarray(d_s).view(np.uint8)])
+    assert out.size == 27 * E * I * H // 16
+    return out
+
+
+FORMATS = [synth.FMT_ASYM_G64, synth.FMT_SYM_G128, synth.FMT_NVFP4]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", [(3, 512, 256), (2, 256, 128), (1, 2048, 512)])
+def test_pack_bytes(fmt, shape):
+    import quantized_moe_expert_amd as m
+    E, H, I = shape
+    say(f"[pack bytes] fmt={fmt} E={E} H={H} I={I}")
+    lay = synth.random_layer(E, H, I, fmt, seed=21, device="cuda")
+    pk = m.prefill_pack(lay)
+    torch.cuda.synchronize()
+    got = pk.cpu().numpy()
+    exp = expected_pack(lay)
+    assert got.size == exp.size
+    bad = np.flatnonzero(got != exp)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:4]}"
+
+
+def _both(lay, x, idx, gate, k):
+    import quantized_moe_expert_amd as m
+    y0 = hip_experts("prefill", lay, x, idx, gate, k).clone()
+    pk = m.prefill_pack(lay)
+    y1 = hip_experts("prefill", m.layer_struct(lay, pack=pk), x, idx, gate, k)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32)), "outputs with the copy differ"
+    return y1
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("T", [1, 37, 200])
+def test_prefill_with_pack_ragged(fmt, T):
+    """Ragged token counts on a 64-expert layer (two column blocks per GEMM)
+    with random codes and scales."""
+    H, I, E, k = 512, 256, 64, 6
+    say(f"[pack ragged] fmt={fmt} T={T}")
+    lay = synth.random_layer(E, H, I, fmt, seed=9, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 9, f"pk/x/{T}", "cuda"))
+    wr = synth.bf16_bits(synth.normal((E, H), 0.05, 9, "pk/w", "cuda"))
+    lg, idx, gate = hip_route(x, wr, None, T, H, E, k)
+    lr = oracle.router(np_u16(x), np_u16(wr), T, H, E)
+    ir, gr = oracle.topk(lr, T, E, k)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    y = _both(lay, x, idx, gate, k)
+    yr = oracle_y(lay, np_u16(x), ir, gr, k)
+    assert_close(y.cpu().numpy(), yr, f"pack ragged fmt={fmt} T={T}")
+
+
+@pytest.mark.parametrize("cfg,fmt", [(3, None), (3, synth.FMT_NVFP4), (5, None)])
+def test_prefill_with_pack_full_size(cfg, fmt):
+    """The 512-token Zipf layer (int4 asym and NVFP4) and the 4096-token
+    symmetric layer: every output bit-identical with the copy, sampled tokens
+    against the oracle."""
+    say(f"[pack full] config {cfg} fmt={fmt}")
+    case = synth.make_case(cfg, device="cuda", fmt=fmt)
+    lay = case.layers[0]
+    lg, idx, gate = hip_route(None, None, case.logits, case.T, case.H, case.E, case.k)
+    y = _both(lay, case.x, idx, gate, case.k)
+    sub = np.unique(np.concatenate([np.arange(0, case.T, max(1, case.T // 24)), [1, case.T - 1]]))
+    lr = np.ascontiguousarray(np_u16(case.logits)[sub])
+    ir, gr = oracle.topk(lr, len(sub), case.E, case.k)
+    assert np.array_equal(idx.cpu().numpy()[sub], ir)
+    yr = oracle_y(lay, np_u16(case.x), ir, gr, case.k, tokens=sub)
+    r, a = assert_close(y.cpu().numpy()[sub], yr, f"pack config {cfg}")
+    say(f"[pack full] config {cfg}: rel L2 {r:.2e}, max abs {a:.2e}")
+
+
+def test_forward_with_pack():
+    """moe_q4_forward through MoeQ4Layer(pack_prefill=True) on the prefill
+    path (T > 64) equals the layer without the copy."""
+    import quantized_moe_expert_amd as m
+    case = synth.make_case(3, device="cuda", T=300)
+    lay = case.layers[0]
+    a = m.MoeQ4Layer(lay, case.k, case.T, mode="prefill")
+    b = m.MoeQ4Layer(lay, case.k, case.T, mode="prefill", pack_prefill=True)
+    ya = a.forward(case.x, logits=case.logits).clone()
+    yb = b.forward(case.x, logits=case.logits)
+    torch.cuda.synchronize()
+    assert torch.equal(ya.view(torch.int32), yb.view(torch.int32))
