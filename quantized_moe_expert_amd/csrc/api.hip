@@ -81,7 +81,7 @@ LayerPtrs layer_ptrs(const moe_q4_layer *w) {
 }
 
 // Grouping regions (shared by group, decode and prefill).
-GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile) {
+GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile, bool schedule = false) {
     const int64_t P = T * k;
     const int64_t nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
     GroupOut g;
@@ -95,6 +95,7 @@ GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile) {
     const bool multi = P > GROUP_SINGLE_MAX;
     g.chunk_cnt = c.take<int32_t>(multi ? nch * E : 0);
     g.chunk_base = c.take<int32_t>(multi ? nch * E : 0);
+    g.order = schedule ? c.take<int32_t>(max_tiles(P, E, rows_per_tile)) : nullptr;
     return g;
 }
 
@@ -126,7 +127,7 @@ struct PrefillWs {
 };
 PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
     PrefillWs p;
-    p.g = carve_group(c, T, E, k, PREFILL_BM);
+    p.g = carve_group(c, T, E, k, PREFILL_BM, true);
     p.x16 = c.take<uint16_t>(T * (int64_t)H);
     p.xexp = c.take<int32_t>(T);
     p.h = c.take<uint16_t>(T * k * (int64_t)I);

@@ -119,6 +119,7 @@ __device__ __forceinline__ int route_in_block(const uint16_t *__restrict__ lg, i
     gl.ntiles = &r_nt;
     gl.rows_per_tile = DECODE_TT;
     gl.chunk_cnt = gl.chunk_base = nullptr;
+    gl.order = nullptr;
     group_block_single(r_idx, P, E, gl);
     __syncthreads();
     const int nt_all = r_nt;

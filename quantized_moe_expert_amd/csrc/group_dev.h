@@ -52,6 +52,23 @@ __device__ inline void emit_offsets_and_tiles(int v, int E, int P, const GroupOu
         t.pad = 0;
     }
     if (e == 0) *g.ntiles = ntot;
+    if (g.order) {
+        // Schedule for the grouped GEMMs: the tiles ranked by their count of
+        // S/4-row subtiles, most first (full tiles, then partial tiles of 4,
+        // 3, 2 and 1 subtiles), each expert's in tile order within a rank.
+        const int nf = e < E ? v / S : 0, rem = e < E ? v - nf * S : 0;
+        const int qp = rem > 0 ? (rem + S / 4 - 1) / (S / 4) : 0;  // subtiles of the partial tile
+        int base = 0;
+        for (int q = 4; q >= 1; --q) {
+            const int cq = (q == 4 ? nf : 0) + (qp == q ? 1 : 0);
+            int tq;
+            const int oq = block_exclusive_scan(cq, lds16, &tq);
+            if (q == 4)
+                for (int j = 0; j < nf; ++j) g.order[base + oq + j] = toff + j;
+            if (qp == q) g.order[base + oq + (q == 4 ? nf : 0)] = toff + nf;
+            base += tq;
+        }
+    }
     *excl_out = excl;
     *tadj_out = toff * S - excl;
 }

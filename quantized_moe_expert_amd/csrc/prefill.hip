@@ -335,10 +335,12 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
 //          epilogue * 2^e(token), SwiGLU -> h (f16).
 // STAGE 2: A = h rows (contiguous sorted rows), B = down codes,
 //          epilogue gate-weighted rows of z (f16) for the combine kernel.
-// Work item w = (tile j, column block cb) with cb fastest.  Workgroups are
-// spread over the 8 XCDs round-robin (XCD = block index mod 8); each XCD
-// takes a contiguous range of work items, so the column blocks of one tile
-// (same A rows) and the tiles of one expert (same weights) meet in one L2.
+// Work items are (tile, column block).  Workgroups are spread over the 8 XCDs
+// round-robin (XCD = block index mod 8).  Tile rank t of the schedule `order`
+// (largest tiles first; null: the tile list's own order) goes to XCD t % 8,
+// where its column blocks run one after another (same A rows in one L2).
+// Each XCD so starts with its largest tiles and gets an even share of them,
+// and the small tiles fill the end of the launch.
 // In the ring, A row r (128 bytes per stage) holds its 16-byte chunk c at
 // c ^ ((r >> 1) & 7) and B row rb (32 bytes) at c ^ ((rb >> 3) & 1), so that
 // the fragment reads of 16 lanes hit distinct LDS banks.
@@ -348,17 +350,15 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t *__restrict__ xexp,      // STAGE 1: per-token exponent e
     int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
-    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z) {
+    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z, const int32_t *__restrict__ order) {
     constexpr int G = FMT == 0 || FMT == 3 ? 64 : 128;  // K elements per scale word (see gemm_main)
 
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
-    const int nwork = *ntiles * ncb;
-    const int per = (nwork + 7) / 8;
-    const int bx = blockIdx.x;
-    if (bx / 8 >= per) return;
-    const int w = (bx % 8) * per + bx / 8;
-    if (w >= nwork) return;
-    const int j = w / ncb, cb = w % ncb;
+    const int bx = blockIdx.x, local = bx / 8;
+    const int t = (local / ncb) * 8 + bx % 8;  // rank in the schedule
+    if (t >= *ntiles) return;
+    const int cb = local % ncb;
+    const int j = order ? order[t] : t;
     const Tile tile = tiles[j];
     const int e = tile.expert, rows = tile.rows, row0 = tile.row0;
     const int K = STAGE == 1 ? H : I;
@@ -1208,14 +1208,14 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
     const int64_t tiles = max_tiles(T * k, L.E, BM);
     hipLaunchKernelGGL(x_to_f16_kernel<FMT == 3 ? 0 : 1>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H,
                        x16, xexp);
-    const unsigned nb1 = (unsigned)(((I / 128) * tiles + 7) / 8 * 8);
-    const unsigned nb2 = (unsigned)(((H / BROWS) * tiles + 7) / 8 * 8);
+    const unsigned nb1 = (unsigned)(8 * ((tiles + 7) / 8) * (I / 128));  // 8 XCDs x ranks per XCD x column blocks
+    const unsigned nb2 = (unsigned)(8 * ((tiles + 7) / 8) * (H / BROWS));
     launch_k(grouped_gemm_kernel<FMT, 1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
              (const uint16_t *)x16, (const int32_t *)xexp, H, I, k, L, (const Tile *)g.tiles,
-             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z);
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
     launch_k(grouped_gemm_kernel<FMT, 2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, (const int32_t *)nullptr, H, I, k, L, (const Tile *)g.tiles,
-             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z);
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
                        (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();
