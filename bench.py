@@ -234,9 +234,9 @@ def main():
             shareds = [s0] + [clone_shared(s0) for _ in range(n_sx - 1)]
     torch.cuda.synchronize()
     log(f"[bench] generated {args.workload} inputs in {time.time() - t0:.1f}s")
-    # the prefill path reads the prefill copy of the weights (int4 and NVFP4),
-    # made once here like any load-time weight conversion, outside the timing
-    use_pack = mode == "prefill" and not shared_gemm and not fp8 and not args.no_pack
+    # the prefill path reads the prefill copy of the weights, made once here
+    # like any load-time weight conversion, outside the timing
+    use_pack = mode == "prefill" and not shared_gemm and not args.no_pack
     packs = [m.prefill_pack(l) for l in layers] if use_pack else [None] * len(layers)
     structs = [m.layer_struct(l, pack=p) for l, p in zip(layers, packs)]
     sstructs = [m.shared_struct(sx) for sx in shareds] if shareds else None

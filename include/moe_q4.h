@@ -152,12 +152,12 @@ typedef struct moe_q4_shared_expert {
 } moe_q4_shared_expert;
 
 /*
- * Prefill copy of a layer's routed weights (int4 formats and NVFP4).  The
- * prefill GEMMs read, per K-step of 64 inputs, 32 bytes of codes from each of
- * a tile's 256 weight rows; in the canonical layout those are 256 separate
+ * Prefill copy of a layer's routed weights.  The prefill GEMMs read, per
+ * K-step of 64 inputs, 32 bytes of codes (64 for block FP8) from each of a
+ * tile's 256 weight rows; in the canonical layout those are 256 separate
  * cache lines per step.  The copy stores each (expert, column block, K-step)
  * tile contiguously, so one step of a tile is 8 KB of consecutive codes plus
- * 1 KB of consecutive scale words.  It is made once per set of weights (a
+ * 1 KB of consecutive scale words (block FP8: 16 KB of codes).  It is made once per set of weights (a
  * reordering, bit for bit: the results of the prefill path are the same with
  * or without it) and then set in the layer's `prefill_pack` field; the
  * decode path reads the canonical arrays either way.
@@ -174,12 +174,17 @@ typedef struct moe_q4_shared_expert {
  *                  down rows 256c .. 256c+255, halves swapped as above.
  *   down scales    [E][H/256][I/64][256] uint32 at 13*E*I*H/8, as above.
  * Total 27*E*I*H/16 bytes (moe_q4_prefill_pack_size); dst 256-byte aligned.
+ * Block FP8: codes only (its block scales are read from the canonical array):
+ *   gate|up codes  [E][I/128][H/64][256][64] at 0, down codes
+ *                  [E][H/256][I/64][256][64] at 2*E*I*H; a slot's four
+ *                  16-byte quarters q are stored at q ^ ((slot >> 2) & 3).
+ *   Total 3*E*I*H bytes.
  */
 MOE_Q4_API size_t moe_q4_prefill_pack_size(const moe_q4_layer *w);
 
 /* Writes the prefill copy of w's weights (w->prefill_pack is ignored) to
- * dst on `stream`.  MOE_Q4_ERR_UNSUPPORTED for block FP8 or shapes the
- * prefill path does not take; MOE_Q4_ERR_INVALID_ARG when dst is NULL,
+ * dst on `stream`.  MOE_Q4_ERR_UNSUPPORTED for shapes the prefill path does
+ * not take; MOE_Q4_ERR_INVALID_ARG when dst is NULL,
  * misaligned or smaller than moe_q4_prefill_pack_size(w).  The copy stays
  * valid while the canonical weights are unchanged. */
 MOE_Q4_API int moe_q4_prefill_pack(const moe_q4_layer *w, void *dst, size_t dst_bytes, moe_q4_stream stream);
@@ -257,8 +262,8 @@ MOE_Q4_API int moe_q4_decode(const void *x, const int32_t *topk_idx, const float
  * fp32 into y (float [T][H], written whole; deterministic).  Same arguments
  * as moe_q4_decode; ws >= moe_q4_workspace_size(MOE_Q4_WS_PREFILL, ...).
  */
-/* With w->prefill_pack set (not for block FP8) the GEMMs read that copy
- * instead of the canonical codes and scales; the results are identical. */
+/* With w->prefill_pack set the GEMMs read that copy instead of the
+ * canonical codes and scale words; the results are identical. */
 MOE_Q4_API int moe_q4_prefill(const void *x, const int32_t *topk_idx, const float *topk_gate,
                    int64_t T, int32_t k, const moe_q4_layer *w, float *y,
                    void *ws, size_t ws_bytes, moe_q4_stream stream);

@@ -58,7 +58,6 @@ int check_layer(const moe_q4_layer *w, bool prefill) {
     if (!pow2_between(w->hidden, 64, 2048) || !pow2_between(w->inter, 64, 2048)) return MOE_Q4_ERR_UNSUPPORTED;
     if (w->hidden % G || w->inter % G) return MOE_Q4_ERR_UNSUPPORTED;
     if (prefill && (w->inter % 128 || w->hidden % 256)) return MOE_Q4_ERR_UNSUPPORTED;
-    if (w->prefill_pack && w->format == MOE_Q4_FP8_B128) return MOE_Q4_ERR_UNSUPPORTED;
     if (!aligned(w->prefill_pack, 256)) return MOE_Q4_ERR_INVALID_ARG;
     return MOE_Q4_OK;
 }
@@ -459,23 +458,21 @@ static int check_pack_source(const moe_q4_layer *w, moe_q4_layer *plain) {
     if (!w) return MOE_Q4_ERR_INVALID_ARG;
     *plain = *w;
     plain->prefill_pack = nullptr;
-    int st = check_layer(plain, true);
-    if (st) return st;
-    if (plain->format == MOE_Q4_FP8_B128) return MOE_Q4_ERR_UNSUPPORTED;
-    return MOE_Q4_OK;
+    return check_layer(plain, true);
 }
 
 size_t moe_q4_prefill_pack_size(const moe_q4_layer *w) {
     moe_q4_layer plain;
     if (check_pack_source(w, &plain)) return 0;
-    return pack_layout(plain.num_experts, plain.hidden, plain.inter).total;
+    return pack_layout(plain.num_experts, plain.hidden, plain.inter, plain.format).total;
 }
 
 int moe_q4_prefill_pack(const moe_q4_layer *w, void *dst, size_t dst_bytes, moe_q4_stream stream) {
     moe_q4_layer plain;
     int st = check_pack_source(w, &plain);
     if (st) return st;
-    if (!dst || !aligned(dst, 256) || dst_bytes < pack_layout(plain.num_experts, plain.hidden, plain.inter).total)
+    if (!dst || !aligned(dst, 256) ||
+        dst_bytes < pack_layout(plain.num_experts, plain.hidden, plain.inter, plain.format).total)
         return MOE_Q4_ERR_INVALID_ARG;
     return hip_status(
         launch_prefill_pack(layer_ptrs(&plain), static_cast<uint8_t *>(dst), reinterpret_cast<hipStream_t>(stream)));

@@ -35,12 +35,15 @@ struct LayerPtrs {
 };
 
 // Byte offsets of the prefill copy's regions: gate|up codes, gate|up scale
-// words, down codes, down scale words, and its size.
+// words, down codes, down scale words, and its size.  Block FP8 (format 2)
+// has one byte per code and no scale regions (its block scales are read
+// from the canonical array).
 struct PackLayout {
     size_t gu_q, gu_s, d_q, d_s, total;
 };
-__host__ __device__ inline PackLayout pack_layout(int E, int H, int I) {
+__host__ __device__ inline PackLayout pack_layout(int E, int H, int I, int fmt) {
     const size_t eih = (size_t)E * I * H;
+    if (fmt == 2) return PackLayout{0, 2 * eih, 2 * eih, 3 * eih, 3 * eih};
     return PackLayout{0, eih, eih + eih / 8, eih + eih / 8 + eih / 2, eih + eih / 8 + eih / 2 + eih / 16};
 }
 

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (L.pack) {
         // prefill copy: per K-step, tile (e, cb) holds its 256 rows' chunks in
         // slot order (8 KB) and their scale words in row order (1 KB)
-        const PackLayout pl = pack_layout(L.E, H, I);
+        const PackLayout pl = pack_layout(L.E, H, I, FMT);
         const size_t tile = (size_t)e * ncb + cb;
         const uint8_t *q = L.pack + (STAGE == 1 ? pl.gu_q : pl.d_q) + tile * (size_t)c.nk * B_BYTES;
 #pragma unroll
@@ -566,6 +566,7 @@ struct Gemm8Ctx {
     uint32_t a_off[4];
     const uint8_t *b_base[B8_LOADS];
     uint32_t b_off[B8_LOADS];
+    uint32_t b_kstep;    // bytes between K-steps of a weight row chunk
     const float *sc[2];  // block scales of this wave's two N-subtiles, one per 128 inputs
     uint8_t *ring;
     int brow[2];
@@ -584,7 +585,7 @@ __device__ __forceinline__ void issue_stage8(const Gemm8Ctx &c, int ks, int slot
                                          16, 0, 0);
 #pragma unroll
     for (int i = 0; i < B8_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * KS) + c.b_off[i]),
+        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * c.b_kstep) + c.b_off[i]),
                                          (__attribute__((address_space(3))) void *)(sb + (i * 4 + wave) * 1024),
                                          16, 0, 0);
 }
@@ -696,15 +697,13 @@ template <int STAGE>
 __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_gemm_fp8_kernel(
     const uint16_t *__restrict__ act, int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
-    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z) {
+    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z, const int32_t *__restrict__ order) {
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
-    const int nwork = *ntiles * ncb;
-    const int per = (nwork + 7) / 8;
-    const int bx = blockIdx.x;
-    if (bx / 8 >= per) return;
-    const int w = (bx % 8) * per + bx / 8;
-    if (w >= nwork) return;
-    const int j = w / ncb, cb = w % ncb;
+    const int bx = blockIdx.x, local = bx / 8;
+    const int t = (local / ncb) * 8 + bx % 8;  // rank in the schedule (as grouped_gemm_kernel)
+    if (t >= *ntiles) return;
+    const int cb = local % ncb;
+    const int j = order ? order[t] : t;
     const Tile tile = tiles[j];
     const int e = tile.expert, rows = tile.rows, row0 = tile.row0;
     const int K = STAGE == 1 ? H : I;
@@ -756,6 +755,19 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
             wrow = (uint32_t)e * H + col_base + rb;
         }
         c.b_off[i] = wrow * (uint32_t)K + 16u * ch;
+    }
+    c.b_kstep = KS;
+    if (L.pack) {
+        // prefill copy: per K-step, tile (e, cb) holds its 256 rows' 64-byte chunks in slot order
+        const PackLayout pl = pack_layout(L.E, H, I, 2);
+        const uint8_t *q =
+            L.pack + (STAGE == 1 ? pl.gu_q : pl.d_q) + ((size_t)e * ncb + cb) * (size_t)c.nk * B8_BYTES;
+#pragma unroll
+        for (int i = 0; i < B8_LOADS; ++i) {
+            c.b_base[i] = q;
+            c.b_off[i] = 16u * (uint32_t)((i * 4 + wave) * 64 + lane);
+        }
+        c.b_kstep = B8_BYTES;
     }
     const int nkb = K / 128;
 #pragma unroll
@@ -1125,15 +1137,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 //
 // Gather of the canonical codes and scale words into the GEMMs' tile order
 // (the layout is stated with moe_q4_prefill_pack in the public header).
-// Codes: one thread per 16-byte chunk of the copy; slot S of a K-step holds
-// chunk (S % 2) ^ ((row >> 3) & 1) of row S / 2, the order in which the
-// GEMM's direct-to-LDS loads place them.
-template <int STAGE>
+// Codes: one thread per 16-byte chunk of the copy, in the order in which the
+// GEMM's direct-to-LDS loads place them: with RB bytes of a row per K-step
+// (32: 4-bit codes, 64: FP8), slot S of a K-step holds chunk
+// (S % 2) ^ ((row >> 3) & 1) of row S / 2, or (S % 4) ^ ((row >> 2) & 3) of
+// row S / 4.
+template <int STAGE, int RB>
 __global__ __launch_bounds__(256) void pack_codes_kernel(LayerPtrs L, uint8_t *__restrict__ dst) {
     const int H = L.H, I = L.I;
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
     const int K = STAGE == 1 ? H : I, nk = K / KS;
-    constexpr int SLOTS = B_BYTES / 16;
+    constexpr int SLOTS = BROWS * RB / 16;
     const int64_t n = (int64_t)L.E * ncb * nk * SLOTS;
     const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= n) return;
@@ -1142,7 +1156,8 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(LayerPtrs L, uint8_t *_
     const int ks = (int)(t % nk);
     const int64_t tile = t / nk;
     const int cb = (int)(tile % ncb), e = (int)(tile / ncb);
-    const int rb = S / 2, ch = (S % 2) ^ ((rb >> 3) & 1);
+    constexpr int CPR = RB / 16;  // chunks per row and K-step
+    const int rb = S / CPR, ch = CPR == 2 ? (S % 2) ^ ((rb >> 3) & 1) : (S % 4) ^ ((rb >> 2) & 3);
     const uint8_t *src;
     size_t row;
     if (STAGE == 1) {
@@ -1152,8 +1167,9 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(LayerPtrs L, uint8_t *_
         src = L.dq;
         row = (size_t)e * H + cb * BROWS + rb;
     }
-    const uint4 v = *reinterpret_cast<const uint4 *>(src + row * (size_t)(K / 2) + ks * (KS / 2) + 16 * ch);
-    const PackLayout pl = pack_layout(L.E, H, I);
+    const size_t row_bytes = (size_t)K * RB / KS;
+    const uint4 v = *reinterpret_cast<const uint4 *>(src + row * row_bytes + (size_t)ks * RB + 16 * ch);
+    const PackLayout pl = pack_layout(L.E, H, I, L.fmt);
     *reinterpret_cast<uint4 *>(dst + (STAGE == 1 ? pl.gu_q : pl.d_q) + (size_t)o * 16) = v;
 }
 
@@ -1185,16 +1201,23 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(LayerPtrs L, uint8_t *
     }
     const size_t byte = ((row * (size_t)(K / G) + (size_t)(ks * KS / G)) * esz) & ~(size_t)3;
     const uint32_t wv = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(src) + byte);
-    const PackLayout pl = pack_layout(L.E, H, I);
+    const PackLayout pl = pack_layout(L.E, H, I, L.fmt);
     reinterpret_cast<uint32_t *>(dst + (STAGE == 1 ? pl.gu_s : pl.d_s))[o] = wv;
 }
 
 hipError_t launch_prefill_pack(const LayerPtrs &L, uint8_t *dst, hipStream_t s) {
     const int64_t E = L.E, H = L.H, I = L.I;
-    const int64_t n1 = E * (I / 128) * (H / KS) * (B_BYTES / 16), n2 = E * (H / BROWS) * (I / KS) * (B_BYTES / 16);
-    const int64_t s1 = E * (I / 128) * (H / KS) * BROWS, s2 = E * (H / BROWS) * (I / KS) * BROWS;
-    hipLaunchKernelGGL(pack_codes_kernel<1>, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, L, dst);
-    hipLaunchKernelGGL(pack_codes_kernel<2>, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, L, dst);
+    const int64_t t1 = E * (I / 128) * (H / KS), t2 = E * (H / BROWS) * (I / KS);  // (tile, K-step) blocks
+    if (L.fmt == 2) {  // block FP8: 64 bytes per row and K-step, no scale regions
+        const int64_t n1 = t1 * (BROWS * 64 / 16), n2 = t2 * (BROWS * 64 / 16);
+        hipLaunchKernelGGL((pack_codes_kernel<1, 64>), dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, L, dst);
+        hipLaunchKernelGGL((pack_codes_kernel<2, 64>), dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, L, dst);
+        return hipGetLastError();
+    }
+    const int64_t n1 = t1 * (BROWS * 32 / 16), n2 = t2 * (BROWS * 32 / 16);
+    const int64_t s1 = t1 * BROWS, s2 = t2 * BROWS;
+    hipLaunchKernelGGL((pack_codes_kernel<1, 32>), dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, L, dst);
+    hipLaunchKernelGGL((pack_codes_kernel<2, 32>), dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, L, dst);
     hipLaunchKernelGGL(pack_scales_kernel<1>, dim3((unsigned)((s1 + 255) / 256)), dim3(256), 0, s, L, dst);
     hipLaunchKernelGGL(pack_scales_kernel<2>, dim3((unsigned)((s2 + 255) / 256)), dim3(256), 0, s, L, dst);
     return hipGetLastError();
@@ -1235,13 +1258,14 @@ static hipError_t launch_prefill_fp8(const uint16_t *x, const float *gate, int64
                                      hipEvent_t const *ev) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
-    const unsigned nb1 = (unsigned)(((I / 128) * tiles + 7) / 8 * 8);
-    const unsigned nb2 = (unsigned)(((H / BROWS) * tiles + 7) / 8 * 8);
+    const unsigned nb1 = (unsigned)(8 * ((tiles + 7) / 8) * (I / 128));  // as launch_prefill_fmt
+    const unsigned nb2 = (unsigned)(8 * ((tiles + 7) / 8) * (H / BROWS));
     launch_k(grouped_gemm_fp8_kernel<1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, x,
-             H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z);
+             H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z,
+             (const int32_t *)g.order);
     launch_k(grouped_gemm_fp8_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles,
-             (const int32_t *)g.perm, gate, h, z);
+             (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
                        (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();

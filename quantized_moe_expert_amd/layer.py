@@ -19,8 +19,7 @@ class MoeQ4Layer:
     "prefill" (grouped-GEMM path).  ``shared``: the layer's shared expert
     (hidden, inter and the six int8 code / f16 scale tensors) or None;
     forward() then adds its output to every token's.  ``pack_prefill``: make
-    the prefill copy of the weights (int4 formats and NVFP4), which the
-    prefill GEMMs then read.
+    the prefill copy of the weights, which the prefill GEMMs then read.
     """
 
     def __init__(self, weights, k: int, max_tokens: int, mode: str = "decode", device="cuda", shared=None,

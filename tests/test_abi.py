@@ -274,7 +274,7 @@ def test_prefill_pack_validation():
     nv = _layer(fmt=3, E=8, H=256, I=128)
     nv.global_scale = FAKE
     assert m.moe_q4_prefill_pack_size(nv) == 27 * 8 * 128 * 256 // 16
-    assert m.moe_q4_prefill_pack_size(_layer(fmt=2)) == 0            # block FP8: no copy
+    assert m.moe_q4_prefill_pack_size(_layer(fmt=2)) == 3 * 256 * 512 * 2048  # block FP8: codes only
     assert m.moe_q4_prefill_pack_size(_layer(H=64, I=64)) == 0       # not a prefill shape
     assert m.moe_q4_prefill_pack_size(_layer(null="gate_q")) == 0
     lay = _layer()
@@ -286,10 +286,9 @@ def test_prefill_pack_validation():
     assert pack(lay, dst=None) == _lib.ERR_INVALID_ARG
     assert pack(lay, dst=FAKE + 16) == _lib.ERR_INVALID_ARG       # 256-byte alignment
     assert pack(lay, nbytes=need - 1) == _lib.ERR_INVALID_ARG
-    assert pack(_layer(fmt=2)) == _lib.ERR_UNSUPPORTED
     assert pack(_layer(H=64, I=64)) == _lib.ERR_UNSUPPORTED
     assert pack(_layer(null="down_sm")) == _lib.ERR_INVALID_ARG
-    # the field itself: 256-byte aligned, and not for block FP8
+    # the field itself: 256-byte aligned
     lay.prefill_pack = FAKE + 64
     assert _decode(lay, prefill=True) == _lib.ERR_INVALID_ARG
     assert _decode(lay) == _lib.ERR_INVALID_ARG
@@ -298,4 +297,5 @@ def test_prefill_pack_validation():
     assert _decode(lay, prefill=True, ws_bytes=16) == _lib.ERR_WORKSPACE
     fp8 = _layer(fmt=2)
     fp8.prefill_pack = FAKE
-    assert _decode(fp8, prefill=True) == _lib.ERR_UNSUPPORTED
+    assert _decode(fp8, prefill=True, T=0) == _lib.OK
+    assert _decode(fp8, prefill=True, ws_bytes=16) == _lib.ERR_WORKSPACE

@@ -8,7 +8,7 @@ Bars:
   * the prefill path gives bit-identical outputs with and without the copy,
     and with it stays within relative L2 2e-3 and max abs 1e-2 of the fp64
     oracle.
-Formats: int4 asymmetric g64, symmetric g128 and NVFP4.  Shapes: two column
+Formats: int4 asymmetric g64, symmetric g128, block FP8 and NVFP4.  Shapes: two column
 blocks and several K-steps per GEMM at small sizes with ragged token counts;
 the 512-token Zipf layer and the 4096-token symmetric layer at full size
 (all tokens bit-identical, sampled tokens against the oracle).
@@ -55,6 +55,20 @@ def _tiles_codes(rows, ncb, block_rows, K):
     return t.reshape(-1)
 
 
+def _tiles_codes_fp8(rows, ncb, block_rows, K):
+    """[E][N][K] FP8 codes -> [E][ncb][K/64][block_rows][64], the 16-byte
+    quarter q of a row's 64 bytes stored at q ^ ((row >> 2) & 3)."""
+    E = rows.shape[0]
+    t = rows.reshape(E, ncb, block_rows, K // 64, 4, 16).transpose(0, 1, 3, 2, 4, 5)
+    out = np.empty_like(t)
+    sel = (np.arange(block_rows) >> 2) & 3
+    for q in range(4):
+        for x in range(4):
+            r = sel == x
+            out[:, :, :, r, q ^ x] = t[:, :, :, r, q]
+    return out.reshape(-1)
+
+
 # canonical scale entries: (inputs per entry, bytes per entry)
 ENTRY = {synth.FMT_ASYM_G64: (64, 4), synth.FMT_SYM_G128: (128, 2), synth.FMT_NVFP4: (16, 1)}
 
@@ -72,6 +86,14 @@ def _step_words(sm, E, N, K, fmt):
 
 def expected_pack(lay):
     E, H, I, fmt = lay.num_experts, lay.hidden, lay.inter, lay.fmt
+    if fmt == synth.FMT_FP8_B128:
+        gq = _host_bytes(lay.gate_q).reshape(E, I, H)
+        uq = _host_bytes(lay.up_q).reshape(E, I, H)
+        dq = _host_bytes(lay.down_q).reshape(E, H, I)
+        gu = np.concatenate([gq.reshape(E, I // 128, 128, H), uq.reshape(E, I // 128, 128, H)], axis=2)
+        out = np.concatenate([_tiles_codes_fp8(gu, I // 128, 256, H), _tiles_codes_fp8(dq, H // 256, 256, I)])
+        assert out.size == 3 * E * I * H
+        return out
     gq = _host_bytes(lay.gate_q).reshape(E, I, H // 2)
     uq = _host_bytes(lay.up_q).reshape(E, I, H // 2)
     dq = _host_bytes(lay.down_q).reshape(E, H, I // 2)
@@ -89,7 +111,7 @@ def expected_pack(lay):
     return out
 
 
-FORMATS = [synth.FMT_ASYM_G64, synth.FMT_SYM_G128, synth.FMT_NVFP4]
+FORMATS = [synth.FMT_ASYM_G64, synth.FMT_SYM_G128, synth.FMT_FP8_B128, synth.FMT_NVFP4]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -137,11 +159,12 @@ def test_prefill_with_pack_ragged(fmt, T):
     assert_close(y.cpu().numpy(), yr, f"pack ragged fmt={fmt} T={T}")
 
 
-@pytest.mark.parametrize("cfg,fmt", [(3, None), (3, synth.FMT_NVFP4), (5, None)])
+@pytest.mark.parametrize("cfg,fmt", [(3, None), (3, synth.FMT_NVFP4), (3, synth.FMT_FP8_B128), (5, None),
+                                     (5, synth.FMT_FP8_B128)])
 def test_prefill_with_pack_full_size(cfg, fmt):
-    """The 512-token Zipf layer (int4 asym and NVFP4) and the 4096-token
-    symmetric layer: every output bit-identical with the copy, sampled tokens
-    against the oracle."""
+    """The 512-token Zipf layer (int4 asym, NVFP4, block FP8) and the
+    4096-token layer (int4 sym, block FP8): every output bit-identical with
+    the copy, sampled tokens against the oracle."""
     say(f"[pack full] config {cfg} fmt={fmt}")
     case = synth.make_case(cfg, device="cuda", fmt=fmt)
     lay = case.layers[0]
