@@ -574,10 +574,10 @@ __global__ __launch_bounds__(256) void decode_router_kernel(
     }
 }
 
-// Routing of a few tokens in one launch.  Workgroup b (16 waves) computes
-// the router logit of expert b for every token (wave w: tokens w, w + 16,
-// ...); the tokens' input rows are staged in LDS 16 at a time (formed once
-// per workgroup).  The logits travel to the workgroup that arrives last
+// Routing of a few tokens in one launch.  A workgroup (16 waves) computes
+// the router logits of ROUTE_EG experts for ROUTE_TG tokens, one (expert,
+// token) dot per wave; the tokens' input rows are staged in LDS once per
+// workgroup (so every input row is formed E / ROUTE_EG times, not E).  The logits travel to the workgroup that arrives last
 // through agent-scope relaxed atomic stores and loads (coherent across the
 // XCDs' L2 caches) and a counter in the workspace (zero between calls): each
 // workgroup waits for its stores to complete, then counts itself in.  This
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     __shared__ int s_last;
     __shared__ uint16_t s_lg[ROUTE_LDS_LOGITS];
     __shared__ int32_t s_idx[GROUP_SINGLE_MAX];
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[ROUTE_TC * 2048];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[ROUTE_TG * 2048];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = gridDim.x;
     const int64_t n = (int64_t)T * H;
@@ -609,87 +609,67 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
     }
     const uint16_t *lsrc = logits;
     if (wr) {
-        const int e = blockIdx.x;  // grid = E
+        // workgroup = (group of ROUTE_EG experts, group of ROUTE_TG tokens);
+        // wave w takes expert w / ROUTE_TG and token w % ROUTE_TG of them
+        const int neg = (E + ROUTE_EG - 1) / ROUTE_EG;
+        const int eg = blockIdx.x % neg, tg = blockIdx.x / neg;
+        const int e = eg * ROUTE_EG + wave / ROUTE_TG, tl = wave % ROUTE_TG;
+        const int t0 = tg * ROUTE_TG;
+        const int tc = T - t0 < ROUTE_TG ? T - t0 : ROUTE_TG;
         // the expert's router row, 8 bf16 per lane and quarter (H <= 2048)
         uint4 wv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int hh = (q * WAVE + lane) * 8;
             wv[q] = make_uint4(0, 0, 0, 0);
-            if (hh < H) wv[q] = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
+            if (e < E && hh < H) wv[q] = *reinterpret_cast<const uint4 *>(wr + (size_t)e * H + hh);
         }
-        const double b = bias ? (double)bias[e] : 0.0;
-        for (int t0 = 0; t0 < T; t0 += ROUTE_TC) {
-            const int tc = T - t0 < ROUTE_TC ? T - t0 : ROUTE_TC;
-            const int nvec = tc * (H / 8);  // <= ROUTE_TC * 256 = 4 pieces per thread
-            __syncthreads();  // previous chunk consumed
-            {
-                // all pieces' loads in flight together
-                uint4 v[4];
-                float4 ya[4], yb[4];
+        const double b = bias && e < E ? (double)bias[e] : 0.0;
+        // the group's input rows (with the residual) in LDS, 16 bytes per piece
+        for (int i = tid; i < tc * (H / 8); i += blockDim.x) {
+            const size_t gi = (size_t)(t0 + i / (H / 8)) * H + (i % (H / 8)) * 8;
+            uint4 o = *reinterpret_cast<const uint4 *>(x + gi);
+            if (yres) {
+                const float4 ya = *reinterpret_cast<const float4 *>(yres + gi);
+                const float4 yb = *reinterpret_cast<const float4 *>(yres + gi + 4);
+                const float yv[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+                uint32_t w4[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = tid + r * 1024;
-                    if (i < nvec) {
-                        const size_t gi = (size_t)(t0 + i / (H / 8)) * H + (i % (H / 8)) * 8;
-                        v[r] = *reinterpret_cast<const uint4 *>(x + gi);
-                        if (yres) {
-                            ya[r] = *reinterpret_cast<const float4 *>(yres + gi);
-                            yb[r] = *reinterpret_cast<const float4 *>(yres + gi + 4);
-                        }
-                    }
+                for (int jj = 0; jj < 4; ++jj) {
+                    const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(w4[jj] & 0xffffu) + yv[2 * jj]);
+                    const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(w4[jj] >> 16) + yv[2 * jj + 1]);
+                    w4[jj] = lo | (hi << 16);
                 }
+                o = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+            }
+            *reinterpret_cast<uint4 *>(&s_x[(i / (H / 8)) * H + (i % (H / 8)) * 8]) = o;
+        }
+        __syncthreads();
+        if (e < E && tl < tc) {
+            double acc = 0.0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = tid + r * 1024;
-                    if (i < nvec) {
-                        uint4 o = v[r];
-                        if (yres) {
-                            const float yv[8] = {ya[r].x, ya[r].y, ya[r].z, ya[r].w,
-                                                 yb[r].x, yb[r].y, yb[r].z, yb[r].w};
-                            uint32_t w4[4] = {o.x, o.y, o.z, o.w};
+            for (int q = 0; q < 4; ++q) {
+                const int hh = (q * WAVE + lane) * 8;
+                if (hh < H) {
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(&s_x[tl * H + hh]);
+                    const uint32_t xs4[4] = {xv.x, xv.y, xv.z, xv.w};
+                    const uint32_t ws4[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
 #pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) {
-                                const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(w4[jj] & 0xffffu) + yv[2 * jj]);
-                                const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(w4[jj] >> 16) + yv[2 * jj + 1]);
-                                w4[jj] = lo | (hi << 16);
-                            }
-                            o = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-                        }
-                        *reinterpret_cast<uint4 *>(&s_x[(i / (H / 8)) * H + (i % (H / 8)) * 8]) = o;
+                    for (int jj = 0; jj < 4; ++jj) {
+                        acc = fma((double)bf16_to_f32(xs4[jj] & 0xffffu), (double)bf16_to_f32(ws4[jj] & 0xffffu),
+                                  acc);
+                        acc = fma((double)bf16_to_f32(xs4[jj] >> 16), (double)bf16_to_f32(ws4[jj] >> 16), acc);
                     }
                 }
             }
-            __syncthreads();
-            for (int tl = wave; tl < tc; tl += 16) {
-                double acc = 0.0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int hh = (q * WAVE + lane) * 8;
-                    if (hh < H) {
-                        const uint4 xv = *reinterpret_cast<const uint4 *>(&s_x[tl * H + hh]);
-                        const uint32_t xs4[4] = {xv.x, xv.y, xv.z, xv.w};
-                        uint32_t ws4[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
-                        // converted per token (a wave takes one token when T <= 16):
-                        // hoisting 32 doubles out of the loop would spill
-                        asm volatile("" : "+v"(ws4[0]), "+v"(ws4[1]), "+v"(ws4[2]), "+v"(ws4[3]));
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            acc = fma((double)bf16_to_f32(xs4[jj] & 0xffffu), (double)bf16_to_f32(ws4[jj] & 0xffffu),
-                                      acc);
-                            acc = fma((double)bf16_to_f32(xs4[jj] >> 16), (double)bf16_to_f32(ws4[jj] >> 16), acc);
-                        }
-                    }
-                }
-                acc = wave_sum_f64_dpp(acc);
-                if (lane == 63) {
-                    const int t = t0 + tl;
-                    const uint16_t v = f32_to_bf16_rne((float)(acc + b));
-                    logits[(size_t)t * E + e] = v;
-                    if (tail)
-                        __hip_atomic_store(handoff + (size_t)t * E + e, (unsigned int)v, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                }
+            acc = wave_sum_f64_dpp(acc);
+            if (lane == 63) {
+                const int t = t0 + tl;
+                const uint16_t v = f32_to_bf16_rne((float)(acc + b));
+                logits[(size_t)t * E + e] = v;
+                if (tail)
+                    __hip_atomic_store(handoff + (size_t)t * E + e, (unsigned int)v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         if (!tail) return;  // top-k and grouping run in the next launch
@@ -821,7 +801,7 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
     }
     if (wr && T * E > ROUTE_LDS_LOGITS) return hipErrorInvalidValue;
     if (T * k > GROUP_SINGLE_MAX) return hipErrorInvalidValue;
-    const int nb = wr ? E : 1;
+    const int nb = wr ? (E + ROUTE_EG - 1) / ROUTE_EG * ((T + ROUTE_TG - 1) / ROUTE_TG) : 1;
     const int npl = (E + 63) / 64;
 #define LAUNCH(N) \
     launch_k(decode_route_group_kernel<N>, dim3(nb), dim3(1024), s, e0, e1, x, yres, xout, wr, bias, T, H, E, k, \

@@ -51,7 +51,8 @@ constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chu
 constexpr int GROUP_SINGLE_MAX = 1024;   // pairs handled by the one-block grouping
 constexpr int PREFILL_BM = 128;          // rows per prefill tile
 constexpr int ROUTE_LDS_LOGITS = 16384;  // T * E limit of the one-launch decode routing
-constexpr int ROUTE_TC = 16;             // tokens staged per pass of the one-launch routing
+constexpr int ROUTE_TG = 4;              // tokens per workgroup of the one-launch routing
+constexpr int ROUTE_EG = 4;              // experts per workgroup of it (ROUTE_TG * ROUTE_EG = 16 waves)
 constexpr int DEC_ROUTE_EMAX = 256;      // experts of the per-workgroup decode routing
 constexpr int DEC_ROUTE_PMAX = 256;      // (token, slot) pairs of the per-workgroup decode routing
 constexpr int DEC_ROUTE_PMAX_FAST = 64;  // pairs up to which the forward call uses it
