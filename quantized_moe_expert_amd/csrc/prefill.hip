@@ -147,13 +147,23 @@ constexpr int S_BYTES = BROWS * 4;              // 1 KB: one scale word per weig
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
 constexpr int B_LOADS = B_BYTES / 16 / PF_BLOCK;  // 2 sixteen-byte loads per thread and stage
 
-// The ring holds NST full stages; a tile with fewer 32-row subtiles uses
-// shorter stages (A takes 4 KB per subtile) and so fits more of them in the
-// same bytes, which keeps more K-steps in flight for small tiles.
+// The LDS ring holds the A rows of each stage (4 KB per 32-row subtile in
+// use); a lane's codes and scale words of a stage go to registers (10 VGPRs
+// per stage beside 32 accumulators per subtile).  Single-subtile tiles keep
+// five K-steps in flight, the others four.
 template <int MS>
-constexpr int stage_bytes() { return MS * (A_BYTES / 4) + B_BYTES + S_BYTES; }
+constexpr int stage_bytes() { return MS * (A_BYTES / 4); }
 template <int MS>
-constexpr int ring_depth() { return (NST * STAGE_BYTES) / stage_bytes<MS>() > 6 ? 6 : (NST * STAGE_BYTES) / stage_bytes<MS>(); }
+constexpr int ring_depth() { return MS == 1 ? 5 : 4; }
+// Each ring slot is an LDS array of its own.  The compiler orders a read of
+// LDS after every direct-to-LDS load that may write the same bytes; with one
+// array for the whole ring it could not tell the slots apart and made each
+// step wait for the loads just issued for later steps.  Slots 0-2 also hold
+// 32 rows of the epilogue's output tile.
+constexpr int RSLOT_BIG = 32 * (BROWS + 8) * 2;  // 16,896 B
+constexpr int RSLOT3 = RSLOT_BIG;
+constexpr int RSLOT4 = stage_bytes<1>();
+static_assert(stage_bytes<4>() <= RSLOT_BIG && ring_depth<4>() == 4 && ring_depth<1>() == 5, "ring slots fit");
 
 // Wait until at most n stages of LPS loads each are in flight (n <= 4; the
 // count must be an immediate).
@@ -173,14 +183,14 @@ __device__ __forceinline__ void wait_stages(int n) {
 struct GemmCtx {
     const uint8_t *a_base;
     uint32_t a_off[4];               // A chunk of each 32-row subtile
-    const uint8_t *b_base[B_LOADS];
-    uint32_t b_off[B_LOADS];
+    const uint8_t *b_base[2];        // per N-subtile: codes of the lane's weight row
+    uint32_t b_off[2];               //   the lane's 16 bytes of K-step 0
     uint32_t b_kstep;                // bytes between K-steps of a weight row chunk
-    const uint8_t *s_base;
-    uint32_t s_off;                  // scale entry of group 0 of weight row `tid`
+    const uint8_t *s_base[2];        // per N-subtile: the row's scale words
+    uint32_t s_off[2];               //   its entry of group 0 (before 4-byte alignment)
     uint32_t s_step;                 // bytes between groups: 4 (scale+min) or 2 (scale); 0 in the copy
     uint32_t s_kstep;                // bytes between K-steps: 0, or 1 KB in the copy
-    uint8_t *ring;
+    uint8_t *ring[5];                // the ring slots
     int brow[2];                     // this lane's weight rows (block-local) of the two N-subtiles
     uint32_t spar[2];                // sym: parity of the scale entry of group 0 of brow[ns]
     int nk;                          // K-steps
@@ -195,14 +205,14 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
-// One thread's share of K-step `ks` (group g) into ring slot `slot`: MS A
-// loads (one per 32-row subtile in use) and B_LOADS B loads of 16 bytes, and
-// the dword holding weight row tid's scale entry of group g, all lane-ordered.
+// One thread's share of K-step `ks` (group g): MS A loads of 16 bytes (one
+// per 32-row subtile in use) into ring slot `slot`, lane-ordered; and into
+// registers, the lane's 16 bytes of codes of each of its two weight rows and
+// the word holding each row's scale entry of group g: MS + 4 loads.
 template <int MS>
-__device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int slot, int wave) {
-    uint8_t *sa = c.ring + slot * stage_bytes<MS>();
-    uint8_t *sb = sa + MS * (A_BYTES / 4);
-    uint8_t *ss = sb + B_BYTES;
+__device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int slot, int wave, uint4 (&bq)[2],
+                                            uint32_t (&sw)[2]) {
+    uint8_t *sa = c.ring[slot];
     const uint8_t *ab = c.a_base + (size_t)ks * (KS * 2);  // uniform part of the addresses
 #pragma unroll
     for (int i = 0; i < MS; ++i)
@@ -210,13 +220,12 @@ __device__ __forceinline__ void issue_stage(const GemmCtx &c, int ks, int g, int
                                          (__attribute__((address_space(3))) void *)(sa + (i * 4 + wave) * 1024),
                                          16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((const void *)((c.b_base[i] + (size_t)ks * c.b_kstep) + c.b_off[i]),
-                                         (__attribute__((address_space(3))) void *)(sb + (i * 4 + wave) * 1024),
-                                         16, 0, 0);
-    __builtin_amdgcn_global_load_lds(
-        (const void *)(c.s_base + ((c.s_off + (uint32_t)ks * c.s_kstep + (uint32_t)g * c.s_step) & ~3u)),
-                                     (__attribute__((address_space(3))) void *)(ss + wave * 256), 4, 0, 0);
+    for (int ns = 0; ns < 2; ++ns)
+        bq[ns] = *reinterpret_cast<const uint4 *>(c.b_base[ns] + (size_t)ks * c.b_kstep + c.b_off[ns]);
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+        sw[ns] = *reinterpret_cast<const uint32_t *>(
+            c.s_base[ns] + ((c.s_off[ns] + (uint32_t)ks * c.s_kstep + (uint32_t)g * c.s_step) & ~3u));
 }
 
 // Main loop over K for a tile of MS x 32 rows.
@@ -226,15 +235,22 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
     // block scales per weight row and K-step)
     constexpr int G = FMT == 0 || FMT == 3 ? 64 : 128;
     constexpr int KPG = G / KS;
-    constexpr int LPS = MS + B_LOADS + 1;  // loads per thread and stage
-    constexpr int D = ring_depth<MS>();    // stages in the ring for this tile height
+    constexpr int LPS = MS + 4;          // loads per thread and stage
+    constexpr int D = ring_depth<MS>();  // stages in flight for this tile height
     static_assert(D >= 3 && (D - 2) * LPS <= 63, "wait counts fit vmcnt");
     const int l32 = lane & 31, hf = lane >> 5;
     const int NK = c.nk;
+    uint4 bq[D][2];      // per stage: the lane's codes of its two weight rows
+    uint32_t sw[D][2];   // per stage: their scale words
 
+    // Every step issues one stage, the steps past the end the last K-step
+    // again (never consumed), so that D - 1 stages are always in flight: one
+    // wait count for all steps, and no loads on conditional paths in the loop.
 #pragma unroll
-    for (int u = 0; u < D - 1; ++u)
-        if (u < NK) issue_stage<MS>(c, u, u / KPG, u, wave);
+    for (int u = 0; u < D - 1; ++u) {
+        const int kn = u < NK ? u : NK - 1;
+        issue_stage<MS>(c, kn, kn / KPG, u, wave, bq[u], sw[u]);
+    }
 
     // per N-subtile: scale and min of the current group, for the 1024 + q
     // pairs (index 0) and the 1024 + 16 q pairs (index 1)
@@ -244,91 +260,88 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
     const half2_t off0 = {(_Float16)(FMT == 0 ? 1024.0f : 1032.0f), (_Float16)(FMT == 0 ? 1024.0f : 1032.0f)};
     const half2_t off1 = {(_Float16)(FMT == 0 ? 1024.0f : 1152.0f), (_Float16)(FMT == 0 ? 1024.0f : 1152.0f)};
     const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    for (int kk = 0; kk < NK; kk += D) {
+    // K-step ks from ring slot u (a constant once the callers' loops unroll)
+    auto step = [&](int ks, int u) __attribute__((always_inline)) {
+        wait_stages<LPS>(D - 2);  // K-step ks has landed: only the D - 2 stages issued after it are in flight
+        lds_barrier();            // every wave's share of ks is in LDS; slot (u + D - 1) % D is free
+        const int kn = ks + D - 1 < NK ? ks + D - 1 : NK - 1;
+        issue_stage<MS>(c, kn, kn / KPG, (u + D - 1) % D, wave, bq[(u + D - 1) % D], sw[(u + D - 1) % D]);
+        const uint8_t *sa = c.ring[u];
+        if (FMT == 3) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int ks = kk + u;
-            if (ks < NK) {
-                // K-step ks has landed once only the stages issued after it are in flight
-                wait_stages<LPS>(NK - 1 - ks < D - 2 ? NK - 1 - ks : D - 2);
-                lds_barrier();  // every wave's share of ks is in LDS; slot (u + D - 1) % D is free
-                if (ks + D - 1 < NK) issue_stage<MS>(c, ks + D - 1, (ks + D - 1) / KPG, (u + D - 1) % D, wave);
-                const uint8_t *sa = c.ring + u * stage_bytes<MS>();
-                const uint8_t *sb = sa + MS * (A_BYTES / 4);
-                const uint32_t *ss = reinterpret_cast<const uint32_t *>(sb + B_BYTES);
-                if (FMT == 3) {
+            for (int ns = 0; ns < 2; ++ns) {
+                // blocks 2 hf and 2 hf + 1 of the K-step: k in [32 hf, 32 hf + 32)
+                const uint32_t pw = sw[u][ns] >> (16 * hf);
+                const uint32_t sp =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw, 1.0f, false));
+                nvs[ns][0] = (sp & 0xffffu) * 0x10001u;
+                nvs[ns][1] = (sp >> 16) * 0x10001u;
+            }
+        } else if (ks % KPG == 0) {
 #pragma unroll
-                    for (int ns = 0; ns < 2; ++ns) {
-                        // blocks 2 hf and 2 hf + 1 of the K-step: k in [32 hf, 32 hf + 32)
-                        const uint32_t pw = ss[c.brow[ns]] >> (16 * hf);
-                        const uint32_t sp =
-                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw, 1.0f, false));
-                        nvs[ns][0] = (sp & 0xffffu) * 0x10001u;
-                        nvs[ns][1] = (sp >> 16) * 0x10001u;
-                    }
-                } else if (ks % KPG == 0) {
-#pragma unroll
-                    for (int ns = 0; ns < 2; ++ns) {
-                        const uint32_t pw = ss[c.brow[ns]];
-                        if (FMT == 0) {
-                            s2[ns][0] = __builtin_bit_cast(half2_t, (pw & 0xffffu) * 0x10001u);
-                            m2[ns] = __builtin_bit_cast(half2_t, (pw >> 16) * 0x10001u);
-                        } else {
-                            const uint32_t h = ((c.spar[ns] + (uint32_t)(ks / KPG)) & 1u) ? pw >> 16 : pw & 0xffffu;
-                            s2[ns][0] = __builtin_bit_cast(half2_t, h * 0x10001u);
-                            m2[ns] = s2[ns][0];
-                        }
-                        s2[ns][1] = s2[ns][0] * sixteenth;
-                    }
+            for (int ns = 0; ns < 2; ++ns) {
+                const uint32_t pw = sw[u][ns];
+                if (FMT == 0) {
+                    s2[ns][0] = __builtin_bit_cast(half2_t, (pw & 0xffffu) * 0x10001u);
+                    m2[ns] = __builtin_bit_cast(half2_t, (pw >> 16) * 0x10001u);
+                } else {
+                    const uint32_t h = ((c.spar[ns] + (uint32_t)(ks / KPG)) & 1u) ? pw >> 16 : pw & 0xffffu;
+                    s2[ns][0] = __builtin_bit_cast(half2_t, h * 0x10001u);
+                    m2[ns] = s2[ns][0];
                 }
-                // B: 16 bytes (32 codes) of each of this lane's two weight rows
-                uint4 bw[2];
-#pragma unroll
-                for (int ns = 0; ns < 2; ++ns) {
-                    const int rb = c.brow[ns];
-                    bw[ns] = *reinterpret_cast<const uint4 *>(sb + rb * 32 + 16 * (hf ^ ((rb >> 3) & 1)));
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {  // matrix-core K-steps of 16: elements [32 hf + 8 s, +8) per lane
-                    u32x4_t bv[2];
-#pragma unroll
-                    for (int ns = 0; ns < 2; ++ns) {
-                        const uint32_t word = s == 0 ? bw[ns].x : s == 1 ? bw[ns].y : s == 2 ? bw[ns].z : bw[ns].w;
-                        if constexpr (FMT == 3) {
-                            // E2M1 pairs in natural order times the block scale: exact in f16
-                            const half2_t sc = __builtin_bit_cast(half2_t, nvs[ns][s >> 1]);
-                            auto nv = [&](uint32_t p) {
-                                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p) * sc);
-                            };
-                            bv[ns] = u32x4_t{
-                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0))),
-                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1))),
-                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2))),
-                                nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3)))};
-                        } else {
-                            const uint32_t w8 = word >> 8;
-                            bv[ns] = u32x4_t{
-                                dequant_pair<FMT>(insert_codes<0x000f000fu>(word, kf), off0, s2[ns][0], m2[ns]),
-                                dequant_pair<FMT>(insert_codes<0x00f000f0u>(word, kf), off1, s2[ns][1], m2[ns]),
-                                dequant_pair<FMT>(insert_codes<0x000f000fu>(w8, kf), off0, s2[ns][0], m2[ns]),
-                                dequant_pair<FMT>(insert_codes<0x00f000f0u>(w8, kf), off1, s2[ns][1], m2[ns])};
-                        }
-                    }
-                    const int ch = 4 * hf + s;  // logical 16-byte chunk of the A row
-#pragma unroll
-                    for (int mi = 0; mi < MS; ++mi) {
-                        const int r = 32 * mi + l32;
-                        const uint4 av = *reinterpret_cast<const uint4 *>(sa + r * 128 + 16 * (ch ^ ((r >> 1) & 7)));
-                        const f16x8_t a8 = __builtin_bit_cast(f16x8_t, u32x4_t{av.x, av.y, av.z, av.w});
-                        acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, __builtin_bit_cast(f16x8_t, bv[0]),
-                                                                            acc[mi][0], 0, 0, 0);
-                        acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, __builtin_bit_cast(f16x8_t, bv[1]),
-                                                                            acc[mi][1], 0, 0, 0);
-                    }
-                }
+                s2[ns][1] = s2[ns][0] * sixteenth;
             }
         }
+        // B: 16 bytes (32 codes) of each of this lane's two weight rows
+        const uint4 *bw = bq[u];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // matrix-core K-steps of 16: elements [32 hf + 8 s, +8) per lane
+            u32x4_t bv[2];
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns) {
+                const uint32_t word = s == 0 ? bw[ns].x : s == 1 ? bw[ns].y : s == 2 ? bw[ns].z : bw[ns].w;
+                if constexpr (FMT == 3) {
+                    // E2M1 pairs in natural order times the block scale: exact in f16
+                    const half2_t sc = __builtin_bit_cast(half2_t, nvs[ns][s >> 1]);
+                    auto nv = [&](uint32_t p) {
+                        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p) * sc);
+                    };
+                    bv[ns] = u32x4_t{
+                        nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0))),
+                        nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1))),
+                        nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2))),
+                        nv(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3)))};
+                } else {
+                    const uint32_t w8 = word >> 8;
+                    bv[ns] = u32x4_t{
+                        dequant_pair<FMT>(insert_codes<0x000f000fu>(word, kf), off0, s2[ns][0], m2[ns]),
+                        dequant_pair<FMT>(insert_codes<0x00f000f0u>(word, kf), off1, s2[ns][1], m2[ns]),
+                        dequant_pair<FMT>(insert_codes<0x000f000fu>(w8, kf), off0, s2[ns][0], m2[ns]),
+                        dequant_pair<FMT>(insert_codes<0x00f000f0u>(w8, kf), off1, s2[ns][1], m2[ns])};
+                }
+            }
+            const int ch = 4 * hf + s;  // logical 16-byte chunk of the A row
+#pragma unroll
+            for (int mi = 0; mi < MS; ++mi) {
+                const int r = 32 * mi + l32;
+                const uint4 av = *reinterpret_cast<const uint4 *>(sa + r * 128 + 16 * (ch ^ ((r >> 1) & 7)));
+                const f16x8_t a8 = __builtin_bit_cast(f16x8_t, u32x4_t{av.x, av.y, av.z, av.w});
+                acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, __builtin_bit_cast(f16x8_t, bv[0]),
+                                                                    acc[mi][0], 0, 0, 0);
+                acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, __builtin_bit_cast(f16x8_t, bv[1]),
+                                                                    acc[mi][1], 0, 0, 0);
+            }
+        }
+    };
+    int kk = 0;
+    for (; kk + D <= NK; kk += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) step(kk + u, u);
     }
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)
+        if (kk + u < NK) step(kk + u, u);
+    MOEQ4_WAIT_VM_LDS(0);  // the stages issued past the end have landed before the ring is reused
 }
 
 // STAGE 1: A = x16 rows gathered through perm, B = gate | up codes,
@@ -368,7 +381,11 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int l32 = lane & 31, hf = lane >> 5;
     const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring[NST * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring0[RSLOT_BIG];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring1[RSLOT_BIG];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring2[RSLOT_BIG];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring3[RSLOT3];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring4[RSLOT4];
     __shared__ int s_tok[BM];
     __shared__ float s_rs[BM];  // STAGE 1: 2^e of the row's token; STAGE 2: the row's gate
 
@@ -387,7 +404,11 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
 
     GemmCtx c;
-    c.ring = s_ring;
+    c.ring[0] = s_ring0;
+    c.ring[1] = s_ring1;
+    c.ring[2] = s_ring2;
+    c.ring[3] = s_ring3;
+    c.ring[4] = s_ring4;
     c.nk = K / KS;
     c.a_base = reinterpret_cast<const uint8_t *>(act);
     // A slot S = (i * 4 + wave) * 64 + lane (16 bytes): row S / 8 = 32 i + 8 wave + lane / 8,
@@ -400,63 +421,37 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
         const uint32_t arow = STAGE == 1 ? (uint32_t)s_tok[rr] * (uint32_t)H : (uint32_t)(row0 + rr) * (uint32_t)I;
         c.a_off[i] = (arow + 8u * ch) * 2u;
     }
-    // B slot S: weight row rb = S / 2 (rows 0-127 gate, 128-255 up in GEMM1),
-    // stored chunk S % 2 holding logical chunk (S % 2) ^ ((rb >> 3) & 1).
+    // B: lane (l32, hf) takes, of N-subtile ns, weight row brow[ns] (block
+    // rows 0-127 gate, 128-255 up in GEMM1) and per K-step the half hf of its
+    // 32 code bytes, with the row's scale word.
     const uint32_t row_bytes = (uint32_t)K / 2;
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-        const int S = (i * 4 + wave) * 64 + lane;
-        const int rb = S / 2, ch = (S % 2) ^ ((rb >> 3) & 1);
-        uint32_t wrow;
-        if (STAGE == 1) {
-            c.b_base[i] = i == 0 ? L.gq : L.uq;  // slots of load 0 are rows 0-127, of load 1 rows 128-255
-            wrow = (uint32_t)e * I + col_base + (rb & 127);
-        } else {
-            c.b_base[i] = L.dq;
-            wrow = (uint32_t)e * H + col_base + rb;
-        }
-        c.b_off[i] = wrow * row_bytes + 16u * ch;
-    }
-    // scale entries: thread tid covers weight row tid (waves 0-1 gate, 2-3 up in GEMM1)
-    {
-        const uint32_t esz = FMT == 0 || FMT == 3 ? 4u : 2u;
-        uint32_t wrow;
-        if (STAGE == 1) {
-            c.s_base = reinterpret_cast<const uint8_t *>(tid < 128 ? L.gsm : L.usm);
-            wrow = (uint32_t)e * I + col_base + (tid & 127);
-        } else {
-            c.s_base = reinterpret_cast<const uint8_t *>(L.dsm);
-            wrow = (uint32_t)e * H + col_base + tid;
-        }
-        c.s_off = wrow * (uint32_t)NG * esz;
-        c.s_step = esz;
-    }
-    c.b_kstep = KS / 2;
-    c.s_kstep = 0;
-    if (L.pack) {
-        // prefill copy: per K-step, tile (e, cb) holds its 256 rows' chunks in
-        // slot order (8 KB) and their scale words in row order (1 KB)
-        const PackLayout pl = pack_layout(L.E, H, I, FMT);
-        const size_t tile = (size_t)e * ncb + cb;
-        const uint8_t *q = L.pack + (STAGE == 1 ? pl.gu_q : pl.d_q) + tile * (size_t)c.nk * B_BYTES;
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-            c.b_base[i] = q;
-            c.b_off[i] = 16u * (uint32_t)((i * 4 + wave) * 64 + lane);
-        }
-        c.b_kstep = B_BYTES;
-        c.s_base = L.pack + (STAGE == 1 ? pl.gu_s : pl.d_s) + tile * (size_t)c.nk * S_BYTES;
-        c.s_off = 4u * (uint32_t)tid;
-        c.s_step = 0;
-        c.s_kstep = S_BYTES;
-    }
+    const uint32_t esz = FMT == 0 || FMT == 3 ? 4u : 2u;
+    const PackLayout pl = pack_layout(L.E, H, I, FMT);
+    const size_t tix = (size_t)e * ncb + cb;  // the tile's index in the copy
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
-        c.brow[ns] = STAGE == 1 ? ns * 128 + wave * 32 + l32 : wave * 64 + ns * 32 + l32;
-        const uint32_t wrow = STAGE == 1 ? (uint32_t)e * I + col_base + (c.brow[ns] & 127)
-                                         : (uint32_t)e * H + col_base + c.brow[ns];
+        const int rb = STAGE == 1 ? ns * 128 + wave * 32 + l32 : wave * 64 + ns * 32 + l32;
+        c.brow[ns] = rb;
+        const uint32_t wrow = STAGE == 1 ? (uint32_t)e * I + col_base + (rb & 127) : (uint32_t)e * H + col_base + rb;
         c.spar[ns] = (wrow * (uint32_t)NG) & 1u;
+        if (L.pack) {
+            // prefill copy: per K-step, tile (e, cb) holds its 256 rows' 32-byte
+            // chunks in row order (halves swapped when bit 3 of the row is set),
+            // then their scale words in row order
+            c.b_base[ns] = L.pack + (STAGE == 1 ? pl.gu_q : pl.d_q) + tix * (size_t)c.nk * B_BYTES;
+            c.b_off[ns] = (uint32_t)rb * 32u + 16u * (uint32_t)(hf ^ ((rb >> 3) & 1));
+            c.s_base[ns] = L.pack + (STAGE == 1 ? pl.gu_s : pl.d_s) + tix * (size_t)c.nk * S_BYTES;
+            c.s_off[ns] = 4u * (uint32_t)rb;
+        } else {
+            c.b_base[ns] = STAGE == 1 ? (ns == 0 ? L.gq : L.uq) : L.dq;
+            c.b_off[ns] = wrow * row_bytes + 16u * (uint32_t)hf;
+            c.s_base[ns] = reinterpret_cast<const uint8_t *>(STAGE == 1 ? (ns == 0 ? L.gsm : L.usm) : L.dsm);
+            c.s_off[ns] = wrow * (uint32_t)NG * esz;
+        }
     }
+    c.b_kstep = L.pack ? B_BYTES : KS / 2;
+    c.s_step = L.pack ? 0u : esz;
+    c.s_kstep = L.pack ? S_BYTES : 0u;
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -474,60 +469,53 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     __syncthreads();  // ring no longer read: the epilogue may reuse it
 
-    // ---- epilogue.  Accumulator element r of lane (l32, hf) in M-subtile mi
-    // is row 32 mi + 8 (r / 4) + 4 hf + (r % 4), column l32 of the subtile.
-    if (STAGE == 1) {
-        // h tile [BM][128] f16 in LDS, then coalesced 16-byte stores in PERM8 order.
-        uint16_t *s_h = reinterpret_cast<uint16_t *>(s_ring);
-        constexpr int HP = 128 + 8;
+    // ---- epilogue, one 32-row subtile at a time through ring slots 0-2 in
+    // turn (a slot is written again only after two more barriers).
+    // Accumulator element r of lane (l32, hf) in M-subtile mi is row
+    // 32 mi + 8 (r / 4) + 4 hf + (r % 4), column l32 of the subtile.
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (mi < msub) {
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= msub) break;
+        uint16_t *s_t = reinterpret_cast<uint16_t *>(mi % 3 == 0 ? s_ring0 : mi % 3 == 1 ? s_ring1 : s_ring2);
+        if (STAGE == 1) {
+            // h rows [32][128] f16 in LDS, then coalesced 16-byte stores in PERM8 order
+            constexpr int HP = 128 + 8;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
-                    const float sc = s_rs[row];
-                    const float gv = acc[mi][0][r] * sc;
-                    const float uv = acc[mi][1][r] * sc;
-                    const _Float16 hv = (_Float16)(silu(gv) * uv);
-                    s_h[row * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
+                const float sc = s_rs[32 * mi + lr];
+                const float gv = acc[mi][0][r] * sc;
+                const float uv = acc[mi][1][r] * sc;
+                const _Float16 hv = (_Float16)(silu(gv) * uv);
+                s_t[lr * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
+            }
+            __syncthreads();
+            for (int i = tid; i < 32 * 16; i += PF_BLOCK) {
+                const int lr = i / 16, cc = i % 16, row = 32 * mi + lr;
+                if (row < rows) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(&s_t[lr * HP + cc * 8]);
+                    uint4 o = v;
+                    if (FMT != 3) perm8(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
+                    *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
                 }
             }
-        }
-        __syncthreads();
-        for (int i = tid; i < BM * 16; i += PF_BLOCK) {
-            const int row = i / 16, cc = i % 16;
-            if (row < rows) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(&s_h[row * HP + cc * 8]);
-                uint4 o = v;
-                if (FMT != 3) perm8(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
-                *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
-            }
-        }
-    } else {
-        // z tile [BM][256] f16 in LDS, then coalesced 16-byte stores
-        uint16_t *s_z = reinterpret_cast<uint16_t *>(s_ring);
-        constexpr int ZP = BROWS + 8;
-        static_assert(BM * ZP * 2 <= NST * STAGE_BYTES, "z tile fits the ring");
+        } else {
+            // z rows [32][256] f16 in LDS, then coalesced 16-byte stores
+            constexpr int ZP = BROWS + 8;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (mi < msub) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
-                    const float gt = s_rs[row];
-                    s_z[row * ZP + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
-                    s_z[row * ZP + wave * 64 + 32 + l32] =
-                        __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
+                const float gt = s_rs[32 * mi + lr];
+                s_t[lr * ZP + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
+                s_t[lr * ZP + wave * 64 + 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
             }
-        }
-        __syncthreads();
-        for (int i = tid; i < BM * (BROWS / 8); i += PF_BLOCK) {
-            const int row = i / (BROWS / 8), cc = i % (BROWS / 8);
-            if (row < rows)
-                *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
-                    *reinterpret_cast<const uint4 *>(&s_z[row * ZP + cc * 8]);
+            __syncthreads();
+            for (int i = tid; i < 32 * (BROWS / 8); i += PF_BLOCK) {
+                const int lr = i / (BROWS / 8), cc = i % (BROWS / 8), row = 32 * mi + lr;
+                if (row < rows)
+                    *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
+                        *reinterpret_cast<const uint4 *>(&s_t[lr * ZP + cc * 8]);
+            }
         }
     }
 }
