@@ -545,7 +545,7 @@ constexpr int B8_BYTES = BROWS * KS;             // 16 KB: 256 rows x 64 codes
 constexpr int STAGE8_BYTES = A_BYTES + B8_BYTES;
 constexpr int B8_LOADS = B8_BYTES / 16 / PF_BLOCK;  // 4 sixteen-byte loads per thread and stage
 constexpr int ZP8 = BROWS + 8;
-constexpr int RING8_BYTES = NST8 * STAGE8_BYTES > BM * ZP8 * 2 ? NST8 * STAGE8_BYTES : BM * ZP8 * 2;
+static_assert(32 * ZP8 * 2 <= STAGE8_BYTES, "32 epilogue rows fit a ring slot");
 
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 
@@ -555,15 +555,15 @@ struct Gemm8Ctx {
     const uint8_t *b_base[B8_LOADS];
     uint32_t b_off[B8_LOADS];
     uint32_t b_kstep;    // bytes between K-steps of a weight row chunk
-    const float *sc[2];  // block scales of this wave's two N-subtiles, one per 128 inputs
-    uint8_t *ring;
+    const float *sc;     // LDS: block scales of this wave's two N-subtiles, [2][16] (one per 128 inputs)
+    uint8_t *ring[NST8]; // the ring slots, one LDS array each (see ring_depth)
     int brow[2];
     int nk;
 };
 
 template <int MS>
 __device__ __forceinline__ void issue_stage8(const Gemm8Ctx &c, int ks, int slot, int wave) {
-    uint8_t *sa = c.ring + slot * STAGE8_BYTES;
+    uint8_t *sa = c.ring[slot];
     uint8_t *sb = sa + A_BYTES;
     const uint8_t *ab = c.a_base + (size_t)ks * (KS * 2);
 #pragma unroll
@@ -598,7 +598,7 @@ __device__ __forceinline__ void gemm8_main(const Gemm8Ctx &c, f32x16_t (&acc)[4]
     for (int u = 0; u < NST8 - 1; ++u)
         if (u < NK) issue_stage8<MS>(c, u, u, wave);
     float sig[2] = {1.f, 1.f};
-    float snext[2] = {c.sc[0][0], c.sc[1][0]};
+    float snext[2] = {c.sc[0], c.sc[16]};
     for (int kk = 0; kk < NK; kk += NST8) {
 #pragma unroll
         for (int u = 0; u < NST8; ++u) {
@@ -624,10 +624,10 @@ __device__ __forceinline__ void gemm8_main(const Gemm8Ctx &c, f32x16_t (&acc)[4]
                             }
                             sig[ns] = sb;
                         }
-                        if (2 * (kb + 1) < NK) snext[ns] = c.sc[ns][kb + 1];
+                        if (2 * (kb + 1) < NK) snext[ns] = c.sc[16 * ns + kb + 1];
                     }
                 }
-                const uint8_t *sa = c.ring + u * STAGE8_BYTES;
+                const uint8_t *sa = c.ring[u];
                 const uint8_t *sbp = sa + A_BYTES;
                 // B: the lane's 32 codes (k in [32 hf, 32 hf + 32)) of each of its two weight rows
                 uint4 bw[2][2];
@@ -700,7 +700,9 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int l32 = lane & 31, hf = lane >> 5;
     const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring[RING8_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring0[STAGE8_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring1[STAGE8_BYTES];
+    __shared__ float s_sc8[4][2][16];  // per wave and N-subtile: the block scales along K (K <= 2048)
     __shared__ int s_tok[BM];
     __shared__ float s_gt[BM];  // STAGE 2: the row's gate
     if (tid < BM) {
@@ -717,7 +719,8 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
 
     Gemm8Ctx c;
-    c.ring = s_ring;
+    c.ring[0] = s_ring0;
+    c.ring[1] = s_ring1;
     c.nk = K / KS;
     c.a_base = reinterpret_cast<const uint8_t *>(act);
 #pragma unroll
@@ -765,8 +768,12 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int nrow = STAGE == 1 ? col_base : col_base + wave * 64 + ns * 32;
         const float *sbase = reinterpret_cast<const float *>(STAGE == 1 ? (ns == 0 ? L.gsm : L.usm) : L.dsm);
         const int N = STAGE == 1 ? I : H;
-        c.sc[ns] = sbase + ((size_t)e * (N / 128) + nrow / 128) * nkb;
+        // the wave's own copy in LDS: read in the loop without joining the
+        // vector-memory count that orders the ring
+        const int kb = lane & 15;
+        if ((lane >> 4) == ns && kb < nkb) s_sc8[wave][ns][kb] = sbase[((size_t)e * (N / 128) + nrow / 128) * nkb + kb];
     }
+    c.sc = &s_sc8[wave][0][0];
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -784,48 +791,41 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     __syncthreads();  // ring no longer read: the epilogue may reuse it
 
-    if (STAGE == 1) {
-        uint16_t *s_h = reinterpret_cast<uint16_t *>(s_ring);
-        constexpr int HP = 128 + 8;
+    // epilogue, one 32-row subtile at a time through the two ring slots in turn
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (mi < msub) {
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= msub) break;
+        uint16_t *s_t = reinterpret_cast<uint16_t *>(mi % 2 == 0 ? s_ring0 : s_ring1);
+        if (STAGE == 1) {
+            constexpr int HP = 128 + 8;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
-                    const _Float16 hv = (_Float16)(silu(acc[mi][0][r]) * acc[mi][1][r]);
-                    s_h[row * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
+                const _Float16 hv = (_Float16)(silu(acc[mi][0][r]) * acc[mi][1][r]);
+                s_t[lr * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
             }
-        }
-        __syncthreads();
-        for (int i = tid; i < BM * 16; i += PF_BLOCK) {
-            const int row = i / 16, cc = i % 16;
-            if (row < rows)
-                *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) =
-                    *reinterpret_cast<const uint4 *>(&s_h[row * HP + cc * 8]);
-        }
-    } else {
-        uint16_t *s_z = reinterpret_cast<uint16_t *>(s_ring);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (mi < msub) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
-                    const float gt = s_gt[row];
-                    s_z[row * ZP8 + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
-                    s_z[row * ZP8 + wave * 64 + 32 + l32] =
-                        __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
-                }
+            __syncthreads();
+            for (int i = tid; i < 32 * 16; i += PF_BLOCK) {
+                const int lr = i / 16, cc = i % 16, row = 32 * mi + lr;
+                if (row < rows)
+                    *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) =
+                        *reinterpret_cast<const uint4 *>(&s_t[lr * HP + cc * 8]);
             }
-        }
-        __syncthreads();
-        for (int i = tid; i < BM * (BROWS / 8); i += PF_BLOCK) {
-            const int row = i / (BROWS / 8), cc = i % (BROWS / 8);
-            if (row < rows)
-                *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
-                    *reinterpret_cast<const uint4 *>(&s_z[row * ZP8 + cc * 8]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
+                const float gt = s_gt[32 * mi + lr];
+                s_t[lr * ZP8 + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
+                s_t[lr * ZP8 + wave * 64 + 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
+            }
+            __syncthreads();
+            for (int i = tid; i < 32 * (BROWS / 8); i += PF_BLOCK) {
+                const int lr = i / (BROWS / 8), cc = i % (BROWS / 8), row = 32 * mi + lr;
+                if (row < rows)
+                    *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
+                        *reinterpret_cast<const uint4 *>(&s_t[lr * ZP8 + cc * 8]);
+            }
         }
     }
 }
@@ -853,7 +853,7 @@ constexpr int SG_B_BYTES = BROWS * KS;            // 16 KB: 256 rows x 64 int8 c
 constexpr int SG_STAGE = A_BYTES + SG_B_BYTES;    // 32 KB
 constexpr int SG_B_LOADS = SG_B_BYTES / 16 / PF_BLOCK;  // 4
 constexpr int SG_HP = 128 + 8;
-constexpr int SG_RING = SG_NST * SG_STAGE > BM * SG_HP * 2 ? SG_NST * SG_STAGE : BM * SG_HP * 2;
+static_assert(32 * SG_HP * 2 <= SG_STAGE, "32 epilogue rows fit a ring slot");
 
 struct SGemmCtx {
     const uint8_t *a_base;
@@ -861,14 +861,14 @@ struct SGemmCtx {
     const uint8_t *b_base[SG_B_LOADS];
     uint32_t b_off[SG_B_LOADS];
     const uint16_t *srow[2];  // this lane's two weight rows' group scales
-    uint8_t *ring;
+    uint8_t *ring[SG_NST];  // the ring slots, one LDS array each (see ring_depth)
     int brow[2];
     int nk;
 };
 
 template <int MS>
 __device__ __forceinline__ void sg_issue(const SGemmCtx &c, int ks, int slot, int wave) {
-    uint8_t *sa = c.ring + slot * SG_STAGE;
+    uint8_t *sa = c.ring[slot];
     uint8_t *sb = sa + A_BYTES;
     const uint8_t *ab = c.a_base + (size_t)ks * (KS * 2);
 #pragma unroll
@@ -917,7 +917,7 @@ __device__ __forceinline__ void sg_main(const SGemmCtx &c, f32x16_t (&acc)[4][2]
                         if (2 * (kg + 1) < NK) snext[ns] = (uint32_t)c.srow[ns][kg + 1];
                     }
                 }
-                const uint8_t *sa = c.ring + u * SG_STAGE;
+                const uint8_t *sa = c.ring[u];
                 const uint8_t *sbp = sa + A_BYTES;
                 uint4 bw[2][2];
 #pragma unroll
@@ -977,9 +977,11 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int l32 = lane & 31, hf = lane >> 5;
     const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring[SG_RING];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring0[SG_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring1[SG_STAGE];
     SGemmCtx c;
-    c.ring = s_ring;
+    c.ring[0] = s_ring0;
+    c.ring[1] = s_ring1;
     c.nk = K / KS;
     c.a_base = reinterpret_cast<const uint8_t *>(act);
 #pragma unroll
@@ -1028,27 +1030,27 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();  // ring no longer read
 
     if (STAGE == 1) {
-        uint16_t *s_h = reinterpret_cast<uint16_t *>(s_ring);
+        // one 32-row subtile at a time through the two ring slots in turn
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            if (mi < msub) {
+            if (mi >= msub) break;
+            uint16_t *s_h = reinterpret_cast<uint16_t *>(mi % 2 == 0 ? s_ring0 : s_ring1);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
-                    const float sc = row < rows ? ldexpf(1.0f, xexp[row0 + row]) : 0.f;
-                    const _Float16 hv = (_Float16)(silu(acc[mi][0][r] * sc) * (acc[mi][1][r] * sc));
-                    s_h[row * SG_HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 8 * (r / 4) + 4 * hf + (r % 4), row = 32 * mi + lr;
+                const float sc = row < rows ? ldexpf(1.0f, xexp[row0 + row]) : 0.f;
+                const _Float16 hv = (_Float16)(silu(acc[mi][0][r] * sc) * (acc[mi][1][r] * sc));
+                s_h[lr * SG_HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
             }
-        }
-        __syncthreads();
-        for (int i = tid; i < BM * 16; i += PF_BLOCK) {
-            const int row = i / 16, cc = i % 16;
-            if (row < rows) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(&s_h[row * SG_HP + cc * 8]);
-                const uint4 o = make_uint4((v.x & 0xffffu) | (v.y << 16), (v.x >> 16) | (v.y & 0xffff0000u),
-                                           (v.z & 0xffffu) | (v.w << 16), (v.z >> 16) | (v.w & 0xffff0000u));
-                *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
+            __syncthreads();
+            for (int i = tid; i < 32 * 16; i += PF_BLOCK) {
+                const int lr = i / 16, cc = i % 16, row = 32 * mi + lr;
+                if (row < rows) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(&s_h[lr * SG_HP + cc * 8]);
+                    const uint4 o = make_uint4((v.x & 0xffffu) | (v.y << 16), (v.x >> 16) | (v.y & 0xffff0000u),
+                                               (v.z & 0xffffu) | (v.w << 16), (v.z >> 16) | (v.w & 0xffff0000u));
+                    *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
+                }
             }
         }
     } else {
