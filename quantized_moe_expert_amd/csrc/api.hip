@@ -412,12 +412,17 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
         st = hip_status(launch_router_logits(xin, wr, bias, T, H, E, lg, s));
         if (st) return st;
     }
-    st = hip_status(launch_topk(lg, T, E, k, topk_idx, topk_gate, s));
-    if (st) return st;
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
-    st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
+    const bool prep = T * (int64_t)k > GROUP_SINGLE_MAX;
+    if (prep) {  // top-k, the grouping's count and the f16 rows of x in one launch
+        st = hip_status(launch_prefill_prep(lg, T, E, k, topk_idx, topk_gate, p.g, xin, H, p.x16, p.xexp, L.fmt, s));
+        if (!st) st = hip_status(launch_group_after_count(topk_idx, T, k, E, p.g, s));
+    } else {
+        st = hip_status(launch_topk(lg, T, E, k, topk_idx, topk_gate, s));
+        if (!st) st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
+    }
     if (st) return st;
-    st = hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev));
+    st = hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev, prep));
     return st ? st : shared_after(xin);
 }
 

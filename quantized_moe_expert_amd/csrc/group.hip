@@ -105,6 +105,14 @@ hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const Group
     if (yclear) return hipErrorInvalidValue;  // clearing is only offered on the one-block path
     const int nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
     hipLaunchKernelGGL(group_count_kernel, dim3(nch), dim3(256), 0, s, idx, P, E, g.chunk_cnt);
+    return launch_group_after_count(idx, T, k, E, g, s, e0, e1);
+}
+
+hipError_t launch_group_after_count(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
+                                    hipEvent_t e0, hipEvent_t e1) {
+    const int P = (int)(T * k);
+    if (P <= GROUP_SINGLE_MAX) return hipErrorInvalidValue;
+    const int nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
     hipLaunchKernelGGL(group_colscan_kernel, dim3(E), dim3(nch >= 1024 ? 1024 : ((nch + 63) / 64) * 64), 0, s,
                        nch, E, g);
     launch_k(group_scatter_kernel, dim3(nch), dim3(E > 64 ? ((E + 63) / 64) * 64 : 64), s, e0, e1, idx, P, E, g);

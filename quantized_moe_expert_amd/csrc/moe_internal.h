@@ -87,6 +87,10 @@ hipError_t launch_topk(const uint16_t *logits, int64_t T, int E, int k, int32_t 
 hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
                         float *yclear = nullptr, int64_t yclear_n = 0, hipEvent_t e0 = nullptr,
                         hipEvent_t e1 = nullptr);
+// The multi-block grouping after its count step (T*k > GROUP_SINGLE_MAX,
+// g.chunk_cnt filled, e.g. by launch_prefill_prep).
+hipError_t launch_group_after_count(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
+                                    hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // Decode expert kernels: gate/up + SwiGLU -> h (f16 [T*k][I], each 8-block
 // in PERM8 order, odd elements divided by 16), then down with the
@@ -128,7 +132,14 @@ hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 // combine.  y is written whole (no clearing needed).
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
-                                  float *y, hipStream_t s, hipEvent_t const *ev = nullptr);
+                                  float *y, hipStream_t s, hipEvent_t const *ev = nullptr, bool x16_ready = false);
+// Top-k of the given logits, the grouping's count step and the f16 rows of
+// x (format fmt's order; none for block FP8) in one launch, for
+// T*k > GROUP_SINGLE_MAX (then launch_group_after_count, and the experts
+// with x16_ready).
+hipError_t launch_prefill_prep(const uint16_t *logits, int64_t T, int E, int k, int32_t *idx, float *gate,
+                               const GroupOut &g, const uint16_t *x, int H, uint16_t *x16, int32_t *xexp, int fmt,
+                               hipStream_t s);
 
 // Launch on s; when e0 is given the runtime records e0 / e1 at the kernel's
 // own start and end (AMD extended launch), which times exactly that kernel.

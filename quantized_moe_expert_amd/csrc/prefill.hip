@@ -43,6 +43,7 @@
 // 3-stage ring of 64-element K-steps; each stage also carries the 256 scale
 // words of its group (one 4-byte direct-to-LDS load per thread).
 #include "moe_internal.h"
+#include "route_dev.h"
 #include "shared_dev.h"
 
 namespace moeq4 {
@@ -59,11 +60,9 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // elements inside each group of 8: 0 natural, 1 PERM8 (0,4,1,5,2,6,3,7),
 // 2 PERM4 (0,2,1,3,4,6,5,7).
 template <int ORDER>
-__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restrict__ x, int64_t T, int H,
-                                                       uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+__device__ __forceinline__ void x_row_to_f16(const uint16_t *__restrict__ x, int64_t t, int H,
+                                             uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
     const int lane = threadIdx.x & 63;
-    if (t >= T) return;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + t * H);
     uint32_t mx = 0;
     for (int i = lane; i < H / 8; i += 64) {
@@ -105,6 +104,56 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restric
         dst[i] = make_uint4(p[0], p[1], p[2], p[3]);
     }
     if (lane == 0) xexp[t] = e;
+}
+
+template <int ORDER>
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restrict__ x, int64_t T, int H,
+                                                       uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t < T) x_row_to_f16<ORDER>(x, t, H, x16, xexp);
+}
+
+// Preparation of the prefill path for more than GROUP_SINGLE_MAX pairs, in
+// one launch: workgroup c takes grouping chunk c (pairs 64 c .. 64 c + 63).
+// It takes the top-k of every token with a pair in the chunk and keeps the
+// chunk's pairs (a token across two chunks is ranked by both, each keeping
+// its own pairs), counts them per expert as the grouping's count step does,
+// and converts the x rows of the tokens whose first pair is in the chunk
+// (ORDER as x_to_f16_kernel; none when CONVERT is false).
+constexpr int PREP_WAVES = 8;  // one token of a top-8 chunk per wave
+
+template <int NPL, int ORDER, bool CONVERT>
+__global__ __launch_bounds__(PREP_WAVES * 64) void prefill_prep_kernel(const uint16_t *__restrict__ logits, int64_t T, int E,
+                                                           int k, int32_t *__restrict__ idx,
+                                                           float *__restrict__ gate, int32_t *__restrict__ chunk_cnt,
+                                                           const uint16_t *__restrict__ x, int H,
+                                                           uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
+    __shared__ unsigned long long s_mask[1024];
+    __shared__ int32_t s_ti[PREP_WAVES][32];
+    __shared__ float s_tg[PREP_WAVES][32];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x;
+    const int64_t P = T * k, p0 = (int64_t)c * GROUP_CHUNK;
+    const int64_t p1 = p0 + GROUP_CHUNK < P ? p0 + GROUP_CHUNK : P;
+    for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
+    __syncthreads();
+    for (int64_t t = p0 / k + wave; t <= (p1 - 1) / k; t += PREP_WAVES) {
+        topk_token_wave<NPL>(logits + t * E, E, k, s_ti[wave], s_tg[wave]);
+        if (lane < k) {
+            const int64_t p = t * k + lane;
+            if (p >= p0 && p < p1) {
+                const int32_t e = s_ti[wave][lane];
+                idx[p] = e;
+                gate[p] = s_tg[wave][lane];
+                atomicOr(&s_mask[clamp_expert(e, E)], 1ull << (p - p0));
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) chunk_cnt[(size_t)c * E + e] = __popcll(s_mask[e]);
+    if (CONVERT)
+        for (int64_t t = (p0 + k - 1) / k + wave; t < (p1 + k - 1) / k && t < T; t += PREP_WAVES)
+            x_row_to_f16<ORDER>(x, t, H, x16, xexp);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, int64_t n) {
@@ -1216,11 +1265,12 @@ hipError_t launch_prefill_pack(const LayerPtrs &L, uint8_t *dst, hipStream_t s) 
 template <int FMT>
 static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
-                                     float *y, hipStream_t s, hipEvent_t const *ev) {
+                                     float *y, hipStream_t s, hipEvent_t const *ev, bool x16_ready) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
-    hipLaunchKernelGGL(x_to_f16_kernel<FMT == 3 ? 0 : 1>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H,
-                       x16, xexp);
+    if (!x16_ready)
+        hipLaunchKernelGGL(x_to_f16_kernel<FMT == 3 ? 0 : 1>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T,
+                           H, x16, xexp);
     const unsigned nb1 = (unsigned)(8 * ((tiles + 7) / 8) * (I / 128));  // 8 XCDs x ranks per XCD x column blocks
     const unsigned nb2 = (unsigned)(8 * ((tiles + 7) / 8) * (H / BROWS));
     launch_k(grouped_gemm_kernel<FMT, 1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
@@ -1263,14 +1313,33 @@ static hipError_t launch_prefill_fp8(const uint16_t *x, const float *gate, int64
 
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
-                                  float *y, hipStream_t s, hipEvent_t const *ev) {
+                                  float *y, hipStream_t s, hipEvent_t const *ev, bool x16_ready) {
     switch (L.fmt) {
-        case 0: return launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
-        case 1: return launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
+        case 0: return launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev, x16_ready);
+        case 1: return launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev, x16_ready);
         case 2: return launch_prefill_fp8(x, gate, T, k, L, g, h, z, y, s, ev);
-        case 3: return launch_prefill_fmt<3>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev);
+        case 3: return launch_prefill_fmt<3>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev, x16_ready);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_prefill_prep(const uint16_t *logits, int64_t T, int E, int k, int32_t *idx, float *gate,
+                               const GroupOut &g, const uint16_t *x, int H, uint16_t *x16, int32_t *xexp, int fmt,
+                               hipStream_t s) {
+    const int64_t P = T * k;
+    if (P <= GROUP_SINGLE_MAX || E > 1024 || k > 32) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((P + GROUP_CHUNK - 1) / GROUP_CHUNK)), block(PREP_WAVES * 64);
+    const int npl = (E + 63) / 64;
+#define PREP(N, O, C) \
+    hipLaunchKernelGGL((prefill_prep_kernel<N, O, C>), grid, block, 0, s, logits, T, E, k, idx, gate, g.chunk_cnt, x, H, x16, xexp)
+#define PREP_N(O, C) \
+    if (npl <= 4) PREP(4, O, C); else if (npl <= 8) PREP(8, O, C); else PREP(16, O, C)
+    if (fmt == 2) PREP_N(0, false);       // block FP8: the GEMMs read x as given
+    else if (fmt == 3) PREP_N(0, true);   // NVFP4: x16 in natural order
+    else PREP_N(1, true);                 // int4: x16 in PERM8 order
+#undef PREP_N
+#undef PREP
+    return hipGetLastError();
 }
 
 }  // namespace moeq4

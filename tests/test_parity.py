@@ -385,6 +385,26 @@ def test_forward_given_logits_and_prefill_path():
                      f"forward T={T}")
 
 
+@pytest.mark.parametrize("fmt", [synth.FMT_ASYM_G64, synth.FMT_SYM_G128, synth.FMT_FP8_B128, synth.FMT_NVFP4])
+@pytest.mark.parametrize("T,k", [(300, 8), (229, 6), (1100, 1)])
+def test_forward_prefill_prep(fmt, T, k):
+    """moe_q4_forward above 1024 (token, slot) pairs takes the top-k, the
+    grouping's count and the f16 rows of x in one launch per 64-pair chunk:
+    k = 6 puts tokens across chunk boundaries, every T here leaves a partial
+    last chunk, k = 1 gives 64 tokens per chunk.  Expert indices bit-exact,
+    gates and outputs against the oracle, for every weight format."""
+    H, I, E = 512, 256, 64
+    say(f"[prep] fmt={fmt} T={T} k={k}")
+    lay = synth.random_layer(E, H, I, fmt, seed=13, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 13, f"prep/x/{T}", "cuda"))
+    logits = synth.bf16_bits(synth.normal((T, E), 1.0, 13, f"prep/l/{T}", "cuda"))
+    lg, idx, gate, y, _, _ = _forward(lay, x, None, logits, T, k)
+    ir, gr = oracle.topk(np_u16(logits), T, E, k)
+    assert np.array_equal(idx.cpu().numpy(), ir), "expert indices differ"
+    assert np.allclose(gate.cpu().numpy(), gr, rtol=GATE_RTOL, atol=0), "gates differ"
+    assert_close(y.cpu().numpy(), oracle_y(lay, np_u16(x), ir, gr, k), f"prep fmt={fmt} T={T} k={k}")
+
+
 def test_forward_residual_chain():
     """Frame recipe, 3 layers through moe_q4_forward with the residual fused:
     layer l gets the oracle's x_{l-1} and y_{l-1}; its x_l must equal the
