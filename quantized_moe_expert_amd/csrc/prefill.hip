@@ -114,11 +114,11 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t *__restric
 }
 
 // Preparation of the prefill path for more than GROUP_SINGLE_MAX pairs, in
-// one launch: workgroup c takes grouping chunk c (pairs 64 c .. 64 c + 63).
-// It takes the top-k of every token with a pair in the chunk and keeps the
-// chunk's pairs (a token across two chunks is ranked by both, each keeping
-// its own pairs), counts them per expert as the grouping's count step does,
-// and converts the x rows of the tokens whose first pair is in the chunk
+// one launch.  Workgroup c < nch takes grouping chunk c (pairs 64 c ..
+// 64 c + 63): it takes the top-k of every token with a pair in the chunk and
+// keeps the chunk's pairs (a token across two chunks is ranked by both, each
+// keeping its own pairs) and counts them per expert as the grouping's count
+// step does.  The workgroups after them convert the x rows, one per wave
 // (ORDER as x_to_f16_kernel; none when CONVERT is false).
 constexpr int PREP_WAVES = 8;  // one token of a top-8 chunk per wave
 
@@ -132,8 +132,15 @@ __global__ __launch_bounds__(PREP_WAVES * 64) void prefill_prep_kernel(const uin
     __shared__ int32_t s_ti[PREP_WAVES][32];
     __shared__ float s_tg[PREP_WAVES][32];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t P = T * k;
+    const int nch = (int)((P + GROUP_CHUNK - 1) / GROUP_CHUNK);
+    if ((int)blockIdx.x >= nch) {
+        const int64_t t = (int64_t)(blockIdx.x - nch) * PREP_WAVES + wave;
+        if (CONVERT && t < T) x_row_to_f16<ORDER>(x, t, H, x16, xexp);
+        return;
+    }
     const int c = blockIdx.x;
-    const int64_t P = T * k, p0 = (int64_t)c * GROUP_CHUNK;
+    const int64_t p0 = (int64_t)c * GROUP_CHUNK;
     const int64_t p1 = p0 + GROUP_CHUNK < P ? p0 + GROUP_CHUNK : P;
     for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
     __syncthreads();
@@ -151,9 +158,6 @@ __global__ __launch_bounds__(PREP_WAVES * 64) void prefill_prep_kernel(const uin
     }
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) chunk_cnt[(size_t)c * E + e] = __popcll(s_mask[e]);
-    if (CONVERT)
-        for (int64_t t = (p0 + k - 1) / k + wave; t < (p1 + k - 1) / k && t < T; t += PREP_WAVES)
-            x_row_to_f16<ORDER>(x, t, H, x16, xexp);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, int64_t n) {
@@ -1328,7 +1332,9 @@ hipError_t launch_prefill_prep(const uint16_t *logits, int64_t T, int E, int k, 
                                hipStream_t s) {
     const int64_t P = T * k;
     if (P <= GROUP_SINGLE_MAX || E > 1024 || k > 32) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((P + GROUP_CHUNK - 1) / GROUP_CHUNK)), block(PREP_WAVES * 64);
+    const int64_t nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
+    const int64_t nconv = fmt == 2 ? 0 : (T + PREP_WAVES - 1) / PREP_WAVES;  // row-conversion workgroups
+    const dim3 grid((unsigned)(nch + nconv)), block(PREP_WAVES * 64);
     const int npl = (E + 63) / 64;
 #define PREP(N, O, C) \
     hipLaunchKernelGGL((prefill_prep_kernel<N, O, C>), grid, block, 0, s, logits, T, E, k, idx, gate, g.chunk_cnt, x, H, x16, xexp)
