@@ -191,3 +191,23 @@ def test_forward_with_pack():
     yb = b.forward(case.x, logits=case.logits)
     torch.cuda.synchronize()
     assert torch.equal(ya.view(torch.int32), yb.view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("H,I", [(256, 128), (2048, 128), (256, 2048)])
+def test_prefill_extreme_shapes(fmt, H, I):
+    """The smallest and largest K loops of the grouped GEMMs (2 K-steps in
+    the down GEMM at I = 128, more stages in flight than K-steps; 32 at
+    2048) and single column blocks, with 150 rows per expert on average
+    (full and partial tiles) over the multi-block grouping: outputs against
+    the oracle, and bit-identical with and without the prefill copy."""
+    T, E, k = 600, 8, 2
+    say(f"[pack extreme] fmt={fmt} H={H} I={I}")
+    lay = synth.random_layer(E, H, I, fmt, seed=17, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 17, f"pkx/x/{H}", "cuda"))
+    logits = synth.bf16_bits(synth.normal((T, E), 1.0, 17, f"pkx/l/{H}/{I}", "cuda"))
+    lg, idx, gate = hip_route(None, None, logits, T, H, E, k)
+    ir, gr = oracle.topk(np_u16(logits), T, E, k)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    y = _both(lay, x, idx, gate, k)
+    assert_close(y.cpu().numpy(), oracle_y(lay, np_u16(x), ir, gr, k), f"pack extreme fmt={fmt} H={H} I={I}")
