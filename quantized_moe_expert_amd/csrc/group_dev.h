@@ -82,10 +82,74 @@ __device__ inline void record_tile_pair(const GroupOut &g, int pos, int tadj, in
     if (u < DECODE_TT) g.tiles[r / S].pair[u] = p;
 }
 
+// Grouping of few pairs (P <= GROUP_RANK_MAX, at most one pair per thread)
+// without scans: pair i's sorted position is the number of pairs (e_j, j)
+// ordered before (e_i, i); its row within its expert, its expert's count and
+// offset, and the tiles of the experts before it are counts over the same P
+// pairs (an expert's tiles counted at its first pair).  Same outputs as the
+// scan path below; no tile schedule.
+__device__ inline void group_block_rank(const int32_t *idx, int P, int E, const GroupOut &g) {
+    __shared__ int s_e[GROUP_RANK_MAX];
+    __shared__ int s_nt[GROUP_RANK_MAX];  // tiles of the pair's expert at its first pair, else 0
+    const int tid = threadIdx.x;
+    const int S = g.rows_per_tile;
+    int e = 0, pos = 0, rin = 0, cnt = 0;
+    if (tid < P) s_e[tid] = e = clamp_expert(idx[tid], E);
+    __syncthreads();
+    if (tid < P) {
+#pragma unroll 8
+        for (int j = 0; j < P; ++j) {
+            const int ej = s_e[j];
+            pos += ej < e || (ej == e && j < tid);
+            rin += ej == e && j < tid;
+            cnt += ej == e;
+        }
+        s_nt[tid] = rin == 0 ? (cnt + S - 1) / S : 0;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += blockDim.x) {
+        int c = 0, o = 0;
+#pragma unroll 8
+        for (int j = 0; j < P; ++j) {
+            const int ej = s_e[j];
+            c += ej == x;
+            o += ej < x;
+        }
+        g.cnt[x] = c;
+        g.off[x] = o;
+    }
+    if (tid == 0) g.off[E] = P;
+    if (tid < P) {
+        int toff = 0, ntot = 0;
+#pragma unroll 8
+        for (int j = 0; j < P; ++j) {
+            const int ntj = s_nt[j];
+            ntot += ntj;
+            toff += s_e[j] < e ? ntj : 0;
+        }
+        const int t = toff + rin / S, u = rin % S;
+        g.perm[pos] = tid;
+        g.inv[tid] = pos;
+        if (u == 0) {
+            Tile &tl = g.tiles[t];
+            tl.expert = e;
+            tl.row0 = pos;
+            tl.rows = cnt - rin < S ? cnt - rin : S;
+            tl.pad = 0;
+        }
+        if (u < DECODE_TT) g.tiles[t].pair[u] = tid;
+        if (tid == 0) *g.ntiles = ntot;
+    }
+}
+
 // Whole grouping by one block of 1024 threads (pairs P <= GROUP_SINGLE_MAX).
 // idx may have been written earlier by this same block (visible after a
 // __syncthreads()).
 __device__ inline void group_block_single(const int32_t *idx, int P, int E, const GroupOut &g) {
+    if (P <= GROUP_RANK_MAX && P <= (int)blockDim.x && !g.order) {
+        group_block_rank(idx, P, E, g);
+        return;
+    }
     __shared__ int s_cnt[1024];
     __shared__ int s_base[1024];
     __shared__ unsigned long long s_mask[1024];

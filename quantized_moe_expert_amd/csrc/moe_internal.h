@@ -49,6 +49,7 @@ __host__ __device__ inline PackLayout pack_layout(int E, int H, int I, int fmt) 
 
 constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chunk
 constexpr int GROUP_SINGLE_MAX = 1024;   // pairs handled by the one-block grouping
+constexpr int GROUP_RANK_MAX = 64;       // pairs up to which it ranks them directly (no scans)
 constexpr int PREFILL_BM = 128;          // rows per prefill tile
 constexpr int ROUTE_LDS_LOGITS = 16384;  // T * E limit of the one-launch decode routing
 constexpr int ROUTE_TG = 4;              // tokens per workgroup of the one-launch routing

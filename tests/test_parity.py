@@ -152,8 +152,8 @@ def _hip_group(idx, T, k, E):
     return [t.cpu().numpy() for t in (cnt, off, perm, inv)]
 
 
-@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (4, 2, 16), (16, 8, 256), (64, 8, 256), (128, 8, 256),
-                                   (129, 8, 256), (512, 8, 256), (4096, 8, 256), (333, 3, 1000)])
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (4, 2, 16), (16, 8, 256), (32, 8, 256), (64, 4, 16), (64, 8, 256),
+                                   (128, 8, 256), (129, 8, 256), (512, 8, 256), (4096, 8, 256), (333, 3, 1000)])
 def test_group_exact(T, k, E):
     say(f"[group] T={T} k={k} E={E}")
     g = synth.generator(4, f"grp/{T}/{k}/{E}", "cuda")
