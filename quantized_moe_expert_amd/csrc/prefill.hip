@@ -38,10 +38,13 @@
 // columns, so SwiGLU pairs in registers; GEMM2: two groups of 32 output
 // columns) for every M-subtile of 32 rows the tile uses; the main loop is
 // instantiated per M-subtile count, so ragged tiles issue neither the loads
-// nor the matrix-core work of their empty subtiles.  Both operands travel
+// nor the matrix-core work of their empty subtiles.  The A rows travel
 // global -> LDS by direct-to-LDS loads (global_load_lds_dwordx4) through a
-// 3-stage ring of 64-element K-steps; each stage also carries the 256 scale
-// words of its group (one 4-byte direct-to-LDS load per thread).
+// ring of 64-element K-steps, one LDS array per slot, 4 to 5 stages deep; a
+// lane's codes and scale words of each stage go straight to registers (from
+// the prefill copy when the layer has one: contiguous per wave and step).
+// The tiles are taken largest first (the grouping's schedule), dealt to the
+// XCDs round-robin.
 #include "moe_internal.h"
 #include "route_dev.h"
 #include "shared_dev.h"
@@ -192,13 +195,10 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t v, half2_t off, half2_
 #define MOEQ4_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 0xf) | (((n) >> 4) << 14) | (0x7 << 4))
 
 constexpr int KS = 64;       // contraction elements per pipeline stage
-constexpr int NST = 3;       // LDS ring stages
 constexpr int BROWS = 256;   // weight rows per workgroup (gate 128 + up 128, or 256 down rows)
 constexpr int A_BYTES = BM * KS * 2;            // 16 KB: 128 rows x 64 f16
 constexpr int B_BYTES = BROWS * KS / 2;         // 8 KB: 256 rows x 64 codes
 constexpr int S_BYTES = BROWS * 4;              // 1 KB: one scale word per weight row
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-constexpr int B_LOADS = B_BYTES / 16 / PF_BLOCK;  // 2 sixteen-byte loads per thread and stage
 
 // The LDS ring holds the A rows of each stage (4 KB per 32-row subtile in
 // use); a lane's codes and scale words of a stage go to registers (10 VGPRs
@@ -590,8 +590,10 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
 // nonzero block scale met: at each K-block with scale s != 0 it is multiplied
 // by sigma / s (rounded once) before the block's products, and by sigma at
 // the end.  An all-zero block (scale 0, codes 0) adds nothing.
-// Tiles, work order and the LDS ring are as above, with 64 bytes of codes
-// per weight row and K-step, two ring stages (two workgroups per CU).
+// Tiles and work order are as above.  Both the A rows and the codes (64
+// bytes per weight row and K-step, from the prefill copy when there is one)
+// go through a two-stage LDS ring, one array per slot (two workgroups per
+// CU); each wave's block scales along K sit in a small LDS array of their own.
 
 constexpr int NST8 = 2;
 constexpr int B8_BYTES = BROWS * KS;             // 16 KB: 256 rows x 64 codes
