@@ -32,6 +32,10 @@ Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
                 the shared expert alone for the long prompt's 4096 tokens
                 (matrix-core GEMMs).
 
+The prefill workloads give the layer its prefill copy of the weights
+(moe_q4_prefill_pack, made once before timing, as at weight load); with
+--no-pack the grouped GEMMs read the canonical arrays.
+
 One JSON line on stdout: value = tokens/s of whole steps (inputs resident in
 HBM), roofline of the dominant kernel measured with HIP events recorded on the
 launch stream at its stage boundaries, and the CPU oracle timed on a bounded
