@@ -386,12 +386,12 @@ def test_forward_given_logits_and_prefill_path():
 
 
 @pytest.mark.parametrize("fmt", [synth.FMT_ASYM_G64, synth.FMT_SYM_G128, synth.FMT_FP8_B128, synth.FMT_NVFP4])
-@pytest.mark.parametrize("T,k", [(300, 8), (229, 6), (1100, 1)])
+@pytest.mark.parametrize("T,k", [(300, 8), (229, 6), (1100, 1), (40, 32), (401, 3)])
 def test_forward_prefill_prep(fmt, T, k):
     """moe_q4_forward above 1024 (token, slot) pairs takes the top-k, the
     grouping's count and the f16 rows of x in one launch per 64-pair chunk:
-    k = 6 puts tokens across chunk boundaries, every T here leaves a partial
-    last chunk, k = 1 gives 64 tokens per chunk.  Expert indices bit-exact,
+    k = 6 and 3 put tokens across chunk boundaries, every T here leaves a
+    partial last chunk, k = 1 gives 64 tokens per chunk and k = 32 two.  Expert indices bit-exact,
     gates and outputs against the oracle, for every weight format."""
     H, I, E = 512, 256, 64
     say(f"[prep] fmt={fmt} T={T} k={k}")
