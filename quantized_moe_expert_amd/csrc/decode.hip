@@ -607,7 +607,6 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         yclear[i] = 0.f;
         if (yres) xout[i] = f32_to_bf16_rne(bf16_to_f32(x[i]) + yres[i]);
     }
-    const uint16_t *lsrc = logits;
     if (wr) {
         // workgroup = (group of ROUTE_EG experts, group of ROUTE_TG tokens);
         // wave w takes expert w / ROUTE_TG and token w % ROUTE_TG of them
@@ -690,14 +689,31 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         }
         __syncthreads();
         if (!s_last) return;
-        for (int i = tid; i < T * E; i += blockDim.x)
-            s_lg[i] = (uint16_t)__hip_atomic_load(handoff + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every hand-off load of the thread in flight before the first is
+        // used (one memory round trip, not one per load)
+        constexpr int HO = ROUTE_LDS_LOGITS / 1024;
+        const int n_lg = T * E;
+        uint32_t hv[HO];
+#pragma unroll
+        for (int j = 0; j < HO; ++j) {
+            const int i = tid + j * 1024;
+            if (j * 1024 < n_lg) hv[j] = __hip_atomic_load(handoff + (i < n_lg ? i : n_lg - 1), __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int j = 0; j < HO; ++j) {
+            const int i = tid + j * 1024;
+            if (i < n_lg) s_lg[i] = (uint16_t)hv[j];
+        }
         __syncthreads();
-        lsrc = s_lg;
+        // top-k from the LDS copy (LDS reads, not generic ones)
+        for (int t = wave; t < T; t += 16)
+            topk_token_wave<NPL>(s_lg + (size_t)t * E, E, k, idx + t * k, gate + t * k, s_idx + t * k);
+    } else {
+        if (!tail) return;
+        for (int t = wave; t < T; t += 16)
+            topk_token_wave<NPL>(logits + (size_t)t * E, E, k, idx + t * k, gate + t * k, s_idx + t * k);
     }
-    if (!tail) return;
-    for (int t = wave; t < T; t += 16)
-        topk_token_wave<NPL>(lsrc + (size_t)t * E, E, k, idx + t * k, gate + t * k, s_idx + t * k);
     __syncthreads();
     group_block_single(s_idx, T * k, E, g);
     if (wr && tid < 9)  // every workgroup has counted in: reset for the next call

@@ -33,17 +33,27 @@ __device__ inline int block_exclusive_scan(int v, int *lds16, int *total) {
 __device__ inline void emit_offsets_and_tiles(int v, int E, int P, const GroupOut &g, int *lds16, int *excl_out,
                                               int *tadj_out) {
     const int e = threadIdx.x;
-    int total;
-    const int excl = block_exclusive_scan(v, lds16, &total);
+    const int S = g.rows_per_tile;
+    const int nt = e < E ? (v + S - 1) / S : 0;
+    int excl, toff, ntot;
+    if (P < 32768) {
+        // counts and tile counts in one scan, 16 bits each: every prefix of
+        // either is at most P (an expert's tiles are at most its rows)
+        int tot;
+        const int pk = block_exclusive_scan((e < E ? v : 0) | (nt << 16), lds16, &tot);
+        excl = pk & 0xffff;
+        toff = pk >> 16;
+        ntot = tot >> 16;
+    } else {
+        int total;
+        excl = block_exclusive_scan(v, lds16, &total);
+        toff = block_exclusive_scan(nt, lds16, &ntot);
+    }
     if (e < E) {
         g.cnt[e] = v;
         g.off[e] = excl;
     }
     if (e == 0) g.off[E] = P;
-    const int S = g.rows_per_tile;
-    const int nt = e < E ? (v + S - 1) / S : 0;
-    int ntot;
-    const int toff = block_exclusive_scan(nt, lds16, &ntot);
     for (int j = 0; j < nt; ++j) {
         Tile &t = g.tiles[toff + j];
         t.expert = e;

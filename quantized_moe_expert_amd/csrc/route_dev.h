@@ -50,11 +50,19 @@ template <int NPL>
 __device__ inline void topk_token_wave(const uint16_t *__restrict__ l, int E, int k, int32_t *__restrict__ idx_out,
                                        float *__restrict__ gate_out, int32_t *idx_copy = nullptr) {
     const int lane = threadIdx.x & 63;
+    // every load issued before the first use (clamped index, masked after),
+    // so the NPL reads share one wait
+    uint16_t lv[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int e = j * WAVE + lane;
+        lv[j] = l[e < E ? e : E - 1];
+    }
     uint32_t key[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const int e = j * WAVE + lane;
-        key[j] = e < E ? (bf16_order(l[e]) << 16) | (0xffffu - (uint32_t)e) : 0u;
+        key[j] = e < E ? (bf16_order(lv[j]) << 16) | (0xffffu - (uint32_t)e) : 0u;
     }
     // sorting network, largest first
     auto cswap = [&](int a, int b) {
