@@ -95,6 +95,7 @@ GroupOut carve_group(Carver &c, int64_t T, int E, int k, int rows_per_tile, bool
     g.chunk_cnt = c.take<int32_t>(multi ? nch * E : 0);
     g.chunk_base = c.take<int32_t>(multi ? nch * E : 0);
     g.order = schedule ? c.take<int32_t>(max_tiles(P, E, rows_per_tile)) : nullptr;
+    g.order2 = schedule ? c.take<int32_t>(max_tiles(P, E, rows_per_tile)) : nullptr;
     return g;
 }
 

@@ -690,7 +690,9 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         __syncthreads();
         if (!s_last) return;
         // every hand-off load of the thread in flight before the first is
-        // used (one memory round trip, not one per load)
+        // used (one memory round trip, not one per load); the launch has
+        // 1024 threads and T * E <= ROUTE_LDS_LOGITS
+        static_assert(ROUTE_LDS_LOGITS % 1024 == 0, "hand-off loads per thread");
         constexpr int HO = ROUTE_LDS_LOGITS / 1024;
         const int n_lg = T * E;
         uint32_t hv[HO];

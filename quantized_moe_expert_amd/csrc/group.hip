@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void group_count_kernel(const int32_t *__restr
 // the chunks (chunk order = pair order), written as each chunk's starting rank
 // inside the expert; the total goes to cnt[e].
 __global__ __launch_bounds__(1024) void group_colscan_kernel(int nchunks, int E, GroupOut g) {
-    __shared__ int s_scan[17];
+    __shared__ int s_scan[GROUP_SCAN_LDS];
     const int e = blockIdx.x;
     int carry = 0;
     for (int c0 = 0; c0 < nchunks; c0 += blockDim.x) {
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
     __shared__ unsigned long long s_mask[1024];
     __shared__ int s_off[1024];
     __shared__ int s_tadj[1024];
-    __shared__ int s_scan[17];
+    __shared__ int s_scan[GROUP_SCAN_LDS];
     const int c = blockIdx.x, tid = threadIdx.x;
     const int v = tid < E ? g.cnt[tid] : 0;
     if (tid < E) s_mask[tid] = 0ull;
@@ -68,11 +68,12 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
     if (c == 0) {
         emit_offsets_and_tiles(v, E, P, g, s_scan, &excl, &tadj);
     } else {
-        int total;
-        excl = block_exclusive_scan(v, s_scan, &total);
         const int S = g.rows_per_tile;
-        const int toff = block_exclusive_scan(tid < E ? (v + S - 1) / S : 0, s_scan, &total);
-        tadj = toff * S - excl;
+        const int in[2] = {v, tid < E ? (v + S - 1) / S : 0};
+        int ex[2], tt[2];
+        block_exclusive_scan_n<2>(in, s_scan, ex, tt);
+        excl = ex[0];
+        tadj = ex[1] * S - excl;
     }
     if (tid < E) {
         s_off[tid] = excl;

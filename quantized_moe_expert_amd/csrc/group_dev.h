@@ -6,22 +6,45 @@
 
 namespace moeq4 {
 
-// Exclusive scan over the block (blockDim.x a multiple of 64, at most 1024).
-// Returns the exclusive prefix of v; *total receives the block sum.
-__device__ inline int block_exclusive_scan(int v, int *lds16, int *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int inc = wave_inclusive_scan_i32(v);
-    if (lane == 63) lds16[wave] = inc;
-    __syncthreads();
-    int pre = 0, tot = 0;  // totals of the waves before this one, of all waves
-    for (int w = 0; w < nw; ++w) {
-        const int t = lds16[w];
-        pre += w < wave ? t : 0;
-        tot += t;
+// N exclusive scans over the block at once (blockDim.x a multiple of 64, at
+// most 1024), sharing the two barriers.  lds: GROUP_SCAN_LDS ints.  Each
+// wave publishes its totals; lane w of every wave then reads wave w's, and
+// one wave scan over those lanes gives the wave's prefix (lane wave - 1) and
+// the block total (lane 15): one LDS read per value, few registers.
+constexpr int GROUP_SCAN_N = 5;
+constexpr int GROUP_SCAN_LDS = 16 * GROUP_SCAN_N;
+template <int N>
+__device__ inline void block_exclusive_scan_n(const int (&v)[N], int *lds, int (&excl)[N], int (&total)[N]) {
+    static_assert(N >= 1 && N <= GROUP_SCAN_N, "scan count");
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    int inc[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        inc[j] = wave_inclusive_scan_i32(v[j]);
+        if (lane == 63) lds[16 * j + wave] = inc[j];
     }
-    __syncthreads();  // lds16 free for the next scan
-    *total = tot;
-    return pre + inc - v;
+    __syncthreads();
+    int t[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) t[j] = lane < nw ? lds[16 * j + lane] : 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const int p = wave_inclusive_scan_i32(t[j]);  // lane w: totals of waves 0..w
+        const int pre = wave > 0 ? __builtin_amdgcn_readlane(p, wave - 1) : 0;
+        total[j] = __builtin_amdgcn_readlane(p, 15);  // lanes nw..15 add 0
+        excl[j] = pre + inc[j] - v[j];
+    }
+    __syncthreads();  // lds free for the next scan
+}
+
+// One exclusive scan over the block; *total receives the block sum.
+__device__ inline int block_exclusive_scan(int v, int *lds, int *total) {
+    const int in[1] = {v};
+    int ex[1], tt[1];
+    block_exclusive_scan_n<1>(in, lds, ex, tt);
+    *total = tt[0];
+    return ex[0];
 }
 
 // Offsets + tile list from per-expert counts held by thread e (< E).  Only
@@ -29,25 +52,62 @@ __device__ inline int block_exclusive_scan(int v, int *lds16, int *total) {
 // min(rows, DECODE_TT) is written by record_tile_pair once the sorted
 // positions are known (possibly by other blocks, hence no write of the pair
 // fields here).  *tadj_out = toff * S - excl of expert e (toff: index of its
-// first tile, S: rows per tile).
-__device__ inline void emit_offsets_and_tiles(int v, int E, int P, const GroupOut &g, int *lds16, int *excl_out,
+// first tile, S: rows per tile).  lds: GROUP_SCAN_LDS ints.
+//
+// With g.order, also the schedules of the grouped GEMMs, which run tile rank
+// t on XCD t mod 8, consecutive ranks of one XCD one after another.
+//   order (gate/up GEMM): tiles by their count of S/4-row subtiles, most
+//     first (full tiles, then partial tiles of 4, 3, 2 and 1 subtiles), each
+//     expert's in tile order within a count;
+//   order2 (down GEMM, when set):
+//     A. full tiles, expert order (a paired expert's last one excepted);
+//     B. pairs in blocks of 16 ranks: 8 experts' last full tiles, then their
+//        partial tiles in the same order, so each partial tile runs on its
+//        full tile's XCD right after it and reads the same weights while they
+//        are in that XCD's L2 (the experts with full tiles and a partial one,
+//        in expert order, as many as fill whole blocks of 8);
+//     C. the other partial tiles by subtile count, most first.
+// Largest work first, so each XCD ends with its smallest tiles (order2 gives
+// up some of that for the shared weight reads).
+__device__ inline void emit_offsets_and_tiles(int v, int E, int P, const GroupOut &g, int *lds, int *excl_out,
                                               int *tadj_out) {
     const int e = threadIdx.x;
     const int S = g.rows_per_tile;
-    const int nt = e < E ? (v + S - 1) / S : 0;
-    int excl, toff, ntot;
-    if (P < 32768) {
-        // counts and tile counts in one scan, 16 bits each: every prefix of
-        // either is at most P (an expert's tiles are at most its rows)
+    const int vv = e < E ? v : 0;
+    const int nt = (vv + S - 1) / S;
+    const int nf = vv / S, rem = vv - nf * S;
+    const int qp = rem > 0 ? (rem + S / 4 - 1) / (S / 4) : 0;  // subtiles of the partial tile
+    const int flag = g.order2 && nf > 0 && rem > 0;          // pairing candidate
+    int excl, toff, ntot, pi = 0, npair = 0;
+    if (P < 65536 && P / S + (P < E ? P : E) < 32768) {
+        // counts and tile counts in one value, 16 bits each (every prefix of
+        // the counts is at most P, of the tile counts below 2^15)
+        const int pk = vv | (nt << 16);
         int tot;
-        const int pk = block_exclusive_scan((e < E ? v : 0) | (nt << 16), lds16, &tot);
-        excl = pk & 0xffff;
-        toff = pk >> 16;
+        if (g.order2) {
+            const int in[2] = {pk, flag};
+            int ex[2], tt[2];
+            block_exclusive_scan_n<2>(in, lds, ex, tt);
+            excl = ex[0] & 0xffff;
+            toff = ex[0] >> 16;
+            tot = tt[0];
+            pi = ex[1];
+            npair = tt[1];
+        } else {
+            const int ex = block_exclusive_scan(pk, lds, &tot);
+            excl = ex & 0xffff;
+            toff = ex >> 16;
+        }
         ntot = tot >> 16;
     } else {
-        int total;
-        excl = block_exclusive_scan(v, lds16, &total);
-        toff = block_exclusive_scan(nt, lds16, &ntot);
+        const int in[3] = {vv, nt, flag};
+        int ex[3], tt[3];
+        block_exclusive_scan_n<3>(in, lds, ex, tt);
+        excl = ex[0];
+        toff = ex[1];
+        ntot = tt[1];
+        pi = ex[2];
+        npair = tt[2];
     }
     if (e < E) {
         g.cnt[e] = v;
@@ -58,25 +118,39 @@ __device__ inline void emit_offsets_and_tiles(int v, int E, int P, const GroupOu
         Tile &t = g.tiles[toff + j];
         t.expert = e;
         t.row0 = excl + j * S;
-        t.rows = v - j * S < S ? v - j * S : S;
+        t.rows = vv - j * S < S ? vv - j * S : S;
         t.pad = 0;
     }
     if (e == 0) *g.ntiles = ntot;
     if (g.order) {
-        // Schedule for the grouped GEMMs: the tiles ranked by their count of
-        // S/4-row subtiles, most first (full tiles, then partial tiles of 4,
-        // 3, 2 and 1 subtiles), each expert's in tile order within a rank.
-        const int nf = e < E ? v / S : 0, rem = e < E ? v - nf * S : 0;
-        const int qp = rem > 0 ? (rem + S / 4 - 1) / (S / 4) : 0;  // subtiles of the partial tile
-        int base = 0;
-        for (int q = 4; q >= 1; --q) {
-            const int cq = (q == 4 ? nf : 0) + (qp == q ? 1 : 0);
-            int tq;
-            const int oq = block_exclusive_scan(cq, lds16, &tq);
-            if (q == 4)
-                for (int j = 0; j < nf; ++j) g.order[base + oq + j] = toff + j;
-            if (qp == q) g.order[base + oq + (q == 4 ? nf : 0)] = toff + nf;
-            base += tq;
+        const int in[4] = {nf + (qp == 4), qp == 3, qp == 2, qp == 1};
+        int ex[4], tt[4];
+        block_exclusive_scan_n<4>(in, lds, ex, tt);
+        for (int j = 0; j < nf; ++j) g.order[ex[0] + j] = toff + j;
+        if (qp > 0) {
+            int base = 0;
+            for (int q = 4; q > qp; --q) base += tt[4 - q];
+            g.order[base + ex[4 - qp] + (qp == 4 ? nf : 0)] = toff + nf;
+        }
+    }
+    if (g.order2) {
+        const int nblk = npair / 8;
+        const bool paired = flag && pi < 8 * nblk;
+        // counts per section: A, then C by subtile count 4, 3, 2, 1
+        const int in[5] = {nf - (paired ? 1 : 0), !paired && qp == 4, !paired && qp == 3, !paired && qp == 2,
+                           !paired && qp == 1};
+        int ex[5], tt[5];
+        block_exclusive_scan_n<5>(in, lds, ex, tt);
+        for (int j = 0; j < in[0]; ++j) g.order2[ex[0] + j] = toff + j;
+        const int base_b = tt[0];
+        if (paired) {
+            const int r = base_b + 16 * (pi / 8) + pi % 8;
+            g.order2[r] = toff + nf - 1;
+            g.order2[r + 8] = toff + nf;
+        } else if (qp > 0) {
+            int base = base_b + 16 * nblk;
+            for (int q = 4; q > qp; --q) base += tt[5 - q];
+            g.order2[base + ex[5 - qp]] = toff + nf;
         }
     }
     *excl_out = excl;
@@ -164,7 +238,7 @@ __device__ inline void group_block_single(const int32_t *idx, int P, int E, cons
     __shared__ int s_base[1024];
     __shared__ unsigned long long s_mask[1024];
     __shared__ int s_tadj[1024];
-    __shared__ int s_scan[17];
+    __shared__ int s_scan[GROUP_SCAN_LDS];
     const int tid = threadIdx.x;
     const int nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
     if (nch * E <= 1024) {

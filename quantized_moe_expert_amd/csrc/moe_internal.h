@@ -77,6 +77,7 @@ struct GroupOut {
     int32_t *chunk_cnt;   // [nchunks][E] scratch (multi-block path)
     int32_t *chunk_base;  // [nchunks][E] scratch (multi-block path)
     int32_t *order = nullptr;  // or null: the tiles as the grouped GEMMs take them (see emit_offsets_and_tiles)
+    int32_t *order2 = nullptr;  // or null: the down GEMM's own schedule (else it takes order)
 };
 
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const float *bias, int64_t T, int H,

@@ -1284,7 +1284,8 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
              (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
     launch_k(grouped_gemm_kernel<FMT, 2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, (const int32_t *)nullptr, H, I, k, L, (const Tile *)g.tiles,
-             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z,
+             (const int32_t *)(g.order2 ? g.order2 : g.order));
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
                        (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();
@@ -1311,7 +1312,7 @@ static hipError_t launch_prefill_fp8(const uint16_t *x, const float *gate, int64
              (const int32_t *)g.order);
     launch_k(grouped_gemm_fp8_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles,
-             (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
+             (const int32_t *)g.perm, gate, h, z, (const int32_t *)(g.order2 ? g.order2 : g.order));
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
                        (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();
