@@ -211,3 +211,25 @@ def test_prefill_extreme_shapes(fmt, H, I):
     assert np.array_equal(idx.cpu().numpy(), ir)
     y = _both(lay, x, idx, gate, k)
     assert_close(y.cpu().numpy(), oracle_y(lay, np_u16(x), ir, gr, k), f"pack extreme fmt={fmt} H={H} I={I}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_prefill_paired_down_schedule(fmt):
+    """About 300 rows per expert over 20 experts (two full 128-row tiles and a
+    partial one of about two subtiles each): the down GEMM's schedule pairs
+    16 experts' last full tiles with their partial tiles in two blocks of 8
+    and leaves 4 experts unpaired.  Outputs against the oracle on every
+    token, and bit-identical with and without the prefill copy."""
+    T, H, I, E, k = 1500, 512, 256, 20, 4
+    say(f"[paired schedule] fmt={fmt}")
+    lay = synth.random_layer(E, H, I, fmt, seed=23, device="cuda")
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 23, "pair/x", "cuda"))
+    logits = synth.bf16_bits(synth.normal((T, E), 1.0, 23, "pair/l", "cuda"))
+    lg, idx, gate = hip_route(None, None, logits, T, H, E, k)
+    ir, gr = oracle.topk(np_u16(logits), T, E, k)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    cnt = np.bincount(ir.ravel(), minlength=E)
+    paired = int(np.sum((cnt > 128) & (cnt % 128 != 0)))
+    assert paired >= 16 and paired % 8 != 0, cnt  # whole blocks and leftovers
+    y = _both(lay, x, idx, gate, k)
+    assert_close(y.cpu().numpy(), oracle_y(lay, np_u16(x), ir, gr, k), f"paired schedule fmt={fmt}")
