@@ -410,8 +410,12 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
 // In the ring, A row r (128 bytes per stage) holds its 16-byte chunk c at
 // c ^ ((r >> 1) & 7) and B row rb (32 bytes) at c ^ ((rb >> 3) & 1), so that
 // the fragment reads of 16 lanes hit distinct LDS banks.
-template <int FMT, int STAGE>
-__global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_gemm_kernel(
+// ONE: each workgroup takes one 32-row subtile of a tile (the subtiles of a
+// tile on one XCD, one after another), in a build for single subtiles only:
+// a third of the LDS and the registers of one subtile, three workgroups per
+// CU.  The host takes it when tiles are mostly single subtiles.
+template <int FMT, int STAGE, bool ONE>
+__global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 3 : 2, ONE ? 3 : 2))) void grouped_gemm_kernel(
     const uint16_t *__restrict__ act,      // STAGE 1: x16 [T][H]; STAGE 2: h [P][I]
     const int32_t *__restrict__ xexp,      // STAGE 1: per-token exponent e
     int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
@@ -420,13 +424,21 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int G = FMT == 0 || FMT == 3 ? 64 : 128;  // K elements per scale word (see gemm_main)
 
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
+    constexpr int MSPLIT = ONE ? BM / 32 : 1;  // workgroups per tile and column block
     const int bx = blockIdx.x, local = bx / 8;
-    const int t = (local / ncb) * 8 + bx % 8;  // rank in the schedule
+    const int t = (local / (ncb * MSPLIT)) * 8 + bx % 8;  // rank in the schedule
     if (t >= *ntiles) return;
     const int cb = local % ncb;
     const int j = order ? order[t] : t;
     const Tile tile = tiles[j];
-    const int e = tile.expert, rows = tile.rows, row0 = tile.row0;
+    const int e = tile.expert;
+    int rows = tile.rows, row0 = tile.row0;
+    if constexpr (ONE) {
+        const int m = (local / ncb) % MSPLIT;  // the subtile
+        if (32 * m >= rows) return;
+        row0 += 32 * m;
+        rows = rows - 32 * m < 32 ? rows - 32 * m : 32;
+    }
     const int K = STAGE == 1 ? H : I;
     const int NG = K / G;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -435,9 +447,9 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int col_base = cb * (STAGE == 1 ? 128 : BROWS);
 
     __shared__ __attribute__((aligned(16))) uint8_t s_ring0[RSLOT_BIG];
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring1[RSLOT_BIG];
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring2[RSLOT_BIG];
-    __shared__ __attribute__((aligned(16))) uint8_t s_ring3[RSLOT3];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring1[ONE ? RSLOT4 : RSLOT_BIG];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring2[ONE ? RSLOT4 : RSLOT_BIG];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring3[ONE ? RSLOT4 : RSLOT3];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring4[RSLOT4];
     __shared__ int s_tok[BM];
     __shared__ float s_rs[BM];  // STAGE 1: 2^e of the row's token; STAGE 2: the row's gate
@@ -513,7 +525,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ns][r] = 0.f;
-    const int msub = (rows + 31) / 32;
+    const int msub = ONE ? 1 : (rows + 31) / 32;
     switch (msub) {
         case 1: gemm_main<FMT, 1>(c, acc, wave, lane); break;
         case 2: gemm_main<FMT, 2>(c, acc, wave, lane); break;
@@ -527,7 +539,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Accumulator element r of lane (l32, hf) in M-subtile mi is row
     // 32 mi + 8 (r / 4) + 4 hf + (r % 4), column l32 of the subtile.
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < (ONE ? 1 : 4); ++mi) {
         if (mi >= msub) break;
         uint16_t *s_t = reinterpret_cast<uint16_t *>(mi % 3 == 0 ? s_ring0 : mi % 3 == 1 ? s_ring1 : s_ring2);
         if (STAGE == 1) {
@@ -1277,12 +1289,17 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
     if (!x16_ready)
         hipLaunchKernelGGL(x_to_f16_kernel<FMT == 3 ? 0 : 1>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T,
                            H, x16, xexp);
-    const unsigned nb1 = (unsigned)(8 * ((tiles + 7) / 8) * (I / 128));  // 8 XCDs x ranks per XCD x column blocks
-    const unsigned nb2 = (unsigned)(8 * ((tiles + 7) / 8) * (H / BROWS));
-    launch_k(grouped_gemm_kernel<FMT, 1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
+    // mean rows per expert within one 32-row subtile: the single-subtile build
+    const bool one = T * k <= 32 * (int64_t)L.E;
+    const unsigned split = one ? BM / 32 : 1;
+    const unsigned nb1 = (unsigned)(8 * ((tiles + 7) / 8) * (I / 128)) * split;  // 8 XCDs x ranks x column blocks
+    const unsigned nb2 = (unsigned)(8 * ((tiles + 7) / 8) * (H / BROWS)) * split;
+    auto k1 = one ? grouped_gemm_kernel<FMT, 1, true> : grouped_gemm_kernel<FMT, 1, false>;
+    auto k2 = one ? grouped_gemm_kernel<FMT, 2, true> : grouped_gemm_kernel<FMT, 2, false>;
+    launch_k(k1, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
              (const uint16_t *)x16, (const int32_t *)xexp, H, I, k, L, (const Tile *)g.tiles,
              (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
-    launch_k(grouped_gemm_kernel<FMT, 2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
+    launch_k(k2, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, (const int32_t *)nullptr, H, I, k, L, (const Tile *)g.tiles,
              (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z,
              (const int32_t *)(g.order2 ? g.order2 : g.order));
