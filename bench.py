@@ -4,14 +4,16 @@
 
 Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
 256 routed experts, top-8, SwiGLU inter 512, int4 experts):
-  decode        (default) one decode step of one MoE layer for 1 token:
+  frame         (default) the full-depth decode frame: 40 sequential MoE
+                layers x 16 tokens (own RTN g64 weights and router per
+                layer), residual bf16(x + y) between layers; value is frame
+                tokens/s (16 tokens through all 40 layers per step).
+  decode        one decode step of one MoE layer for 1 token:
                 router GEMV + top-k, grouping, gate/up GEMV + SwiGLU, down
                 GEMV, combine; asym g64 clip-searched weights.  Steps rotate
                 over 40 address-distinct copies of the layer, as successive
                 layers of a 40-layer model would, so experts are read from HBM
                 and not from the 256 MB last-level cache.
-  frame         40 sequential layers x 16 tokens (own RTN g64 weights and
-                router per layer), residual bf16(x + y) between layers.
   prefill       512 tokens, Zipf(1.1)-popular experts (logits given), asym g64.
   long_prefill  4096 tokens, N(0,1) logits given, sym g128.
   tiny          4 tokens, 16 experts, top-2 (correctness size).
@@ -76,9 +78,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="frame", choices=sorted(WORKLOADS))
     p.add_argument("--copies", type=int, default=40, help="address-distinct weight copies (decode)")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="budget of each CPU oracle sample (one at all cores, one at one thread)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-pack", action="store_true",
                    help="prefill GEMMs read the canonical weight arrays instead of the prefill copy")
@@ -400,12 +403,23 @@ def main():
                     "kernel": dom, "avg_us": round(float(stage_avg[0]) * 1e3, 3),
                     "algorithmic_flops": flops, "active_experts": int(act)}
     roof["second_kernel_us"] = round(float(stage_avg[1]) * 1e3, 3)
+    if decode_path and not only_shared:
+        # the whole step's algorithmic HBM bytes: per layer the router rows
+        # (when the GEMV runs), every active expert's three projections once,
+        # x in, y out (the shared expert's codes when present)
+        router_bytes = E * H * 2 if routers[0] is not None else 0
+        shared_all = shared_gateup_bytes(shareds[0]) * 3 // 2 if with_shared else 0  # gate, up, down
+        layer_bytes = router_bytes + act * 3 * proj_bytes + T * H * 2 + T * H * 4 + shared_all
+        step_bytes = layer_bytes * nl_per_step
+        step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+        roof["step"] = {"algorithmic_bytes": int(step_bytes), "achieved": round(step_gbs, 1), "unit": "GB/s",
+                        "frac": round(step_gbs / HBM_PEAK_GBS, 4), "layers": nl_per_step}
 
     # ---- CPU oracle on a bounded sample ------------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args, decode_path, args.cpu_seconds, shareds[0] if with_shared else None,
-                           only_shared)
+                           only_shared, nl_per_step)
 
     names = {"tiny": "tiny layer: 4 tokens, H=256, 16 experts, top-2, I=128, int4 asym g64",
              "decode": "decode step, 1 MoE layer: 1 token, H=2048, 256 experts, top-8, I=512, int4 asym g64 "
@@ -447,12 +461,23 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(case, args, decode_path, budget_s, shared=None, only_shared=False):
-    """The oracle as it stands, on host cores, over a bounded sample of the same workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_sample(case, budget_s, shared, only_shared):
+    """Tokens of layer 0 through the oracle, a few per call, until budget_s
+    of wall time is spent; returns (tokens, seconds, calls, tokens per call)."""
     import numpy as np
 
     import oracle
-    oracle.build(force=False)
     T, H, E, k = case.T, case.H, case.E, case.k
     lay = case.layers[0]
     host_layer = oracle.layer_np(lay)
@@ -460,13 +485,10 @@ def cpu_baseline(case, args, decode_path, budget_s, shared=None, only_shared=Fal
     x_np = case.x.cpu().numpy().view(np.uint16)
     rw = case.router_ws[0].cpu().numpy().view(np.uint16) if case.router_ws else None
     lg_all = case.logits.cpu().numpy().view(np.uint16) if case.logits is not None else None
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    # sample: tokens of the first layer, a few at a time, until the budget is spent
     per = 1 if T == 1 else min(T, 16)
     done_tokens, t_total, reps = 0, 0.0, 0
-    rng_tokens = np.arange(T)
     while t_total < budget_s and reps < 10000:
-        sel = rng_tokens[(reps * per) % T:(reps * per) % T + per]
+        sel = np.arange(T)[(reps * per) % T:(reps * per) % T + per]
         t1 = time.perf_counter()
         xs = np.ascontiguousarray(x_np[sel])
         y = None
@@ -480,12 +502,33 @@ def cpu_baseline(case, args, decode_path, budget_s, shared=None, only_shared=Fal
         t_total += time.perf_counter() - t1
         done_tokens += len(sel)
         reps += 1
-    value = done_tokens / t_total
+    return done_tokens, t_total, reps, per
+
+
+def cpu_baseline(case, args, decode_path, budget_s, shared=None, only_shared=False, layers_per_step=1):
+    """The oracle as it stands, on this host's cores, over a bounded sample of
+    the same workload: once with every core (OMP_NUM_THREADS, else all), once
+    with one thread.  value is in the bench line's unit: tokens/s through all
+    layers of one step (the per-layer rate divided by the layers per step)."""
+    import oracle
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    oracle.set_threads(threads)
+    n_all, t_all, reps_all, per = oracle_sample(case, budget_s, shared, only_shared)
+    oracle.set_threads(1)
+    n_one, t_one, reps_one, _ = oracle_sample(case, budget_s, shared, only_shared)
+    oracle.set_threads(threads)
+    layer_all, layer_one = n_all / t_all, n_one / t_one
     what = "shared expert" if only_shared else (
-        "route + experts + combine" + (" + shared expert" if host_sx is not None else ""))
-    return {"value": round(value, 3), "unit": "tokens/s (one layer)", "cores": threads, "kind": "oracle",
-            "sample": f"{done_tokens} tokens of layer 0 in {reps} calls of {per} token(s), "
-                      f"{t_total:.1f} s ({what}, fp64)"}
+        "route + experts + combine" + (" + shared expert" if shared is not None else ""))
+    unit = "tokens/s" if layers_per_step == 1 else f"tokens/s through {layers_per_step} layers"
+    return {"value": round(layer_all / layers_per_step, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "single_thread_value": round(layer_one / layers_per_step, 4),
+            "per_layer_tokens_s": {"all_cores": round(layer_all, 3), "one_thread": round(layer_one, 3)},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"layer 0 of the workload, {per} token(s) per call: {n_all} tokens in {t_all:.1f} s at "
+                      f"{threads} threads, {n_one} tokens in {t_one:.1f} s at 1 thread ({what}, fp64); "
+                      f"the other layers cost the same per token"}
 
 
 if __name__ == "__main__":

@@ -94,6 +94,16 @@ def _load():
     return _lib
 
 
+def set_threads(n: int) -> int:
+    """Set the number of OpenMP threads the oracle's parallel loops use (the
+    calling thread's setting) and return the previous number."""
+    _load()
+    gomp = ctypes.CDLL("libgomp.so.1")  # the runtime the oracle links; already loaded
+    prev = int(gomp.omp_get_max_threads())
+    gomp.omp_set_num_threads(int(n))
+    return prev
+
+
 def use_library(path):
     """Point every function of this module at another build of the oracle
     (``None`` restores the default build); returns the previous binding."""

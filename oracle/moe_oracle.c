@@ -216,7 +216,7 @@ void oracle_router(const uint16_t *x, const uint16_t *wr, const float *bias,
 static double logit_value(uint16_t b)
 {
     double v = oracle_bf16_value(b);
-    return isnan(v) ? -INFINITY : v;               /* a NaN logit ranks last */
+    return isnan(v) ? -INFINITY : v;  /* a NaN logit ranks as -inf (ties with it by index) */
 }
 
 /* k rounds of "largest remaining logit, lowest expert index among equals";

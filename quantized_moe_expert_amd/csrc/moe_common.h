@@ -30,14 +30,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Orderable key of a bf16 logit: larger value -> larger key, NaN below -inf.
+// Orderable key of a bf16 logit: a larger value gives a larger key and equal
+// values give equal keys, so that the expert index appended below the key
+// decides every tie.  -0 takes the key of +0 (they are equal), and a NaN
+// takes the key of -inf: it ranks as -inf and ties with it.
 __device__ __forceinline__ uint32_t bf16_order(uint32_t b) {
     b &= 0xffffu;
-    if ((b & 0x7fffu) > 0x7f80u) return 0u;
+    if ((b & 0x7fffu) > 0x7f80u) b = 0xff80u;   // NaN -> -inf
+    if (b == 0x8000u) b = 0u;                   // -0 -> +0
     return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
 }
-// The bf16 bits of an order key (inverse of bf16_order; key 0, a NaN's,
-// gives a NaN).
+// The bf16 bits of an order key (inverse of bf16_order on the values it
+// keeps: a NaN comes back as -inf, -0 as +0).
 __device__ __forceinline__ uint32_t bf16_from_order(uint32_t o) {
     o &= 0xffffu;
     return (o & 0x8000u) ? (o & 0x7fffu) : (~o & 0xffffu);

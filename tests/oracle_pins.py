@@ -456,6 +456,31 @@ def pin_topk_adversarial():
     assert list(idx[0]) == list(range(k, 2 * k))
 
 
+def pin_topk_signed_zero_and_nan():
+    """-0 equals +0 and a NaN ranks as -inf: both are ties that go to the lower
+    expert index (the plain ordering of values, NaN read as -inf).  The
+    expected indices are written out by hand; the selected NaN / -inf slot
+    has gate exactly 0."""
+    E, k = 16, 4
+    bits = np.full(E, 0xbf80, dtype=np.uint16)     # -1.0 everywhere
+    bits[[9, 2, 14]] = [0x4000, 0x3f80, 0x3f00]      # 2.0, 1.0, 0.5: three leaders
+    bits[[5, 7, 11]] = [0x8000, 0x0000, 0x8000]      # -0 at 5, +0 at 7, -0 at 11
+    idx, gate = oracle.topk(bits[None, :], 1, E, k)
+    assert list(idx[0]) == [9, 2, 14, 5], idx
+    bits[5] = 0x0000                                 # +0 at 5, -0 at 11: still 5
+    bits[3] = 0x8000                                 # -0 at 3 comes first now
+    idx, _ = oracle.topk(bits[None, :], 1, E, k)
+    assert list(idx[0]) == [9, 2, 14, 3], idx
+    bits = np.full(E, 0xff80, dtype=np.uint16)     # -inf everywhere
+    bits[[0, 6]] = [0x7fc0, 0xffc1]                  # quiet NaN at 0, negative NaN at 6
+    bits[[12, 4, 8]] = [0x3f80, 0x3f80, 0xc000]      # 1.0, 1.0, -2.0
+    idx, gate = oracle.topk(bits[None, :], 1, E, k)
+    assert list(idx[0]) == [4, 12, 8, 0], idx        # NaN at 0 ties the -inf run, lowest index
+    assert gate[0, 3] == 0.0 and gate[0, 0] == gate[0, 1] > 0
+    idx, _ = oracle.topk(bits[None, :], 1, E, 6)
+    assert list(idx[0]) == [4, 12, 8, 0, 1, 2], idx
+
+
 def pin_gates():
     """Gates: softmax over all experts renormalised over the selected; sums; special cases."""
     rng = np.random.default_rng(9)
@@ -629,7 +654,7 @@ def pin_shared_as_routed_expert():
 
 
 ALL_PINS = [pin_f16_decode_all, pin_bf16_decode_all, pin_bf16_round, pin_dequant_golden,
-            pin_dequant_random, pin_router, pin_topk_bruteforce, pin_topk_adversarial,
+            pin_dequant_random, pin_router, pin_topk_bruteforce, pin_topk_adversarial, pin_topk_signed_zero_and_nan,
             pin_gates, pin_group, pin_one_expert_dense, pin_experts_bruteforce,
             pin_gate_linearity, pin_layer_chain, pin_residual, pin_dequant_int8_golden,
             pin_dequant_int8_random, pin_shared_dense, pin_shared_as_routed_expert, pin_e4m3_decode_all,

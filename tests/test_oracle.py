@@ -107,3 +107,27 @@ def test_nvfp4_encoder_round_trip(orc):
             assert (np.abs(w[name] - d) <= (half + 1e-6) * s).all(), name
             blk = (np.abs(d) / s).reshape(N, K // 16, 16).max(axis=2)
             assert (blk >= 4).all(), name
+
+
+def test_tie_logits_put_ties_at_rank_k(orc):
+    """The routing tie tests' input generator does what they rely on: in every
+    token the oracle's k-th pick belongs to a tie (a signed zero, or NaN /
+    -inf) that goes on past rank k, so a wrong tie rule picks another index."""
+    from tie_cases import NEG_INF, tie_logits
+    for T, E, k in ((64, 256, 8), (40, 16, 2), (9, 9, 5)):
+        lg = tie_logits(T, E, k, seed=1 + E)
+        ir, _ = orc.topk(lg, T, E, k)
+        for t in range(T):
+            row = lg[t]
+            zero = (row & 0x7fff) == 0
+            low = (row == NEG_INF) | ((row & 0x7fff) > 0x7f80)
+            cls = zero if zero[ir[t, k - 1]] else low
+            assert cls[ir[t, k - 1]], (T, E, k, t)
+            unpicked = np.setdiff1d(np.flatnonzero(cls), ir[t])
+            assert unpicked.size > 0, (T, E, k, t)
+            # both signs (or both NaN and -inf) occur in the tie in some token
+        kinds = set()
+        for t in range(T):
+            v = lg[t, ir[t, k - 1]]
+            kinds.add("-0" if v == 0x8000 else "+0" if v == 0 else "-inf" if v == NEG_INF else "nan")
+        assert kinds == {"-0", "+0", "-inf", "nan"}, kinds

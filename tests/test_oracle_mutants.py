@@ -28,6 +28,10 @@ MUTANTS = [
     ("router_transposed", "oracle_bf16_value(wr[(size_t)e * H + h])", "oracle_bf16_value(wr[(size_t)h * E + e])"),
     ("router_bias_dropped", "acc += (double)bias[e];", "acc += 0.0;"),
     ("topk_ties_to_higher", "if (best < 0 || v > bv)", "if (best < 0 || v >= bv)"),
+    ("topk_nan_unmapped", "return isnan(v) ? -INFINITY : v;", "return v;"),
+    ("topk_nan_first", "return isnan(v) ? -INFINITY : v;", "return isnan(v) ? INFINITY : v;"),
+    ("topk_signed_zero_ordered", "return isnan(v) ? -INFINITY : v;",
+     "return isnan(v) ? -INFINITY : (v == 0.0 && signbit(v) ? -1e-300 : v);"),
     ("gates_not_normalised", "- l0) / den);", "- l0));"),
     ("gates_no_shift_to_first", "exp(logit_value(l[idx[t * k + i]]) - l0) / den", "exp(logit_value(l[idx[t * k + i]])) / den"),
     ("group_unstable", "for (int64_t p = 0; p < P; p++) {\n        int e = idx[p];",
