@@ -295,6 +295,29 @@ MOE_Q4_API int moe_q4_forward(const void *x, const float *residual_y, void *x_ou
                               void *ws, size_t ws_bytes, moe_q4_stream stream);
 
 /*
+ * moe_q4_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a device array of
+ * MOE_Q4_NOALLOC_SCRATCH_BYTES that the library holds for the life of the
+ * process, one per GPU (its address is looked up on the first call on each
+ * device; the stream must belong to the current device).  No allocation
+ * routine is called.  Shapes whose forward workspace
+ * (moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I)) exceeds
+ * MOE_Q4_NOALLOC_SCRATCH_BYTES return MOE_Q4_ERR_WORKSPACE; that covers the
+ * decode path (T <= 64) at H, I <= 2048 and E <= 1024.  Every call clears the
+ * routing counters with a small kernel on the stream before its launches.
+ * All calls on one GPU share the array: calls that overlap on one GPU (two
+ * streams, two host threads) race and give wrong results; serialise them.
+ * Arguments and results otherwise as moe_q4_forward.
+ */
+#define MOE_Q4_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+MOE_Q4_API int moe_q4_forward_noalloc(const void *x, const float *residual_y, void *x_out,
+                                      const void *router_w, const float *bias, void *logits,
+                                      int64_t T, int32_t k, const moe_q4_layer *w,
+                                      int32_t *topk_idx, float *topk_gate, float *y,
+                                      moe_q4_stream stream);
+
+/*
  * moe_q4_forward with the caller's MOE_Q4_STAGE_EVENTS HIP events recorded at
  * the start and end of its two main kernels (extended launch): decode path
  * events[0..1] the gate/up GEMV, events[2..3] the routing launch (grouping

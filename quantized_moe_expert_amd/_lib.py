@@ -26,7 +26,8 @@ EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_deco
            "moe_q4_workspace_init",
            "moe_q4_shared", "moe_q4_shared_timed", "moe_q4_dequant_int8", "moe_q4_forward_ex",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string",
-           "moe_q4_prefill_pack_size", "moe_q4_prefill_pack")
+           "moe_q4_prefill_pack_size", "moe_q4_prefill_pack", "moe_q4_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 8 << 20  # MOE_Q4_NOALLOC_SCRATCH_BYTES
 STAGE_EVENTS = 4
 
 
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, sz, P, ctypes.POINTER(ctypes.c_void_p)]
         L.moe_q4_forward.restype = ctypes.c_int
         L.moe_q4_forward.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, P, P, sz, P]
+        L.moe_q4_forward_noalloc.restype = ctypes.c_int
+        L.moe_q4_forward_noalloc.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, P, P]
         L.moe_q4_forward_timed.restype = ctypes.c_int
         L.moe_q4_forward_timed.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer), P, P, P, P, sz, P,
                                            ctypes.POINTER(ctypes.c_void_p)]
@@ -236,6 +239,16 @@ def moe_q4_forward(x, residual_y, x_out, router_w, bias, logits, T, k, layer, to
     _check("moe_q4_forward", lib().moe_q4_forward(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias),
                                                    _ptr(logits), T, k, ctypes.byref(st), _ptr(topk_idx),
                                                    _ptr(topk_gate), _ptr(y), w, nb, _stream(stream)))
+
+
+def moe_q4_forward_noalloc(x, residual_y, x_out, router_w, bias, logits, T, k, layer, topk_idx, topk_gate, y,
+                           stream=None):
+    """moe_q4_forward on the library's own per-GPU device array (no workspace argument)."""
+    st = layer_struct(layer) if not isinstance(layer, Layer) else layer
+    _check("moe_q4_forward_noalloc",
+           lib().moe_q4_forward_noalloc(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias),
+                                        _ptr(logits), T, k, ctypes.byref(st), _ptr(topk_idx), _ptr(topk_gate),
+                                        _ptr(y), _stream(stream)))
 
 
 def moe_q4_forward_ex(x, residual_y, x_out, router_w, bias, logits, T, k, layer, shared, topk_idx, topk_gate, y,

@@ -3,7 +3,16 @@
 #include "moe_internal.h"
 #include "shared_dev.h"
 
+#include <mutex>
+
 using namespace moeq4;
+
+// Workspace of moe_q4_forward_noalloc: device memory that the library holds
+// for the life of the process, one copy of this array per GPU.  Host code
+// never uses the array's name as an address (on the host it is a stand-in
+// for the symbol); it uses the device address hipGetSymbolAddress returns
+// for the current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_Q4_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -318,10 +327,11 @@ int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream) {
                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
-static int run_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
-                       void *logits, int64_t T, int32_t k, const moe_q4_layer *w, const moe_q4_shared_expert *sx,
-                       int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes,
-                       moe_q4_stream stream, void *const *events) {
+// Every argument check of the layer forward, before anything is launched
+// (T = 0 passes with no further checks).
+static int forward_checks(const void *x, const float *residual_y, void *x_out, const void *logits, int64_t T,
+                          int32_t k, const moe_q4_layer *w, const moe_q4_shared_expert *sx, const int32_t *topk_idx,
+                          const float *topk_gate, const float *y, void *const *events) {
     int st = check_layer(w, false);
     if (st) return st;
     if (sx) {
@@ -340,12 +350,22 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
         for (int i = 0; i < MOE_Q4_STAGE_EVENTS; ++i)
             if (!events[i]) return MOE_Q4_ERR_INVALID_ARG;
     if (T == 0) return MOE_Q4_OK;
+    if (!forward_uses_decode(T, k) && (check_layer(w, true) || !prefill_fits(T, k, w->hidden, w->inter)))
+        return MOE_Q4_ERR_UNSUPPORTED;
+    return MOE_Q4_OK;
+}
+
+static int run_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
+                       void *logits, int64_t T, int32_t k, const moe_q4_layer *w, const moe_q4_shared_expert *sx,
+                       int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes,
+                       moe_q4_stream stream, void *const *events) {
+    int st = forward_checks(x, residual_y, x_out, logits, T, k, w, sx, topk_idx, topk_gate, y, events);
+    if (st || T == 0) return st;
     const int E = w->num_experts, H = w->hidden, I = w->inter;
     const bool dec = forward_uses_decode(T, k);
     hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-    if (!dec && (check_layer(w, true) || !prefill_fits(T, k, H, I))) return MOE_Q4_ERR_UNSUPPORTED;
     const size_t need_fwd = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
     const size_t need = need_fwd + (sx ? moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, sx->inter) : 0);
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
@@ -449,6 +469,53 @@ int moe_q4_forward_ex(const void *x, const float *residual_y, void *x_out, const
                       void *const *events) {
     return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, shared, topk_idx, topk_gate, y, ws,
                        ws_bytes, stream, events);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mutex;
+void *noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int noalloc_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_Q4_ERR_HIP;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return MOE_Q4_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(noalloc_mutex);
+    if (!noalloc_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_Q4_ERR_HIP;
+        noalloc_ptr[dev] = p;
+    }
+    *out = noalloc_ptr[dev];
+    return MOE_Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_q4_forward_noalloc(const void *x, const float *residual_y, void *x_out, const void *router_w,
+                           const float *bias, void *logits, int64_t T, int32_t k, const moe_q4_layer *w,
+                           int32_t *topk_idx, float *topk_gate, float *y, moe_q4_stream stream) {
+    int st = forward_checks(x, residual_y, x_out, logits, T, k, w, nullptr, topk_idx, topk_gate, y, nullptr);
+    if (st || T == 0) return st;
+    const size_t need = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, w->num_experts, k, w->hidden, w->inter);
+    if (need > MOE_Q4_NOALLOC_SCRATCH_BYTES) return MOE_Q4_ERR_WORKSPACE;
+    void *ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st) return st;
+    // the routing counters must start at zero; a fill kernel (not a memset
+    // node) clears them on the caller's stream before the layer's launches
+    st = hip_status(launch_fill_zero_u32(static_cast<uint32_t *>(ws), CONTROL_BYTES / 4,
+                                         reinterpret_cast<hipStream_t>(stream)));
+    if (st) return st;
+    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, nullptr, topk_idx, topk_gate, y, ws,
+                       MOE_Q4_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_q4_dequant(const moe_q4_layer *w, int32_t expert, int32_t proj, float *out, moe_q4_stream stream) {

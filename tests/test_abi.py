@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -156,6 +156,20 @@ def test_forward_validation():
     assert ft(ev_null) == _lib.ERR_INVALID_ARG  # and non-NULL
     assert ft((ctypes.c_void_p * 4)(*([FAKE] * 4)), T=0) == _lib.OK
     assert L.moe_q4_workspace_init(None, 0, None) == _lib.ERR_WORKSPACE
+    # the entry point on the library's own workspace: the same checks, and
+    # shapes whose forward workspace exceeds its fixed size are refused before
+    # any device call
+    fn = lambda x=FAKE, ry=None, xo=None, T=4, k=8, layer=lay: L.moe_q4_forward_noalloc(
+        x, ry, xo, FAKE, None, FAKE, T, k, ctypes.byref(layer), FAKE, FAKE, FAKE, None)
+    assert fn(T=0) == _lib.OK
+    assert fn(x=None) == _lib.ERR_INVALID_ARG
+    assert fn(ry=FAKE, xo=None) == _lib.ERR_INVALID_ARG
+    assert fn(layer=_layer(fmt=4)) == _lib.ERR_UNSUPPORTED
+    big = m.workspace_size(m.WS_FORWARD, 4096, 256, 8, 2048, 512)
+    assert big > m.NOALLOC_SCRATCH_BYTES
+    assert fn(T=4096) == _lib.ERR_WORKSPACE
+    # every decode-path shape fits: 64 tokens x top-16 (1024 pairs) at H = I = 2048, E = 1024
+    assert m.workspace_size(m.WS_FORWARD, 64, 1024, 16, 2048, 2048) <= m.NOALLOC_SCRATCH_BYTES
     assert L.moe_q4_workspace_init(FAKE, 100, None) == _lib.ERR_WORKSPACE
 
 
