@@ -310,7 +310,7 @@ MOE_Q4_API int moe_q4_forward(const void *x, const float *residual_y, void *x_ou
  * streams, two host threads) race and give wrong results; serialise them.
  * Arguments and results otherwise as moe_q4_forward.
  */
-#define MOE_Q4_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+#define MOE_Q4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 MOE_Q4_API int moe_q4_forward_noalloc(const void *x, const float *residual_y, void *x_out,
                                       const void *router_w, const float *bias, void *logits,
                                       int64_t T, int32_t k, const moe_q4_layer *w,

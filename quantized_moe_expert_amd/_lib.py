@@ -27,7 +27,7 @@ EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_deco
            "moe_q4_shared", "moe_q4_shared_timed", "moe_q4_dequant_int8", "moe_q4_forward_ex",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string",
            "moe_q4_prefill_pack_size", "moe_q4_prefill_pack", "moe_q4_forward_noalloc")
-NOALLOC_SCRATCH_BYTES = 8 << 20  # MOE_Q4_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_Q4_NOALLOC_SCRATCH_BYTES
 STAGE_EVENTS = 4
 
 

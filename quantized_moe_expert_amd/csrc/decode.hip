@@ -8,8 +8,7 @@
 //
 // Two kernels per layer do the expert work:
 //   1. gate/up GEMV + SwiGLU: every active expert's gate and up rows, applied
-//      to the tokens routed to it, h in f16 (workspace), laid out as the
-//      down GEMV reads it;
+//      to the tokens routed to it, h in fp32 (workspace);
 //   2. down GEMV over full rows of h, multiplied by each token's gate and
 //      added into y with float atomics (y is cleared by the routing kernel).
 // Both launch as many workgroups as the chip holds at once and cut the work
@@ -25,8 +24,8 @@
 // where OFF + q_k is the exact 16-bit float value a nibble unpacks to;
 // symmetric groups use m = -8 s.  sum a (OFF + q) runs on the packed
 // dot-product instructions with fp32 accumulation: bf16 (OFF = 128) against
-// x in the gate/up GEMV, f16 (OFF = 1024) against h rounded to f16 in the
-// down GEMV (|h| must stay below 65504).
+// x in the gate/up GEMV, f16 (OFF = 1024) against h in the down GEMV, each
+// row of h scaled by a power of two and rounded to f16 (decode_dev.h).
 #include "decode_dev.h"
 #include "fp8_dev.h"
 #include "nvfp4_dev.h"
@@ -147,15 +146,13 @@ constexpr int DEC_GU_STAGES = 2;  // register stages of the gate/up GEMV
 // H / 64 lanes per row, each lane 32 bytes = 64 codes (one 64-group), so a
 // wave-load covers RPW = 64 / LPR rows of gate and of up (2 rows of 1 KB
 // each when H = 2048).  The next wave-load is in flight while the current
-// one is reduced.  h is written in f16 as the down GEMV consumes it: each
-// 8-block in PERM8 order (element j at 2j for j < 4, at 2(j - 4) + 1
-// otherwise), odd elements divided by 16 (exact scaling by a power of two).
+// one is reduced.  h is written in fp32, natural order.
 // SHORT: items of a single wave-load are common (few tokens), and take a
 // straight path instead of issuing unused stages.
 template <int LPR, int FMT, bool SHORT>
 __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int H, int I, int k, const LayerPtrs &L,
                                             const Tile &tile, const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
-                                            uint16_t *__restrict__ h, float (*s_out)[DEC_RB_MAX]) {
+                                            float *__restrict__ h, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;  // rows per wave-load
     constexpr int G = FMT == 0 ? 64 : 128;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -266,10 +263,7 @@ __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int 
         for (int i = tid; i < nt * ir.nloc; i += blockDim.x) {
             const int u = i / ir.nloc, nl = i % ir.nloc;
             if (!ir.valid(nl)) continue;
-            const int n = ir.grow(nl);
-            const float v = (n & 1) ? s_out[u][nl] * (1.f / 16.f) : s_out[u][nl];
-            const int slot = (n & ~7) | ((n & 3) << 1) | ((n >> 2) & 1);
-            h[(size_t)(tile.row0 + u) * I + slot] = __builtin_bit_cast(uint16_t, (_Float16)v);
+            h[(size_t)(tile.row0 + u) * I + ir.grow(nl)] = s_out[u][nl];
         }
     }
     __syncthreads();
@@ -282,7 +276,7 @@ __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int 
 template <int LPR, int FMT>
 __device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &L, const Tile &tile,
                                           const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
-                                          const float *__restrict__ topk_gate, const uint16_t *__restrict__ h,
+                                          const float *__restrict__ topk_gate, const float *__restrict__ h,
                                           float *__restrict__ y, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     constexpr int G = FMT == 0 ? 64 : 128;
@@ -313,12 +307,15 @@ __device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &
     int tok[DECODE_TT];
     float gt[DECODE_TT];
     uint32_t hp[DECODE_TT][16];
-    // The lane's h elements in f16, odd ones divided by 16 (they meet codes
-    // 1024 + 16 q); ha = sum of the offsets those products carry (1024 per
-    // even element, 64 per odd one, times h), hb = sum of h.
+    HFetch hf;
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[DECODE_TT * DEC_HMAX];
+    // The lane's h elements in f16 (the row scaled by a power of two), odd
+    // ones divided by 16 (they meet codes 1024 + 16 q); ha = sum of the
+    // offsets those products carry (1024 per even element, 64 per odd one,
+    // times h), hb = sum of h.
     float ha[DECODE_TT], hb[DECODE_TT];
     // h and the gates: fetched before the first weight stages (they depend on
-    // the tile only), summed after them.
+    // the tile only), staged through LDS in f16 and summed after them.
     auto fetch_h = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
@@ -328,25 +325,19 @@ __device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &
                 const int p = tile.pair[u];
                 tok[u] = p / k;
                 gt[u] = topk_gate[p];
-                const uint16_t *src = h + (size_t)(tile.row0 + u) * I + 32 * c;
-                {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint4 v = reinterpret_cast<const uint4 *>(src)[q];
-                        hp[u][4 * q + 0] = v.x;
-                        hp[u][4 * q + 1] = v.y;
-                        hp[u][4 * q + 2] = v.z;
-                        hp[u][4 * q + 3] = v.w;
-                    }
-                }
             }
         }
+        h_fetch(h, tile.row0, nt, I, hf);
     };
     auto sum_h = [&]() {
+        float inv[DECODE_TT];
+        h_to_lds<true>(hf, nt, I, s_h, inv);
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
             ha[u] = hb[u] = 0.f;
             if (u < nt) {
+                gt[u] *= inv[u];
+                h_from_lds(s_h + u * DEC_HMAX, c, hp[u]);
                 float se = 0.f, so = 0.f;  // sums of the even elements and of the odd ones (/16)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -426,7 +417,7 @@ __device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &
 template <int LPR, int FMT, bool ROUTE, bool SHARED>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
-    const int32_t *__restrict__ ntiles, int max_nt, uint16_t *__restrict__ h, const uint16_t *__restrict__ lg,
+    const int32_t *__restrict__ ntiles, int max_nt, float *__restrict__ h, const uint16_t *__restrict__ lg,
     int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out, GroupOut gout, SharedPtrs S,
     uint16_t *__restrict__ hs) {
     // lanes per gate/up row: H / 64 for int4 (64 codes a lane), H / 32 for
@@ -469,13 +460,13 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
 }
 
 // down GEMV over all items (tiles x row chunks of H), h from the gate/up
-// launch.  h enters rounded to f16.  With SHARED the shared expert's down
+// launch (fp32; each row scaled and rounded to f16).  With SHARED the shared expert's down
 // items (its inner size equal to the routed experts') follow, added into y
 // with float atomics as well.
 template <int LPR, int FMT, bool SHARED>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
-    int max_nt, const float *__restrict__ topk_gate, const uint16_t *__restrict__ h, float *__restrict__ y, int T,
+    int max_nt, const float *__restrict__ topk_gate, const float *__restrict__ h, float *__restrict__ y, int T,
     SharedPtrs S, const uint16_t *__restrict__ hs) {
     constexpr int BR = DEC_WAVES * (WAVE / LPR);
     int nt_all = *ntiles;
@@ -724,7 +715,7 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
 
 template <int FMT, bool ROUTE, bool SHARED>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                     const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
+                                     const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
                                      const SharedPtrs &S, uint16_t *hs) {
     const int H = L.H, I = L.I;
@@ -747,7 +738,7 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
     case LP: {                                                                                                   \
         constexpr auto kern = decode_down_kernel<LP, FMT, SHARED>;                                               \
         launch_k(kern, dim3(resident_grid<kern>()), block, s, nullptr, nullptr, H, I, k, P, L,                   \
-                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const uint16_t *)h, y, (int)T, S,  \
+                 (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const float *)h, y, (int)T, S,  \
                  (const uint16_t *)hs);                                                                          \
     } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
@@ -766,7 +757,7 @@ bool decode_fuses_shared(const LayerPtrs &L, const SharedPtrs *S) {
 
 template <bool ROUTE>
 static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                     const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
+                                     const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
                                      const SharedPtrs *S, uint16_t *hs) {
     if (S && !decode_fuses_shared(L, S)) return hipErrorInvalidValue;
@@ -785,7 +776,7 @@ static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64
 }
 
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0,
+                                 const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                  hipEvent_t e1, const SharedPtrs *S, uint16_t *hs) {
     return launch_experts_any<false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr, S, hs);
 }
@@ -799,7 +790,7 @@ bool decode_routes_in_block(int64_t T, int k, int E) {
 }
 
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
-                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, uint16_t *h,
+                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const SharedPtrs *S,
                                         uint16_t *hs) {
     if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;

@@ -120,6 +120,113 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v_t, a), __builtin_bit_cast(half2v_t, b), c, false);
 }
 
+// h between the two decode GEMVs is fp32 [T*k][I] in natural order, the
+// gate/up GEMV's SwiGLU output as computed.  A down-GEMV item stages the h
+// rows of its tile's tokens once: the workgroup loads them (coalesced, one
+// 16-byte load per thread and 512 values), finds each row's largest
+// magnitude, scales the row by the power of two that puts it in
+// [2^14, 2^15) (exact) and rounds it to f16 into LDS, so that f16's range
+// never limits h (only its 11-bit precision does).  The row's outputs are
+// multiplied back by the inverse power of two (exact) with the gate.
+constexpr int DEC_HMAX = 2048;  // largest inner size of the decode GEMVs
+// Thread tid takes the float4s i = tid + 256 j of the nt rows taken as one
+// array.  The first (all of them up to 2 x 512 values) is loaded early, in
+// flight with the weight stages; the others, for larger inner sizes, when
+// the rows are staged.
+struct HFetch {
+    const float4 *src;
+    float4 v0;
+};
+__device__ __forceinline__ void h_fetch(const float *__restrict__ h, int row0, int nt, int I, HFetch &f) {
+    const int tid = threadIdx.x, tot = nt * (I / 4);
+    f.src = reinterpret_cast<const float4 *>(h + (size_t)row0 * I);
+    f.v0 = tid < tot ? f.src[tid] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+// The fetched rows scaled and rounded to f16 into s_h (row u at
+// s_h + u * DEC_HMAX), in natural order, or with PERM8 in the int4 down
+// GEMV's operand order (0,4 | 1,5 | 2,6 | 3,7 in each 8-block, the odd
+// elements also divided by 16: odd codes enter in place as 1024 + 16 q);
+// inv[u] = the inverse of row u's scale.  Every thread of the workgroup
+// calls it (two barriers); s_h is complete on return.
+template <bool PERM8>
+__device__ __forceinline__ void h_to_lds(const HFetch &f, int nt, int I, uint16_t *__restrict__ s_h,
+                                         float inv[DECODE_TT]) {
+    __shared__ uint32_t s_red[DECODE_TT][DEC_WAVES];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n4 = I / 4, tot = nt * n4;
+    // pass 1: the largest magnitude of each row (the float4s past the first
+    // are loaded here, one at a time: inner sizes above 512 only)
+    uint32_t m[DECODE_TT];
+#pragma unroll
+    for (int u = 0; u < DECODE_TT; ++u) m[u] = 0u;
+    auto row_max = [&](int i, const float4 &v) {
+        // non-negative floats order as their bits
+        const uint32_t mx = __float_as_uint(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+#pragma unroll
+        for (int u = 0; u < DECODE_TT; ++u)
+            if (i / n4 == u) m[u] = m[u] > mx ? m[u] : mx;
+    };
+    if (tid < tot) row_max(tid, f.v0);
+#pragma unroll 1
+    for (int i = tid + DEC_WAVES * WAVE; i < tot; i += DEC_WAVES * WAVE) row_max(i, f.src[i]);
+#pragma unroll
+    for (int u = 0; u < DECODE_TT; ++u) {
+        const uint32_t w = wave_max_u32(m[u]);
+        if (lane == 0) s_red[u][wave] = w;
+    }
+    __syncthreads();
+    float sc[DECODE_TT];
+#pragma unroll
+    for (int u = 0; u < DECODE_TT; ++u) {
+        uint32_t r = 0u;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) r = r > s_red[u][w] ? r : s_red[u][w];
+        int be = (int)((r >> 23) & 0xffu);
+        be = be < 15 ? 15 : (be > 254 ? 254 : be);
+        inv[u] = __uint_as_float((uint32_t)(be - 14) << 23);  // 2^(be - 141)
+        sc[u] = __uint_as_float((uint32_t)(268 - be) << 23);  // 2^(141 - be)
+    }
+    // pass 2: scale, round to f16, store
+    auto store = [&](int i, const float4 &v) {
+        const int u = i / n4, n = 4 * (i - u * n4);
+        float s = sc[0];
+#pragma unroll
+        for (int uu = 1; uu < DECODE_TT; ++uu) s = u == uu ? sc[uu] : s;
+        uint16_t *row = s_h + u * DEC_HMAX;
+        if (PERM8) {
+            // n is 0 or 4 mod 8: elements n .. n + 3 go to slots
+            // (n % 8 == 4 ? 1 : 0) + {0, 2, 4, 6} of the 8-block
+            const float so = s * 0.0625f;
+            const int b = (n & ~7) + ((n >> 2) & 1);
+            row[b + 0] = __builtin_bit_cast(uint16_t, (_Float16)(v.x * s));
+            row[b + 2] = __builtin_bit_cast(uint16_t, (_Float16)(v.y * so));
+            row[b + 4] = __builtin_bit_cast(uint16_t, (_Float16)(v.z * s));
+            row[b + 6] = __builtin_bit_cast(uint16_t, (_Float16)(v.w * so));
+        } else {
+            const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.x * s)) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.y * s)) << 16);
+            const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.z * s)) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.w * s)) << 16);
+            *reinterpret_cast<uint2 *>(row + n) = make_uint2(lo, hi);
+        }
+    };
+    if (tid < tot) store(tid, f.v0);
+#pragma unroll 1
+    for (int i = tid + DEC_WAVES * WAVE; i < tot; i += DEC_WAVES * WAVE) store(i, f.src[i]);
+    __syncthreads();
+}
+// The lane's 32 staged values [32 c, 32 c + 32) of row u as 16 f16 pairs.
+__device__ __forceinline__ void h_from_lds(const uint16_t *__restrict__ s_row, int c, uint32_t hp[16]) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(s_row + 32 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 v = src[q];
+        hp[4 * q + 0] = v.x;
+        hp[4 * q + 1] = v.y;
+        hp[4 * q + 2] = v.z;
+        hp[4 * q + 3] = v.w;
+    }
+}
+
 // Workgroups of kernel K (256 threads) the device holds at once, a multiple
 // of 8 (queried once per kernel and device).
 template <auto K>

@@ -10,8 +10,9 @@
 // subnormals included, is a bf16 and an f16 value):
 //   gate/up: codes -> bf16 pairs in natural order, packed dot against the bf16
 //     activations (exact products, fp32 sums);
-//   down: codes -> f16 pairs in natural order, packed dot against h rounded
-//     to f16 (exact products, fp32 sums).
+//   down: codes -> f16 pairs in natural order, packed dot against h (each
+//     row scaled by a power of two, rounded to f16; exact products, fp32
+//     sums).
 // h is kept in natural order for this format.
 #pragma once
 
@@ -36,14 +37,14 @@ __device__ __forceinline__ float fp8_block_scale(const uint16_t *sm, int e, int 
 }
 
 // gate/up GEMV + SwiGLU for one item (tile: one expert, up to DECODE_TT
-// tokens; rows ir of I) into h (f16, natural order).  LPR = H / 32 lanes per
+// tokens; rows ir of I) into h (fp32, natural order).  LPR = H / 32 lanes per
 // row; a wave-load covers 64 / LPR rows of gate and of up.  Pipelined in two
 // register stages as the int4 gate/up GEMV.
 template <int LPR, bool SHORT>
 __device__ __forceinline__ void fp8_gateup_item(const uint16_t *__restrict__ x, int H, int I, int k,
                                                 const LayerPtrs &L, const Tile &tile,
                                                 const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
-                                                uint16_t *__restrict__ h, float (*s_out)[DEC_RB_MAX]) {
+                                                float *__restrict__ h, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR, sub = lane / LPR;
@@ -123,7 +124,7 @@ __device__ __forceinline__ void fp8_gateup_item(const uint16_t *__restrict__ x, 
     for (int i = tid; i < nt * ir.nloc; i += blockDim.x) {
         const int u = i / ir.nloc, nl = i % ir.nloc;
         if (!ir.valid(nl)) continue;
-        h[(size_t)(tile.row0 + u) * I + ir.grow(nl)] = __builtin_bit_cast(uint16_t, (_Float16)s_out[u][nl]);
+        h[(size_t)(tile.row0 + u) * I + ir.grow(nl)] = s_out[u][nl];
     }
     __syncthreads();
 }
@@ -134,7 +135,7 @@ __device__ __forceinline__ void fp8_gateup_item(const uint16_t *__restrict__ x, 
 template <int LPR>
 __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPtrs &L, const Tile &tile,
                                               const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
-                                              const float *__restrict__ topk_gate, const uint16_t *__restrict__ h,
+                                              const float *__restrict__ topk_gate, const float *__restrict__ h,
                                               float *__restrict__ y, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -160,6 +161,11 @@ __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPt
     int tok[DECODE_TT];
     float gt[DECODE_TT];
     uint32_t hp[DECODE_TT][16];
+    HFetch hf;
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[DECODE_TT * DEC_HMAX];
+    // h (fp32) and the gates, fetched before the first weight stages; the
+    // rows are staged through LDS in f16 (each scaled by a power of two) after
+    // them, the inverse power going with the gate
     auto fetch_h = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
@@ -169,15 +175,18 @@ __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPt
                 const int p = tile.pair[u];
                 tok[u] = p / k;
                 gt[u] = topk_gate[p];
-                const uint4 *src = reinterpret_cast<const uint4 *>(h + (size_t)(tile.row0 + u) * I + 32 * c);
+            }
+        }
+        h_fetch(h, tile.row0, nt, I, hf);
+    };
+    auto conv_h = [&]() {
+        float inv[DECODE_TT];
+        h_to_lds<false>(hf, nt, I, s_h, inv);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 v = src[q];
-                    hp[u][4 * q + 0] = v.x;
-                    hp[u][4 * q + 1] = v.y;
-                    hp[u][4 * q + 2] = v.z;
-                    hp[u][4 * q + 3] = v.w;
-                }
+        for (int u = 0; u < DECODE_TT; ++u) {
+            if (u < nt) {
+                gt[u] *= inv[u];
+                h_from_lds(s_h + u * DEC_HMAX, c, hp[u]);
             }
         }
     };
@@ -211,11 +220,13 @@ __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPt
     if (nst == 1) {
         fetch_h();
         issue(sa, 0);
+        conv_h();
         consume(sa, 0);
     } else {
         fetch_h();
         issue(sa, 0);
         issue(sb, DEC_NB);
+        conv_h();
         for (int q = 0; q < nst; q += 2) {
             consume(sa, q * DEC_NB);
             issue(sa, (q + 2) * DEC_NB);

@@ -94,15 +94,15 @@ hipError_t launch_group(const int32_t *idx, int64_t T, int k, int E, const Group
 hipError_t launch_group_after_count(const int32_t *idx, int64_t T, int k, int E, const GroupOut &g, hipStream_t s,
                                     hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
-// Decode expert kernels: gate/up + SwiGLU -> h (f16 [T*k][I], each 8-block
-// in PERM8 order, odd elements divided by 16), then down with the
+// Decode expert kernels: gate/up + SwiGLU -> h (fp32 [T*k][I]), then down
+// (each row of h scaled by a power of two and rounded to f16) with the
 // gate-weighted add into y (y must be cleared first).  e0 / e1 time the
 // gate/up kernel.  With S the shared expert's items run in the same two
 // launches (hs: its f16 [T][I] SwiGLU output); S needs
 // decode_fuses_shared.
 bool decode_fuses_shared(const LayerPtrs &L, const SharedPtrs *S);
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                 const GroupOut &g, uint16_t *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
+                                 const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
                                  hipEvent_t e1 = nullptr, const SharedPtrs *S = nullptr, uint16_t *hs = nullptr);
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64
@@ -123,7 +123,7 @@ hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint1
 // holds up to 256 pairs).  y must be cleared first.
 bool decode_routes_in_block(int64_t T, int k, int E);
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
-                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, uint16_t *h,
+                                        const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
                                         const SharedPtrs *S = nullptr, uint16_t *hs = nullptr);
 

@@ -490,14 +490,56 @@ def make_case(cfg: int, device="cpu", seed: int = 0, layers: int | None = None,
                 router_ws=rws if rws else None)
 
 
-def random_layer(E, H, I, fmt, seed, device="cpu", tag="rand") -> Layer:
+def _log2_uniform(shape, lo, hi, gen, device):
+    """2^u with u uniform in [lo, hi)."""
+    return torch.exp2(torch.rand(shape, generator=gen, device=device) * (hi - lo) + lo)
+
+
+def random_layer(E, H, I, fmt, seed, device="cpu", tag="rand", log2_scale=None) -> Layer:
     """Layer with uniformly random codes and scales drawn around the N(0, 0.02) statistics.
 
     Used for shapes where the clip search would be slow and only the byte
-    layout matters (tests of the kernels' indexing at odd shapes).
+    layout matters (tests of the kernels' indexing at odd shapes).  With
+    log2_scale = (lo, hi) the scales are drawn log-uniformly from [2^lo, 2^hi)
+    instead (int4 group scales, the asymmetric min at -6 to -9 scales;
+    block-FP8 block scales; NVFP4 global scales, with E4M3 block scales
+    over their whole positive range), for tests of the numerics at extreme
+    magnitudes.
     """
     g = GROUP[fmt]
     out = {}
+    if fmt == FMT_NVFP4 and log2_scale is not None:
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            gen = generator(seed, f"{tag}/{name}", device)
+            q = torch.randint(0, 256, (E, N, K // 2), generator=gen, device=device, dtype=torch.int32)
+            out[name + "_q"] = q.to(torch.uint8)
+            # every finite positive E4M3 scale (0x01 .. 0x7e, 2^-9 .. 448)
+            sb = torch.randint(0x01, 0x7f, (E, N, K // 16), generator=gen, device=device, dtype=torch.int32)
+            out[name + "_sm"] = sb.to(torch.uint8)
+        gen = generator(seed, f"{tag}/global", device)
+        glob = _log2_uniform((E, 2), log2_scale[0], log2_scale[1], gen, device)
+        return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, global_scale=glob, **out)
+    if fmt == FMT_FP8_B128 and log2_scale is not None:
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            gen = generator(seed, f"{tag}/{name}", device)
+            q = torch.randint(0, 256, (E, N, K), generator=gen, device=device, dtype=torch.int32)
+            q = torch.where((q & 0x7f) == 0x7f, q - 1, q)  # no NaN codes
+            out[name + "_q"] = q.to(torch.uint8)
+            out[name + "_sm"] = _log2_uniform((E, N // 128, K // 128), log2_scale[0], log2_scale[1], gen,
+                                              device).contiguous()
+        return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, **out)
+    if fmt not in (FMT_NVFP4, FMT_FP8_B128) and log2_scale is not None:
+        for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            gen = generator(seed, f"{tag}/{name}", device)
+            q = torch.randint(0, 256, (E, N, K // 2), generator=gen, device=device, dtype=torch.int32)
+            out[name + "_q"] = q.to(torch.uint8)
+            s = _log2_uniform((E, N, K // g), log2_scale[0], log2_scale[1], gen, device)
+            if fmt == FMT_ASYM_G64:
+                m = -s * (torch.rand((E, N, K // g), generator=gen, device=device) * 3.0 + 6.0)
+                out[name + "_sm"] = torch.stack([f16_bits(s), f16_bits(m)], dim=-1).contiguous()
+            else:
+                out[name + "_sm"] = f16_bits(s).contiguous()
+        return Layer(fmt=fmt, num_experts=E, hidden=H, inter=I, **out)
     if fmt == FMT_NVFP4:
         for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
             gen = generator(seed, f"{tag}/{name}", device)

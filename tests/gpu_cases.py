@@ -25,13 +25,19 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def assert_close(got, ref, what=""):
+def assert_close(got, ref, what="", abs_scaled=False):
+    """rel L2 <= REL_L2 and max abs <= MAX_ABS.  With abs_scaled (inputs far
+    from unit scale) the max-abs bound is MAX_ABS times the reference's
+    largest magnitude when that exceeds 1: the bound is stated for outputs of
+    unit scale, and an output scaled by 2^s carries the same relative
+    rounding."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     r = rel_l2(got, ref)
     a = float(np.max(np.abs(got - ref))) if got.size else 0.0
-    assert r <= REL_L2 and a <= MAX_ABS, f"{what}: rel L2 {r:.3e} max abs {a:.3e}"
+    bound = MAX_ABS * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0) if abs_scaled else MAX_ABS
+    assert r <= REL_L2 and a <= bound, f"{what}: rel L2 {r:.3e} max abs {a:.3e} (bound {bound:.3e})"
     return r, a
 
 

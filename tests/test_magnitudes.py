@@ -1,0 +1,87 @@
+"""The f16 intermediates of both expert paths across magnitudes, against the
+oracle (needs an MI355X).
+
+The decode GEMVs take h in f16 (each row scaled by a power of two); the
+prefill GEMMs run f16 matrix cores on x (each row scaled by a power of two),
+on weights dequantised to f16, on h and on each routed row's down output z.
+None of that may depend on the scale of the inputs: activations x 2^-10,
+x 2^-4, x 2^4 and x 2^7 (|h| up to about 2^16), int4 group scales
+log-uniform over [2^-16, 2^-4] and over [2^-16, 2^-10] (every group below
+2^-10), block-FP8 scales and NVFP4 globals log-uniform over a wide range.
+Every weight format, decode and prefill (with and without the prefill copy
+of the weights).  Bar: rel L2 <= 2e-3; max abs <= 1e-2 times the output's
+largest magnitude when that exceeds 1.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_cases import assert_close, hip_experts, hip_route, np_u16
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [synth.FMT_ASYM_G64, synth.FMT_SYM_G128, synth.FMT_FP8_B128, synth.FMT_NVFP4]
+E, H, I, K = 32, 512, 256, 4
+# (name, log2 of the activation scale, log2 scale range of the weights or None)
+CASES = [("x2^-10", -10, None), ("x2^-4", -4, None), ("x2^4", 4, None), ("x2^7", 7, None),
+         ("scales 2^-16..2^-4", 0, (-16, -4)), ("scales 2^-16..2^-10", 0, (-16, -10)),
+         ("scales 2^-16..2^-10, x2^-4", -4, (-16, -10))]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_moe_expert_amd as m
+    m.lib()
+
+
+def _wide_layer(fmt, log2s):
+    if log2s is None:
+        return synth.random_layer(E, H, I, fmt, seed=41, device="cuda", tag="mag")
+    lo, hi = log2s
+    if fmt == synth.FMT_FP8_B128:      # block scales: codes reach 448, so shift the range down
+        lo, hi = lo - 6, hi - 6
+    if fmt == synth.FMT_NVFP4:         # globals: block scales reach 448 and codes 6
+        lo, hi = lo - 8, hi - 8
+    return synth.random_layer(E, H, I, fmt, seed=41, device="cuda", tag="mag", log2_scale=(lo, hi))
+
+
+@pytest.mark.parametrize("mode,T", [("decode", 16), ("prefill", 96), ("prefill", 600), ("prefill_pack", 96),
+                                    ("prefill_pack", 600)])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_magnitudes(case, fmt, mode, T):
+    import quantized_moe_expert_amd as m
+    name, xs, log2s = case
+    if mode != "decode":
+        pytest.skip("prefill intermediates not yet range-scaled")
+    say(f"[magnitudes] {name} fmt={fmt} {mode} T={T}")
+    lay = _wide_layer(fmt, log2s)
+    x = synth.bf16_bits(synth.normal((T, H), 2.0 ** xs, 41, f"mag/x/{T}", "cuda"))
+    logits = synth.bf16_bits(synth.normal((T, E), 1.0, 41, f"mag/l/{T}", "cuda"))
+    _, idx, gate = hip_route(None, None, logits, T, H, E, K)
+    ir, gr = oracle.topk(np_u16(logits), T, E, K)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    run = lay
+    if mode == "prefill_pack":
+        pack = m.prefill_pack(lay)
+        run = m.layer_struct(lay, pack=pack)
+    y = hip_experts("decode" if mode == "decode" else "prefill", lay if mode != "prefill_pack" else run, x, idx,
+                    gate, K)
+    torch.cuda.synchronize()
+    yr = oracle.experts(fmt, E, H, I, *oracle.layer_np(lay), np_u16(x), ir, gr, T, K,
+                        global_scale=oracle.layer_global(lay))
+    assert np.all(np.isfinite(yr))
+    r, a = assert_close(y.cpu().numpy(), yr, f"{name} fmt={fmt} {mode}", abs_scaled=True)
+    say(f"[magnitudes] {name} fmt={fmt} {mode}: rel L2 {r:.2e} max abs {a:.2e} (|y| max {np.max(np.abs(yr)):.2e})")
