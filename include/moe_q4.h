@@ -169,11 +169,19 @@ typedef struct moe_q4_shared_expert {
  *                  when bit 3 of the slot index is set.
  *   gate|up scales [E][I/128][H/64][256] uint32 at E*I*H: for K-step j and
  *                  slot r, the 4-byte-aligned word of the row's canonical
- *                  scale array that holds its group 64j/G entry.
+ *                  scale array that holds its group 64j/G entry, both f16
+ *                  halves multiplied by 2^L of the slot's row (one rounding;
+ *                  int4 formats, see the lifts below).
  *   down codes     [E][H/256][I/64][256][32] at 9*E*I*H/8: block c holds
  *                  down rows 256c .. 256c+255, halves swapped as above.
  *   down scales    [E][H/256][I/64][256] uint32 at 13*E*I*H/8, as above.
- * Total 27*E*I*H/16 bytes (moe_q4_prefill_pack_size); dst 256-byte aligned.
+ *   gate|up lifts  [E][I/128][256] int8 at 27*E*I*H/16 (int4 formats only):
+ *                  L = 10 - floor(log2 A) of each slot's row, A the largest
+ *                  magnitude among the row's f16 scales and mins (0 if A is
+ *                  0); the GEMM multiplies the row's outputs by 2^-L.
+ *   down lifts     [E][H/256][256] int8 after them (int4 formats only).
+ * Total 27*E*I*H/16 bytes, plus 2*E*I + E*H for the int4 formats
+ * (moe_q4_prefill_pack_size); dst 256-byte aligned.
  * Block FP8: codes only (its block scales are read from the canonical array):
  *   gate|up codes  [E][I/128][H/64][256][64] at 0, down codes
  *                  [E][H/256][I/64][256][64] at 2*E*I*H; a slot's four
@@ -233,8 +241,10 @@ MOE_Q4_API int moe_q4_group(const int32_t *topk_idx, int64_t T, int32_t k, int32
  * Expert layer for few tokens (tuned for T <= 64): grouping (which also
  * clears y), then two kernels of fused-dequant GEMVs that stream the active
  * experts' packed nibbles once: gate and up with SwiGLU in fp32 into h
- * (workspace), then the down GEMV over full rows with h rounded to f16 (so
- * |h| must stay below 65504), multiplied by the gate and added into y with
+ * (workspace, fp32), then the down GEMV over full rows with each row of h
+ * scaled by a power of two (its largest magnitude into [2^14, 2^15)) and
+ * rounded to f16, so f16's range does not limit h; the outputs are
+ * multiplied by the gate and the inverse power of two and added into y with
  * float atomics (y may differ between runs in the last bits).  The group
  * scale and min are applied exactly in fp32 (drama-q4 card, "What's
  * quantized": scale and min per group of 64; drama-3-w4a16 card: scale per
@@ -253,13 +263,16 @@ MOE_Q4_API int moe_q4_decode(const void *x, const int32_t *topk_idx, const float
  * Expert layer for many tokens (tuned for T >= 64): grouping, then grouped
  * GEMMs on the f16 matrix cores with fp32 accumulation.  Each x row is scaled
  * by a power of two and converted to f16 exactly (elements more than 2^31
- * below the row's largest magnitude may round); weights are dequantised to
- * f16 in registers with one rounding each (s q + m, or s (q - 8)), so a
- * dequantised weight must stay below 65504 in magnitude; h between the two
- * products is rounded to f16, so |h| must stay below 65504 too.  Each
- * routed row's gate-weighted down output is rounded to f16 as well (so it
- * must stay below 65504 in magnitude) and a token's k rows are summed in
- * fp32 into y (float [T][H], written whole; deterministic).  Same arguments
+ * below the row's largest magnitude may round); int4 weights are
+ * dequantised to f16 in registers with one rounding each (s q + m, or
+ * s (q - 8)), each weight row lifted by the power of two that puts it below
+ * 2^15 and keeps its groups' scale / 16 normal (groups more than 2^24 below
+ * the row's largest scale lose precision; FP8 and NVFP4 codes enter
+ * exactly); h between the two products and each routed row's gate-weighted
+ * down output are rounded to f16 per (row, 128 columns) after scaling by a
+ * power of two (largest magnitude into [2^14, 2^15)), so f16's range limits
+ * none of them, and a token's k rows are summed in fp32 into y (float
+ * [T][H], written whole; deterministic).  Same arguments
  * as moe_q4_decode; ws >= moe_q4_workspace_size(MOE_Q4_WS_PREFILL, ...).
  */
 /* With w->prefill_pack set the GEMMs read that copy instead of the

@@ -131,8 +131,10 @@ struct PrefillWs {
     GroupOut g;
     uint16_t *x16;   // x as f16 after the per-row power-of-two scale [T][H]
     int32_t *xexp;   // that scale's exponent per token
-    uint16_t *h;     // SwiGLU output per sorted row, f16 [T*k][I]
-    uint16_t *z;     // gate-weighted down output per sorted row, f16 [T*k][H]
+    uint16_t *h;     // SwiGLU output per sorted row, f16 [T*k][I] (scaled per 128-column block)
+    uint16_t *z;     // gate-weighted down output per sorted row, f16 [T*k][H] (scaled per 128 columns)
+    int8_t *hx;      // h's power-of-two exponents [T*k][I/128]
+    int8_t *zx;      // z's [T*k][H/64]
 };
 PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
     PrefillWs p;
@@ -141,6 +143,8 @@ PrefillWs carve_prefill(Carver &c, int64_t T, int E, int k, int H, int I) {
     p.xexp = c.take<int32_t>(T);
     p.h = c.take<uint16_t>(T * k * (int64_t)I);
     p.z = c.take<uint16_t>(T * k * (int64_t)H);
+    p.hx = c.take<int8_t>(T * k * (int64_t)(I / 128 > 0 ? I / 128 : 1));
+    p.zx = c.take<int8_t>(T * k * (int64_t)(H / 64 > 0 ? H / 64 : 1));
     return p;
 }
 
@@ -294,7 +298,7 @@ static int run_experts(bool prefill, const void *x, const int32_t *topk_idx, con
     PrefillWs p = carve_prefill(c, T, E, k, H, I);
     st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     if (st) return st;
-    return hip_status(launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev));
+    return hip_status(launch_prefill_experts(xb, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, p.hx, p.zx, y, s, ev));
 }
 
 int moe_q4_decode(const void *x, const int32_t *topk_idx, const float *topk_gate, int64_t T, int32_t k,
@@ -443,7 +447,8 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
         if (!st) st = hip_status(launch_group(topk_idx, T, k, E, p.g, s));
     }
     if (st) return st;
-    st = hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, y, s, ev, prep));
+    st = hip_status(launch_prefill_experts(xin, topk_gate, T, k, L, p.g, p.x16, p.xexp, p.h, p.z, p.hx, p.zx, y, s, ev,
+                                           prep));
     return st ? st : shared_after(xin);
 }
 

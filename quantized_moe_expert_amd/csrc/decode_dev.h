@@ -180,10 +180,9 @@ __device__ __forceinline__ void h_to_lds(const HFetch &f, int nt, int I, uint16_
         uint32_t r = 0u;
 #pragma unroll
         for (int w = 0; w < DEC_WAVES; ++w) r = r > s_red[u][w] ? r : s_red[u][w];
-        int be = (int)((r >> 23) & 0xffu);
-        be = be < 15 ? 15 : (be > 254 ? 254 : be);
-        inv[u] = __uint_as_float((uint32_t)(be - 14) << 23);  // 2^(be - 141)
-        sc[u] = __uint_as_float((uint32_t)(268 - be) << 23);  // 2^(141 - be)
+        const RowScale rs = row_scale(__uint_as_float(r));
+        sc[u] = rs.sc;
+        inv[u] = exp2i(-rs.s);
     }
     // pass 2: scale, round to f16, store
     auto store = [&](int i, const float4 &v) {

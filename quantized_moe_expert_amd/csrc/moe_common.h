@@ -47,6 +47,33 @@ __device__ __forceinline__ uint32_t bf16_from_order(uint32_t o) {
     return (o & 0x8000u) ? (o & 0x7fffu) : (~o & 0xffffu);
 }
 
+// Two floats rounded to f16 (nearest even) as one packed pair, a in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+// 2^s as a float, s clamped to the normal range [-126, 127].
+__device__ __forceinline__ float exp2i(int s) {
+    s = s < -126 ? -126 : (s > 127 ? 127 : s);
+    return __uint_as_float((uint32_t)(s + 127) << 23);
+}
+
+// The power of two 2^s that puts values whose largest magnitude is m in
+// [2^14, 2^15) before rounding them to f16: s = 14 - floor(log2 m), clamped
+// to [-64, 64] (largest magnitudes between 2^-50 and 2^78 reach the range
+// exactly).  Zero gets s = 64, the largest, so that among blocks scaled this
+// way an all-zero block never sets the common unit.
+struct RowScale {
+    float sc;  // 2^s
+    int s;
+};
+__device__ __forceinline__ RowScale row_scale(float m) {
+    int be = (int)((__float_as_uint(m) >> 23) & 0xffu);  // 127 + floor(log2 m) for normal m
+    be = be < 77 ? 77 : (be > 205 ? 205 : be);
+    return RowScale{__uint_as_float((uint32_t)(268 - be) << 23), 141 - be};
+}
+
 // ---------------------------------------------------------------- nibbles
 //
 // A packed dword holds 8 consecutive codes, code j in bits [4j, 4j+4).
@@ -115,6 +142,16 @@ template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
                                                                  0xf, false));
+}
+
+// Largest value over each row of 16 lanes, in every lane of it (DPP moves;
+// for non-negative values, as lanes outside the row mask read 0).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f32<0xb1>(v));   // lane ^ 1
+    v = fmaxf(v, dpp_f32<0x4e>(v));   // lane ^ 2
+    v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+    return v;
 }
 
 // Sum over aligned segments of W lanes with DPP moves only (no LDS).  For

@@ -35,16 +35,44 @@ struct LayerPtrs {
 };
 
 // Byte offsets of the prefill copy's regions: gate|up codes, gate|up scale
-// words, down codes, down scale words, and its size.  Block FP8 (format 2)
-// has one byte per code and no scale regions (its block scales are read
-// from the canonical array).
+// words, down codes, down scale words, the int4 formats' per-row lifts
+// (gate|up, down), and its size.  Block FP8 (format 2) has one byte per
+// code and no scale regions (its block scales are read from the canonical
+// array); NVFP4 (format 3) has no lifts.
 struct PackLayout {
-    size_t gu_q, gu_s, d_q, d_s, total;
+    size_t gu_q, gu_s, d_q, d_s, gu_l, d_l, total;
 };
 __host__ __device__ inline PackLayout pack_layout(int E, int H, int I, int fmt) {
     const size_t eih = (size_t)E * I * H;
-    if (fmt == 2) return PackLayout{0, 2 * eih, 2 * eih, 3 * eih, 3 * eih};
-    return PackLayout{0, eih, eih + eih / 8, eih + eih / 8 + eih / 2, eih + eih / 8 + eih / 2 + eih / 16};
+    if (fmt == 2) return PackLayout{0, 2 * eih, 2 * eih, 3 * eih, 3 * eih, 3 * eih, 3 * eih};
+    const size_t end = eih + eih / 8 + eih / 2 + eih / 16;
+    if (fmt == 3) return PackLayout{0, eih, eih + eih / 8, eih + eih / 8 + eih / 2, end, end, end};
+    return PackLayout{0, eih, eih + eih / 8, eih + eih / 8 + eih / 2, end, end + 2 * (size_t)E * I,
+                      end + 2 * (size_t)E * I + (size_t)E * H};
+}
+
+// Power-of-two lift L of an int4 weight row (formats 0 and 1) in the prefill
+// GEMMs: with A the largest magnitude of the row's f16 scales and mins
+// (every |w| <= 16 A), the row's scale and min are taken times 2^L, L = 10 -
+// floor(log2 A), so the row's weights dequantise to f16 below 2^15 and its
+// small groups keep scale / 16 a normal f16; the output column is
+// multiplied by 2^-L.  a_bits: A's f16 bit pattern (0: L = 0).
+__host__ __device__ inline int row_lift_from_max(uint32_t a_bits) {
+    a_bits &= 0x7fffu;
+    if (a_bits == 0u) return 0;
+    const int e = (int)(a_bits >> 10);
+    int lg;  // floor(log2 A)
+    if (e > 0) {
+        lg = e - 15;
+    } else {  // subnormal: A = m 2^-24
+        int m = (int)a_bits, b = -1;
+        while (m) {
+            m >>= 1;
+            ++b;
+        }
+        lg = b - 24;
+    }
+    return 10 - lg;
 }
 
 constexpr int GROUP_CHUNK = 64;          // (token, slot) pairs per grouping chunk
@@ -130,11 +158,13 @@ hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logit
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
-// Grouped GEMMs of the prefill path; z: f16 [T*k][H] workspace of the
-// combine.  y is written whole (no clearing needed).
+// Grouped GEMMs of the prefill path; h: f16 [T*k][I] and its exponents hx
+// int8 [T*k][I/128]; z: f16 [T*k][H] (the combine's input) and its
+// exponents zx int8 [T*k][H/64].  y is written whole (no clearing needed).
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
-                                  float *y, hipStream_t s, hipEvent_t const *ev = nullptr, bool x16_ready = false);
+                                  int8_t *hx, int8_t *zx, float *y, hipStream_t s, hipEvent_t const *ev = nullptr,
+                                  bool x16_ready = false);
 // Top-k of the given logits, the grouping's count step and the f16 rows of
 // x (format fmt's order; none for block FP8) in one launch, for
 // T*k > GROUP_SINGLE_MAX (then launch_group_after_count, and the experts

@@ -11,14 +11,25 @@
 //    a power of two 2^-e that puts the row's largest magnitude in
 //    [2^14, 2^15).  The conversion is exact for every element within 2^31 of
 //    that maximum (f16 keeps bf16's 8-bit significand down to 2^-24), and the
-//    GEMM1 outputs are multiplied back by 2^e.  h is rounded to f16 by GEMM1,
-//    so |h| must stay below 65504.
+//    GEMM1 outputs are multiplied back by 2^e.
+//  * h: GEMM1 rounds h to f16 after scaling it by powers of two: each row by
+//    2^-2e (h grows as the square of its token's activations, so this puts
+//    every token in the same range), then the workgroup's 128 columns of
+//    its rows by the 2^s that puts their largest magnitude in [2^14, 2^15);
+//    s is stored beside h (int8, per row and 128-column block).  GEMM2 takes
+//    the smallest s of its rows' blocks, s_min, as its unit and folds
+//    2^(s_min - s_b) into the dequantised weights of block b (a power of
+//    two: exact), and multiplies its outputs by 2^-s_min.  So f16's range
+//    never limits h, only its 11-bit precision does.
 //  * Weights: a code unpacks to the exact f16 1024 + q; subtracting 1024
 //    (asym) or 1032 (sym) gives q or q - 8 exactly, and one packed f16 fma
 //    (s q + m) or multiply (s (q - 8)) dequantises two weights with a single
 //    rounding to f16 (relative error <= 2^-11 per weight; the GEMM sums
 //    these errors with random signs, about 2^-12 relative on an output).
-//    Per-group scales therefore never touch the fp32 accumulators.
+//    Per-group scales therefore never touch the fp32 accumulators.  Each
+//    int4 weight row's scales and mins enter lifted by a power of two 2^L
+//    (row_lift_from_max: the row's weights below 2^15, its small groups'
+//    scale / 16 a normal f16), and the output column is multiplied by 2^-L.
 //
 // Layout of the f16 activations (x16, h): inside every group of 8 elements
 // the order is 0,4,1,5,2,6,3,7 (PERM8), the order in which a packed code
@@ -26,8 +37,11 @@
 // the same 8 contraction indices.
 //
 // Combine.  GEMM2 writes each routed row's gate-weighted output once, as f16
-// (z, [T*k][H] in sorted row order, |z| must stay below 65504), with
-// coalesced stores; a last kernel sums each token's k rows in fp32 into y.
+// (z, [T*k][H] in sorted row order), scaled by 2^-2e per row and by the
+// power of two s_z that puts the largest magnitude of each 32-row x
+// 64-column piece in [2^14, 2^15) (stored per row and 64 columns), with
+// coalesced stores;
+// a last kernel sums each token's k rows times 2^(2e - s_z) in fp32 into y.
 // Scattering the rows into y with float atomics (k adds per output, done at
 // the memory side so that the XCDs' L2s agree) took longer than GEMM2's
 // matrix work.
@@ -178,8 +192,8 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ p, i
 // and 6 of a dword) or v = 1024 + 16 q (codes 1 and 5, 3 and 7, taken in
 // place: see insert_codes): (v - off) is exact and equals q, q - 8, 16 q or
 // 16 q - 128; times s2 (the group scale, or scale / 16 for the 16 q pairs,
-// exact while scale / 16 is a normal f16) plus m2 (asym min) it is s q + m or
-// s (q - 8), rounded once to f16.
+// exact while scale / 16 is a normal f16: the row lift keeps it so) plus m2
+// (asym min) it is s q + m or s (q - 8), rounded once to f16.
 template <int FMT>
 __device__ __forceinline__ uint32_t dequant_pair(uint32_t v, half2_t off, half2_t s2, half2_t m2) {
     const half2_t q = __builtin_bit_cast(half2_t, v) - off;
@@ -247,6 +261,9 @@ struct GemmCtx {
     int brow[2];                     // this lane's weight rows (block-local) of the two N-subtiles
     uint32_t spar[2];                // sym: parity of the scale entry of group 0 of brow[ns]
     int nk;                          // K-steps
+    int lexp[2];                     // int4: the rows' lifts L, applied to the scale words when
+    bool lift_rt;                    //   lift_rt (the canonical arrays; the copy holds them lifted)
+    const float *fb;                 // GEMM2: LDS [16], 2^(s_min - s_b) per 128-input block b (null in GEMM1)
 };
 
 // Barrier between the waves of the block that orders their LDS traffic
@@ -320,13 +337,15 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
         const int kn = ks + D - 1 < NK ? ks + D - 1 : NK - 1;
         issue_stage<MS>(c, kn, kn / KPG, (u + D - 1) % D, wave, bq[(u + D - 1) % D], sw[(u + D - 1) % D]);
         const uint8_t *sa = c.ring[u];
+        // GEMM2: this 128-input block's factor 2^(s_min - s_b), folded into the weights
+        const float fbk = c.fb ? c.fb[ks >> 1] : 1.0f;
         if (FMT == 3) {
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns) {
                 // blocks 2 hf and 2 hf + 1 of the K-step: k in [32 hf, 32 hf + 32)
                 const uint32_t pw = sw[u][ns] >> (16 * hf);
                 const uint32_t sp =
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw, 1.0f, false));
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pw, fbk, false));
                 nvs[ns][0] = (sp & 0xffffu) * 0x10001u;
                 nvs[ns][1] = (sp >> 16) * 0x10001u;
             }
@@ -335,12 +354,27 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
             for (int ns = 0; ns < 2; ++ns) {
                 const uint32_t pw = sw[u][ns];
                 if (FMT == 0) {
-                    s2[ns][0] = __builtin_bit_cast(half2_t, (pw & 0xffffu) * 0x10001u);
-                    m2[ns] = __builtin_bit_cast(half2_t, (pw >> 16) * 0x10001u);
+                    uint32_t sb = pw & 0xffffu, mb = pw >> 16;
+                    if (c.lift_rt) {
+                        sb = __builtin_bit_cast(uint16_t, __builtin_ldexpf16(__builtin_bit_cast(_Float16, (uint16_t)sb),
+                                                                             c.lexp[ns]));
+                        mb = __builtin_bit_cast(uint16_t, __builtin_ldexpf16(__builtin_bit_cast(_Float16, (uint16_t)mb),
+                                                                             c.lexp[ns]));
+                    }
+                    s2[ns][0] = __builtin_bit_cast(half2_t, sb * 0x10001u);
+                    m2[ns] = __builtin_bit_cast(half2_t, mb * 0x10001u);
                 } else {
-                    const uint32_t h = ((c.spar[ns] + (uint32_t)(ks / KPG)) & 1u) ? pw >> 16 : pw & 0xffffu;
+                    uint32_t h = ((c.spar[ns] + (uint32_t)(ks / KPG)) & 1u) ? pw >> 16 : pw & 0xffffu;
+                    if (c.lift_rt)
+                        h = __builtin_bit_cast(uint16_t, __builtin_ldexpf16(__builtin_bit_cast(_Float16, (uint16_t)h),
+                                                                            c.lexp[ns]));
                     s2[ns][0] = __builtin_bit_cast(half2_t, h * 0x10001u);
                     m2[ns] = s2[ns][0];
+                }
+                if (c.fb) {
+                    const half2_t f2 = {(_Float16)fbk, (_Float16)fbk};
+                    s2[ns][0] = s2[ns][0] * f2;
+                    m2[ns] = m2[ns] * f2;
                 }
                 s2[ns][1] = s2[ns][0] * sixteenth;
             }
@@ -397,6 +431,42 @@ __device__ __forceinline__ void gemm_main(const GemmCtx &c, f32x16_t (&acc)[4][2
     MOEQ4_WAIT_VM_LDS(0);  // the stages issued past the end have landed before the ring is reused
 }
 
+// The largest of the workgroup's non-negative values v (one per thread), in
+// every thread (a barrier; s_red: 4 words of LDS).
+__device__ __forceinline__ float block_max_nonneg(float v, uint32_t *s_red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t w = wave_max_u32(__float_as_uint(v));  // non-negative floats order as their bits
+    if (lane == 0) s_red[wave] = w;
+    __syncthreads();
+    uint32_t m = s_red[0];
+#pragma unroll
+    for (int i = 1; i < PF_BLOCK / 64; ++i) m = m > s_red[i] ? m : s_red[i];
+    return __uint_as_float(m);
+}
+
+// The largest f16 magnitude (as bits) among an int4 weight row's scales and
+// mins in the canonical scale array: asym [NG] words {scale, min}, sym [NG]
+// scales.
+template <int FMT>
+__device__ __forceinline__ uint32_t canonical_row_max(const uint16_t *__restrict__ sm, size_t row, int NG) {
+    uint32_t a = 0u;
+    if (FMT == 0) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(sm) + row * NG;
+        for (int i = 0; i < NG; ++i) {
+            const uint32_t v = w[i], lo = v & 0x7fffu, hi = (v >> 16) & 0x7fffu;
+            a = lo > a ? lo : a;
+            a = hi > a ? hi : a;
+        }
+    } else {
+        const uint16_t *h = sm + row * NG;
+        for (int i = 0; i < NG; ++i) {
+            const uint32_t v = h[i] & 0x7fffu;
+            a = v > a ? v : a;
+        }
+    }
+    return a;
+}
+
 // STAGE 1: A = x16 rows gathered through perm, B = gate | up codes,
 //          epilogue * 2^e(token), SwiGLU -> h (f16).
 // STAGE 2: A = h rows (contiguous sorted rows), B = down codes,
@@ -420,7 +490,9 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 
     const int32_t *__restrict__ xexp,      // STAGE 1: per-token exponent e
     int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
-    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z, const int32_t *__restrict__ order) {
+    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z, const int32_t *__restrict__ order,
+    int8_t *__restrict__ hx,   // h's exponent per row and 128-column block: STAGE 1 writes, STAGE 2 reads
+    int8_t *__restrict__ zx) { // STAGE 2: z's exponent per row and 64 columns
     constexpr int G = FMT == 0 || FMT == 3 ? 64 : 128;  // K elements per scale word (see gemm_main)
 
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
@@ -452,19 +524,38 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 
     __shared__ __attribute__((aligned(16))) uint8_t s_ring3[ONE ? RSLOT4 : RSLOT3];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring4[RSLOT4];
     __shared__ int s_tok[BM];
-    __shared__ float s_rs[BM];  // STAGE 1: 2^e of the row's token; STAGE 2: the row's gate
+    __shared__ float s_rs[BM];  // STAGE 1: 2^e of the row's token; STAGE 2: the row's gate times 2^-s_min
+    __shared__ float s_ri[BM];  // STAGE 1: 2^-e
+    __shared__ float s_fb[16];  // STAGE 2: 2^(s_min - s_b) per 128-input block b of h
+    __shared__ uint32_t s_red[PF_BLOCK / 64];
+    const int nbh = I / 128;    // h blocks of 128 (<= 16)
 
+    // STAGE 2: the exponents of h's blocks are the same for all the rows of
+    // this workgroup (they were scaled by one GEMM1 workgroup per block)
+    int smin = 64;
+    if (STAGE == 2 && tid < BM)
+        for (int b = 0; b < nbh; ++b) {
+            const int sb = hx[(size_t)row0 * nbh + b];
+            smin = sb < smin ? sb : smin;
+        }
+    if (STAGE == 2 && tid < nbh) s_fb[tid] = exp2i(smin - (int)hx[(size_t)row0 * nbh + tid]);
     if (tid < BM) {
         int t = 0;
-        float v = 0.f;
+        float v = 0.f, vi = 0.f;
         if (tid < rows) {
             const int p = perm[row0 + tid];
             t = p / k;
-            v = STAGE == 2 ? topk_gate[p] : ldexpf(1.0f, xexp[t]);
-            if (FMT == 3) v *= L.glob[2 * e + (STAGE == 2 ? 1 : 0)];  // NVFP4 global scale
+            v = STAGE == 2 ? topk_gate[p] * exp2i(-smin) : ldexpf(1.0f, xexp[t]);
+            vi = STAGE == 2 ? 0.f : ldexpf(1.0f, -xexp[t]);
+            if (FMT == 3) {  // NVFP4 global scale (gate and up share theirs)
+                const float gs = L.glob[2 * e + (STAGE == 2 ? 1 : 0)];
+                v *= gs;
+                vi *= gs;
+            }
         }
         s_tok[tid] = t;
         s_rs[tid] = v;
+        s_ri[tid] = vi;
     }
     __syncthreads();
 
@@ -493,12 +584,26 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 
     const uint32_t esz = FMT == 0 || FMT == 3 ? 4u : 2u;
     const PackLayout pl = pack_layout(L.E, H, I, FMT);
     const size_t tix = (size_t)e * ncb + cb;  // the tile's index in the copy
+    float lf[2] = {1.f, 1.f};                 // the output columns' 2^-L
+    c.lift_rt = (FMT == 0 || FMT == 1) && !L.pack;
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
         const int rb = STAGE == 1 ? ns * 128 + wave * 32 + l32 : wave * 64 + ns * 32 + l32;
         c.brow[ns] = rb;
         const uint32_t wrow = STAGE == 1 ? (uint32_t)e * I + col_base + (rb & 127) : (uint32_t)e * H + col_base + rb;
         c.spar[ns] = (wrow * (uint32_t)NG) & 1u;
+        c.lexp[ns] = 0;
+        if (FMT == 0 || FMT == 1) {
+            int lift;
+            if (L.pack) {
+                lift = (int)(int8_t)L.pack[(STAGE == 1 ? pl.gu_l : pl.d_l) + tix * BROWS + rb];
+            } else {
+                const uint16_t *sm = STAGE == 1 ? (ns == 0 ? L.gsm : L.usm) : L.dsm;
+                lift = row_lift_from_max(canonical_row_max<FMT == 0 ? 0 : 1>(sm, wrow, NG));
+            }
+            c.lexp[ns] = lift;
+            lf[ns] = exp2i(-lift);
+        }
         if (L.pack) {
             // prefill copy: per K-step, tile (e, cb) holds its 256 rows' 32-byte
             // chunks in row order (halves swapped when bit 3 of the row is set),
@@ -517,6 +622,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 
     c.b_kstep = L.pack ? B_BYTES : KS / 2;
     c.s_step = L.pack ? 0u : esz;
     c.s_kstep = L.pack ? S_BYTES : 0u;
+    c.fb = STAGE == 2 ? s_fb : nullptr;
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -534,10 +640,35 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 
     }
     __syncthreads();  // ring no longer read: the epilogue may reuse it
 
-    // ---- epilogue, one 32-row subtile at a time through ring slots 0-2 in
-    // turn (a slot is written again only after two more barriers).
+    // ---- epilogue: values in the unit that their f16 rounding uses (h:
+    // per row h 2^-2e; z: per row z 2^-2e = g 2^-s_min acc), times the power
+    // of two 2^s that puts their largest magnitude in [2^14, 2^15)
+    // (row_scale), one 32-row subtile at a time through ring slots 0-2 in
+    // turn (a slot is written again only after two more barriers): f16 in
+    // LDS, then coalesced 16-byte stores.  h takes one s for the
+    // workgroup's 128 columns of all its rows (GEMM2 folds it into its
+    // weights, so it must be uniform over a GEMM2 workgroup's rows); z one s
+    // per subtile and wave (64 columns), stored per row for the combine.
     // Accumulator element r of lane (l32, hf) in M-subtile mi is row
     // 32 mi + 8 (r / 4) + 4 hf + (r % 4), column l32 of the subtile.
+    __shared__ int s_zs[4][PF_BLOCK / 64];
+    RowScale rs{1.0f, 0};
+    if (STAGE == 1) {
+        float mloc = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < (ONE ? 1 : 4); ++mi) {
+            if (mi >= msub) break;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+                // h 2^-2e = silu(a) (b 2^-2e) with a = acc 2^e and b 2^-2e = acc 2^-e
+                const float hn = silu(acc[mi][0][r] * s_rs[lr] * lf[0]) * (acc[mi][1][r] * s_ri[lr] * lf[1]);
+                acc[mi][0][r] = hn;
+                mloc = fmaxf(mloc, fabsf(hn));
+            }
+        }
+        rs = row_scale(block_max_nonneg(mloc, s_red));
+    }
 #pragma unroll
     for (int mi = 0; mi < (ONE ? 1 : 4); ++mi) {
         if (mi >= msub) break;
@@ -548,11 +679,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
-                const float sc = s_rs[32 * mi + lr];
-                const float gv = acc[mi][0][r] * sc;
-                const float uv = acc[mi][1][r] * sc;
-                const _Float16 hv = (_Float16)(silu(gv) * uv);
-                s_t[lr * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
+                s_t[lr * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(acc[mi][0][r] * rs.sc));
             }
             __syncthreads();
             for (int i = tid; i < 32 * 16; i += PF_BLOCK) {
@@ -562,24 +689,39 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 
                     uint4 o = v;
                     if (FMT != 3) perm8(v.x, v.y, v.z, v.w, o.x, o.y, o.z, o.w);
                     *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
+                    if (cc == 0) hx[(size_t)(row0 + row) * nbh + cb] = (int8_t)rs.s;
                 }
             }
         } else {
-            // z rows [32][256] f16 in LDS, then coalesced 16-byte stores
+            // z rows [32][256] f16 in LDS (this wave's 64 columns with their own s), then coalesced 16-byte stores
             constexpr int ZP = BROWS + 8;
+            float mloc = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) {
+                    const float zn = acc[mi][ns][r] * s_rs[lr] * lf[ns];
+                    acc[mi][ns][r] = zn;
+                    mloc = fmaxf(mloc, fabsf(zn));
+                }
+            }
+            const RowScale zs = row_scale(__uint_as_float(wave_max_u32(__float_as_uint(mloc))));
+            if (lane == 0) s_zs[mi][wave] = zs.s;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
-                const float gt = s_rs[32 * mi + lr];
-                s_t[lr * ZP + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
-                s_t[lr * ZP + wave * 64 + 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
+                s_t[lr * ZP + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(acc[mi][0][r] * zs.sc));
+                s_t[lr * ZP + wave * 64 + 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(acc[mi][1][r] * zs.sc));
             }
             __syncthreads();
             for (int i = tid; i < 32 * (BROWS / 8); i += PF_BLOCK) {
                 const int lr = i / (BROWS / 8), cc = i % (BROWS / 8), row = 32 * mi + lr;
-                if (row < rows)
+                if (row < rows) {
                     *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
                         *reinterpret_cast<const uint4 *>(&s_t[lr * ZP + cc * 8]);
+                    if ((cc & 7) == 0) zx[(size_t)(row0 + row) * (H / 64) + (col_base + cc * 8) / 64] = (int8_t)s_zs[mi][cc >> 3];
+                }
             }
         }
     }
@@ -752,7 +894,8 @@ template <int STAGE>
 __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_gemm_fp8_kernel(
     const uint16_t *__restrict__ act, int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
-    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z, const int32_t *__restrict__ order) {
+    uint16_t *__restrict__ h_out, uint16_t *__restrict__ z, const int32_t *__restrict__ order,
+    int8_t *__restrict__ hx, int8_t *__restrict__ zx) {  // exponents of h and z, as grouped_gemm_kernel
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
     const int bx = blockIdx.x, local = bx / 8;
     const int t = (local / ncb) * 8 + bx % 8;  // rank in the schedule (as grouped_gemm_kernel)
@@ -771,14 +914,24 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(16))) uint8_t s_ring1[STAGE8_BYTES];
     __shared__ float s_sc8[4][2][16];  // per wave and N-subtile: the block scales along K (K <= 2048)
     __shared__ int s_tok[BM];
-    __shared__ float s_gt[BM];  // STAGE 2: the row's gate
+    __shared__ float s_gt[BM];  // STAGE 1: 1 (0 for padding rows); STAGE 2: the row's gate times 2^-s_min
+    __shared__ float s_fb[16];  // STAGE 2: 2^(s_min - s_b) per 128-input block b of h
+    __shared__ uint32_t s_red[PF_BLOCK / 64];
+    const int nbh = I / 128;
+    int smin = 64;  // as grouped_gemm_kernel (no per-token exponent: x enters as given)
+    if (STAGE == 2 && tid < BM)
+        for (int b = 0; b < nbh; ++b) {
+            const int sb = hx[(size_t)row0 * nbh + b];
+            smin = sb < smin ? sb : smin;
+        }
+    if (STAGE == 2 && tid < nbh) s_fb[tid] = exp2i(smin - (int)hx[(size_t)row0 * nbh + tid]);
     if (tid < BM) {
         int t = 0;
         float v = 0.f;
         if (tid < rows) {
             const int p = perm[row0 + tid];
             t = p / k;
-            v = STAGE == 2 ? topk_gate[p] : 1.f;
+            v = STAGE == 2 ? topk_gate[p] * exp2i(-smin) : 1.f;
         }
         s_tok[tid] = t;
         s_gt[tid] = v;
@@ -837,8 +990,11 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int N = STAGE == 1 ? I : H;
         // the wave's own copy in LDS: read in the loop without joining the
         // vector-memory count that orders the ring
+        // GEMM2: each block's scale times the factor 2^(s_min - s_b) of h's block
         const int kb = lane & 15;
-        if ((lane >> 4) == ns && kb < nkb) s_sc8[wave][ns][kb] = sbase[((size_t)e * (N / 128) + nrow / 128) * nkb + kb];
+        if ((lane >> 4) == ns && kb < nkb)
+            s_sc8[wave][ns][kb] =
+                sbase[((size_t)e * (N / 128) + nrow / 128) * nkb + kb] * (STAGE == 2 ? s_fb[kb] : 1.0f);
     }
     c.sc = &s_sc8[wave][0][0];
 
@@ -858,7 +1014,25 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     __syncthreads();  // ring no longer read: the epilogue may reuse it
 
-    // epilogue, one 32-row subtile at a time through the two ring slots in turn
+    // epilogue as grouped_gemm_kernel's (without a per-token exponent), one
+    // 32-row subtile at a time through the two ring slots in turn
+    __shared__ int s_zs[4][PF_BLOCK / 64];
+    RowScale rs{1.0f, 0};
+    if (STAGE == 1) {
+        float mloc = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi >= msub) break;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+                const float hv = silu(acc[mi][0][r]) * acc[mi][1][r] * s_gt[lr];
+                acc[mi][0][r] = hv;
+                mloc = fmaxf(mloc, fabsf(hv));
+            }
+        }
+        rs = row_scale(block_max_nonneg(mloc, s_red));
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         if (mi >= msub) break;
@@ -868,30 +1042,45 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
-                const _Float16 hv = (_Float16)(silu(acc[mi][0][r]) * acc[mi][1][r]);
-                s_t[lr * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
+                s_t[lr * HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(acc[mi][0][r] * rs.sc));
             }
             __syncthreads();
             for (int i = tid; i < 32 * 16; i += PF_BLOCK) {
                 const int lr = i / 16, cc = i % 16, row = 32 * mi + lr;
-                if (row < rows)
+                if (row < rows) {
                     *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) =
                         *reinterpret_cast<const uint4 *>(&s_t[lr * HP + cc * 8]);
+                    if (cc == 0) hx[(size_t)(row0 + row) * nbh + cb] = (int8_t)rs.s;
+                }
             }
         } else {
+            float mloc = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) {
+                    const float zn = acc[mi][ns][r] * s_gt[lr];
+                    acc[mi][ns][r] = zn;
+                    mloc = fmaxf(mloc, fabsf(zn));
+                }
+            }
+            const RowScale zs = row_scale(__uint_as_float(wave_max_u32(__float_as_uint(mloc))));
+            if (lane == 0) s_zs[mi][wave] = zs.s;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
-                const float gt = s_gt[32 * mi + lr];
-                s_t[lr * ZP8 + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][0][r]));
-                s_t[lr * ZP8 + wave * 64 + 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(gt * acc[mi][1][r]));
+                s_t[lr * ZP8 + wave * 64 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(acc[mi][0][r] * zs.sc));
+                s_t[lr * ZP8 + wave * 64 + 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(acc[mi][1][r] * zs.sc));
             }
             __syncthreads();
             for (int i = tid; i < 32 * (BROWS / 8); i += PF_BLOCK) {
                 const int lr = i / (BROWS / 8), cc = i % (BROWS / 8), row = 32 * mi + lr;
-                if (row < rows)
+                if (row < rows) {
                     *reinterpret_cast<uint4 *>(z + (size_t)(row0 + row) * H + col_base + cc * 8) =
                         *reinterpret_cast<const uint4 *>(&s_t[lr * ZP8 + cc * 8]);
+                    if ((cc & 7) == 0) zx[(size_t)(row0 + row) * (H / 64) + (col_base + cc * 8) / 64] = (int8_t)s_zs[mi][cc >> 3];
+                }
             }
         }
     }
@@ -1167,21 +1356,28 @@ hipError_t launch_shared_gemm(const uint16_t *x, int64_t T, const SharedPtrs &S,
 
 // y[t] = sum over the token's k routed rows of z (fp32).  One workgroup of
 // 256 threads per token, 8 columns per thread and pass.
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ z, const int32_t *__restrict__ inv,
-                                                      int64_t T, int k, int H, int64_t P, float *__restrict__ y) {
+// Row r of z is z 2^(s - 2e): 2^-2e per token (xexp: e per token, or null
+// for 0) and 2^s per row and 64 columns (zx[r * H / 64 + c / 64], for
+// column c), both taken off here.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ z, const int8_t *__restrict__ zx,
+                                                      const int32_t *__restrict__ xexp,
+                                                      const int32_t *__restrict__ inv, int64_t T, int k, int H,
+                                                      int64_t P, float *__restrict__ y) {
     const int64_t t = blockIdx.x;
     if (t >= T) return;
+    const int e2 = xexp ? 2 * xexp[t] : 0;
     for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
         float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < k; ++i) {
             int64_t row = inv[t * k + i];
             row = row < 0 ? 0 : (row >= P ? P - 1 : row);
             const uint4 v = *reinterpret_cast<const uint4 *>(z + row * H + c);
+            const float f = exp2i(e2 - (int)zx[row * (H / 64) + (c / 64)]);
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                s[2 * q] += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xffffu));
-                s[2 * q + 1] += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16));
+                s[2 * q] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xffffu)), f, s[2 * q]);
+                s[2 * q + 1] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16)), f, s[2 * q + 1]);
             }
         }
         float4 *dst = reinterpret_cast<float4 *>(y + t * H + c);
@@ -1230,8 +1426,39 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(LayerPtrs L, uint8_t *_
     *reinterpret_cast<uint4 *>(dst + (STAGE == 1 ? pl.gu_q : pl.d_q) + (size_t)o * 16) = v;
 }
 
+// Lifts (int4 formats): one thread per weight row slot r of a tile: the
+// row's power-of-two lift L (row_lift_from_max over its canonical scales and
+// mins), one signed byte.
+template <int STAGE>
+__global__ __launch_bounds__(256) void pack_lift_kernel(LayerPtrs L, uint8_t *__restrict__ dst) {
+    const int H = L.H, I = L.I;
+    const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
+    const int K = STAGE == 1 ? H : I;
+    const int64_t n = (int64_t)L.E * ncb * BROWS;
+    const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (o >= n) return;
+    const int r = (int)(o % BROWS);
+    const int64_t tile = o / BROWS;
+    const int cb = (int)(tile % ncb), e = (int)(tile / ncb);
+    const uint16_t *src;
+    size_t row;
+    if (STAGE == 1) {
+        src = r < 128 ? L.gsm : L.usm;
+        row = (size_t)e * I + cb * 128 + (r & 127);
+    } else {
+        src = L.dsm;
+        row = (size_t)e * H + cb * BROWS + r;
+    }
+    const int lift = L.fmt == 0 ? row_lift_from_max(canonical_row_max<0>(src, row, K / 64))
+                                : row_lift_from_max(canonical_row_max<1>(src, row, K / 128));
+    const PackLayout pl = pack_layout(L.E, H, I, L.fmt);
+    dst[(STAGE == 1 ? pl.gu_l : pl.d_l) + o] = (uint8_t)(int8_t)lift;
+}
+
 // Scale words: one thread per word; K-step j of slot r gets the aligned word
-// of the row's canonical scale array holding its group 64 j / G entry.
+// of the row's canonical scale array holding its group 64 j / G entry, its
+// f16 halves times 2^L (the row's lift: ldexp, one rounding) for the int4
+// formats.
 template <int STAGE>
 __global__ __launch_bounds__(256) void pack_scales_kernel(LayerPtrs L, uint8_t *__restrict__ dst) {
     const int H = L.H, I = L.I;
@@ -1257,8 +1484,14 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(LayerPtrs L, uint8_t *
         row = (size_t)e * H + cb * BROWS + r;
     }
     const size_t byte = ((row * (size_t)(K / G) + (size_t)(ks * KS / G)) * esz) & ~(size_t)3;
-    const uint32_t wv = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(src) + byte);
+    uint32_t wv = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(src) + byte);
     const PackLayout pl = pack_layout(L.E, H, I, L.fmt);
+    if (L.fmt == 0 || L.fmt == 1) {
+        const int lift = (int)(int8_t)dst[(STAGE == 1 ? pl.gu_l : pl.d_l) + tile * BROWS + r];
+        const uint32_t lo = __builtin_bit_cast(uint16_t, __builtin_ldexpf16(__builtin_bit_cast(_Float16, (uint16_t)(wv & 0xffffu)), lift));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, __builtin_ldexpf16(__builtin_bit_cast(_Float16, (uint16_t)(wv >> 16)), lift));
+        wv = lo | (hi << 16);
+    }
     reinterpret_cast<uint32_t *>(dst + (STAGE == 1 ? pl.gu_s : pl.d_s))[o] = wv;
 }
 
@@ -1275,6 +1508,11 @@ hipError_t launch_prefill_pack(const LayerPtrs &L, uint8_t *dst, hipStream_t s) 
     const int64_t s1 = t1 * BROWS, s2 = t2 * BROWS;
     hipLaunchKernelGGL((pack_codes_kernel<1, 32>), dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, L, dst);
     hipLaunchKernelGGL((pack_codes_kernel<2, 32>), dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, L, dst);
+    if (L.fmt == 0 || L.fmt == 1) {  // the lifts first: the scale words are taken times 2^L
+        const int64_t l1 = E * (I / 128) * BROWS, l2 = E * (H / BROWS) * BROWS;
+        hipLaunchKernelGGL(pack_lift_kernel<1>, dim3((unsigned)((l1 + 255) / 256)), dim3(256), 0, s, L, dst);
+        hipLaunchKernelGGL(pack_lift_kernel<2>, dim3((unsigned)((l2 + 255) / 256)), dim3(256), 0, s, L, dst);
+    }
     hipLaunchKernelGGL(pack_scales_kernel<1>, dim3((unsigned)((s1 + 255) / 256)), dim3(256), 0, s, L, dst);
     hipLaunchKernelGGL(pack_scales_kernel<2>, dim3((unsigned)((s2 + 255) / 256)), dim3(256), 0, s, L, dst);
     return hipGetLastError();
@@ -1283,7 +1521,8 @@ hipError_t launch_prefill_pack(const LayerPtrs &L, uint8_t *dst, hipStream_t s) 
 template <int FMT>
 static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
-                                     float *y, hipStream_t s, hipEvent_t const *ev, bool x16_ready) {
+                                     int8_t *hx, int8_t *zx, float *y, hipStream_t s, hipEvent_t const *ev,
+                                     bool x16_ready) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
     if (!x16_ready)
@@ -1298,13 +1537,13 @@ static hipError_t launch_prefill_fmt(const uint16_t *x, const float *gate, int64
     auto k2 = one ? grouped_gemm_kernel<FMT, 2, true> : grouped_gemm_kernel<FMT, 2, false>;
     launch_k(k1, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
              (const uint16_t *)x16, (const int32_t *)xexp, H, I, k, L, (const Tile *)g.tiles,
-             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order);
+             (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z, (const int32_t *)g.order, hx, zx);
     launch_k(k2, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, (const int32_t *)nullptr, H, I, k, L, (const Tile *)g.tiles,
              (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z,
-             (const int32_t *)(g.order2 ? g.order2 : g.order));
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
-                       (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
+             (const int32_t *)(g.order2 ? g.order2 : g.order), hx, zx);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z, (const int8_t *)zx,
+                       (const int32_t *)xexp, (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();
 }
 
@@ -1318,31 +1557,32 @@ hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
 }
 
 static hipError_t launch_prefill_fp8(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                     const GroupOut &g, uint16_t *h, uint16_t *z, float *y, hipStream_t s,
-                                     hipEvent_t const *ev) {
+                                     const GroupOut &g, uint16_t *h, uint16_t *z, int8_t *hx, int8_t *zx, float *y,
+                                     hipStream_t s, hipEvent_t const *ev) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
     const unsigned nb1 = (unsigned)(8 * ((tiles + 7) / 8) * (I / 128));  // as launch_prefill_fmt
     const unsigned nb2 = (unsigned)(8 * ((tiles + 7) / 8) * (H / BROWS));
     launch_k(grouped_gemm_fp8_kernel<1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, x,
              H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z,
-             (const int32_t *)g.order);
+             (const int32_t *)g.order, hx, zx);
     launch_k(grouped_gemm_fp8_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles,
-             (const int32_t *)g.perm, gate, h, z, (const int32_t *)(g.order2 ? g.order2 : g.order));
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z,
-                       (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
+             (const int32_t *)g.perm, gate, h, z, (const int32_t *)(g.order2 ? g.order2 : g.order), hx, zx);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z, (const int8_t *)zx,
+                       (const int32_t *)nullptr, (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                   const GroupOut &g, uint16_t *x16, int32_t *xexp, uint16_t *h, uint16_t *z,
-                                  float *y, hipStream_t s, hipEvent_t const *ev, bool x16_ready) {
+                                  int8_t *hx, int8_t *zx, float *y, hipStream_t s, hipEvent_t const *ev,
+                                  bool x16_ready) {
     switch (L.fmt) {
-        case 0: return launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev, x16_ready);
-        case 1: return launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev, x16_ready);
-        case 2: return launch_prefill_fp8(x, gate, T, k, L, g, h, z, y, s, ev);
-        case 3: return launch_prefill_fmt<3>(x, gate, T, k, L, g, x16, xexp, h, z, y, s, ev, x16_ready);
+        case 0: return launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, hx, zx, y, s, ev, x16_ready);
+        case 1: return launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, hx, zx, y, s, ev, x16_ready);
+        case 2: return launch_prefill_fp8(x, gate, T, k, L, g, h, z, hx, zx, y, s, ev);
+        case 3: return launch_prefill_fmt<3>(x, gate, T, k, L, g, x16, xexp, h, z, hx, zx, y, s, ev, x16_ready);
         default: return hipErrorInvalidValue;
     }
 }

@@ -279,12 +279,13 @@ def test_nvfp4_layer_validation():
 
 
 def test_prefill_pack_validation():
-    """The prefill copy: its size (27 E I H / 16 bytes, a host computation),
-    the formats and shapes it takes, and the checks of dst and of the
-    layer's prefill_pack field."""
+    """The prefill copy: its size (27 E I H / 16 bytes, plus a lift byte per
+    weight row for int4, a host computation), the formats and shapes it
+    takes, and the checks of dst and of the layer's prefill_pack field."""
     lib = m.lib()
     for fmt in (0, 1):
-        assert m.moe_q4_prefill_pack_size(_layer(fmt=fmt)) == 27 * 256 * 512 * 2048 // 16
+        assert m.moe_q4_prefill_pack_size(_layer(fmt=fmt)) == \
+            27 * 256 * 512 * 2048 // 16 + 2 * 256 * 512 + 256 * 2048
     nv = _layer(fmt=3, E=8, H=256, I=128)
     nv.global_scale = FAKE
     assert m.moe_q4_prefill_pack_size(nv) == 27 * 8 * 128 * 256 // 16

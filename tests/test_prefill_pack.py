@@ -4,7 +4,8 @@ path, through the C ABI (needs an MI355X).
 Bars:
   * the copy is bit-exact against its layout as the public header states it,
     built here on the host from the canonical arrays by reshapes and
-    transposes (a reordering: no arithmetic);
+    transposes, and for the int4 formats each row's power-of-two lift and its
+    scale words times 2^L;
   * the prefill path gives bit-identical outputs with and without the copy,
     and with it stays within relative L2 2e-3 and max abs 1e-2 of the fp64
     oracle.
@@ -84,6 +85,23 @@ def _step_words(sm, E, N, K, fmt):
     return words[byte // 4].reshape(E, N, K // 64)
 
 
+def _row_lifts(sm, E, N, K, fmt):
+    """[E][N] int: a row's power-of-two lift L = 10 - floor(log2 A), A the
+    largest magnitude among its f16 scales (and mins), 0 for A = 0."""
+    halves = _host_bytes(sm).view(np.float16).reshape(E, N, -1).astype(np.float64)
+    a = np.max(np.abs(halves), axis=2)
+    lg = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 10 - lg, 0).astype(np.int64)
+
+
+def _lift_words(words, lifts):
+    """Both f16 halves of each uint32 word times 2^L of its row (one rounding)."""
+    w = np.ascontiguousarray(words)
+    h = w.view(np.float16).reshape(*w.shape, 2).astype(np.float64)
+    out = np.ldexp(h, lifts[..., None, None]).astype(np.float16)
+    return np.ascontiguousarray(out).view(np.uint32).reshape(w.shape)
+
+
 def expected_pack(lay):
     E, H, I, fmt = lay.num_experts, lay.hidden, lay.inter, lay.fmt
     if fmt == synth.FMT_FP8_B128:
@@ -101,13 +119,25 @@ def expected_pack(lay):
     gu = np.concatenate([gq.reshape(E, I // 128, 128, H // 2), uq.reshape(E, I // 128, 128, H // 2)], axis=2)
     gu_q = _tiles_codes(gu, I // 128, 256, H)
     d_q = _tiles_codes(dq, H // 256, 256, I)
-    gw = _step_words(lay.gate_sm, E, I, H, fmt).reshape(E, I // 128, 128, H // 64)
-    uw = _step_words(lay.up_sm, E, I, H, fmt).reshape(E, I // 128, 128, H // 64)
+    gw = _step_words(lay.gate_sm, E, I, H, fmt)
+    uw = _step_words(lay.up_sm, E, I, H, fmt)
+    dw = _step_words(lay.down_sm, E, H, I, fmt)
+    int4 = fmt in (synth.FMT_ASYM_G64, synth.FMT_SYM_G128)
+    if int4:  # scale words lifted by the row's power of two
+        gl = _row_lifts(lay.gate_sm, E, I, H, fmt)
+        ul = _row_lifts(lay.up_sm, E, I, H, fmt)
+        dl = _row_lifts(lay.down_sm, E, H, I, fmt)
+        gw, uw, dw = _lift_words(gw, gl), _lift_words(uw, ul), _lift_words(dw, dl)
+    gw = gw.reshape(E, I // 128, 128, H // 64)
+    uw = uw.reshape(E, I // 128, 128, H // 64)
     gu_s = np.concatenate([gw, uw], axis=2).transpose(0, 1, 3, 2).reshape(-1)
-    d_s = _step_words(lay.down_sm, E, H, I, fmt).reshape(E, H // 256, 256, I // 64).transpose(0, 1, 3, 2).reshape(-1)
-    out = np.concatenate([gu_q, np.ascontiguousarray(gu_s).view(np.uint8), d_q,
-                          np.ascontiguousarray(d_s).view(np.uint8)])
-    assert out.size == 27 * E * I * H // 16
+    d_s = dw.reshape(E, H // 256, 256, I // 64).transpose(0, 1, 3, 2).reshape(-1)
+    parts = [gu_q, np.ascontiguousarray(gu_s).view(np.uint8), d_q, np.ascontiguousarray(d_s).view(np.uint8)]
+    if int4:  # the lifts: gate|up [E][I/128][256] (gate rows, then up rows), down [E][H/256][256]
+        gul = np.concatenate([gl.reshape(E, I // 128, 128), ul.reshape(E, I // 128, 128)], axis=2)
+        parts += [gul.astype(np.int8).reshape(-1).view(np.uint8), dl.astype(np.int8).reshape(-1).view(np.uint8)]
+    out = np.concatenate(parts)
+    assert out.size == 27 * E * I * H // 16 + (2 * E * I + E * H if int4 else 0)
     return out
 
 
