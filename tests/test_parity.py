@@ -4,8 +4,7 @@ Bars: dequantised weights, router logits, expert indices, histogram, offsets
 and permutation bit-exact; gates within 1e-6 relative; layer outputs within
 relative L2 2e-3 and max abs 1e-2 of the fp64 oracle.  Inputs are the seeded
 synthetic workloads (synth.make_case) at full size, plus small and ragged
-shapes; where a full-size output is too large for the oracle, sampled tokens
-are compared (the layer is token-wise independent).
+shapes; every token of the full-size layers is compared.
 """
 from __future__ import annotations
 
@@ -212,10 +211,27 @@ def test_prefill_configs(cfg):
     _layer_parity(get_case(cfg), "prefill")
 
 
-def test_prefill_long_sym_sampled():
+def test_prefill_long_sym_all_tokens():
+    """The 4096-token symmetric-g128 layer: every token against the oracle."""
+    _layer_parity(get_case(5), "prefill")
+
+
+def test_forward_long_sym_packed_all_tokens():
+    """The long-prompt layer as the benchmark runs it: moe_q4_forward with
+    the logits given and the prefill copy of the weights (top-k, grouping
+    count and x conversion in one launch, then the grouped GEMMs); every
+    token against the oracle."""
+    import quantized_moe_expert_amd as m
     case = get_case(5)
-    tokens = np.unique(np.concatenate([np.arange(0, 4096, 97), [1, 2, 4094, 4095]]))
-    _layer_parity(case, "prefill", tokens=tokens)
+    lay = case.layers[0]
+    pk = m.prefill_pack(lay)
+    st = m.layer_struct(lay, pack=pk)
+    lg, idx, gate, y, _, _ = _forward(st, case.x, None, case.logits, case.T, case.k)
+    torch.cuda.synchronize()
+    ir, gr = oracle.topk(np_u16(case.logits), case.T, case.E, case.k)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    r, a = assert_close(y.cpu().numpy(), oracle_y(lay, np_u16(case.x), ir, gr, case.k), "forward long packed")
+    say(f"[forward packed] config 5, all 4096 tokens: rel L2 {r:.2e}, max abs {a:.2e}")
 
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])
