@@ -85,6 +85,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-pack", action="store_true",
                    help="prefill GEMMs read the canonical weight arrays instead of the prefill copy")
+    p.add_argument("--deterministic", action="store_true",
+                   help="moe_q4_forward_det: decode y summed per token in slot order (run-to-run identical)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy 3 times (HBM counter calibration) and exit")
     return p.parse_args()
@@ -247,7 +249,7 @@ def main():
     packs = [m.prefill_pack(l) for l in layers] if use_pack else [None] * len(layers)
     structs = [m.layer_struct(l, pack=p) for l, p in zip(layers, packs)]
     sstructs = [m.shared_struct(sx) for sx in shareds] if shareds else None
-    ws_bytes = m.workspace_size(m.WS_FORWARD, T, E, k, H, I)
+    ws_bytes = m.workspace_size(m.WS_FORWARD_DET if args.deterministic else m.WS_FORWARD, T, E, k, H, I)
     if with_shared:
         ws_bytes += m.workspace_size(m.WS_SHARED, T, 1, 1, H, SHARED_INTER)
     wsf = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -279,13 +281,14 @@ def main():
         rw = routers[li] if routers[0] is not None else None
         logits_in = lg if rw is not None else case.logits
         sx = sstructs[li] if sstructs else None
+        fwd = m.moe_q4_forward_det if args.deterministic else m.moe_q4_forward_ex
         if base_wl == "frame" and j > 0:
             x_prev = case.x if j == 1 else xbuf[(j - 1) & 1]
-            m.moe_q4_forward_ex(x_prev, ybuf[(j - 1) & 1], xbuf[j & 1], rw, None, logits_in, T, k, structs[li], sx,
-                                idx, gate, ybuf[j & 1], wsf, events=evs)
+            fwd(x_prev, ybuf[(j - 1) & 1], xbuf[j & 1], rw, None, logits_in, T, k, structs[li], sx,
+                idx, gate, ybuf[j & 1], wsf, events=evs)
         else:
-            m.moe_q4_forward_ex(case.x, None, None, rw, None, logits_in, T, k, structs[li], sx, idx, gate,
-                                ybuf[j & 1], wsf, events=evs)
+            fwd(case.x, None, None, rw, None, logits_in, T, k, structs[li], sx, idx, gate,
+                ybuf[j & 1], wsf, events=evs)
 
     def step():
         """One step: every layer of the workload once."""
@@ -455,7 +458,7 @@ def main():
                       "format": "int8_sym_g128" if only_shared else {
                           synth.FMT_ASYM_G64: "asym_g64", synth.FMT_SYM_G128: "sym_g128",
                           synth.FMT_FP8_B128: "fp8_e4m3_b128", synth.FMT_NVFP4: "nvfp4"}[case.fmt],
-                      "shared_expert": with_shared,
+                      "shared_expert": with_shared, "deterministic": bool(args.deterministic),
                       "weights": "prefill copy" if use_pack else "canonical"},
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)

@@ -88,7 +88,8 @@ typedef enum {
     MOE_Q4_WS_PREFILL = 2,
     MOE_Q4_WS_GROUP = 3,
     MOE_Q4_WS_FORWARD = 4,
-    MOE_Q4_WS_SHARED = 5    /* moe_q4_shared: pass the shared expert's H and I */
+    MOE_Q4_WS_SHARED = 5,   /* moe_q4_shared: pass the shared expert's H and I */
+    MOE_Q4_WS_FORWARD_DET = 6  /* moe_q4_forward_det */
 } moe_q4_ws_kind;
 
 /*
@@ -269,9 +270,11 @@ MOE_Q4_API int moe_q4_decode(const void *x, const int32_t *topk_idx, const float
  * 2^15 and keeps its groups' scale / 16 normal (groups more than 2^24 below
  * the row's largest scale lose precision; FP8 and NVFP4 codes enter
  * exactly); h between the two products and each routed row's gate-weighted
- * down output are rounded to f16 per (row, 128 columns) after scaling by a
- * power of two (largest magnitude into [2^14, 2^15)), so f16's range limits
- * none of them, and a token's k rows are summed in fp32 into y (float
+ * down output are rounded to f16 after scaling by a power of two chosen per
+ * block (h: 128 columns of I, one exponent for all rows of a work tile; the
+ * down output: 32 rows by 64 columns of H) that puts the block's largest
+ * magnitude into [2^14, 2^15), so f16's range limits none of them, and a
+ * token's k rows are summed in fp32 into y (float
  * [T][H], written whole; deterministic).  Same arguments
  * as moe_q4_decode; ws >= moe_q4_workspace_size(MOE_Q4_WS_PREFILL, ...).
  */
@@ -360,6 +363,28 @@ MOE_Q4_API int moe_q4_forward_ex(const void *x, const float *residual_y, void *x
                                  const float *bias, void *logits, int64_t T, int32_t k, const moe_q4_layer *w,
                                  const moe_q4_shared_expert *shared, int32_t *topk_idx, float *topk_gate, float *y,
                                  void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
+
+/*
+ * moe_q4_forward_ex with a run-to-run bit-identical y on the decode path
+ * (drama-rs page, "Tests": every kernel checked against a plain reference;
+ * the same input must give the same output).  moe_q4_forward_ex's decode
+ * path adds each routed row into y with float atomics, whose order, and so
+ * whose last bits, vary between runs.  Here the down launch stores each
+ * routed (token, slot) row, gate applied, in the workspace ([T*k][H] fp32),
+ * and one more launch sums a token's rows in slot order 0, 1, ..., k-1
+ * into y; the shared expert (if any) then runs in moe_q4_shared's own
+ * launches and is added last.  The prefill path is the same as
+ * moe_q4_forward_ex's (already slot-ordered).  Arguments, layouts and
+ * errors as moe_q4_forward_ex, except the workspace:
+ *   ws  >= moe_q4_workspace_size(MOE_Q4_WS_FORWARD_DET, T, E, k, H, I)
+ *          (+ moe_q4_workspace_size(MOE_Q4_WS_SHARED, ...) with a shared
+ *          expert),
+ * its control block cleared once by moe_q4_workspace_init.
+ */
+MOE_Q4_API int moe_q4_forward_det(const void *x, const float *residual_y, void *x_out, const void *router_w,
+                                  const float *bias, void *logits, int64_t T, int32_t k, const moe_q4_layer *w,
+                                  const moe_q4_shared_expert *shared, int32_t *topk_idx, float *topk_gate, float *y,
+                                  void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
 
 /* Clears the control block of a workspace used with moe_q4_forward (once,
  * after allocation).  Enqueued on stream. */

@@ -17,7 +17,7 @@ ASYM_G64 = 0
 SYM_G128 = 1
 FP8_B128 = 2
 NVFP4 = 3
-WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP, WS_FORWARD, WS_SHARED = 0, 1, 2, 3, 4, 5
+WS_ROUTE, WS_DECODE, WS_PREFILL, WS_GROUP, WS_FORWARD, WS_SHARED, WS_FORWARD_DET = 0, 1, 2, 3, 4, 5, 6
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 # every entry point declared in include/moe_q4.h
@@ -26,7 +26,7 @@ EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_deco
            "moe_q4_workspace_init",
            "moe_q4_shared", "moe_q4_shared_timed", "moe_q4_dequant_int8", "moe_q4_forward_ex",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string",
-           "moe_q4_prefill_pack_size", "moe_q4_prefill_pack", "moe_q4_forward_noalloc")
+           "moe_q4_prefill_pack_size", "moe_q4_prefill_pack", "moe_q4_forward_noalloc", "moe_q4_forward_det")
 NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_Q4_NOALLOC_SCRATCH_BYTES
 STAGE_EVENTS = 4
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.moe_q4_forward_ex.argtypes = [P, P, P, P, P, P, i64, i32, ctypes.POINTER(Layer),
                                         ctypes.POINTER(SharedExpert), P, P, P, P, sz, P,
                                         ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_q4_forward_det.restype = ctypes.c_int
+        L.moe_q4_forward_det.argtypes = L.moe_q4_forward_ex.argtypes
         L.moe_q4_workspace_init.restype = ctypes.c_int
         L.moe_q4_workspace_init.argtypes = [P, sz, P]
         L.moe_q4_dequant.restype = ctypes.c_int
@@ -252,7 +254,7 @@ def moe_q4_forward_noalloc(x, residual_y, x_out, router_w, bias, logits, T, k, l
 
 
 def moe_q4_forward_ex(x, residual_y, x_out, router_w, bias, logits, T, k, layer, shared, topk_idx, topk_gate, y,
-                      ws, stream=None, events=None):
+                      ws, stream=None, events=None, _name="moe_q4_forward_ex"):
     """moe_q4_forward with the layer's shared expert (None: without); ``events``: None or 4 hipEvent_t
     handles as moe_q4_forward_timed."""
     w, nb = _ws(ws)
@@ -261,10 +263,18 @@ def moe_q4_forward_ex(x, residual_y, x_out, router_w, bias, logits, T, k, layer,
     if shared is not None:
         sx = ctypes.byref(shared_struct(shared) if not isinstance(shared, SharedExpert) else shared)
     ev = (ctypes.c_void_p * STAGE_EVENTS)(*[int(e) for e in events]) if events is not None else None
-    _check("moe_q4_forward_ex",
-           lib().moe_q4_forward_ex(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias), _ptr(logits),
-                                   T, k, ctypes.byref(st), sx, _ptr(topk_idx), _ptr(topk_gate), _ptr(y), w, nb,
-                                   _stream(stream), ev))
+    _check(_name,
+           getattr(lib(), _name)(_ptr(x), _ptr(residual_y), _ptr(x_out), _ptr(router_w), _ptr(bias), _ptr(logits),
+                                 T, k, ctypes.byref(st), sx, _ptr(topk_idx), _ptr(topk_gate), _ptr(y), w, nb,
+                                 _stream(stream), ev))
+
+
+def moe_q4_forward_det(x, residual_y, x_out, router_w, bias, logits, T, k, layer, shared, topk_idx, topk_gate, y,
+                       ws, stream=None, events=None):
+    """moe_q4_forward_ex with a run-to-run identical decode y (routed rows summed in slot order); the
+    workspace from workspace_size(WS_FORWARD_DET, ...)."""
+    moe_q4_forward_ex(x, residual_y, x_out, router_w, bias, logits, T, k, layer, shared, topk_idx, topk_gate, y,
+                      ws, stream, events, _name="moe_q4_forward_det")
 
 
 def moe_q4_workspace_init(ws, stream=None):

@@ -211,10 +211,15 @@ size_t moe_q4_workspace_size(int which, int64_t T, int32_t E, int32_t k, int32_t
         case MOE_Q4_WS_DECODE: carve_decode(c, T, E, k, H, I); break;
         case MOE_Q4_WS_PREFILL: carve_prefill(c, T, E, k, H, I); break;
         case MOE_Q4_WS_FORWARD:
+        case MOE_Q4_WS_FORWARD_DET:
             c.take<char>(CONTROL_BYTES);
             c.take<unsigned int>(T * (int64_t)E);  // logit hand-off of the one-launch routing
-            if (forward_uses_decode(T, k)) carve_decode(c, T, E, k, H, I);
-            else carve_prefill(c, T, E, k, H, I);
+            if (forward_uses_decode(T, k)) {
+                carve_decode(c, T, E, k, H, I);
+                if (which == MOE_Q4_WS_FORWARD_DET) c.take<float>(T * k * (int64_t)H);  // routed rows
+            } else {
+                carve_prefill(c, T, E, k, H, I);
+            }
             break;
         case MOE_Q4_WS_SHARED: carve_shared(c, T, H, I); break;
         default: return 0;
@@ -362,7 +367,7 @@ static int forward_checks(const void *x, const float *residual_y, void *x_out, c
 static int run_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
                        void *logits, int64_t T, int32_t k, const moe_q4_layer *w, const moe_q4_shared_expert *sx,
                        int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes,
-                       moe_q4_stream stream, void *const *events) {
+                       moe_q4_stream stream, void *const *events, bool det = false) {
     int st = forward_checks(x, residual_y, x_out, logits, T, k, w, sx, topk_idx, topk_gate, y, events);
     if (st || T == 0) return st;
     const int E = w->num_experts, H = w->hidden, I = w->inter;
@@ -370,7 +375,7 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
-    const size_t need_fwd = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, T, E, k, H, I);
+    const size_t need_fwd = moe_q4_workspace_size(det ? MOE_Q4_WS_FORWARD_DET : MOE_Q4_WS_FORWARD, T, E, k, H, I);
     const size_t need = need_fwd + (sx ? moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, sx->inter) : 0);
     if (!ws || ws_bytes < need) return MOE_Q4_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -385,7 +390,9 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
         sws = carve_shared(cs, T, H, sx->inter);
         hs = sws.h;
     }
-    const bool fuse = sx && dec && decode_fuses_shared(L, &S);
+    // the deterministic decode keeps the shared expert out of the routed
+    // launches (its rows would be added with atomics)
+    const bool fuse = sx && dec && !det && decode_fuses_shared(L, &S);
     const SharedPtrs *Sf = fuse ? &S : nullptr;
     // the shared expert on its own, after the routed experts: y += its output
     auto shared_after = [&](const uint16_t *xin_) {
@@ -399,6 +406,7 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     uint16_t *lg = static_cast<uint16_t *>(logits);
     if (dec) {
         DecodeWs d = carve_decode(c, T, E, k, H, I);
+        float *zrows = det ? c.take<float>(T * k * (int64_t)H) : nullptr;
         if ((forward_fused_route(T, E) || !wr) && decode_routes_in_block(T, k, E)) {
             // router GEMV (+ residual, y clear) in one launch; the expert GEMV
             // launches route the tokens in every workgroup
@@ -408,7 +416,8 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
                                                       e3));
             if (st) return st;
             st = hip_status(
-                launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s, e0, e1, Sf, hs));
+                launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s, e0, e1, Sf, hs,
+                                             zrows));
             return st ? st : shared_after(xin);
         }
         if (forward_fused_route(T, E) || !wr) {
@@ -425,7 +434,7 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
             if (!st) st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H, e2, e3));
         }
         if (st) return st;
-        st = hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1, Sf, hs));
+        st = hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1, Sf, hs, zrows));
         return st ? st : shared_after(xin);
     }
     if (residual_y) {
@@ -474,6 +483,14 @@ int moe_q4_forward_ex(const void *x, const float *residual_y, void *x_out, const
                       void *const *events) {
     return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, shared, topk_idx, topk_gate, y, ws,
                        ws_bytes, stream, events);
+}
+
+int moe_q4_forward_det(const void *x, const float *residual_y, void *x_out, const void *router_w,
+                       const float *bias, void *logits, int64_t T, int32_t k, const moe_q4_layer *w,
+                       const moe_q4_shared_expert *shared, int32_t *topk_idx, float *topk_gate, float *y, void *ws,
+                       size_t ws_bytes, moe_q4_stream stream, void *const *events) {
+    return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, shared, topk_idx, topk_gate, y, ws,
+                       ws_bytes, stream, events, true);
 }
 
 }  // extern "C"

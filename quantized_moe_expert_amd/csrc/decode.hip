@@ -277,7 +277,8 @@ template <int LPR, int FMT>
 __device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &L, const Tile &tile,
                                           const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
                                           const float *__restrict__ topk_gate, const float *__restrict__ h,
-                                          float *__restrict__ y, float (*s_out)[DEC_RB_MAX]) {
+                                          float *__restrict__ y, float *__restrict__ zrows,
+                                          float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     constexpr int G = FMT == 0 ? 64 : 128;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -399,11 +400,8 @@ __device__ __forceinline__ void down_item(int H, int I, int k, const LayerPtrs &
         }
     }
     __syncthreads();
-    // one float atomic per output and routed (token, slot), coalesced
-    for (int i = tid; i < nt * ir.nloc; i += blockDim.x) {
-        const int u = i / ir.nloc, d = i % ir.nloc;
-        if (ir.valid(d)) unsafeAtomicAdd(y + (size_t)tok[u] * H + ir.grow(d), s_out[u][d]);
-    }
+    // one float atomic (or one store) per output and routed (token, slot)
+    emit_down_rows(y, zrows, tile, tok, nt, H, ir, s_out);
     __syncthreads();
 }
 
@@ -467,7 +465,7 @@ template <int LPR, int FMT, bool SHARED>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     int max_nt, const float *__restrict__ topk_gate, const float *__restrict__ h, float *__restrict__ y, int T,
-    SharedPtrs S, const uint16_t *__restrict__ hs) {
+    SharedPtrs S, const uint16_t *__restrict__ hs, float *__restrict__ zrows) {
     constexpr int BR = DEC_WAVES * (WAVE / LPR);
     int nt_all = *ntiles;
     nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
@@ -478,9 +476,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
         const Tile tile = sane_tile(tiles[j], L.E, P);
         const ItemRows<BR> ir = item_rows<BR>(chunk, it, H);
         if (ir.steps <= 0) continue;
-        if constexpr (FMT == 2) fp8_down_item<LPR>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
-        else if constexpr (FMT == 3) nvfp4_down_item<LPR>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
-        else down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, s_out);
+        if constexpr (FMT == 2) fp8_down_item<LPR>(H, I, k, L, tile, ir, topk_gate, h, y, zrows, s_out);
+        else if constexpr (FMT == 3) nvfp4_down_item<LPR>(H, I, k, L, tile, ir, topk_gate, h, y, zrows, s_out);
+        else down_item<LPR, FMT>(H, I, k, L, tile, ir, topk_gate, h, y, zrows, s_out);
     }
     if constexpr (SHARED && LPR >= 4) {
         const int ntt = (T + DECODE_TT - 1) / DECODE_TT;
@@ -713,11 +711,49 @@ __global__ __launch_bounds__(1024) void decode_route_group_kernel(
         __hip_atomic_store(counter + ROUTE_COUNTER_STRIDE * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// y[t] = z[t k] + z[t k + 1] + ... + z[t k + k - 1] (rows of H floats), the
+// routed rows of a token added in slot order, so that every run gives the
+// same bits; one float4 of y per thread.
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ z, int T, int k, int H,
+                                                             float *__restrict__ y) {
+    const int h4 = H / 4;
+    const int64_t n4 = (int64_t)T * h4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / h4, c = i % h4;
+        const float4 *zr = reinterpret_cast<const float4 *>(z) + t * k * h4 + c;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < k; s0 += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < k) v[j] = zr[(int64_t)(s0 + j) * h4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (s0 + j < k) {
+                    acc.x += v[j].x;
+                    acc.y += v[j].y;
+                    acc.z += v[j].z;
+                    acc.w += v[j].w;
+                }
+        }
+        reinterpret_cast<float4 *>(y)[i] = acc;
+    }
+}
+
+hipError_t launch_decode_combine(const float *z, int64_t T, int k, int H, float *y, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    if (H % 4 || k < 1) return hipErrorInvalidValue;
+    const int64_t n4 = T * (H / 4);
+    const int grid = (int)((n4 + 255) / 256 < 1024 ? (n4 + 255) / 256 : 1024);
+    launch_k(decode_combine_kernel, dim3(grid), dim3(256), s, nullptr, nullptr, z, (int)T, k, H, y);
+    return hipGetLastError();
+}
+
 template <int FMT, bool ROUTE, bool SHARED>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
-                                     const SharedPtrs &S, uint16_t *hs) {
+                                     const SharedPtrs &S, uint16_t *hs, float *zrows) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
     const int mt = (int)max_tiles(P, L.E, DECODE_TT);
@@ -739,12 +775,13 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
         constexpr auto kern = decode_down_kernel<LP, FMT, SHARED>;                                               \
         launch_k(kern, dim3(resident_grid<kern>()), block, s, nullptr, nullptr, H, I, k, P, L,                   \
                  (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const float *)h, y, (int)T, S,  \
-                 (const uint16_t *)hs);                                                                          \
+                 (const uint16_t *)hs, zrows);                                                                   \
     } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
+    if (zrows) return launch_decode_combine(zrows, T, k, H, y, s);
     return hipGetLastError();
 }
 
@@ -759,15 +796,15 @@ template <bool ROUTE>
 static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
-                                     const SharedPtrs *S, uint16_t *hs) {
-    if (S && !decode_fuses_shared(L, S)) return hipErrorInvalidValue;
+                                     const SharedPtrs *S, uint16_t *hs, float *zrows) {
+    if (S && (zrows || !decode_fuses_shared(L, S))) return hipErrorInvalidValue;
     const SharedPtrs none{};
 #define FMT_CASE(F)                                                                                            \
     case F:                                                                                                    \
         return S ? launch_experts_fmt<F, ROUTE, true>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, \
-                                                      *S, hs)                                                  \
+                                                      *S, hs, nullptr)                                         \
                  : launch_experts_fmt<F, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out,      \
-                                                       gate_out, none, nullptr);
+                                                       gate_out, none, nullptr, zrows);
     switch (L.fmt) {
         FMT_CASE(0) FMT_CASE(1) FMT_CASE(2) FMT_CASE(3)
         default: return hipErrorInvalidValue;
@@ -777,8 +814,8 @@ static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64
 
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1, const SharedPtrs *S, uint16_t *hs) {
-    return launch_experts_any<false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr, S, hs);
+                                 hipEvent_t e1, const SharedPtrs *S, uint16_t *hs, float *zrows) {
+    return launch_experts_any<false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr, S, hs, zrows);
 }
 
 // Every expert workgroup repeats this routing before its first weight load,
@@ -792,9 +829,9 @@ bool decode_routes_in_block(int64_t T, int k, int E) {
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const SharedPtrs *S,
-                                        uint16_t *hs) {
+                                        uint16_t *hs, float *zrows) {
     if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;
-    return launch_experts_any<true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate, S, hs);
+    return launch_experts_any<true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate, S, hs, zrows);
 }
 
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,

@@ -111,6 +111,28 @@ __device__ __forceinline__ ItemRows<BR> item_rows(int chunk, const Items &it, in
     return r;
 }
 
+// A down item's outputs (s_out[u][d]: pair u of the tile, local row d,
+// gate applied): added into y[token] with one float atomic each, or, with
+// zrows, stored as row d of the routed pair's own [H] row of zrows (a
+// [T * k][H] array that a slot-ordered sum turns into y).
+template <int BR>
+__device__ __forceinline__ void emit_down_rows(float *__restrict__ y, float *__restrict__ zrows, const Tile &tile,
+                                               const int (&tok)[DECODE_TT], int nt, int H, const ItemRows<BR> &ir,
+                                               float (*s_out)[DEC_RB_MAX]) {
+    for (int i = threadIdx.x; i < nt * ir.nloc; i += blockDim.x) {
+        const int u = i / ir.nloc, d = i % ir.nloc;
+        if (!ir.valid(d)) continue;
+        // pair / token of slot u by selects (a dynamic index would move the
+        // per-thread arrays to memory)
+        int p = tile.pair[0], t = tok[0];
+#pragma unroll
+        for (int q = 1; q < DECODE_TT; ++q)
+            if (u == q) p = tile.pair[q], t = tok[q];
+        if (zrows) zrows[(size_t)p * H + ir.grow(d)] = s_out[u][d];
+        else unsafeAtomicAdd(y + (size_t)t * H + ir.grow(d), s_out[u][d]);
+    }
+}
+
 constexpr int DEC_WAVES = 4;  // waves per decode workgroup
 constexpr int DEC_NB = 2;     // row loads per lane per pipeline stage
 

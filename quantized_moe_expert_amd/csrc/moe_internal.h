@@ -127,11 +127,16 @@ hipError_t launch_group_after_count(const int32_t *idx, int64_t T, int k, int E,
 // gate-weighted add into y (y must be cleared first).  e0 / e1 time the
 // gate/up kernel.  With S the shared expert's items run in the same two
 // launches (hs: its f16 [T][I] SwiGLU output); S needs
-// decode_fuses_shared.
+// decode_fuses_shared.  With zrows ([T*k][H] floats) the down kernel stores
+// each routed row there instead of adding into y, and a third launch sums
+// each token's rows into y in slot order (run-to-run identical y); zrows
+// excludes S.
 bool decode_fuses_shared(const LayerPtrs &L, const SharedPtrs *S);
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
-                                 hipEvent_t e1 = nullptr, const SharedPtrs *S = nullptr, uint16_t *hs = nullptr);
+                                 hipEvent_t e1 = nullptr, const SharedPtrs *S = nullptr, uint16_t *hs = nullptr,
+                                 float *zrows = nullptr);
+hipError_t launch_decode_combine(const float *z, int64_t T, int k, int H, float *y, hipStream_t s);
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64
 // tokens in one launch; clears y (T*H floats); with yres writes the residual
@@ -153,7 +158,8 @@ bool decode_routes_in_block(int64_t T, int k, int E);
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
-                                        const SharedPtrs *S = nullptr, uint16_t *hs = nullptr);
+                                        const SharedPtrs *S = nullptr, uint16_t *hs = nullptr,
+                                        float *zrows = nullptr);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);

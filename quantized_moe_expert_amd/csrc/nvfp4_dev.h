@@ -148,7 +148,8 @@ template <int LPR>
 __device__ __forceinline__ void nvfp4_down_item(int H, int I, int k, const LayerPtrs &L, const Tile &tile,
                                                 const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
                                                 const float *__restrict__ topk_gate, const float *__restrict__ h,
-                                                float *__restrict__ y, float (*s_out)[DEC_RB_MAX]) {
+                                                float *__restrict__ y, float *__restrict__ zrows,
+                                                float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR, sub = lane / LPR;
@@ -260,10 +261,7 @@ __device__ __forceinline__ void nvfp4_down_item(int H, int I, int k, const Layer
         }
     }
     __syncthreads();
-    for (int i = tid; i < nt * ir.nloc; i += blockDim.x) {
-        const int u = i / ir.nloc, d = i % ir.nloc;
-        if (ir.valid(d)) unsafeAtomicAdd(y + (size_t)tok[u] * H + ir.grow(d), s_out[u][d]);
-    }
+    emit_down_rows(y, zrows, tile, tok, nt, H, ir, s_out);
     __syncthreads();
 }
 

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -171,6 +171,26 @@ def test_forward_validation():
     # every decode-path shape fits: 64 tokens x top-16 (1024 pairs) at H = I = 2048, E = 1024
     assert m.workspace_size(m.WS_FORWARD, 64, 1024, 16, 2048, 2048) <= m.NOALLOC_SCRATCH_BYTES
     assert L.moe_q4_workspace_init(FAKE, 100, None) == _lib.ERR_WORKSPACE
+
+
+def test_forward_det_validation():
+    """The slot-ordered decode entry point: its workspace adds the [T*k][H] fp32 routed rows on the decode
+    path only, and it refuses a workspace sized for moe_q4_forward."""
+    L = m.lib()
+    lay = _layer()
+    for T, k in ((1, 8), (16, 8), (64, 16)):
+        base = m.workspace_size(m.WS_FORWARD, T, 256, k, 2048, 512)
+        det = m.workspace_size(m.WS_FORWARD_DET, T, 256, k, 2048, 512)
+        assert det >= base + T * k * 2048 * 4
+        assert det <= base + T * k * 2048 * 4 + 4096
+    assert m.workspace_size(m.WS_FORWARD_DET, 4096, 256, 8, 2048, 512) == \
+        m.workspace_size(m.WS_FORWARD, 4096, 256, 8, 2048, 512)
+    f = lambda x=FAKE, T=16, nb=1 << 30, layer=lay: L.moe_q4_forward_det(
+        x, None, None, FAKE, None, FAKE, T, 8, ctypes.byref(layer), None, FAKE, FAKE, FAKE, FAKE, nb, None, None)
+    assert f(T=0) == _lib.OK
+    assert f(x=None) == _lib.ERR_INVALID_ARG
+    assert f(layer=_layer(fmt=4)) == _lib.ERR_UNSUPPORTED
+    assert f(nb=m.workspace_size(m.WS_FORWARD, 16, 256, 8, 2048, 512)) == _lib.ERR_WORKSPACE
 
 
 def test_dequant_and_residual_validation():
