@@ -374,9 +374,9 @@ def main():
                 "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_bytes": int(alg_bytes)}
     elif decode_path:
         # dominant kernel: gate/up GEMV + SwiGLU: reads the gate and up codes and
-        # scales of every active expert once and the activations, writes h (f16)
+        # scales of every active expert once and the activations, writes h (fp32)
         dom = "decode_gateup_kernel"
-        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 2 + sx_bytes
+        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 4 + sx_bytes
         achieved = alg_bytes / (stage_avg[0] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -566,12 +566,23 @@ __global__ __launch_bounds__(256) void decode_router_kernel(
 // Routing of a few tokens in one launch.  A workgroup (16 waves) computes
 // the router logits of ROUTE_EG experts for ROUTE_TG tokens, one (expert,
 // token) dot per wave; the tokens' input rows are staged in LDS once per
-// workgroup (so every input row is formed E / ROUTE_EG times, not E).  The logits travel to the workgroup that arrives last
-// through agent-scope relaxed atomic stores and loads (coherent across the
-// XCDs' L2 caches) and a counter in the workspace (zero between calls): each
-// workgroup waits for its stores to complete, then counts itself in.  This
-// avoids whole-L2 write-back and invalidate fences, which cost far more than
-// the routing itself when hundreds of workgroups issue them.  The last
+// workgroup (so every input row is formed E / ROUTE_EG times, not E).  The
+// logits travel to the workgroup that arrives last through agent-scope
+// relaxed atomic stores and loads (coherent across the XCDs' L2 caches) and
+// a counter in the workspace (zero between calls): each workgroup waits for
+// its stores to complete, then counts itself in.  Why this is ordered
+// without release / acquire: (1) every shared value is itself an
+// agent-scope atomic, so all of them live at the device's coherence point
+// and no cache needs writing back or invalidating; (2) s_waitcnt vmcnt(0)
+// returns only once each store is acknowledged there, and the workgroup's
+// barrier puts every wave's wait before thread 0's count-in; (3) the last
+// workgroup issues its loads only after the count-in's returned value,
+// through a barrier, so no load can be served before that value existed.
+// A fence would add what (1) makes unnecessary: whole-L2 write-back and
+// invalidate, which cost far more than the routing itself when hundreds of
+// workgroups issue them.  A launch that never completes would leave the
+// counter non-zero (the next call's output is then wrong, not hung);
+// moe_q4_workspace_init clears it.  The last
 // workgroup stages the logits in LDS, takes the top-k of every token and
 // groups the pairs by expert (from LDS copies of the indices).  Without
 // router weights one workgroup does top-k and grouping on the given logits.
