@@ -353,7 +353,7 @@ def main():
     lay0 = layers[0]
     proj_bytes = expert_bytes(lay0) // 3        # one projection of one expert (codes + scales)
     P = T * k
-    sx_bytes = shared_gateup_bytes(shareds[0]) + T * SHARED_INTER * 2 if with_shared else 0
+    sx_bytes = shared_gateup_bytes(shareds[0]) + T * SHARED_INTER * 4 if with_shared else 0  # + h (fp32) out
     if shared_gemm:
         # dominant kernel: the shared gate/up GEMM + SwiGLU on the matrix cores
         dom = "shared_gemm_kernel<1> (gate/up f16 GEMM + SwiGLU)"
@@ -364,7 +364,7 @@ def main():
                 "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_flops": flops}
     elif only_shared:
         # dominant kernel: the shared gate/up GEMV + SwiGLU: its int8 codes and
-        # scales once, the activations, h (f16) out
+        # scales once, the activations, h (fp32) out
         dom = "shared_gateup_kernel"
         alg_bytes = sx_bytes + T * H * 2
         achieved = alg_bytes / (stage_avg[0] * 1e-3) / 1e9

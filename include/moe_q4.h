@@ -417,12 +417,16 @@ MOE_Q4_API int moe_q4_prefill_timed(const void *x, const int32_t *topk_idx, cons
  * Up to 64 tokens (or H not a multiple of 256): two GEMV launches that
  * stream the int8 codes: gate and up with SwiGLU (products of codes and x
  * exact in fp32, fp32 sums, each 128-group's scale applied to its partial
- * sum) into h rounded to f16 (|h| must stay below 65504), then the down GEMV
- * (exact products of codes and f16 h, fp32 sums).  From 65 tokens: x scaled
- * per token by a power of two into f16 (as moe_q4_prefill), then two dense
- * f16 matrix-core GEMMs whose weights are s * q rounded once to f16; h is
- * rounded to f16 between them.  y is written by one thread per output
- * (deterministic).
+ * sum) into fp32 h, then the down GEMV, which scales each token's h row by
+ * the power of two that puts its largest magnitude in [2^14, 2^15) before
+ * rounding it to f16 (exact products of codes and f16 h, fp32 sums, the
+ * power of two taken off the result).  From 65 tokens: x scaled per token by
+ * a power of two 2^-e into f16 (as moe_q4_prefill), then two dense f16
+ * matrix-core GEMMs whose weights are s * q rounded once to f16; h is
+ * rounded to f16 between them after scaling each token's row by 2^-2e and
+ * each block of 128 h columns of a tile of tokens by a power of two (both
+ * taken off in the down GEMM).  So f16's range limits neither x nor h on
+ * either path.  y is written by one thread per output (deterministic).
  *   x   bf16 [T][H];  y  float [T][H], read when accumulate != 0
  *   ws  >= moe_q4_workspace_size(MOE_Q4_WS_SHARED, T, 1, 1, H, I) bytes
  * Same conventions as the other entry points; T * H and T * I below 2^31.

@@ -163,23 +163,27 @@ int check_shared(const moe_q4_shared_expert *sx) {
 // exponents when it runs.
 bool shared_uses_gemm(int64_t T, int H) { return T >= SHARED_GEMM_MIN_T && H % 256 == 0; }
 struct SharedWs {
-    uint16_t *h;
+    float *h;  // fp32 [T][I] (GEMV path); the GEMM path keeps f16 h in its first half
     uint16_t *x16;
     int32_t *xexp;
+    int8_t *hx;  // GEMM path: h's exponents [T][I / 128]
 };
 SharedWs carve_shared(Carver &c, int64_t T, int H, int I) {
     SharedWs w;
-    w.h = c.take<uint16_t>(T * (int64_t)I);
+    w.h = c.take<float>(T * (int64_t)I);
     const bool gemm = shared_uses_gemm(T, H);
     w.x16 = c.take<uint16_t>(gemm ? T * (int64_t)H : 0);
     w.xexp = c.take<int32_t>(gemm ? T : 0);
+    w.hx = c.take<int8_t>(gemm ? T * (int64_t)(I / 128) : 0);
     return w;
 }
 hipError_t launch_shared_any(const uint16_t *x, int64_t T, const SharedPtrs &S, const SharedWs &w, float *y,
                              bool accumulate, hipStream_t s, hipEvent_t const *ev) {
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr, e2 = ev ? ev[2] : nullptr,
                e3 = ev ? ev[3] : nullptr;
-    if (shared_uses_gemm(T, S.H)) return launch_shared_gemm(x, T, S, w.x16, w.xexp, w.h, y, accumulate, s, e0, e1, e2, e3);
+    if (shared_uses_gemm(T, S.H))
+        return launch_shared_gemm(x, T, S, w.x16, w.xexp, reinterpret_cast<uint16_t *>(w.h), w.hx, y, accumulate, s,
+                                  e0, e1, e2, e3);
     return launch_shared(x, T, S, w.h, y, accumulate, s, e0, e1, e2, e3);
 }
 
@@ -383,7 +387,7 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
     // the shared expert's h follows the forward regions
     SharedPtrs S{};
     SharedWs sws{};
-    uint16_t *hs = nullptr;
+    float *hs = nullptr;
     if (sx) {
         S = shared_ptrs(sx);
         Carver cs{static_cast<char *>(ws) + need_fwd};

@@ -417,7 +417,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_gateup_kernel(
     const uint16_t *__restrict__ x, int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, int max_nt, float *__restrict__ h, const uint16_t *__restrict__ lg,
     int T, int32_t *__restrict__ idx_out, float *__restrict__ gate_out, GroupOut gout, SharedPtrs S,
-    uint16_t *__restrict__ hs) {
+    float *__restrict__ hs) {
     // lanes per gate/up row: H / 64 for int4 (64 codes a lane), H / 32 for
     // fp8 (32 codes a lane)
     constexpr int LPG = FMT == 2 ? 2 * LPR : LPR;
@@ -465,7 +465,7 @@ template <int LPR, int FMT, bool SHARED>
 __global__ __launch_bounds__(DEC_WAVES * 64) void decode_down_kernel(
     int H, int I, int k, int P, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
     int max_nt, const float *__restrict__ topk_gate, const float *__restrict__ h, float *__restrict__ y, int T,
-    SharedPtrs S, const uint16_t *__restrict__ hs, float *__restrict__ zrows) {
+    SharedPtrs S, const float *__restrict__ hs, float *__restrict__ zrows) {
     constexpr int BR = DEC_WAVES * (WAVE / LPR);
     int nt_all = *ntiles;
     nt_all = nt_all < 0 ? 0 : (nt_all > max_nt ? max_nt : nt_all);
@@ -764,7 +764,7 @@ template <int FMT, bool ROUTE, bool SHARED>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
-                                     const SharedPtrs &S, uint16_t *hs, float *zrows) {
+                                     const SharedPtrs &S, float *hs, float *zrows) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
     const int mt = (int)max_tiles(P, L.E, DECODE_TT);
@@ -786,7 +786,7 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
         constexpr auto kern = decode_down_kernel<LP, FMT, SHARED>;                                               \
         launch_k(kern, dim3(resident_grid<kern>()), block, s, nullptr, nullptr, H, I, k, P, L,                   \
                  (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const float *)h, y, (int)T, S,  \
-                 (const uint16_t *)hs, zrows);                                                                   \
+                 (const float *)hs, zrows);                                                                   \
     } break;
         CASE(2) CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE
@@ -807,7 +807,7 @@ template <bool ROUTE>
 static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
-                                     const SharedPtrs *S, uint16_t *hs, float *zrows) {
+                                     const SharedPtrs *S, float *hs, float *zrows) {
     if (S && (zrows || !decode_fuses_shared(L, S))) return hipErrorInvalidValue;
     const SharedPtrs none{};
 #define FMT_CASE(F)                                                                                            \
@@ -825,7 +825,7 @@ static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64
 
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1, const SharedPtrs *S, uint16_t *hs, float *zrows) {
+                                 hipEvent_t e1, const SharedPtrs *S, float *hs, float *zrows) {
     return launch_experts_any<false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr, S, hs, zrows);
 }
 
@@ -840,7 +840,7 @@ bool decode_routes_in_block(int64_t T, int k, int E) {
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const SharedPtrs *S,
-                                        uint16_t *hs, float *zrows) {
+                                        float *hs, float *zrows) {
     if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;
     return launch_experts_any<true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate, S, hs, zrows);
 }

@@ -167,10 +167,12 @@ __device__ __forceinline__ void h_fetch(const float *__restrict__ h, int row0, i
 // The fetched rows scaled and rounded to f16 into s_h (row u at
 // s_h + u * DEC_HMAX), in natural order, or with PERM8 in the int4 down
 // GEMV's operand order (0,4 | 1,5 | 2,6 | 3,7 in each 8-block, the odd
-// elements also divided by 16: odd codes enter in place as 1024 + 16 q);
-// inv[u] = the inverse of row u's scale.  Every thread of the workgroup
-// calls it (two barriers); s_h is complete on return.
-template <bool PERM8>
+// elements also divided by 16: odd codes enter in place as 1024 + 16 q),
+// or with PAIR02 in the int8 down GEMV's order (n0, n2, n1, n3 in each
+// 4-block: the pairs it forms from a code word); inv[u] = the inverse of
+// row u's scale.  Every thread of the workgroup calls it (two barriers);
+// s_h is complete on return.
+template <bool PERM8, bool PAIR02 = false>
 __device__ __forceinline__ void h_to_lds(const HFetch &f, int nt, int I, uint16_t *__restrict__ s_h,
                                          float inv[DECODE_TT]) {
     __shared__ uint32_t s_red[DECODE_TT][DEC_WAVES];
@@ -222,6 +224,8 @@ __device__ __forceinline__ void h_to_lds(const HFetch &f, int nt, int I, uint16_
             row[b + 2] = __builtin_bit_cast(uint16_t, (_Float16)(v.y * so));
             row[b + 4] = __builtin_bit_cast(uint16_t, (_Float16)(v.z * s));
             row[b + 6] = __builtin_bit_cast(uint16_t, (_Float16)(v.w * so));
+        } else if (PAIR02) {
+            *reinterpret_cast<uint2 *>(row + n) = make_uint2(pack_f16x2(v.x * s, v.z * s), pack_f16x2(v.y * s, v.w * s));
         } else {
             const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.x * s)) |
                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.y * s)) << 16);

@@ -126,7 +126,7 @@ hipError_t launch_group_after_count(const int32_t *idx, int64_t T, int k, int E,
 // (each row of h scaled by a power of two and rounded to f16) with the
 // gate-weighted add into y (y must be cleared first).  e0 / e1 time the
 // gate/up kernel.  With S the shared expert's items run in the same two
-// launches (hs: its f16 [T][I] SwiGLU output); S needs
+// launches (hs: its fp32 [T][I] SwiGLU output); S needs
 // decode_fuses_shared.  With zrows ([T*k][H] floats) the down kernel stores
 // each routed row there instead of adding into y, and a third launch sums
 // each token's rows into y in slot order (run-to-run identical y); zrows
@@ -134,7 +134,7 @@ hipError_t launch_group_after_count(const int32_t *idx, int64_t T, int k, int E,
 bool decode_fuses_shared(const LayerPtrs &L, const SharedPtrs *S);
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
-                                 hipEvent_t e1 = nullptr, const SharedPtrs *S = nullptr, uint16_t *hs = nullptr,
+                                 hipEvent_t e1 = nullptr, const SharedPtrs *S = nullptr, float *hs = nullptr,
                                  float *zrows = nullptr);
 hipError_t launch_decode_combine(const float *z, int64_t T, int k, int H, float *y, hipStream_t s);
 
@@ -158,7 +158,7 @@ bool decode_routes_in_block(int64_t T, int k, int E);
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
-                                        const SharedPtrs *S = nullptr, uint16_t *hs = nullptr,
+                                        const SharedPtrs *S = nullptr, float *hs = nullptr,
                                         float *zrows = nullptr);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
@@ -194,18 +194,19 @@ hipError_t launch_dequant(const LayerPtrs &L, int expert, int proj, float *out, 
 hipError_t launch_prefill_pack(const LayerPtrs &L, uint8_t *dst, hipStream_t s);
 
 // Shared expert (int8 symmetric group 128) for few tokens: gate/up + SwiGLU
-// -> h (f16 [T][I] workspace), then down -> y = (accumulate ? y : 0) + o.
+// -> h (fp32 [T][I] workspace), then down (each h row scaled by a power of
+// two and rounded to f16) -> y = (accumulate ? y : 0) + o.
 // e0 / e1 time the gate/up kernel, e2 / e3 the down kernel.
-hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *h, float *y, bool accumulate,
+hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, float *h, float *y, bool accumulate,
                          hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr, hipEvent_t e2 = nullptr,
                          hipEvent_t e3 = nullptr);
 hipError_t launch_dequant_int8(const SharedPtrs &S, int proj, float *out, hipStream_t s);
 // Shared expert for many tokens: dense f16 matrix-core GEMMs (x16, xexp: the
-// [T][H] f16 activations and per-token exponents, h: [T][I] f16, both
-// workspace).  Needs H % 256 == 0.
+// [T][H] f16 activations and per-token exponents, h: [T][I] f16 and hx: its
+// exponents [T][I / 128], all workspace).  Needs H % 256 == 0, I <= 2048.
 constexpr int SHARED_GEMM_MIN_T = 65;  // token count from which the GEMMs run
 hipError_t launch_shared_gemm(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *x16, int32_t *xexp,
-                              uint16_t *h, float *y, bool accumulate, hipStream_t s, hipEvent_t e0 = nullptr,
+                              uint16_t *h, int8_t *hx, float *y, bool accumulate, hipStream_t s, hipEvent_t e0 = nullptr,
                               hipEvent_t e1 = nullptr, hipEvent_t e2 = nullptr, hipEvent_t e3 = nullptr);
 hipError_t launch_residual(const uint16_t *x, const float *y, int64_t n, uint16_t *out, hipStream_t s);
 

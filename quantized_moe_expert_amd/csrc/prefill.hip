@@ -1100,9 +1100,14 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
 // exactly, and one packed multiply by the row's group scale rounds s q once
 // to f16 (as the int4 path rounds its weights).  A code dword gives the pairs
 // (q0, q2) and (q1, q3), so x16 and h are kept in PERM4 order (0,2,1,3 in each
-// group of 4).  x16 is x scaled per token by a power of two (x_to_f16);
-// GEMM1 multiplies back, GEMM2 writes y (or adds into it) from the
-// accumulators, each output owned by one lane.
+// group of 4).  x16 is x scaled per token by a power of two 2^-e
+// (x_to_f16).  h is scaled as in the routed GEMM1: each row by 2^-2e, then
+// the workgroup's 128 columns of its rows by the 2^s that puts their largest
+// magnitude in [2^14, 2^15) (s stored per row and 128-column block in hx);
+// GEMM2 runs on the same row tiles, folds 2^(s_min - s_b) into its scales of
+// input block b (a group of 128 is one h block) and writes y (or adds into
+// it) from the accumulators times 2^(2e - s_min), each output owned by one
+// lane.  So f16's range limits neither x nor h.
 
 constexpr int SG_NST = 2;
 constexpr int SG_B_BYTES = BROWS * KS;            // 16 KB: 256 rows x 64 int8 codes
@@ -1117,6 +1122,7 @@ struct SGemmCtx {
     const uint8_t *b_base[SG_B_LOADS];
     uint32_t b_off[SG_B_LOADS];
     const uint16_t *srow[2];  // this lane's two weight rows' group scales
+    const uint32_t *fb;       // GEMM2: LDS [16], 2^(s_min - s_b) per group (h block) b as an f16 pair
     uint8_t *ring[SG_NST];  // the ring slots, one LDS array each (see ring_depth)
     int brow[2];
     int nk;
@@ -1149,7 +1155,7 @@ __device__ __forceinline__ uint2 sg_codes(uint32_t w, uint32_t kf, half2_t sc) {
     return make_uint2(__builtin_bit_cast(uint32_t, a * sc), __builtin_bit_cast(uint32_t, b * sc));
 }
 
-template <int MS>
+template <int MS, bool FB>
 __device__ __forceinline__ void sg_main(const SGemmCtx &c, f32x16_t (&acc)[4][2], int wave, int lane) {
     const int l32 = lane & 31, hf = lane >> 5;
     const int NK = c.nk;
@@ -1157,6 +1163,7 @@ __device__ __forceinline__ void sg_main(const SGemmCtx &c, f32x16_t (&acc)[4][2]
     sg_issue<MS>(c, 0, 0, wave);
     half2_t sc[2];
     uint32_t snext[2] = {(uint32_t)c.srow[0][0], (uint32_t)c.srow[1][0]};
+    uint32_t fnext = 0x3c003c00u;  // GEMM2: the next group's factor (1.0 until read)
     for (int kk = 0; kk < NK; kk += SG_NST) {
 #pragma unroll
         for (int u = 0; u < SG_NST; ++u) {
@@ -1167,11 +1174,15 @@ __device__ __forceinline__ void sg_main(const SGemmCtx &c, f32x16_t (&acc)[4][2]
                 if (ks + 1 < NK) sg_issue<MS>(c, ks + 1, (u + 1) % SG_NST, wave);
                 if ((ks & 1) == 0) {  // a new group of 128 inputs
                     const int kg = ks >> 1;
+                    if (FB && kg == 0) fnext = c.fb[0];  // after the first barrier
+                    const half2_t f2 = __builtin_bit_cast(half2_t, fnext);
 #pragma unroll
                     for (int ns = 0; ns < 2; ++ns) {
                         sc[ns] = __builtin_bit_cast(half2_t, snext[ns] * 0x10001u);
+                        if (FB) sc[ns] = sc[ns] * f2;
                         if (2 * (kg + 1) < NK) snext[ns] = (uint32_t)c.srow[ns][kg + 1];
                     }
+                    if (FB && 2 * (kg + 1) < NK) fnext = c.fb[kg + 1];
                 }
                 const uint8_t *sa = c.ring[u];
                 const uint8_t *sbp = sa + A_BYTES;
@@ -1210,13 +1221,16 @@ __device__ __forceinline__ void sg_main(const SGemmCtx &c, f32x16_t (&acc)[4][2]
     }
 }
 
-// STAGE 1: A = x16 rows (PERM4), B = gate | up codes, epilogue * 2^e, SwiGLU
-//          -> h (f16, PERM4).
-// STAGE 2: A = h rows, B = down codes, epilogue y = (accumulate ? y : 0) + acc.
+// STAGE 1: A = x16 rows (PERM4), B = gate | up codes, epilogue SwiGLU of the
+//          accumulators times 2^e, scaled as above -> h (f16, PERM4), hx.
+// STAGE 2: A = h rows, B = down codes (scales times 2^(s_min - s_b)),
+//          epilogue y = (accumulate ? y : 0) + acc 2^(2e - s_min).
+// Both launches take the same tile_rows, so a GEMM2 tile's rows share their
+// h exponents.
 template <int STAGE>
 __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_gemm_kernel(
     const uint16_t *__restrict__ act, const int32_t *__restrict__ xexp, int T, int H, int I, SharedPtrs S,
-    uint16_t *__restrict__ h_out, float *__restrict__ y, int accumulate, int tile_rows) {
+    uint16_t *__restrict__ h_out, int8_t *__restrict__ hx, float *__restrict__ y, int accumulate, int tile_rows) {
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
     const int ntiles = (T + tile_rows - 1) / tile_rows;
     const int nwork = ntiles * ncb;
@@ -1235,7 +1249,30 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     __shared__ __attribute__((aligned(16))) uint8_t s_ring0[SG_STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring1[SG_STAGE];
+    __shared__ uint32_t s_red[PF_BLOCK / 64];
+    __shared__ uint32_t s_fb[16];  // STAGE 2: 2^(s_min - s_b) per h block b (I <= 2048), f16 pair
+    __shared__ __attribute__((aligned(16))) int32_t s_xe[BM];  // the tile rows' exponents e
+    const int nbh = I / 128;
+    // STAGE 2: the tile's h exponents (one per 128-column block, the same
+    // for all its rows) and their smallest
+    int smin = 64;
+    if (STAGE == 2) {
+        int sb[16];  // all loads issued before the first use
+#pragma unroll
+        for (int b = 0; b < 16; ++b) sb[b] = b < nbh ? (int)hx[(size_t)row0 * nbh + b] : 64;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) smin = sb[b] < smin ? sb[b] : smin;
+        if (tid < 16) {
+            int mine = 64;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) mine = tid == b ? sb[b] : mine;
+            const _Float16 f = (_Float16)exp2i(smin - mine);
+            s_fb[tid] = __builtin_bit_cast(uint16_t, f) * 0x10001u;
+        }
+    }
+    if (tid < rows) s_xe[tid] = xexp[row0 + tid];  // read after the main loop's barriers
     SGemmCtx c;
+    c.fb = s_fb;
     c.ring[0] = s_ring0;
     c.ring[1] = s_ring1;
     c.nk = K / KS;
@@ -1278,14 +1315,36 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int r = 0; r < 16; ++r) acc[mi][ns][r] = 0.f;
     const int msub = (rows + 31) / 32;
     switch (msub) {
-        case 1: sg_main<1>(c, acc, wave, lane); break;
-        case 2: sg_main<2>(c, acc, wave, lane); break;
-        case 3: sg_main<3>(c, acc, wave, lane); break;
-        default: sg_main<4>(c, acc, wave, lane); break;
+        case 1: sg_main<1, STAGE == 2>(c, acc, wave, lane); break;
+        case 2: sg_main<2, STAGE == 2>(c, acc, wave, lane); break;
+        case 3: sg_main<3, STAGE == 2>(c, acc, wave, lane); break;
+        default: sg_main<4, STAGE == 2>(c, acc, wave, lane); break;
     }
     __syncthreads();  // ring no longer read
 
     if (STAGE == 1) {
+        // h 2^-2e = silu(acc 2^e) (acc_u 2^-e) per row, then one power of two
+        // for the workgroup's block
+        float mloc = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi >= msub) break;
+            const int4 *xe4 = reinterpret_cast<const int4 *>(s_xe + 32 * mi + 4 * hf);  // rows r % 4 of group r / 4
+            const int4 ev[4] = {xe4[0], xe4[2], xe4[4], xe4[6]};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
+                float hn = 0.f;
+                if (row < rows) {
+                    const int4 q = ev[r / 4];
+                    const int e = r % 4 == 0 ? q.x : (r % 4 == 1 ? q.y : (r % 4 == 2 ? q.z : q.w));
+                    hn = silu(acc[mi][0][r] * exp2i(e)) * (acc[mi][1][r] * exp2i(-e));
+                }
+                acc[mi][0][r] = hn;
+                mloc = fmaxf(mloc, fabsf(hn));
+            }
+        }
+        const RowScale rs = row_scale(block_max_nonneg(mloc, s_red));
         // one 32-row subtile at a time through the two ring slots in turn
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -1293,10 +1352,8 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
             uint16_t *s_h = reinterpret_cast<uint16_t *>(mi % 2 == 0 ? s_ring0 : s_ring1);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int lr = 8 * (r / 4) + 4 * hf + (r % 4), row = 32 * mi + lr;
-                const float sc = row < rows ? ldexpf(1.0f, xexp[row0 + row]) : 0.f;
-                const _Float16 hv = (_Float16)(silu(acc[mi][0][r] * sc) * (acc[mi][1][r] * sc));
-                s_h[lr * SG_HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, hv);
+                const int lr = 8 * (r / 4) + 4 * hf + (r % 4);
+                s_h[lr * SG_HP + wave * 32 + l32] = __builtin_bit_cast(uint16_t, (_Float16)(acc[mi][0][r] * rs.sc));
             }
             __syncthreads();
             for (int i = tid; i < 32 * 16; i += PF_BLOCK) {
@@ -1306,6 +1363,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
                     const uint4 o = make_uint4((v.x & 0xffffu) | (v.y << 16), (v.x >> 16) | (v.y & 0xffff0000u),
                                                (v.z & 0xffffu) | (v.w << 16), (v.z >> 16) | (v.w & 0xffff0000u));
                     *reinterpret_cast<uint4 *>(h_out + (size_t)(row0 + row) * I + cb * 128 + cc * 8) = o;
+                    if (cc == 0) hx[(size_t)(row0 + row) * nbh + cb] = (int8_t)rs.s;
                 }
             }
         }
@@ -1313,14 +1371,19 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             if (mi < msub) {
+                const int4 *xe4 = reinterpret_cast<const int4 *>(s_xe + 32 * mi + 4 * hf);
+                const int4 ev[4] = {xe4[0], xe4[2], xe4[4], xe4[6]};
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
                     if (row < rows) {
+                        const int4 q = ev[r / 4];
+                        const int e = r % 4 == 0 ? q.x : (r % 4 == 1 ? q.y : (r % 4 == 2 ? q.z : q.w));
+                        const float f = exp2i(2 * e - smin);
 #pragma unroll
                         for (int ns = 0; ns < 2; ++ns) {
                             float *dst = y + (size_t)(row0 + row) * H + col_base + wave * 64 + ns * 32 + l32;
-                            *dst = accumulate ? *dst + acc[mi][ns][r] : acc[mi][ns][r];
+                            *dst = accumulate ? *dst + acc[mi][ns][r] * f : acc[mi][ns][r] * f;
                         }
                     }
                 }
@@ -1340,17 +1403,22 @@ static int sg_tile_rows(int64_t T, int ncb) {
 }
 
 hipError_t launch_shared_gemm(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *x16, int32_t *xexp,
-                              uint16_t *h, float *y, bool accumulate, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
-                              hipEvent_t e2, hipEvent_t e3) {
+                              uint16_t *h, int8_t *hx, float *y, bool accumulate, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1, hipEvent_t e2, hipEvent_t e3) {
     const int H = S.H, I = S.I;
+    if (I > 2048) return hipErrorInvalidValue;  // s_fb holds 16 blocks
     hipLaunchKernelGGL(x_to_f16_kernel<2>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H, x16, xexp);
-    const int tr1 = sg_tile_rows(T, I / 128), tr2 = sg_tile_rows(T, H / BROWS);
+    // one tiling for both launches, so that a GEMM2 tile's rows share their
+    // h exponents: the larger tile of the two choices (measured faster than
+    // the smaller one for both GEMMs at 4096 tokens, H = 2048, I = 512)
+    const int tr_a = sg_tile_rows(T, I / 128), tr_b = sg_tile_rows(T, H / BROWS);
+    const int tr1 = tr_a < tr_b ? tr_b : tr_a, tr2 = tr1;
     const unsigned nb1 = (unsigned)(((I / 128) * ((T + tr1 - 1) / tr1) + 7) / 8 * 8);
     const unsigned nb2 = (unsigned)(((H / BROWS) * ((T + tr2 - 1) / tr2) + 7) / 8 * 8);
     launch_k(shared_gemm_kernel<1>, dim3(nb1), dim3(PF_BLOCK), s, e0, e1, (const uint16_t *)x16,
-             (const int32_t *)xexp, (int)T, H, I, S, h, y, accumulate ? 1 : 0, tr1);
+             (const int32_t *)xexp, (int)T, H, I, S, h, hx, y, accumulate ? 1 : 0, tr1);
     launch_k(shared_gemm_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, e2, e3, (const uint16_t *)h, (const int32_t *)xexp,
-             (int)T, H, I, S, h, y, accumulate ? 1 : 0, tr2);
+             (int)T, H, I, S, h, hx, y, accumulate ? 1 : 0, tr2);
     return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@ namespace moeq4 {
 
 template <int LPR>
 __global__ __launch_bounds__(DEC_WAVES * 64) void shared_gateup_kernel(const uint16_t *__restrict__ x, int T,
-                                                                       SharedPtrs S, uint16_t *__restrict__ h) {
+                                                                       SharedPtrs S, float *__restrict__ h) {
     constexpr int BR = DEC_WAVES * (WAVE / LPR);
     const int ntt = (T + DECODE_TT - 1) / DECODE_TT;
     const Items it = decode_items(ntt, S.I, S.I / BR);
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void shared_gateup_kernel(const uin
 
 template <int LPR>
 __global__ __launch_bounds__(DEC_WAVES * 64) void shared_down_kernel(int T, SharedPtrs S,
-                                                                     const uint16_t *__restrict__ h,
+                                                                     const float *__restrict__ h,
                                                                      float *__restrict__ y, int accumulate) {
     constexpr int BR = DEC_WAVES * (WAVE / LPR);
     const int ntt = (T + DECODE_TT - 1) / DECODE_TT;
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void shared_down_kernel(int T, Shar
     }
 }
 
-hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint16_t *h, float *y, bool accumulate,
+hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, float *h, float *y, bool accumulate,
                          hipStream_t s, hipEvent_t e0, hipEvent_t e1, hipEvent_t e2, hipEvent_t e3) {
     const dim3 block(DEC_WAVES * 64);
     switch (S.H / 32) {
@@ -57,7 +57,7 @@ hipError_t launch_shared(const uint16_t *x, int64_t T, const SharedPtrs &S, uint
     case LP: {                                                                                                \
         constexpr auto kern = shared_down_kernel<LP>;                                                         \
         launch_k(kern, dim3(resident_grid<kern>()), block, s, e2, e3, (int)T, S,                              \
-                 (const uint16_t *)h, y, accumulate ? 1 : 0);                                                 \
+                 (const float *)h, y, accumulate ? 1 : 0);                                                    \
     } break;
         CASE(4) CASE(8) CASE(16) CASE(32) CASE(64)
 #undef CASE

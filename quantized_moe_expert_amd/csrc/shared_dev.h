@@ -36,10 +36,6 @@ struct SharedPtrs {
 constexpr int SX_GROUP = 128;
 constexpr uint32_t SX_FLIP = 0x80808080u;  // signed byte q -> u = q + 128
 
-// h slot of element n: each 4-block holds (n0, n2), (n1, n3), the pairs the
-// down GEMV forms from a code word.
-__device__ __forceinline__ int sx_h_slot(int n) { return (n & ~3) | ((n & 1) << 1) | ((n >> 1) & 1); }
-
 // f16 pair (1024 + u_a, 1024 + u_b) -> (q_a, q_b), exact.
 __device__ __forceinline__ uint32_t sx_codes_f16(uint32_t pair) {
     const half2v_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
@@ -47,14 +43,14 @@ __device__ __forceinline__ uint32_t sx_codes_f16(uint32_t pair) {
 }
 
 // gate/up GEMV + SwiGLU of tokens tok0 .. tok0 + nt - 1 over rows ir of I,
-// h (f16, [T][I] in sx_h_slot order) out.  LPR = H / 32 lanes per row, each
+// h (fp32, [T][I]) out.  LPR = H / 32 lanes per row, each
 // lane 32 codes (two 16-byte loads); a wave-load covers RPW = 64 / LPR rows
 // of gate and of up.  Pipelined in two register stages as the routed
 // gate/up GEMV.
 template <int LPR>
 __device__ __forceinline__ void shared_gateup_item(const uint16_t *__restrict__ x, const SharedPtrs &S, int tok0,
                                                    int nt, const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
-                                                   uint16_t *__restrict__ h, float (*s_out)[DEC_RB_MAX]) {
+                                                   float *__restrict__ h, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     const int H = S.H, I = S.I;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -155,21 +151,23 @@ __device__ __forceinline__ void shared_gateup_item(const uint16_t *__restrict__ 
     for (int i = tid; i < nt * ir.nloc; i += blockDim.x) {
         const int u = i / ir.nloc, nl = i % ir.nloc;
         if (!ir.valid(nl)) continue;
-        const int n = ir.grow(nl);
-        h[(size_t)(tok0 + u) * I + sx_h_slot(n)] = __builtin_bit_cast(uint16_t, (_Float16)s_out[u][nl]);
+        h[(size_t)(tok0 + u) * I + ir.grow(nl)] = s_out[u][nl];
     }
     __syncthreads();
 }
 
 // down GEMV of tokens tok0 .. tok0 + nt - 1 over output rows ir of H, full
-// rows of h (LPR = I / 32 lanes per row, 32 codes each), added into y:
+// rows of h (LPR = I / 32 lanes per row, 32 codes each; each token's fp32 h
+// row staged once per item in LDS, scaled by the power of two that puts its
+// largest magnitude in [2^14, 2^15) and rounded to f16, the outputs scaled
+// back; h_to_lds), added into y:
 // ATOMIC with float atomics (y shared with the routed experts' adds),
 // otherwise y = (accumulate ? y : 0) + o by the one thread that owns the
 // output.
 template <int LPR, bool ATOMIC>
 __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, int nt,
                                                  const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
-                                                 const uint16_t *__restrict__ h, float *__restrict__ y,
+                                                 const float *__restrict__ h, float *__restrict__ y,
                                                  bool accumulate, float (*s_out)[DEC_RB_MAX]) {
     constexpr int RPW = WAVE / LPR;
     const int H = S.H, I = S.I;
@@ -195,12 +193,20 @@ __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, 
             st.s[b] = S.ds[row * smr + gi];
         }
     };
+    // the tokens' h rows: fetched before the first weight stages, staged in
+    // LDS after them; then the lane's 32 values of each (f16 pairs (n0, n2),
+    // (n1, n3) of each 4-block)
+    HFetch hfe;
+    __shared__ __attribute__((aligned(16))) uint16_t s_hs[DECODE_TT * DEC_HMAX];
     uint32_t hp[DECODE_TT][16];
-    auto fetch_h = [&]() {
+    float hinv[DECODE_TT];
+    auto fetch_h = [&]() { h_fetch(h, tok0, nt, I, hfe); };
+    auto conv_h = [&]() {
+        h_to_lds<false, true>(hfe, nt, I, s_hs, hinv);
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
             if (u < nt) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(h + (size_t)(tok0 + u) * I + 32 * c);
+                const uint4 *src = reinterpret_cast<const uint4 *>(s_hs + u * DEC_HMAX + 32 * c);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const uint4 v = src[q];
@@ -234,7 +240,7 @@ __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, 
 #pragma unroll
             for (int u = 0; u < DECODE_TT; ++u) {
                 if (u < nt) {
-                    const float o = seg_sum_dpp<LPR>(sd * a[u]);
+                    const float o = seg_sum_dpp<LPR>(sd * a[u]) * hinv[u];
                     if (c == LPR - 1 && ir.valid_step(s0 + b, lrow)) s_out[u][dl] = o;
                 }
             }
@@ -245,11 +251,13 @@ __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, 
     if (nst == 1) {
         fetch_h();
         issue(sa, 0);
+        conv_h();
         consume(sa, 0);
     } else {
         fetch_h();
         issue(sa, 0);
         issue(sb, DEC_NB);
+        conv_h();
         for (int q = 0; q < nst; q += 2) {
             consume(sa, q * DEC_NB);
             issue(sa, (q + 2) * DEC_NB);

@@ -9,7 +9,8 @@ x 2^-4, x 2^4 and x 2^7 (|h| up to about 2^16), int4 group scales
 log-uniform over [2^-16, 2^-4] and over [2^-16, 2^-10] (every group below
 2^-10), block-FP8 scales and NVFP4 globals log-uniform over a wide range.
 Every weight format, decode and prefill (with and without the prefill copy
-of the weights).  Bar: rel L2 <= 2e-3; max abs <= 1e-2 times the output's
+of the weights).  The shared expert likewise, on both of its paths (see
+test_shared_expert_magnitudes).  Bar: rel L2 <= 2e-3; max abs <= 1e-2 times the output's
 largest magnitude when that exceeds 1.
 """
 from __future__ import annotations
@@ -83,3 +84,61 @@ def test_magnitudes(case, fmt, mode, T):
     assert np.all(np.isfinite(yr))
     r, a = assert_close(y.cpu().numpy(), yr, f"{name} fmt={fmt} {mode}", abs_scaled=True)
     say(f"[magnitudes] {name} fmt={fmt} {mode}: rel L2 {r:.2e} max abs {a:.2e} (|y| max {np.max(np.abs(yr)):.2e})")
+
+
+# ------------------------------------------------------------ shared expert
+
+def _host(sx):
+    return [t.cpu().numpy() for t in sx.tensors()]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["alone", "in_layer"])
+@pytest.mark.parametrize("T", [1, 16, 100])
+@pytest.mark.parametrize("xs", [-10, -4, 4, 9, "mix"], ids=lambda v: f"x2^{v}")
+def test_shared_expert_magnitudes(xs, T, fused):
+    """The shared expert at activation scales 2^9 (|h| far above f16's 65504) and 2^-10 (h near f16's
+    subnormals).  Up to 64 tokens (GEMV path, its own launches or its items inside the layer's decode
+    launches) h is kept in fp32 and each token's row is scaled by a power of two before the f16 down
+    product; from 65 tokens (matrix-core GEMMs, after the routed GEMMs of a prefill layer) h is stored in
+    f16 scaled per row by 2^-2e and per 128-column block by a power of two, both taken off in the down
+    GEMM.  "mix" gives each token its own scale, 2^-10 to 2^9, so the rows of one GEMM tile differ by up
+    to 2^38 in |h|.  Every case must meet the bar."""
+    import quantized_moe_expert_amd as m
+    Hs, Is = 512, 256
+    say(f"[magnitudes shared] x2^{xs} T={T} fused={fused}")
+    sx = synth.random_shared(Hs, Is, seed=43, device="cuda", tag="mag_shared")
+    if xs == "mix":
+        row = torch.tensor([2.0 ** (-10 + (7 * t) % 20) for t in range(T)], device="cuda")[:, None]
+        x = synth.bf16_bits(synth.normal((T, Hs), 1.0, 43, f"mag/sx/{T}", "cuda") * row)
+    else:
+        x = synth.bf16_bits(synth.normal((T, Hs), 2.0 ** xs, 43, f"mag/sx/{T}", "cuda"))
+    x_np = np_u16(x)
+    if not fused:
+        ws = torch.empty(max(m.workspace_size(m.WS_SHARED, T, 1, 1, Hs, Is), 256), dtype=torch.uint8,
+                         device="cuda")
+        y = torch.full((T, Hs), float("nan"), dtype=torch.float32, device="cuda")
+        m.moe_q4_shared(x, T, sx, y, 0, ws)
+        torch.cuda.synchronize()
+        yr = oracle.shared(Hs, Is, *_host(sx), x_np, T)
+    else:
+        # the layer's routed experts with the same inner size, so the shared items run in its launches
+        lay = synth.random_layer(E, Hs, Is, synth.FMT_ASYM_G64, seed=43, device="cuda", tag="mag_shared_l")
+        logits = synth.bf16_bits(synth.normal((T, E), 1.0, 43, f"mag/sl/{T}", "cuda"))
+        nb = m.workspace_size(m.WS_FORWARD, T, E, K, Hs, Is) + m.workspace_size(m.WS_SHARED, T, 1, 1, Hs, Is)
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+        m.moe_q4_workspace_init(ws)
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        gate = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        y = torch.full((T, Hs), float("nan"), dtype=torch.float32, device="cuda")
+        m.moe_q4_forward_ex(x, None, None, None, None, logits.clone(), T, K, lay, sx, idx, gate, y, ws)
+        torch.cuda.synchronize()
+        _, ir, gr, yl = oracle.moe_layer(lay, x_np, T, K, logits=np_u16(logits))
+        assert np.array_equal(idx.cpu().numpy(), ir)
+        yr = oracle.shared(Hs, Is, *_host(sx), x_np, T, y_in=yl)
+    assert np.all(np.isfinite(yr))
+    yg = y.cpu().numpy()
+    r, a = assert_close(yg, yr, f"shared x2^{xs} T={T} fused={fused}", abs_scaled=True)
+    if xs == "mix":  # the small tokens are invisible in the whole output's norms: each row on its own
+        for t in range(T):
+            assert_close(yg[t], yr[t], f"shared mix T={T} fused={fused} token {t}", abs_scaled=True)
+    say(f"[magnitudes shared] x2^{xs}: rel L2 {r:.2e} max abs {a:.2e} (|y| max {np.max(np.abs(yr)):.2e})")
