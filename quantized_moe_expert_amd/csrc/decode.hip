@@ -143,10 +143,15 @@ constexpr int DEC_GU_STAGES = 2;  // register stages of the gate/up GEMV
 
 // gate/up GEMV + SwiGLU for one item (tile: one expert, up to DECODE_TT
 // tokens; rows ir of I) into h.  Lanes run along the input dimension: LPR =
-// H / 64 lanes per row, each lane 32 bytes = 64 codes (one 64-group), so a
-// wave-load covers RPW = 64 / LPR rows of gate and of up (2 rows of 1 KB
-// each when H = 2048).  The next wave-load is in flight while the current
-// one is reduced.  h is written in fp32, natural order.
+// H / 64 lanes per row, each lane 32 bytes = 64 codes, so a wave-load covers
+// RPW = 64 / LPR rows of gate and of up (2 rows of 1 KB each when H = 2048).
+// Lane c takes bytes [16c, 16c + 16) of the row's first half and of its
+// second half, so each 16-byte load instruction reads whole cache lines
+// (32 B per lane in one piece left every line half read by each of two
+// instructions: frame 2.29 against 2.31 ms, decode step 17.75 against
+// 18.1 us); each half lies in one scale group.  The next wave-load is in
+// flight while the current one is reduced.  h is written in fp32, natural
+// order.
 // SHORT: items of a single wave-load are common (few tokens), and take a
 // straight path instead of issuing unused stages.
 template <int LPR, int FMT, bool SHORT>
@@ -159,11 +164,12 @@ __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int 
     const int c = lane % LPR, sub = lane / LPR;
     const size_t row_bytes = (size_t)H / 2;
     const size_t smr = (size_t)(H / G) * (FMT == 0 ? 2 : 1);
-    const int gi = (64 * c) / G;
+    // lane c: codes [32c, 32c + 32) and [H/2 + 32c, H/2 + 32c + 32)
+    const int gi0 = (32 * c) / G, gi1 = (H / 2 + 32 * c) / G;
     const uint32_t kb = opaque_magic(MAGIC_BF16);
     struct Stage {
         uint4 g[2], u[2];
-        uint32_t gs, us;
+        uint32_t gs[2], us[2];
     };
     const int e = tile.expert, nt = tile.rows;
     const int steps = ir.steps;         // wave-loads per wave
@@ -171,48 +177,57 @@ __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int 
     auto row_of = [&](int s) { return s * (DEC_WAVES * RPW) + lrow; };
     auto issue = [&](Stage &st, int s) {
         const size_t row = (size_t)e * I + (ir.valid_step(s, lrow) ? ir.grow_step(s, lrow) : ir.grow(0));
-        const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 32 * c);
-        const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 32 * c);
+        const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * row_bytes + 16 * c);
+        const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * row_bytes + 16 * c);
         st.g[0] = gp[0];
-        st.g[1] = gp[1];
+        st.g[1] = gp[LPR];
         st.u[0] = up[0];
-        st.u[1] = up[1];
-        st.gs = load_group_word<FMT>(L.gsm + row * smr, gi);
-        st.us = load_group_word<FMT>(L.usm + row * smr, gi);
+        st.u[1] = up[LPR];
+        st.gs[0] = load_group_word<FMT>(L.gsm + row * smr, gi0);
+        st.gs[1] = load_group_word<FMT>(L.gsm + row * smr, gi1);
+        st.us[0] = load_group_word<FMT>(L.usm + row * smr, gi0);
+        st.us[1] = load_group_word<FMT>(L.usm + row * smr, gi1);
     };
     // Activations: fetched before the first weight stages (they depend on
     // the tile only), reordered after them, so that waiting for them leaves
     // the stages in flight.
     uint32_t xp[DECODE_TT][32];
-    float xs[DECODE_TT];
+    float xs[DECODE_TT][2];
     auto fetch_x = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
             if (u < nt) {
                 const uint16_t *xrow = x + (size_t)(tile.pair[u] / k) * H;
-                fetch_x_chunk(xrow, 2 * c, xp[u]);
-                fetch_x_chunk(xrow, 2 * c + 1, xp[u] + 16);
+                fetch_x_chunk(xrow, c, xp[u]);
+                fetch_x_chunk(xrow, LPR + c, xp[u] + 16);
             }
         }
     };
     auto prep_x = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
-            xs[u] = 0.f;
-            if (u < nt) xs[u] = perm_x_chunk(xp[u]) + perm_x_chunk(xp[u] + 16);
+            xs[u][0] = xs[u][1] = 0.f;
+            if (u < nt) {
+                xs[u][0] = perm_x_chunk(xp[u]);
+                xs[u][1] = perm_x_chunk(xp[u] + 16);
+            }
         }
     };
     Stage st[DEC_GU_STAGES];
     auto consume = [&](const Stage &st, int s) {
         const int nl = row_of(s);
-        float sg, mg, su, mu;
-        group_params<FMT>(st.gs, sg, mg);
-        group_params<FMT>(st.us, su, mu);
-        const float cg = mg - OFFSET_BF16 * sg, cu = mu - OFFSET_BF16 * su;
-        // one code quad unpacked at a time, applied to every token of the tile
-        float dg[DECODE_TT], du[DECODE_TT];
+        float sg[2], mg[2], su[2], mu[2], cg[2], cu[2];
 #pragma unroll
-        for (int u = 0; u < DECODE_TT; ++u) dg[u] = du[u] = 0.f;
+        for (int hh = 0; hh < 2; ++hh) {
+            group_params<FMT>(st.gs[hh], sg[hh], mg[hh]);
+            group_params<FMT>(st.us[hh], su[hh], mu[hh]);
+            cg[hh] = mg[hh] - OFFSET_BF16 * sg[hh];
+            cu[hh] = mu[hh] - OFFSET_BF16 * su[hh];
+        }
+        // one code quad unpacked at a time, applied to every token of the tile
+        float dg[DECODE_TT][2], du[DECODE_TT][2];
+#pragma unroll
+        for (int u = 0; u < DECODE_TT; ++u) dg[u][0] = dg[u][1] = du[u][0] = du[u][1] = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             uint32_t wq[16];
@@ -220,16 +235,18 @@ __device__ __forceinline__ void gateup_item(const uint16_t *__restrict__ x, int 
 #pragma unroll
             for (int u = 0; u < DECODE_TT; ++u) {
                 if (u < nt) {
-                    if (q < 2) dg[u] = dot16(wq, xp[u] + 16 * (q & 1), dg[u]);
-                    else du[u] = dot16(wq, xp[u] + 16 * (q & 1), du[u]);
+                    if (q < 2) dg[u][q & 1] = dot16(wq, xp[u] + 16 * (q & 1), 0.f);
+                    else du[u][q & 1] = dot16(wq, xp[u] + 16 * (q & 1), 0.f);
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
             if (u < nt) {
-                const float pg = seg_sum_dpp<LPR>(fmaf(sg, dg[u], cg * xs[u]));
-                const float pu = seg_sum_dpp<LPR>(fmaf(su, du[u], cu * xs[u]));
+                const float pg = seg_sum_dpp<LPR>(fmaf(sg[0], dg[u][0], cg[0] * xs[u][0]) +
+                                                  fmaf(sg[1], dg[u][1], cg[1] * xs[u][1]));
+                const float pu = seg_sum_dpp<LPR>(fmaf(su[0], du[u][0], cu[0] * xs[u][0]) +
+                                                  fmaf(su[1], du[u][1], cu[1] * xs[u][1]));
                 if (c == LPR - 1 && ir.valid_step(s, lrow)) s_out[u][nl] = silu(pg) * pu;
             }
         }
