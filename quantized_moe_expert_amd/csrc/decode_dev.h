@@ -21,6 +21,23 @@ __device__ __forceinline__ void fetch_x_chunk(const uint16_t *__restrict__ xrow,
         xp[4 * j + 3] = v.w;
     }
 }
+// Activations [16c, 16c + 16) and [n2 + 16c, n2 + 16c + 16) of a bf16 row
+// (the two 16-code halves a lane takes when its loads are split across the
+// row's halves, n2 = half the row), natural order, 4 pairs each.
+__device__ __forceinline__ void fetch_x_halves(const uint16_t *__restrict__ xrow, int c, int n2, uint32_t xp[16]) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(xrow + hh * n2 + 16 * c);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 v = src[j];
+            xp[8 * hh + 4 * j + 0] = v.x;
+            xp[8 * hh + 4 * j + 1] = v.y;
+            xp[8 * hh + 4 * j + 2] = v.z;
+            xp[8 * hh + 4 * j + 3] = v.w;
+        }
+    }
+}
 // The fetched chunk put in PERM8 order in place; returns its sum.
 __device__ __forceinline__ float perm_x_chunk(uint32_t xp[16]) {
     float xs = 0.f;
@@ -238,6 +255,23 @@ __device__ __forceinline__ void h_to_lds(const HFetch &f, int nt, int I, uint16_
 #pragma unroll 1
     for (int i = tid + DEC_WAVES * WAVE; i < tot; i += DEC_WAVES * WAVE) store(i, f.src[i]);
     __syncthreads();
+}
+// The lane's 32 staged values [16 c, 16 c + 16) and [n2 + 16 c, n2 + 16 c +
+// 16) of a row (n2 = half the row) as 16 f16 pairs.
+__device__ __forceinline__ void h_from_lds_halves(const uint16_t *__restrict__ s_row, int c, int n2,
+                                                  uint32_t hp[16]) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(s_row + hh * n2 + 16 * c);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint4 v = src[q];
+            hp[8 * hh + 4 * q + 0] = v.x;
+            hp[8 * hh + 4 * q + 1] = v.y;
+            hp[8 * hh + 4 * q + 2] = v.z;
+            hp[8 * hh + 4 * q + 3] = v.w;
+        }
+    }
 }
 // The lane's 32 staged values [32 c, 32 c + 32) of row u as 16 f16 pairs.
 __device__ __forceinline__ void h_from_lds(const uint16_t *__restrict__ s_row, int c, uint32_t hp[16]) {

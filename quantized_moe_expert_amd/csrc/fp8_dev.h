@@ -3,9 +3,11 @@
 // released experts' format: drama-3-w4a16 card, "At a glance" table, each
 // matrix dequantised with its block scales, "How it was made").
 //
-// A lane takes 32 consecutive codes of a row (two 16-byte loads), which lie
-// in one 128-input block, so the block scale multiplies the lane's partial
-// sum before the lanes of a row are added.  Codes are converted two at a time
+// A lane takes 32 codes of a row as two 16-byte loads, [16c, 16c + 16) of
+// the row's first half and of its second half (so each load instruction
+// reads whole cache lines); each half lies in one 128-input block, whose
+// scale multiplies the half's partial sum before the lanes of a row are
+// added.  Codes are converted two at a time
 // by the gfx950 conversion instructions, exactly (every E4M3 value, the
 // subnormals included, is a bf16 and an f16 value):
 //   gate/up: codes -> bf16 pairs in natural order, packed dot against the bf16
@@ -50,7 +52,7 @@ __device__ __forceinline__ void fp8_gateup_item(const uint16_t *__restrict__ x, 
     const int c = lane % LPR, sub = lane / LPR;
     struct Stage {
         uint4 g[2], u[2];
-        float gs, us;
+        float gs[2], us[2];
     };
     const int e = tile.expert, nt = tile.rows;
     const int steps = ir.steps;
@@ -58,26 +60,29 @@ __device__ __forceinline__ void fp8_gateup_item(const uint16_t *__restrict__ x, 
     auto issue = [&](Stage &st, int s) {
         const int n = ir.valid_step(s, lrow) ? ir.grow_step(s, lrow) : ir.grow(0);
         const size_t row = (size_t)e * I + n;
-        const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * H + 32 * c);
-        const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * H + 32 * c);
+        const uint4 *gp = reinterpret_cast<const uint4 *>(L.gq + row * H + 16 * c);
+        const uint4 *up = reinterpret_cast<const uint4 *>(L.uq + row * H + 16 * c);
         st.g[0] = gp[0];
-        st.g[1] = gp[1];
+        st.g[1] = gp[LPR];
         st.u[0] = up[0];
-        st.u[1] = up[1];
-        st.gs = fp8_block_scale(L.gsm, e, I, H, n, 32 * c);
-        st.us = fp8_block_scale(L.usm, e, I, H, n, 32 * c);
+        st.u[1] = up[LPR];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            st.gs[hh] = fp8_block_scale(L.gsm, e, I, H, n, hh * (H / 2) + 16 * c);
+            st.us[hh] = fp8_block_scale(L.usm, e, I, H, n, hh * (H / 2) + 16 * c);
+        }
     };
     uint32_t xp[DECODE_TT][16];  // the lane's 32 activations of each token, bf16 pairs
     auto fetch_x = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u)
-            if (u < nt) fetch_x_chunk(x + (size_t)(tile.pair[u] / k) * H, c, xp[u]);
+            if (u < nt) fetch_x_halves(x + (size_t)(tile.pair[u] / k) * H, c, H / 2, xp[u]);
     };
     auto consume = [&](const Stage &st, int s) {
         const int nl = s * (DEC_WAVES * RPW) + lrow;
-        float dg[DECODE_TT], du[DECODE_TT];
+        float dg[DECODE_TT][2], du[DECODE_TT][2];
 #pragma unroll
-        for (int u = 0; u < DECODE_TT; ++u) dg[u] = du[u] = 0.f;
+        for (int u = 0; u < DECODE_TT; ++u) dg[u][0] = dg[u][1] = du[u][0] = du[u][1] = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint4 v = q == 0 ? st.g[0] : q == 1 ? st.g[1] : q == 2 ? st.u[0] : st.u[1];
@@ -85,12 +90,12 @@ __device__ __forceinline__ void fp8_gateup_item(const uint16_t *__restrict__ x, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t lo = e4m3_pair_bf16<false>(d4[j]), hi = e4m3_pair_bf16<true>(d4[j]);
-                const int xi = 8 * (q & 1) + 2 * j;  // x words of codes 4j .. 4j + 3
+                const int xi = 8 * (q & 1) + 2 * j;  // x words of codes 4j .. 4j + 3 of half q & 1
 #pragma unroll
                 for (int u = 0; u < DECODE_TT; ++u) {
                     if (u < nt) {
-                        if (q < 2) dg[u] = dot2_bf16(hi, xp[u][xi + 1], dot2_bf16(lo, xp[u][xi], dg[u]));
-                        else du[u] = dot2_bf16(hi, xp[u][xi + 1], dot2_bf16(lo, xp[u][xi], du[u]));
+                        float &a = q < 2 ? dg[u][q & 1] : du[u][q & 1];
+                        a = dot2_bf16(hi, xp[u][xi + 1], dot2_bf16(lo, xp[u][xi], a));
                     }
                 }
             }
@@ -98,8 +103,8 @@ __device__ __forceinline__ void fp8_gateup_item(const uint16_t *__restrict__ x, 
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
             if (u < nt) {
-                const float pg = seg_sum_dpp<LPR>(st.gs * dg[u]);
-                const float pu = seg_sum_dpp<LPR>(st.us * du[u]);
+                const float pg = seg_sum_dpp<LPR>(fmaf(st.gs[0], dg[u][0], st.gs[1] * dg[u][1]));
+                const float pu = seg_sum_dpp<LPR>(fmaf(st.us[0], du[u][0], st.us[1] * du[u][1]));
                 if (c == LPR - 1 && ir.valid_step(s, lrow)) s_out[u][nl] = silu(pg) * pu;
             }
         }
@@ -143,7 +148,7 @@ __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPt
     const int c = lane % LPR, sub = lane / LPR;
     struct Stage {
         uint4 v[DEC_NB][2];
-        float s[DEC_NB];
+        float s[DEC_NB][2];
     };
     const int e = tile.expert, nt = tile.rows;
     const int steps = ir.steps;
@@ -153,10 +158,11 @@ __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPt
         for (int b = 0; b < DEC_NB; ++b) {
             const int sb_ = s0 + b;
             const int d = ir.valid_step(sb_, lrow) ? ir.grow_step(sb_, lrow) : ir.grow(0);
-            const uint4 *src = reinterpret_cast<const uint4 *>(L.dq + ((size_t)e * H + d) * I + 32 * c);
+            const uint4 *src = reinterpret_cast<const uint4 *>(L.dq + ((size_t)e * H + d) * I + 16 * c);
             st.v[b][0] = src[0];
-            st.v[b][1] = src[1];
-            st.s[b] = fp8_block_scale(L.dsm, e, H, I, d, 32 * c);
+            st.v[b][1] = src[LPR];
+            st.s[b][0] = fp8_block_scale(L.dsm, e, H, I, d, 16 * c);
+            st.s[b][1] = fp8_block_scale(L.dsm, e, H, I, d, I / 2 + 16 * c);
         }
     };
     int tok[DECODE_TT];
@@ -187,7 +193,7 @@ __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPt
         for (int u = 0; u < DECODE_TT; ++u) {
             if (u < nt) {
                 gt[u] *= inv[u];
-                h_from_lds(s_h + u * DEC_HMAX, c, hp[u]);
+                h_from_lds_halves(s_h + u * DEC_HMAX, c, I / 2, hp[u]);
             }
         }
     };
@@ -197,20 +203,21 @@ __device__ __forceinline__ void fp8_down_item(int H, int I, int k, const LayerPt
             const int dl = (s0 + b) * (DEC_WAVES * RPW) + lrow;
             const uint32_t d8[8] = {st.v[b][0].x, st.v[b][0].y, st.v[b][0].z, st.v[b][0].w,
                                     st.v[b][1].x, st.v[b][1].y, st.v[b][1].z, st.v[b][1].w};
-            float a[DECODE_TT];
+            float a[DECODE_TT][2];
 #pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) a[u] = 0.f;
+            for (int u = 0; u < DECODE_TT; ++u) a[u][0] = a[u][1] = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t lo = e4m3_pair_f16<false>(d8[j]), hi = e4m3_pair_f16<true>(d8[j]);
 #pragma unroll
                 for (int u = 0; u < DECODE_TT; ++u)
-                    if (u < nt) a[u] = dot2_f16(hi, hp[u][2 * j + 1], dot2_f16(lo, hp[u][2 * j], a[u]));
+                    if (u < nt)
+                        a[u][j / 4] = dot2_f16(hi, hp[u][2 * j + 1], dot2_f16(lo, hp[u][2 * j], a[u][j / 4]));
             }
 #pragma unroll
             for (int u = 0; u < DECODE_TT; ++u) {
                 if (u < nt) {
-                    const float o = seg_sum_dpp<LPR>(st.s[b] * a[u]);
+                    const float o = seg_sum_dpp<LPR>(fmaf(st.s[b][0], a[u][0], st.s[b][1] * a[u][1]));
                     if (c == LPR - 1 && ir.valid_step(s0 + b, lrow)) s_out[u][dl] = gt[u] * o;
                 }
             }

@@ -44,9 +44,10 @@ __device__ __forceinline__ uint32_t sx_codes_f16(uint32_t pair) {
 
 // gate/up GEMV + SwiGLU of tokens tok0 .. tok0 + nt - 1 over rows ir of I,
 // h (fp32, [T][I]) out.  LPR = H / 32 lanes per row, each
-// lane 32 codes (two 16-byte loads); a wave-load covers RPW = 64 / LPR rows
-// of gate and of up.  Pipelined in two register stages as the routed
-// gate/up GEMV.
+// lane 32 codes: [16c, 16c + 16) of the row's first half and of its second
+// half (two 16-byte loads, each instruction reading whole cache lines; each
+// half in one 128-group); a wave-load covers RPW = 64 / LPR rows of gate and
+// of up.  Pipelined in two register stages as the routed gate/up GEMV.
 template <int LPR>
 __device__ __forceinline__ void shared_gateup_item(const uint16_t *__restrict__ x, const SharedPtrs &S, int tok0,
                                                    int nt, const ItemRows<DEC_WAVES * WAVE / LPR> &ir,
@@ -55,52 +56,55 @@ __device__ __forceinline__ void shared_gateup_item(const uint16_t *__restrict__ 
     const int H = S.H, I = S.I;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR, sub = lane / LPR;
-    const int gi = (32 * c) / SX_GROUP;
+    const int gi0 = (16 * c) / SX_GROUP, gi1 = (H / 2 + 16 * c) / SX_GROUP;
     const size_t smr = (size_t)(H / SX_GROUP);
     struct Stage {
         uint4 g[2], u[2];
-        uint32_t gs, us;
+        uint32_t gs[2], us[2];
     };
     const int steps = ir.steps;
     const int lrow = wave * RPW + sub;
     auto issue = [&](Stage &st, int s) {
         const size_t row = (size_t)(ir.valid_step(s, lrow) ? ir.grow_step(s, lrow) : ir.grow(0));
-        const uint4 *gp = reinterpret_cast<const uint4 *>(S.gq + row * H + 32 * c);
-        const uint4 *up = reinterpret_cast<const uint4 *>(S.uq + row * H + 32 * c);
+        const uint4 *gp = reinterpret_cast<const uint4 *>(S.gq + row * H + 16 * c);
+        const uint4 *up = reinterpret_cast<const uint4 *>(S.uq + row * H + 16 * c);
         st.g[0] = gp[0];
-        st.g[1] = gp[1];
+        st.g[1] = gp[LPR];
         st.u[0] = up[0];
-        st.u[1] = up[1];
-        st.gs = S.gs[row * smr + gi];
-        st.us = S.us[row * smr + gi];
+        st.u[1] = up[LPR];
+        st.gs[0] = S.gs[row * smr + gi0];
+        st.gs[1] = S.gs[row * smr + gi1];
+        st.us[0] = S.us[row * smr + gi0];
+        st.us[1] = S.us[row * smr + gi1];
     };
     uint32_t xp[DECODE_TT][16];
-    float xf[DECODE_TT][32], xs[DECODE_TT];
+    float xf[DECODE_TT][32], xs[DECODE_TT][2];
     auto fetch_x = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u)
-            if (u < nt) fetch_x_chunk(x + (size_t)(tok0 + u) * H, c, xp[u]);
+            if (u < nt) fetch_x_halves(x + (size_t)(tok0 + u) * H, c, H / 2, xp[u]);
     };
     auto prep_x = [&]() {
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
-            xs[u] = 0.f;
+            xs[u][0] = xs[u][1] = 0.f;
             if (u < nt) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     xf[u][2 * j] = bf16_to_f32(xp[u][j] & 0xffffu);
                     xf[u][2 * j + 1] = bf16_to_f32(xp[u][j] >> 16);
-                    xs[u] += xf[u][2 * j] + xf[u][2 * j + 1];
+                    xs[u][j / 8] += xf[u][2 * j] + xf[u][2 * j + 1];
                 }
             }
         }
     };
     auto consume = [&](const Stage &st, int s) {
         const int nl = s * (DEC_WAVES * RPW) + lrow;
-        const float sg = f16_to_f32((uint16_t)st.gs), su = f16_to_f32((uint16_t)st.us);
-        float dg[DECODE_TT], du[DECODE_TT];
+        const float sg[2] = {f16_to_f32((uint16_t)st.gs[0]), f16_to_f32((uint16_t)st.gs[1])};
+        const float su[2] = {f16_to_f32((uint16_t)st.us[0]), f16_to_f32((uint16_t)st.us[1])};
+        float dg[DECODE_TT][2], du[DECODE_TT][2];
 #pragma unroll
-        for (int u = 0; u < DECODE_TT; ++u) dg[u] = du[u] = 0.f;
+        for (int u = 0; u < DECODE_TT; ++u) dg[u][0] = dg[u][1] = du[u][0] = du[u][1] = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint4 v = q == 0 ? st.g[0] : q == 1 ? st.g[1] : q == 2 ? st.u[0] : st.u[1];
@@ -110,12 +114,12 @@ __device__ __forceinline__ void shared_gateup_item(const uint16_t *__restrict__ 
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const float f = (float)((d4[j] >> (8 * b)) & 0xffu);  // u, exact
-                    const int e = 16 * (q & 1) + 4 * j + b;
+                    const int e = 16 * (q & 1) + 4 * j + b;  // half q & 1
 #pragma unroll
                     for (int u = 0; u < DECODE_TT; ++u) {
                         if (u < nt) {
-                            if (q < 2) dg[u] = fmaf(f, xf[u][e], dg[u]);
-                            else du[u] = fmaf(f, xf[u][e], du[u]);
+                            if (q < 2) dg[u][q & 1] = fmaf(f, xf[u][e], dg[u][q & 1]);
+                            else du[u][q & 1] = fmaf(f, xf[u][e], du[u][q & 1]);
                         }
                     }
                 }
@@ -123,8 +127,10 @@ __device__ __forceinline__ void shared_gateup_item(const uint16_t *__restrict__ 
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
             if (u < nt) {
-                const float pg = seg_sum_dpp<LPR>(sg * fmaf(-128.f, xs[u], dg[u]));
-                const float pu = seg_sum_dpp<LPR>(su * fmaf(-128.f, xs[u], du[u]));
+                const float pg = seg_sum_dpp<LPR>(fmaf(sg[0], fmaf(-128.f, xs[u][0], dg[u][0]),
+                                                       sg[1] * fmaf(-128.f, xs[u][1], dg[u][1])));
+                const float pu = seg_sum_dpp<LPR>(fmaf(su[0], fmaf(-128.f, xs[u][0], du[u][0]),
+                                                       su[1] * fmaf(-128.f, xs[u][1], du[u][1])));
                 if (c == LPR - 1 && ir.valid_step(s, lrow)) s_out[u][nl] = silu(pg) * pu;
             }
         }
@@ -157,7 +163,8 @@ __device__ __forceinline__ void shared_gateup_item(const uint16_t *__restrict__ 
 }
 
 // down GEMV of tokens tok0 .. tok0 + nt - 1 over output rows ir of H, full
-// rows of h (LPR = I / 32 lanes per row, 32 codes each; each token's fp32 h
+// rows of h (LPR = I / 32 lanes per row, 32 codes each, split across the
+// row's halves as in the gate/up GEMV; each token's fp32 h
 // row staged once per item in LDS, scaled by the power of two that puts its
 // largest magnitude in [2^14, 2^15) and rounded to f16, the outputs scaled
 // back; h_to_lds), added into y:
@@ -173,12 +180,12 @@ __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, 
     const int H = S.H, I = S.I;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR, sub = lane / LPR;
-    const int gi = (32 * c) / SX_GROUP;
+    const int gi0 = (16 * c) / SX_GROUP, gi1 = (I / 2 + 16 * c) / SX_GROUP;
     const size_t smr = (size_t)(I / SX_GROUP);
     const uint32_t kf = opaque_magic(MAGIC_F16);
     struct Stage {
         uint4 v[DEC_NB][2];
-        uint32_t s[DEC_NB];
+        uint32_t s[DEC_NB][2];
     };
     const int steps = ir.steps;
     const int lrow = wave * RPW + sub;
@@ -187,10 +194,11 @@ __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, 
         for (int b = 0; b < DEC_NB; ++b) {
             const int sb_ = s0 + b;
             const size_t row = (size_t)(ir.valid_step(sb_, lrow) ? ir.grow_step(sb_, lrow) : ir.grow(0));
-            const uint4 *src = reinterpret_cast<const uint4 *>(S.dq + row * I + 32 * c);
+            const uint4 *src = reinterpret_cast<const uint4 *>(S.dq + row * I + 16 * c);
             st.v[b][0] = src[0];
-            st.v[b][1] = src[1];
-            st.s[b] = S.ds[row * smr + gi];
+            st.v[b][1] = src[LPR];
+            st.s[b][0] = S.ds[row * smr + gi0];
+            st.s[b][1] = S.ds[row * smr + gi1];
         }
     };
     // the tokens' h rows: fetched before the first weight stages, staged in
@@ -205,29 +213,19 @@ __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, 
         h_to_lds<false, true>(hfe, nt, I, s_hs, hinv);
 #pragma unroll
         for (int u = 0; u < DECODE_TT; ++u) {
-            if (u < nt) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(s_hs + u * DEC_HMAX + 32 * c);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 v = src[q];
-                    hp[u][4 * q + 0] = v.x;
-                    hp[u][4 * q + 1] = v.y;
-                    hp[u][4 * q + 2] = v.z;
-                    hp[u][4 * q + 3] = v.w;
-                }
-            }
+            if (u < nt) h_from_lds_halves(s_hs + u * DEC_HMAX, c, I / 2, hp[u]);
         }
     };
     auto consume = [&](const Stage &st, int s0) {
 #pragma unroll
         for (int b = 0; b < DEC_NB; ++b) {
             const int dl = (s0 + b) * (DEC_WAVES * RPW) + lrow;
-            const float sd = f16_to_f32((uint16_t)st.s[b]);
+            const float sd0 = f16_to_f32((uint16_t)st.s[b][0]), sd1 = f16_to_f32((uint16_t)st.s[b][1]);
             const uint32_t d8[8] = {st.v[b][0].x, st.v[b][0].y, st.v[b][0].z, st.v[b][0].w,
                                     st.v[b][1].x, st.v[b][1].y, st.v[b][1].z, st.v[b][1].w};
-            float a[DECODE_TT];
+            float a[DECODE_TT][2];
 #pragma unroll
-            for (int u = 0; u < DECODE_TT; ++u) a[u] = 0.f;
+            for (int u = 0; u < DECODE_TT; ++u) a[u][0] = a[u][1] = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t w = d8[j] ^ SX_FLIP;
@@ -235,12 +233,13 @@ __device__ __forceinline__ void shared_down_item(const SharedPtrs &S, int tok0, 
                 const uint32_t qb = sx_codes_f16(insert_codes<0x00ff00ffu>(w >> 8, kf));  // codes 1, 3
 #pragma unroll
                 for (int u = 0; u < DECODE_TT; ++u)
-                    if (u < nt) a[u] = dot2_f16(qb, hp[u][2 * j + 1], dot2_f16(qa, hp[u][2 * j], a[u]));
+                    if (u < nt)
+                        a[u][j / 4] = dot2_f16(qb, hp[u][2 * j + 1], dot2_f16(qa, hp[u][2 * j], a[u][j / 4]));
             }
 #pragma unroll
             for (int u = 0; u < DECODE_TT; ++u) {
                 if (u < nt) {
-                    const float o = seg_sum_dpp<LPR>(sd * a[u]) * hinv[u];
+                    const float o = seg_sum_dpp<LPR>(fmaf(sd0, a[u][0], sd1 * a[u][1])) * hinv[u];
                     if (c == LPR - 1 && ir.valid_step(s0 + b, lrow)) s_out[u][dl] = o;
                 }
             }
