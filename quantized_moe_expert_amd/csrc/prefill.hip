@@ -468,9 +468,11 @@ __device__ __forceinline__ uint32_t canonical_row_max(const uint16_t *__restrict
 }
 
 // STAGE 1: A = x16 rows gathered through perm, B = gate | up codes,
-//          epilogue * 2^e(token), SwiGLU -> h (f16).
+//          epilogue SwiGLU of the accumulators times 2^e(token) -> h (f16,
+//          scaled per row and per block as described at the epilogue).
 // STAGE 2: A = h rows (contiguous sorted rows), B = down codes,
-//          epilogue gate-weighted rows of z (f16) for the combine kernel.
+//          epilogue gate-weighted rows of z (f16, scaled the same way) for
+//          the combine kernel.
 // Work items are (tile, column block).  Workgroups are spread over the 8 XCDs
 // round-robin (XCD = block index mod 8).  Tile rank t of the schedule `order`
 // (largest tiles first; null: the tile list's own order) goes to XCD t % 8,

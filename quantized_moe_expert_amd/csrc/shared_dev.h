@@ -17,9 +17,11 @@
 //     the lane's sum of x taken once per token;
 //   down: u is inserted into the mantissa of the f16 pair (1024, 1024) and
 //     1152 is subtracted, which leaves q exactly as f16; q * h is exact in
-//     fp32 against h rounded to f16.
-// The group scale multiplies each lane's partial sum (a lane's 32 codes lie
-// in one group) before the lanes of a row are added.
+//     fp32 against h scaled per token row by a power of two and rounded to
+//     f16.
+// A lane's codes are two 16-byte pieces, one in each half of the row, each
+// inside one group; the group scale multiplies each piece's partial sum
+// before the lanes of a row are added.
 #pragma once
 
 #include "decode_dev.h"
