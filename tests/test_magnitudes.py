@@ -142,3 +142,25 @@ def test_shared_expert_magnitudes(xs, T, fused):
         for t in range(T):
             assert_close(yg[t], yr[t], f"shared mix T={T} fused={fused} token {t}", abs_scaled=True)
     say(f"[magnitudes shared] x2^{xs}: rel L2 {r:.2e} max abs {a:.2e} (|y| max {np.max(np.abs(yr)):.2e})")
+
+
+@pytest.mark.parametrize("T", [16, 100, 300])
+def test_shared_expert_magnitudes_wide_inner(T):
+    """Inner size 2048: the GEMV path stages 2048-wide h rows, and the GEMM path keeps 16 exponent bytes
+    per token (one per 128 columns of h) and folds 16 block factors into the down GEMM's scales; per-token
+    activation scales 2^-10 to 2^9, each row checked on its own."""
+    import quantized_moe_expert_amd as m
+    Hs, Is = 256, 2048
+    say(f"[magnitudes shared wide] T={T}")
+    sx = synth.random_shared(Hs, Is, seed=47, device="cuda", tag="mag_shared_wide")
+    row = torch.tensor([2.0 ** (-10 + (5 * t) % 20) for t in range(T)], device="cuda")[:, None]
+    x = synth.bf16_bits(synth.normal((T, Hs), 1.0, 47, f"mag/sxw/{T}", "cuda") * row)
+    ws = torch.empty(max(m.workspace_size(m.WS_SHARED, T, 1, 1, Hs, Is), 256), dtype=torch.uint8, device="cuda")
+    y = torch.full((T, Hs), float("nan"), dtype=torch.float32, device="cuda")
+    m.moe_q4_shared(x, T, sx, y, 0, ws)
+    torch.cuda.synchronize()
+    yr = oracle.shared(Hs, Is, *_host(sx), np_u16(x), T)
+    yg = y.cpu().numpy()
+    assert_close(yg, yr, f"shared wide T={T}", abs_scaled=True)
+    for t in range(T):
+        assert_close(yg[t], yr[t], f"shared wide T={T} token {t}", abs_scaled=True)
