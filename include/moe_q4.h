@@ -271,7 +271,8 @@ MOE_Q4_API int moe_q4_decode(const void *x, const int32_t *topk_idx, const float
  * the row's largest scale lose precision; FP8 and NVFP4 codes enter
  * exactly); h between the two products and each routed row's gate-weighted
  * down output are rounded to f16 after scaling by a power of two chosen per
- * block (h: 128 columns of I, one exponent for all rows of a work tile; the
+ * block, after each row's 2^-2e with 2^e the power of two of its token's x
+ * (h: 128 columns of I, one exponent for all rows of a work tile; the
  * down output: 32 rows by 64 columns of H) that puts the block's largest
  * magnitude into [2^14, 2^15), so f16's range limits none of them, and a
  * token's k rows are summed in fp32 into y (float

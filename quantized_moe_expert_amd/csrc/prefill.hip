@@ -75,7 +75,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // One wave per row: e = floor(log2 max|x|) - 14 (0 for a zero row or one
 // holding inf / NaN), x16 = f16(x * 2^-e), xexp[t] = e.  ORDER of the
 // elements inside each group of 8: 0 natural, 1 PERM8 (0,4,1,5,2,6,3,7),
-// 2 PERM4 (0,2,1,3,4,6,5,7).
+// 2 PERM4 (0,2,1,3,4,6,5,7); 3: xexp only (no x16; the block-FP8 GEMMs read
+// x as given and use e only to scale h and z).
 template <int ORDER>
 __device__ __forceinline__ void x_row_to_f16(const uint16_t *__restrict__ x, int64_t t, int H,
                                              uint16_t *__restrict__ x16, int32_t *__restrict__ xexp) {
@@ -98,8 +99,8 @@ __device__ __forceinline__ void x_row_to_f16(const uint16_t *__restrict__ x, int
         const int be = (int)(mx >> 7);                  // biased exponent (0: subnormal)
         e = (be == 0 ? -126 : be - 127) - 14;
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(x16 + t * H);
-    for (int i = lane; i < H / 8; i += 64) {
+    uint4 *dst = ORDER == 3 ? nullptr : reinterpret_cast<uint4 *>(x16 + t * H);
+    for (int i = lane; ORDER != 3 && i < H / 8; i += 64) {
         const uint4 v = src[i];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t o[4];
@@ -897,7 +898,8 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t *__restrict__ act, int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles,
     const int32_t *__restrict__ ntiles, const int32_t *__restrict__ perm, const float *__restrict__ topk_gate,
     uint16_t *__restrict__ h_out, uint16_t *__restrict__ z, const int32_t *__restrict__ order,
-    int8_t *__restrict__ hx, int8_t *__restrict__ zx) {  // exponents of h and z, as grouped_gemm_kernel
+    int8_t *__restrict__ hx, int8_t *__restrict__ zx,  // exponents of h and z, as grouped_gemm_kernel
+    const int32_t *__restrict__ xexp) {                 // STAGE 1: the per-token exponent e
     const int ncb = STAGE == 1 ? I / 128 : H / BROWS;
     const int bx = blockIdx.x, local = bx / 8;
     const int t = (local / ncb) * 8 + bx % 8;  // rank in the schedule (as grouped_gemm_kernel)
@@ -916,11 +918,11 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(16))) uint8_t s_ring1[STAGE8_BYTES];
     __shared__ float s_sc8[4][2][16];  // per wave and N-subtile: the block scales along K (K <= 2048)
     __shared__ int s_tok[BM];
-    __shared__ float s_gt[BM];  // STAGE 1: 1 (0 for padding rows); STAGE 2: the row's gate times 2^-s_min
+    __shared__ float s_gt[BM];  // STAGE 1: 2^-e of the row's token (0 for padding rows); STAGE 2: gate 2^-s_min
     __shared__ float s_fb[16];  // STAGE 2: 2^(s_min - s_b) per 128-input block b of h
     __shared__ uint32_t s_red[PF_BLOCK / 64];
     const int nbh = I / 128;
-    int smin = 64;  // as grouped_gemm_kernel (no per-token exponent: x enters as given)
+    int smin = 64;  // as grouped_gemm_kernel
     if (STAGE == 2 && tid < BM)
         for (int b = 0; b < nbh; ++b) {
             const int sb = hx[(size_t)row0 * nbh + b];
@@ -933,7 +935,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (tid < rows) {
             const int p = perm[row0 + tid];
             t = p / k;
-            v = STAGE == 2 ? topk_gate[p] * exp2i(-smin) : 1.f;
+            v = STAGE == 2 ? topk_gate[p] * exp2i(-smin) : exp2i(-xexp[t]);
         }
         s_tok[tid] = t;
         s_gt[tid] = v;
@@ -1016,8 +1018,10 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     __syncthreads();  // ring no longer read: the epilogue may reuse it
 
-    // epilogue as grouped_gemm_kernel's (without a per-token exponent), one
-    // 32-row subtile at a time through the two ring slots in turn
+    // epilogue as grouped_gemm_kernel's, one 32-row subtile at a time through
+    // the two ring slots in turn.  x enters unscaled, so GEMM1 forms
+    // h 2^-2e = (silu(acc) 2^-e) (acc_u 2^-e) here; GEMM2's z then carries
+    // 2^-2e as well, which the combine takes off.
     __shared__ int s_zs[4][PF_BLOCK / 64];
     RowScale rs{1.0f, 0};
     if (STAGE == 1) {
@@ -1028,7 +1032,7 @@ __global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = 32 * mi + 8 * (r / 4) + 4 * hf + (r % 4);
-                const float hv = silu(acc[mi][0][r]) * acc[mi][1][r] * s_gt[lr];
+                const float hv = (silu(acc[mi][0][r]) * s_gt[lr]) * (acc[mi][1][r] * s_gt[lr]);
                 acc[mi][0][r] = hv;
                 mloc = fmaxf(mloc, fabsf(hv));
             }
@@ -1627,20 +1631,24 @@ hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
 }
 
 static hipError_t launch_prefill_fp8(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
-                                     const GroupOut &g, uint16_t *h, uint16_t *z, int8_t *hx, int8_t *zx, float *y,
-                                     hipStream_t s, hipEvent_t const *ev) {
+                                     const GroupOut &g, int32_t *xexp, uint16_t *h, uint16_t *z, int8_t *hx,
+                                     int8_t *zx, float *y, hipStream_t s, hipEvent_t const *ev, bool xexp_ready) {
     const int H = L.H, I = L.I;
     const int64_t tiles = max_tiles(T * k, L.E, BM);
+    if (!xexp_ready)  // the per-token exponents only
+        hipLaunchKernelGGL(x_to_f16_kernel<3>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, H,
+                           (uint16_t *)nullptr, xexp);
     const unsigned nb1 = (unsigned)(8 * ((tiles + 7) / 8) * (I / 128));  // as launch_prefill_fmt
     const unsigned nb2 = (unsigned)(8 * ((tiles + 7) / 8) * (H / BROWS));
     launch_k(grouped_gemm_fp8_kernel<1>, dim3(nb1), dim3(PF_BLOCK), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, x,
              H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles, (const int32_t *)g.perm, gate, h, z,
-             (const int32_t *)g.order, hx, zx);
+             (const int32_t *)g.order, hx, zx, (const int32_t *)xexp);
     launch_k(grouped_gemm_fp8_kernel<2>, dim3(nb2), dim3(PF_BLOCK), s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr,
              (const uint16_t *)h, H, I, k, L, (const Tile *)g.tiles, (const int32_t *)g.ntiles,
-             (const int32_t *)g.perm, gate, h, z, (const int32_t *)(g.order2 ? g.order2 : g.order), hx, zx);
+             (const int32_t *)g.perm, gate, h, z, (const int32_t *)(g.order2 ? g.order2 : g.order), hx, zx,
+             (const int32_t *)nullptr);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, s, (const uint16_t *)z, (const int8_t *)zx,
-                       (const int32_t *)nullptr, (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
+                       (const int32_t *)xexp, (const int32_t *)g.inv, T, k, H, T * (int64_t)k, y);
     return hipGetLastError();
 }
 
@@ -1651,7 +1659,7 @@ hipError_t launch_prefill_experts(const uint16_t *x, const float *gate, int64_t 
     switch (L.fmt) {
         case 0: return launch_prefill_fmt<0>(x, gate, T, k, L, g, x16, xexp, h, z, hx, zx, y, s, ev, x16_ready);
         case 1: return launch_prefill_fmt<1>(x, gate, T, k, L, g, x16, xexp, h, z, hx, zx, y, s, ev, x16_ready);
-        case 2: return launch_prefill_fp8(x, gate, T, k, L, g, h, z, hx, zx, y, s, ev);
+        case 2: return launch_prefill_fp8(x, gate, T, k, L, g, xexp, h, z, hx, zx, y, s, ev, x16_ready);
         case 3: return launch_prefill_fmt<3>(x, gate, T, k, L, g, x16, xexp, h, z, hx, zx, y, s, ev, x16_ready);
         default: return hipErrorInvalidValue;
     }
@@ -1663,14 +1671,14 @@ hipError_t launch_prefill_prep(const uint16_t *logits, int64_t T, int E, int k, 
     const int64_t P = T * k;
     if (P <= GROUP_SINGLE_MAX || E > 1024 || k > 32) return hipErrorInvalidValue;
     const int64_t nch = (P + GROUP_CHUNK - 1) / GROUP_CHUNK;
-    const int64_t nconv = fmt == 2 ? 0 : (T + PREP_WAVES - 1) / PREP_WAVES;  // row-conversion workgroups
+    const int64_t nconv = (T + PREP_WAVES - 1) / PREP_WAVES;  // row-conversion workgroups
     const dim3 grid((unsigned)(nch + nconv)), block(PREP_WAVES * 64);
     const int npl = (E + 63) / 64;
 #define PREP(N, O, C) \
     hipLaunchKernelGGL((prefill_prep_kernel<N, O, C>), grid, block, 0, s, logits, T, E, k, idx, gate, g.chunk_cnt, x, H, x16, xexp)
 #define PREP_N(O, C) \
     if (npl <= 4) PREP(4, O, C); else if (npl <= 8) PREP(8, O, C); else PREP(16, O, C)
-    if (fmt == 2) PREP_N(0, false);       // block FP8: the GEMMs read x as given
+    if (fmt == 2) PREP_N(3, true);        // block FP8: the GEMMs read x as given; the exponents only
     else if (fmt == 3) PREP_N(0, true);   // NVFP4: x16 in natural order
     else PREP_N(1, true);                 // int4: x16 in PERM8 order
 #undef PREP_N

@@ -86,6 +86,36 @@ def test_magnitudes(case, fmt, mode, T):
     say(f"[magnitudes] {name} fmt={fmt} {mode}: rel L2 {r:.2e} max abs {a:.2e} (|y| max {np.max(np.abs(yr)):.2e})")
 
 
+@pytest.mark.parametrize("mode,T", [("decode", 16), ("prefill", 96), ("prefill", 600), ("prefill_pack", 600)])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_magnitudes_mixed_tokens(fmt, mode, T):
+    """Tokens of one call at scales 2^-10 to 2^9 (each token its own): the rows of a prefill tile then differ
+    by up to 2^19 in |x| and 2^38 in |h|, while the GEMMs' h and z exponents are shared over a tile's rows per
+    block of columns (after each row's own 2^-2e).  Every token's row must meet the bar on its own."""
+    import quantized_moe_expert_amd as m
+    say(f"[magnitudes mixed] fmt={fmt} {mode} T={T}")
+    lay = _wide_layer(fmt, None)
+    row = torch.tensor([2.0 ** (-10 + (7 * t) % 20) for t in range(T)], device="cuda")[:, None]
+    x = synth.bf16_bits(synth.normal((T, H), 1.0, 53, f"mag/xm/{T}", "cuda") * row)
+    logits = synth.bf16_bits(synth.normal((T, E), 1.0, 53, f"mag/lm/{T}", "cuda"))
+    _, idx, gate = hip_route(None, None, logits, T, H, E, K)
+    ir, gr = oracle.topk(np_u16(logits), T, E, K)
+    assert np.array_equal(idx.cpu().numpy(), ir)
+    pack = m.prefill_pack(lay) if mode == "prefill_pack" else None  # kept alive through the call
+    run = m.layer_struct(lay, pack=pack) if pack is not None else lay
+    y = hip_experts("decode" if mode == "decode" else "prefill", run, x, idx, gate, K)
+    torch.cuda.synchronize()
+    yr = oracle.experts(fmt, E, H, I, *oracle.layer_np(lay), np_u16(x), ir, gr, T, K,
+                        global_scale=oracle.layer_global(lay))
+    yg = y.cpu().numpy()
+    assert_close(yg, yr, f"mixed fmt={fmt} {mode}", abs_scaled=True)
+    worst = 0.0
+    for t in range(T):
+        r, _ = assert_close(yg[t], yr[t], f"mixed fmt={fmt} {mode} token {t}", abs_scaled=True)
+        worst = max(worst, r)
+    say(f"[magnitudes mixed] fmt={fmt} {mode}: worst per-token rel L2 {worst:.2e}")
+
+
 # ------------------------------------------------------------ shared expert
 
 def _host(sx):
