@@ -486,9 +486,12 @@ __device__ __forceinline__ uint32_t canonical_row_max(const uint16_t *__restrict
 // ONE: each workgroup takes one 32-row subtile of a tile (the subtiles of a
 // tile on one XCD, one after another), in a build for single subtiles only:
 // a third of the LDS and the registers of one subtile, three workgroups per
-// CU.  The host takes it when tiles are mostly single subtiles.
+// CU for GEMM1 and four for GEMM2 (128 VGPRs, no spills; four for GEMM1 as
+// well made the NVFP4 GEMM1 slower).  The host takes it when tiles are
+// mostly single subtiles.
 template <int FMT, int STAGE, bool ONE>
-__global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? 3 : 2, ONE ? 3 : 2))) void grouped_gemm_kernel(
+__global__ __launch_bounds__(PF_BLOCK) __attribute__((amdgpu_waves_per_eu(ONE ? (STAGE == 2 ? 4 : 3) : 2,
+                                                                          ONE ? (STAGE == 2 ? 4 : 3) : 2))) void grouped_gemm_kernel(
     const uint16_t *__restrict__ act,      // STAGE 1: x16 [T][H]; STAGE 2: h [P][I]
     const int32_t *__restrict__ xexp,      // STAGE 1: per-token exponent e
     int H, int I, int k, LayerPtrs L, const Tile *__restrict__ tiles, const int32_t *__restrict__ ntiles,
