@@ -34,6 +34,12 @@ Workloads (seeded synthetic inputs, shapes of the pages' model: hidden 2048,
                 the shared expert alone for the long prompt's 4096 tokens
                 (matrix-core GEMMs).
 
+With --lanes N the frame workloads run as one moe_q4_frame call per step:
+the 16 tokens split into N token lanes, each through all 40 layers on its own
+stream over 1/N of the expert kernels' resident grid, so one lane's layers
+overlap the other's (cross-layer pipelining); the roofline is then per lane
+launch.
+
 The prefill workloads give the layer its prefill copy of the weights
 (moe_q4_prefill_pack, made once before timing, as at weight load); with
 --no-pack the grouped GEMMs read the canonical arrays.
@@ -87,6 +93,8 @@ def parse():
                    help="prefill GEMMs read the canonical weight arrays instead of the prefill copy")
     p.add_argument("--deterministic", action="store_true",
                    help="moe_q4_forward_det: decode y summed per token in slot order (run-to-run identical)")
+    p.add_argument("--lanes", type=int, default=None,
+                   help="frame workloads: run the frame as this many token lanes on their own streams (moe_q4_frame)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy 3 times (HBM counter calibration) and exit")
     return p.parse_args()
@@ -260,6 +268,32 @@ def main():
     ybuf = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(2)]
     xbuf = [torch.empty_like(case.x), torch.empty_like(case.x)]
     state = {"i": 0}
+    lanes = args.lanes
+    if lanes is not None and (base_wl != "frame" or args.deterministic):
+        raise SystemExit("--lanes applies to the frame workloads (without --deterministic)")
+    if lanes is not None:
+        # the frame as token lanes: one moe_q4_frame call per step
+        nlay = len(layers)
+        fr = {"xc": torch.empty((nlay - 1, T, H), dtype=case.x.dtype, device=dev),
+              "yc": torch.empty((nlay, T, H), dtype=torch.float32, device=dev),
+              "lg": torch.empty((nlay, T, E), dtype=torch.int16, device=dev),
+              "idx": torch.empty((nlay, T, k), dtype=torch.int32, device=dev),
+              "gate": torch.empty((nlay, T, k), dtype=torch.float32, device=dev)}
+        fr["ws"] = torch.empty(max(m.frame_workspace_size(T, E, k, H, I, SHARED_INTER if with_shared else 0, lanes),
+                                   256), dtype=torch.uint8, device=dev)
+        lane_streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(lanes - 1)]
+
+        def frame_call(evs=None):
+            m.moe_q4_frame(case.x, T, k, structs, routers, sstructs, fr["xc"], fr["yc"], fr["lg"], fr["idx"],
+                           fr["gate"], lanes, lane_streams, fr["ws"], events=evs)
+
+        def lanes_fork():
+            for s_ in lane_streams[1:]:
+                s_.wait_stream(torch.cuda.current_stream())
+
+        def lanes_join():
+            for s_ in lane_streams[1:]:
+                torch.cuda.current_stream().wait_stream(s_)
 
     def layer_ids():
         if base_wl == "decode":
@@ -292,6 +326,9 @@ def main():
 
     def step():
         """One step: every layer of the workload once."""
+        if lanes is not None:
+            frame_call()
+            return
         for j, li in enumerate(layer_ids()):
             call(j, li, None)
         state["i"] += 1
@@ -301,6 +338,12 @@ def main():
         the start and end of the call's two main kernels (gate/up and routing
         launches for decode, the two grouped GEMMs for prefill, gate/up and
         down launches of the shared expert alone) on the launch stream."""
+        if lanes is not None:  # per (layer, lane): events[(j * lanes + i) * 4 ...]
+            frame_call([e.cuda_event for evs in evsets for e in evs])
+            for j in range(len(layers)):
+                for i in range(lanes):
+                    routed.append(fr["idx"][j, T * i // lanes:T * (i + 1) // lanes].clone())
+            return
         for j, li in enumerate(layer_ids()):
             call(j, li, [e.cuda_event for e in evsets[j]])
             if not only_shared:
@@ -310,14 +353,22 @@ def main():
     routed = []
 
     # ---- warmup + timed steps ------------------------------------------------
+    if lanes is not None:
+        lanes_fork()
     for _ in range(W):
         step()
+    if lanes is not None:
+        lanes_join()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
+    if lanes is not None:  # the lane streams start after `start` and `stop` follows them all
+        lanes_fork()
     for _ in range(K):
         step()
+    if lanes is not None:
+        lanes_join()
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -329,15 +380,20 @@ def main():
     # ---- stage timing of the dominant kernel (same work, events on the stream)
     nev = m.STAGE_EVENTS
     prof_steps = max(1, min(K, 50 if nl_per_step == 1 else 2))
-    ev_sets = [[[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(nl_per_step)]
+    per_call = nl_per_step * (lanes or 1)  # event sets per step: one per layer (and lane)
+    ev_sets = [[[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(per_call)]
                for _ in range(prof_steps)]
     for per_step in ev_sets:  # materialise the event handles
         for evs in per_step:
             for e in evs:
                 e.record()
     torch.cuda.synchronize()
+    if lanes is not None:
+        lanes_fork()
     for per_step in ev_sets:
         step_profiled(per_step)
+    if lanes is not None:
+        lanes_join()
     torch.cuda.synchronize()
     # [0]: the dominant kernel (decode gate/up GEMV / prefill gate-up GEMM),
     # [1]: the second kernel (decode routing launch / prefill down GEMM); each is the span
@@ -352,8 +408,10 @@ def main():
     act = float(np.mean([torch.unique(r).numel() for r in routed])) if routed else 0.0
     lay0 = layers[0]
     proj_bytes = expert_bytes(lay0) // 3        # one projection of one expert (codes + scales)
-    P = T * k
-    sx_bytes = shared_gateup_bytes(shareds[0]) + T * SHARED_INTER * 4 if with_shared else 0  # + h (fp32) out
+    nlanes = lanes or 1
+    Tl = T // nlanes  # tokens per launch (per lane with --lanes)
+    P = Tl * k
+    sx_bytes = shared_gateup_bytes(shareds[0]) + Tl * SHARED_INTER * 4 if with_shared else 0  # + h (fp32) out
     if shared_gemm:
         # dominant kernel: the shared gate/up GEMM + SwiGLU on the matrix cores
         dom = "shared_gemm_kernel<1> (gate/up f16 GEMM + SwiGLU)"
@@ -376,12 +434,13 @@ def main():
         # dominant kernel: gate/up GEMV + SwiGLU: reads the gate and up codes and
         # scales of every active expert once and the activations, writes h (fp32)
         dom = "decode_gateup_kernel"
-        alg_bytes = act * 2 * proj_bytes + T * H * 2 + P * I * 4 + sx_bytes
+        alg_bytes = act * 2 * proj_bytes + Tl * H * 2 + P * I * 4 + sx_bytes
         achieved = alg_bytes / (stage_avg[0] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(dom, args.workload, "decode.hip"), "kernel": dom + (
-                    " (routed and shared items)" if with_shared else ""),
+                "traffic": None if lanes else recorded_traffic(dom, args.workload, "decode.hip"), "kernel": dom + (
+                    " (routed and shared items)" if with_shared else "") + (
+                    f" (one lane's launch, {lanes} lanes side by side)" if lanes else ""),
                 "avg_us": round(float(stage_avg[0]) * 1e3, 3), "algorithmic_bytes": int(alg_bytes),
                 "active_experts": int(act)}
     else:
@@ -412,7 +471,7 @@ def main():
         # x in, y out (the shared expert's codes when present)
         router_bytes = E * H * 2 if routers[0] is not None else 0
         shared_all = shared_gateup_bytes(shareds[0]) * 3 // 2 if with_shared else 0  # gate, up, down
-        layer_bytes = router_bytes + act * 3 * proj_bytes + T * H * 2 + T * H * 4 + shared_all
+        layer_bytes = nlanes * (router_bytes + act * 3 * proj_bytes + Tl * H * 2 + Tl * H * 4 + shared_all)
         step_bytes = layer_bytes * nl_per_step
         step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
         roof["step"] = {"algorithmic_bytes": int(step_bytes), "achieved": round(step_gbs, 1), "unit": "GB/s",
@@ -459,7 +518,7 @@ def main():
                           synth.FMT_ASYM_G64: "asym_g64", synth.FMT_SYM_G128: "sym_g128",
                           synth.FMT_FP8_B128: "fp8_e4m3_b128", synth.FMT_NVFP4: "nvfp4"}[case.fmt],
                       "shared_expert": with_shared, "deterministic": bool(args.deterministic),
-                      "weights": "prefill copy" if use_pack else "canonical"},
+                      "weights": "prefill copy" if use_pack else "canonical", "lanes": nlanes},
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 

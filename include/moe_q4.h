@@ -387,6 +387,56 @@ MOE_Q4_API int moe_q4_forward_det(const void *x, const float *residual_y, void *
                                   const moe_q4_shared_expert *shared, int32_t *topk_idx, float *topk_gate, float *y,
                                   void *ws, size_t ws_bytes, moe_q4_stream stream, void *const *events);
 
+/*
+ * A decode frame: n_layers MoE layers in sequence over T tokens, the
+ * residual chain of the backbone (drama-rs page, "Experts: where they run":
+ * the experts of every layer set the speed of a frame), run as `lanes`
+ * token lanes side by side.  Every step of the chain works token by token
+ * (routing, experts, combine, the residual step), so lane i takes token rows
+ * [T*i/lanes, T*(i+1)/lanes) through all n_layers layers on streams[i], and
+ * layer j of one lane overlaps layers j - 1 and j + 1 of another: one lane's
+ * routing and kernel ramps run beside the other's weight streaming (the
+ * pages' engine hides the gaps between its weight-streaming launches by
+ * prefetching the next kernel's weights into L2; drama-rs page, "Footprint
+ * and speed").  Each lane's expert GEMVs take 1/lanes of the GPU's resident
+ * grid.  Measured on MI355X at 16 tokens x 40 layers of 256 experts: two
+ * lanes 2.21 ms per frame against 2.30 ms for one; three or four lanes, or
+ * two with whole-GPU grids, were slower.
+ *   x          bf16 [T][H]: layer 0's input.
+ *   layers     [n_layers]: one shape (E, H, I) for every layer; router_w
+ *              [n_layers] bf16 [E][H] router weights (required); shared:
+ *              NULL or [n_layers] shared experts of one inner size.
+ *   x_chain    bf16 [n_layers - 1][T][H] (out; NULL when n_layers == 1):
+ *              entry j - 1 is layer j's input bf16(x_{j-1} + y_{j-1}).
+ *   y_chain    float [n_layers][T][H] (out): entry j is layer j's y.
+ *   logits     bf16 [n_layers][T][E], topk_idx int32 [n_layers][T][k],
+ *   topk_gate  float [n_layers][T][k] (out): each layer's routing.
+ *   lanes      1 .. MOE_Q4_FRAME_MAX_LANES, at most T; lanes == 1 is
+ *              n_layers moe_q4_forward_ex calls on streams[0].
+ *   streams    [lanes] streams.  Inputs must be complete before any of
+ *              them reaches the call, and the outputs are complete when all
+ *              of them have passed it (the caller orders the streams, e.g.
+ *              with events); the lanes share no memory.
+ *   ws         >= moe_q4_frame_workspace_size(T, E, k, H, I, shared inter
+ *              size or 0, lanes) bytes, untouched until every stream has
+ *              passed the call; the call clears its routing counters itself
+ *              (no moe_q4_workspace_init needed).
+ *   events     NULL, or n_layers * lanes * MOE_Q4_STAGE_EVENTS events:
+ *              entries [(j * lanes + i) * MOE_Q4_STAGE_EVENTS, +4) are
+ *              recorded as moe_q4_forward_ex's for layer j of lane i.
+ * Results equal moe_q4_forward_ex applied layer by layer to each lane's
+ * rows.  Every argument of every layer and lane is checked before the first
+ * launch; a launch failure after some launches returns MOE_Q4_ERR_HIP with
+ * the earlier work enqueued.
+ */
+#define MOE_Q4_FRAME_MAX_LANES 4
+MOE_Q4_API size_t moe_q4_frame_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I,
+                                              int32_t shared_inter, int32_t lanes);
+MOE_Q4_API int moe_q4_frame(const void *x, int64_t T, int32_t k, int32_t n_layers, const moe_q4_layer *layers,
+                            const void *const *router_w, const moe_q4_shared_expert *shared, void *x_chain,
+                            float *y_chain, void *logits, int32_t *topk_idx, float *topk_gate, int32_t lanes,
+                            const moe_q4_stream *streams, void *ws, size_t ws_bytes, void *const *events);
+
 /* Clears the control block of a workspace used with moe_q4_forward (once,
  * after allocation).  Enqueued on stream. */
 MOE_Q4_API int moe_q4_workspace_init(void *ws, size_t ws_bytes, moe_q4_stream stream);

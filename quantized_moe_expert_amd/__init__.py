@@ -13,7 +13,8 @@ from ._lib import (ASYM_G64, SYM_G128, FP8_B128, NVFP4, WS_DECODE, WS_GROUP, WS_
                    moe_q4_forward_timed, moe_q4_workspace_init, WS_SHARED, SharedExpert, shared_struct,
                    moe_q4_shared, moe_q4_dequant_int8, moe_q4_forward_ex, moe_q4_shared_timed,
                    moe_q4_prefill_pack_size, moe_q4_prefill_pack, prefill_pack,
-                   moe_q4_forward_noalloc, NOALLOC_SCRATCH_BYTES, moe_q4_forward_det, WS_FORWARD_DET)
+                   moe_q4_forward_noalloc, NOALLOC_SCRATCH_BYTES, moe_q4_forward_det, WS_FORWARD_DET,
+                   FRAME_MAX_LANES, frame_workspace_size, moe_q4_frame)
 from .layer import MoeQ4Layer
 
 __all__ = ["ASYM_G64", "SYM_G128", "FP8_B128", "NVFP4", "WS_DECODE", "WS_GROUP", "WS_PREFILL", "WS_ROUTE", "EXPORTS", "MoeQ4Error",
@@ -23,4 +24,5 @@ __all__ = ["ASYM_G64", "SYM_G128", "FP8_B128", "NVFP4", "WS_DECODE", "WS_GROUP",
            "moe_q4_forward_timed", "moe_q4_workspace_init", "WS_SHARED", "SharedExpert", "shared_struct",
            "moe_q4_shared", "moe_q4_dequant_int8", "moe_q4_forward_ex", "moe_q4_shared_timed",
            "moe_q4_prefill_pack_size", "moe_q4_prefill_pack", "prefill_pack",
-           "moe_q4_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_q4_forward_det", "WS_FORWARD_DET"]
+           "moe_q4_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_q4_forward_det", "WS_FORWARD_DET",
+           "FRAME_MAX_LANES", "frame_workspace_size", "moe_q4_frame"]

@@ -26,9 +26,11 @@ EXPORTS = ("moe_q4_workspace_size", "moe_q4_route", "moe_q4_group", "moe_q4_deco
            "moe_q4_workspace_init",
            "moe_q4_shared", "moe_q4_shared_timed", "moe_q4_dequant_int8", "moe_q4_forward_ex",
            "moe_q4_dequant", "moe_q4_residual_bf16", "moe_q4_error_string",
-           "moe_q4_prefill_pack_size", "moe_q4_prefill_pack", "moe_q4_forward_noalloc", "moe_q4_forward_det")
+           "moe_q4_prefill_pack_size", "moe_q4_prefill_pack", "moe_q4_forward_noalloc", "moe_q4_forward_det",
+           "moe_q4_frame_workspace_size", "moe_q4_frame")
 NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_Q4_NOALLOC_SCRATCH_BYTES
 STAGE_EVENTS = 4
+FRAME_MAX_LANES = 4  # MOE_Q4_FRAME_MAX_LANES
 
 
 class MoeQ4Error(RuntimeError):
@@ -92,6 +94,12 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(ctypes.c_void_p)]
         L.moe_q4_forward_det.restype = ctypes.c_int
         L.moe_q4_forward_det.argtypes = L.moe_q4_forward_ex.argtypes
+        L.moe_q4_frame_workspace_size.restype = sz
+        L.moe_q4_frame_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+        L.moe_q4_frame.restype = ctypes.c_int
+        L.moe_q4_frame.argtypes = [P, i64, i32, i32, ctypes.POINTER(Layer), ctypes.POINTER(ctypes.c_void_p),
+                                   ctypes.POINTER(SharedExpert), P, P, P, P, P, i32,
+                                   ctypes.POINTER(ctypes.c_void_p), P, sz, ctypes.POINTER(ctypes.c_void_p)]
         L.moe_q4_workspace_init.restype = ctypes.c_int
         L.moe_q4_workspace_init.argtypes = [P, sz, P]
         L.moe_q4_dequant.restype = ctypes.c_int
@@ -275,6 +283,30 @@ def moe_q4_forward_det(x, residual_y, x_out, router_w, bias, logits, T, k, layer
     workspace from workspace_size(WS_FORWARD_DET, ...)."""
     moe_q4_forward_ex(x, residual_y, x_out, router_w, bias, logits, T, k, layer, shared, topk_idx, topk_gate, y,
                       ws, stream, events, _name="moe_q4_forward_det")
+
+
+def frame_workspace_size(T: int, E: int, k: int, H: int, I: int, shared_inter: int, lanes: int) -> int:
+    return int(lib().moe_q4_frame_workspace_size(int(T), int(E), int(k), int(H), int(I), int(shared_inter),
+                                                 int(lanes)))
+
+
+def moe_q4_frame(x, T, k, layers, routers, shared, x_chain, y_chain, logits, topk_idx, topk_gate, lanes, streams,
+                 ws, events=None):
+    """A decode frame of len(layers) layers as ``lanes`` token lanes, lane i on streams[i] (torch streams or
+    raw handles); ``layers`` / ``shared``: lists of Layer / SharedExpert structs (or objects with their
+    tensors), ``shared`` None for none; ``events``: None or len(layers) * lanes * STAGE_EVENTS handles."""
+    n = len(layers)
+    lay = (Layer * n)(*[l if isinstance(l, Layer) else layer_struct(l) for l in layers])
+    rws = (ctypes.c_void_p * n)(*[_ptr(r) for r in routers])
+    sx = None
+    if shared is not None:
+        sx = (SharedExpert * n)(*[s if isinstance(s, SharedExpert) else shared_struct(s) for s in shared])
+    sts = (ctypes.c_void_p * len(streams))(*[_stream(s) for s in streams])
+    ev = (ctypes.c_void_p * len(events))(*[int(e) for e in events]) if events is not None else None
+    w, nb = _ws(ws)
+    _check("moe_q4_frame",
+           lib().moe_q4_frame(_ptr(x), T, k, n, lay, rws, sx, _ptr(x_chain), _ptr(y_chain), _ptr(logits),
+                              _ptr(topk_idx), _ptr(topk_gate), lanes, sts, w, nb, ev))
 
 
 def moe_q4_workspace_init(ws, stream=None):

@@ -371,7 +371,7 @@ static int forward_checks(const void *x, const float *residual_y, void *x_out, c
 static int run_forward(const void *x, const float *residual_y, void *x_out, const void *router_w, const float *bias,
                        void *logits, int64_t T, int32_t k, const moe_q4_layer *w, const moe_q4_shared_expert *sx,
                        int32_t *topk_idx, float *topk_gate, float *y, void *ws, size_t ws_bytes,
-                       moe_q4_stream stream, void *const *events, bool det = false) {
+                       moe_q4_stream stream, void *const *events, bool det = false, int grid_div = 1) {
     int st = forward_checks(x, residual_y, x_out, logits, T, k, w, sx, topk_idx, topk_gate, y, events);
     if (st || T == 0) return st;
     const int E = w->num_experts, H = w->hidden, I = w->inter;
@@ -421,7 +421,7 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
             if (st) return st;
             st = hip_status(
                 launch_decode_experts_routed(xin, lg, T, k, L, d.g, topk_idx, topk_gate, d.h, y, s, e0, e1, Sf, hs,
-                                             zrows));
+                                             zrows, grid_div));
             return st ? st : shared_after(xin);
         }
         if (forward_fused_route(T, E) || !wr) {
@@ -438,7 +438,8 @@ static int run_forward(const void *x, const float *residual_y, void *x_out, cons
             if (!st) st = hip_status(launch_group(topk_idx, T, k, E, d.g, s, y, T * (int64_t)H, e2, e3));
         }
         if (st) return st;
-        st = hip_status(launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1, Sf, hs, zrows));
+        st = hip_status(
+            launch_decode_experts(xin, topk_gate, T, k, L, d.g, d.h, y, s, e0, e1, Sf, hs, zrows, grid_div));
         return st ? st : shared_after(xin);
     }
     if (residual_y) {
@@ -495,6 +496,113 @@ int moe_q4_forward_det(const void *x, const float *residual_y, void *x_out, cons
                        size_t ws_bytes, moe_q4_stream stream, void *const *events) {
     return run_forward(x, residual_y, x_out, router_w, bias, logits, T, k, w, shared, topk_idx, topk_gate, y, ws,
                        ws_bytes, stream, events, true);
+}
+
+// ------------------------------------------------------------ frame in token lanes
+
+// One lane's workspace: the layer forward's (with the shared expert's after
+// it), for the lane's tokens.
+static size_t frame_lane_bytes(int64_t TL, int32_t E, int32_t k, int32_t H, int32_t I, int32_t shared_inter) {
+    size_t b = moe_q4_workspace_size(MOE_Q4_WS_FORWARD, TL, E, k, H, I);
+    if (shared_inter > 0) b += moe_q4_workspace_size(MOE_Q4_WS_SHARED, TL, 1, 1, H, shared_inter);
+    return align_up(b);
+}
+
+// Token rows [r0, r1) of lane i of `lanes` over T tokens.
+static void frame_lane_rows(int64_t T, int i, int lanes, int64_t *r0, int64_t *r1) {
+    *r0 = T * i / lanes;
+    *r1 = T * (i + 1) / lanes;
+}
+
+size_t moe_q4_frame_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t shared_inter,
+                                   int32_t lanes) {
+    if (T <= 0 || lanes < 1 || lanes > MOE_Q4_FRAME_MAX_LANES || lanes > T || shared_inter < 0) return 0;
+    const int64_t TL = (T + lanes - 1) / lanes;  // the largest lane
+    const size_t b = frame_lane_bytes(TL, E, k, H, I, shared_inter);
+    return b ? b * (size_t)lanes : 0;
+}
+
+int moe_q4_frame(const void *x, int64_t T, int32_t k, int32_t n_layers, const moe_q4_layer *layers,
+                 const void *const *router_w, const moe_q4_shared_expert *shared, void *x_chain, float *y_chain,
+                 void *logits, int32_t *topk_idx, float *topk_gate, int32_t lanes, const moe_q4_stream *streams,
+                 void *ws, size_t ws_bytes, void *const *events) {
+    if (T < 0 || n_layers < 1 || !layers || !router_w || !streams) return MOE_Q4_ERR_INVALID_ARG;
+    if (lanes < 1 || lanes > MOE_Q4_FRAME_MAX_LANES || (T > 0 && lanes > T)) return MOE_Q4_ERR_INVALID_ARG;
+    if (!x || !y_chain || !logits || !topk_idx || !topk_gate || (n_layers > 1 && !x_chain))
+        return MOE_Q4_ERR_INVALID_ARG;
+    const int E = layers[0].num_experts, H = layers[0].hidden, I = layers[0].inter;
+    const int32_t sinter = shared ? shared[0].inter : 0;
+    for (int j = 0; j < n_layers; ++j) {
+        if (!router_w[j]) return MOE_Q4_ERR_INVALID_ARG;
+        if (layers[j].num_experts != E || layers[j].hidden != H || layers[j].inter != I)
+            return MOE_Q4_ERR_INVALID_ARG;
+        if (shared && shared[j].inter != sinter) return MOE_Q4_ERR_INVALID_ARG;
+    }
+    if (events)
+        for (int64_t i = 0; i < (int64_t)n_layers * lanes * MOE_Q4_STAGE_EVENTS; ++i)
+            if (!events[i]) return MOE_Q4_ERR_INVALID_ARG;
+    int st = check_layer(&layers[0], false);
+    if (st) return st;
+    if (T == 0) return MOE_Q4_OK;
+    const size_t lane_b = frame_lane_bytes((T + lanes - 1) / lanes, E, k, H, I, sinter);
+    if (!lane_b) return MOE_Q4_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < lane_b * (size_t)lanes) return MOE_Q4_ERR_WORKSPACE;
+
+    // the pointers of layer j, lane i
+    struct LanePtrs {
+        const void *x;
+        const float *yres;
+        void *xout, *lg;
+        int32_t *idx;
+        float *gate, *y;
+        void *const *ev;
+    };
+    auto lane_ptrs = [&](int j, int i) {
+        int64_t r0, r1;
+        frame_lane_rows(T, i, lanes, &r0, &r1);
+        const int64_t TH = T * (int64_t)H;
+        LanePtrs p;
+        // layer j > 0: the residual step bf16(x_{j-1} + y_{j-1}) is its
+        // input x_j, written to x_chain[j - 1]
+        uint16_t *xc = static_cast<uint16_t *>(x_chain);
+        const uint16_t *xprev = j <= 1 ? static_cast<const uint16_t *>(x) : xc + (j - 2) * TH;
+        p.x = xprev + r0 * H;
+        p.yres = j == 0 ? nullptr : y_chain + (j - 1) * TH + r0 * H;
+        p.xout = j == 0 ? nullptr : static_cast<void *>(xc + (j - 1) * TH + r0 * H);
+        p.lg = static_cast<uint16_t *>(logits) + (j * T + r0) * (int64_t)E;
+        p.idx = topk_idx + (j * T + r0) * (int64_t)k;
+        p.gate = topk_gate + (j * T + r0) * (int64_t)k;
+        p.y = y_chain + j * TH + r0 * H;
+        p.ev = events ? events + ((int64_t)j * lanes + i) * MOE_Q4_STAGE_EVENTS : nullptr;
+        return p;
+    };
+    // every check before the first launch
+    for (int j = 0; j < n_layers; ++j)
+        for (int i = 0; i < lanes; ++i) {
+            int64_t r0, r1;
+            frame_lane_rows(T, i, lanes, &r0, &r1);
+            const LanePtrs p = lane_ptrs(j, i);
+            st = forward_checks(p.x, p.yres, p.xout, p.lg, r1 - r0, k, &layers[j], shared ? &shared[j] : nullptr,
+                                p.idx, p.gate, p.y, p.ev);
+            if (st) return st;
+        }
+    char *wsb = static_cast<char *>(ws);
+    for (int i = 0; i < lanes; ++i) {  // each lane's routing counters start at zero
+        st = hip_status(launch_fill_zero_u32(reinterpret_cast<uint32_t *>(wsb + lane_b * i), CONTROL_BYTES / 4,
+                                             reinterpret_cast<hipStream_t>(streams[i])));
+        if (st) return st;
+    }
+    for (int j = 0; j < n_layers; ++j)
+        for (int i = 0; i < lanes; ++i) {
+            int64_t r0, r1;
+            frame_lane_rows(T, i, lanes, &r0, &r1);
+            const LanePtrs p = lane_ptrs(j, i);
+            st = run_forward(p.x, p.yres, p.xout, router_w[j], nullptr, p.lg, r1 - r0, k, &layers[j],
+                             shared ? &shared[j] : nullptr, p.idx, p.gate, p.y, wsb + lane_b * i, lane_b,
+                             streams[i], p.ev, false, lanes);
+            if (st) return st;
+        }
+    return MOE_Q4_OK;
 }
 
 }  // extern "C"

@@ -781,16 +781,21 @@ template <int FMT, bool ROUTE, bool SHARED>
 static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
-                                     const SharedPtrs &S, float *hs, float *zrows) {
+                                     const SharedPtrs &S, float *hs, float *zrows, int grid_div) {
     const int H = L.H, I = L.I;
     const int P = (int)(T * k);
+    // 1/grid_div of the resident grid, a multiple of 8 (at least 8)
+    auto grid = [&](int resident) {
+        const int v = resident / grid_div / 8 * 8;
+        return dim3(v < 8 ? 8 : v);
+    };
     const int mt = (int)max_tiles(P, L.E, DECODE_TT);
     const dim3 block(DEC_WAVES * 64);
     switch (H / 64) {
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
         constexpr auto kern = decode_gateup_kernel<LP, FMT, ROUTE, SHARED>;                                      \
-        launch_k(kern, dim3(resident_grid<kern>()), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,   \
+        launch_k(kern, grid(resident_grid<kern>()), block, s, e0, e1, x, H, I, k, P, L, (const Tile *)g.tiles,    \
                  (const int32_t *)g.ntiles, mt, h, lg, (int)T, idx_out, gate_out, g, S, hs);                     \
     } break;
         CASE(1) CASE(2) CASE(4) CASE(8) CASE(16) CASE(32)
@@ -801,7 +806,7 @@ static hipError_t launch_experts_fmt(const uint16_t *x, const float *gate, int64
 #define CASE(LP)                                                                                                 \
     case LP: {                                                                                                   \
         constexpr auto kern = decode_down_kernel<LP, FMT, SHARED>;                                               \
-        launch_k(kern, dim3(resident_grid<kern>()), block, s, nullptr, nullptr, H, I, k, P, L,                   \
+        launch_k(kern, grid(resident_grid<kern>()), block, s, nullptr, nullptr, H, I, k, P, L,                    \
                  (const Tile *)g.tiles, (const int32_t *)g.ntiles, mt, gate, (const float *)h, y, (int)T, S,  \
                  (const float *)hs, zrows);                                                                   \
     } break;
@@ -824,15 +829,16 @@ template <bool ROUTE>
 static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                      const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
                                      hipEvent_t e1, const uint16_t *lg, int32_t *idx_out, float *gate_out,
-                                     const SharedPtrs *S, float *hs, float *zrows) {
+                                     const SharedPtrs *S, float *hs, float *zrows, int grid_div) {
     if (S && (zrows || !decode_fuses_shared(L, S))) return hipErrorInvalidValue;
+    if (grid_div < 1) return hipErrorInvalidValue;
     const SharedPtrs none{};
 #define FMT_CASE(F)                                                                                            \
     case F:                                                                                                    \
         return S ? launch_experts_fmt<F, ROUTE, true>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out, gate_out, \
-                                                      *S, hs, nullptr)                                         \
+                                                      *S, hs, nullptr, grid_div)                               \
                  : launch_experts_fmt<F, ROUTE, false>(x, gate, T, k, L, g, h, y, s, e0, e1, lg, idx_out,      \
-                                                       gate_out, none, nullptr, zrows);
+                                                       gate_out, none, nullptr, zrows, grid_div);
     switch (L.fmt) {
         FMT_CASE(0) FMT_CASE(1) FMT_CASE(2) FMT_CASE(3)
         default: return hipErrorInvalidValue;
@@ -842,8 +848,9 @@ static hipError_t launch_experts_any(const uint16_t *x, const float *gate, int64
 
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1, const SharedPtrs *S, float *hs, float *zrows) {
-    return launch_experts_any<false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr, S, hs, zrows);
+                                 hipEvent_t e1, const SharedPtrs *S, float *hs, float *zrows, int grid_div) {
+    return launch_experts_any<false>(x, gate, T, k, L, g, h, y, s, e0, e1, nullptr, nullptr, nullptr, S, hs, zrows,
+                                     grid_div);
 }
 
 // Every expert workgroup repeats this routing before its first weight load,
@@ -857,9 +864,10 @@ bool decode_routes_in_block(int64_t T, int k, int E) {
 hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logits, int64_t T, int k,
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const SharedPtrs *S,
-                                        float *hs, float *zrows) {
+                                        float *hs, float *zrows, int grid_div) {
     if (!decode_routes_in_block(T, k, L.E)) return hipErrorInvalidValue;
-    return launch_experts_any<true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate, S, hs, zrows);
+    return launch_experts_any<true>(x, gate, T, k, L, g, h, y, s, e0, e1, logits, idx, gate, S, hs, zrows,
+                                    grid_div);
 }
 
 hipError_t launch_decode_route_group(const uint16_t *x, const float *yres, uint16_t *xout, const uint16_t *wr,

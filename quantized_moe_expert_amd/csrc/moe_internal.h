@@ -130,12 +130,14 @@ hipError_t launch_group_after_count(const int32_t *idx, int64_t T, int k, int E,
 // decode_fuses_shared.  With zrows ([T*k][H] floats) the down kernel stores
 // each routed row there instead of adding into y, and a third launch sums
 // each token's rows into y in slot order (run-to-run identical y); zrows
-// excludes S.
+// excludes S.  grid_div > 1 launches each expert kernel over 1/grid_div of
+// its resident grid (a multiple of 8, so the XCD dealing is unchanged), for
+// token lanes that run side by side on their own streams.
 bool decode_fuses_shared(const LayerPtrs &L, const SharedPtrs *S);
 hipError_t launch_decode_experts(const uint16_t *x, const float *gate, int64_t T, int k, const LayerPtrs &L,
                                  const GroupOut &g, float *h, float *y, hipStream_t s, hipEvent_t e0 = nullptr,
                                  hipEvent_t e1 = nullptr, const SharedPtrs *S = nullptr, float *hs = nullptr,
-                                 float *zrows = nullptr);
+                                 float *zrows = nullptr, int grid_div = 1);
 hipError_t launch_decode_combine(const float *z, int64_t T, int k, int H, float *y, hipStream_t s);
 
 // Router logits (when wr != null), top-k and one-block grouping of T <= 64
@@ -159,7 +161,7 @@ hipError_t launch_decode_experts_routed(const uint16_t *x, const uint16_t *logit
                                         const LayerPtrs &L, const GroupOut &g, int32_t *idx, float *gate, float *h,
                                         float *y, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr,
                                         const SharedPtrs *S = nullptr, float *hs = nullptr,
-                                        float *zrows = nullptr);
+                                        float *zrows = nullptr, int grid_div = 1);
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero_u32(uint32_t *p, int64_t n, hipStream_t s);

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     assert set(names) == set(m.EXPORTS)
     lib = m.lib()
     for n in names:
@@ -171,6 +171,48 @@ def test_forward_validation():
     # every decode-path shape fits: 64 tokens x top-16 (1024 pairs) at H = I = 2048, E = 1024
     assert m.workspace_size(m.WS_FORWARD, 64, 1024, 16, 2048, 2048) <= m.NOALLOC_SCRATCH_BYTES
     assert L.moe_q4_workspace_init(FAKE, 100, None) == _lib.ERR_WORKSPACE
+
+
+def test_frame_validation():
+    """moe_q4_frame checks every layer and lane before its first launch."""
+    L = m.lib()
+    P = ctypes.c_void_p
+
+    def call(T=16, n=2, lanes=2, layers=None, routers=None, x=FAKE, xc=FAKE, nb=1 << 30, ws=FAKE, streams=None,
+             events=None):
+        layers = layers or [_layer() for _ in range(n)]
+        lay = (_lib.Layer * len(layers))(*layers)
+        rw = (P * n)(*(routers or [FAKE] * n))
+        sts = (P * max(lanes, 1))(*([None] * max(lanes, 1))) if streams is None else streams
+        return L.moe_q4_frame(x, T, 8, n, lay, rw, None, xc, FAKE, FAKE, FAKE, FAKE, lanes, sts, ws, nb, events)
+
+    assert call(T=0) == _lib.OK
+    assert call(n=0, layers=[_layer()]) == _lib.ERR_INVALID_ARG
+    assert call(lanes=0) == _lib.ERR_INVALID_ARG
+    assert call(lanes=m.FRAME_MAX_LANES + 1) == _lib.ERR_INVALID_ARG
+    assert call(T=1, lanes=2) == _lib.ERR_INVALID_ARG           # more lanes than tokens
+    assert call(x=None) == _lib.ERR_INVALID_ARG
+    assert call(xc=None) == _lib.ERR_INVALID_ARG                # two layers need the chain
+    assert call(routers=[FAKE, None]) == _lib.ERR_INVALID_ARG
+    assert call(layers=[_layer(), _layer(I=256)]) == _lib.ERR_INVALID_ARG  # one shape per frame
+    assert call(layers=[_layer(), _layer(fmt=4)]) == _lib.ERR_UNSUPPORTED  # layer 1 checked before any launch
+    assert call(layers=[_layer(), _layer(null="down_q")]) == _lib.ERR_INVALID_ARG
+    assert call(ws=None) == _lib.ERR_WORKSPACE
+    need = m.frame_workspace_size(16, 256, 8, 2048, 512, 0, 2)
+    assert need >= 2 * m.workspace_size(m.WS_FORWARD, 8, 256, 8, 2048, 512)
+    assert call(nb=need - 1) == _lib.ERR_WORKSPACE
+    assert call(x=FAKE + 2) == _lib.ERR_INVALID_ARG             # misaligned activations
+    assert L.moe_q4_frame(FAKE, 16, 8, 2, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, None, FAKE, 1 << 30,
+                          None) == _lib.ERR_INVALID_ARG
+    ev = (P * (2 * 2 * m.STAGE_EVENTS))(*([FAKE] * 15 + [None]))
+    assert call(events=ev) == _lib.ERR_INVALID_ARG
+    # sizes: lanes split the tokens as evenly as possible; out-of-range asks give 0
+    assert m.frame_workspace_size(5, 256, 8, 2048, 512, 0, 2) == 2 * m.frame_workspace_size(3, 256, 8, 2048, 512,
+                                                                                             0, 1)
+    assert m.frame_workspace_size(16, 256, 8, 2048, 512, 0, 0) == 0
+    assert m.frame_workspace_size(2, 256, 8, 2048, 512, 0, 3) == 0
+    assert m.frame_workspace_size(16, 256, 8, 2048, 512, 512, 1) > m.frame_workspace_size(16, 256, 8, 2048, 512, 0,
+                                                                                          1)
 
 
 def test_forward_det_validation():
