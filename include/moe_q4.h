@@ -400,7 +400,7 @@ MOE_Q4_API int moe_q4_forward_det(const void *x, const float *residual_y, void *
  * prefetching the next kernel's weights into L2; drama-rs page, "Footprint
  * and speed").  Each lane's expert GEMVs take 1/lanes of the GPU's resident
  * grid.  Measured on MI355X at 16 tokens x 40 layers of 256 experts: two
- * lanes 2.21 ms per frame against 2.30 ms for one; three or four lanes, or
+ * lanes 2.21 ms per frame against 2.30 ms for one; four lanes, or
  * two with whole-GPU grids, were slower.
  *   x          bf16 [T][H]: layer 0's input.
  *   layers     [n_layers]: one shape (E, H, I) for every layer; router_w
