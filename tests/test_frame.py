@@ -116,11 +116,12 @@ def test_frame_lanes_recipe(lanes):
     check_chain(case, lanes, run_frame(case, lanes))
 
 
-@pytest.mark.parametrize("T,lanes", [(5, 2), (5, 3), (7, 4), (40, 2)])
+@pytest.mark.parametrize("T,lanes", [(5, 2), (5, 3), (7, 4), (40, 2), (300, 2)])
 def test_frame_lanes_ragged(T, lanes):
-    """Uneven lanes (5 tokens as 2 + 3 and 1 + 2 + 2, 7 as 1 + 2 + 2 + 2) and
+    """Uneven lanes (5 tokens as 2 + 3 and 1 + 2 + 2, 7 as 1 + 2 + 2 + 2),
     lanes of 20 tokens (160 pairs: the routing launch's one-block grouping
-    instead of routing in the expert launches), 2 layers."""
+    instead of routing in the expert launches) and of 150 tokens (1200
+    pairs: the prefill path, its grouped GEMMs side by side), 2 layers."""
     case = frame_case(2, T)
     check_chain(case, lanes, run_frame(case, lanes), what=f"frame T={T}")
 
