@@ -49,11 +49,11 @@ def lane_streams(n):
     return [torch.cuda.current_stream()] + _streams[:n - 1]
 
 
-def frame_case(layers, T):
-    key = (layers, T)
+def frame_case(layers, T, fmt=None):
+    key = (layers, T, fmt)
     if key not in _cases:
-        say(f"[gen] frame recipe, {layers} layers, T={T}")
-        _cases[key] = synth.make_case(4, device="cuda", layers=layers, T=T)
+        say(f"[gen] frame recipe, {layers} layers, T={T}, format {fmt}")
+        _cases[key] = synth.make_case(4, device="cuda", layers=layers, T=T, fmt=fmt)
         torch.cuda.synchronize()
     return _cases[key]
 
@@ -124,6 +124,13 @@ def test_frame_lanes_ragged(T, lanes):
     pairs: the prefill path, its grouped GEMMs side by side), 2 layers."""
     case = frame_case(2, T)
     check_chain(case, lanes, run_frame(case, lanes), what=f"frame T={T}")
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_FP8_B128, synth.FMT_NVFP4])
+def test_frame_lanes_formats(fmt):
+    """Two lanes of 8 tokens, 2 layers, with block-FP8 and NVFP4 experts."""
+    case = frame_case(2, 16, fmt)
+    check_chain(case, 2, run_frame(case, 2), what=f"frame fmt {fmt}")
 
 
 def test_frame_lanes_shared_expert():
